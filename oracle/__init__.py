@@ -1,0 +1,22 @@
+"""CPU oracle for packed ternary weight-streaming decode.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package's smoke check and
+the benchmark's CPU-baseline leg may import this package.  The GPU path never
+calls it and shares no code with it.
+
+Everything here is plain numpy in float64, written from the page "The Neutrino
+Engine" (fermionresearch.com), and from the build's own packed-format
+specification for the packed-byte decoder/encoder:
+
+* ``reference``       - ternary GEMV with row scales, int8 vocabulary GEMV,
+                        greedy argmax, embedding-row gather, the decode-step
+                        composition;
+* ``packed_format``   - encoder/decoder of the 2-bit packed ternary format;
+* ``accounting``      - byte accounting of the 8B shape and the KV cache.
+
+Parity status of each function is stated in its module.  One part is
+"parity unpinned": the internals of the pages' own packed format (the pages
+name it but never specify it), so the build's 2-bit format is pinned only by
+its own specification and round trips, not by the pages.
+"""
+from . import accounting, packed_format, reference  # noqa: F401
