@@ -1,0 +1,222 @@
+/*
+ * pwg.h - C ABI of the packed ternary weight-streaming decode library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What it computes comes from the page "The Neutrino Engine"
+ * (fermionresearch.com):
+ *   - section "A 104 microsecond floor inside a 694 microsecond step": batch-1
+ *     decode applies every layer's attention and feed-forward projections to
+ *     the current activations, one multiply-accumulate per weight per token;
+ *     the output projection scores the hidden state against the whole
+ *     vocabulary; packed weights are read in place, with no float copy and no
+ *     tensor read twice per token;
+ *   - section "The file is not the traffic": projections are ternary with row
+ *     scales; two int8 vocabulary tables of 151,936 x 4,096; the input side
+ *     reads only the selected rows, the output side scores the whole table;
+ *   - intro and section "The same weights take four execution paths": decode
+ *     is greedy (argmax) and the loader re-arranges the same values for the
+ *     device at load time.
+ *
+ * Conventions (every entry point):
+ *   - Return value: PWG_OK (0) on success, a negative PWG_ERR_* code on
+ *     failure; pwg_last_error() then returns a message for the calling thread.
+ *     Arguments are validated before anything is enqueued; a failed call has
+ *     enqueued no work.  No C++ exception crosses this boundary.
+ *   - Ownership: the caller owns and allocates every buffer.  The GPU entry
+ *     points allocate nothing, free nothing and never synchronise, so they may
+ *     be recorded into a HIP graph with stream capture.
+ *   - Device pointers are plain device addresses (e.g. a torch tensor's
+ *     data_ptr()); host pointers are plain host addresses.  Every device
+ *     pointer must be 16-byte aligned (PWG_ERR_ALIGN otherwise).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  GPU
+ *     entry points are asynchronous on that stream.
+ *   - Shapes: rows >= 1; cols a multiple of 64 and at most PWG_MAX_COLS.
+ *     batch is 1, 4, 8 or 16.
+ *   - Floating-point inputs must be finite.
+ */
+#ifndef PWG_H
+#define PWG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+#pragma GCC visibility push(default)
+
+#define PWG_VERSION 1
+#define PWG_MAX_COLS 16384
+
+enum {
+  PWG_OK = 0,
+  PWG_ERR_ARG = -1,         /* null pointer, bad shape, bad batch, bad id on host */
+  PWG_ERR_ALIGN = -2,       /* a device pointer is not 16-byte aligned */
+  PWG_ERR_SIZE = -3,        /* an output buffer or workspace is too small */
+  PWG_ERR_VALUE = -4,       /* a weight outside {-1, 0, +1}; message names (row, col) */
+  PWG_ERR_HIP = -5,         /* a HIP runtime error; message has hipGetErrorString */
+  PWG_ERR_UNSUPPORTED = -6  /* valid request this build does not implement */
+};
+
+/* Step schedules for pwg_decode_step_weights. */
+enum {
+  PWG_SCHEDULE_LEVELS = 0,     /* one kernel per dependency level, in decoder order */
+  PWG_SCHEDULE_PERSISTENT = 1  /* one persistent kernel; device-wide level barriers */
+};
+
+/* ---------------------------------------------------------------------------
+ * Packed ternary format "T2" (2 bits per weight).  The pages name their own
+ * packed type but do not specify it; this is the library's format, arranged
+ * at load time as the page's loader does.
+ *   - logical W in {-1,0,+1}^(rows x cols), cols % 64 == 0;
+ *   - row-major: row r is bytes [r*cols/4, (r+1)*cols/4);
+ *   - each row is little-endian 32-bit words; word j holds weights
+ *     k = 16*j + m (m = 0..15); weight m's code is at bit
+ *     p(m) = 8*((m%8)/2) + 4*(m/8) + 2*(m%2): byte b holds weights 2b, 2b+1
+ *     in its low nibble and 8+2b, 9+2b in its high nibble;
+ *   - code = two's complement of w in 2 bits (0 -> 00, +1 -> 01, -1 -> 11);
+ *   - no header; row scales are separate float32 arrays.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of a packed T2 blob: rows*cols/4.  Returns 0 for an invalid shape
+ * (rows < 1, cols < 64, cols % 64 != 0).  Pure host function. */
+size_t pwg_packed_size(int64_t rows, int64_t cols);
+
+/* Pack a logical ternary matrix into T2 (page section "The same weights take
+ * four execution paths": the same values arranged for the device at load
+ * time).  Synchronous host code; may use several threads internally.
+ *   w_host       host, int8 row-major rows x cols, values in {-1, 0, +1}
+ *   out_host     host, at least pwg_packed_size(rows, cols) bytes
+ *   out_bytes    host, receives the bytes written (may be NULL)
+ * Errors: PWG_ERR_ARG (null / bad shape), PWG_ERR_SIZE (capacity too small),
+ * PWG_ERR_VALUE (a value outside {-1,0,1}; out_host contents unspecified). */
+int pwg_pack_weights(const int8_t* w_host, int64_t rows, int64_t cols,
+                     void* out_host, size_t out_capacity, size_t* out_bytes);
+
+/* Inverse of pwg_pack_weights (host).  PWG_ERR_VALUE on a 0b10 code. */
+int pwg_unpack_weights(const void* packed_host, int64_t rows, int64_t cols,
+                       int8_t* w_out_host);
+
+/* Ternary GEMV (page section "A 104 microsecond floor ...": each projection
+ * applied to the current activations; section "The file is not the
+ * traffic": ternary weights with row scales):
+ *     y[b, r] = row_scale[r] * sum_k W[r, k] * x[b, k]
+ *   w_packed     device, T2 blob of rows x cols
+ *   row_scale    device, float32[rows]
+ *   x            device, float32[batch][cols] row-major
+ *   y            device, float32[batch][rows] row-major (written, not accumulated)
+ * Accuracy: float32-class.  The sum is formed exactly in integers over a
+ * 22-bit fixed-point rounding of x with one exponent per vector, then scaled
+ * in float32; see the design notes for the error bound.
+ * Errors: PWG_ERR_ARG, PWG_ERR_ALIGN, PWG_ERR_HIP. */
+int pwg_ternary_gemv(const void* w_packed, const float* row_scale,
+                     int64_t rows, int64_t cols,
+                     const float* x, int32_t batch,
+                     float* y, void* stream);
+
+/* Workspace bytes needed by pwg_int8_gemv_argmax for (rows, batch). */
+size_t pwg_argmax_workspace_bytes(int64_t rows, int32_t batch);
+
+/* int8 output projection fused with greedy argmax (page sections "A 104
+ * microsecond floor ..." - the output projection scores the full vocabulary -
+ * and "The file is not the traffic" - int8 tables of 151,936 x 4,096):
+ *     logit[b, v] = row_scale[v] * sum_k table[v, k] * h[b, k]
+ *     token_out[b] = argmax_v logit[b, v], lowest v on ties
+ *   table        device, int8 rows x cols row-major (read in place)
+ *   row_scale    device, float32[rows]
+ *   h            device, float32[batch][cols]
+ *   workspace    device, >= pwg_argmax_workspace_bytes(rows, batch); scratch
+ *                (contents on entry are ignored)
+ *   token_out    device, int32[batch]
+ *   logits_out   device float32[batch][rows] or NULL (written only if given)
+ * Two kernels: a fused GEMV + per-block (max, index), then one block that
+ * reduces the pairs.  Deterministic bit for bit.
+ * Errors: PWG_ERR_ARG, PWG_ERR_ALIGN, PWG_ERR_SIZE, PWG_ERR_HIP. */
+int pwg_int8_gemv_argmax(const int8_t* table, const float* row_scale,
+                         int64_t rows, int64_t cols,
+                         const float* h, int32_t batch,
+                         void* workspace, size_t workspace_bytes,
+                         int32_t* token_out, float* logits_out,
+                         void* stream);
+
+/* Embedding-row gather (page section "The file is not the traffic": only the
+ * selected input rows are read):
+ *     rows_out[i, :] = table[ids[i], :]; scales_out[i] = row_scale[ids[i]];
+ *     deq_out[i, k] = float32(table[ids[i], k] * row_scale[ids[i]])
+ *   table        device, int8 rows x cols;  row_scale device float32[rows]
+ *   ids          device, int32[n]
+ *   rows_out     device, int8[n][cols];  scales_out device float32[n]
+ *   deq_out      device float32[n][cols] or NULL
+ * An id outside [0, rows) is not dereferenced: its output row is zero and
+ * its scale NaN.  n == 0 is a no-op.
+ * Errors: PWG_ERR_ARG, PWG_ERR_ALIGN, PWG_ERR_HIP. */
+int pwg_embed_gather(const int8_t* table, const float* row_scale,
+                     int64_t rows, int64_t cols,
+                     const int32_t* ids, int32_t n,
+                     int8_t* rows_out, float* scales_out, float* deq_out,
+                     void* stream);
+
+/* One ternary GEMV level of a decode step (matrices that share an input are
+ * stacked by rows: q|k|v and gate|up). */
+typedef struct pwg_level {
+  const void* w_packed;    /* device, T2 rows x cols */
+  const float* row_scale;  /* device, float32[rows] */
+  const float* x;          /* device, float32[cols] */
+  float* y;                /* device, float32[rows] */
+  int64_t rows;
+  int64_t cols;
+} pwg_level;
+
+/* Whole batch-1 decode step over the weights (page section "A 104
+ * microsecond floor ...", Fig. 1: one step = embedding row, every layer's
+ * projections in decoder order, the output projection and the greedy token):
+ *   embedding gather of *token_in -> levels[0 .. n_levels-1] in order ->
+ *   int8 output projection of h + argmax -> *token_out.
+ * All pointers except `levels` are device pointers; `levels` is a host array
+ * read during the call (for the persistent schedule it is read by
+ * pwg_step_plan instead).  token_in and token_out may alias (the token then
+ * feeds the next step on the device). */
+typedef struct pwg_step_desc {
+  int32_t n_levels;
+  int32_t schedule;              /* PWG_SCHEDULE_* */
+  const pwg_level* levels;       /* host array [n_levels] */
+  const int8_t* out_table;       /* int8 vocab x hidden */
+  const float* out_scale;        /* float32[vocab] */
+  const float* h;                /* float32[hidden] */
+  int64_t vocab;
+  int64_t hidden;
+  const int8_t* emb_table;       /* int8 vocab x hidden */
+  const float* emb_scale;        /* float32[vocab] */
+  const int32_t* token_in;       /* int32[1] */
+  int32_t* token_out;            /* int32[1] */
+  int8_t* emb_row_out;           /* int8[hidden] */
+  float* emb_scale_out;          /* float32[1] */
+  float* emb_deq_out;            /* float32[hidden] or NULL */
+  float* logits_out;             /* float32[vocab] or NULL */
+  void* workspace;               /* >= pwg_step_workspace_bytes(desc) */
+  size_t workspace_bytes;
+} pwg_step_desc;
+
+/* Workspace bytes for a step description (depends on shapes and schedule). */
+size_t pwg_step_workspace_bytes(const pwg_step_desc* desc);
+
+/* Prepare the workspace of a step: validates the description and, for the
+ * persistent schedule, writes the device-side level table and resets the
+ * barrier words.  Synchronous (it waits for its own copies); call it once per
+ * set of buffers, outside stream capture, before pwg_decode_step_weights. */
+int pwg_step_plan(const pwg_step_desc* desc, void* stream);
+
+/* Enqueue one step on `stream` (capturable; no allocation, no sync). */
+int pwg_decode_step_weights(const pwg_step_desc* desc, void* stream);
+
+/* Thread-local message of the last failed call on this thread ("" if none). */
+const char* pwg_last_error(void);
+
+/* PWG_VERSION of the built library. */
+int pwg_version(void);
+
+#pragma GCC visibility pop
+#ifdef __cplusplus
+}
+#endif
+#endif /* PWG_H */

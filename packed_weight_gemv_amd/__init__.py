@@ -1,0 +1,247 @@
+"""Python binding of libpwg (packed ternary weight-streaming decode on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libpwg.so.  PyTorch supplies device memory and streams.  The names
+match the C ABI in include/pwg.h without the ``pwg_`` prefix.
+
+The library must be built first (``python packed_weight_gemv_amd/build.py``
+or ``__graft_entry__.build()``); importing this package raises if it is
+missing, and there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "PwgError", "lib", "packed_size", "pack_weights", "unpack_weights", "ternary_gemv",
+    "argmax_workspace_bytes", "int8_gemv_argmax", "embed_gather", "Level", "StepDesc",
+    "step_workspace_bytes", "step_plan", "decode_step_weights", "last_error", "version",
+    "SCHEDULE_LEVELS", "SCHEDULE_PERSISTENT", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpwg.so")
+
+PWG_OK = 0
+ERR_NAMES = {-1: "PWG_ERR_ARG", -2: "PWG_ERR_ALIGN", -3: "PWG_ERR_SIZE", -4: "PWG_ERR_VALUE",
+             -5: "PWG_ERR_HIP", -6: "PWG_ERR_UNSUPPORTED"}
+SCHEDULE_LEVELS = 0
+SCHEDULE_PERSISTENT = 1
+
+
+class PwgError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERR_NAMES.get(code, code)}: {message}")
+        self.code = code
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libpwg.so is not built ({LIB_PATH}); run `python packed_weight_gemv_amd/build.py`")
+
+# PyTorch ships its own HIP runtime (same soname as the system one).  Loading
+# torch first makes libpwg bind to that runtime instead of pulling in a
+# second copy, so tensors, streams and kernels share one runtime.
+try:
+    import torch  # noqa: F401
+except ImportError:  # host-only use (packer, argument checks)
+    pass
+
+lib = C.CDLL(LIB_PATH)
+
+_i64, _i32, _sz, _vp = C.c_int64, C.c_int32, C.c_size_t, C.c_void_p
+
+
+class Level(C.Structure):
+    _fields_ = [("w_packed", _vp), ("row_scale", _vp), ("x", _vp), ("y", _vp), ("rows", _i64), ("cols", _i64)]
+
+
+class _StepDesc(C.Structure):
+    _fields_ = [
+        ("n_levels", _i32), ("schedule", _i32), ("levels", C.POINTER(Level)),
+        ("out_table", _vp), ("out_scale", _vp), ("h", _vp), ("vocab", _i64), ("hidden", _i64),
+        ("emb_table", _vp), ("emb_scale", _vp), ("token_in", _vp), ("token_out", _vp),
+        ("emb_row_out", _vp), ("emb_scale_out", _vp), ("emb_deq_out", _vp), ("logits_out", _vp),
+        ("workspace", _vp), ("workspace_bytes", _sz),
+    ]
+
+
+def _sig(name, restype, *argtypes):
+    f = getattr(lib, name)
+    f.restype = restype
+    f.argtypes = list(argtypes)
+    return f
+
+
+_packed_size = _sig("pwg_packed_size", _sz, _i64, _i64)
+_pack = _sig("pwg_pack_weights", C.c_int, _vp, _i64, _i64, _vp, _sz, C.POINTER(_sz))
+_unpack = _sig("pwg_unpack_weights", C.c_int, _vp, _i64, _i64, _vp)
+_tgemv = _sig("pwg_ternary_gemv", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp)
+_argmax_ws = _sig("pwg_argmax_workspace_bytes", _sz, _i64, _i32)
+_i8argmax = _sig("pwg_int8_gemv_argmax", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _sz, _vp, _vp, _vp)
+_gather = _sig("pwg_embed_gather", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _vp)
+_step_ws = _sig("pwg_step_workspace_bytes", _sz, C.POINTER(_StepDesc))
+_step_plan = _sig("pwg_step_plan", C.c_int, C.POINTER(_StepDesc), _vp)
+_step = _sig("pwg_decode_step_weights", C.c_int, C.POINTER(_StepDesc), _vp)
+_last_error = _sig("pwg_last_error", C.c_char_p)
+_version = _sig("pwg_version", C.c_int)
+
+EXPORTED = ["pwg_packed_size", "pwg_pack_weights", "pwg_unpack_weights", "pwg_ternary_gemv",
+            "pwg_argmax_workspace_bytes", "pwg_int8_gemv_argmax", "pwg_embed_gather",
+            "pwg_step_workspace_bytes", "pwg_step_plan", "pwg_decode_step_weights",
+            "pwg_last_error", "pwg_version"]
+
+
+def last_error() -> str:
+    return _last_error().decode()
+
+
+def version() -> int:
+    return _version()
+
+
+def _check(rc: int):
+    if rc != PWG_OK:
+        raise PwgError(rc, last_error())
+
+
+def _ptr(t) -> int | None:
+    """Device or host address of a torch tensor (None stays None)."""
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------- host packer
+def packed_size(rows: int, cols: int) -> int:
+    return _packed_size(rows, cols)
+
+
+def pack_weights(w: np.ndarray) -> np.ndarray:
+    """Pack an int8 (rows, cols) ternary matrix into a uint8 T2 blob (host)."""
+    w = np.ascontiguousarray(w, dtype=np.int8)
+    if w.ndim != 2:
+        raise ValueError("w must be 2-D")
+    rows, cols = w.shape
+    n = _packed_size(rows, cols)
+    out = np.empty(max(n, 1), dtype=np.uint8)
+    written = _sz(0)
+    _check(_pack(w.ctypes.data, rows, cols, out.ctypes.data, out.nbytes if n else 0, C.byref(written)))
+    return out[:written.value]
+
+
+def unpack_weights(blob: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    out = np.empty((rows, cols), dtype=np.int8)
+    if blob.size < _packed_size(rows, cols):
+        raise ValueError("blob too small")
+    _check(_unpack(blob.ctypes.data, rows, cols, out.ctypes.data))
+    return out
+
+
+# ---------------------------------------------------------------- GPU entry points
+def ternary_gemv(w_packed, row_scale, rows: int, cols: int, x, y=None, stream=None):
+    """y = row_scale * (W @ x) for x of shape (cols,) or (batch, cols)."""
+    import torch
+    batch = 1 if x.dim() == 1 else x.shape[0]
+    if y is None:
+        y = torch.empty((rows,) if x.dim() == 1 else (batch, rows), dtype=torch.float32, device=x.device)
+    _check(_tgemv(_ptr(w_packed), _ptr(row_scale), rows, cols, _ptr(x), batch, _ptr(y), _stream(stream)))
+    return y
+
+
+def argmax_workspace_bytes(rows: int, batch: int = 1) -> int:
+    return _argmax_ws(rows, batch)
+
+
+def int8_gemv_argmax(table, row_scale, h, workspace=None, token_out=None, logits_out=None, stream=None):
+    """Greedy token(s) of logits = row_scale * (table @ h); h is (cols,) or (batch, cols)."""
+    import torch
+    rows, cols = table.shape
+    batch = 1 if h.dim() == 1 else h.shape[0]
+    if workspace is None:
+        workspace = torch.empty(max(1, _argmax_ws(rows, batch)), dtype=torch.uint8, device=h.device)
+    if token_out is None:
+        token_out = torch.empty(batch, dtype=torch.int32, device=h.device)
+    _check(_i8argmax(_ptr(table), _ptr(row_scale), rows, cols, _ptr(h), batch, _ptr(workspace),
+                     workspace.numel() * workspace.element_size(), _ptr(token_out), _ptr(logits_out),
+                     _stream(stream)))
+    return token_out
+
+
+def embed_gather(table, row_scale, ids, rows_out=None, scales_out=None, deq_out=None, dequant=True, stream=None):
+    """Rows table[ids], their scales and (optionally) float32 dequantised rows."""
+    import torch
+    rows, cols = table.shape
+    n = ids.numel()
+    dev = ids.device
+    if rows_out is None:
+        rows_out = torch.empty((n, cols), dtype=torch.int8, device=dev)
+    if scales_out is None:
+        scales_out = torch.empty(max(n, 1), dtype=torch.float32, device=dev)
+    if dequant and deq_out is None:
+        deq_out = torch.empty((n, cols), dtype=torch.float32, device=dev)
+    _check(_gather(_ptr(table), _ptr(row_scale), rows, cols, _ptr(ids), n, _ptr(rows_out), _ptr(scales_out),
+                   _ptr(deq_out) if dequant else None, _stream(stream)))
+    return rows_out, scales_out[:n], (deq_out if dequant else None)
+
+
+# ---------------------------------------------------------------- decode step
+@dataclass
+class StepDesc:
+    """Python-side description of a decode step; keeps every tensor alive."""
+    levels: list            # [(w_packed, row_scale, x, y, rows, cols)]
+    out_table: object
+    out_scale: object
+    h: object
+    emb_table: object
+    emb_scale: object
+    token_in: object
+    token_out: object
+    emb_row_out: object
+    emb_scale_out: object
+    emb_deq_out: object = None
+    logits_out: object = None
+    workspace: object = None
+    schedule: int = SCHEDULE_LEVELS
+    _c: object = field(default=None, repr=False)
+    _levels_c: object = field(default=None, repr=False)
+
+    def c(self):
+        if self._c is None:
+            arr = (Level * max(1, len(self.levels)))()
+            for i, (w, s, x, y, r, k) in enumerate(self.levels):
+                arr[i] = Level(_ptr(w), _ptr(s), _ptr(x), _ptr(y), r, k)
+            self._levels_c = arr
+            vocab, hidden = self.out_table.shape
+            ws = self.workspace
+            self._c = _StepDesc(
+                len(self.levels), self.schedule, C.cast(arr, C.POINTER(Level)),
+                _ptr(self.out_table), _ptr(self.out_scale), _ptr(self.h), vocab, hidden,
+                _ptr(self.emb_table), _ptr(self.emb_scale), _ptr(self.token_in), _ptr(self.token_out),
+                _ptr(self.emb_row_out), _ptr(self.emb_scale_out), _ptr(self.emb_deq_out), _ptr(self.logits_out),
+                _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size())
+        return self._c
+
+
+def step_workspace_bytes(desc: StepDesc) -> int:
+    return _step_ws(C.byref(desc.c()))
+
+
+def step_plan(desc: StepDesc, stream=None):
+    _check(_step_plan(C.byref(desc.c()), _stream(stream)))
+
+
+def decode_step_weights(desc: StepDesc, stream=None):
+    _check(_step(C.byref(desc.c()), _stream(stream)))

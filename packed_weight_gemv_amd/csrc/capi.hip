@@ -1,0 +1,164 @@
+// C entry points: argument validation, then the launchers.  Nothing here
+// allocates or synchronises except pwg_step_plan (documented as such).
+#include <hip/hip_runtime.h>
+
+#include "pwg_internal.h"
+
+using namespace pwg;
+
+namespace {
+
+int check_ptr(const void* p, const char* fn, const char* name) {
+  if (p == nullptr) return fail(PWG_ERR_ARG, "%s: %s is null", fn, name);
+  if (!aligned16(p)) return fail(PWG_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, name);
+  return PWG_OK;
+}
+
+int check_shape(int64_t rows, int64_t cols, const char* fn) {
+  if (rows < 1 || rows > (int64_t{1} << 30))
+    return fail(PWG_ERR_ARG, "%s: rows must be in [1, 2^30] (got %lld)", fn, (long long)rows);
+  if (!valid_cols(cols))
+    return fail(PWG_ERR_ARG, "%s: cols must be a multiple of 64 in [64, %d] (got %lld)", fn, PWG_MAX_COLS,
+                (long long)cols);
+  return PWG_OK;
+}
+
+#define TRY(expr)                 \
+  do {                            \
+    const int _rc = (expr);       \
+    if (_rc != PWG_OK) return _rc; \
+  } while (0)
+
+int validate_ternary(const void* w, const float* s, int64_t rows, int64_t cols, const float* x, int32_t batch,
+                     const float* y, const char* fn) {
+  TRY(check_shape(rows, cols, fn));
+  if (!valid_batch(batch)) return fail(PWG_ERR_ARG, "%s: batch must be 1, 4, 8 or 16 (got %d)", fn, batch);
+  TRY(check_ptr(w, fn, "w_packed"));
+  TRY(check_ptr(s, fn, "row_scale"));
+  TRY(check_ptr(x, fn, "x"));
+  TRY(check_ptr(y, fn, "y"));
+  return PWG_OK;
+}
+
+int validate_int8(const int8_t* t, const float* s, int64_t rows, int64_t cols, const char* fn) {
+  TRY(check_shape(rows, cols, fn));
+  if (cols > kMaxInt8Cols)
+    return fail(PWG_ERR_UNSUPPORTED, "%s: int8 tables wider than %lld columns are not supported", fn,
+                (long long)kMaxInt8Cols);
+  if (rows >= (int64_t{1} << 31) - 1) return fail(PWG_ERR_ARG, "%s: too many rows", fn);
+  TRY(check_ptr(t, fn, "table"));
+  TRY(check_ptr(s, fn, "row_scale"));
+  return PWG_OK;
+}
+
+size_t argmax_ws(int64_t rows, int32_t batch) { return int8_partials(rows) * sizeof(unsigned long long) * batch; }
+
+}  // namespace
+
+extern "C" int pwg_ternary_gemv(const void* w_packed, const float* row_scale, int64_t rows, int64_t cols,
+                                const float* x, int32_t batch, float* y, void* stream) {
+  TRY(validate_ternary(w_packed, row_scale, rows, cols, x, batch, y, "pwg_ternary_gemv"));
+  return launch_ternary_gemv(w_packed, row_scale, rows, cols, x, batch, y, stream);
+}
+
+extern "C" size_t pwg_argmax_workspace_bytes(int64_t rows, int32_t batch) {
+  if (rows < 1 || !valid_batch(batch)) return 0;
+  return argmax_ws(rows, batch);
+}
+
+extern "C" int pwg_int8_gemv_argmax(const int8_t* table, const float* row_scale, int64_t rows, int64_t cols,
+                                    const float* h, int32_t batch, void* workspace, size_t workspace_bytes,
+                                    int32_t* token_out, float* logits_out, void* stream) {
+  const char* fn = "pwg_int8_gemv_argmax";
+  TRY(validate_int8(table, row_scale, rows, cols, fn));
+  if (!valid_batch(batch)) return fail(PWG_ERR_ARG, "%s: batch must be 1, 4, 8 or 16 (got %d)", fn, batch);
+  TRY(check_ptr(h, fn, "h"));
+  TRY(check_ptr(workspace, fn, "workspace"));
+  TRY(check_ptr(token_out, fn, "token_out"));
+  if (logits_out && !aligned16(logits_out)) return fail(PWG_ERR_ALIGN, "%s: logits_out is not 16-byte aligned", fn);
+  if (workspace_bytes < argmax_ws(rows, batch))
+    return fail(PWG_ERR_SIZE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, argmax_ws(rows, batch));
+  return launch_int8_gemv_argmax(table, row_scale, rows, cols, h, batch, workspace, token_out, logits_out, stream);
+}
+
+extern "C" int pwg_embed_gather(const int8_t* table, const float* row_scale, int64_t rows, int64_t cols,
+                                const int32_t* ids, int32_t n, int8_t* rows_out, float* scales_out, float* deq_out,
+                                void* stream) {
+  const char* fn = "pwg_embed_gather";
+  TRY(check_shape(rows, cols, fn));
+  if (rows >= (int64_t{1} << 31) - 1) return fail(PWG_ERR_ARG, "%s: too many rows", fn);
+  if (n < 0 || n > (1 << 24)) return fail(PWG_ERR_ARG, "%s: n must be in [0, 2^24] (got %d)", fn, n);
+  if (n == 0) return PWG_OK;
+  TRY(check_ptr(table, fn, "table"));
+  TRY(check_ptr(row_scale, fn, "row_scale"));
+  TRY(check_ptr(ids, fn, "ids"));
+  TRY(check_ptr(rows_out, fn, "rows_out"));
+  TRY(check_ptr(scales_out, fn, "scales_out"));
+  if (deq_out && !aligned16(deq_out)) return fail(PWG_ERR_ALIGN, "%s: deq_out is not 16-byte aligned", fn);
+  return launch_embed_gather(table, row_scale, rows, cols, ids, n, rows_out, scales_out, deq_out, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Decode step
+// ---------------------------------------------------------------------------
+namespace {
+
+int validate_step(const pwg_step_desc* d) {
+  const char* fn = "pwg_decode_step_weights";
+  if (!d) return fail(PWG_ERR_ARG, "%s: desc is null", fn);
+  if (d->schedule != PWG_SCHEDULE_LEVELS && d->schedule != PWG_SCHEDULE_PERSISTENT)
+    return fail(PWG_ERR_ARG, "%s: unknown schedule %d", fn, d->schedule);
+  if (d->n_levels < 0 || d->n_levels > 4096) return fail(PWG_ERR_ARG, "%s: n_levels out of range", fn);
+  if (d->n_levels > 0 && !d->levels) return fail(PWG_ERR_ARG, "%s: levels is null", fn);
+  for (int i = 0; i < d->n_levels; ++i) {
+    const pwg_level& L = d->levels[i];
+    const int rc = validate_ternary(L.w_packed, L.row_scale, L.rows, L.cols, L.x, 1, L.y, fn);
+    if (rc != PWG_OK) return fail(rc, "%s (level %d)", pwg_last_error(), i);
+  }
+  TRY(validate_int8(d->out_table, d->out_scale, d->vocab, d->hidden, fn));
+  TRY(check_ptr(d->h, fn, "h"));
+  TRY(check_ptr(d->emb_table, fn, "emb_table"));
+  TRY(check_ptr(d->emb_scale, fn, "emb_scale"));
+  TRY(check_ptr(d->token_in, fn, "token_in"));
+  TRY(check_ptr(d->token_out, fn, "token_out"));
+  TRY(check_ptr(d->emb_row_out, fn, "emb_row_out"));
+  TRY(check_ptr(d->emb_scale_out, fn, "emb_scale_out"));
+  if (d->emb_deq_out && !aligned16(d->emb_deq_out)) return fail(PWG_ERR_ALIGN, "%s: emb_deq_out misaligned", fn);
+  if (d->logits_out && !aligned16(d->logits_out)) return fail(PWG_ERR_ALIGN, "%s: logits_out misaligned", fn);
+  TRY(check_ptr(d->workspace, fn, "workspace"));
+  return PWG_OK;
+}
+
+}  // namespace
+
+extern "C" size_t pwg_step_workspace_bytes(const pwg_step_desc* d) {
+  if (!d || d->vocab < 1) return 0;
+  return argmax_ws(d->vocab, 1) + step_persistent_workspace(d);
+}
+
+extern "C" int pwg_step_plan(const pwg_step_desc* d, void* stream) {
+  TRY(validate_step(d));
+  if (d->workspace_bytes < pwg_step_workspace_bytes(d))
+    return fail(PWG_ERR_SIZE, "pwg_step_plan: workspace %zu < %zu bytes", d->workspace_bytes,
+                pwg_step_workspace_bytes(d));
+  if (d->schedule == PWG_SCHEDULE_PERSISTENT) return step_persistent_plan(d, argmax_ws(d->vocab, 1), stream);
+  return PWG_OK;
+}
+
+extern "C" int pwg_decode_step_weights(const pwg_step_desc* d, void* stream) {
+  TRY(validate_step(d));
+  if (d->workspace_bytes < pwg_step_workspace_bytes(d))
+    return fail(PWG_ERR_SIZE, "pwg_decode_step_weights: workspace %zu < %zu bytes", d->workspace_bytes,
+                pwg_step_workspace_bytes(d));
+  if (d->schedule == PWG_SCHEDULE_PERSISTENT) return step_persistent_launch(d, argmax_ws(d->vocab, 1), stream);
+  // Levels schedule: embedding row, every level in decoder order, output
+  // projection + argmax, all on one stream.
+  TRY(launch_embed_gather(d->emb_table, d->emb_scale, d->vocab, d->hidden, d->token_in, 1, d->emb_row_out,
+                          d->emb_scale_out, d->emb_deq_out, stream));
+  for (int i = 0; i < d->n_levels; ++i) {
+    const pwg_level& L = d->levels[i];
+    TRY(launch_ternary_gemv(L.w_packed, L.row_scale, L.rows, L.cols, L.x, 1, L.y, stream));
+  }
+  return launch_int8_gemv_argmax(d->out_table, d->out_scale, d->vocab, d->hidden, d->h, 1, d->workspace,
+                                 d->token_out, d->logits_out, stream);
+}

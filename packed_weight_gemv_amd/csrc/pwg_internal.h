@@ -1,0 +1,41 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+#include <cstdint>
+#include <cstddef>
+
+#include "../../include/pwg.h"
+
+namespace pwg {
+
+// Records a formatted message for pwg_last_error() on this thread and
+// returns `code`, so call sites can write `return fail(PWG_ERR_ARG, ...)`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool valid_batch(int32_t b) { return b == 1 || b == 4 || b == 8 || b == 16; }
+inline bool valid_cols(int64_t cols) { return cols >= 64 && cols % 64 == 0 && cols <= PWG_MAX_COLS; }
+// The int8 kernels keep 48 dwords of activation limbs per 4,096 columns in
+// VGPRs; beyond 8,192 columns they would spill.
+constexpr int64_t kMaxInt8Cols = 8192;
+
+// Launchers (asynchronous, arguments already validated).
+int launch_ternary_gemv(const void* w, const float* s, int64_t rows, int64_t cols,
+                        const float* x, int32_t batch, float* y, void* stream);
+int launch_int8_gemv_argmax(const int8_t* table, const float* s, int64_t rows, int64_t cols,
+                            const float* h, int32_t batch, void* ws, int32_t* token,
+                            float* logits, void* stream);
+size_t int8_partials(int64_t rows);
+size_t t2_lds_bytes(int64_t cols);
+size_t i8_lds_bytes(int64_t cols);
+int launch_embed_gather(const int8_t* table, const float* s, int64_t rows, int64_t cols,
+                        const int32_t* ids, int32_t n, int8_t* rows_out, float* scales_out,
+                        float* deq_out, void* stream);
+
+// Persistent (single-kernel) step schedule.  `ws_offset` is where its part of
+// the step workspace starts (the argmax partials come first).
+size_t step_persistent_workspace(const pwg_step_desc* d);
+int step_persistent_plan(const pwg_step_desc* d, size_t ws_offset, void* stream);
+int step_persistent_launch(const pwg_step_desc* d, size_t ws_offset, void* stream);
+
+}  // namespace pwg

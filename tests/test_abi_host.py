@@ -1,0 +1,159 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+symbol include/pwg.h declares, packs T2 bit-exactly as the oracle's
+independent encoder does, and rejects bad arguments with the documented codes
+before anything reaches the GPU."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import packed_format as pf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+pwg = pytest.importorskip("packed_weight_gemv_amd")
+
+ERR_ARG, ERR_ALIGN, ERR_SIZE, ERR_VALUE, ERR_UNSUPPORTED = -1, -2, -3, -4, -6
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "pwg.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pwg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    declared = header_functions()
+    assert len(declared) >= 12
+    for name in declared:
+        assert hasattr(pwg.lib, name), name
+    assert sorted(pwg.EXPORTED) == declared
+
+
+def test_version_and_error_string():
+    assert pwg.version() == 1
+    assert isinstance(pwg.last_error(), str)
+
+
+def test_packed_size():
+    assert pwg.packed_size(4096, 4096) == 4096 * 4096 // 4
+    assert pwg.packed_size(1, 64) == 16
+    for bad in ((0, 64), (1, 0), (1, 100), (-1, 64)):
+        assert pwg.packed_size(*bad) == 0
+
+
+@pytest.mark.parametrize("shape", [(1, 64), (3, 128), (37, 1024), (5, 4160), (2048, 4096)])
+def test_pack_matches_oracle_encoder_bit_for_bit(shape):
+    rng = np.random.default_rng(shape[0] * 7 + shape[1])
+    w = rng.integers(-1, 2, size=shape, dtype=np.int8)
+    blob = pwg.pack_weights(w)
+    assert blob.size == pf.packed_nbytes(*shape)
+    assert np.array_equal(blob, pf.encode(w))
+    assert np.array_equal(pf.decode(blob, *shape), w)
+    assert np.array_equal(pwg.unpack_weights(blob, *shape), w)
+
+
+def test_pack_large_multithreaded_matches_oracle():
+    rng = np.random.default_rng(5)
+    w = rng.integers(-1, 2, size=(1536, 4096), dtype=np.int8)   # above the threading threshold
+    assert np.array_equal(pwg.pack_weights(w), pf.encode(w))
+
+
+def test_pack_hand_fixture(golden_dir):
+    import json
+    case = json.load(open(os.path.join(golden_dir, "t2_bytes.json")))["cases"][0]
+    w = np.zeros((case["rows"], case["cols"]), np.int8)
+    for k, v in case["nonzero"].items():
+        w[0, int(k)] = v
+    assert pwg.pack_weights(w).tobytes() == bytes.fromhex(case["bytes_hex"])
+
+
+def test_pack_rejects_values_outside_ternary_and_names_the_first():
+    w = np.zeros((4, 128), np.int8)
+    w[2, 77] = 2
+    w[3, 5] = -2
+    with pytest.raises(pwg.PwgError) as e:
+        pwg.pack_weights(w)
+    assert e.value.code == ERR_VALUE
+    assert "row 2" in str(e.value) and "col 77" in str(e.value)
+
+
+def test_pack_argument_errors():
+    w = np.zeros((2, 64), np.int8)
+    out = np.zeros(32, np.uint8)
+    n = C.c_size_t(0)
+    assert pwg._pack(None, 2, 64, out.ctypes.data, 32, C.byref(n)) == ERR_ARG
+    assert pwg._pack(w.ctypes.data, 2, 64, None, 32, C.byref(n)) == ERR_ARG
+    assert pwg._pack(w.ctypes.data, 2, 60, out.ctypes.data, 32, C.byref(n)) == ERR_ARG
+    assert pwg._pack(w.ctypes.data, 0, 64, out.ctypes.data, 32, C.byref(n)) == ERR_ARG
+    assert pwg._pack(w.ctypes.data, 2, 64, out.ctypes.data, 31, C.byref(n)) == ERR_SIZE
+    assert pwg._pack(w.ctypes.data, 2, 64, out.ctypes.data, 32, C.byref(n)) == 0 and n.value == 32
+
+
+def test_unpack_rejects_invalid_code():
+    blob = np.zeros(16, np.uint8)
+    blob[9] = 0b10 << 4   # word 2, byte 1, high nibble, low pair: weight 32 + 10
+    with pytest.raises(pwg.PwgError) as e:
+        pwg.unpack_weights(blob, 1, 64)
+    assert e.value.code == ERR_VALUE and "col 42" in str(e.value)
+
+
+# Fake, never-dereferenced device addresses: validation must reject the call
+# before any HIP work is enqueued.
+A = 1 << 20          # 16-byte aligned
+MIS = A + 4          # misaligned
+
+
+def test_ternary_gemv_argument_errors():
+    f = pwg._tgemv
+    assert f(None, A, 8, 64, A, 1, A, None) == ERR_ARG
+    assert f(A, A, 0, 64, A, 1, A, None) == ERR_ARG
+    assert f(A, A, 8, 96, A, 1, A, None) == ERR_ARG
+    assert f(A, A, 8, 16448, A, 1, A, None) == ERR_ARG          # above the column limit
+    assert f(A, A, 8, 64, A, 3, A, None) == ERR_ARG             # batch not in {1,4,8,16}
+    assert f(A, A, 8, 64, MIS, 1, A, None) == ERR_ALIGN
+    assert f(A, A, 8, 64, A, 1, None, None) == ERR_ARG
+    assert f(A, A, 8, 64, A, 2, A, None) == ERR_ARG and "batch" in pwg.last_error()
+
+
+def test_int8_argmax_argument_errors():
+    f = pwg._i8argmax
+    ws = pwg.argmax_workspace_bytes(1000, 1)
+    assert ws >= 8 and pwg.argmax_workspace_bytes(1000, 4) == 4 * ws
+    assert pwg.argmax_workspace_bytes(0, 1) == 0 and pwg.argmax_workspace_bytes(10, 3) == 0
+    assert f(A, A, 1000, 4096, A, 1, A, ws - 8, A, None, None) == ERR_SIZE
+    assert f(A, A, 1000, 4096, A, 1, None, ws, A, None, None) == ERR_ARG
+    assert f(A, A, 1000, 4096, A, 1, A, ws, A, MIS, None) == ERR_ALIGN
+    assert f(A, A, 1000, 12288, A, 1, A, ws, A, None, None) == ERR_UNSUPPORTED
+    assert f(A, A, 1000, 4096, A, 5, A, ws, A, None, None) == ERR_ARG
+
+
+def test_embed_gather_argument_errors():
+    f = pwg._gather
+    assert f(A, A, 100, 4096, A, 0, A, A, None, None) == 0           # n == 0 is a no-op
+    assert f(A, A, 100, 4096, A, -1, A, A, None, None) == ERR_ARG
+    assert f(None, A, 100, 4096, A, 4, A, A, None, None) == ERR_ARG
+    assert f(A, A, 100, 4096, A, 4, A, A, MIS, None) == ERR_ALIGN
+
+
+def test_step_argument_errors():
+    assert pwg._step(None, None) == ERR_ARG
+    d = pwg._StepDesc()
+    d.n_levels = 0
+    d.schedule = 7
+    assert pwg._step(C.byref(d), None) == ERR_ARG and "schedule" in pwg.last_error()
+    d.schedule = pwg.SCHEDULE_LEVELS
+    d.vocab, d.hidden = 1000, 4096
+    for name in ("out_table", "out_scale", "h", "emb_table", "emb_scale", "token_in", "token_out",
+                 "emb_row_out", "emb_scale_out", "workspace"):
+        setattr(d, name, A)
+    d.workspace_bytes = 0
+    assert pwg._step(C.byref(d), None) == ERR_SIZE
+    d.workspace_bytes = pwg._step_ws(C.byref(d))
+    d.h = MIS
+    assert pwg._step(C.byref(d), None) == ERR_ALIGN
+    d.h = A
+    lv = (pwg.Level * 1)(pwg.Level(A, A, A, A, 8, 100))
+    d.n_levels, d.levels = 1, C.cast(lv, C.POINTER(pwg.Level))
+    assert pwg._step(C.byref(d), None) == ERR_ARG and "level 0" in pwg.last_error()

@@ -1,0 +1,198 @@
+"""GPU parity of the HIP path against the float64 oracle, through the C ABI.
+
+Every input comes from the seeded generators in synth/; expected values come
+from oracle/ only.  Criteria: tests/parity.py."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import reference as ref
+from tests.parity import assert_gemv, gemv_report, token_ok
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import packed_weight_gemv_amd as pwg  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def packed_on_gpu(w):
+    return dev(pwg.pack_weights(w))
+
+
+def run_ternary(w, s, x):
+    rows, cols = w.shape
+    y = pwg.ternary_gemv(packed_on_gpu(w), dev(s), rows, cols, dev(x))
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+# ------------------------------------------------------------------ ternary GEMV
+def test_single_gemv_1024_seed0():
+    w, s, x = synth.single_gemv()
+    y = run_ternary(w, s, x)
+    assert_gemv(y, ref.ternary_gemv(w, s, x), ref.ternary_gemv_magnitude(w, s, x), "1024x1024")
+
+
+SHAPES = [(1, 64), (3, 128), (5, 192), (7, 320), (2, 448), (37, 1024), (64, 2048), (1000, 4096),
+          (257, 4160), (65, 12288), (33, 16384), (1, 8192), (6144, 4096), (4096, 12288), (24576, 4096)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{r}x{c}" for r, c in SHAPES])
+def test_ternary_shapes(shape):
+    rows, cols = shape
+    m = synth.ternary_matrix((90, rows, cols), rows, cols)
+    x = synth.normal_f32(synth.rng_for(91, rows, cols), cols)
+    y = run_ternary(m.w, m.scale, x)
+    assert_gemv(y, ref.ternary_gemv(m.w, m.scale, x), ref.ternary_gemv_magnitude(m.w, m.scale, x), str(shape))
+
+
+def test_ternary_zero_input_gives_exact_zero():
+    m = synth.ternary_matrix((92, 0), 300, 4096)
+    y = run_ternary(m.w, m.scale, np.zeros(4096, np.float32))
+    assert not y.any()
+
+
+@pytest.mark.parametrize("kind", ["outlier", "tiny", "huge", "mixed_scales"])
+def test_ternary_activation_ranges(kind):
+    rows, cols = 513, 4096
+    m = synth.ternary_matrix((93, 0), rows, cols)
+    x = synth.normal_f32(synth.rng_for(94, 0), cols).astype(np.float64)
+    if kind == "outlier":
+        x[1234] = 3000.0
+    elif kind == "tiny":
+        x *= 1e-30
+    elif kind == "huge":
+        x *= 1e30
+    else:   # a different magnitude in every 64-element chunk
+        x *= 10.0 ** np.repeat(np.arange(-8, 8), 256)
+    x = x.astype(np.float32)
+    y = run_ternary(m.w, m.scale, x)
+    yr, mag = ref.ternary_gemv(m.w, m.scale, x), ref.ternary_gemv_magnitude(m.w, m.scale, x)
+    if kind != "outlier":
+        assert_gemv(y, yr, mag, kind)
+        return
+    # One element 3000x the others: its 64-element chunk is quantised relative
+    # to 3000, so that chunk's terms carry up to 2^-23 * 3000 each.  The
+    # aggregate bound still holds; each element must meet the kernel's own
+    # error model (2^-22 of the chunk maximum per nonzero term, twice the
+    # rounding half-ulp, plus the float32 magnitude floor).
+    rep = gemv_report(y, yr, mag)
+    assert rep["rel_l2"] <= 1e-5, rep
+    chunk_max = np.abs(x.astype(np.float64)).reshape(-1, 64).max(axis=1)
+    bound = np.abs(m.scale.astype(np.float64)) * (np.abs(m.w).reshape(rows, -1, 64).sum(axis=2) @ chunk_max) * 2.0 ** -22
+    assert (np.abs(y - yr) <= bound + 1e-6 * mag).all()
+
+
+def test_ternary_extreme_weights():
+    cols = 4096
+    w = np.stack([np.ones(cols, np.int8), -np.ones(cols, np.int8), np.zeros(cols, np.int8),
+                  np.tile(np.array([1, -1], np.int8), cols // 2)])
+    s = np.array([0.5, 0.25, 1.0, 0.125], np.float32)
+    x = synth.normal_f32(synth.rng_for(95, 0), cols)
+    y = run_ternary(w, s, x)
+    assert y[2] == 0.0
+    assert_gemv(y, ref.ternary_gemv(w, s, x), ref.ternary_gemv_magnitude(w, s, x), "extreme")
+
+
+@pytest.mark.parametrize("batch", [4, 8, 16])
+def test_ternary_batch(batch):
+    rows, cols = 1536, 4096
+    m = synth.ternary_matrix((96, batch), rows, cols)
+    xb = synth.batch_inputs(batch, cols, 0)
+    y = run_ternary(m.w, m.scale, xb)
+    assert y.shape == (batch, rows)
+    yr = ref.ternary_gemv(m.w, m.scale, xb)
+    for b in range(batch):
+        assert_gemv(y[b], yr[b], ref.ternary_gemv_magnitude(m.w, m.scale, xb[b]), f"batch row {b}")
+
+
+def test_ternary_is_deterministic():
+    m = synth.ternary_matrix((97, 0), 24576, 4096)
+    x = synth.normal_f32(synth.rng_for(97, 1), 4096)
+    wp, sp, xp = packed_on_gpu(m.w), dev(m.scale), dev(x)
+    outs = [pwg.ternary_gemv(wp, sp, 24576, 4096, xp).cpu().numpy() for _ in range(3)]
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+# ------------------------------------------------------------ int8 projection
+def run_argmax(q, t, h, logits=True):
+    qd, td, hd = dev(q), dev(t), dev(h)
+    lo = torch.empty((h.shape[0], q.shape[0]) if h.ndim == 2 else q.shape[0], dtype=torch.float32, device=DEV) if logits else None
+    tok = pwg.int8_gemv_argmax(qd, td, hd, logits_out=lo)
+    torch.cuda.synchronize()
+    return tok.cpu().numpy(), (lo.cpu().numpy() if logits else None)
+
+
+I8_SHAPES = [(1, 64), (100, 128), (999, 1024), (5000, 4096), (3, 8192)]
+
+
+@pytest.mark.parametrize("shape", I8_SHAPES, ids=[f"{r}x{c}" for r, c in I8_SHAPES])
+def test_int8_argmax_shapes(shape):
+    rows, cols = shape
+    tab = synth.int8_table((98, rows, cols), rows, cols)
+    h = synth.normal_f32(synth.rng_for(99, rows), cols)
+    tok, lg = run_argmax(tab.q, tab.scale, h)
+    lr = ref.int8_logits(tab.q, tab.scale, h)
+    assert_gemv(lg, lr, ref.int8_logits_magnitude(tab.q, tab.scale, h), str(shape))
+    assert token_ok(tok[0], lr)
+
+
+def test_vocab_projection_full_size_and_gather():
+    """151,936 x 4,096 int8 output table + argmax, and 64 embedding rows."""
+    out_t, emb_t, ids, h = synth.vocab_workload()
+    tok, lg = run_argmax(out_t.q, out_t.scale, h)
+    lr = ref.int8_logits(out_t.q, out_t.scale, h)
+    assert_gemv(lg, lr, ref.int8_logits_magnitude(out_t.q, out_t.scale, h), "vocab")
+    assert token_ok(tok[0], lr)
+    rows, scales, deq = pwg.embed_gather(dev(emb_t.q), dev(emb_t.scale), dev(ids))
+    torch.cuda.synchronize()
+    er, es, ed = ref.embed_gather(emb_t.q, emb_t.scale, ids)
+    assert np.array_equal(rows.cpu().numpy(), er)
+    assert np.array_equal(scales.cpu().numpy(), es)
+    assert np.array_equal(deq.cpu().numpy(), ed)
+
+
+def test_argmax_ties_go_to_lowest_index():
+    rows, cols = 20000, 4096
+    tab = synth.int8_table((100, 0), rows, cols)
+    h = synth.normal_f32(synth.rng_for(100, 1), cols)
+    lr = ref.int8_logits(tab.q, tab.scale, h)
+    top = int(np.argmax(lr))
+    q = tab.q.copy()
+    t = tab.scale.copy()
+    for dup in (17, 9000, rows - 1):   # identical rows score identical logits
+        q[dup] = q[top]
+        t[dup] = t[top]
+    tok, _ = run_argmax(q, t, h, logits=False)
+    assert tok[0] == min(17, top)
+
+
+def test_argmax_batch():
+    rows, cols, batch = 30000, 4096, 4
+    tab = synth.int8_table((101, 0), rows, cols)
+    hb = synth.batch_inputs(batch, cols, 7)
+    tok, lg = run_argmax(tab.q, tab.scale, hb)
+    lr = ref.int8_logits(tab.q, tab.scale, hb)
+    for b in range(batch):
+        assert token_ok(tok[b], lr[b])
+        assert_gemv(lg[b], lr[b], ref.int8_logits_magnitude(tab.q, tab.scale, hb[b]), f"batch {b}")
+
+
+def test_gather_invalid_ids_give_zero_rows_and_nan_scale():
+    tab = synth.int8_table((102, 0), 500, 256)
+    ids = np.array([3, -1, 500, 499], np.int32)
+    rows, scales, deq = pwg.embed_gather(dev(tab.q), dev(tab.scale), dev(ids))
+    torch.cuda.synchronize()
+    r, s, d = rows.cpu().numpy(), scales.cpu().numpy(), deq.cpu().numpy()
+    assert np.array_equal(r[0], tab.q[3]) and np.array_equal(r[3], tab.q[499])
+    assert not r[1].any() and not r[2].any() and not d[1].any()
+    assert np.isnan(s[1]) and np.isnan(s[2]) and s[0] == tab.scale[3]

@@ -1,0 +1,110 @@
+"""GPU parity of whole decode steps (levels schedule) against the oracle,
+including replay from a captured HIP graph."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import reference as ref
+from tests.parity import assert_gemv, token_ok
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import packed_weight_gemv_amd as pwg  # noqa: E402
+from packed_weight_gemv_amd.workload import build_step  # noqa: E402
+
+SMALL = {"q": (256, 256), "k": (64, 256), "v": (64, 256), "o": (256, 256),
+         "gate": (768, 256), "up": (768, 256), "down": (256, 768)}
+
+
+def outputs(wl):
+    d = wl.desc
+    return {
+        "levels": [lv[3].cpu().numpy() for lv in d.levels],
+        "token": int(d.token_out.cpu()[0]),
+        "emb_row": d.emb_row_out.cpu().numpy(),
+        "emb_scale": float(d.emb_scale_out.cpu()[0]),
+        "emb_deq": d.emb_deq_out.cpu().numpy(),
+        "logits": None if d.logits_out is None else d.logits_out.cpu().numpy(),
+    }
+
+
+def check_against_oracle(wl, out, token_in, full_levels):
+    """Sampled rows of every level (all rows when full_levels), the logits,
+    the token and the gathered embedding row."""
+    for smp, y in zip(wl.samples, out["levels"]):
+        yr = ref.ternary_gemv(smp.w, smp.scale, smp.x)
+        mag = ref.ternary_gemv_magnitude(smp.w, smp.scale, smp.x)
+        assert_gemv(y[smp.rows], yr, mag, f"layer {smp.layer} {smp.level}")
+    if full_levels:
+        for layer in range(len(wl.level_shapes) // 4):
+            mats = synth.layer(synth.W_STEP, layer, SMALL)
+            xs = synth.layer_inputs(synth.W_STEP, layer, hidden=256, inter=768)
+            for i, (name, members, _) in enumerate(synth.LEVELS):
+                m = synth.stacked(mats, members)
+                assert_gemv(out["levels"][4 * layer + i], ref.ternary_gemv(m.w, m.scale, xs[name]),
+                            ref.ternary_gemv_magnitude(m.w, m.scale, xs[name]), f"full {layer} {name}")
+    lr = ref.int8_logits(wl.out_table.q, wl.out_table.scale, wl.h)
+    if out["logits"] is not None:
+        assert_gemv(out["logits"], lr, ref.int8_logits_magnitude(wl.out_table.q, wl.out_table.scale, wl.h), "logits")
+    assert token_ok(out["token"], lr)
+    er, es, ed = ref.embed_gather(wl.emb_table.q, wl.emb_table.scale, [token_in])
+    assert np.array_equal(out["emb_row"], er[0])
+    assert out["emb_scale"] == es[0]
+    assert np.array_equal(out["emb_deq"], ed[0])
+
+
+def test_small_step_matches_oracle_everywhere():
+    wl = build_step(n_layers=3, shapes=SMALL, vocab=1000, hidden=256, with_logits=True)
+    pwg.step_plan(wl.desc)
+    pwg.decode_step_weights(wl.desc)
+    torch.cuda.synchronize()
+    check_against_oracle(wl, outputs(wl), wl.token0, full_levels=True)
+
+
+def test_8b_shape_two_layers_full_vocab_sampled():
+    wl = build_step(n_layers=2, with_logits=True)
+    assert [s[2:] for s in wl.level_shapes[:4]] == [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)]
+    pwg.step_plan(wl.desc)
+    pwg.decode_step_weights(wl.desc)
+    torch.cuda.synchronize()
+    out = outputs(wl)
+    check_against_oracle(wl, out, wl.token0, full_levels=False)
+    # the next step gathers the row of the token this step produced
+    pwg.decode_step_weights(wl.desc)
+    torch.cuda.synchronize()
+    check_against_oracle(wl, outputs(wl), out["token"], full_levels=False)
+
+
+def test_graph_replay_matches_eager():
+    wl = build_step(n_layers=2, shapes=SMALL, vocab=1000, hidden=256, with_logits=True)
+    pwg.step_plan(wl.desc)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        # two eager steps: the second gathers the row of the first step's token,
+        # as every later step does (h is fixed, so the token no longer changes)
+        pwg.decode_step_weights(wl.desc, stream=s)
+        pwg.decode_step_weights(wl.desc, stream=s)
+        s.synchronize()
+        eager = outputs(wl)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            pwg.decode_step_weights(wl.desc, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for lv in wl.desc.levels:      # eager work between replays: clobber outputs
+            lv[3].fill_(float("nan"))
+        wl.desc.logits_out.fill_(float("nan"))
+        wl.desc.emb_deq_out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = outputs(wl)
+        for a, b in zip(got["levels"], eager["levels"]):
+            assert np.array_equal(a, b), f"replay {rep}"
+        assert np.array_equal(got["logits"], eager["logits"])
+        assert got["token"] == eager["token"]
+        assert np.array_equal(got["emb_deq"], eager["emb_deq"])
+    check_against_oracle(wl, got, eager["token"], full_levels=True)
