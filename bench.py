@@ -1,0 +1,281 @@
+"""Benchmark: batch-1 8B-shape decode-step weight stream on one MI355X.
+
+One step = embedding row of the previous token, 36 layers x 4 ternary levels
+(q|k|v 6144x4096, o 4096x4096, gate|up 24576x4096, down 4096x12288) in
+decoder order, the int8 output projection (151,936 x 4,096) and the greedy
+argmax.  The step is captured once into a HIP graph and replayed; inputs are
+resident in HBM before the timed region starts.
+
+Order of work (the release-gate policy of the page "The Neutrino Engine",
+sections "One changed token fails the release" and "The engine also runs
+weights we did not train": identity is checked before any timing):
+  1. build the seeded synthetic workload and upload it;
+  2. parity: sampled rows of every level, the full logits' argmax and the
+     embedding row against the CPU oracle; abort on any failure;
+  3. warm up W graph replays, time K replays (HIP events on the replay stream);
+  4. the same for the levels schedule (one kernel per level) and for a null
+     graph with as many empty kernels, to split launch/dependency overhead
+     from DRAM time;
+  5. the oracle timed on a bounded sample of the same workload (rank 0).
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_BPS = 8.0e12
+METRIC = "achieved weight GB/s (% of HBM peak) + µs per batch-1 8B-shape decode step"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=256)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--schedule", choices=["persistent", "levels"], default="persistent")
+    p.add_argument("--layers", type=int, default=36)
+    p.add_argument("--no-compare", action="store_true", help="skip the levels-schedule and null-graph timings")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-layers", type=int, default=2, help="layers in the oracle's timed sample")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "packed_weight_gemv_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def time_graph(graph, stream, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            graph.replay()
+        e1.record(stream)
+    e1.synchronize()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms per replay
+
+
+def capture(fn, stream):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        fn()                      # one eager run before capture
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def parity(wl, ref, token_in):
+    """Sampled level rows, full logits argmax, embedding row."""
+    import numpy as np
+
+    from tests.parity import gemv_report, token_ok
+    worst = {"rel_l2": 0.0, "max_rel_to_magnitude": 0.0}
+    n_rows = 0
+    for smp, lv in zip(wl.samples, wl.desc.levels):
+        y = lv[3][torch_index(smp.rows)].cpu().numpy()
+        r = gemv_report(y, ref.ternary_gemv(smp.w, smp.scale, smp.x), ref.ternary_gemv_magnitude(smp.w, smp.scale, smp.x))
+        if not (r["ok"] and r["finite"]):
+            raise SystemExit(f"parity failed at layer {smp.layer} level {smp.level}: {r}")
+        worst["rel_l2"] = max(worst["rel_l2"], r["rel_l2"])
+        worst["max_rel_to_magnitude"] = max(worst["max_rel_to_magnitude"], r["max_rel_to_magnitude"])
+        n_rows += len(smp.rows)
+    lr = ref.int8_logits(wl.out_table.q, wl.out_table.scale, wl.h)
+    token = int(wl.desc.token_out.cpu()[0])
+    if not token_ok(token, lr):
+        raise SystemExit(f"parity failed: token {token} vs oracle {int(np.argmax(lr))}")
+    er, es, _ = ref.embed_gather(wl.emb_table.q, wl.emb_table.scale, [token_in])
+    if not np.array_equal(wl.desc.emb_row_out.cpu().numpy(), er[0]) or float(wl.desc.emb_scale_out.cpu()[0]) != es[0]:
+        raise SystemExit("parity failed: embedding row")
+    _, gap = ref.greedy_token(lr)
+    return {"levels_checked": len(wl.samples), "rows_checked": n_rows, "token": token, "oracle_top2_gap": gap,
+            "worst_level_rel_l2": worst["rel_l2"], "worst_rel_to_magnitude": worst["max_rel_to_magnitude"]}
+
+
+def torch_index(rows):
+    import torch
+    return torch.from_numpy(rows).to("cuda:0")
+
+
+def cpu_baseline(n_layers_sample: int, step_bytes: int):
+    """The oracle, as it stands, on layers 0..n-1 of the same seeded workload
+    and the full output projection; extrapolated to a 36-layer step."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import synth
+    from oracle import reference as ref
+    layer_s = []
+    for layer in range(n_layers_sample):
+        mats = synth.layer(synth.W_STEP, layer)
+        xs = synth.layer_inputs(synth.W_STEP, layer)
+        levels = [(synth.stacked(mats, members), xs[name]) for name, members, _ in synth.LEVELS]
+        t0 = time.perf_counter()
+        for m, x in levels:
+            ref.ternary_gemv(m.w, m.scale, x)
+        layer_s.append(time.perf_counter() - t0)
+        del mats, levels
+    out_t, _, _, h = synth.vocab_workload(n_ids=1, workload=synth.W_STEP)
+    t0 = time.perf_counter()
+    lg = ref.int8_logits(out_t.q, out_t.scale, h)
+    ref.greedy_token(lg)
+    vocab_s = time.perf_counter() - t0
+    step_s = float(np.mean(layer_s)) * synth.N_LAYERS + vocab_s
+    threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    return {
+        "value": step_bytes / step_s / 1e9, "unit": "GB/s",
+        "us_per_step": step_s * 1e6, "cores": int(threads), "kind": "oracle",
+        "sample": (f"{n_layers_sample} of 36 layers (all 4 levels each, float64 numpy) plus the full "
+                   f"151936x4096 output projection and argmax, timed once; the per-layer mean is scaled to 36 layers"),
+        "sample_seconds": float(sum(layer_s) + vocab_s),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is not built "
+                                   "(see the design notes for how the path would shard)", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np  # noqa: F401
+    import torch
+
+    import packed_weight_gemv_amd as pwg
+    from oracle import reference as ref
+    from packed_weight_gemv_amd.workload import build_step
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    schedule = pwg.SCHEDULE_PERSISTENT if args.schedule == "persistent" else pwg.SCHEDULE_LEVELS
+    t0 = time.time()
+    wl = build_step(n_layers=args.layers, schedule=pwg.SCHEDULE_PERSISTENT, with_logits=False)
+    log(f"workload built in {time.time() - t0:.1f}s: {len(wl.desc.levels)} levels")
+    bytes_ = wl.algorithmic_bytes()
+    step_bytes = bytes_["total"]
+
+    stream = torch.cuda.Stream()
+
+    def run(desc_schedule):
+        wl.desc.schedule = desc_schedule
+        wl.desc._c = None
+        pwg.step_plan(wl.desc, stream=stream)
+        return lambda: pwg.decode_step_weights(wl.desc, stream=stream)
+
+    # 2. parity of the schedule that is timed (two steps: the second gathers
+    #    the row of the first step's token, as every timed step does)
+    step_fn = run(schedule)
+    with torch.cuda.stream(stream):
+        step_fn()
+        stream.synchronize()
+        token1 = int(wl.desc.token_out.cpu()[0])
+        step_fn()
+        stream.synchronize()
+    pwg.step_status(wl.desc, stream=stream)
+    par = parity(wl, ref, token1)
+    log(f"parity ok: {par}")
+
+    # 3. timed graph replays
+    graph = capture(step_fn, stream)
+    ms = time_graph(graph, stream, args.steps, args.warmup)
+    pwg.step_status(wl.desc, stream=stream)
+    log(f"{args.schedule}: {ms * 1e3:.1f} us/step")
+    kernels_per_step = 1 if schedule == pwg.SCHEDULE_PERSISTENT else len(wl.desc.levels) + 3
+
+    extra = {}
+    if not args.no_compare:
+        other = pwg.SCHEDULE_LEVELS if schedule == pwg.SCHEDULE_PERSISTENT else pwg.SCHEDULE_PERSISTENT
+        other_fn = run(other)
+        g2 = capture(other_fn, stream)
+        ms_other = time_graph(g2, stream, args.steps, args.warmup)
+        pwg.step_status(wl.desc, stream=stream)
+        extra["levels_schedule_us" if other == pwg.SCHEDULE_LEVELS else "persistent_schedule_us"] = ms_other * 1e3
+        del g2
+        # null twin graph: as many empty kernels as the levels schedule launches
+        one = torch.zeros(1, device="cuda:0")
+        n_null = len(wl.desc.levels) + 3
+        gnull = capture(lambda: [one.add_(0) for _ in range(n_null)], stream)
+        ms_null = time_graph(gnull, stream, args.steps, args.warmup)
+        extra["null_graph_us"] = ms_null * 1e3
+        extra["null_graph_kernels"] = n_null
+        run(schedule)  # restore the timed schedule's plan
+
+    achieved_bps = step_bytes / (ms * 1e-3)
+    floor_us = step_bytes / PEAK_HBM_BPS * 1e6
+    result = {
+        "metric": METRIC,
+        "value": achieved_bps / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "us_per_step": ms * 1e3,
+        "pct_of_hbm_peak": 100.0 * achieved_bps / PEAK_HBM_BPS,
+        "floor_us": floor_us,
+        "step_over_floor": ms * 1e3 / floor_us,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "ternary x int4-limb dot (i32 exact) / int8 x int8-limb dot (i32 exact), f32 scale",
+        "data": "synthetic seeded (ternary iid p=1/3, int8 U[-127,127], activations N(0,1))",
+        "config": {
+            "workload": (f"8B-shape batch-1 decode step: embedding row + {args.layers} layers x (q|k|v 6144x4096, "
+                         "o 4096x4096, gate|up 24576x4096, down 4096x12288) ternary T2 + int8 output projection "
+                         "151936x4096 + greedy argmax, one HIP graph per step"),
+            "schedule": args.schedule,
+            "kernels_per_step": kernels_per_step,
+            "algorithmic_bytes_per_step": bytes_,
+        },
+        "parity": par,
+    }
+    result.update(extra)
+
+    # roofline of the dominant kernel
+    if schedule == pwg.SCHEDULE_PERSISTENT:
+        traffic = None
+        tfile = os.path.join(ROOT, "profiles", "step_kernel_traffic.json")
+        if os.path.exists(tfile):
+            t = json.load(open(tfile))
+            if t.get("kernel_source_sha") == kernel_source_sha() and t.get("layers") == args.layers:
+                traffic = t.get("hbm_bytes_per_launch")
+        result["roofline"] = {"bound": "hbm", "achieved": achieved_bps / 1e9, "peak": PEAK_HBM_BPS / 1e9,
+                              "unit": "GB/s", "frac": achieved_bps / PEAK_HBM_BPS, "traffic": traffic,
+                              "kernel": "step_kernel (whole step, one launch)",
+                              "per_launch_bytes": step_bytes,
+                              "avg_launch_us": ms * 1e3}
+    result["kernel_source_sha"] = kernel_source_sha()
+
+    # 5. oracle CPU baseline (bounded sample)
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        result["cpu_baseline"] = cpu_baseline(args.cpu_layers, step_bytes)
+        log(f"cpu baseline in {time.time() - t0:.1f}s")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

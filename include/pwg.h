@@ -206,8 +206,17 @@ size_t pwg_step_workspace_bytes(const pwg_step_desc* desc);
  * set of buffers, outside stream capture, before pwg_decode_step_weights. */
 int pwg_step_plan(const pwg_step_desc* desc, void* stream);
 
-/* Enqueue one step on `stream` (capturable; no allocation, no sync). */
+/* Enqueue one step on `stream` (capturable; no allocation, no sync).
+ * Persistent schedule: one kernel with one workgroup per CU; every level
+ * barrier wait is bounded (about 0.5 s), after which the kernel records a
+ * timeout and ends instead of hanging; pwg_step_status reports it. */
 int pwg_decode_step_weights(const pwg_step_desc* desc, void* stream);
+
+/* Synchronously reads the step's status word (persistent schedule; always
+ * PWG_OK for the levels schedule): PWG_ERR_HIP with a message if a level
+ * barrier timed out or workgroups were not placed as planned.  Not for the
+ * hot path. */
+int pwg_step_status(const pwg_step_desc* desc, void* stream);
 
 /* Thread-local message of the last failed call on this thread ("" if none). */
 const char* pwg_last_error(void);

@@ -19,7 +19,7 @@ import numpy as np
 __all__ = [
     "PwgError", "lib", "packed_size", "pack_weights", "unpack_weights", "ternary_gemv",
     "argmax_workspace_bytes", "int8_gemv_argmax", "embed_gather", "Level", "StepDesc",
-    "step_workspace_bytes", "step_plan", "decode_step_weights", "last_error", "version",
+    "step_workspace_bytes", "step_plan", "decode_step_weights", "step_status", "last_error", "version",
     "SCHEDULE_LEVELS", "SCHEDULE_PERSISTENT", "LIB_PATH",
 ]
 
@@ -85,13 +85,14 @@ _gather = _sig("pwg_embed_gather", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp
 _step_ws = _sig("pwg_step_workspace_bytes", _sz, C.POINTER(_StepDesc))
 _step_plan = _sig("pwg_step_plan", C.c_int, C.POINTER(_StepDesc), _vp)
 _step = _sig("pwg_decode_step_weights", C.c_int, C.POINTER(_StepDesc), _vp)
+_step_status = _sig("pwg_step_status", C.c_int, C.POINTER(_StepDesc), _vp)
 _last_error = _sig("pwg_last_error", C.c_char_p)
 _version = _sig("pwg_version", C.c_int)
 
 EXPORTED = ["pwg_packed_size", "pwg_pack_weights", "pwg_unpack_weights", "pwg_ternary_gemv",
             "pwg_argmax_workspace_bytes", "pwg_int8_gemv_argmax", "pwg_embed_gather",
             "pwg_step_workspace_bytes", "pwg_step_plan", "pwg_decode_step_weights",
-            "pwg_last_error", "pwg_version"]
+            "pwg_step_status", "pwg_last_error", "pwg_version"]
 
 
 def last_error() -> str:
@@ -245,3 +246,8 @@ def step_plan(desc: StepDesc, stream=None):
 
 def decode_step_weights(desc: StepDesc, stream=None):
     _check(_step(C.byref(desc.c()), _stream(stream)))
+
+
+def step_status(desc: StepDesc, stream=None):
+    """Raises if a persistent step recorded a barrier timeout (synchronous)."""
+    _check(_step_status(C.byref(desc.c()), _stream(stream)))

@@ -145,6 +145,12 @@ extern "C" int pwg_step_plan(const pwg_step_desc* d, void* stream) {
   return PWG_OK;
 }
 
+extern "C" int pwg_step_status(const pwg_step_desc* d, void* stream) {
+  TRY(validate_step(d));
+  if (d->schedule != PWG_SCHEDULE_PERSISTENT) return PWG_OK;
+  return step_persistent_status(d, argmax_ws(d->vocab, 1), stream);
+}
+
 extern "C" int pwg_decode_step_weights(const pwg_step_desc* d, void* stream) {
   TRY(validate_step(d));
   if (d->workspace_bytes < pwg_step_workspace_bytes(d))

@@ -100,37 +100,98 @@ __device__ __forceinline__ void t2_limbs_from_u(const unsigned u[16], unsigned o
   }
 }
 
-// Writes the T2 limb planes of x[0..cols) into lds and the per-chunk
-// exponents into lds_e[cols/64].  All threads of the block must call it and
-// blockDim.x must be a multiple of 64 (a chunk's four groups then sit in four
-// consecutive lanes of one wave, active together).
-__device__ __forceinline__ void t2_prepare_x(const float* __restrict__ x, int cols, unsigned* lds, int* lds_e) {
+// Activation registers of a thread: up to G groups of 16 floats.  Loading
+// them is split from converting them so that a caller can issue the loads
+// early (they head the memory queue) and convert later.
+template <int G>
+struct T2XRegs {
+  float4 v[G][4];
+};
+
+// Loads groups g = threadIdx.x + i * blockDim.x (i < G) of x.
+template <int G>
+__device__ __forceinline__ void t2_x_load(const float* __restrict__ x, int cols, T2XRegs<G>& xr) {
   const int ngroups = cols >> 4;
   const float4* x4 = reinterpret_cast<const float4*>(x);
-  for (int g = threadIdx.x; g < ngroups; g += blockDim.x) {
-    float4 v[4];
-    float m = 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v[q] = x4[4 * g + q];
-      m = fmaxf(m, fmaxf(fmaxf(fabsf(v[q].x), fabsf(v[q].y)), fmaxf(fabsf(v[q].z), fabsf(v[q].w))));
-    }
-    const int E = fixed_exponent(max4(m), kFixedBits);
-    unsigned u[16];
+  for (int i = 0; i < G; ++i) {
+    const int g = threadIdx.x + i * blockDim.x;
+    if (g < ngroups) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      u[4 * q + 0] = biased_fixed(v[q].x, E, kT2Bias);
-      u[4 * q + 1] = biased_fixed(v[q].y, E, kT2Bias);
-      u[4 * q + 2] = biased_fixed(v[q].z, E, kT2Bias);
-      u[4 * q + 3] = biased_fixed(v[q].w, E, kT2Bias);
+      for (int q = 0; q < 4; ++q) xr.v[i][q] = x4[4 * g + q];
     }
-    unsigned out[12];
-    t2_limbs_from_u(u, out);
-    u32x4* dst = reinterpret_cast<u32x4*>(lds + (g >> 2) * kT2ChunkDwords + (g & 3) * 12);
-    dst[0] = u32x4{out[0], out[1], out[2], out[3]};
-    dst[1] = u32x4{out[4], out[5], out[6], out[7]};
-    dst[2] = u32x4{out[8], out[9], out[10], out[11]};
-    if ((g & 3) == 0) lds_e[g >> 2] = E;
+  }
+}
+
+// Converts the loaded groups into the T2 limb planes in lds and the per-chunk
+// exponents in lds_e, then synchronises the block.  blockDim.x must be a
+// multiple of 64 (a chunk's four groups then sit in four consecutive lanes of
+// one wave, active together) and G * blockDim.x must cover cols / 16.
+template <int G>
+__device__ __forceinline__ void t2_x_convert(const T2XRegs<G>& xr, int cols, unsigned* lds, int* lds_e) {
+  const int ngroups = cols >> 4;
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const int g = threadIdx.x + i * blockDim.x;
+    if (g < ngroups) {
+      const float4* v = xr.v[i];
+      float m = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v[q].x), fabsf(v[q].y)), fmaxf(fabsf(v[q].z), fabsf(v[q].w))));
+      const int E = fixed_exponent(max4(m), kFixedBits);
+      unsigned u[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u[4 * q + 0] = biased_fixed(v[q].x, E, kT2Bias);
+        u[4 * q + 1] = biased_fixed(v[q].y, E, kT2Bias);
+        u[4 * q + 2] = biased_fixed(v[q].z, E, kT2Bias);
+        u[4 * q + 3] = biased_fixed(v[q].w, E, kT2Bias);
+      }
+      unsigned out[12];
+      t2_limbs_from_u(u, out);
+      u32x4* dst = reinterpret_cast<u32x4*>(lds + (g >> 2) * kT2ChunkDwords + (g & 3) * 12);
+      dst[0] = u32x4{out[0], out[1], out[2], out[3]};
+      dst[1] = u32x4{out[4], out[5], out[6], out[7]};
+      dst[2] = u32x4{out[8], out[9], out[10], out[11]};
+      if ((g & 3) == 0) lds_e[g >> 2] = E;
+    }
+  }
+  __syncthreads();
+}
+
+// Load + convert in one go, for any cols (loops over groups).
+__device__ __forceinline__ void t2_prepare_x(const float* __restrict__ x, int cols, unsigned* lds, int* lds_e) {
+  const int ngroups = cols >> 4;
+  for (int base = 0; base < ngroups; base += blockDim.x) {
+    T2XRegs<1> xr;
+    const int g = base + threadIdx.x;
+    if (g < ngroups) {
+      const float4* x4 = reinterpret_cast<const float4*>(x);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xr.v[0][q] = x4[4 * g + q];
+      const float4* v = xr.v[0];
+      float m = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v[q].x), fabsf(v[q].y)), fmaxf(fabsf(v[q].z), fabsf(v[q].w))));
+      const int E = fixed_exponent(max4(m), kFixedBits);
+      unsigned u[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u[4 * q + 0] = biased_fixed(v[q].x, E, kT2Bias);
+        u[4 * q + 1] = biased_fixed(v[q].y, E, kT2Bias);
+        u[4 * q + 2] = biased_fixed(v[q].z, E, kT2Bias);
+        u[4 * q + 3] = biased_fixed(v[q].w, E, kT2Bias);
+      }
+      unsigned out[12];
+      t2_limbs_from_u(u, out);
+      u32x4* dst = reinterpret_cast<u32x4*>(lds + (g >> 2) * kT2ChunkDwords + (g & 3) * 12);
+      dst[0] = u32x4{out[0], out[1], out[2], out[3]};
+      dst[1] = u32x4{out[4], out[5], out[6], out[7]};
+      dst[2] = u32x4{out[8], out[9], out[10], out[11]};
+      if ((g & 3) == 0) lds_e[g >> 2] = E;
+    }
   }
   __syncthreads();
 }
@@ -147,22 +208,50 @@ __device__ __forceinline__ void t2_prepare_x(const float* __restrict__ x, int co
 constexpr int kI8ChunkDwords = 12;
 constexpr unsigned kI8Bias = 0x808080u;
 
-__device__ __forceinline__ void i8_prepare_x(const float* __restrict__ h, int cols, unsigned* lds, int* lds_e) {
+template <int G>
+struct I8XRegs {
+  float4 v[G];
+};
+
+template <int G>
+__device__ __forceinline__ void i8_x_load(const float* __restrict__ h, int cols, I8XRegs<G>& xr) {
   const int ngroups = cols >> 2;  // groups of 4 elements
   const float4* h4 = reinterpret_cast<const float4*>(h);
-  for (int g = threadIdx.x; g < ngroups; g += blockDim.x) {
-    const float4 v = h4[g];
-    const float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    const int E = fixed_exponent(max4(m), kFixedBits);
-    unsigned T[3];
-    gather_bytes4(biased_fixed(v.x, E, kI8Bias), biased_fixed(v.y, E, kI8Bias), biased_fixed(v.z, E, kI8Bias),
-                  biased_fixed(v.w, E, kI8Bias), T);
-    unsigned* dst = lds + (g >> 2) * kI8ChunkDwords + (g & 3) * 3;
-    dst[0] = T[0] ^ 0x80808080u;
-    dst[1] = T[1] ^ 0x80808080u;
-    dst[2] = T[2] ^ 0x80808080u;
-    if ((g & 3) == 0) lds_e[g >> 2] = E;
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const int g = threadIdx.x + i * blockDim.x;
+    if (g < ngroups) xr.v[i] = h4[g];
   }
+}
+
+__device__ __forceinline__ void i8_convert_group(const float4 v, int g, unsigned* lds, int* lds_e) {
+  const float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  const int E = fixed_exponent(max4(m), kFixedBits);
+  unsigned T[3];
+  gather_bytes4(biased_fixed(v.x, E, kI8Bias), biased_fixed(v.y, E, kI8Bias), biased_fixed(v.z, E, kI8Bias),
+                biased_fixed(v.w, E, kI8Bias), T);
+  unsigned* dst = lds + (g >> 2) * kI8ChunkDwords + (g & 3) * 3;
+  dst[0] = T[0] ^ 0x80808080u;
+  dst[1] = T[1] ^ 0x80808080u;
+  dst[2] = T[2] ^ 0x80808080u;
+  if ((g & 3) == 0) lds_e[g >> 2] = E;
+}
+
+template <int G>
+__device__ __forceinline__ void i8_x_convert(const I8XRegs<G>& xr, int cols, unsigned* lds, int* lds_e) {
+  const int ngroups = cols >> 2;
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const int g = threadIdx.x + i * blockDim.x;
+    if (g < ngroups) i8_convert_group(xr.v[i], g, lds, lds_e);
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void i8_prepare_x(const float* __restrict__ h, int cols, unsigned* lds, int* lds_e) {
+  const int ngroups = cols >> 2;
+  const float4* h4 = reinterpret_cast<const float4*>(h);
+  for (int g = threadIdx.x; g < ngroups; g += blockDim.x) i8_convert_group(h4[g], g, lds, lds_e);
   __syncthreads();
 }
 

@@ -37,5 +37,6 @@ int launch_embed_gather(const int8_t* table, const float* s, int64_t rows, int64
 size_t step_persistent_workspace(const pwg_step_desc* d);
 int step_persistent_plan(const pwg_step_desc* d, size_t ws_offset, void* stream);
 int step_persistent_launch(const pwg_step_desc* d, size_t ws_offset, void* stream);
+int step_persistent_status(const pwg_step_desc* d, size_t ws_offset, void* stream);
 
 }  // namespace pwg

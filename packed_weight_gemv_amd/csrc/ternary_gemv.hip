@@ -19,35 +19,15 @@
 // accumulators with shifts, converts once to float and reduces over T lanes.
 #include "device_common.h"
 #include "pwg_internal.h"
+#include "t2_rows.h"
 
 namespace pwg {
 namespace {
 
 using namespace dev;
 
-// acc[l] += 4 * sum over the chunk's 64 weights of w * digit_l(x).
-__device__ __forceinline__ void t2_chunk_dot(const u32x4 wv, const unsigned* X, int acc[6]) {
-  const unsigned wd[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const unsigned hi = wd[j] & 0xCCCCCCCCu;
-    const unsigned lo = (wd[j] << 2) & 0xCCCCCCCCu;
-#pragma unroll
-    for (int l = 0; l < 6; ++l) {
-      acc[l] = dot8(lo, X[12 * j + l], acc[l]);
-      acc[l] = dot8(hi, X[12 * j + 6 + l], acc[l]);
-    }
-  }
-}
-
-// sum_l acc[l] * 16^l (exact: |result| <= 4 * 64 * 2^22 = 2^30).
-__device__ __forceinline__ int combine_limbs6(const int acc[6]) {
-  unsigned v = static_cast<unsigned>(acc[5]);
-#pragma unroll
-  for (int l = 4; l >= 0; --l) v = v * 16u + static_cast<unsigned>(acc[l]);
-  return static_cast<int>(v);
-}
-
+// Rows narrower than 64 chunks: T lanes (a power of two) share a row and a
+// wave works on 64 / T rows at a time.
 template <int T, int C, int U, int WPB>
 __global__ __launch_bounds__(WPB * 64) void ternary_gemv_kernel(const u32x4* __restrict__ w,
                                                                  const float* __restrict__ scale, int rows,
@@ -106,7 +86,7 @@ __global__ __launch_bounds__(WPB * 64) void ternary_gemv_kernel(const u32x4* __r
       for (int c = 0; c < C; ++c) {
         int acc[6] = {0, 0, 0, 0, 0, 0};
         t2_chunk_dot(Wv[u][c], X[c], acc);
-        part += ldexpf(static_cast<float>(combine_limbs6(acc)), Ec[c]);
+        part += ldexpf(static_cast<float>(static_cast<int>(combine_limbs6(acc))), Ec[c]);
       }
       const float total = group_sum<T>(part);
       const long r = (g + u) * RW + ri;
@@ -131,6 +111,47 @@ __global__ __launch_bounds__(WPB * 64) void ternary_gemv_kernel(const u32x4* __r
   }
 }
 
+// Rows of 64 or more chunks: the whole wave works on one row at a time, in
+// tiles of U rows with NB tiles in flight (see t2_rows.h).  G > 0: the
+// activation loads are issued before the first weight tiles; G == 0: the
+// activation is prepared after priming (widest rows, to save registers).
+template <int C, int U, int NB, int WPB, int G>
+__global__ __launch_bounds__(WPB * 64) void t2_rows_kernel(const u32x4* __restrict__ w,
+                                                           const float* __restrict__ scale, int rows, int cols,
+                                                           const float* __restrict__ x, float* __restrict__ y) {
+  extern __shared__ __align__(16) unsigned lds[];
+  const int nchunks = cols >> 6;
+  int* lds_e = reinterpret_cast<int*>(lds + nchunks * kT2ChunkDwords);
+  const unsigned lane = threadIdx.x & 63u;
+  const unsigned wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long gw = static_cast<long>(blockIdx.x) * WPB + wave, nw = static_cast<long>(gridDim.x) * WPB;
+  const long r0 = gw * rows / nw, r1 = (gw + 1) * rows / nw;
+
+  T2XRegs<(G > 0 ? G : 1)> xr;
+  if constexpr (G > 0) t2_x_load<G>(x, cols, xr);
+  T2Tile<C, U> tiles[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    if (r0 + b * U < r1) t2_tile_load<C, U>(w, scale, nchunks, r0 + b * U, r1, lane, tiles[b]);
+  if constexpr (G > 0) t2_x_convert<G>(xr, cols, lds, lds_e);
+  else t2_prepare_x(x, cols, lds, lds_e);
+  T2Lane<C> st;
+  t2_lane_init<C>(st, lds, lds_e, nchunks, lane);
+
+  for (long r = r0; r < r1; r += NB * U) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const long rb = r + b * U;
+      if (rb < r1) {
+        const float v = t2_tile_compute<C, U>(st, tiles[b], rb, r1);
+        const long row = rb + row_of<U>(static_cast<int>(lane >> 4));
+        if ((lane & (64u / U - 1u)) == 0u && row < r1) y[row] = v;
+        if (rb + NB * U < r1) t2_tile_load<C, U>(w, scale, nchunks, rb + NB * U, r1, lane, tiles[b]);
+      }
+    }
+  }
+}
+
 struct Instance {
   const void* fn;
   int wpb;
@@ -143,12 +164,17 @@ Instance make() {
   return Instance{reinterpret_cast<const void*>(&ternary_gemv_kernel<T, C, U, WPB>), WPB, 64 / T, 0};
 }
 
+template <int C, int U, int NB, int WPB, int G>
+Instance make_rows() {
+  return Instance{reinterpret_cast<const void*>(&t2_rows_kernel<C, U, NB, WPB, G>), WPB, 1, 0};
+}
+
 // Smallest lane count T (power of two) whose C chunks cover the row.
 Instance* pick(int cols) {
   static Instance t1 = make<1, 1, 4, 16>(), t2 = make<2, 1, 4, 16>(), t4 = make<4, 1, 4, 16>(),
                   t8 = make<8, 1, 4, 16>(), t16 = make<16, 1, 4, 16>(), t32 = make<32, 1, 4, 16>(),
-                  t64 = make<64, 1, 4, 16>(), c2 = make<64, 2, 4, 8>(), c3 = make<64, 3, 2, 8>(),
-                  c4 = make<64, 4, 2, 4>();
+                  t64 = make_rows<1, 4, 2, 16, 1>(), c2 = make_rows<2, 2, 2, 8, 1>(), c3 = make_rows<3, 1, 2, 8, 2>(),
+                  c4 = make_rows<4, 1, 2, 4, 0>();
   const int nchunks = cols / 64;
   if (nchunks <= 1) return &t1;
   if (nchunks <= 2) return &t2;

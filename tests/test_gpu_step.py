@@ -56,30 +56,40 @@ def check_against_oracle(wl, out, token_in, full_levels):
     assert np.array_equal(out["emb_deq"], ed[0])
 
 
-def test_small_step_matches_oracle_everywhere():
-    wl = build_step(n_layers=3, shapes=SMALL, vocab=1000, hidden=256, with_logits=True)
+SCHEDULES = [pwg.SCHEDULE_LEVELS, pwg.SCHEDULE_PERSISTENT]
+SCHED_IDS = ["levels", "persistent"]
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES, ids=SCHED_IDS)
+def test_small_step_matches_oracle_everywhere(schedule):
+    wl = build_step(n_layers=3, shapes=SMALL, vocab=1000, hidden=256, with_logits=True, schedule=schedule)
     pwg.step_plan(wl.desc)
     pwg.decode_step_weights(wl.desc)
     torch.cuda.synchronize()
+    pwg.step_status(wl.desc)
     check_against_oracle(wl, outputs(wl), wl.token0, full_levels=True)
 
 
-def test_8b_shape_two_layers_full_vocab_sampled():
-    wl = build_step(n_layers=2, with_logits=True)
+@pytest.mark.parametrize("schedule", SCHEDULES, ids=SCHED_IDS)
+def test_8b_shape_two_layers_full_vocab_sampled(schedule):
+    wl = build_step(n_layers=2, with_logits=True, schedule=schedule)
     assert [s[2:] for s in wl.level_shapes[:4]] == [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)]
     pwg.step_plan(wl.desc)
     pwg.decode_step_weights(wl.desc)
     torch.cuda.synchronize()
+    pwg.step_status(wl.desc)
     out = outputs(wl)
     check_against_oracle(wl, out, wl.token0, full_levels=False)
     # the next step gathers the row of the token this step produced
     pwg.decode_step_weights(wl.desc)
     torch.cuda.synchronize()
+    pwg.step_status(wl.desc)
     check_against_oracle(wl, outputs(wl), out["token"], full_levels=False)
 
 
-def test_graph_replay_matches_eager():
-    wl = build_step(n_layers=2, shapes=SMALL, vocab=1000, hidden=256, with_logits=True)
+@pytest.mark.parametrize("schedule", SCHEDULES, ids=SCHED_IDS)
+def test_graph_replay_matches_eager(schedule):
+    wl = build_step(n_layers=2, shapes=SMALL, vocab=1000, hidden=256, with_logits=True, schedule=schedule)
     pwg.step_plan(wl.desc)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
@@ -107,4 +117,25 @@ def test_graph_replay_matches_eager():
         assert np.array_equal(got["logits"], eager["logits"])
         assert got["token"] == eager["token"]
         assert np.array_equal(got["emb_deq"], eager["emb_deq"])
+    pwg.step_status(wl.desc)
     check_against_oracle(wl, got, eager["token"], full_levels=True)
+
+
+def test_persistent_many_steps_stay_identical():
+    """Barrier epochs advance every step; 50 back-to-back steps must all
+    finish (no timeout) and give the same outputs as the first."""
+    wl = build_step(n_layers=4, shapes=SMALL, vocab=1000, hidden=256, with_logits=True,
+                    schedule=pwg.SCHEDULE_PERSISTENT)
+    pwg.step_plan(wl.desc)
+    pwg.decode_step_weights(wl.desc)
+    pwg.decode_step_weights(wl.desc)
+    torch.cuda.synchronize()
+    first = outputs(wl)
+    for _ in range(50):
+        pwg.decode_step_weights(wl.desc)
+    torch.cuda.synchronize()
+    pwg.step_status(wl.desc)
+    last = outputs(wl)
+    for a, b in zip(first["levels"], last["levels"]):
+        assert np.array_equal(a, b)
+    assert np.array_equal(first["logits"], last["logits"]) and first["token"] == last["token"]
