@@ -40,11 +40,14 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=256)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--schedule", choices=["persistent", "levels"], default="persistent")
+    p.add_argument("--schedule", choices=["persistent", "levels", "stream"], default="persistent")
     p.add_argument("--layers", type=int, default=36)
     p.add_argument("--no-compare", action="store_true", help="skip the levels-schedule and null-graph timings")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-layers", type=int, default=2, help="layers in the oracle's timed sample")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle's timed sample")
+    p.add_argument("--counters", action="store_true",
+                   help="counter-collection run: 3 eager steps of the timed schedule plus a 1 GiB device copy "
+                        "(the known-size reference for FETCH_SIZE / WRITE_SIZE); prints nothing else")
     return p.parse_args()
 
 
@@ -122,16 +125,19 @@ def torch_index(rows):
     return torch.from_numpy(rows).to("cuda:0")
 
 
-def cpu_baseline(n_layers_sample: int, step_bytes: int):
-    """The oracle, as it stands, on layers 0..n-1 of the same seeded workload
-    and the full output projection; extrapolated to a 36-layer step."""
+def cpu_baseline(target_s: float, step_bytes: int):
+    """The oracle, as it stands, on the first layers of the same seeded
+    workload (as many as fit in about target_s seconds, at least one) and the
+    full output projection; the per-layer mean is scaled to 36 layers."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     import synth
     from oracle import reference as ref
     layer_s = []
-    for layer in range(n_layers_sample):
+    for layer in range(synth.N_LAYERS):
+        if layer_s and sum(layer_s) + float(np.mean(layer_s)) > target_s:
+            break
         mats = synth.layer(synth.W_STEP, layer)
         xs = synth.layer_inputs(synth.W_STEP, layer)
         levels = [(synth.stacked(mats, members), xs[name]) for name, members, _ in synth.LEVELS]
@@ -150,7 +156,7 @@ def cpu_baseline(n_layers_sample: int, step_bytes: int):
     return {
         "value": step_bytes / step_s / 1e9, "unit": "GB/s",
         "us_per_step": step_s * 1e6, "cores": int(threads), "kind": "oracle",
-        "sample": (f"{n_layers_sample} of 36 layers (all 4 levels each, float64 numpy) plus the full "
+        "sample": (f"{len(layer_s)} of 36 layers (all 4 levels each, float64 numpy) plus the full "
                    f"151936x4096 output projection and argmax, timed once; the per-layer mean is scaled to 36 layers"),
         "sample_seconds": float(sum(layer_s) + vocab_s),
     }
@@ -170,7 +176,8 @@ def main():
     from packed_weight_gemv_amd.workload import build_step
 
     assert torch.cuda.is_available(), "bench needs a GPU"
-    schedule = pwg.SCHEDULE_PERSISTENT if args.schedule == "persistent" else pwg.SCHEDULE_LEVELS
+    schedule = {"persistent": pwg.SCHEDULE_PERSISTENT, "levels": pwg.SCHEDULE_LEVELS,
+                "stream": pwg.SCHEDULE_STREAM}[args.schedule]
     t0 = time.time()
     wl = build_step(n_layers=args.layers, schedule=pwg.SCHEDULE_PERSISTENT, with_logits=False)
     log(f"workload built in {time.time() - t0:.1f}s: {len(wl.desc.levels)} levels")
@@ -178,6 +185,20 @@ def main():
     step_bytes = bytes_["total"]
 
     stream = torch.cuda.Stream()
+    if args.counters:
+        wl.desc.schedule = schedule
+        wl.desc._c = None
+        pwg.step_plan(wl.desc, stream=stream)
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                pwg.decode_step_weights(wl.desc, stream=stream)
+            src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")   # 1 GiB
+            dst = torch.empty_like(src)
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        pwg.step_status(wl.desc, stream=stream)
+        log("counter run done: 3 steps + one 1 GiB device-to-device copy")
+        return
 
     def run(desc_schedule):
         wl.desc.schedule = desc_schedule
@@ -207,13 +228,21 @@ def main():
 
     extra = {}
     if not args.no_compare:
-        other = pwg.SCHEDULE_LEVELS if schedule == pwg.SCHEDULE_PERSISTENT else pwg.SCHEDULE_PERSISTENT
-        other_fn = run(other)
-        g2 = capture(other_fn, stream)
-        ms_other = time_graph(g2, stream, args.steps, args.warmup)
-        pwg.step_status(wl.desc, stream=stream)
-        extra["levels_schedule_us" if other == pwg.SCHEDULE_LEVELS else "persistent_schedule_us"] = ms_other * 1e3
-        del g2
+        names = {pwg.SCHEDULE_LEVELS: "levels", pwg.SCHEDULE_PERSISTENT: "persistent", pwg.SCHEDULE_STREAM: "stream"}
+        for other in (pwg.SCHEDULE_LEVELS, pwg.SCHEDULE_PERSISTENT, pwg.SCHEDULE_STREAM):
+            if other == schedule:
+                continue
+            other_fn = run(other)
+            with torch.cuda.stream(stream):   # parity of the compared schedule's token
+                other_fn()
+                stream.synchronize()
+            pwg.step_status(wl.desc, stream=stream)
+            g2 = capture(other_fn, stream)
+            ms_other = time_graph(g2, stream, args.steps, args.warmup)
+            pwg.step_status(wl.desc, stream=stream)
+            extra[f"{names[other]}_schedule_us"] = ms_other * 1e3
+            del g2
+            log(f"{names[other]}: {ms_other * 1e3:.1f} us/step")
         # null twin graph: as many empty kernels as the levels schedule launches
         one = torch.zeros(1, device="cuda:0")
         n_null = len(wl.desc.levels) + 3
@@ -272,7 +301,7 @@ def main():
     # 5. oracle CPU baseline (bounded sample)
     if not args.no_cpu_baseline:
         t0 = time.time()
-        result["cpu_baseline"] = cpu_baseline(args.cpu_layers, step_bytes)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds, step_bytes)
         log(f"cpu baseline in {time.time() - t0:.1f}s")
     print(json.dumps(result), flush=True)
 

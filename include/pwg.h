@@ -60,8 +60,16 @@ enum {
 
 /* Step schedules for pwg_decode_step_weights. */
 enum {
-  PWG_SCHEDULE_LEVELS = 0,     /* one kernel per dependency level, in decoder order */
-  PWG_SCHEDULE_PERSISTENT = 1  /* one persistent kernel; device-wide level barriers */
+  PWG_SCHEDULE_LEVELS = 0,      /* one kernel per dependency level, in decoder order */
+  PWG_SCHEDULE_PERSISTENT = 1,  /* one persistent kernel; a device-wide barrier after
+                                   every level, so level L+1 starts only when all of
+                                   level L is done (the dependency of a chained step) */
+  PWG_SCHEDULE_STREAM = 2       /* the persistent kernel without level barriers: each
+                                   workgroup takes the levels in decoder order, but
+                                   levels overlap across workgroups.  Valid only when
+                                   no level reads another level's output (as in a
+                                   step over fixed inputs); it measures the weight
+                                   stream alone, without dependency waits */
 };
 
 /* ---------------------------------------------------------------------------

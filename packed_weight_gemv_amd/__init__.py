@@ -20,7 +20,7 @@ __all__ = [
     "PwgError", "lib", "packed_size", "pack_weights", "unpack_weights", "ternary_gemv",
     "argmax_workspace_bytes", "int8_gemv_argmax", "embed_gather", "Level", "StepDesc",
     "step_workspace_bytes", "step_plan", "decode_step_weights", "step_status", "last_error", "version",
-    "SCHEDULE_LEVELS", "SCHEDULE_PERSISTENT", "LIB_PATH",
+    "SCHEDULE_LEVELS", "SCHEDULE_PERSISTENT", "SCHEDULE_STREAM", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpwg.so")
@@ -30,6 +30,7 @@ ERR_NAMES = {-1: "PWG_ERR_ARG", -2: "PWG_ERR_ALIGN", -3: "PWG_ERR_SIZE", -4: "PW
              -5: "PWG_ERR_HIP", -6: "PWG_ERR_UNSUPPORTED"}
 SCHEDULE_LEVELS = 0
 SCHEDULE_PERSISTENT = 1
+SCHEDULE_STREAM = 2
 
 
 class PwgError(RuntimeError):

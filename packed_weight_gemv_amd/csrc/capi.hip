@@ -106,7 +106,8 @@ namespace {
 int validate_step(const pwg_step_desc* d) {
   const char* fn = "pwg_decode_step_weights";
   if (!d) return fail(PWG_ERR_ARG, "%s: desc is null", fn);
-  if (d->schedule != PWG_SCHEDULE_LEVELS && d->schedule != PWG_SCHEDULE_PERSISTENT)
+  if (d->schedule != PWG_SCHEDULE_LEVELS && d->schedule != PWG_SCHEDULE_PERSISTENT &&
+      d->schedule != PWG_SCHEDULE_STREAM)
     return fail(PWG_ERR_ARG, "%s: unknown schedule %d", fn, d->schedule);
   if (d->n_levels < 0 || d->n_levels > 4096) return fail(PWG_ERR_ARG, "%s: n_levels out of range", fn);
   if (d->n_levels > 0 && !d->levels) return fail(PWG_ERR_ARG, "%s: levels is null", fn);
@@ -141,13 +142,13 @@ extern "C" int pwg_step_plan(const pwg_step_desc* d, void* stream) {
   if (d->workspace_bytes < pwg_step_workspace_bytes(d))
     return fail(PWG_ERR_SIZE, "pwg_step_plan: workspace %zu < %zu bytes", d->workspace_bytes,
                 pwg_step_workspace_bytes(d));
-  if (d->schedule == PWG_SCHEDULE_PERSISTENT) return step_persistent_plan(d, argmax_ws(d->vocab, 1), stream);
+  if (d->schedule != PWG_SCHEDULE_LEVELS) return step_persistent_plan(d, argmax_ws(d->vocab, 1), stream);
   return PWG_OK;
 }
 
 extern "C" int pwg_step_status(const pwg_step_desc* d, void* stream) {
   TRY(validate_step(d));
-  if (d->schedule != PWG_SCHEDULE_PERSISTENT) return PWG_OK;
+  if (d->schedule == PWG_SCHEDULE_LEVELS) return PWG_OK;
   return step_persistent_status(d, argmax_ws(d->vocab, 1), stream);
 }
 
@@ -156,7 +157,7 @@ extern "C" int pwg_decode_step_weights(const pwg_step_desc* d, void* stream) {
   if (d->workspace_bytes < pwg_step_workspace_bytes(d))
     return fail(PWG_ERR_SIZE, "pwg_decode_step_weights: workspace %zu < %zu bytes", d->workspace_bytes,
                 pwg_step_workspace_bytes(d));
-  if (d->schedule == PWG_SCHEDULE_PERSISTENT) return step_persistent_launch(d, argmax_ws(d->vocab, 1), stream);
+  if (d->schedule != PWG_SCHEDULE_LEVELS) return step_persistent_launch(d, argmax_ws(d->vocab, 1), stream);
   // Levels schedule: embedding row, every level in decoder order, output
   // projection + argmax, all on one stream.
   TRY(launch_embed_gather(d->emb_table, d->emb_scale, d->vocab, d->hidden, d->token_in, 1, d->emb_row_out,

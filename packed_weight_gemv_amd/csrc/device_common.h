@@ -108,15 +108,17 @@ struct T2XRegs {
   float4 v[G][4];
 };
 
-// Loads groups g = threadIdx.x + i * blockDim.x (i < G) of x.
+// Loads groups g = t + i * nt (i < G) of x, where t = threadIdx.x - first and
+// nt = blockDim.x - first (threads below `first` load nothing).
 template <int G>
-__device__ __forceinline__ void t2_x_load(const float* __restrict__ x, int cols, T2XRegs<G>& xr) {
+__device__ __forceinline__ void t2_x_load(const float* __restrict__ x, int cols, T2XRegs<G>& xr, int first = 0) {
   const int ngroups = cols >> 4;
   const float4* x4 = reinterpret_cast<const float4*>(x);
+  const int t = static_cast<int>(threadIdx.x) - first, nt = static_cast<int>(blockDim.x) - first;
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    const int g = threadIdx.x + i * blockDim.x;
-    if (g < ngroups) {
+    const int g = t + i * nt;
+    if (t >= 0 && g < ngroups) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) xr.v[i][q] = x4[4 * g + q];
     }
@@ -124,16 +126,18 @@ __device__ __forceinline__ void t2_x_load(const float* __restrict__ x, int cols,
 }
 
 // Converts the loaded groups into the T2 limb planes in lds and the per-chunk
-// exponents in lds_e, then synchronises the block.  blockDim.x must be a
-// multiple of 64 (a chunk's four groups then sit in four consecutive lanes of
-// one wave, active together) and G * blockDim.x must cover cols / 16.
+// exponents in lds_e, then synchronises the block.  blockDim.x and `first`
+// must be multiples of 64 (a chunk's four groups then sit in four consecutive
+// lanes of one wave, active together) and G * (blockDim.x - first) must cover
+// cols / 16.
 template <int G>
-__device__ __forceinline__ void t2_x_convert(const T2XRegs<G>& xr, int cols, unsigned* lds, int* lds_e) {
+__device__ __forceinline__ void t2_x_convert(const T2XRegs<G>& xr, int cols, unsigned* lds, int* lds_e, int first = 0) {
   const int ngroups = cols >> 4;
+  const int t = static_cast<int>(threadIdx.x) - first, nt = static_cast<int>(blockDim.x) - first;
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    const int g = threadIdx.x + i * blockDim.x;
-    if (g < ngroups) {
+    const int g = t + i * nt;
+    if (t >= 0 && g < ngroups) {
       const float4* v = xr.v[i];
       float m = 0.f;
 #pragma unroll
@@ -214,13 +218,14 @@ struct I8XRegs {
 };
 
 template <int G>
-__device__ __forceinline__ void i8_x_load(const float* __restrict__ h, int cols, I8XRegs<G>& xr) {
+__device__ __forceinline__ void i8_x_load(const float* __restrict__ h, int cols, I8XRegs<G>& xr, int first = 0) {
   const int ngroups = cols >> 2;  // groups of 4 elements
   const float4* h4 = reinterpret_cast<const float4*>(h);
+  const int t = static_cast<int>(threadIdx.x) - first, nt = static_cast<int>(blockDim.x) - first;
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    const int g = threadIdx.x + i * blockDim.x;
-    if (g < ngroups) xr.v[i] = h4[g];
+    const int g = t + i * nt;
+    if (t >= 0 && g < ngroups) xr.v[i] = h4[g];
   }
 }
 
@@ -238,12 +243,13 @@ __device__ __forceinline__ void i8_convert_group(const float4 v, int g, unsigned
 }
 
 template <int G>
-__device__ __forceinline__ void i8_x_convert(const I8XRegs<G>& xr, int cols, unsigned* lds, int* lds_e) {
+__device__ __forceinline__ void i8_x_convert(const I8XRegs<G>& xr, int cols, unsigned* lds, int* lds_e, int first = 0) {
   const int ngroups = cols >> 2;
+  const int t = static_cast<int>(threadIdx.x) - first, nt = static_cast<int>(blockDim.x) - first;
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    const int g = threadIdx.x + i * blockDim.x;
-    if (g < ngroups) i8_convert_group(xr.v[i], g, lds, lds_e);
+    const int g = t + i * nt;
+    if (t >= 0 && g < ngroups) i8_convert_group(xr.v[i], g, lds, lds_e);
   }
   __syncthreads();
 }

@@ -64,11 +64,12 @@ struct alignas(256) Plan {
   unsigned status;
   unsigned gen;            // completed steps (barrier epochs derive from it)
   unsigned n_levels;
-  unsigned n_barriers;     // n_levels + 1
+  unsigned n_barriers;     // barriers per step: n_levels + 1 (ordered) or 1
   unsigned mode;           // kBarrierL2 or kBarrierFlat
   unsigned grid;
   unsigned per_xcd[8];
   unsigned xcd_mask;
+  unsigned ordered;        // 1: level barriers; 0: levels only ordered within each workgroup
   int vocab, hidden, i8c;
   const u32x4* out_table;
   const float* out_scale;
@@ -174,17 +175,29 @@ struct Barrier {
 // the wave's rows, wait for the previous level, convert the input to limb
 // planes, then stream the rows (t2_rows.h).  Returns false when the wait timed
 // out (the same answer in every thread of the block).
+// Wave 0 polls the barrier, so it issues no loads before the wait: a wave's
+// loads complete in order, and its polls would otherwise queue behind them.
+// The activation is loaded by waves 1..7; wave 0 loads its first tiles
+// after the wait.
 template <int C, int U, int NB, int G, class Wait>
-__device__ bool t2_level(const DevLevel& L, long r0, long r1, unsigned lane, unsigned* lds, Wait&& wait_prev) {
+__device__ bool t2_level(const DevLevel& L, long r0, long r1, unsigned lane, unsigned wave, unsigned* lds,
+                         Wait&& wait_prev) {
   T2XRegs<G> xr;
-  t2_x_load<G>(L.x, L.cols, xr);
+  t2_x_load<G>(L.x, L.cols, xr, 64);
   T2Tile<C, U> tiles[NB];
+  if (wave != 0) {
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-    if (r0 + b * U < r1) t2_tile_load<C, U>(L.w, L.scale, L.nchunks, r0 + b * U, r1, lane, tiles[b]);
+    for (int b = 0; b < NB; ++b)
+      if (r0 + b * U < r1) t2_tile_load<C, U>(L.w, L.scale, L.nchunks, r0 + b * U, r1, lane, tiles[b]);
+  }
   if (wait_prev()) return false;
+  if (wave == 0) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (r0 + b * U < r1) t2_tile_load<C, U>(L.w, L.scale, L.nchunks, r0 + b * U, r1, lane, tiles[b]);
+  }
   int* lds_e = reinterpret_cast<int*>(lds + L.nchunks * kT2ChunkDwords);
-  t2_x_convert<G>(xr, L.cols, lds, lds_e);
+  t2_x_convert<G>(xr, L.cols, lds, lds_e, 64);
   T2Lane<C> st;
   t2_lane_init<C>(st, lds, lds_e, L.nchunks, lane);
   for (long r = r0; r < r1; r += NB * U) {
@@ -268,6 +281,7 @@ __device__ __forceinline__ void i8_tile_compute(const Plan& P, long r, long r1, 
   }
 }
 
+template <bool kOrdered>
 __global__ __launch_bounds__(kThreads, 1) void step_kernel(Plan* plan) {
   extern __shared__ __align__(16) unsigned lds[];
   const Plan& P = *plan;
@@ -313,29 +327,37 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(Plan* plan) {
   for (unsigned li = 0; li < P.n_levels; ++li) {
     const DevLevel L = levels[li];
     const long r0 = gw * L.rows / nw, r1 = (gw + 1) * L.rows / nw;
-    auto wait_prev = [&]() -> bool { return li > 0 ? bar.wait(li - 1) : false; };
+    auto wait_prev = [&]() -> bool { return (kOrdered && li > 0) ? bar.wait(li - 1) : false; };
     bool ok;
-    if (L.c == 1) ok = t2_level<1, 4, 3, 1>(L, r0, r1, lane, lds, wait_prev);
-    else if (L.c == 2) ok = t2_level<2, 2, 2, 1>(L, r0, r1, lane, lds, wait_prev);
-    else ok = t2_level<3, 1, 1, 2>(L, r0, r1, lane, lds, wait_prev);
+    // G covers cols/16 groups with the 448 loading threads of waves 1..7
+    if (L.c == 1) ok = t2_level<1, 4, 3, 1>(L, r0, r1, lane, wave, lds, wait_prev);
+    else if (L.c == 2) ok = t2_level<2, 2, 2, 2>(L, r0, r1, lane, wave, lds, wait_prev);
+    else ok = t2_level<3, 1, 1, 2>(L, r0, r1, lane, wave, lds, wait_prev);
     if (!ok) return;
-    bar.arrive(li);
+    if (kOrdered) bar.arrive(li);
   }
 
   // output projection + per-workgroup argmax
   {
-    constexpr int U = 2, NB = 2, G = 2;  // G * 512 threads * 4 elements covers hidden <= 4096
+    constexpr int U = 2, NB = 2, G = 3;  // G * 448 threads * 4 elements covers hidden <= 4096
     const long r0 = gw * P.vocab / nw, r1 = (gw + 1) * P.vocab / nw;
     I8XRegs<G> hr;
-    i8_x_load<G>(P.h, P.hidden, hr);
+    i8_x_load<G>(P.h, P.hidden, hr, 64);
     I8Tile<U> tiles[NB];
+    if (wave != 0) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-      if (r0 + b * U < r1) i8_tile_load<U>(P, r0 + b * U, r1, lane, tiles[b]);
-    if (P.n_levels > 0 && bar.wait(P.n_levels - 1)) return;
+      for (int b = 0; b < NB; ++b)
+        if (r0 + b * U < r1) i8_tile_load<U>(P, r0 + b * U, r1, lane, tiles[b]);
+    }
+    if (kOrdered && P.n_levels > 0 && bar.wait(P.n_levels - 1)) return;
+    if (wave == 0) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        if (r0 + b * U < r1) i8_tile_load<U>(P, r0 + b * U, r1, lane, tiles[b]);
+    }
     const int nchunks = P.hidden >> 4;
     int* lds_e = reinterpret_cast<int*>(lds + nchunks * kI8ChunkDwords);
-    i8_x_convert<G>(hr, P.hidden, lds, lds_e);
+    i8_x_convert<G>(hr, P.hidden, lds, lds_e, 64);
     unsigned H[kMaxI8C][12];
     int Ec[kMaxI8C];
 #pragma unroll
@@ -377,9 +399,10 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(Plan* plan) {
       st_sc64(&partials[blockIdx.x], m);
     }
   }
-  bar.arrive(P.n_levels);
+  const unsigned final_barrier = kOrdered ? P.n_levels : 0u;
+  bar.arrive(final_barrier);
   if (blockIdx.x == 0) {
-    if (bar.wait(P.n_levels)) return;
+    if (bar.wait(final_barrier)) return;
     if (threadIdx.x < 64) {
       unsigned long long k = 0ull;
       for (unsigned b = threadIdx.x; b < gridDim.x; b += 64) {
@@ -440,7 +463,8 @@ int grid_for(const pwg_step_desc* d, GridInfo* gi) {
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   gi->lds = step_lds_bytes(d);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(&step_kernel), kThreads, gi->lds);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(&step_kernel<true>), kThreads, gi->lds);
   if (e != hipSuccess) return fail(PWG_ERR_HIP, "persistent step: device query failed: %s", hipGetErrorString(e));
   if (occ < 1) return fail(PWG_ERR_UNSUPPORTED, "persistent step: kernel does not fit on a CU");
   gi->grid = cus < static_cast<int>(kMaxGrid) ? cus : static_cast<int>(kMaxGrid);  // one workgroup per CU
@@ -450,7 +474,7 @@ int grid_for(const pwg_step_desc* d, GridInfo* gi) {
 }  // namespace
 
 size_t step_persistent_workspace(const pwg_step_desc* d) {
-  if (!d || d->schedule != PWG_SCHEDULE_PERSISTENT || d->n_levels < 0) return 0;
+  if (!d || (d->schedule != PWG_SCHEDULE_PERSISTENT && d->schedule != PWG_SCHEDULE_STREAM) || d->n_levels < 0) return 0;
   return layout_for(d->n_levels).total + 256;  // + 256 for aligning the plan
 }
 
@@ -499,7 +523,8 @@ int step_persistent_plan(const pwg_step_desc* d, size_t ws_offset, void* stream)
   h.status = kStatusOk;
   h.gen = 0;
   h.n_levels = static_cast<unsigned>(d->n_levels);
-  h.n_barriers = h.n_levels + 1;
+  h.ordered = d->schedule == PWG_SCHEDULE_STREAM ? 0u : 1u;
+  h.n_barriers = h.ordered ? h.n_levels + 1 : 1u;  // unordered: only the final (argmax) barrier
   h.mode = uniform && census[0] > 0 ? kBarrierL2 : kBarrierFlat;
   h.grid = static_cast<unsigned>(gi.grid);
   h.xcd_mask = 0;
@@ -551,7 +576,10 @@ int step_persistent_launch(const pwg_step_desc* d, size_t ws_offset, void* strea
   const int rc = grid_for(d, &gi);
   if (rc != PWG_OK) return rc;
   Plan* dplan = plan_ptr(d, ws_offset);
-  hipLaunchKernelGGL(step_kernel, dim3(gi.grid), dim3(kThreads), gi.lds, reinterpret_cast<hipStream_t>(stream), dplan);
+  if (d->schedule == PWG_SCHEDULE_STREAM)
+    hipLaunchKernelGGL(step_kernel<false>, dim3(gi.grid), dim3(kThreads), gi.lds, reinterpret_cast<hipStream_t>(stream), dplan);
+  else
+    hipLaunchKernelGGL(step_kernel<true>, dim3(gi.grid), dim3(kThreads), gi.lds, reinterpret_cast<hipStream_t>(stream), dplan);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PWG_ERR_HIP, "persistent step launch: %s", hipGetErrorString(e));
   return PWG_OK;

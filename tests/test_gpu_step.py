@@ -56,8 +56,8 @@ def check_against_oracle(wl, out, token_in, full_levels):
     assert np.array_equal(out["emb_deq"], ed[0])
 
 
-SCHEDULES = [pwg.SCHEDULE_LEVELS, pwg.SCHEDULE_PERSISTENT]
-SCHED_IDS = ["levels", "persistent"]
+SCHEDULES = [pwg.SCHEDULE_LEVELS, pwg.SCHEDULE_PERSISTENT, pwg.SCHEDULE_STREAM]
+SCHED_IDS = ["levels", "persistent", "stream"]
 
 
 @pytest.mark.parametrize("schedule", SCHEDULES, ids=SCHED_IDS)
@@ -121,11 +121,11 @@ def test_graph_replay_matches_eager(schedule):
     check_against_oracle(wl, got, eager["token"], full_levels=True)
 
 
-def test_persistent_many_steps_stay_identical():
+@pytest.mark.parametrize("schedule", SCHEDULES[1:], ids=SCHED_IDS[1:])
+def test_persistent_many_steps_stay_identical(schedule):
     """Barrier epochs advance every step; 50 back-to-back steps must all
     finish (no timeout) and give the same outputs as the first."""
-    wl = build_step(n_layers=4, shapes=SMALL, vocab=1000, hidden=256, with_logits=True,
-                    schedule=pwg.SCHEDULE_PERSISTENT)
+    wl = build_step(n_layers=4, shapes=SMALL, vocab=1000, hidden=256, with_logits=True, schedule=schedule)
     pwg.step_plan(wl.desc)
     pwg.decode_step_weights(wl.desc)
     pwg.decode_step_weights(wl.desc)
