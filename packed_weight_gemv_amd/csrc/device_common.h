@@ -164,6 +164,41 @@ __device__ __forceinline__ void t2_x_convert(const T2XRegs<G>& xr, int cols, uns
   __syncthreads();
 }
 
+// Converts activations staged raw (float32) in LDS into limb planes; all
+// threads of the block take part (groups g = threadIdx.x + i * blockDim.x).
+__device__ __forceinline__ void t2_convert_staged(const float* xs, int cols, unsigned* lds, int* lds_e) {
+  const int ngroups = cols >> 4;
+  for (int base = 0; base < ngroups; base += blockDim.x) {
+    const int g = base + threadIdx.x;
+    if (g < ngroups) {
+      float4 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = reinterpret_cast<const float4*>(xs)[4 * g + q];
+      float m = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v[q].x), fabsf(v[q].y)), fmaxf(fabsf(v[q].z), fabsf(v[q].w))));
+      const int E = fixed_exponent(max4(m), kFixedBits);
+      unsigned u[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u[4 * q + 0] = biased_fixed(v[q].x, E, kT2Bias);
+        u[4 * q + 1] = biased_fixed(v[q].y, E, kT2Bias);
+        u[4 * q + 2] = biased_fixed(v[q].z, E, kT2Bias);
+        u[4 * q + 3] = biased_fixed(v[q].w, E, kT2Bias);
+      }
+      unsigned out[12];
+      t2_limbs_from_u(u, out);
+      u32x4* dst = reinterpret_cast<u32x4*>(lds + (g >> 2) * kT2ChunkDwords + (g & 3) * 12);
+      dst[0] = u32x4{out[0], out[1], out[2], out[3]};
+      dst[1] = u32x4{out[4], out[5], out[6], out[7]};
+      dst[2] = u32x4{out[8], out[9], out[10], out[11]};
+      if ((g & 3) == 0) lds_e[g >> 2] = E;
+    }
+  }
+  __syncthreads();
+}
+
 // Load + convert in one go, for any cols (loops over groups).
 __device__ __forceinline__ void t2_prepare_x(const float* __restrict__ x, int cols, unsigned* lds, int* lds_e) {
   const int ngroups = cols >> 4;

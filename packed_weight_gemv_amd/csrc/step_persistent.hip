@@ -43,10 +43,10 @@ constexpr unsigned long long kSpinLimit = 50000000ull;  // 0.5 s at the 100 MHz 
 
 enum : unsigned { kBarrierL2 = 0, kBarrierFlat = 1 };
 enum : unsigned { kStatusOk = 0, kStatusTimeout = 1 };
+// state words: [0] status, [1] completed steps (barrier epochs derive from it)
+enum : unsigned { kStateStatus = 0, kStateGen = 1 };
 
-// Dynamic LDS requested by the step kernel: more than half of the 160 KiB of
-// a CU, so no CU can hold two of its workgroups.
-constexpr size_t kStepLdsBytes = 96 * 1024;
+
 
 struct DevLevel {
   const u32x4* w;
@@ -59,10 +59,11 @@ struct DevLevel {
   int c;        // chunks per lane
 };
 
-// Device-side plan, written by pwg_step_plan into the workspace.
+// Device-side plan, written by pwg_step_plan into the workspace.  It is
+// constant while a step runs (the kernel takes it as a read-only argument,
+// so its fields are read with scalar loads); the words the kernel writes
+// live in the state, counter, flag and partial-key areas that follow it.
 struct alignas(256) Plan {
-  unsigned status;
-  unsigned gen;            // completed steps (barrier epochs derive from it)
   unsigned n_levels;
   unsigned n_barriers;     // barriers per step: n_levels + 1 (ordered) or 1
   unsigned mode;           // kBarrierL2 or kBarrierFlat
@@ -82,8 +83,8 @@ struct alignas(256) Plan {
   float* emb_scale_out;
   float4* emb_deq_out;
   float* logits_out;
-  // offsets (bytes from the plan) of the barrier words, partial keys and level table
-  unsigned long long counters_off, flags_off, partials_off, levels_off, calib_off;
+  // offsets (bytes from the plan) of the state words, barrier words, partial keys and level table
+  unsigned long long state_off, counters_off, flags_off, partials_off, levels_off, calib_off;
 };
 
 constexpr size_t kCountersBytes = 8 * 128;                  // one 64-bit counter per 128-byte line
@@ -111,14 +112,15 @@ __device__ __forceinline__ bool reached(unsigned f, unsigned e) { return static_
 __device__ __forceinline__ unsigned xcc_id() { return __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 7u; }
 
 struct Barrier {
-  Plan* plan;
+  const Plan* plan;
+  unsigned* state;
   unsigned long long* counters;
   unsigned* flags;
   unsigned xcd;
   unsigned base;  // gen * n_barriers
 
   // Arrive at barrier j: the workgroup's stores are complete before it counts.
-  __device__ void arrive(unsigned j) {
+  __device__ __forceinline__ void arrive(unsigned j) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -137,9 +139,31 @@ struct Barrier {
     }
   }
 
+  // Arrival by the control wave alone, after it stored the workgroup's
+  // outputs of the level: the agent-scope release writes back this XCD's L2
+  // and waits for the wave's stores, so the outputs are visible device-wide
+  // before the count.  The compute waves are not held up: their outstanding
+  // loads are weight prefetches, which need no ordering.
+  __device__ __forceinline__ void arrive_release(unsigned j) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (threadIdx.x == 0) {
+      const unsigned epoch = base + j + 1;
+      if (plan->mode == kBarrierL2) {
+        const unsigned long long old =
+            __hip_atomic_fetch_add(&counters[xcd * 16], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const unsigned long long target = static_cast<unsigned long long>(epoch) * plan->per_xcd[xcd];
+        if (old + 1 == target) {
+          for (int r = 0; r < kReplicas; ++r) st_sc(&flags[r * 64 + xcd], epoch);
+        }
+      } else {
+        st_sc(&flags[kReplicas * 64 + blockIdx.x], epoch);
+      }
+    }
+  }
+
   // Wait until every workgroup has arrived at barrier j.  Returns true when
   // the wait timed out; the answer is the same for every thread of the block.
-  __device__ bool wait(unsigned j) {
+  __device__ __forceinline__ bool wait(unsigned j) {
     __shared__ int timed_out;
     if (threadIdx.x < 64) {
       const unsigned epoch = base + j + 1;
@@ -162,7 +186,7 @@ struct Barrier {
       }
       if (lane == 0) {
         timed_out = late ? 1 : 0;
-        if (late) st_sc(&plan->status, kStatusTimeout);
+        if (late) st_sc(&state[kStateStatus], kStatusTimeout);
       }
     }
     __syncthreads();
@@ -170,228 +194,417 @@ struct Barrier {
   }
 };
 
-// ----------------------------------------------------------------- ternary
-// One ternary level for one wave: read the level input and prime NB tiles of
-// the wave's rows, wait for the previous level, convert the input to limb
-// planes, then stream the rows (t2_rows.h).  Returns false when the wait timed
-// out (the same answer in every thread of the block).
-// Wave 0 polls the barrier, so it issues no loads before the wait: a wave's
-// loads complete in order, and its polls would otherwise queue behind them.
-// The activation is loaded by waves 1..7; wave 0 loads its first tiles
-// after the wait.
-template <int C, int U, int NB, int G, class Wait>
-__device__ bool t2_level(const DevLevel& L, long r0, long r1, unsigned lane, unsigned wave, unsigned* lds,
-                         Wait&& wait_prev) {
-  T2XRegs<G> xr;
-  t2_x_load<G>(L.x, L.cols, xr, 64);
-  T2Tile<C, U> tiles[NB];
-  if (wave != 0) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-      if (r0 + b * U < r1) t2_tile_load<C, U>(L.w, L.scale, L.nchunks, r0 + b * U, r1, lane, tiles[b]);
-  }
-  if (wait_prev()) return false;
-  if (wave == 0) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-      if (r0 + b * U < r1) t2_tile_load<C, U>(L.w, L.scale, L.nchunks, r0 + b * U, r1, lane, tiles[b]);
-  }
-  int* lds_e = reinterpret_cast<int*>(lds + L.nchunks * kT2ChunkDwords);
-  t2_x_convert<G>(xr, L.cols, lds, lds_e, 64);
-  T2Lane<C> st;
-  t2_lane_init<C>(st, lds, lds_e, L.nchunks, lane);
-  for (long r = r0; r < r1; r += NB * U) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const long rb = r + b * U;
-      if (rb < r1) {
-        const float v = t2_tile_compute<C, U>(st, tiles[b], rb, r1);
-        const long row = rb + row_of<U>(static_cast<int>(lane >> 4));
-        if ((lane & (64u / U - 1u)) == 0u && row < r1) st_sc(L.y + row, v);
-        if (rb + NB * U < r1) t2_tile_load<C, U>(L.w, L.scale, L.nchunks, rb + NB * U, r1, lane, tiles[b]);
-      }
-    }
-  }
-  __syncthreads();  // every wave has its limbs in registers before the LDS is reused
-  return true;
+// ----------------------------------------------------------------- streaming
+// LDS budget of the step kernel (bytes).
+constexpr int kComputeWaves = kWpb - 1;                 // waves 1..7; wave 0 is the control wave
+constexpr int kRingSlots = 8;                           // 1 KiB slots per compute wave
+constexpr int kSlotBytes = 1024;                        // 64 lanes x 16 bytes
+constexpr int kMaxT2Cols = 64 * 64 * kMaxC;             // 12288
+constexpr int kMaxWgRows = 640;                         // rows of one level per workgroup
+constexpr size_t kRingBytes = static_cast<size_t>(kComputeWaves) * kRingSlots * kSlotBytes;
+constexpr size_t kStageBytes = kMaxT2Cols * 4;
+constexpr size_t kPlaneBytes = static_cast<size_t>(kMaxT2Cols / 64) * (kT2ChunkDwords + 1) * 4;
+constexpr size_t kScaleBytes = 2 * kMaxWgRows * 4;
+constexpr size_t kOutBytes = kMaxWgRows * 4;              // a level's outputs of the workgroup (ordered)
+constexpr size_t kStepSmem = kRingBytes + kStageBytes + kPlaneBytes + kScaleBytes + kOutBytes;
+
+#define PWG_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// One asynchronous 16-byte-per-lane copy from global memory into LDS: lane i
+// lands at lds + 16 * i.  No VGPR is written; completion is tracked by vmcnt.
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, PWG_LDS(lds), 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, PWG_LDS(lds), 4, 0, 0);
 }
 
-// ----------------------------------------------------------------- int8 vocab
-template <int U>
-struct I8Tile {
-  u32x4 q[U][kMaxI8C];
-  float s;  // scale of the tile row this lane reports
+// Waits until at most n of this wave's vector-memory operations are
+// outstanding (n >= kRingSlots waits for kRingSlots - 1: waiting longer is
+// always safe).  Loads retire in order, so when every load issued after a
+// given one may still be pending, that one has completed.  The count is an
+// immediate of the instruction, hence the branches; n is wave-uniform and
+// is tested from the most common value (a full ring) down.
+__device__ __forceinline__ void wait_vm_le(unsigned n) {
+#define PWG_VM(k) __builtin_amdgcn_s_waitcnt(((k) & 15) | (((k) >> 4) << 14) | (7 << 4) | (15 << 8))
+  static_assert(kRingSlots == 8, "wait_vm_le covers counts up to 7");
+  if (n >= 7) { PWG_VM(7); }
+  else if (n == 6) { PWG_VM(6); }
+  else if (n == 5) { PWG_VM(5); }
+  else if (n == 4) { PWG_VM(4); }
+  else if (n == 3) { PWG_VM(3); }
+  else if (n == 2) { PWG_VM(2); }
+  else if (n == 1) { PWG_VM(1); }
+  else { PWG_VM(0); }
+#undef PWG_VM
+}
+
+// Rows of level `li` owned by workgroup `b` of `nb`: [R0, R1); compute wave
+// k (0..6) of the workgroup owns [r0, r1) inside it.
+__device__ __forceinline__ void wg_rows(long rows, unsigned b, unsigned nb, long& R0, long& R1) {
+  R0 = static_cast<long>(b) * rows / nb;
+  R1 = static_cast<long>(b + 1) * rows / nb;
+}
+__device__ __forceinline__ void wave_rows(long R0, long R1, unsigned k, long& r0, long& r1) {
+  r0 = R0 + static_cast<long>(k) * (R1 - R0) / kComputeWaves;
+  r1 = R0 + static_cast<long>(k + 1) * (R1 - R0) / kComputeWaves;
+}
+
+// Wave-uniform copies (the values are the same in every lane; this keeps
+// them in scalar registers, so the level table is read with scalar loads
+// that do not wait behind the wave's outstanding weight copies).
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ unsigned uni(unsigned v) { return static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<int>(v))); }
+template <typename T>
+__device__ __forceinline__ T* uni(T* p) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = uni(static_cast<unsigned>(v)), hi = uni(static_cast<unsigned>(v >> 32));
+  return reinterpret_cast<T*>((static_cast<unsigned long long>(hi) << 32) | lo);
+}
+
+// The producer half of a compute wave: walks the wave's rows of every level
+// (then of the vocabulary table) and copies each row's slots into the ring.
+struct Producer {
+  const DevLevel* levels;
+  unsigned n_levels;
+  int vocab, hidden;
+  const u32x4* out_table;
+  unsigned nwg;       // workgroups of the launch
+  unsigned k;         // compute-wave index 0..6
+  unsigned lane;
+  unsigned issued;    // slots issued (one DMA each)
+  unsigned level;     // level being produced (n_levels = vocabulary, n_levels + 1 = done)
+  int row, row_end;
+  int chunk, chunks_per_row, nchunks;
+  const u32x4* base;
+  unsigned char* ring;
+
+  __device__ __forceinline__ void enter_level() {
+    level = uni(level);
+    while (level <= n_levels) {
+      int rows;
+      if (level < n_levels) {
+        rows = uni(levels[level].rows);
+        nchunks = uni(levels[level].nchunks);
+        chunks_per_row = uni(levels[level].c);
+        base = uni(levels[level].w);
+      } else {
+        rows = vocab;
+        nchunks = hidden >> 4;
+        chunks_per_row = (nchunks + 63) / 64;
+        base = out_table;
+      }
+      long R0, R1, r0, r1;
+      wg_rows(rows, blockIdx.x, nwg, R0, R1);
+      wave_rows(R0, R1, k, r0, r1);
+      row = uni(static_cast<int>(r0));
+      row_end = uni(static_cast<int>(r1));
+      chunk = 0;
+      if (row < row_end) return;
+      level = uni(level + 1);
+    }
+  }
+
+  // Issues one slot if the ring has room (issued - consumed < kRingSlots).
+  __device__ __forceinline__ bool issue(unsigned consumed) {
+    if (uni(level) > n_levels || uni(issued) - uni(consumed) >= static_cast<unsigned>(kRingSlots)) return false;
+    unsigned c = lane + 64u * static_cast<unsigned>(chunk);
+    c = c < static_cast<unsigned>(nchunks) ? c : static_cast<unsigned>(nchunks - 1);
+    dma16(base + static_cast<long>(row) * nchunks + c, ring + (issued % kRingSlots) * kSlotBytes);
+    issued = uni(issued + 1);
+    chunk = uni(chunk + 1);
+    if (chunk == chunks_per_row) {
+      chunk = 0;
+      row = uni(row + 1);
+      if (row == row_end) {
+        level = uni(level + 1);
+        enter_level();
+      }
+    }
+    return true;
+  }
+  __device__ __forceinline__ void fill(unsigned consumed) {
+    while (issue(consumed)) {
+    }
+  }
 };
 
-template <int U>
-__device__ __forceinline__ void i8_tile_load(const Plan& P, long r, long r1, unsigned lane, I8Tile<U>& t) {
-  const int nchunks = P.hidden >> 4;
+// The consumer half: takes the next row's C slots out of the ring.
+template <int C>
+__device__ __forceinline__ void take_row(Producer& pr, unsigned& consumed, const unsigned char* ring, unsigned lane,
+                                         u32x4 (&w)[C]) {
+  // the row's last slot has index consumed + C - 1; everything issued after it may still be in flight
+  wait_vm_le(pr.issued - consumed - C);
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (r + u < r1) {
-      const u32x4* row = P.out_table + (r + u) * static_cast<long>(nchunks);
-#pragma unroll
-      for (int c = 0; c < kMaxI8C; ++c) {
-        unsigned chunk = lane + 64u * c;
-        chunk = chunk < static_cast<unsigned>(nchunks) ? chunk : static_cast<unsigned>(nchunks - 1);
-        t.q[u][c] = __builtin_nontemporal_load(row + chunk);
-      }
-    }
-  }
-  const long rs = r + row_of<U>(static_cast<int>(lane >> 4));
-  t.s = rs < r1 ? P.out_scale[rs] : 0.f;
+  for (int c = 0; c < C; ++c)
+    w[c] = *reinterpret_cast<const u32x4*>(ring + ((consumed + c) % kRingSlots) * kSlotBytes + lane * 16);
+  consumed += C;
 }
 
-// Logits of tile rows [r, r + U); each reporting lane (one per tile row)
-// folds its row into its running (max, lowest index).
-template <int U>
-__device__ __forceinline__ void i8_tile_compute(const Plan& P, long r, long r1, unsigned lane, const I8Tile<U>& t,
-                                                const unsigned (&H)[kMaxI8C][12], const int (&Ec)[kMaxI8C],
-                                                float& best, unsigned& best_idx) {
-  float p[U];
+// Consumes the wave's rows of one ternary level (C chunks of 64 words per
+// lane and row), four rows per tile reduction.  Results go to y, or to the
+// workgroup's LDS output buffer when `out_buf` is set.
+template <int C>
+__device__ __forceinline__ void t2_consume_level(const DevLevel& L, long r0, long r1, long R0, const float* scales,
+                                                 unsigned lane, Producer& pr, unsigned& consumed,
+                                                 const unsigned char* ring, const unsigned* planes,
+                                                 const int* plane_e, float* out_buf) {
+  T2Lane<C> st;
+  t2_lane_init<C>(st, planes, plane_e, L.nchunks, lane);
+  for (long r = r0; r < r1; r += 4) {
+    float p[4];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    p[u] = 0.f;
-    if (r + u < r1) {
+    for (int u = 0; u < 4; ++u) {
+      p[u] = 0.f;
+      if (r + u < r1) {
+        u32x4 w[C];
+        take_row<C>(pr, consumed, ring, lane, w);
 #pragma unroll
-      for (int c = 0; c < kMaxI8C; ++c) {
-        int a0 = 0, a1 = 0, a2 = 0;
-        const unsigned qd[4] = {t.q[u][c].x, t.q[u][c].y, t.q[u][c].z, t.q[u][c].w};
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          a0 = dot4(qd[g], H[c][3 * g + 0], a0);
-          a1 = dot4(qd[g], H[c][3 * g + 1], a1);
-          a2 = dot4(qd[g], H[c][3 * g + 2], a2);
+        for (int c = 0; c < C; ++c) {
+          t2_chunk_dot(w[c], st.X[c], st.acc[c]);
+          const unsigned comb = combine_limbs6(st.acc[c]);
+          const int v = static_cast<int>(comb - st.prev[c]);
+          st.prev[c] = comb;
+          p[u] += ldexpf(static_cast<float>(v), st.Ec[c]);
         }
-        // each limb sum is exact in float32 (|a| <= 16*127*128 < 2^24); the shifts are exact
-        const float pc = fmaf(static_cast<float>(a2), 65536.0f, fmaf(static_cast<float>(a1), 256.0f, static_cast<float>(a0)));
-        p[u] += ldexpf(pc, Ec[c]);
+        pr.fill(consumed);  // the row's slots were read (their values are in use above)
+      }
+    }
+    const long row = r + row_of<4>(static_cast<int>(lane >> 4));
+    const float total = tile_reduce<4>(p);
+    if ((lane & 15u) == 0u && row < r1) {
+      const float v = scales[row - R0] * total;
+      if (out_buf) out_buf[row - R0] = v;  // published by the control wave
+      else L.y[row] = v;
+    }
+  }
+}
+
+__device__ __forceinline__ void i8_consume_level(const Plan& P, long r0, long r1, long R0, const float* scales, unsigned lane,
+                                 Producer& pr, unsigned& consumed, const unsigned char* ring,
+                                 const unsigned* planes, const int* plane_e, float& best, unsigned& best_idx) {
+  const int nchunks = P.hidden >> 4;
+  unsigned H[kMaxI8C][12];
+  int Ec[kMaxI8C];
+#pragma unroll
+  for (int c = 0; c < kMaxI8C; ++c) {
+    const unsigned chunk = lane + 64u * c;
+    const bool ok = chunk < static_cast<unsigned>(nchunks);
+    Ec[c] = ok ? -plane_e[chunk] : 0;
+    const u32x4* src = reinterpret_cast<const u32x4*>(planes + (ok ? chunk : 0u) * kI8ChunkDwords);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const u32x4 v = ok ? src[q] : u32x4{0u, 0u, 0u, 0u};
+      H[c][4 * q] = v.x; H[c][4 * q + 1] = v.y; H[c][4 * q + 2] = v.z; H[c][4 * q + 3] = v.w;
+    }
+  }
+  const int cpr = (nchunks + 63) / 64;  // slots per row (4 for hidden = 4096)
+  for (long r = r0; r < r1; r += 4) {
+    float p[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      p[u] = 0.f;
+      if (r + u < r1) {
+        u32x4 q[kMaxI8C];
+        wait_vm_le(pr.issued - consumed - cpr);
+#pragma unroll
+        for (int c = 0; c < kMaxI8C; ++c)
+          q[c] = c < cpr ? *reinterpret_cast<const u32x4*>(ring + ((consumed + c) % kRingSlots) * kSlotBytes + lane * 16)
+                         : u32x4{0u, 0u, 0u, 0u};
+        consumed += cpr;
+#pragma unroll
+        for (int c = 0; c < kMaxI8C; ++c) {
+          int a0 = 0, a1 = 0, a2 = 0;
+          const unsigned qd[4] = {q[c].x, q[c].y, q[c].z, q[c].w};
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            a0 = dot4(qd[g], H[c][3 * g + 0], a0);
+            a1 = dot4(qd[g], H[c][3 * g + 1], a1);
+            a2 = dot4(qd[g], H[c][3 * g + 2], a2);
+          }
+          // each limb sum is exact in float32 (|a| <= 16*127*128 < 2^24); the shifts are exact
+          const float pc = fmaf(static_cast<float>(a2), 65536.0f, fmaf(static_cast<float>(a1), 256.0f, static_cast<float>(a0)));
+          p[u] += ldexpf(pc, Ec[c]);
+        }
+        pr.fill(consumed);
+      }
+    }
+    const long row = r + row_of<4>(static_cast<int>(lane >> 4));
+    const float total = tile_reduce<4>(p);
+    if ((lane & 15u) == 0u && row < r1) {
+      const float logit = scales[row - R0] * total;
+      if (P.logits_out) P.logits_out[row] = logit;
+      if (logit > best) {  // rows of one lane ascend: ties keep the lower index
+        best = logit;
+        best_idx = static_cast<unsigned>(row);
       }
     }
   }
-  const float logit = t.s * tile_reduce<U>(p);
-  const long row = r + row_of<U>(static_cast<int>(lane >> 4));
-  if ((lane & (64u / U - 1u)) == 0u && row < r1) {
-    if (P.logits_out) P.logits_out[row] = logit;
-    // rows of one lane ascend, so ties keep the lower index
-    if (logit > best) {
-      best = logit;
-      best_idx = static_cast<unsigned>(row);
-    }
-  }
+}
+
+// Control wave: copies level `li`'s input vector into LDS (li == n_levels:
+// the hidden state).
+__device__ __forceinline__ void stage_x(const Plan& P, const DevLevel* levels, unsigned li, unsigned lane,
+                                        float* stage) {
+  const float* x = li < P.n_levels ? levels[li].x : P.h;
+  const int cols = li < P.n_levels ? levels[li].cols : static_cast<int>(P.hidden);
+  // Lanes past the end are masked off: a masked lane neither reads nor writes.
+  for (int o = 0; o < cols; o += 256)
+    if (o + 4 * static_cast<int>(lane) < cols) dma16(x + o + 4 * lane, stage + o);
+}
+
+// Control wave: copies the workgroup's row scales of level `li` into LDS
+// (li == n_levels: the vocabulary scales).  Scales are constant inputs.
+__device__ __forceinline__ void stage_scales(const Plan& P, const DevLevel* levels, unsigned li, unsigned lane,
+                                             float* scales) {
+  const float* s = li < P.n_levels ? levels[li].scale : P.out_scale;
+  const long rows = li < P.n_levels ? levels[li].rows : P.vocab;
+  long R0, R1;
+  wg_rows(rows, blockIdx.x, P.grid, R0, R1);
+  for (long o = R0; o < R1; o += 64)
+    if (o + lane < R1) dma4(s + o + lane, scales + (o - R0));
 }
 
 template <bool kOrdered>
-__global__ __launch_bounds__(kThreads, 1) void step_kernel(Plan* plan) {
-  extern __shared__ __align__(16) unsigned lds[];
+__global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restrict__ plan,
+                                                            const DevLevel* __restrict__ levels, unsigned* state,
+                                                            unsigned long long* counters, unsigned* flags,
+                                                            unsigned long long* partials) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* ring_all = smem;
+  float* stage = reinterpret_cast<float*>(smem + kRingBytes);
+  unsigned* planes = reinterpret_cast<unsigned*>(smem + kRingBytes + kStageBytes);
+  float* scale_buf = reinterpret_cast<float*>(smem + kRingBytes + kStageBytes + kPlaneBytes);
+
   const Plan& P = *plan;
-  char* base_ptr = reinterpret_cast<char*>(plan);
   Barrier bar;
   bar.plan = plan;
-  bar.counters = reinterpret_cast<unsigned long long*>(base_ptr + P.counters_off);
-  bar.flags = reinterpret_cast<unsigned*>(base_ptr + P.flags_off);
+  bar.state = state;
+  bar.counters = counters;
+  bar.flags = flags;
   bar.xcd = xcc_id();
-  const unsigned gen = ld_sc(&plan->gen);
+  const unsigned gen = ld_sc(&state[kStateGen]);
   bar.base = gen * P.n_barriers;
-  const DevLevel* levels = reinterpret_cast<const DevLevel*>(base_ptr + P.levels_off);
-  unsigned long long* partials = reinterpret_cast<unsigned long long*>(base_ptr + P.partials_off);
 
   const unsigned lane = threadIdx.x & 63u;
   const unsigned wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const long gw = static_cast<long>(blockIdx.x) * kWpb + wave, nw = static_cast<long>(gridDim.x) * kWpb;
+  const unsigned k = wave - 1;  // compute-wave index (unused by wave 0)
+  unsigned char* ring = ring_all + static_cast<size_t>(wave == 0 ? 0 : k) * kRingSlots * kSlotBytes;
 
-  // embedding row of the previous token (workgroup 0)
-  if (blockIdx.x == 0) {
-    const int id = *P.token_in;
-    const bool ok = id >= 0 && id < P.vocab;
-    const int nchunks = P.hidden >> 4;
-    const float s = ok ? P.emb_scale[id] : __builtin_nanf("");
-    if (threadIdx.x == 0) *P.emb_scale_out = s;
-    for (int c = threadIdx.x; c < nchunks; c += kThreads) {
-      const u32x4 v = ok ? P.emb_table[static_cast<size_t>(id) * nchunks + c] : u32x4{0u, 0u, 0u, 0u};
-      P.emb_row_out[c] = v;
-      if (P.emb_deq_out) {
-        const unsigned wd[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          P.emb_deq_out[4 * c + q] =
-              ok ? make_float4(static_cast<float>(static_cast<int8_t>(wd[q] & 0xFF)) * s,
-                               static_cast<float>(static_cast<int8_t>((wd[q] >> 8) & 0xFF)) * s,
-                               static_cast<float>(static_cast<int8_t>((wd[q] >> 16) & 0xFF)) * s,
-                               static_cast<float>(static_cast<int8_t>(wd[q] >> 24)) * s)
-                 : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
-  }
+  Producer pr;
+  pr.levels = levels;
+  pr.n_levels = P.n_levels;
+  pr.vocab = P.vocab;
+  pr.hidden = P.hidden;
+  pr.out_table = P.out_table;
+  pr.nwg = P.grid;
+  pr.k = k;
+  pr.lane = lane;
+  pr.issued = 0;
+  pr.level = 0;
+  pr.ring = ring;
+  unsigned consumed = 0;
 
-  for (unsigned li = 0; li < P.n_levels; ++li) {
-    const DevLevel L = levels[li];
-    const long r0 = gw * L.rows / nw, r1 = (gw + 1) * L.rows / nw;
-    auto wait_prev = [&]() -> bool { return (kOrdered && li > 0) ? bar.wait(li - 1) : false; };
-    bool ok;
-    // G covers cols/16 groups with the 448 loading threads of waves 1..7
-    if (L.c == 1) ok = t2_level<1, 4, 3, 1>(L, r0, r1, lane, wave, lds, wait_prev);
-    else if (L.c == 2) ok = t2_level<2, 2, 2, 2>(L, r0, r1, lane, wave, lds, wait_prev);
-    else ok = t2_level<3, 1, 1, 2>(L, r0, r1, lane, wave, lds, wait_prev);
-    if (!ok) return;
-    if (kOrdered) bar.arrive(li);
-  }
-
-  // output projection + per-workgroup argmax
-  {
-    constexpr int U = 2, NB = 2, G = 3;  // G * 448 threads * 4 elements covers hidden <= 4096
-    const long r0 = gw * P.vocab / nw, r1 = (gw + 1) * P.vocab / nw;
-    I8XRegs<G> hr;
-    i8_x_load<G>(P.h, P.hidden, hr, 64);
-    I8Tile<U> tiles[NB];
-    if (wave != 0) {
+  if (wave == 0) {
+    stage_x(P, levels, 0, lane, stage);
+    stage_scales(P, levels, 0, lane, scale_buf);
+    // embedding row of the previous token (workgroup 0)
+    if (blockIdx.x == 0) {
+      const int id = *P.token_in;
+      const bool ok = id >= 0 && id < P.vocab;
+      const int nchunks = P.hidden >> 4;
+      const float s = ok ? P.emb_scale[id] : __builtin_nanf("");
+      if (lane == 0) *P.emb_scale_out = s;
+      // wave-uniform trip count: a loop whose exit differed between lanes
+      // would make everything merged after this branch divergent
+      for (int c0 = 0; c0 < nchunks; c0 += 64) {
+        const int c = c0 + static_cast<int>(lane);
+        if (c < nchunks) {
+          const u32x4 v = ok ? P.emb_table[static_cast<size_t>(id) * nchunks + c] : u32x4{0u, 0u, 0u, 0u};
+          P.emb_row_out[c] = v;
+          if (P.emb_deq_out) {
+            const unsigned wd[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-        if (r0 + b * U < r1) i8_tile_load<U>(P, r0 + b * U, r1, lane, tiles[b]);
-    }
-    if (kOrdered && P.n_levels > 0 && bar.wait(P.n_levels - 1)) return;
-    if (wave == 0) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-        if (r0 + b * U < r1) i8_tile_load<U>(P, r0 + b * U, r1, lane, tiles[b]);
-    }
-    const int nchunks = P.hidden >> 4;
-    int* lds_e = reinterpret_cast<int*>(lds + nchunks * kI8ChunkDwords);
-    i8_x_convert<G>(hr, P.hidden, lds, lds_e, 64);
-    unsigned H[kMaxI8C][12];
-    int Ec[kMaxI8C];
-#pragma unroll
-    for (int c = 0; c < kMaxI8C; ++c) {
-      const unsigned chunk = lane + 64u * c;
-      const bool ok = chunk < static_cast<unsigned>(nchunks);
-      Ec[c] = ok ? -lds_e[chunk] : 0;
-      const u32x4* src = reinterpret_cast<const u32x4*>(lds + (ok ? chunk : 0u) * kI8ChunkDwords);
-#pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        const u32x4 v = ok ? src[q] : u32x4{0u, 0u, 0u, 0u};
-        H[c][4 * q] = v.x; H[c][4 * q + 1] = v.y; H[c][4 * q + 2] = v.z; H[c][4 * q + 3] = v.w;
-      }
-    }
-    float best = -__builtin_inff();
-    unsigned best_idx = 0xFFFFFFFFu;
-    for (long r = r0; r < r1; r += NB * U) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const long rb = r + b * U;
-        if (rb < r1) {
-          i8_tile_compute<U>(P, rb, r1, lane, tiles[b], H, Ec, best, best_idx);
-          if (rb + NB * U < r1) i8_tile_load<U>(P, rb + NB * U, r1, lane, tiles[b]);
+            for (int q = 0; q < 4; ++q)
+              P.emb_deq_out[4 * c + q] =
+                  ok ? make_float4(static_cast<float>(static_cast<int8_t>(wd[q] & 0xFF)) * s,
+                                   static_cast<float>(static_cast<int8_t>((wd[q] >> 8) & 0xFF)) * s,
+                                   static_cast<float>(static_cast<int8_t>((wd[q] >> 16) & 0xFF)) * s,
+                                   static_cast<float>(static_cast<int8_t>(wd[q] >> 24)) * s)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
         }
       }
     }
-    // wave (max, lowest index) over its reporting lanes, then the workgroup's
-    unsigned long long k = best_idx == 0xFFFFFFFFu ? 0ull : argmax_key(best, best_idx);
+  } else {
+    pr.enter_level();
+    pr.fill(consumed);
+  }
+
+  float best = -__builtin_inff();
+  unsigned best_idx = 0xFFFFFFFFu;
+  float* out_buf = kOrdered ? reinterpret_cast<float*>(smem + kRingBytes + kStageBytes + kPlaneBytes + kScaleBytes)
+                            : nullptr;
+  for (unsigned li = 0; li <= P.n_levels; ++li) {
+    // Ordered: level li starts once level li-1 is complete everywhere, and
+    // only then is its input read (it may be an output of level li-1).  The
+    // agent-scope acquire drops stale lines of the input from this XCD's L2.
+    if (kOrdered && li > 0) {
+      if (bar.wait(li - 1)) return;
+      if (wave == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        stage_x(P, levels, li, lane, stage);
+      }
+    }
+    if (wave == 0) __builtin_amdgcn_s_waitcnt(0);  // this level's input and scales have landed
+    __syncthreads();
+    float* scales = scale_buf + (li & 1u) * kMaxWgRows;
+    const bool vocab = li == P.n_levels;
+    const int cols = vocab ? P.hidden : levels[li].cols;
+    int* plane_e = reinterpret_cast<int*>(planes + (vocab ? (cols >> 4) * kI8ChunkDwords : (cols >> 6) * kT2ChunkDwords));
+    if (vocab) i8_prepare_x(stage, cols, planes, plane_e);
+    else t2_convert_staged(stage, cols, planes, plane_e);
+    // compute waves copy their limbs into registers inside the consume
+    // functions; the stage buffer is free again (the conversion ended with a
+    // block barrier), and the planes are rewritten only after the next one
+    long R0, R1;
+    wg_rows(vocab ? P.vocab : levels[li].rows, blockIdx.x, P.grid, R0, R1);
+    if (wave == 0) {
+      // Next level's constant inputs; without ordering also its activations
+      // (the levels are then independent by contract).
+      if (li < P.n_levels) {
+        stage_scales(P, levels, li + 1, lane, scale_buf + ((li + 1) & 1u) * kMaxWgRows);
+        if (!kOrdered) stage_x(P, levels, li + 1, lane, stage);
+      }
+    } else {
+      long r0, r1;
+      wave_rows(R0, R1, k, r0, r1);
+      if (vocab) {
+        i8_consume_level(P, r0, r1, R0, scales, lane, pr, consumed, ring, planes, plane_e, best, best_idx);
+      } else {
+        const DevLevel& L = levels[li];
+        if (L.c == 1) t2_consume_level<1>(L, r0, r1, R0, scales, lane, pr, consumed, ring, planes, plane_e, out_buf);
+        else if (L.c == 2) t2_consume_level<2>(L, r0, r1, R0, scales, lane, pr, consumed, ring, planes, plane_e, out_buf);
+        else t2_consume_level<3>(L, r0, r1, R0, scales, lane, pr, consumed, ring, planes, plane_e, out_buf);
+      }
+    }
+    __syncthreads();  // planes, this level's scales and outputs are complete
+    if (kOrdered && !vocab && wave == 0) {
+      float* y = levels[li].y;
+      for (long o = lane; o < R1 - R0; o += 64) y[R0 + o] = out_buf[o];
+      bar.arrive_release(li);
+    }
+  }
+
+  // workgroup (max, lowest index) of the vocabulary rows
+  {
+    unsigned long long key = best_idx == 0xFFFFFFFFu ? 0ull : argmax_key(best, best_idx);
     for (int off = 32; off >= 1; off >>= 1) {
-      const unsigned long long o = __shfl_xor(k, off, kWave);
-      k = o > k ? o : k;
+      const unsigned long long o = __shfl_xor(key, off, kWave);
+      key = o > key ? o : key;
     }
     __shared__ unsigned long long wkeys[kWpb];
-    if (lane == 0) wkeys[wave] = k;
+    if (lane == 0) wkeys[wave] = key;
     __syncthreads();
     if (threadIdx.x == 0) {
       unsigned long long m = 0ull;
@@ -404,18 +617,18 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(Plan* plan) {
   if (blockIdx.x == 0) {
     if (bar.wait(final_barrier)) return;
     if (threadIdx.x < 64) {
-      unsigned long long k = 0ull;
-      for (unsigned b = threadIdx.x; b < gridDim.x; b += 64) {
+      unsigned long long m = 0ull;
+      for (unsigned b = threadIdx.x; b < P.grid; b += 64) {
         const unsigned long long o = ld_sc64(&partials[b]);
-        k = o > k ? o : k;
+        m = o > m ? o : m;
       }
       for (int off = 32; off >= 1; off >>= 1) {
-        const unsigned long long o = __shfl_xor(k, off, kWave);
-        k = o > k ? o : k;
+        const unsigned long long o = __shfl_xor(m, off, kWave);
+        m = o > m ? o : m;
       }
       if (threadIdx.x == 0) {
-        *P.token_out = static_cast<int>(argmax_key_index(k));
-        st_sc(&plan->gen, gen + 1);
+        *P.token_out = static_cast<int>(argmax_key_index(m));
+        st_sc(&state[kStateGen], gen + 1);
       }
     }
   }
@@ -427,7 +640,7 @@ __global__ void xcc_calibrate(unsigned* out) {
 
 // ----------------------------------------------------------------- host side
 struct Layout {
-  size_t plan = 0, counters = 0, flags = 0, partials = 0, levels = 0, calib = 0, total = 0;
+  size_t plan = 0, state = 0, counters = 0, flags = 0, partials = 0, levels = 0, calib = 0, total = 0;
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -435,7 +648,8 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 Layout layout_for(int n_levels) {
   Layout L;
   L.plan = 0;
-  L.counters = align_up(sizeof(Plan), 256);
+  L.state = align_up(sizeof(Plan), 256);
+  L.counters = L.state + 256;
   L.flags = L.counters + kCountersBytes;
   L.partials = align_up(L.flags + kFlagsBytes, 256);
   L.levels = align_up(L.partials + kMaxGrid * 8, 256);
@@ -449,14 +663,7 @@ struct GridInfo {
   size_t lds = 0;
 };
 
-size_t step_lds_bytes(const pwg_step_desc* d) {
-  size_t lds = i8_lds_bytes(d->hidden);
-  for (int i = 0; i < d->n_levels; ++i) {
-    const size_t b = t2_lds_bytes(d->levels[i].cols);
-    lds = b > lds ? b : lds;
-  }
-  return lds > kStepLdsBytes ? lds : kStepLdsBytes;
-}
+size_t step_lds_bytes(const pwg_step_desc*) { return kStepSmem; }
 
 int grid_for(const pwg_step_desc* d, GridInfo* gi) {
   int dev = 0, cus = 0, occ = 0;
@@ -484,7 +691,16 @@ static Plan* plan_ptr(const pwg_step_desc* d, size_t ws_offset) {
 }
 
 int step_persistent_plan(const pwg_step_desc* d, size_t ws_offset, void* stream) {
+  GridInfo gi0;
+  const int rc0 = grid_for(d, &gi0);
+  if (rc0 != PWG_OK) return rc0;
+  auto too_many = [&](int64_t rows) { return (rows + gi0.grid - 1) / gi0.grid > kMaxWgRows; };
+  if (too_many(d->vocab))
+    return fail(PWG_ERR_UNSUPPORTED, "pwg_step_plan: persistent schedules support up to %d vocabulary rows per CU",
+                kMaxWgRows);
   for (int i = 0; i < d->n_levels; ++i) {
+    if (too_many(d->levels[i].rows))
+      return fail(PWG_ERR_UNSUPPORTED, "pwg_step_plan: level %d has more than %d rows per CU", i, kMaxWgRows);
     const pwg_level& L = d->levels[i];
     if (L.cols > 64 * 64 * kMaxC)
       return fail(PWG_ERR_UNSUPPORTED, "pwg_step_plan: persistent schedule supports cols <= %d (level %d has %lld)",
@@ -520,8 +736,6 @@ int step_persistent_plan(const pwg_step_desc* d, size_t ws_offset, void* stream)
   for (int x = 1; x < 8; ++x) uniform = uniform && census[x] == census[0];
 
   Plan h{};
-  h.status = kStatusOk;
-  h.gen = 0;
   h.n_levels = static_cast<unsigned>(d->n_levels);
   h.ordered = d->schedule == PWG_SCHEDULE_STREAM ? 0u : 1u;
   h.n_barriers = h.ordered ? h.n_levels + 1 : 1u;  // unordered: only the final (argmax) barrier
@@ -546,6 +760,7 @@ int step_persistent_plan(const pwg_step_desc* d, size_t ws_offset, void* stream)
   h.emb_scale_out = d->emb_scale_out;
   h.emb_deq_out = reinterpret_cast<float4*>(d->emb_deq_out);
   h.logits_out = d->logits_out;
+  h.state_off = lay.state;
   h.counters_off = lay.counters;
   h.flags_off = lay.flags;
   h.partials_off = lay.partials;
@@ -576,10 +791,18 @@ int step_persistent_launch(const pwg_step_desc* d, size_t ws_offset, void* strea
   const int rc = grid_for(d, &gi);
   if (rc != PWG_OK) return rc;
   Plan* dplan = plan_ptr(d, ws_offset);
+  char* dbase = reinterpret_cast<char*>(dplan);
+  const Layout lay = layout_for(d->n_levels);
+  const DevLevel* lv = reinterpret_cast<const DevLevel*>(dbase + lay.levels);
+  unsigned* state = reinterpret_cast<unsigned*>(dbase + lay.state);
+  auto* counters = reinterpret_cast<unsigned long long*>(dbase + lay.counters);
+  auto* flags = reinterpret_cast<unsigned*>(dbase + lay.flags);
+  auto* partials = reinterpret_cast<unsigned long long*>(dbase + lay.partials);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (d->schedule == PWG_SCHEDULE_STREAM)
-    hipLaunchKernelGGL(step_kernel<false>, dim3(gi.grid), dim3(kThreads), gi.lds, reinterpret_cast<hipStream_t>(stream), dplan);
+    hipLaunchKernelGGL(step_kernel<false>, dim3(gi.grid), dim3(kThreads), gi.lds, st, dplan, lv, state, counters, flags, partials);
   else
-    hipLaunchKernelGGL(step_kernel<true>, dim3(gi.grid), dim3(kThreads), gi.lds, reinterpret_cast<hipStream_t>(stream), dplan);
+    hipLaunchKernelGGL(step_kernel<true>, dim3(gi.grid), dim3(kThreads), gi.lds, st, dplan, lv, state, counters, flags, partials);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PWG_ERR_HIP, "persistent step launch: %s", hipGetErrorString(e));
   return PWG_OK;
@@ -589,7 +812,8 @@ int step_persistent_status(const pwg_step_desc* d, size_t ws_offset, void* strea
   Plan* dplan = plan_ptr(d, ws_offset);
   unsigned s = 0;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpyAsync(&s, &dplan->status, 4, hipMemcpyDeviceToHost, st);
+  const unsigned* state = reinterpret_cast<const unsigned*>(reinterpret_cast<char*>(dplan) + layout_for(d->n_levels).state);
+  hipError_t e = hipMemcpyAsync(&s, &state[kStateStatus], 4, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return fail(PWG_ERR_HIP, "pwg_step_status: %s", hipGetErrorString(e));
   if (s == kStatusTimeout) return fail(PWG_ERR_HIP, "persistent step: a level barrier timed out");

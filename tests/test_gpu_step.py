@@ -1,4 +1,4 @@
-"""GPU parity of whole decode steps (levels schedule) against the oracle,
+"""GPU parity of whole decode steps (every schedule) against the oracle,
 including replay from a captured HIP graph."""
 import numpy as np
 import pytest
@@ -139,3 +139,63 @@ def test_persistent_many_steps_stay_identical(schedule):
     for a, b in zip(first["levels"], last["levels"]):
         assert np.array_equal(a, b)
     assert np.array_equal(first["logits"], last["logits"]) and first["token"] == last["token"]
+
+
+def chain_levels(wl):
+    """Rewires a built step so that every level reads a prefix of the previous
+    level's output and h is the last level's output: a chained step, in which
+    each level depends on the one before it."""
+    d = wl.desc
+    lv = [list(t) for t in d.levels]
+    for i in range(1, len(lv)):
+        lv[i][2] = lv[i - 1][3][: lv[i][5]]
+    d.levels = [tuple(t) for t in lv]
+    d.h = lv[-1][3][: d.out_table.shape[1]]
+    d._c = None
+    return lv[0][2]
+
+
+def chained_oracle(mats, x0, out_table):
+    """Composes the oracle's GEMVs level by level over the stacked level
+    matrices `mats`; each level output is rounded to float32, the type the
+    step stores it in."""
+    x = x0
+    ys = []
+    for m in mats:
+        xin = x[: m.w.shape[1]]
+        ys.append((m, xin, ref.ternary_gemv(m.w, m.scale, xin)))
+        x = ys[-1][2].astype(np.float32)
+    h = x[: out_table.q.shape[1]]
+    return ys, h, ref.int8_logits(out_table.q, out_table.scale, h)
+
+
+@pytest.mark.parametrize("size", ["small", "8b"])
+@pytest.mark.parametrize("schedule", SCHEDULES[:2], ids=SCHED_IDS[:2])
+def test_chained_levels_see_previous_outputs(schedule, size):
+    """The ordered schedules must honour level dependencies: level L+1 reads
+    what level L wrote in the same step.  Two steps with different first
+    inputs also rule out stale cached activations from the step before."""
+    n_layers, shapes, vocab, hidden = (3, SMALL, 1000, 256) if size == "small" else (2, None, synth.VOCAB, synth.HIDDEN)
+    wl = build_step(n_layers=n_layers, shapes=shapes, vocab=vocab, hidden=hidden, with_logits=True, schedule=schedule)
+    x0 = chain_levels(wl)
+    pwg.step_plan(wl.desc)
+    x0_host = x0.cpu().numpy().copy()
+    layers = [synth.layer(synth.W_STEP, layer, shapes) for layer in range(n_layers)]
+    mats = [synth.stacked(lm, members) for lm in layers for _, members, _ in synth.LEVELS]
+    del layers
+    token_in = wl.token0
+    for step, factor in enumerate((1.0, -0.5)):
+        x0.copy_(torch.from_numpy(x0_host * np.float32(factor)))   # exact scaling
+        print(f"chained step {step} schedule {schedule} size {size}", flush=True)
+        pwg.decode_step_weights(wl.desc)
+        torch.cuda.synchronize()
+        pwg.step_status(wl.desc)
+        out = outputs(wl)
+        ys, h, lr = chained_oracle(mats, x0_host * np.float32(factor), wl.out_table)
+        for i, ((m, xin, yr), y) in enumerate(zip(ys, out["levels"])):
+            assert_gemv(y, yr, ref.ternary_gemv_magnitude(m.w, m.scale, xin), f"step {step} level {i}")
+        assert_gemv(out["logits"], lr, ref.int8_logits_magnitude(wl.out_table.q, wl.out_table.scale, h), "logits")
+        assert token_ok(out["token"], lr)
+        er, _, _ = ref.embed_gather(wl.emb_table.q, wl.emb_table.scale, [token_in])
+        assert np.array_equal(out["emb_row"], er[0])
+        token_in = out["token"]
