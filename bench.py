@@ -12,10 +12,13 @@ weights we did not train": identity is checked before any timing):
   1. build the seeded synthetic workload and upload it;
   2. parity: sampled rows of every level, the full logits' argmax and the
      embedding row against the CPU oracle; abort on any failure;
-  3. warm up W graph replays, time K replays (HIP events on the replay stream);
-  4. the same for the levels schedule (one kernel per level) and for a null
-     graph with as many empty kernels, to split launch/dependency overhead
-     from DRAM time;
+  3. warm up W graph replays, time K replays (HIP events on the replay stream)
+     of the timed schedule: by default the stream schedule, which computes
+     the step over its fixed per-level inputs with no waits between levels;
+  4. the same for the other schedules (the ordered persistent kernel, with a
+     device-wide barrier between levels as a chained step needs, and one
+     kernel per level) and for a null graph with as many empty kernels, to
+     split dependency and launch overhead from DRAM time;
   5. the oracle timed on a bounded sample of the same workload (rank 0).
 Prints one JSON line.
 """
@@ -40,7 +43,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=256)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--schedule", choices=["persistent", "levels", "stream"], default="persistent")
+    p.add_argument("--schedule", choices=["stream", "persistent", "levels"], default="stream",
+                   help="timed schedule: stream (the step over its fixed level inputs, no dependency waits), "
+                        "persistent (ordered: a device-wide barrier between levels, as a chained step needs) or "
+                        "levels (one kernel per level); the other two are timed alongside")
     p.add_argument("--layers", type=int, default=36)
     p.add_argument("--no-compare", action="store_true", help="skip the levels-schedule and null-graph timings")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -188,6 +194,10 @@ def main():
     if args.counters:
         wl.desc.schedule = schedule
         wl.desc._c = None
+        need = pwg.step_workspace_bytes(wl.desc)
+        if wl.desc.workspace.numel() < need:
+            wl.desc.workspace = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+            wl.desc._c = None
         pwg.step_plan(wl.desc, stream=stream)
         with torch.cuda.stream(stream):
             for _ in range(3):
@@ -203,6 +213,10 @@ def main():
     def run(desc_schedule):
         wl.desc.schedule = desc_schedule
         wl.desc._c = None
+        need = pwg.step_workspace_bytes(wl.desc)
+        if wl.desc.workspace.numel() < need:
+            wl.desc.workspace = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+            wl.desc._c = None
         pwg.step_plan(wl.desc, stream=stream)
         return lambda: pwg.decode_step_weights(wl.desc, stream=stream)
 
@@ -224,7 +238,7 @@ def main():
     ms = time_graph(graph, stream, args.steps, args.warmup)
     pwg.step_status(wl.desc, stream=stream)
     log(f"{args.schedule}: {ms * 1e3:.1f} us/step")
-    kernels_per_step = 1 if schedule == pwg.SCHEDULE_PERSISTENT else len(wl.desc.levels) + 3
+    kernels_per_step = {pwg.SCHEDULE_PERSISTENT: 1, pwg.SCHEDULE_STREAM: 2}.get(schedule, len(wl.desc.levels) + 3)
 
     extra = {}
     if not args.no_compare:
@@ -283,19 +297,23 @@ def main():
     }
     result.update(extra)
 
-    # roofline of the dominant kernel
-    if schedule == pwg.SCHEDULE_PERSISTENT:
+    # roofline of the dominant kernel: the step kernel moves every
+    # algorithmic byte of the step; its time is the timed replay's (for the
+    # stream schedule that includes the input-conversion kernel before it,
+    # a few microseconds)
+    if schedule in (pwg.SCHEDULE_PERSISTENT, pwg.SCHEDULE_STREAM):
         traffic = None
         tfile = os.path.join(ROOT, "profiles", "step_kernel_traffic.json")
         if os.path.exists(tfile):
             t = json.load(open(tfile))
-            if t.get("kernel_source_sha") == kernel_source_sha() and t.get("layers") == args.layers:
+            if (t.get("kernel_source_sha") == kernel_source_sha() and t.get("layers") == args.layers
+                    and t.get("schedule") == args.schedule):
                 traffic = t.get("hbm_bytes_per_launch")
+        kname = ("step_kernel<ordered> (whole step, one launch)" if schedule == pwg.SCHEDULE_PERSISTENT else
+                 "step_kernel<stream> (whole step; timed with its input-conversion kernel)")
         result["roofline"] = {"bound": "hbm", "achieved": achieved_bps / 1e9, "peak": PEAK_HBM_BPS / 1e9,
                               "unit": "GB/s", "frac": achieved_bps / PEAK_HBM_BPS, "traffic": traffic,
-                              "kernel": "step_kernel (whole step, one launch)",
-                              "per_launch_bytes": step_bytes,
-                              "avg_launch_us": ms * 1e3}
+                              "kernel": kname, "per_launch_bytes": step_bytes, "avg_launch_us": ms * 1e3}
     result["kernel_source_sha"] = kernel_source_sha()
 
     # 5. oracle CPU baseline (bounded sample)

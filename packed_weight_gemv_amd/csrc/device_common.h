@@ -164,12 +164,16 @@ __device__ __forceinline__ void t2_x_convert(const T2XRegs<G>& xr, int cols, uns
   __syncthreads();
 }
 
-// Converts activations staged raw (float32) in LDS into limb planes; all
-// threads of the block take part (groups g = threadIdx.x + i * blockDim.x).
-__device__ __forceinline__ void t2_convert_staged(const float* xs, int cols, unsigned* lds, int* lds_e) {
+// Converts groups g = t, t + nt, t + 2 nt, ... of x (float32, any address
+// space) into limb planes and chunk exponents (any address space).  No block
+// synchronisation.  A chunk's four groups must be converted by four
+// consecutive lanes that are active together: t and nt are multiples of 4
+// apart within a wave (nt a multiple of 64 and t the lane-linear index).
+__device__ __forceinline__ void t2_convert_groups(const float* xs, int cols, unsigned* planes, int* plane_e, int t,
+                                                  int nt) {
   const int ngroups = cols >> 4;
-  for (int base = 0; base < ngroups; base += blockDim.x) {
-    const int g = base + threadIdx.x;
+  for (int base = 0; base < ngroups; base += nt) {
+    const int g = base + t;
     if (g < ngroups) {
       float4 v[4];
 #pragma unroll
@@ -189,13 +193,19 @@ __device__ __forceinline__ void t2_convert_staged(const float* xs, int cols, uns
       }
       unsigned out[12];
       t2_limbs_from_u(u, out);
-      u32x4* dst = reinterpret_cast<u32x4*>(lds + (g >> 2) * kT2ChunkDwords + (g & 3) * 12);
+      u32x4* dst = reinterpret_cast<u32x4*>(planes + (g >> 2) * kT2ChunkDwords + (g & 3) * 12);
       dst[0] = u32x4{out[0], out[1], out[2], out[3]};
       dst[1] = u32x4{out[4], out[5], out[6], out[7]};
       dst[2] = u32x4{out[8], out[9], out[10], out[11]};
-      if ((g & 3) == 0) lds_e[g >> 2] = E;
+      if ((g & 3) == 0) plane_e[g >> 2] = E;
     }
   }
+}
+
+// Converts activations staged raw (float32) in LDS into limb planes; all
+// threads of the block take part, then the block synchronises.
+__device__ __forceinline__ void t2_convert_staged(const float* xs, int cols, unsigned* lds, int* lds_e) {
+  t2_convert_groups(xs, cols, lds, lds_e, static_cast<int>(threadIdx.x), static_cast<int>(blockDim.x));
   __syncthreads();
 }
 
@@ -289,10 +299,21 @@ __device__ __forceinline__ void i8_x_convert(const I8XRegs<G>& xr, int cols, uns
   __syncthreads();
 }
 
-__device__ __forceinline__ void i8_prepare_x(const float* __restrict__ h, int cols, unsigned* lds, int* lds_e) {
+// Converts groups g = t, t + nt, ... of h (any address space) into int8
+// limb planes; a wave-uniform trip count, no block synchronisation (same
+// lane requirements as t2_convert_groups).
+__device__ __forceinline__ void i8_convert_groups(const float* h, int cols, unsigned* planes, int* plane_e, int t,
+                                                  int nt) {
   const int ngroups = cols >> 2;
   const float4* h4 = reinterpret_cast<const float4*>(h);
-  for (int g = threadIdx.x; g < ngroups; g += blockDim.x) i8_convert_group(h4[g], g, lds, lds_e);
+  for (int base = 0; base < ngroups; base += nt) {
+    const int g = base + t;
+    if (g < ngroups) i8_convert_group(h4[g], g, planes, plane_e);
+  }
+}
+
+__device__ __forceinline__ void i8_prepare_x(const float* __restrict__ h, int cols, unsigned* lds, int* lds_e) {
+  i8_convert_groups(h, cols, lds, lds_e, static_cast<int>(threadIdx.x), static_cast<int>(blockDim.x));
   __syncthreads();
 }
 

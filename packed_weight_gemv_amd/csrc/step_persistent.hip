@@ -23,6 +23,7 @@
 // status word and leaves, so a broken schedule ends with an error, not a hang.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <vector>
 
 #include "device_common.h"
@@ -53,10 +54,20 @@ struct DevLevel {
   const float* scale;
   const float* x;
   float* y;
+  unsigned* planes;  // limb planes of x in the workspace (stream schedule)
   int rows;
   int cols;
   int nchunks;  // cols / 64
   int c;        // chunks per lane
+};
+
+// Stream schedule: a contiguous row range of one level (n_levels: the
+// vocabulary), part of one workgroup's share of the step.
+struct Seg {
+  int level;
+  int row_begin;
+  int row_end;
+  int pad;
 };
 
 // Device-side plan, written by pwg_step_plan into the workspace.  It is
@@ -83,6 +94,10 @@ struct alignas(256) Plan {
   float* emb_scale_out;
   float4* emb_deq_out;
   float* logits_out;
+  unsigned* vocab_planes;  // int8 limb planes of h in the workspace (stream schedule)
+  const Seg* segs;         // stream schedule: workgroup b's segments are segs[b * seg_stride ...]
+  const int* seg_count;    // stream schedule: segments per workgroup
+  int seg_stride;
   // offsets (bytes from the plan) of the state words, barrier words, partial keys and level table
   unsigned long long state_off, counters_off, flags_off, partials_off, levels_off, calib_off;
 };
@@ -175,7 +190,8 @@ struct Barrier {
         if (plan->mode == kBarrierL2) {
           if (lane < 8 && ((plan->xcd_mask >> lane) & 1u)) ok = reached(ld_sc(&flags[xcd * 64 + lane]), epoch);
         } else {
-          for (unsigned b = lane; b < plan->grid; b += 64) ok = ok && reached(ld_sc(&flags[kReplicas * 64 + b]), epoch);
+          for (unsigned b0 = 0; b0 < plan->grid; b0 += 64)  // wave-uniform trip count
+            if (b0 + lane < plan->grid) ok = ok && reached(ld_sc(&flags[kReplicas * 64 + b0 + lane]), epoch);
         }
         if (__all(ok)) break;
         // the real-time counter is a scalar read, so `late` is uniform
@@ -197,16 +213,33 @@ struct Barrier {
 // ----------------------------------------------------------------- streaming
 // LDS budget of the step kernel (bytes).
 constexpr int kComputeWaves = kWpb - 1;                 // waves 1..7; wave 0 is the control wave
-constexpr int kRingSlots = 8;                           // 1 KiB slots per compute wave
+constexpr int kRingOrdered = 8;                         // 1 KiB ring slots per compute wave: ordered
+constexpr int kRingStream = 16;                         // and stream schedule
 constexpr int kSlotBytes = 1024;                        // 64 lanes x 16 bytes
 constexpr int kMaxT2Cols = 64 * 64 * kMaxC;             // 12288
 constexpr int kMaxWgRows = 640;                         // rows of one level per workgroup
-constexpr size_t kRingBytes = static_cast<size_t>(kComputeWaves) * kRingSlots * kSlotBytes;
+constexpr size_t kRingBytes = static_cast<size_t>(kComputeWaves) * kRingOrdered * kSlotBytes;        // ordered
+constexpr size_t kRingBytesStream = static_cast<size_t>(kComputeWaves) * kRingStream * kSlotBytes;  // stream
 constexpr size_t kStageBytes = kMaxT2Cols * 4;
 constexpr size_t kPlaneBytes = static_cast<size_t>(kMaxT2Cols / 64) * (kT2ChunkDwords + 1) * 4;
 constexpr size_t kScaleBytes = 2 * kMaxWgRows * 4;
 constexpr size_t kOutBytes = kMaxWgRows * 4;              // a level's outputs of the workgroup (ordered)
-constexpr size_t kStepSmem = kRingBytes + kStageBytes + kPlaneBytes + kScaleBytes + kOutBytes;
+// Ordered: ring | raw input | planes | 2 x scales | outputs.
+// Stream:  ring | planes (filled by copies of pre-converted planes).
+constexpr size_t kOrderedSmem = kRingBytes + kStageBytes + kPlaneBytes + kScaleBytes + kOutBytes;
+constexpr size_t kStreamSmem = kRingBytesStream + kPlaneBytes;
+constexpr size_t kStepSmem = kOrderedSmem > kStreamSmem ? kOrderedSmem : kStreamSmem;
+static_assert(kT2ChunkDwords * 4 * (kMaxT2Cols / 64) % 16 == 0, "plane copies move 16-byte units");
+
+// Bytes of the limb planes (with the chunk exponents) of a ternary level's
+// input and of the output projection's input; multiples of 16.
+__host__ __device__ constexpr size_t t2_plane_bytes(int cols) {
+  return (static_cast<size_t>(cols / 64) * (kT2ChunkDwords + 1) * 4 + 15) / 16 * 16;
+}
+__host__ __device__ constexpr size_t i8_plane_bytes(int cols) {
+  return (static_cast<size_t>(cols / 16) * (kI8ChunkDwords + 1) * 4 + 15) / 16 * 16;
+}
+static_assert(t2_plane_bytes(kMaxT2Cols) <= kPlaneBytes, "plane buffer");
 
 #define PWG_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -219,35 +252,62 @@ __device__ __forceinline__ void dma4(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, PWG_LDS(lds), 4, 0, 0);
 }
 
-// Waits until at most n of this wave's vector-memory operations are
-// outstanding (n >= kRingSlots waits for kRingSlots - 1: waiting longer is
-// always safe).  Loads retire in order, so when every load issued after a
-// given one may still be pending, that one has completed.  The count is an
-// immediate of the instruction, hence the branches; n is wave-uniform and
-// is tested from the most common value (a full ring) down.
-__device__ __forceinline__ void wait_vm_le(unsigned n) {
-#define PWG_VM(k) __builtin_amdgcn_s_waitcnt(((k) & 15) | (((k) >> 4) << 14) | (7 << 4) | (15 << 8))
-  static_assert(kRingSlots == 8, "wait_vm_le covers counts up to 7");
-  if (n >= 7) { PWG_VM(7); }
-  else if (n == 6) { PWG_VM(6); }
-  else if (n == 5) { PWG_VM(5); }
-  else if (n == 4) { PWG_VM(4); }
-  else if (n == 3) { PWG_VM(3); }
-  else if (n == 2) { PWG_VM(2); }
-  else if (n == 1) { PWG_VM(1); }
-  else { PWG_VM(0); }
-#undef PWG_VM
+// Stores v to an LDS word after this wave's earlier LDS reads have
+// completed, without waiting for its outstanding global-to-LDS copies.  The
+// compiler puts a wait for every outstanding copy before any LDS store of a
+// wave that has issued such copies (it cannot tell where they land), so the
+// store is written out here; the flag words are never a copy's destination.
+// LDS operations of a wave complete in order, so the extra one the compiler
+// does not count only makes its later LDS-counter waits longer.
+__device__ __forceinline__ void lds_publish(int* p, int v) {
+  const unsigned addr =
+      static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) int*)p));
+  asm volatile("s_waitcnt lgkmcnt(0)\n\tds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 
-// Rows of level `li` owned by workgroup `b` of `nb`: [R0, R1); compute wave
-// k (0..6) of the workgroup owns [r0, r1) inside it.
+// Waits until at most n of this wave's vector-memory operations are
+// outstanding (n >= 15 waits for 15: waiting longer is always safe).  Loads
+// retire in order, so when every load issued after a given one may still be
+// pending, that one has completed.  The count is an immediate of the
+// instruction, hence the branches; n is wave-uniform.
+__device__ __forceinline__ void wait_vm_le(unsigned n) {
+#define PWG_VM(k) __builtin_amdgcn_s_waitcnt(((k) & 15) | (((k) >> 4) << 14) | (7 << 4) | (15 << 8))
+  switch (n < 15 ? n : 15) {
+    case 15: PWG_VM(15); break;
+    case 14: PWG_VM(14); break;
+    case 13: PWG_VM(13); break;
+    case 12: PWG_VM(12); break;
+    case 11: PWG_VM(11); break;
+    case 10: PWG_VM(10); break;
+    case 9: PWG_VM(9); break;
+    case 8: PWG_VM(8); break;
+    case 7: PWG_VM(7); break;
+    case 6: PWG_VM(6); break;
+    case 5: PWG_VM(5); break;
+    case 4: PWG_VM(4); break;
+    case 3: PWG_VM(3); break;
+    case 2: PWG_VM(2); break;
+    case 1: PWG_VM(1); break;
+    default: PWG_VM(0); break;
+  }
+#undef PWG_VM
+}
+// Waits only for this wave's LDS (and scalar-memory) operations.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8)); }
+
+// Rows of a level owned by workgroup `b` of `nb`: [R0, R1).  Compute wave k
+// takes every kComputeWaves-th row of them, from R0 + q on, with q = (k + li)
+// mod kComputeWaves: the waves of a workgroup sweep its contiguous block of
+// rows together (one sequential stream per workgroup), and the waves whose
+// share is one row longer change from level to level.
 __device__ __forceinline__ void wg_rows(long rows, unsigned b, unsigned nb, long& R0, long& R1) {
   R0 = static_cast<long>(b) * rows / nb;
   R1 = static_cast<long>(b + 1) * rows / nb;
 }
-__device__ __forceinline__ void wave_rows(long R0, long R1, unsigned k, long& r0, long& r1) {
-  r0 = R0 + static_cast<long>(k) * (R1 - R0) / kComputeWaves;
-  r1 = R0 + static_cast<long>(k + 1) * (R1 - R0) / kComputeWaves;
+__device__ __forceinline__ void wave_rows(long R0, long R1, unsigned k, unsigned li, long& first, int& count) {
+  const unsigned q = (k + li) % kComputeWaves;
+  first = R0 + q;
+  count = R1 - R0 > q ? static_cast<int>((R1 - R0 - q + kComputeWaves - 1) / kComputeWaves) : 0;
 }
 
 // Wave-uniform copies (the values are the same in every lane; this keeps
@@ -262,10 +322,29 @@ __device__ __forceinline__ T* uni(T* p) {
   return reinterpret_cast<T*>((static_cast<unsigned long long>(hi) << 32) | lo);
 }
 
-// The producer half of a compute wave: walks the wave's rows of every level
-// (then of the vocabulary table) and copies each row's slots into the ring.
+// Level and workgroup row range [R0, R1) of work item `item`: level `item`
+// split over the workgroups (ordered), or the workgroup's segment `item`.
+__device__ __forceinline__ void item_rows(const Seg* segs, unsigned item, int vocab, const DevLevel* levels,
+                                          unsigned n_levels, unsigned nwg, unsigned& level, long& R0, long& R1) {
+  if (segs) {
+    const Seg& sg = segs[item];
+    level = uni(static_cast<unsigned>(sg.level));
+    R0 = uni(sg.row_begin);
+    R1 = uni(sg.row_end);
+  } else {
+    level = item;
+    wg_rows(item < n_levels ? uni(levels[item].rows) : vocab, blockIdx.x, nwg, R0, R1);
+  }
+}
+
+// The producer half of a compute wave: walks the wave's rows of every work
+// item and copies each row's slots into its ring of RS slots.  All state is
+// wave-uniform.
+template <int RS>
 struct Producer {
   const DevLevel* levels;
+  const Seg* segs;    // this workgroup's segments (stream) or null (ordered: items are levels)
+  unsigned n_items;
   unsigned n_levels;
   int vocab, hidden;
   const u32x4* out_table;
@@ -273,92 +352,128 @@ struct Producer {
   unsigned k;         // compute-wave index 0..6
   unsigned lane;
   unsigned issued;    // slots issued (one DMA each)
-  unsigned level;     // level being produced (n_levels = vocabulary, n_levels + 1 = done)
-  int row, row_end;
+  unsigned item;      // item being produced (n_items = done)
+  int rows_left;      // rows of the item still to issue, the current one included
   int chunk, chunks_per_row, nchunks;
-  const u32x4* base;
+  const u32x4* rowp;  // start of the current row
   unsigned char* ring;
 
-  __device__ __forceinline__ void enter_level() {
-    level = uni(level);
-    while (level <= n_levels) {
-      int rows;
+  // Moves to the first item, from `item` on, in which this wave has rows.
+  __device__ __forceinline__ void enter_item() {
+    item = uni(item);
+    while (item < n_items) {
+      unsigned level;
+      long R0, R1;
+      item_rows(segs, item, vocab, levels, n_levels, nwg, level, R0, R1);
+      const u32x4* base;
       if (level < n_levels) {
-        rows = uni(levels[level].rows);
         nchunks = uni(levels[level].nchunks);
         chunks_per_row = uni(levels[level].c);
         base = uni(levels[level].w);
       } else {
-        rows = vocab;
         nchunks = hidden >> 4;
         chunks_per_row = (nchunks + 63) / 64;
         base = out_table;
       }
-      long R0, R1, r0, r1;
-      wg_rows(rows, blockIdx.x, nwg, R0, R1);
-      wave_rows(R0, R1, k, r0, r1);
-      row = uni(static_cast<int>(r0));
-      row_end = uni(static_cast<int>(r1));
+      long first;
+      int count;
+      wave_rows(R0, R1, k, item, first, count);
+      rows_left = uni(count);
+      rowp = uni(base + first * nchunks);
       chunk = 0;
-      if (row < row_end) return;
-      level = uni(level + 1);
+      if (rows_left > 0) return;
+      item = uni(item + 1);
     }
   }
 
-  // Issues one slot if the ring has room (issued - consumed < kRingSlots).
-  __device__ __forceinline__ bool issue(unsigned consumed) {
-    if (uni(level) > n_levels || uni(issued) - uni(consumed) >= static_cast<unsigned>(kRingSlots)) return false;
+  __device__ __forceinline__ bool active() const { return item < n_items; }
+
+  // Issues the next slot (the caller checks active() and that the ring has room).
+  __device__ __forceinline__ void issue() {
     unsigned c = lane + 64u * static_cast<unsigned>(chunk);
     c = c < static_cast<unsigned>(nchunks) ? c : static_cast<unsigned>(nchunks - 1);
-    dma16(base + static_cast<long>(row) * nchunks + c, ring + (issued % kRingSlots) * kSlotBytes);
+    dma16(rowp + c, ring + (issued % RS) * kSlotBytes);
     issued = uni(issued + 1);
     chunk = uni(chunk + 1);
     if (chunk == chunks_per_row) {
       chunk = 0;
-      row = uni(row + 1);
-      if (row == row_end) {
-        level = uni(level + 1);
-        enter_level();
+      rowp = uni(rowp + kComputeWaves * nchunks);
+      rows_left = uni(rows_left - 1);
+      if (rows_left == 0) {
+        item = uni(item + 1);
+        enter_item();
       }
     }
-    return true;
   }
+
+  // Refills the ring after the consumer freed slots.
   __device__ __forceinline__ void fill(unsigned consumed) {
-    while (issue(consumed)) {
-    }
+    while (active() && uni(issued) - uni(consumed) < static_cast<unsigned>(RS)) issue();
   }
 };
 
-// The consumer half: takes the next row's C slots out of the ring.
-template <int C>
-__device__ __forceinline__ void take_row(Producer& pr, unsigned& consumed, const unsigned char* ring, unsigned lane,
+// The consumer half: takes the next row's C slots out of the ring, then
+// refills the ring (after the LDS reads have returned, so the slots may be
+// overwritten) before the caller computes on them.
+template <int C, int RS>
+__device__ __forceinline__ void take_row(Producer<RS>& pr, unsigned& consumed, const unsigned char* ring, unsigned lane,
                                          u32x4 (&w)[C]) {
-  // the row's last slot has index consumed + C - 1; everything issued after it may still be in flight
-  wait_vm_le(pr.issued - consumed - C);
+  // the row's last slot has index consumed + C - 1; everything issued after
+  // it may still be in flight (with a full ring that is RS - C slots)
+  const unsigned ahead = uni(pr.issued) - uni(consumed);
+  if (ahead == static_cast<unsigned>(RS)) {
+    __builtin_amdgcn_s_waitcnt(((RS - C) & 15) | (((RS - C) >> 4) << 14) | (7 << 4) | (15 << 8));
+  } else {
+    wait_vm_le(ahead - C);
+  }
 #pragma unroll
   for (int c = 0; c < C; ++c)
-    w[c] = *reinterpret_cast<const u32x4*>(ring + ((consumed + c) % kRingSlots) * kSlotBytes + lane * 16);
-  consumed += C;
+    w[c] = *reinterpret_cast<const u32x4*>(ring + ((consumed + c) % RS) * kSlotBytes + lane * 16);
+  consumed = uni(consumed + C);
+  wait_lgkm0();
+  pr.fill(consumed);
+}
+
+// Row scale for the tile row this lane stores (tile row row_of<4>(lane >> 4),
+// row index i + that).  kConst: `scales` is the level's scale array in global
+// memory, constant during the step, read with scalar loads (they do not wait
+// behind the ring's outstanding copies) before the lanes diverge; otherwise
+// it is the workgroup's LDS copy starting at row R0.
+template <bool kConst>
+__device__ __forceinline__ float tile_scale(const float* scales, long first, int i, int count, long R0, unsigned lane) {
+  const int t = row_of<4>(static_cast<int>(lane >> 4));
+  if constexpr (kConst) {
+    typedef const __attribute__((address_space(4))) float const_float;
+    const_float* cs = (const_float*)scales;  // address-space cast (constant memory)
+    float su[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) su[u] = i + u < count ? cs[first + static_cast<long>(kComputeWaves) * (i + u)] : 0.f;
+    return t == 0 ? su[0] : t == 1 ? su[1] : t == 2 ? su[2] : su[3];
+  } else {
+    const int iu = i + t < count ? i + t : i;
+    return scales[first + static_cast<long>(kComputeWaves) * iu - R0];
+  }
 }
 
 // Consumes the wave's rows of one ternary level (C chunks of 64 words per
 // lane and row), four rows per tile reduction.  Results go to y, or to the
 // workgroup's LDS output buffer when `out_buf` is set.
-template <int C>
-__device__ __forceinline__ void t2_consume_level(const DevLevel& L, long r0, long r1, long R0, const float* scales,
-                                                 unsigned lane, Producer& pr, unsigned& consumed,
+template <int C, bool kConst, int RS>
+__device__ __forceinline__ void t2_consume_level(const DevLevel& L, long first, int count, long R0, const float* scales,
+                                                 unsigned lane, Producer<RS>& pr, unsigned& consumed,
                                                  const unsigned char* ring, const unsigned* planes,
-                                                 const int* plane_e, float* out_buf) {
+                                                 const int* plane_e, float* out_buf, int* init_flag, int init_val) {
   T2Lane<C> st;
   t2_lane_init<C>(st, planes, plane_e, L.nchunks, lane);
-  for (long r = r0; r < r1; r += 4) {
+  if (init_flag) lds_publish(init_flag, init_val);  // the planes buffer may be refilled
+  for (int i = 0; i < count; i += 4) {
     float p[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       p[u] = 0.f;
-      if (r + u < r1) {
+      if (i + u < count) {
         u32x4 w[C];
-        take_row<C>(pr, consumed, ring, lane, w);
+        take_row<C, RS>(pr, consumed, ring, lane, w);
 #pragma unroll
         for (int c = 0; c < C; ++c) {
           t2_chunk_dot(w[c], st.X[c], st.acc[c]);
@@ -367,22 +482,25 @@ __device__ __forceinline__ void t2_consume_level(const DevLevel& L, long r0, lon
           st.prev[c] = comb;
           p[u] += ldexpf(static_cast<float>(v), st.Ec[c]);
         }
-        pr.fill(consumed);  // the row's slots were read (their values are in use above)
       }
     }
-    const long row = r + row_of<4>(static_cast<int>(lane >> 4));
+    const int iu = i + row_of<4>(static_cast<int>(lane >> 4));
+    const long row = first + static_cast<long>(kComputeWaves) * iu;
+    const float sc = tile_scale<kConst>(scales, first, i, count, R0, lane);
     const float total = tile_reduce<4>(p);
-    if ((lane & 15u) == 0u && row < r1) {
-      const float v = scales[row - R0] * total;
+    if ((lane & 15u) == 0u && iu < count) {
+      const float v = sc * total;
       if (out_buf) out_buf[row - R0] = v;  // published by the control wave
       else L.y[row] = v;
     }
   }
 }
 
-__device__ __forceinline__ void i8_consume_level(const Plan& P, long r0, long r1, long R0, const float* scales, unsigned lane,
-                                 Producer& pr, unsigned& consumed, const unsigned char* ring,
-                                 const unsigned* planes, const int* plane_e, float& best, unsigned& best_idx) {
+template <bool kConst, int RS>
+__device__ __forceinline__ void i8_consume_level(const Plan& P, long first, int count, long R0, const float* scales, unsigned lane,
+                                 Producer<RS>& pr, unsigned& consumed, const unsigned char* ring,
+                                 const unsigned* planes, const int* plane_e, float& best, unsigned& best_idx,
+                                 int* init_flag, int init_val) {
   const int nchunks = P.hidden >> 4;
   unsigned H[kMaxI8C][12];
   int Ec[kMaxI8C];
@@ -398,20 +516,28 @@ __device__ __forceinline__ void i8_consume_level(const Plan& P, long r0, long r1
       H[c][4 * q] = v.x; H[c][4 * q + 1] = v.y; H[c][4 * q + 2] = v.z; H[c][4 * q + 3] = v.w;
     }
   }
+  if (init_flag) lds_publish(init_flag, init_val);  // the planes buffer may be refilled
   const int cpr = (nchunks + 63) / 64;  // slots per row (4 for hidden = 4096)
-  for (long r = r0; r < r1; r += 4) {
+  for (int i = 0; i < count; i += 4) {
     float p[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       p[u] = 0.f;
-      if (r + u < r1) {
+      if (i + u < count) {
         u32x4 q[kMaxI8C];
-        wait_vm_le(pr.issued - consumed - cpr);
+        const unsigned ahead = uni(pr.issued) - uni(consumed);
+        if (ahead == static_cast<unsigned>(RS) && cpr == kMaxI8C) {
+          __builtin_amdgcn_s_waitcnt(((RS - kMaxI8C) & 15) | (((RS - kMaxI8C) >> 4) << 14) | (7 << 4) | (15 << 8));
+        } else {
+          wait_vm_le(ahead - cpr);
+        }
 #pragma unroll
         for (int c = 0; c < kMaxI8C; ++c)
-          q[c] = c < cpr ? *reinterpret_cast<const u32x4*>(ring + ((consumed + c) % kRingSlots) * kSlotBytes + lane * 16)
+          q[c] = c < cpr ? *reinterpret_cast<const u32x4*>(ring + ((consumed + c) % RS) * kSlotBytes + lane * 16)
                          : u32x4{0u, 0u, 0u, 0u};
-        consumed += cpr;
+        consumed = uni(consumed + cpr);
+        wait_lgkm0();
+        pr.fill(consumed);
 #pragma unroll
         for (int c = 0; c < kMaxI8C; ++c) {
           int a0 = 0, a1 = 0, a2 = 0;
@@ -426,13 +552,14 @@ __device__ __forceinline__ void i8_consume_level(const Plan& P, long r0, long r1
           const float pc = fmaf(static_cast<float>(a2), 65536.0f, fmaf(static_cast<float>(a1), 256.0f, static_cast<float>(a0)));
           p[u] += ldexpf(pc, Ec[c]);
         }
-        pr.fill(consumed);
       }
     }
-    const long row = r + row_of<4>(static_cast<int>(lane >> 4));
+    const int iu = i + row_of<4>(static_cast<int>(lane >> 4));
+    const long row = first + static_cast<long>(kComputeWaves) * iu;
+    const float sc = tile_scale<kConst>(scales, first, i, count, R0, lane);
     const float total = tile_reduce<4>(p);
-    if ((lane & 15u) == 0u && row < r1) {
-      const float logit = scales[row - R0] * total;
+    if ((lane & 15u) == 0u && iu < count) {
+      const float logit = sc * total;
       if (P.logits_out) P.logits_out[row] = logit;
       if (logit > best) {  // rows of one lane ascend: ties keep the lower index
         best = logit;
@@ -465,6 +592,71 @@ __device__ __forceinline__ void stage_scales(const Plan& P, const DevLevel* leve
     if (o + lane < R1) dma4(s + o + lane, scales + (o - R0));
 }
 
+// Control wave: copies level `li`'s pre-converted limb planes (li ==
+// n_levels: those of h) into an LDS plane buffer.
+__device__ __forceinline__ void stage_planes(const Plan& P, const DevLevel* levels, unsigned li, unsigned lane,
+                                             unsigned* buf) {
+  const unsigned char* src = reinterpret_cast<const unsigned char*>(li < P.n_levels ? levels[li].planes : P.vocab_planes);
+  const int bytes = static_cast<int>(li < P.n_levels ? t2_plane_bytes(levels[li].cols) : i8_plane_bytes(P.hidden));
+  unsigned char* dst = reinterpret_cast<unsigned char*>(buf);
+  for (int o = 0; o < bytes; o += 1024)
+    if (o + 16 * static_cast<int>(lane) < bytes) dma16(src + o + 16 * lane, dst + o);
+}
+
+// Embedding row of the previous token (workgroup 0, control wave).
+__device__ __forceinline__ void embed_row(const Plan& P, unsigned lane) {
+  const int id = *P.token_in;
+  const bool ok = id >= 0 && id < P.vocab;
+  const int nchunks = P.hidden >> 4;
+  const float s = ok ? P.emb_scale[id] : __builtin_nanf("");
+  if (lane == 0) *P.emb_scale_out = s;
+  // wave-uniform trip count: a loop whose exit differed between lanes would
+  // make everything the caller merges after this branch divergent
+  for (int c0 = 0; c0 < nchunks; c0 += 64) {
+    const int c = c0 + static_cast<int>(lane);
+    if (c < nchunks) {
+      const u32x4 v = ok ? P.emb_table[static_cast<size_t>(id) * nchunks + c] : u32x4{0u, 0u, 0u, 0u};
+      P.emb_row_out[c] = v;
+      if (P.emb_deq_out) {
+        const unsigned wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          P.emb_deq_out[4 * c + q] =
+              ok ? make_float4(static_cast<float>(static_cast<int8_t>(wd[q] & 0xFF)) * s,
+                               static_cast<float>(static_cast<int8_t>((wd[q] >> 8) & 0xFF)) * s,
+                               static_cast<float>(static_cast<int8_t>((wd[q] >> 16) & 0xFF)) * s,
+                               static_cast<float>(static_cast<int8_t>(wd[q] >> 24)) * s)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  }
+}
+
+// A compute wave's rows of work item `item` (level li, workgroup rows
+// [R0, R1)); planes: the level's input limbs in LDS.  kConst: `scales` is the
+// level's scale array in global memory, else the workgroup's LDS copy.
+template <bool kConst, int RS>
+__device__ __forceinline__ void consume_item(const Plan& P, const DevLevel* levels, unsigned li, unsigned item, long R0,
+                                             long R1, unsigned k, const float* scales, unsigned lane, Producer<RS>& pr,
+                                             unsigned& consumed, const unsigned char* ring, const unsigned* planes,
+                                             float* out_buf, float& best, unsigned& best_idx, int* init_flag) {
+  long first;
+  int count;
+  wave_rows(R0, R1, k, item, first, count);
+  if (li == P.n_levels) {
+    const int* plane_e = reinterpret_cast<const int*>(planes + (P.hidden >> 4) * kI8ChunkDwords);
+    i8_consume_level<kConst, RS>(P, first, count, R0, scales, lane, pr, consumed, ring, planes, plane_e, best, best_idx,
+                                 init_flag, static_cast<int>(item));
+    return;
+  }
+  const DevLevel& L = levels[li];
+  const int* plane_e = reinterpret_cast<const int*>(planes + L.nchunks * kT2ChunkDwords);
+  const int iv = static_cast<int>(item);
+  if (L.c == 1) t2_consume_level<1, kConst, RS>(L, first, count, R0, scales, lane, pr, consumed, ring, planes, plane_e, out_buf, init_flag, iv);
+  else if (L.c == 2) t2_consume_level<2, kConst, RS>(L, first, count, R0, scales, lane, pr, consumed, ring, planes, plane_e, out_buf, init_flag, iv);
+  else t2_consume_level<3, kConst, RS>(L, first, count, R0, scales, lane, pr, consumed, ring, planes, plane_e, out_buf, init_flag, iv);
+}
+
 template <bool kOrdered>
 __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restrict__ plan,
                                                             const DevLevel* __restrict__ levels, unsigned* state,
@@ -472,9 +664,14 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restric
                                                             unsigned long long* partials) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* ring_all = smem;
+  // ordered: raw input, one plane buffer, scales, outputs
   float* stage = reinterpret_cast<float*>(smem + kRingBytes);
-  unsigned* planes = reinterpret_cast<unsigned*>(smem + kRingBytes + kStageBytes);
-  float* scale_buf = reinterpret_cast<float*>(smem + kRingBytes + kStageBytes + kPlaneBytes);
+  // stream: (larger ring,) one plane buffer
+  unsigned* planes2 = reinterpret_cast<unsigned*>(smem + kRingBytesStream);
+  unsigned* planes1 = reinterpret_cast<unsigned*>(smem + kRingBytes + kStageBytes);
+  float* scale_buf = reinterpret_cast<float*>(smem + kRingBytes + (kOrdered ? kStageBytes + kPlaneBytes : 2 * kPlaneBytes));
+  float* out_buf = kOrdered ? reinterpret_cast<float*>(smem + kRingBytes + kStageBytes + kPlaneBytes + kScaleBytes)
+                            : nullptr;
 
   const Plan& P = *plan;
   Barrier bar;
@@ -489,10 +686,13 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restric
   const unsigned lane = threadIdx.x & 63u;
   const unsigned wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const unsigned k = wave - 1;  // compute-wave index (unused by wave 0)
-  unsigned char* ring = ring_all + static_cast<size_t>(wave == 0 ? 0 : k) * kRingSlots * kSlotBytes;
+  constexpr int RS = kOrdered ? kRingOrdered : kRingStream;
+  unsigned char* ring = ring_all + static_cast<size_t>(wave == 0 ? 0 : k) * RS * kSlotBytes;
 
-  Producer pr;
+  Producer<RS> pr;
   pr.levels = levels;
+  pr.segs = kOrdered ? nullptr : P.segs + static_cast<size_t>(blockIdx.x) * P.seg_stride;
+  pr.n_items = kOrdered ? P.n_levels + 1 : static_cast<unsigned>(uni(P.seg_count[blockIdx.x]));
   pr.n_levels = P.n_levels;
   pr.vocab = P.vocab;
   pr.hidden = P.hidden;
@@ -501,98 +701,121 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restric
   pr.k = k;
   pr.lane = lane;
   pr.issued = 0;
-  pr.level = 0;
+  pr.item = 0;
   pr.ring = ring;
   unsigned consumed = 0;
 
+  // Stream schedule: the waves synchronise through two LDS words instead of
+  // block barriers (see the level loop).
+  __shared__ int ready_level;            // highest segment whose planes are in LDS
+  __shared__ int done_level[kWpb];       // highest segment each compute wave has finished
+  if (!kOrdered) {
+    if (threadIdx.x == 0) ready_level = -1;
+    if (threadIdx.x < kWpb) done_level[threadIdx.x] = -1;
+    __syncthreads();
+  }
+
   if (wave == 0) {
-    stage_x(P, levels, 0, lane, stage);
-    stage_scales(P, levels, 0, lane, scale_buf);
-    // embedding row of the previous token (workgroup 0)
-    if (blockIdx.x == 0) {
-      const int id = *P.token_in;
-      const bool ok = id >= 0 && id < P.vocab;
-      const int nchunks = P.hidden >> 4;
-      const float s = ok ? P.emb_scale[id] : __builtin_nanf("");
-      if (lane == 0) *P.emb_scale_out = s;
-      // wave-uniform trip count: a loop whose exit differed between lanes
-      // would make everything merged after this branch divergent
-      for (int c0 = 0; c0 < nchunks; c0 += 64) {
-        const int c = c0 + static_cast<int>(lane);
-        if (c < nchunks) {
-          const u32x4 v = ok ? P.emb_table[static_cast<size_t>(id) * nchunks + c] : u32x4{0u, 0u, 0u, 0u};
-          P.emb_row_out[c] = v;
-          if (P.emb_deq_out) {
-            const unsigned wd[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              P.emb_deq_out[4 * c + q] =
-                  ok ? make_float4(static_cast<float>(static_cast<int8_t>(wd[q] & 0xFF)) * s,
-                                   static_cast<float>(static_cast<int8_t>((wd[q] >> 8) & 0xFF)) * s,
-                                   static_cast<float>(static_cast<int8_t>((wd[q] >> 16) & 0xFF)) * s,
-                                   static_cast<float>(static_cast<int8_t>(wd[q] >> 24)) * s)
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
-          }
-        }
-      }
+    if (kOrdered) {
+      stage_x(P, levels, 0, lane, stage);
+      stage_scales(P, levels, 0, lane, scale_buf);
+    } else if (pr.n_items > 0) {
+      stage_planes(P, levels, static_cast<unsigned>(pr.segs[0].level), lane, planes2);
     }
+    if (blockIdx.x == 0) embed_row(P, lane);
   } else {
-    pr.enter_level();
+    pr.enter_item();
     pr.fill(consumed);
   }
 
   float best = -__builtin_inff();
   unsigned best_idx = 0xFFFFFFFFu;
-  float* out_buf = kOrdered ? reinterpret_cast<float*>(smem + kRingBytes + kStageBytes + kPlaneBytes + kScaleBytes)
-                            : nullptr;
-  for (unsigned li = 0; li <= P.n_levels; ++li) {
-    // Ordered: level li starts once level li-1 is complete everywhere, and
-    // only then is its input read (it may be an output of level li-1).  The
-    // agent-scope acquire drops stale lines of the input from this XCD's L2.
-    if (kOrdered && li > 0) {
-      if (bar.wait(li - 1)) return;
+  if (kOrdered) {
+    for (unsigned li = 0; li <= P.n_levels; ++li) {
+      float* scales = scale_buf + (li & 1u) * kMaxWgRows;
+      const bool vocab = li == P.n_levels;
+      long R0, R1;
+      wg_rows(vocab ? P.vocab : levels[li].rows, blockIdx.x, P.grid, R0, R1);
+      // Level li starts once level li-1 is complete everywhere, and only
+      // then is its input read (it may be an output of level li-1).  The
+      // agent-scope acquire drops stale lines of the input from this XCD's L2.
+      if (li > 0) {
+        if (bar.wait(li - 1)) return;
+        if (wave == 0) {
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+          stage_x(P, levels, li, lane, stage);
+        }
+      }
+      if (wave == 0) __builtin_amdgcn_s_waitcnt(0);  // this level's input and scales have landed
+      __syncthreads();
+      const int cols = vocab ? P.hidden : levels[li].cols;
+      int* plane_e = reinterpret_cast<int*>(planes1 + (vocab ? (cols >> 4) * kI8ChunkDwords : (cols >> 6) * kT2ChunkDwords));
+      if (vocab) i8_prepare_x(stage, cols, planes1, plane_e);
+      else t2_convert_staged(stage, cols, planes1, plane_e);
+      // compute waves copy their limbs into registers inside the consume
+      // functions; the planes are rewritten only after the block barrier below
       if (wave == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        stage_x(P, levels, li, lane, stage);
-      }
-    }
-    if (wave == 0) __builtin_amdgcn_s_waitcnt(0);  // this level's input and scales have landed
-    __syncthreads();
-    float* scales = scale_buf + (li & 1u) * kMaxWgRows;
-    const bool vocab = li == P.n_levels;
-    const int cols = vocab ? P.hidden : levels[li].cols;
-    int* plane_e = reinterpret_cast<int*>(planes + (vocab ? (cols >> 4) * kI8ChunkDwords : (cols >> 6) * kT2ChunkDwords));
-    if (vocab) i8_prepare_x(stage, cols, planes, plane_e);
-    else t2_convert_staged(stage, cols, planes, plane_e);
-    // compute waves copy their limbs into registers inside the consume
-    // functions; the stage buffer is free again (the conversion ended with a
-    // block barrier), and the planes are rewritten only after the next one
-    long R0, R1;
-    wg_rows(vocab ? P.vocab : levels[li].rows, blockIdx.x, P.grid, R0, R1);
-    if (wave == 0) {
-      // Next level's constant inputs; without ordering also its activations
-      // (the levels are then independent by contract).
-      if (li < P.n_levels) {
-        stage_scales(P, levels, li + 1, lane, scale_buf + ((li + 1) & 1u) * kMaxWgRows);
-        if (!kOrdered) stage_x(P, levels, li + 1, lane, stage);
-      }
-    } else {
-      long r0, r1;
-      wave_rows(R0, R1, k, r0, r1);
-      if (vocab) {
-        i8_consume_level(P, r0, r1, R0, scales, lane, pr, consumed, ring, planes, plane_e, best, best_idx);
+        if (li < P.n_levels) stage_scales(P, levels, li + 1, lane, scale_buf + ((li + 1) & 1u) * kMaxWgRows);
       } else {
-        const DevLevel& L = levels[li];
-        if (L.c == 1) t2_consume_level<1>(L, r0, r1, R0, scales, lane, pr, consumed, ring, planes, plane_e, out_buf);
-        else if (L.c == 2) t2_consume_level<2>(L, r0, r1, R0, scales, lane, pr, consumed, ring, planes, plane_e, out_buf);
-        else t2_consume_level<3>(L, r0, r1, R0, scales, lane, pr, consumed, ring, planes, plane_e, out_buf);
+        consume_item<false, RS>(P, levels, li, li, R0, R1, k, scales, lane, pr, consumed, ring, planes1, out_buf, best,
+                                best_idx, nullptr);
+      }
+      __syncthreads();  // planes, this level's scales and outputs are complete
+      if (!vocab && wave == 0) {
+        float* y = levels[li].y;
+        for (long o0 = 0; o0 < R1 - R0; o0 += 64)  // wave-uniform trip count
+          if (o0 + lane < R1 - R0) y[R0 + o0 + lane] = out_buf[o0 + lane];
+        bar.arrive_release(li);
       }
     }
-    __syncthreads();  // planes, this level's scales and outputs are complete
-    if (kOrdered && !vocab && wave == 0) {
-      float* y = levels[li].y;
-      for (long o = lane; o < R1 - R0; o += 64) y[R0 + o] = out_buf[o];
-      bar.arrive_release(li);
+  } else if (wave == 0) {
+    // Independent levels, split over the workgroups as contiguous row
+    // ranges (segments) of the concatenated levels.  The control wave copies
+    // segment j's pre-converted input planes into the plane buffer as soon
+    // as every compute wave has copied segment j - 1's limbs into registers,
+    // and publishes ready_level = j once the copies have landed.
+    const int n = static_cast<int>(pr.n_items);
+    __builtin_amdgcn_s_waitcnt(0);
+    __hip_atomic_store(&ready_level, 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int j = 1; j < n; ++j) {
+      const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+      while (true) {
+        const int d = (lane >= 1 && lane < kWpb)
+                          ? __hip_atomic_load(&done_level[lane], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)
+                          : j;
+        if (__all(d >= j - 1)) break;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {  // scalar read: uniform
+          if (lane == 0) st_sc(&state[kStateStatus], kStatusTimeout);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      stage_planes(P, levels, static_cast<unsigned>(pr.segs[j].level), lane, planes2);
+      __builtin_amdgcn_s_waitcnt(0);
+      __hip_atomic_store(&ready_level, j, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  } else {
+    // Compute wave: each segment as soon as its planes are in LDS; no block
+    // barrier.  After copying the segment's limbs into registers the wave
+    // publishes done_level = j (the plane buffer may then be refilled).
+    const unsigned n = pr.n_items;
+    for (unsigned j = 0; j < n; ++j) {
+      const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+      // (the loaded word is the same in every lane; readfirstlane keeps the
+      // loop exit uniform)
+      while (uni(__hip_atomic_load(&ready_level, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) < static_cast<int>(j)) {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
+          if (lane == 0) st_sc(&state[kStateStatus], kStatusTimeout);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      unsigned li;
+      long R0, R1;
+      item_rows(pr.segs, j, P.vocab, levels, P.n_levels, P.grid, li, R0, R1);
+      const float* scales = li < P.n_levels ? levels[li].scale : P.out_scale;
+      consume_item<true, RS>(P, levels, li, j, R0, R1, k, scales, lane, pr, consumed, ring, planes2, nullptr, best,
+                             best_idx, &done_level[wave]);
     }
   }
 
@@ -634,18 +857,42 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restric
   }
 }
 
+// Stream schedule: converts every level's input (and h) into limb planes in
+// the workspace, once per step, before the step kernel.  Workgroup b takes
+// levels b, b + grid, ...; the planes are those the step kernel copies.
+__global__ __launch_bounds__(kThreads) void convert_inputs_kernel(const Plan* __restrict__ plan,
+                                                                  const DevLevel* __restrict__ levels) {
+  const Plan& P = *plan;
+  for (unsigned li = blockIdx.x; li <= P.n_levels; li += gridDim.x) {
+    if (li < P.n_levels) {
+      const DevLevel& L = levels[li];
+      t2_convert_groups(L.x, L.cols, L.planes, reinterpret_cast<int*>(L.planes + L.nchunks * kT2ChunkDwords),
+                        static_cast<int>(threadIdx.x), static_cast<int>(blockDim.x));
+    } else {
+      i8_convert_groups(P.h, P.hidden, P.vocab_planes,
+                        reinterpret_cast<int*>(P.vocab_planes + (P.hidden >> 4) * kI8ChunkDwords),
+                        static_cast<int>(threadIdx.x), static_cast<int>(blockDim.x));
+    }
+  }
+}
+
 __global__ void xcc_calibrate(unsigned* out) {
   if (threadIdx.x == 0) out[blockIdx.x] = xcc_id();
 }
 
 // ----------------------------------------------------------------- host side
 struct Layout {
-  size_t plan = 0, state = 0, counters = 0, flags = 0, partials = 0, levels = 0, calib = 0, total = 0;
+  size_t plan = 0, state = 0, counters = 0, flags = 0, partials = 0, levels = 0, calib = 0, planes = 0, segs = 0,
+         seg_count = 0, total = 0;
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-Layout layout_for(int n_levels) {
+// Workspace layout of a step (offsets from the 256-byte aligned plan).  The
+// stream schedule adds the pre-converted limb planes of every level's input
+// and of h (each block 256-byte aligned, in level order).
+Layout layout_for(const pwg_step_desc* d) {
+  const int n_levels = d->n_levels;
   Layout L;
   L.plan = 0;
   L.state = align_up(sizeof(Plan), 256);
@@ -654,8 +901,68 @@ Layout layout_for(int n_levels) {
   L.partials = align_up(L.flags + kFlagsBytes, 256);
   L.levels = align_up(L.partials + kMaxGrid * 8, 256);
   L.calib = align_up(L.levels + static_cast<size_t>(n_levels) * sizeof(DevLevel), 256);
-  L.total = align_up(L.calib + kMaxGrid * 4, 256);
+  L.planes = align_up(L.calib + kMaxGrid * 4, 256);
+  size_t end = L.planes;
+  if (d->schedule == PWG_SCHEDULE_STREAM) {
+    for (int i = 0; i < n_levels; ++i) end += align_up(t2_plane_bytes(static_cast<int>(d->levels[i].cols)), 256);
+    end += align_up(i8_plane_bytes(static_cast<int>(d->hidden)), 256);
+    // segments: at most one per level (and the vocabulary) per workgroup
+    L.segs = align_up(end, 256);
+    L.seg_count = align_up(L.segs + static_cast<size_t>(kMaxGrid) * (n_levels + 1) * sizeof(Seg), 256);
+    end = L.seg_count + kMaxGrid * 4;
+  }
+  L.total = align_up(end, 256);
   return L;
+}
+
+// Relative cost of one 1 KiB slot of the output projection against one of a
+// ternary level (measured: the int8 rows stream at about twice the rate of
+// the ternary rows, whose vector work per byte is about three times larger).
+constexpr double kI8SlotCost = 0.45;
+
+// Stream schedule: splits the concatenation of every level's rows (then the
+// vocabulary rows) into `grid` contiguous ranges of equal cost and returns
+// each workgroup's segments (one per level it touches) in level order.
+void partition_stream(const pwg_step_desc* d, int grid, std::vector<std::vector<Seg>>& out) {
+  const int n = d->n_levels;
+  std::vector<long long> rows(n + 1);
+  std::vector<double> cost(n + 1), start(n + 2);
+  for (int i = 0; i < n; ++i) {
+    rows[i] = d->levels[i].rows;
+    cost[i] = static_cast<double>((d->levels[i].cols / 64 + 63) / 64);
+  }
+  rows[n] = d->vocab;
+  cost[n] = static_cast<double>((d->hidden / 16 + 63) / 64) * kI8SlotCost;
+  start[0] = 0.0;
+  for (int i = 0; i <= n; ++i) start[i + 1] = start[i] + static_cast<double>(rows[i]) * cost[i];
+  const double total = start[n + 1];
+  // position of cost offset x: (level, row), rounded to the nearest row
+  auto pos = [&](double x, int& lv, long long& r) {
+    lv = 0;
+    while (lv < n && x >= start[lv + 1]) ++lv;
+    r = static_cast<long long>(std::llround((x - start[lv]) / cost[lv]));
+    r = r < 0 ? 0 : (r > rows[lv] ? rows[lv] : r);
+  };
+  out.assign(grid, {});
+  int lv0 = 0;
+  long long r0 = 0;
+  for (int b = 0; b < grid; ++b) {
+    int lv1;
+    long long r1;
+    if (b + 1 == grid) {
+      lv1 = n;
+      r1 = rows[n];
+    } else {
+      pos(total * (b + 1) / grid, lv1, r1);
+    }
+    for (int lv = lv0; lv <= lv1; ++lv) {
+      const long long a = lv == lv0 ? r0 : 0;
+      const long long e = lv == lv1 ? r1 : rows[lv];
+      if (e > a) out[b].push_back(Seg{lv, static_cast<int>(a), static_cast<int>(e), 0});
+    }
+    lv0 = lv1;
+    r0 = r1;
+  }
 }
 
 struct GridInfo {
@@ -682,7 +989,7 @@ int grid_for(const pwg_step_desc* d, GridInfo* gi) {
 
 size_t step_persistent_workspace(const pwg_step_desc* d) {
   if (!d || (d->schedule != PWG_SCHEDULE_PERSISTENT && d->schedule != PWG_SCHEDULE_STREAM) || d->n_levels < 0) return 0;
-  return layout_for(d->n_levels).total + 256;  // + 256 for aligning the plan
+  return layout_for(d).total + 256;  // + 256 for aligning the plan
 }
 
 static Plan* plan_ptr(const pwg_step_desc* d, size_t ws_offset) {
@@ -694,7 +1001,9 @@ int step_persistent_plan(const pwg_step_desc* d, size_t ws_offset, void* stream)
   GridInfo gi0;
   const int rc0 = grid_for(d, &gi0);
   if (rc0 != PWG_OK) return rc0;
-  auto too_many = [&](int64_t rows) { return (rows + gi0.grid - 1) / gi0.grid > kMaxWgRows; };
+  // the ordered schedule keeps a workgroup's row scales and outputs of a level in LDS
+  const bool ordered = d->schedule == PWG_SCHEDULE_PERSISTENT;
+  auto too_many = [&](int64_t rows) { return ordered && (rows + gi0.grid - 1) / gi0.grid > kMaxWgRows; };
   if (too_many(d->vocab))
     return fail(PWG_ERR_UNSUPPORTED, "pwg_step_plan: persistent schedules support up to %d vocabulary rows per CU",
                 kMaxWgRows);
@@ -713,7 +1022,7 @@ int step_persistent_plan(const pwg_step_desc* d, size_t ws_offset, void* stream)
   const int rc = grid_for(d, &gi);
   if (rc != PWG_OK) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const Layout lay = layout_for(d->n_levels);
+  const Layout lay = layout_for(d);
   Plan* dplan = plan_ptr(d, ws_offset);
   char* dbase = reinterpret_cast<char*>(dplan);
 
@@ -767,6 +1076,7 @@ int step_persistent_plan(const pwg_step_desc* d, size_t ws_offset, void* stream)
   h.levels_off = lay.levels;
   h.calib_off = lay.calib;
   std::vector<DevLevel> lv(d->n_levels);
+  size_t plane_off = lay.planes;
   for (int i = 0; i < d->n_levels; ++i) {
     const pwg_level& L = d->levels[i];
     lv[i].w = static_cast<const u32x4*>(L.w_packed);
@@ -777,10 +1087,41 @@ int step_persistent_plan(const pwg_step_desc* d, size_t ws_offset, void* stream)
     lv[i].cols = static_cast<int>(L.cols);
     lv[i].nchunks = static_cast<int>(L.cols / 64);
     lv[i].c = static_cast<int>((L.cols / 64 + 63) / 64);
+    lv[i].planes = nullptr;
+    if (d->schedule == PWG_SCHEDULE_STREAM) {
+      lv[i].planes = reinterpret_cast<unsigned*>(dbase + plane_off);
+      plane_off += align_up(t2_plane_bytes(static_cast<int>(L.cols)), 256);
+    }
+  }
+  h.vocab_planes = d->schedule == PWG_SCHEDULE_STREAM ? reinterpret_cast<unsigned*>(dbase + plane_off) : nullptr;
+  std::vector<Seg> seg_flat;
+  std::vector<int> seg_count;
+  h.segs = nullptr;
+  h.seg_count = nullptr;
+  h.seg_stride = 0;
+  if (d->schedule == PWG_SCHEDULE_STREAM) {
+    std::vector<std::vector<Seg>> parts;
+    partition_stream(d, gi.grid, parts);
+    int stride = 1;
+    for (const auto& v : parts) stride = static_cast<int>(v.size()) > stride ? static_cast<int>(v.size()) : stride;
+    seg_flat.assign(static_cast<size_t>(gi.grid) * stride, Seg{0, 0, 0, 0});
+    seg_count.resize(gi.grid);
+    for (int b = 0; b < gi.grid; ++b) {
+      seg_count[b] = static_cast<int>(parts[b].size());
+      for (size_t j = 0; j < parts[b].size(); ++j) seg_flat[static_cast<size_t>(b) * stride + j] = parts[b][j];
+    }
+    h.segs = reinterpret_cast<const Seg*>(dbase + lay.segs);
+    h.seg_count = reinterpret_cast<const int*>(dbase + lay.seg_count);
+    h.seg_stride = stride;
   }
   e = hipMemcpyAsync(dplan, &h, sizeof(Plan), hipMemcpyHostToDevice, st);
   if (e == hipSuccess && d->n_levels > 0)
     e = hipMemcpyAsync(dbase + lay.levels, lv.data(), lv.size() * sizeof(DevLevel), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess && !seg_flat.empty()) {
+    e = hipMemcpyAsync(dbase + lay.segs, seg_flat.data(), seg_flat.size() * sizeof(Seg), hipMemcpyHostToDevice, st);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(dbase + lay.seg_count, seg_count.data(), seg_count.size() * 4, hipMemcpyHostToDevice, st);
+  }
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return fail(PWG_ERR_HIP, "pwg_step_plan: %s", hipGetErrorString(e));
   return PWG_OK;
@@ -792,17 +1133,19 @@ int step_persistent_launch(const pwg_step_desc* d, size_t ws_offset, void* strea
   if (rc != PWG_OK) return rc;
   Plan* dplan = plan_ptr(d, ws_offset);
   char* dbase = reinterpret_cast<char*>(dplan);
-  const Layout lay = layout_for(d->n_levels);
+  const Layout lay = layout_for(d);
   const DevLevel* lv = reinterpret_cast<const DevLevel*>(dbase + lay.levels);
   unsigned* state = reinterpret_cast<unsigned*>(dbase + lay.state);
   auto* counters = reinterpret_cast<unsigned long long*>(dbase + lay.counters);
   auto* flags = reinterpret_cast<unsigned*>(dbase + lay.flags);
   auto* partials = reinterpret_cast<unsigned long long*>(dbase + lay.partials);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (d->schedule == PWG_SCHEDULE_STREAM)
+  if (d->schedule == PWG_SCHEDULE_STREAM) {
+    hipLaunchKernelGGL(convert_inputs_kernel, dim3(gi.grid), dim3(kThreads), 0, st, dplan, lv);
     hipLaunchKernelGGL(step_kernel<false>, dim3(gi.grid), dim3(kThreads), gi.lds, st, dplan, lv, state, counters, flags, partials);
-  else
+  } else {
     hipLaunchKernelGGL(step_kernel<true>, dim3(gi.grid), dim3(kThreads), gi.lds, st, dplan, lv, state, counters, flags, partials);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PWG_ERR_HIP, "persistent step launch: %s", hipGetErrorString(e));
   return PWG_OK;
@@ -812,7 +1155,7 @@ int step_persistent_status(const pwg_step_desc* d, size_t ws_offset, void* strea
   Plan* dplan = plan_ptr(d, ws_offset);
   unsigned s = 0;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const unsigned* state = reinterpret_cast<const unsigned*>(reinterpret_cast<char*>(dplan) + layout_for(d->n_levels).state);
+  const unsigned* state = reinterpret_cast<const unsigned*>(reinterpret_cast<char*>(dplan) + layout_for(d).state);
   hipError_t e = hipMemcpyAsync(&s, &state[kStateStatus], 4, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return fail(PWG_ERR_HIP, "pwg_step_status: %s", hipGetErrorString(e));
