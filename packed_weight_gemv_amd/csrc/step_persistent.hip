@@ -224,10 +224,15 @@ constexpr size_t kStageBytes = kMaxT2Cols * 4;
 constexpr size_t kPlaneBytes = static_cast<size_t>(kMaxT2Cols / 64) * (kT2ChunkDwords + 1) * 4;
 constexpr size_t kScaleBytes = 2 * kMaxWgRows * 4;
 constexpr size_t kOutBytes = kMaxWgRows * 4;              // a level's outputs of the workgroup (ordered)
+// Stream schedule: each compute wave's row scales arrive in blocks of
+// kScaleBlock rows through a ring of kScaleBufs blocks in LDS.
+constexpr int kScaleBlock = 64;
+constexpr int kScaleBufs = 4;
+constexpr size_t kScaleRingBytes = static_cast<size_t>(kComputeWaves) * kScaleBufs * kScaleBlock * 4;
 // Ordered: ring | raw input | planes | 2 x scales | outputs.
-// Stream:  ring | planes (filled by copies of pre-converted planes).
+// Stream:  ring | planes (filled by copies of pre-converted planes) | scale rings.
 constexpr size_t kOrderedSmem = kRingBytes + kStageBytes + kPlaneBytes + kScaleBytes + kOutBytes;
-constexpr size_t kStreamSmem = kRingBytesStream + kPlaneBytes;
+constexpr size_t kStreamSmem = kRingBytesStream + kPlaneBytes + kScaleRingBytes;
 constexpr size_t kStepSmem = kOrderedSmem > kStreamSmem ? kOrderedSmem : kStreamSmem;
 static_assert(kT2ChunkDwords * 4 * (kMaxT2Cols / 64) % 16 == 0, "plane copies move 16-byte units");
 
@@ -292,23 +297,22 @@ __device__ __forceinline__ void wait_vm_le(unsigned n) {
   }
 #undef PWG_VM
 }
-// Waits only for this wave's LDS (and scalar-memory) operations.
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8)); }
 
 // Rows of a level owned by workgroup `b` of `nb`: [R0, R1).  Compute wave k
-// takes every kComputeWaves-th row of them, from R0 + q on, with q = (k + li)
-// mod kComputeWaves: the waves of a workgroup sweep its contiguous block of
-// rows together (one sequential stream per workgroup), and the waves whose
-// share is one row longer change from level to level.
+// takes a contiguous share of them, share q = (k + li) mod kComputeWaves
+// (rows first, first + 1, ...): each wave streams a contiguous block, and
+// the waves whose share is one row longer change from item to item.
 __device__ __forceinline__ void wg_rows(long rows, unsigned b, unsigned nb, long& R0, long& R1) {
   R0 = static_cast<long>(b) * rows / nb;
   R1 = static_cast<long>(b + 1) * rows / nb;
 }
 __device__ __forceinline__ void wave_rows(long R0, long R1, unsigned k, unsigned li, long& first, int& count) {
   const unsigned q = (k + li) % kComputeWaves;
-  first = R0 + q;
-  count = R1 - R0 > q ? static_cast<int>((R1 - R0 - q + kComputeWaves - 1) / kComputeWaves) : 0;
+  first = R0 + static_cast<long>(q) * (R1 - R0) / kComputeWaves;
+  count = static_cast<int>(R0 + static_cast<long>(q + 1) * (R1 - R0) / kComputeWaves - first);
 }
+// Row stride between a wave's consecutive rows.
+constexpr int kRowStride = 1;
 
 // Wave-uniform copies (the values are the same in every lane; this keeps
 // them in scalar registers, so the level table is read with scalar loads
@@ -327,10 +331,13 @@ __device__ __forceinline__ T* uni(T* p) {
 __device__ __forceinline__ void item_rows(const Seg* segs, unsigned item, int vocab, const DevLevel* levels,
                                           unsigned n_levels, unsigned nwg, unsigned& level, long& R0, long& R1) {
   if (segs) {
-    const Seg& sg = segs[item];
-    level = uni(static_cast<unsigned>(sg.level));
-    R0 = uni(sg.row_begin);
-    R1 = uni(sg.row_end);
+    // written by the plan before the launch and constant during the step:
+    // scalar loads (a vector load would wait behind the ring's copies)
+    typedef const __attribute__((address_space(4))) Seg const_seg;
+    const_seg* cs = (const_seg*)segs;
+    level = uni(static_cast<unsigned>(cs[item].level));
+    R0 = uni(cs[item].row_begin);
+    R1 = uni(cs[item].row_end);
   } else {
     level = item;
     wg_rows(item < n_levels ? uni(levels[item].rows) : vocab, blockIdx.x, nwg, R0, R1);
@@ -348,6 +355,7 @@ struct Producer {
   unsigned n_levels;
   int vocab, hidden;
   const u32x4* out_table;
+  const float* out_scale;
   unsigned nwg;       // workgroups of the launch
   unsigned k;         // compute-wave index 0..6
   unsigned lane;
@@ -357,6 +365,17 @@ struct Producer {
   int chunk, chunks_per_row, nchunks;
   const u32x4* rowp;  // start of the current row
   unsigned char* ring;
+  // Row scales through the scale ring (stream schedule; sring null: none).
+  // A block of kScaleBlock rows of the item is copied before its first row's
+  // slots, so a wait for a row's slots also covers its scale.
+  float* sring;
+  const float* scale_src;  // the item's scale array
+  long first;              // the item's first row of this wave (rows first + kComputeWaves * i)
+  int count;               // the item's rows of this wave
+  int fast_rows;           // upcoming rows issue_row_fast may issue (see plan_fast)
+  unsigned sb_issued;      // scale blocks issued
+  unsigned sb_consumed;    // scale blocks the consumer is done with
+  unsigned sb_cons_base;   // consumer: scale blocks of the items before the current one
 
   // Moves to the first item, from `item` on, in which this wave has rows.
   __device__ __forceinline__ void enter_item() {
@@ -370,26 +389,64 @@ struct Producer {
         nchunks = uni(levels[level].nchunks);
         chunks_per_row = uni(levels[level].c);
         base = uni(levels[level].w);
+        scale_src = uni(levels[level].scale);
       } else {
         nchunks = hidden >> 4;
         chunks_per_row = (nchunks + 63) / 64;
         base = out_table;
+        scale_src = out_scale;
       }
-      long first;
-      int count;
       wave_rows(R0, R1, k, item, first, count);
       rows_left = uni(count);
       rowp = uni(base + first * nchunks);
       chunk = 0;
-      if (rows_left > 0) return;
+      if (rows_left > 0) {
+        plan_fast();
+        return;
+      }
       item = uni(item + 1);
     }
+    fast_rows = 0;
+  }
+
+  // Rows from the next one on that are plain: whole rows of 64-chunk
+  // multiples, not the item's last row, not starting a scale block.  Those
+  // take the straight-line issue_row_fast.
+  __device__ __forceinline__ void plan_fast() {
+    const int ri = count - rows_left;  // index of the next row within the item
+    int n = rows_left - 1;
+    if (chunk != 0 || (nchunks & 63) != 0) n = 0;
+    if (sring) {
+      const int to_block = kScaleBlock - 1 - (ri % kScaleBlock);  // plain rows before the next block start
+      n = ri % kScaleBlock == 0 ? 0 : (n < to_block ? n : to_block);
+    }
+    fast_rows = uni(n);
   }
 
   __device__ __forceinline__ bool active() const { return item < n_items; }
 
-  // Issues the next slot (the caller checks active() and that the ring has room).
+  // Whether the next slot may be issued: the ring has room and, when the
+  // slot starts a scale block, the scale ring has a free block.
+  __device__ __forceinline__ bool can_issue(unsigned consumed) const {
+    if (!active() || uni(issued) - uni(consumed) >= static_cast<unsigned>(RS)) return false;
+    if (sring && chunk == 0 && (count - rows_left) % kScaleBlock == 0)
+      return uni(sb_issued) - uni(sb_consumed) < static_cast<unsigned>(kScaleBufs);
+    return true;
+  }
+
+  // Issues the next slot (the caller checks can_issue()).
   __device__ __forceinline__ void issue() {
+    if (sring && chunk == 0) {
+      const int ri = count - rows_left;  // the row's index within the item
+      if (ri % kScaleBlock == 0) {
+        // scales of rows ri .. ri + 63 (lane i: row ri + i; lanes past the
+        // item's rows copy nothing)
+        if (ri + static_cast<int>(lane) < count)
+          dma4(scale_src + first + static_cast<long>(kRowStride) * (ri + static_cast<int>(lane)),
+               sring + (sb_issued % kScaleBufs) * kScaleBlock);
+        sb_issued = uni(sb_issued + 1);
+      }
+    }
     unsigned c = lane + 64u * static_cast<unsigned>(chunk);
     c = c < static_cast<unsigned>(nchunks) ? c : static_cast<unsigned>(nchunks - 1);
     dma16(rowp + c, ring + (issued % RS) * kSlotBytes);
@@ -397,62 +454,88 @@ struct Producer {
     chunk = uni(chunk + 1);
     if (chunk == chunks_per_row) {
       chunk = 0;
-      rowp = uni(rowp + kComputeWaves * nchunks);
+      rowp = uni(rowp + kRowStride * nchunks);
       rows_left = uni(rows_left - 1);
       if (rows_left == 0) {
         item = uni(item + 1);
         enter_item();
+      } else {
+        plan_fast();
       }
+    } else {
+      fast_rows = 0;
     }
+  }
+
+  // Issues one plain row of C chunks (fast_rows > 0, chunks_per_row == C,
+  // and the ring has C free slots): no bookkeeping branches.
+  template <int C>
+  __device__ __forceinline__ void issue_row_fast() {
+#pragma unroll
+    for (int c = 0; c < C; ++c) dma16(rowp + lane + 64u * c, ring + ((issued + c) % RS) * kSlotBytes);
+    issued = uni(issued + C);
+    rowp = uni(rowp + kRowStride * nchunks);
+    rows_left = uni(rows_left - 1);
+    fast_rows = uni(fast_rows - 1);
   }
 
   // Refills the ring after the consumer freed slots.
   __device__ __forceinline__ void fill(unsigned consumed) {
-    while (active() && uni(issued) - uni(consumed) < static_cast<unsigned>(RS)) issue();
+    while (can_issue(consumed)) issue();
   }
 };
 
-// The consumer half: takes the next row's C slots out of the ring, then
-// refills the ring (after the LDS reads have returned, so the slots may be
-// overwritten) before the caller computes on them.
+// The consumer half: takes the next row's C slots out of the ring and
+// refills the ring before the caller computes on them.
 template <int C, int RS>
 __device__ __forceinline__ void take_row(Producer<RS>& pr, unsigned& consumed, const unsigned char* ring, unsigned lane,
                                          u32x4 (&w)[C]) {
-  // the row's last slot has index consumed + C - 1; everything issued after
-  // it may still be in flight (with a full ring that is RS - C slots)
+  // The row's last slot has index consumed + C - 1; everything issued after
+  // it may still be in flight.  Slots are refilled one row late (below), so
+  // in the steady state RS - C slots are ahead and RS - 2C may stay in flight.
   const unsigned ahead = uni(pr.issued) - uni(consumed);
-  if (ahead == static_cast<unsigned>(RS)) {
-    __builtin_amdgcn_s_waitcnt(((RS - C) & 15) | (((RS - C) >> 4) << 14) | (7 << 4) | (15 << 8));
+  if (ahead == static_cast<unsigned>(RS - C)) {
+    __builtin_amdgcn_s_waitcnt(((RS - 2 * C) & 15) | (((RS - 2 * C) >> 4) << 14) | (7 << 4) | (15 << 8));
   } else {
     wait_vm_le(ahead - C);
   }
 #pragma unroll
   for (int c = 0; c < C; ++c)
     w[c] = *reinterpret_cast<const u32x4*>(ring + ((consumed + c) % RS) * kSlotBytes + lane * 16);
+  // Refill the slots of the rows before this one: their LDS reads have
+  // returned (their values were used), while this row's reads may still be
+  // in flight, so its slots wait until the next row.  In the steady state
+  // that is one plain row of the same shape: the straight-line issue.
+  if (pr.fast_rows > 0 && pr.chunks_per_row == C && ahead == static_cast<unsigned>(RS) - C) {
+    pr.template issue_row_fast<C>();
+  } else {
+    pr.fill(consumed);
+  }
   consumed = uni(consumed + C);
-  wait_lgkm0();
-  pr.fill(consumed);
 }
 
 // Row scale for the tile row this lane stores (tile row row_of<4>(lane >> 4),
-// row index i + that).  kConst: `scales` is the level's scale array in global
-// memory, constant during the step, read with scalar loads (they do not wait
-// behind the ring's outstanding copies) before the lanes diverge; otherwise
-// it is the workgroup's LDS copy starting at row R0.
-template <bool kConst>
-__device__ __forceinline__ float tile_scale(const float* scales, long first, int i, int count, long R0, unsigned lane) {
+// row index i + that).  kRing: from the wave's scale ring, where the item's
+// scale blocks start at block number sb0; otherwise from the workgroup's LDS
+// copy of the level's scales starting at row R0.
+template <bool kRing, int RS>
+__device__ __forceinline__ float tile_scale(const float* scales, long first, int i, int count, long R0, unsigned lane,
+                                            const Producer<RS>& pr, unsigned sb0) {
   const int t = row_of<4>(static_cast<int>(lane >> 4));
-  if constexpr (kConst) {
-    typedef const __attribute__((address_space(4))) float const_float;
-    const_float* cs = (const_float*)scales;  // address-space cast (constant memory)
-    float su[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) su[u] = i + u < count ? cs[first + static_cast<long>(kComputeWaves) * (i + u)] : 0.f;
-    return t == 0 ? su[0] : t == 1 ? su[1] : t == 2 ? su[2] : su[3];
+  const int iu = i + t < count ? i + t : i;
+  if constexpr (kRing) {
+    const unsigned blk = sb0 + static_cast<unsigned>(iu / kScaleBlock);
+    return pr.sring[(blk % kScaleBufs) * kScaleBlock + iu % kScaleBlock];
   } else {
-    const int iu = i + t < count ? i + t : i;
-    return scales[first + static_cast<long>(kComputeWaves) * iu - R0];
+    return scales[first + static_cast<long>(kRowStride) * iu - R0];
   }
+}
+
+// After a tile of rows i .. i + 3: the consumer is done with a scale block
+// when the tile ends one (blocks hold kScaleBlock rows, a multiple of 4).
+template <int RS>
+__device__ __forceinline__ void tile_done(Producer<RS>& pr, int i, int count) {
+  if ((i + 4) % kScaleBlock == 0 || i + 4 >= count) pr.sb_consumed = uni(pr.sb_consumed + 1);
 }
 
 // Consumes the wave's rows of one ternary level (C chunks of 64 words per
@@ -466,6 +549,8 @@ __device__ __forceinline__ void t2_consume_level(const DevLevel& L, long first, 
   T2Lane<C> st;
   t2_lane_init<C>(st, planes, plane_e, L.nchunks, lane);
   if (init_flag) lds_publish(init_flag, init_val);  // the planes buffer may be refilled
+  const unsigned sb0 = pr.sb_cons_base;              // this item's first scale block
+  if (kConst) pr.sb_cons_base = uni(sb0 + static_cast<unsigned>((count + kScaleBlock - 1) / kScaleBlock));
   for (int i = 0; i < count; i += 4) {
     float p[4];
 #pragma unroll
@@ -485,8 +570,9 @@ __device__ __forceinline__ void t2_consume_level(const DevLevel& L, long first, 
       }
     }
     const int iu = i + row_of<4>(static_cast<int>(lane >> 4));
-    const long row = first + static_cast<long>(kComputeWaves) * iu;
-    const float sc = tile_scale<kConst>(scales, first, i, count, R0, lane);
+    const long row = first + static_cast<long>(kRowStride) * iu;
+    const float sc = tile_scale<kConst, RS>(scales, first, i, count, R0, lane, pr, sb0);
+    if (kConst) tile_done(pr, i, count);
     const float total = tile_reduce<4>(p);
     if ((lane & 15u) == 0u && iu < count) {
       const float v = sc * total;
@@ -517,6 +603,8 @@ __device__ __forceinline__ void i8_consume_level(const Plan& P, long first, int 
     }
   }
   if (init_flag) lds_publish(init_flag, init_val);  // the planes buffer may be refilled
+  const unsigned sb0 = pr.sb_cons_base;              // this item's first scale block
+  if (kConst) pr.sb_cons_base = uni(sb0 + static_cast<unsigned>((count + kScaleBlock - 1) / kScaleBlock));
   const int cpr = (nchunks + 63) / 64;  // slots per row (4 for hidden = 4096)
   for (int i = 0; i < count; i += 4) {
     float p[4];
@@ -526,8 +614,8 @@ __device__ __forceinline__ void i8_consume_level(const Plan& P, long first, int 
       if (i + u < count) {
         u32x4 q[kMaxI8C];
         const unsigned ahead = uni(pr.issued) - uni(consumed);
-        if (ahead == static_cast<unsigned>(RS) && cpr == kMaxI8C) {
-          __builtin_amdgcn_s_waitcnt(((RS - kMaxI8C) & 15) | (((RS - kMaxI8C) >> 4) << 14) | (7 << 4) | (15 << 8));
+        if (ahead == static_cast<unsigned>(RS - kMaxI8C) && cpr == kMaxI8C) {  // steady state (see take_row)
+          __builtin_amdgcn_s_waitcnt(((RS - 2 * kMaxI8C) & 15) | (((RS - 2 * kMaxI8C) >> 4) << 14) | (7 << 4) | (15 << 8));
         } else {
           wait_vm_le(ahead - cpr);
         }
@@ -535,9 +623,12 @@ __device__ __forceinline__ void i8_consume_level(const Plan& P, long first, int 
         for (int c = 0; c < kMaxI8C; ++c)
           q[c] = c < cpr ? *reinterpret_cast<const u32x4*>(ring + ((consumed + c) % RS) * kSlotBytes + lane * 16)
                          : u32x4{0u, 0u, 0u, 0u};
+        if (pr.fast_rows > 0 && pr.chunks_per_row == kMaxI8C && ahead == static_cast<unsigned>(RS - kMaxI8C)) {
+          pr.template issue_row_fast<kMaxI8C>();  // slots of the rows before this one (see take_row)
+        } else {
+          pr.fill(consumed);
+        }
         consumed = uni(consumed + cpr);
-        wait_lgkm0();
-        pr.fill(consumed);
 #pragma unroll
         for (int c = 0; c < kMaxI8C; ++c) {
           int a0 = 0, a1 = 0, a2 = 0;
@@ -555,8 +646,9 @@ __device__ __forceinline__ void i8_consume_level(const Plan& P, long first, int 
       }
     }
     const int iu = i + row_of<4>(static_cast<int>(lane >> 4));
-    const long row = first + static_cast<long>(kComputeWaves) * iu;
-    const float sc = tile_scale<kConst>(scales, first, i, count, R0, lane);
+    const long row = first + static_cast<long>(kRowStride) * iu;
+    const float sc = tile_scale<kConst, RS>(scales, first, i, count, R0, lane, pr, sb0);
+    if (kConst) tile_done(pr, i, count);
     const float total = tile_reduce<4>(p);
     if ((lane & 15u) == 0u && iu < count) {
       const float logit = sc * total;
@@ -703,6 +795,15 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restric
   pr.issued = 0;
   pr.item = 0;
   pr.ring = ring;
+  pr.out_scale = P.out_scale;
+  pr.sring = kOrdered ? nullptr
+                      : reinterpret_cast<float*>(smem + kRingBytesStream + kPlaneBytes) +
+                            static_cast<size_t>(wave == 0 ? 0 : k) * kScaleBufs * kScaleBlock;
+  pr.sb_issued = 0;
+  pr.sb_consumed = 0;
+  pr.sb_cons_base = 0;
+  pr.first = 0;
+  pr.count = 0;
   unsigned consumed = 0;
 
   // Stream schedule: the waves synchronise through two LDS words instead of
