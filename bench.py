@@ -50,6 +50,7 @@ def parse():
     p.add_argument("--layers", type=int, default=36)
     p.add_argument("--no-compare", action="store_true", help="skip the levels-schedule and null-graph timings")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-small-batch", action="store_true", help="skip the small-batch (B = 1, 4, 8, 16) timings")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle's timed sample")
     p.add_argument("--counters", action="store_true",
                    help="counter-collection run: 3 eager steps of the timed schedule plus a 1 GiB device copy "
@@ -166,6 +167,48 @@ def cpu_baseline(target_s: float, step_bytes: int):
                    f"151936x4096 output projection and argmax, timed once; the per-layer mean is scaled to 36 layers"),
         "sample_seconds": float(sum(layer_s) + vocab_s),
     }
+
+
+def small_batch(wl, stream, reps=50):
+    """One 8B-shape layer's four levels and the int8 output projection with
+    argmax, applied to B activation vectors per pass (weights stream once per
+    pass whatever B is); one HIP graph per B.  Reports weight bytes per
+    second and effective integer operations per second (2 per weight per
+    vector)."""
+    import torch
+
+    import packed_weight_gemv_amd as pwg
+    import synth
+    levels = [(w, sc, r, k) for (w, sc, _, _, r, k) in wl.desc.levels[:4]]
+    table, tscale = wl.desc.out_table, wl.desc.out_scale
+    vocab, hidden = table.shape
+    t2_weights = sum(r * k for _, _, r, k in levels)
+    bytes_ = sum(w.numel() * w.element_size() + sc.numel() * 4 for w, sc, _, _ in levels) + table.numel() + tscale.numel() * 4
+    out = []
+    for batch in (1, 4, 8, 16):
+        xs = [torch.from_numpy(synth.batch_inputs(batch, k, 20 + i)).to("cuda:0") for i, (_, _, _, k) in enumerate(levels)]
+        ys = [torch.empty((batch, r), dtype=torch.float32, device="cuda:0") for _, _, r, _ in levels]
+        h = torch.from_numpy(synth.batch_inputs(batch, hidden, 30)).to("cuda:0")
+        ws = torch.zeros(pwg.argmax_workspace_bytes(vocab, batch), dtype=torch.uint8, device="cuda:0")
+        tok = torch.empty(batch, dtype=torch.int32, device="cuda:0")
+
+        def one():
+            for (w, sc, r, k), x, y in zip(levels, xs, ys):
+                pwg.ternary_gemv(w, sc, r, k, x if batch > 1 else x[0], y=y if batch > 1 else y[0], stream=stream)
+            pwg.int8_gemv_argmax(table, tscale, h if batch > 1 else h[0], workspace=ws, token_out=tok, stream=stream)
+        g = capture(one, stream)
+        ms = time_graph(g, stream, reps, 5)
+        us = ms * 1e3
+        ops = 2.0 * (t2_weights + vocab * hidden) * batch
+        out.append({"batch": batch, "us_per_pass": us, "weight_GBps": bytes_ / us / 1e3,
+                    "pct_of_hbm_peak": 100.0 * bytes_ / (us * 1e-6) / PEAK_HBM_BPS,
+                    "effective_Tops": ops / us / 1e6})
+        log(f"small batch B={batch}: {us:.1f} us per pass, {bytes_ / us / 1e3:.0f} GB/s, {ops / us / 1e6:.1f} Top/s")
+        del g
+    return {"config": ("one 8B-shape layer (q|k|v 6144x4096, o 4096x4096, gate|up 24576x4096, down 4096x12288 "
+                       "ternary) + int8 output projection 151936x4096 with per-vector argmax, B fp32 N(0,1) "
+                       "vectors per pass, one HIP graph per B"),
+            "weight_bytes_per_pass": bytes_, "results": out}
 
 
 def main():
@@ -315,6 +358,9 @@ def main():
                               "unit": "GB/s", "frac": achieved_bps / PEAK_HBM_BPS, "traffic": traffic,
                               "kernel": kname, "per_launch_bytes": step_bytes, "avg_launch_us": ms * 1e3}
     result["kernel_source_sha"] = kernel_source_sha()
+
+    if not args.no_small_batch:
+        result["small_batch"] = small_batch(wl, stream)
 
     # 5. oracle CPU baseline (bounded sample)
     if not args.no_cpu_baseline:

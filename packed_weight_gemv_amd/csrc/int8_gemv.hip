@@ -232,6 +232,7 @@ size_t int8_partials(int64_t rows) {
 
 int launch_int8_gemv_argmax(const int8_t* table, const float* s, int64_t rows, int64_t cols, const float* h,
                             int32_t batch, void* ws, int32_t* token, float* logits, void* stream) {
+  if (batch > 1) return launch_int8_gemv_argmax_batch(table, s, rows, cols, h, batch, ws, token, logits, stream);
   I8Instance* in = pick_i8(static_cast<int>(cols));
   const size_t lds = i8_lds_bytes(cols);
   unsigned grid = i8_grid(in, rows, lds);

@@ -26,6 +26,12 @@ int launch_int8_gemv_argmax(const int8_t* table, const float* s, int64_t rows, i
                             const float* h, int32_t batch, void* ws, int32_t* token,
                             float* logits, void* stream);
 size_t int8_partials(int64_t rows);
+// Weight-stationary variants for batch > 1 (batch_gemv.hip).
+int launch_ternary_gemv_batch(const void* w, const float* s, int64_t rows, int64_t cols,
+                              const float* x, int32_t batch, float* y, void* stream);
+int launch_int8_gemv_argmax_batch(const int8_t* table, const float* s, int64_t rows, int64_t cols,
+                                  const float* h, int32_t batch, void* ws, int32_t* token,
+                                  float* logits, void* stream);
 size_t t2_lds_bytes(int64_t cols);
 size_t i8_lds_bytes(int64_t cols);
 int launch_embed_gather(const int8_t* table, const float* s, int64_t rows, int64_t cols,

@@ -204,6 +204,7 @@ size_t t2_lds_bytes(int64_t cols) { return static_cast<size_t>(cols / 64) * (kT2
 
 int launch_ternary_gemv(const void* w, const float* s, int64_t rows, int64_t cols, const float* x, int32_t batch,
                         float* y, void* stream) {
+  if (batch > 1) return launch_ternary_gemv_batch(w, s, rows, cols, x, batch, y, stream);
   Instance* in = pick(static_cast<int>(cols));
   const size_t lds = t2_lds_bytes(cols);
   if (in->max_active == 0) {

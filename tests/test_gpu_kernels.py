@@ -115,6 +115,22 @@ def test_ternary_batch(batch):
         assert_gemv(y[b], yr[b], ref.ternary_gemv_magnitude(m.w, m.scale, xb[b]), f"batch row {b}")
 
 
+BATCH_SHAPES = [(5, 64, 4), (1536, 4096, 16), (257, 8192, 8), (1000, 12288, 4), (33, 16384, 16), (4099, 4096, 8)]
+
+
+@pytest.mark.parametrize("shape", BATCH_SHAPES, ids=[f"{r}x{c}xB{b}" for r, c, b in BATCH_SHAPES])
+def test_ternary_batch_weights_read_once(shape):
+    """The weight-stationary batch kernels (every chunks-per-lane instance,
+    ragged row tails, batch not a multiple of the vector group)."""
+    rows, cols, batch = shape
+    m = synth.ternary_matrix((103, rows, cols), rows, cols)
+    xb = synth.batch_inputs(batch, cols, 3)
+    y = run_ternary(m.w, m.scale, xb)
+    yr = ref.ternary_gemv(m.w, m.scale, xb)
+    for b in range(batch):
+        assert_gemv(y[b], yr[b], ref.ternary_gemv_magnitude(m.w, m.scale, xb[b]), f"{shape} vector {b}")
+
+
 def test_ternary_is_deterministic():
     m = synth.ternary_matrix((97, 0), 24576, 4096)
     x = synth.normal_f32(synth.rng_for(97, 1), 4096)
@@ -185,6 +201,39 @@ def test_argmax_batch():
     for b in range(batch):
         assert token_ok(tok[b], lr[b])
         assert_gemv(lg[b], lr[b], ref.int8_logits_magnitude(tab.q, tab.scale, hb[b]), f"batch {b}")
+
+
+I8_BATCH_SHAPES = [(999, 1024, 8), (5000, 4096, 16), (257, 2048, 4), (3, 8192, 4), (70001, 4096, 8)]
+
+
+@pytest.mark.parametrize("shape", I8_BATCH_SHAPES, ids=[f"{r}x{c}xB{b}" for r, c, b in I8_BATCH_SHAPES])
+def test_argmax_batch_shapes(shape):
+    rows, cols, batch = shape
+    tab = synth.int8_table((104, rows, cols), rows, cols)
+    hb = synth.batch_inputs(batch, cols, 11)
+    tok, lg = run_argmax(tab.q, tab.scale, hb)
+    lr = ref.int8_logits(tab.q, tab.scale, hb)
+    for b in range(batch):
+        assert token_ok(tok[b], lr[b]), f"{shape} vector {b}"
+        assert_gemv(lg[b], lr[b], ref.int8_logits_magnitude(tab.q, tab.scale, hb[b]), f"{shape} vector {b}")
+
+
+def test_argmax_batch_ties_per_column():
+    """Every column keeps the lowest index among equal maxima."""
+    rows, cols, batch = 20000, 4096, 4
+    tab = synth.int8_table((105, 0), rows, cols)
+    hb = synth.batch_inputs(batch, cols, 12)
+    q, t = tab.q.copy(), tab.scale.copy()
+    lr = ref.int8_logits(q, t, hb)
+    tops = [int(np.argmax(lr[b])) for b in range(batch)]
+    for top in tops:            # duplicate each column's best row further down and further up
+        for dup in (min(top + 5000, rows - 1), max(top - 7000, 0)):
+            q[dup], t[dup] = q[top], t[top]
+    lr2 = ref.int8_logits(q, t, hb)
+    tok, _ = run_argmax(q, t, hb, logits=False)
+    for b in range(batch):
+        best = lr2[b].max()
+        assert tok[b] == int(np.flatnonzero(lr2[b] == best)[0]), f"vector {b}"
 
 
 def test_gather_invalid_ids_give_zero_rows_and_nan_scale():
