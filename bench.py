@@ -179,8 +179,9 @@ def small_batch(wl, stream, reps=50):
 
     import packed_weight_gemv_amd as pwg
     import synth
-    levels = [(w, sc, r, k) for (w, sc, _, _, r, k) in wl.desc.levels[:4]]
-    table, tscale = wl.desc.out_table, wl.desc.out_scale
+    rows_w, table = wl.weights[pwg.LAYOUT_ROWS]   # the per-call kernels take row-major weights
+    levels = [(w, sc, r, k) for w, (_, sc, _, _, r, k) in zip(rows_w[:4], wl.desc.levels[:4])]
+    tscale = wl.desc.out_scale
     vocab, hidden = table.shape
     t2_weights = sum(r * k for _, _, r, k in levels)
     bytes_ = sum(w.numel() * w.element_size() + sc.numel() * 4 for w, sc, _, _ in levels) + table.numel() + tscale.numel() * 4
@@ -228,19 +229,17 @@ def main():
     schedule = {"persistent": pwg.SCHEDULE_PERSISTENT, "levels": pwg.SCHEDULE_LEVELS,
                 "stream": pwg.SCHEDULE_STREAM}[args.schedule]
     t0 = time.time()
-    wl = build_step(n_layers=args.layers, schedule=pwg.SCHEDULE_PERSISTENT, with_logits=False)
+    # both weight arrangements when other schedules or the small-batch
+    # kernels (row-major) run next to a tiled stream step
+    both = not (args.no_compare and args.no_small_batch)
+    wl = build_step(n_layers=args.layers, schedule=schedule, with_logits=False, both_layouts=both)
     log(f"workload built in {time.time() - t0:.1f}s: {len(wl.desc.levels)} levels")
     bytes_ = wl.algorithmic_bytes()
     step_bytes = bytes_["total"]
 
     stream = torch.cuda.Stream()
     if args.counters:
-        wl.desc.schedule = schedule
-        wl.desc._c = None
-        need = pwg.step_workspace_bytes(wl.desc)
-        if wl.desc.workspace.numel() < need:
-            wl.desc.workspace = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
-            wl.desc._c = None
+        wl.set_schedule(schedule)
         pwg.step_plan(wl.desc, stream=stream)
         with torch.cuda.stream(stream):
             for _ in range(3):
@@ -254,12 +253,7 @@ def main():
         return
 
     def run(desc_schedule):
-        wl.desc.schedule = desc_schedule
-        wl.desc._c = None
-        need = pwg.step_workspace_bytes(wl.desc)
-        if wl.desc.workspace.numel() < need:
-            wl.desc.workspace = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
-            wl.desc._c = None
+        wl.set_schedule(desc_schedule)
         pwg.step_plan(wl.desc, stream=stream)
         return lambda: pwg.decode_step_weights(wl.desc, stream=stream)
 
@@ -326,7 +320,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "ternary x int4-limb dot (i32 exact) / int8 x int8-limb dot (i32 exact), f32 scale",
+        "dtype": ("ternary FP4 x FP4-digit block-scaled MFMA (exact products, f32 sums) / int8 x int8-digit MFMA "
+                  "(i32 exact), f32 scale" if schedule == pwg.SCHEDULE_STREAM else
+                  "ternary x int4-limb dot (i32 exact) / int8 x int8-limb dot (i32 exact), f32 scale"),
         "data": "synthetic seeded (ternary iid p=1/3, int8 U[-127,127], activations N(0,1))",
         "config": {
             "workload": (f"8B-shape batch-1 decode step: embedding row + {args.layers} layers x (q|k|v 6144x4096, "
@@ -353,7 +349,7 @@ def main():
                     and t.get("schedule") == args.schedule):
                 traffic = t.get("hbm_bytes_per_launch")
         kname = ("step_kernel<ordered> (whole step, one launch)" if schedule == pwg.SCHEDULE_PERSISTENT else
-                 "step_kernel<stream> (whole step; timed with its input-conversion kernel)")
+                 "stream_step_kernel<8> (whole step; timed with its input-conversion kernel)")
         result["roofline"] = {"bound": "hbm", "achieved": achieved_bps / 1e9, "peak": PEAK_HBM_BPS / 1e9,
                               "unit": "GB/s", "frac": achieved_bps / PEAK_HBM_BPS, "traffic": traffic,
                               "kernel": kname, "per_launch_bytes": step_bytes, "avg_launch_us": ms * 1e3}

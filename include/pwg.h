@@ -45,7 +45,7 @@ extern "C" {
 #endif
 #pragma GCC visibility push(default)
 
-#define PWG_VERSION 1
+#define PWG_VERSION 2
 #define PWG_MAX_COLS 16384
 
 enum {
@@ -64,12 +64,23 @@ enum {
   PWG_SCHEDULE_PERSISTENT = 1,  /* one persistent kernel; a device-wide barrier after
                                    every level, so level L+1 starts only when all of
                                    level L is done (the dependency of a chained step) */
-  PWG_SCHEDULE_STREAM = 2       /* the persistent kernel without level barriers: each
-                                   workgroup takes the levels in decoder order, but
-                                   levels overlap across workgroups.  Valid only when
-                                   no level reads another level's output (as in a
-                                   step over fixed inputs); it measures the weight
-                                   stream alone, without dependency waits */
+  PWG_SCHEDULE_STREAM = 2       /* one matrix-core kernel (after a small input
+                                   conversion kernel) without level barriers: the
+                                   16-row blocks of all levels and of the vocabulary
+                                   are split over the CUs, so levels overlap.  Valid
+                                   only when no level reads another level's output
+                                   (as in a step over fixed inputs); it measures the
+                                   weight stream alone, without dependency waits.
+                                   Needs PWG_LAYOUT_TILED weights, every level's cols
+                                   and hidden a multiple of 256 and at most 12288 */
+};
+
+/* Weight arrangements of a step description (pwg_step_desc.weight_layout). */
+enum {
+  PWG_LAYOUT_ROWS = 0,   /* T2 blobs and the int8 output table row-major
+                            (schedules LEVELS and PERSISTENT) */
+  PWG_LAYOUT_TILED = 1   /* the same bytes in 16-row x 64-byte tiles, see
+                            pwg_tile_rows (schedule STREAM) */
 };
 
 /* ---------------------------------------------------------------------------
@@ -122,6 +133,35 @@ int pwg_ternary_gemv(const void* w_packed, const float* row_scale,
                      const float* x, int32_t batch,
                      float* y, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Tiled arrangement (page section "The same weights take four execution
+ * paths": the loader arranges the stored values for the device at load
+ * time).  A row-major byte matrix of `rows` rows of `row_bytes` bytes (a T2
+ * blob: row_bytes = cols / 4; an int8 table: row_bytes = cols) becomes
+ * 16-row x 64-byte tiles of 1 KiB:
+ *   - rows are padded with zero bytes to a multiple of 16;
+ *   - tile (rb, tc) covers rows 16 rb .. 16 rb + 15 and bytes 64 tc .. 64 tc + 63
+ *     and sits at byte offset (rb * (row_bytes / 64) + tc) * 1024;
+ *   - inside a tile, byte (row 16 rb + i, column 64 tc + 16 q + b) is at
+ *     offset 256 q + 16 i + b  (i < 16, q < 4, b < 16).
+ * One wave load instruction (64 lanes x 16 bytes) then reads one tile and
+ * lane 16 q + i holds row i's bytes 16 q .. 16 q + 15 of the window: the
+ * operand layout of the 16 x 16 matrix-core instructions.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of the tiled arrangement: ceil(rows / 16) * 16 * row_bytes; 0 for an
+ * invalid shape (rows < 1, row_bytes < 64 or not a multiple of 64). */
+size_t pwg_tiled_size(int64_t rows, int64_t row_bytes);
+
+/* Writes the tiled arrangement of a row-major device matrix (asynchronous on
+ * `stream`, capturable, allocates nothing).
+ *   src          device, rows x row_bytes bytes, row-major
+ *   dst          device, at least pwg_tiled_size(rows, row_bytes) bytes; must
+ *                not overlap src
+ * Errors: PWG_ERR_ARG (null, bad shape), PWG_ERR_ALIGN, PWG_ERR_SIZE, PWG_ERR_HIP. */
+int pwg_tile_rows(const void* src, int64_t rows, int64_t row_bytes,
+                  void* dst, size_t dst_bytes, void* stream);
+
 /* Workspace bytes needed by pwg_int8_gemv_argmax for (rows, batch). */
 size_t pwg_argmax_workspace_bytes(int64_t rows, int32_t batch);
 
@@ -167,7 +207,7 @@ int pwg_embed_gather(const int8_t* table, const float* row_scale,
 /* One ternary GEMV level of a decode step (matrices that share an input are
  * stacked by rows: q|k|v and gate|up). */
 typedef struct pwg_level {
-  const void* w_packed;    /* device, T2 rows x cols */
+  const void* w_packed;    /* device, T2 rows x cols (arranged as weight_layout says) */
   const float* row_scale;  /* device, float32[rows] */
   const float* x;          /* device, float32[cols] */
   float* y;                /* device, float32[rows] */
@@ -187,13 +227,15 @@ typedef struct pwg_level {
 typedef struct pwg_step_desc {
   int32_t n_levels;
   int32_t schedule;              /* PWG_SCHEDULE_* */
+  int32_t weight_layout;         /* PWG_LAYOUT_*: of every w_packed and of out_table */
+  int32_t reserved;              /* 0 */
   const pwg_level* levels;       /* host array [n_levels] */
-  const int8_t* out_table;       /* int8 vocab x hidden */
+  const int8_t* out_table;       /* int8 vocab x hidden (arranged as weight_layout says) */
   const float* out_scale;        /* float32[vocab] */
   const float* h;                /* float32[hidden] */
   int64_t vocab;
   int64_t hidden;
-  const int8_t* emb_table;       /* int8 vocab x hidden */
+  const int8_t* emb_table;       /* int8 vocab x hidden, row-major (rows are gathered) */
   const float* emb_scale;        /* float32[vocab] */
   const int32_t* token_in;       /* int32[1] */
   int32_t* token_out;            /* int32[1] */
@@ -209,21 +251,28 @@ typedef struct pwg_step_desc {
 size_t pwg_step_workspace_bytes(const pwg_step_desc* desc);
 
 /* Prepare the workspace of a step: validates the description and, for the
- * persistent schedule, writes the device-side level table and resets the
- * barrier words.  Synchronous (it waits for its own copies); call it once per
- * set of buffers, outside stream capture, before pwg_decode_step_weights. */
+ * persistent and stream schedules, writes the device-side level table and
+ * work split and resets the barrier and status words.  Synchronous (it waits
+ * for its own copies); call it once per set of buffers, outside stream
+ * capture, before pwg_decode_step_weights.
+ * Errors: PWG_ERR_ARG, PWG_ERR_ALIGN, PWG_ERR_SIZE, PWG_ERR_HIP,
+ * PWG_ERR_UNSUPPORTED (a shape or layout the schedule does not take). */
 int pwg_step_plan(const pwg_step_desc* desc, void* stream);
 
 /* Enqueue one step on `stream` (capturable; no allocation, no sync).
  * Persistent schedule: one kernel with one workgroup per CU; every level
  * barrier wait is bounded (about 0.5 s), after which the kernel records a
- * timeout and ends instead of hanging; pwg_step_status reports it. */
+ * timeout and ends instead of hanging; pwg_step_status reports it.
+ * Stream schedule: a conversion kernel (every level's input and h into
+ * matrix-core operands in the workspace), then one kernel with one workgroup
+ * per CU; its only waits are inside a workgroup and are bounded the same way.
+ * The step's workspace is rewritten by every call: calls that overlap on one
+ * workspace race. */
 int pwg_decode_step_weights(const pwg_step_desc* desc, void* stream);
 
-/* Synchronously reads the step's status word (persistent schedule; always
- * PWG_OK for the levels schedule): PWG_ERR_HIP with a message if a level
- * barrier timed out or workgroups were not placed as planned.  Not for the
- * hot path. */
+/* Synchronously reads the step's status word (persistent and stream
+ * schedules; always PWG_OK for the levels schedule): PWG_ERR_HIP with a
+ * message if a bounded wait timed out.  Not for the hot path. */
 int pwg_step_status(const pwg_step_desc* desc, void* stream);
 
 /* Thread-local message of the last failed call on this thread ("" if none). */

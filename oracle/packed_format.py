@@ -27,6 +27,21 @@ from __future__ import annotations
 
 import numpy as np
 
+# Device tile arrangement (load-time re-arrangement of the stored values, page
+# "The Neutrino Engine", section "The same weights take four execution
+# paths"), written from its definition:
+#
+# * input: a row-major byte matrix of `rows` rows of `row_bytes` bytes
+#   (row_bytes a multiple of 64);
+# * rows are padded with zero bytes to a multiple of 16;
+# * tiles of 16 rows x 64 bytes (1 KiB) follow each other row-block by
+#   row-block, and within a row block from the left: tile (rb, tc) is the
+#   (rb * row_bytes / 64 + tc)-th 1 KiB of the output;
+# * inside a tile, the byte of row 16 rb + i and column 64 tc + 16 q + b
+#   (i < 16, q < 4, b < 16) sits at offset 256 q + 16 i + b.
+TILE_ROWS = 16
+TILE_BYTES = 64
+
 INVALID_CODE = 0b10
 
 
@@ -72,3 +87,36 @@ def decode(blob, rows: int, cols: int) -> np.ndarray:
             raise ValueError(f"invalid code 0b10 at row {r}, col {16 * j + m}")
         out[:, :, m] = np.where(code == 0b11, -1, code).astype(np.int8)
     return out.reshape(rows, cols)
+
+
+def tiled_nbytes(rows: int, row_bytes: int) -> int:
+    if rows < 1 or row_bytes < TILE_BYTES or row_bytes % TILE_BYTES:
+        raise ValueError("rows >= 1 and row_bytes a positive multiple of 64")
+    return -(-rows // TILE_ROWS) * TILE_ROWS * row_bytes
+
+
+def tile16x64(mat: np.ndarray) -> np.ndarray:
+    """The tile arrangement of a (rows, row_bytes) uint8 matrix, as a flat
+    uint8 array: pad the rows with zeros, cut into 16 x 64 tiles, and inside a
+    tile put the four 16-byte column quarters one after another, each holding
+    the 16 rows' slices of that quarter in row order."""
+    mat = np.ascontiguousarray(mat, dtype=np.uint8)
+    rows, row_bytes = mat.shape
+    out_rows = tiled_nbytes(rows, row_bytes) // row_bytes
+    padded = np.zeros((out_rows, row_bytes), np.uint8)
+    padded[:rows] = mat
+    # axes: row block, row in block (i), tile column, quarter (q), byte (b)
+    t = padded.reshape(out_rows // TILE_ROWS, TILE_ROWS, row_bytes // TILE_BYTES, 4, 16)
+    # to: row block, tile column, quarter, row in block, byte
+    return np.ascontiguousarray(t.transpose(0, 2, 3, 1, 4)).reshape(-1)
+
+
+def untile16x64(flat: np.ndarray, rows: int, row_bytes: int) -> np.ndarray:
+    """Inverse of tile16x64 (drops the padding rows)."""
+    flat = np.ascontiguousarray(flat, dtype=np.uint8).reshape(-1)
+    n = tiled_nbytes(rows, row_bytes)
+    if flat.size != n:
+        raise ValueError("size does not match the tiled arrangement")
+    out_rows = n // row_bytes
+    t = flat.reshape(out_rows // TILE_ROWS, row_bytes // TILE_BYTES, 4, TILE_ROWS, 16)
+    return np.ascontiguousarray(t.transpose(0, 3, 1, 2, 4)).reshape(out_rows, row_bytes)[:rows]

@@ -20,7 +20,8 @@ __all__ = [
     "PwgError", "lib", "packed_size", "pack_weights", "unpack_weights", "ternary_gemv",
     "argmax_workspace_bytes", "int8_gemv_argmax", "embed_gather", "Level", "StepDesc",
     "step_workspace_bytes", "step_plan", "decode_step_weights", "step_status", "last_error", "version",
-    "SCHEDULE_LEVELS", "SCHEDULE_PERSISTENT", "SCHEDULE_STREAM", "LIB_PATH",
+    "tiled_size", "tile_rows", "SCHEDULE_LEVELS", "SCHEDULE_PERSISTENT", "SCHEDULE_STREAM",
+    "LAYOUT_ROWS", "LAYOUT_TILED", "layout_for_schedule", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpwg.so")
@@ -31,6 +32,13 @@ ERR_NAMES = {-1: "PWG_ERR_ARG", -2: "PWG_ERR_ALIGN", -3: "PWG_ERR_SIZE", -4: "PW
 SCHEDULE_LEVELS = 0
 SCHEDULE_PERSISTENT = 1
 SCHEDULE_STREAM = 2
+LAYOUT_ROWS = 0
+LAYOUT_TILED = 1
+
+
+def layout_for_schedule(schedule: int) -> int:
+    """Weight arrangement a schedule takes (the stream schedule runs on tiles)."""
+    return LAYOUT_TILED if schedule == SCHEDULE_STREAM else LAYOUT_ROWS
 
 
 class PwgError(RuntimeError):
@@ -61,7 +69,8 @@ class Level(C.Structure):
 
 class _StepDesc(C.Structure):
     _fields_ = [
-        ("n_levels", _i32), ("schedule", _i32), ("levels", C.POINTER(Level)),
+        ("n_levels", _i32), ("schedule", _i32), ("weight_layout", _i32), ("reserved", _i32),
+        ("levels", C.POINTER(Level)),
         ("out_table", _vp), ("out_scale", _vp), ("h", _vp), ("vocab", _i64), ("hidden", _i64),
         ("emb_table", _vp), ("emb_scale", _vp), ("token_in", _vp), ("token_out", _vp),
         ("emb_row_out", _vp), ("emb_scale_out", _vp), ("emb_deq_out", _vp), ("logits_out", _vp),
@@ -83,6 +92,8 @@ _tgemv = _sig("pwg_ternary_gemv", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp,
 _argmax_ws = _sig("pwg_argmax_workspace_bytes", _sz, _i64, _i32)
 _i8argmax = _sig("pwg_int8_gemv_argmax", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _sz, _vp, _vp, _vp)
 _gather = _sig("pwg_embed_gather", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _vp)
+_tiled_size = _sig("pwg_tiled_size", _sz, _i64, _i64)
+_tile_rows = _sig("pwg_tile_rows", C.c_int, _vp, _i64, _i64, _vp, _sz, _vp)
 _step_ws = _sig("pwg_step_workspace_bytes", _sz, C.POINTER(_StepDesc))
 _step_plan = _sig("pwg_step_plan", C.c_int, C.POINTER(_StepDesc), _vp)
 _step = _sig("pwg_decode_step_weights", C.c_int, C.POINTER(_StepDesc), _vp)
@@ -92,6 +103,7 @@ _version = _sig("pwg_version", C.c_int)
 
 EXPORTED = ["pwg_packed_size", "pwg_pack_weights", "pwg_unpack_weights", "pwg_ternary_gemv",
             "pwg_argmax_workspace_bytes", "pwg_int8_gemv_argmax", "pwg_embed_gather",
+            "pwg_tiled_size", "pwg_tile_rows",
             "pwg_step_workspace_bytes", "pwg_step_plan", "pwg_decode_step_weights",
             "pwg_step_status", "pwg_last_error", "pwg_version"]
 
@@ -199,6 +211,22 @@ def embed_gather(table, row_scale, ids, rows_out=None, scales_out=None, deq_out=
     return rows_out, scales_out[:n], (deq_out if dequant else None)
 
 
+# ---------------------------------------------------------------- tiled arrangement
+def tiled_size(rows: int, row_bytes: int) -> int:
+    return _tiled_size(rows, row_bytes)
+
+
+def tile_rows(src, rows: int, row_bytes: int, dst=None, stream=None):
+    """16-row x 64-byte tile arrangement of a row-major device byte matrix
+    (a T2 blob: row_bytes = cols // 4; an int8 table: row_bytes = cols)."""
+    import torch
+    need = _tiled_size(rows, row_bytes)
+    if dst is None:
+        dst = torch.empty(max(need, 16), dtype=torch.uint8, device=src.device)
+    _check(_tile_rows(_ptr(src), rows, row_bytes, _ptr(dst), dst.numel() * dst.element_size(), _stream(stream)))
+    return dst
+
+
 # ---------------------------------------------------------------- decode step
 @dataclass
 class StepDesc:
@@ -217,6 +245,9 @@ class StepDesc:
     logits_out: object = None
     workspace: object = None
     schedule: int = SCHEDULE_LEVELS
+    weight_layout: int = LAYOUT_ROWS
+    vocab: int | None = None        # rows of the output table (when it is stored tiled)
+    hidden: int | None = None
     _c: object = field(default=None, repr=False)
     _levels_c: object = field(default=None, repr=False)
 
@@ -226,10 +257,11 @@ class StepDesc:
             for i, (w, s, x, y, r, k) in enumerate(self.levels):
                 arr[i] = Level(_ptr(w), _ptr(s), _ptr(x), _ptr(y), r, k)
             self._levels_c = arr
-            vocab, hidden = self.out_table.shape
+            vocab = self.vocab if self.vocab is not None else self.out_table.shape[0]
+            hidden = self.hidden if self.hidden is not None else self.out_table.shape[1]
             ws = self.workspace
             self._c = _StepDesc(
-                len(self.levels), self.schedule, C.cast(arr, C.POINTER(Level)),
+                len(self.levels), self.schedule, self.weight_layout, 0, C.cast(arr, C.POINTER(Level)),
                 _ptr(self.out_table), _ptr(self.out_scale), _ptr(self.h), vocab, hidden,
                 _ptr(self.emb_table), _ptr(self.emb_scale), _ptr(self.token_in), _ptr(self.token_out),
                 _ptr(self.emb_row_out), _ptr(self.emb_scale_out), _ptr(self.emb_deq_out), _ptr(self.logits_out),

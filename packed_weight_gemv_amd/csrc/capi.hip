@@ -23,12 +23,6 @@ int check_shape(int64_t rows, int64_t cols, const char* fn) {
   return PWG_OK;
 }
 
-#define TRY(expr)                 \
-  do {                            \
-    const int _rc = (expr);       \
-    if (_rc != PWG_OK) return _rc; \
-  } while (0)
-
 int validate_ternary(const void* w, const float* s, int64_t rows, int64_t cols, const float* x, int32_t batch,
                      const float* y, const char* fn) {
   TRY(check_shape(rows, cols, fn));
@@ -99,6 +93,26 @@ extern "C" int pwg_embed_gather(const int8_t* table, const float* row_scale, int
 }
 
 // ---------------------------------------------------------------------------
+// Tiled arrangement
+// ---------------------------------------------------------------------------
+extern "C" size_t pwg_tiled_size(int64_t rows, int64_t row_bytes) { return tiled_bytes(rows, row_bytes); }
+
+extern "C" int pwg_tile_rows(const void* src, int64_t rows, int64_t row_bytes, void* dst, size_t dst_bytes,
+                             void* stream) {
+  const char* fn = "pwg_tile_rows";
+  if (rows < 1 || rows > (int64_t{1} << 30) || row_bytes < 64 || row_bytes % 64 != 0 || row_bytes > (int64_t{1} << 20))
+    return fail(PWG_ERR_ARG, "%s: rows must be in [1, 2^30] and row_bytes a multiple of 64 in [64, 2^20]", fn);
+  TRY(check_ptr(src, fn, "src"));
+  TRY(check_ptr(dst, fn, "dst"));
+  const size_t need = tiled_bytes(rows, row_bytes);
+  if (dst_bytes < need) return fail(PWG_ERR_SIZE, "%s: dst has %zu bytes, needs %zu", fn, dst_bytes, need);
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  const size_t src_bytes = static_cast<size_t>(rows) * static_cast<size_t>(row_bytes);
+  if (s0 < d0 + need && d0 < s0 + src_bytes) return fail(PWG_ERR_ARG, "%s: src and dst overlap", fn);
+  return launch_tile_rows(src, rows, row_bytes, dst, stream);
+}
+
+// ---------------------------------------------------------------------------
 // Decode step
 // ---------------------------------------------------------------------------
 namespace {
@@ -110,13 +124,26 @@ int validate_step(const pwg_step_desc* d) {
       d->schedule != PWG_SCHEDULE_STREAM)
     return fail(PWG_ERR_ARG, "%s: unknown schedule %d", fn, d->schedule);
   if (d->n_levels < 0 || d->n_levels > 4096) return fail(PWG_ERR_ARG, "%s: n_levels out of range", fn);
+  if (d->weight_layout != PWG_LAYOUT_ROWS && d->weight_layout != PWG_LAYOUT_TILED)
+    return fail(PWG_ERR_ARG, "%s: unknown weight layout %d", fn, d->weight_layout);
+  const int want = d->schedule == PWG_SCHEDULE_STREAM ? PWG_LAYOUT_TILED : PWG_LAYOUT_ROWS;
+  if (d->weight_layout != want)
+    return fail(PWG_ERR_UNSUPPORTED, "%s: schedule %d takes weight layout %d (got %d)", fn, d->schedule, want,
+                d->weight_layout);
   if (d->n_levels > 0 && !d->levels) return fail(PWG_ERR_ARG, "%s: levels is null", fn);
   for (int i = 0; i < d->n_levels; ++i) {
     const pwg_level& L = d->levels[i];
     const int rc = validate_ternary(L.w_packed, L.row_scale, L.rows, L.cols, L.x, 1, L.y, fn);
     if (rc != PWG_OK) return fail(rc, "%s (level %d)", pwg_last_error(), i);
   }
-  TRY(validate_int8(d->out_table, d->out_scale, d->vocab, d->hidden, fn));
+  if (d->schedule == PWG_SCHEDULE_STREAM) {
+    TRY(check_shape(d->vocab, d->hidden, fn));
+    TRY(check_ptr(d->out_table, fn, "out_table"));
+    TRY(check_ptr(d->out_scale, fn, "out_scale"));
+    TRY(step_stream_check(d));
+  } else {
+    TRY(validate_int8(d->out_table, d->out_scale, d->vocab, d->hidden, fn));
+  }
   TRY(check_ptr(d->h, fn, "h"));
   TRY(check_ptr(d->emb_table, fn, "emb_table"));
   TRY(check_ptr(d->emb_scale, fn, "emb_scale"));
@@ -134,6 +161,7 @@ int validate_step(const pwg_step_desc* d) {
 
 extern "C" size_t pwg_step_workspace_bytes(const pwg_step_desc* d) {
   if (!d || d->vocab < 1) return 0;
+  if (d->schedule == PWG_SCHEDULE_STREAM) return step_stream_workspace(d);
   return argmax_ws(d->vocab, 1) + step_persistent_workspace(d);
 }
 
@@ -142,6 +170,7 @@ extern "C" int pwg_step_plan(const pwg_step_desc* d, void* stream) {
   if (d->workspace_bytes < pwg_step_workspace_bytes(d))
     return fail(PWG_ERR_SIZE, "pwg_step_plan: workspace %zu < %zu bytes", d->workspace_bytes,
                 pwg_step_workspace_bytes(d));
+  if (d->schedule == PWG_SCHEDULE_STREAM) return step_stream_plan(d, 0, stream);
   if (d->schedule != PWG_SCHEDULE_LEVELS) return step_persistent_plan(d, argmax_ws(d->vocab, 1), stream);
   return PWG_OK;
 }
@@ -149,6 +178,7 @@ extern "C" int pwg_step_plan(const pwg_step_desc* d, void* stream) {
 extern "C" int pwg_step_status(const pwg_step_desc* d, void* stream) {
   TRY(validate_step(d));
   if (d->schedule == PWG_SCHEDULE_LEVELS) return PWG_OK;
+  if (d->schedule == PWG_SCHEDULE_STREAM) return step_stream_status(d, 0, stream);
   return step_persistent_status(d, argmax_ws(d->vocab, 1), stream);
 }
 
@@ -157,6 +187,7 @@ extern "C" int pwg_decode_step_weights(const pwg_step_desc* d, void* stream) {
   if (d->workspace_bytes < pwg_step_workspace_bytes(d))
     return fail(PWG_ERR_SIZE, "pwg_decode_step_weights: workspace %zu < %zu bytes", d->workspace_bytes,
                 pwg_step_workspace_bytes(d));
+  if (d->schedule == PWG_SCHEDULE_STREAM) return step_stream_launch(d, 0, stream);
   if (d->schedule != PWG_SCHEDULE_LEVELS) return step_persistent_launch(d, argmax_ws(d->vocab, 1), stream);
   // Levels schedule: embedding row, every level in decoder order, output
   // projection + argmax, all on one stream.

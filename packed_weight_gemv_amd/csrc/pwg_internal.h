@@ -12,6 +12,12 @@ namespace pwg {
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
 
+#define TRY(expr)                  \
+  do {                             \
+    const int _rc = (expr);        \
+    if (_rc != PWG_OK) return _rc; \
+  } while (0)
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool valid_batch(int32_t b) { return b == 1 || b == 4 || b == 8 || b == 16; }
 inline bool valid_cols(int64_t cols) { return cols >= 64 && cols % 64 == 0 && cols <= PWG_MAX_COLS; }
@@ -44,5 +50,16 @@ size_t step_persistent_workspace(const pwg_step_desc* d);
 int step_persistent_plan(const pwg_step_desc* d, size_t ws_offset, void* stream);
 int step_persistent_launch(const pwg_step_desc* d, size_t ws_offset, void* stream);
 int step_persistent_status(const pwg_step_desc* d, size_t ws_offset, void* stream);
+
+// Stream schedule on the matrix cores (step_stream.hip): tiled weights.
+int step_stream_check(const pwg_step_desc* d);
+size_t step_stream_workspace(const pwg_step_desc* d);
+int step_stream_plan(const pwg_step_desc* d, size_t ws_offset, void* stream);
+int step_stream_launch(const pwg_step_desc* d, size_t ws_offset, void* stream);
+int step_stream_status(const pwg_step_desc* d, size_t ws_offset, void* stream);
+
+// 16-row x 64-byte tile arrangement (tile.hip).
+size_t tiled_bytes(int64_t rows, int64_t row_bytes);
+int launch_tile_rows(const void* src, int64_t rows, int64_t row_bytes, void* dst, void* stream);
 
 }  // namespace pwg

@@ -1,0 +1,83 @@
+// Data layout of the stream schedule (matrix-core step): the converted
+// activation operands of each level in the workspace, and the plan tables.
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+#include "device_common.h"
+
+namespace pwg {
+namespace stream {
+
+// Operand bytes of one MFMA: ternary B = 4 lane groups x 12 digit columns x
+// 16 bytes (32 FP4 nibbles); int8 B = 4 lane groups x 3 digit columns x 16 bytes.
+constexpr int kTernaryMfmaBytes = 4 * 12 * 16;
+constexpr int kInt8MfmaBytes = 4 * 3 * 16;
+constexpr int kSectionMfmas = 4;                  // int8 MFMAs per exponent section (256 values of h)
+constexpr int kMaxStreamCols = 12288;             // two operand buffers of this width fit in LDS
+constexpr size_t kMaxLds = 160 * 1024;
+constexpr size_t kFlagBytes = 128;                // ready word, done words, per-wave argmax keys
+constexpr size_t kParkBytes = 16 * 1024;          // tiles a wave re-reads after its last one
+enum { kKindTernary = 0, kKindInt8 = 1 };
+
+// Ternary level region (per K = cols): B digits of every MFMA, then the B
+// scale dwords (per group of 4 MFMAs, one per lane), then the A scale dwords
+// (per group of 4 MFMAs, one per lane group).  One scale byte per MFMA.
+__host__ __device__ constexpr size_t ternary_mfmas(int64_t cols) { return static_cast<size_t>(cols / 128); }
+__host__ __device__ constexpr size_t ternary_quads(int64_t cols) { return (ternary_mfmas(cols) + 3) / 4; }
+__host__ __device__ constexpr size_t ternary_bsc_off(int64_t cols) { return ternary_mfmas(cols) * kTernaryMfmaBytes; }
+__host__ __device__ constexpr size_t ternary_asc_off(int64_t cols) { return ternary_bsc_off(cols) + ternary_quads(cols) * 256; }
+__host__ __device__ constexpr size_t ternary_region_bytes(int64_t cols) { return ternary_asc_off(cols) + ternary_quads(cols) * 16; }
+// int8 (h) region: B digits of every MFMA, then one int32 exponent per section.
+__host__ __device__ constexpr size_t int8_exp_off(int64_t hidden) { return static_cast<size_t>(hidden / 64) * kInt8MfmaBytes; }
+__host__ __device__ constexpr size_t int8_region_bytes(int64_t hidden) {
+  return (int8_exp_off(hidden) + static_cast<size_t>((hidden / 64 + kSectionMfmas - 1) / kSectionMfmas) * 4 + 15) / 16 * 16;
+}
+static_assert(ternary_region_bytes(kMaxStreamCols) % 16 == 0, "regions are copied in 16-byte units");
+
+// One ternary level or (last entry) the vocabulary.
+struct Level {
+  const unsigned char* w;   // tiled weights (16-row x 64-byte tiles)
+  const float* scale;       // row scales
+  const float* x;           // input (ternary: x; vocabulary: h)
+  float* y;                 // output (ternary: y; vocabulary: logits or null)
+  const unsigned char* b;   // converted operand region (workspace)
+  unsigned char* b_out;     // same region, written by the conversion kernel
+  int rows, cols;
+  int tiles;                // tiles per 16-row block
+  int kind;                 // kKindTernary or kKindInt8
+  int bsc_off, asc_off;     // ternary: scale offsets; int8: bsc_off = exponent offset
+  int b_bytes;              // region bytes (a multiple of 16)
+  int pad;
+};
+
+// Blocks [b0, b1) of level `level`: one contiguous part of a workgroup's range.
+struct Seg {
+  int level, b0, b1, pad;
+};
+
+struct Plan {
+  int n_levels;             // ternary levels; levels[n_levels] is the vocabulary
+  int grid;
+  int seg_stride;
+  int buf_bytes;            // one LDS operand buffer
+  int vocab, hidden;
+  int depth;                // tiles in flight per compute wave
+  int pad;
+  const int* seg_count;     // [grid]
+  const float* h;
+  const dev::u32x4* emb_table;
+  const float* emb_scale;
+  const int32_t* token_in;
+  int32_t* token_out;
+  dev::u32x4* emb_row_out;
+  float* emb_scale_out;
+  float4* emb_deq_out;
+  const unsigned char* park; // kParkBytes of workspace
+  unsigned long long* partials;
+  unsigned* arrivals;
+  unsigned* status;
+};
+
+}  // namespace stream
+}  // namespace pwg

@@ -1,0 +1,862 @@
+// Stream schedule of the decode step on the CDNA4 matrix cores.
+//
+// Page "The Neutrino Engine": section "A 104 microsecond floor inside a 694
+// microsecond step" (batch-1 decode applies every projection to the current
+// activations once per token, the output projection scores the whole
+// vocabulary, the token is the greedy argmax), section "The file is not the
+// traffic" (ternary projections with row scales, int8 vocabulary tables) and
+// section "The same weights take four execution paths" (the loader arranges
+// the stored values for the device at load time: here, 16-row x 64-byte
+// tiles, one 1 KiB tile per wave load instruction).
+//
+// Ternary levels run on v_mfma_scale_f32_16x16x128_f8f6f4 with both operands
+// in FP4 (e2m1).  Operand A is 16 weight rows x 128 weights: masking a T2
+// word with 0xCCCCCCCC, and again after a 2-bit left shift, leaves nibbles
+// 0b0100 / 0b1100 / 0 for w = +1 / -1 / 0, which are the FP4 values +2, -2
+// and 0, so a 16-byte tile slice becomes the A operands of two instructions
+// with three VALU operations per word.  Operand B is 128 x 16: column n holds
+// base-4 digit n (n < 12) of the activations rounded to 23-bit fixed point per
+// 32-element block, with the sign applied; the E8M0 block scales (one per 32
+// K-values and operand lane) carry the block exponent and the digit weight.
+// Digits and weights are small integers, so every product is exact; the
+// instruction sums in float32.
+//
+// The int8 output projection runs on v_mfma_i32_16x16x64_i8: A is the tile
+// as stored, B's columns are three balanced base-256 digits of h rounded to
+// 23-bit fixed point per 256-element section; four instructions accumulate
+// exactly in int32 before one conversion to float per section.
+//
+// Work: 16-row blocks of every level and of the vocabulary, split over the
+// workgroups (one per CU) as contiguous ranges of equal cost, and within a
+// workgroup over 7 compute waves.  Each compute wave streams its tiles through
+// a ring of D registers (D tiles in flight, loads issued D tiles ahead across
+// block, level and segment boundaries).  Wave 0 copies each segment's
+// converted activation operands into one of two LDS buffers, ahead of the
+// compute waves.  The last workgroup to finish reduces the argmax.
+#include <algorithm>
+#include <cmath>
+#include <vector>
+
+#include "device_common.h"
+#include "pwg_internal.h"
+#include "step_stream.h"
+
+namespace pwg {
+namespace {
+
+using namespace dev;
+using namespace stream;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 8;               // wave 0: control; waves 1..7: compute
+constexpr int kCompute = kWaves - 1;
+constexpr int kThreads = kWaves * 64;
+constexpr unsigned kMask = 0xCCCCCCCCu;
+constexpr unsigned long long kSpinLimit = 50000000ull;  // 0.5 s of the 100 MHz real-time counter
+enum : unsigned { kStatusOk = 0, kStatusTimeout = 1 };
+
+#define PWG_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+typedef const __attribute__((address_space(4))) float cfloat;
+// Global-address-space views: generic (flat) accesses would also count on
+// the LDS counter, and every LDS wait would then wait for the weight loads.
+typedef const __attribute__((address_space(1))) u32x4 g_u32x4;
+typedef __attribute__((address_space(1))) float g_float;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) f32x4 g_f32x4;
+typedef const __attribute__((address_space(1))) f32x4 cg_f32x4;
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ unsigned uni(unsigned v) {
+  return static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
+}
+template <typename T>
+__device__ __forceinline__ T* uni(T* p) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = uni(static_cast<unsigned>(v)), hi = uni(static_cast<unsigned>(v >> 32));
+  return reinterpret_cast<T*>((static_cast<unsigned long long>(hi) << 32) | lo);
+}
+
+// LDS flag store that does not make the compiler wait for outstanding
+// global-to-LDS copies first (the flags are never a copy's destination).
+__device__ __forceinline__ void lds_publish(int* p, int v) {
+  const unsigned addr = static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) int*)p));
+  asm volatile("s_waitcnt lgkmcnt(0)\n\tds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ int lds_acquire(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Sum over the 16 lanes of a DPP row; every lane ends with the same total.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // lane ^ 1
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // lane ^ 2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // half mirror
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // mirror
+  return v;
+}
+
+// Blocks [b0, b1) of segment range [s0, s1) that compute wave k takes.
+__device__ __forceinline__ void wave_blocks(int s0, int s1, int k, int& b0, int& b1) {
+  const int n = s1 - s0;
+  b0 = s0 + (k * n) / kCompute;
+  b1 = s0 + ((k + 1) * n) / kCompute;
+}
+
+// The tile stream of one compute wave: the wave's blocks of every segment of
+// its workgroup, in order, as contiguous runs of 1 KiB tiles.  A run is a
+// whole number of blocks and a block a whole number of load groups, so runs
+// change only between groups.  State is wave-uniform.
+struct TileStream {
+  const Seg* segs;
+  const Level* levels;
+  int nseg, k;
+  int ps;                     // segment of the current run
+  const unsigned char* ptr;   // this lane's 16 bytes of the next tile
+  const unsigned char* park;  // kParkBytes re-read once the stream is exhausted
+  int left;                   // tiles left in the current run
+
+  // Moves to the next non-empty run from segment ps on (or parks).
+  __device__ __forceinline__ void open(unsigned lane) {
+    while (ps < nseg) {
+      const Seg& s = segs[ps];
+      int b0, b1;
+      wave_blocks(s.b0, s.b1, k, b0, b1);
+      const Level& L = levels[s.level];
+      if (b1 > b0) {
+        ptr = uni(L.w) + (static_cast<size_t>(b0) * L.tiles) * 1024u + lane * 16u;
+        left = uni((b1 - b0) * L.tiles);
+        return;
+      }
+      ps = uni(ps + 1);
+    }
+    ptr = park + lane * 16u;
+    left = 0;
+  }
+  // Before a group of loads: switch runs at a run's end.
+  __device__ __forceinline__ void refresh(unsigned lane) {
+    if (left == 0) {
+      if (ps < nseg) ps = uni(ps + 1);
+      open(lane);
+    }
+  }
+  __device__ __forceinline__ u32x4 load(int j) const {
+    return __builtin_nontemporal_load((const g_u32x4*)(ptr + 1024 * j));
+  }
+  // After a group of D loads (branch-free, so the loop body stays one basic
+  // block and the scheduling barriers around it hold).
+  template <int D>
+  __device__ __forceinline__ void advance() {
+    const int step = left > 0 ? D : 0;
+    ptr += step * 1024;
+    left = uni(left - step);
+  }
+};
+
+// A operands of one ternary tile slice: FP4 nibbles +2 / -2 / 0 of the 64
+// weights in this lane's 16 bytes (two MFMAs' worth).
+__device__ __forceinline__ void ternary_unpack(const u32x4 v, v8i& a0, v8i& a1) {
+  a0 = v8i{static_cast<int>(v.x & kMask), static_cast<int>((v.x << 2) & kMask), static_cast<int>(v.y & kMask),
+           static_cast<int>((v.y << 2) & kMask), 0, 0, 0, 0};
+  a1 = v8i{static_cast<int>(v.z & kMask), static_cast<int>((v.z << 2) & kMask), static_cast<int>(v.w & kMask),
+           static_cast<int>((v.w << 2) & kMask), 0, 0, 0, 0};
+}
+
+// Two FP4 MFMAs over K-values 256 t .. 256 t + 255 of a ternary block.
+// buf: the level's operand region in LDS; kOdd: t is odd (the scale bytes of
+// MFMAs 2t, 2t + 1 are then bytes 2 and 3 of the dwords read at t - 1).
+template <bool kOdd>
+__device__ __forceinline__ void ternary_mfma(const v8i& a0, const v8i& a1, int t, const unsigned char* buf,
+                                             int bsc_off, int asc_off, unsigned boff, unsigned lane, unsigned g,
+                                             unsigned& sb, unsigned& sa, v4f& acc0, v4f& acc1) {
+  const u32x4 b0 = *reinterpret_cast<const u32x4*>(buf + (2 * t) * kTernaryMfmaBytes + boff);
+  const u32x4 b1 = *reinterpret_cast<const u32x4*>(buf + (2 * t + 1) * kTernaryMfmaBytes + boff);
+  if (!kOdd) {  // scales of MFMAs 2t .. 2t + 3 (one byte each)
+    sb = *reinterpret_cast<const unsigned*>(buf + bsc_off + (t >> 1) * 256 + lane * 4);
+    sa = *reinterpret_cast<const unsigned*>(buf + asc_off + (t >> 1) * 16 + g * 4);
+  }
+  const v8i B0 = {static_cast<int>(b0.x), static_cast<int>(b0.y), static_cast<int>(b0.z), static_cast<int>(b0.w), 0, 0, 0, 0};
+  const v8i B1 = {static_cast<int>(b1.x), static_cast<int>(b1.y), static_cast<int>(b1.z), static_cast<int>(b1.w), 0, 0, 0, 0};
+  if (kOdd) {
+    acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, B0, acc0, 4, 4, 2, static_cast<int>(sa), 2, static_cast<int>(sb));
+    acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, B1, acc1, 4, 4, 3, static_cast<int>(sa), 3, static_cast<int>(sb));
+  } else {
+    acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, B0, acc0, 4, 4, 0, static_cast<int>(sa), 0, static_cast<int>(sb));
+    acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, B1, acc1, 4, 4, 1, static_cast<int>(sa), 1, static_cast<int>(sb));
+  }
+}
+
+// One int8 MFMA over K-values 64 t .. 64 t + 63 of a vocabulary block.
+__device__ __forceinline__ void int8_mfma(const u32x4 v, int t, const unsigned char* buf, unsigned boff, v4i& iacc) {
+  const u32x4 b = *reinterpret_cast<const u32x4*>(buf + t * kInt8MfmaBytes + boff);
+  const v4i A = {static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w)};
+  const v4i B = {static_cast<int>(b.x), static_cast<int>(b.y), static_cast<int>(b.z), static_cast<int>(b.w)};
+  iacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, iacc, 0, 0, 0);
+}
+// End of an exponent section (4 tiles): the exact int32 sums, scaled into
+// the float accumulator.
+__device__ __forceinline__ void int8_section(int t, const unsigned char* buf, int exp_off, int cexp, v4i& iacc,
+                                             v4f& facc) {
+  const int e = *reinterpret_cast<const int*>(buf + exp_off + (t / kSectionMfmas) * 4) + cexp;
+  // |iacc| <= 4 * 64 * 127 * 128 < 2^24: the conversion is exact
+  facc.x += ldexpf(static_cast<float>(iacc.x), e);
+  facc.y += ldexpf(static_cast<float>(iacc.y), e);
+  facc.z += ldexpf(static_cast<float>(iacc.z), e);
+  facc.w += ldexpf(static_cast<float>(iacc.w), e);
+  iacc = v4i{0, 0, 0, 0};
+}
+
+// The 16 row scales of block `blk` (rows 16 blk .. 16 blk + 15, clamped to
+// rows - 1) through scalar loads; returns the scale of row 4 g + i.
+__device__ __forceinline__ v4f block_scales(const float* scale, int blk, int rows, unsigned g) {
+  cfloat* s = (cfloat*)scale;
+  float r[16];
+  const int base = blk * 16;
+  if (base + 16 <= rows) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = s[base + i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = s[base + i < rows ? base + i : rows - 1];
+  }
+  // (readfirstlane keeps the values in scalar registers: otherwise the
+  // per-lane choice below becomes a per-lane vector load)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r[i] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(r[i])));
+  v4f out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = g == 0 ? r[i] : g == 1 ? r[4 + i] : g == 2 ? r[8 + i] : r[12 + i];
+  return out;
+}
+
+// Embedding row of the previous token (workgroup 0, control wave).
+__device__ __forceinline__ void embed_row(const Plan& P, unsigned lane) {
+  const int id = *P.token_in;
+  const bool ok = id >= 0 && id < P.vocab;
+  const int nchunks = P.hidden >> 4;
+  const float s = ok ? P.emb_scale[id] : __builtin_nanf("");
+  if (lane == 0) *P.emb_scale_out = s;
+  for (int c0 = 0; c0 < nchunks; c0 += 64) {  // wave-uniform trip count
+    const int c = c0 + static_cast<int>(lane);
+    if (c < nchunks) {
+      const u32x4 v = ok ? P.emb_table[static_cast<size_t>(id) * nchunks + c] : u32x4{0u, 0u, 0u, 0u};
+      P.emb_row_out[c] = v;
+      if (P.emb_deq_out) {
+        const unsigned wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          P.emb_deq_out[4 * c + q] =
+              ok ? make_float4(static_cast<float>(static_cast<int8_t>(wd[q] & 0xFF)) * s,
+                               static_cast<float>(static_cast<int8_t>((wd[q] >> 8) & 0xFF)) * s,
+                               static_cast<float>(static_cast<int8_t>((wd[q] >> 16) & 0xFF)) * s,
+                               static_cast<float>(static_cast<int8_t>(wd[q] >> 24)) * s)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __restrict__ plan,
+                                                                   const Level* __restrict__ levels,
+                                                                   const Seg* __restrict__ all_segs) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const Plan& P = *plan;
+  const unsigned lane = threadIdx.x & 63u;
+  const unsigned wave = uni(threadIdx.x >> 6);
+  const int nseg = uni(P.seg_count[blockIdx.x]);
+  const Seg* segs = all_segs + static_cast<size_t>(blockIdx.x) * P.seg_stride;
+  const int buf_bytes = P.buf_bytes;
+  int* ready = reinterpret_cast<int*>(smem + 2 * buf_bytes);  // highest segment whose operands are in LDS
+  int* done = ready + 1;                                       // [kWaves]: highest segment a wave finished
+  unsigned long long* wkeys = reinterpret_cast<unsigned long long*>(smem + 2 * buf_bytes + 64);
+  if (threadIdx.x == 0) *ready = -1;
+  if (threadIdx.x < kWaves) done[threadIdx.x] = -1;
+  __syncthreads();
+
+  float best = -__builtin_inff();
+  unsigned best_idx = 0xFFFFFFFFu;
+  if (wave == 0) {
+    // Control wave: segment s's operand region into buffer s & 1, once every
+    // compute wave is done with segment s - 2 (the buffer's last user).
+    bool late = false;
+    for (int s = 0; s < nseg; ++s) {
+      if (s >= 2) {
+        const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+        while (true) {
+          const int d = (lane >= 1 && lane < kWaves) ? lds_acquire(&done[lane]) : s;
+          if (__all(d >= s - 2)) break;
+          if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
+            late = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      const Level& L = levels[segs[s].level];
+      const unsigned char* src = uni(L.b);
+      const int bytes = uni(L.b_bytes);
+      unsigned char* dst = smem + (s & 1) * buf_bytes;
+      for (int o = 0; o < bytes; o += 1024)
+        if (o + 16 * static_cast<int>(lane) < bytes)
+          __builtin_amdgcn_global_load_lds(src + o + 16 * lane, PWG_LDS(dst + o), 16, 0, 0);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed in LDS
+      lds_publish(ready, s);
+      if (s == 0 && blockIdx.x == 0) embed_row(P, lane);
+    }
+    if (nseg == 0 && blockIdx.x == 0) embed_row(P, lane);
+    if (late && lane == 0) __hip_atomic_store(P.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    const int k = static_cast<int>(wave) - 1;
+    const unsigned n = lane & 15u, g = lane >> 4;
+    TileStream ts;
+    ts.segs = segs;
+    ts.levels = levels;
+    ts.nseg = nseg;
+    ts.k = k;
+    ts.ps = 0;
+    ts.park = P.park;
+    ts.open(lane);
+    // Two groups of G tile registers: one group's loads are in flight while
+    // the other group is consumed (G == 0: one tile at a time, no prefetch).
+    constexpr int GR = G > 0 ? G : 1;
+    u32x4 ra[GR], rb[GR];
+    auto issue = [&](u32x4(&x)[GR]) {
+      ts.refresh(lane);
+#pragma unroll
+      for (int j = 0; j < GR; ++j) x[j] = ts.load(j);
+      ts.template advance<GR>();
+    };
+    if (G > 0) issue(ra);
+
+    const unsigned tboff = (12u * g + (n < 12u ? n : n - 12u)) * 16u;  // ternary B entry of this lane
+    const unsigned iboff = (3u * g + n % 3u) * 16u;                    // int8 B entry of this lane
+    const int icexp = n < 3u ? static_cast<int>(8u * n) : -1000;       // digit weight (columns >= 3 vanish)
+    bool late = false;
+    for (int s = 0; s < nseg; ++s) {
+      const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+      while (uni(lds_acquire(ready)) < s) {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
+          late = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      const unsigned char* buf = smem + (s & 1) * buf_bytes;
+      const Seg& sg = segs[s];
+      const Level& L = levels[sg.level];
+      int b0, b1;
+      wave_blocks(sg.b0, sg.b1, k, b0, b1);
+      const int T = uni(L.tiles);
+      const int rows = uni(L.rows);
+      const float* scale = uni(L.scale);
+      float* y = uni(L.y);
+      if (uni(L.kind) == kKindTernary) {
+        const int bsc_off = uni(L.bsc_off), asc_off = uni(L.asc_off);
+        // G tiles starting at tile t0 (a multiple of G, G even: the parity of
+        // tile t0 + j is that of j)
+        auto group = [&](const u32x4(&x)[GR], int t0, v4f& acc0, v4f& acc1, unsigned& sb, unsigned& sa) {
+#pragma unroll
+          for (int j = 0; j < GR; ++j) {
+            v8i a0, a1;
+            ternary_unpack(x[j], a0, a1);
+            const int t = t0 + j;
+            const bool odd = G > 0 ? (j & 1) != 0 : (t & 1) != 0;
+            if (odd) ternary_mfma<true>(a0, a1, t, buf, bsc_off, asc_off, tboff, lane, g, sb, sa, acc0, acc1);
+            else ternary_mfma<false>(a0, a1, t, buf, bsc_off, asc_off, tboff, lane, g, sb, sa, acc0, acc1);
+          }
+        };
+        for (int blk = b0; blk < b1; ++blk) {
+          v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+          unsigned sb = 0, sa = 0;
+          if (G > 0) {
+            for (int it = 0; it < T; it += 2 * GR) {
+              issue(rb);
+              __builtin_amdgcn_sched_barrier(0);
+              group(ra, it, acc0, acc1, sb, sa);
+              __builtin_amdgcn_sched_barrier(0);
+              issue(ra);
+              __builtin_amdgcn_sched_barrier(0);
+              group(rb, it + GR, acc0, acc1, sb, sa);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          } else {
+            for (int it = 0; it < T; ++it) {
+              issue(ra);
+              group(ra, it, acc0, acc1, sb, sa);
+            }
+          }
+          v4f a = acc0 + acc1;  // rows 4g + i, digit column n
+          const v4f sc = block_scales(scale, blk, rows, g);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a[i] = row16_sum(n < 12u ? a[i] : 0.f) * sc[i];
+          const int r0 = blk * 16 + static_cast<int>(4 * g);
+          if (n == 0) {
+            if (r0 + 3 < rows) {
+              *(g_f32x4*)(y + r0) = f32x4{a[0], a[1], a[2], a[3]};
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (r0 + i < rows) ((g_float*)y)[r0 + i] = a[i];
+            }
+          }
+        }
+      } else {
+        const int exp_off = uni(L.bsc_off);
+        // G tiles starting at tile t0; exponent sections of 4 tiles (T and G
+        // are multiples of 4 unless G == 0)
+        auto group = [&](const u32x4(&x)[GR], int t0, v4i& iacc, v4f& facc) {
+#pragma unroll
+          for (int j = 0; j < GR; ++j) {
+            const int t = t0 + j;
+            int8_mfma(x[j], t, buf, iboff, iacc);
+            const bool end = G > 0 ? (j % kSectionMfmas) == kSectionMfmas - 1 : (t % kSectionMfmas) == kSectionMfmas - 1;
+            if (end) int8_section(t, buf, exp_off, icexp, iacc, facc);
+          }
+        };
+        for (int blk = b0; blk < b1; ++blk) {
+          v4i iacc = {0, 0, 0, 0};
+          v4f facc = {0.f, 0.f, 0.f, 0.f};
+          if (G > 0) {
+            for (int it = 0; it < T; it += 2 * GR) {
+              issue(rb);
+              __builtin_amdgcn_sched_barrier(0);
+              group(ra, it, iacc, facc);
+              __builtin_amdgcn_sched_barrier(0);
+              issue(ra);
+              __builtin_amdgcn_sched_barrier(0);
+              group(rb, it + GR, iacc, facc);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          } else {
+            for (int it = 0; it < T; ++it) {
+              issue(ra);
+              group(ra, it, iacc, facc);
+            }
+          }
+          const v4f sc = block_scales(scale, blk, rows, g);
+          v4f lg;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lg[i] = row16_sum(facc[i]) * sc[i];
+          const int r0 = blk * 16 + static_cast<int>(4 * g);
+          if (n == 0) {
+            if (y) {
+              if (r0 + 3 < rows) {
+                *(g_f32x4*)(y + r0) = f32x4{lg[0], lg[1], lg[2], lg[3]};
+              } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if (r0 + i < rows) ((g_float*)y)[r0 + i] = lg[i];
+              }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (r0 + i < rows && lg[i] > best) {  // a lane's rows ascend: ties keep the lower index
+                best = lg[i];
+                best_idx = static_cast<unsigned>(r0 + i);
+              }
+          }
+        }
+      }
+      lds_publish(&done[wave], s);  // this wave no longer reads buffer s & 1
+    }
+    if (late && lane == 0) __hip_atomic_store(P.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // Workgroup (max, lowest index) of its vocabulary rows, then the last
+  // workgroup to arrive reduces every workgroup's key into the token.
+  unsigned long long key = best_idx == 0xFFFFFFFFu ? 0ull : argmax_key(best, best_idx);
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned long long o = __shfl_xor(key, off, kWave);
+    key = o > key ? o : key;
+  }
+  if (lane == 0) wkeys[wave] = key;
+  __syncthreads();
+  if (wave == 0) {
+    unsigned last = 0;
+    if (lane == 0) {
+      unsigned long long m = 0ull;
+      for (int i = 0; i < kWaves; ++i) m = wkeys[i] > m ? wkeys[i] : m;
+      __hip_atomic_store(&P.partials[blockIdx.x], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned prev = __hip_atomic_fetch_add(P.arrivals, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      last = prev == static_cast<unsigned>(P.grid) - 1u ? 1u : 0u;
+    }
+    if (uni(last)) {
+      unsigned long long m = 0ull;
+      for (int b = static_cast<int>(lane); b < P.grid; b += 64) {
+        const unsigned long long o = __hip_atomic_load(&P.partials[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        m = o > m ? o : m;
+      }
+      for (int off = 32; off >= 1; off >>= 1) {
+        const unsigned long long o = __shfl_xor(m, off, kWave);
+        m = o > m ? o : m;
+      }
+      if (lane == 0) {
+        *P.token_out = static_cast<int>(argmax_key_index(m));
+        __hip_atomic_store(P.arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next step
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------- conversion
+// Bit offset of weight-in-block κ's nibble: the T2 word masks deliver, in A
+// dword dd, nibble p = the weight with index κ(dd, p) of the 32-weight block
+// (dd = 0, 2: the odd weights of a nibble pair; dd = 1, 3: the even ones).
+__device__ __forceinline__ int kappa(int dd, int p) { return 16 * (dd >> 1) + 8 * (p & 1) + 2 * (p >> 1) + (1 - (dd & 1)); }
+
+// Ternary level input: thread (β, cg) of level L converts 32-element block β
+// (digit columns 3 cg .. 3 cg + 2) into the B operand entries of MFMA
+// m = 2 (β / 8) + β % 2, lane group g = (β % 8) / 2, and their scale bytes.
+__device__ void convert_ternary(const Level& L, int tid) {
+  const int beta = tid >> 2, cg = tid & 3;
+  if (beta >= L.cols / 32) return;
+  const cg_f32x4* xs = (const cg_f32x4*)(L.x + 32 * beta);
+  float x[32];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const f32x4 v = xs[q];
+    x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  const int e = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) : 0;  // amax < 2^e
+  unsigned X[32];
+  unsigned S[4] = {0u, 0u, 0u, 0u};  // sign bits (bit 3 of each nibble) in A nibble order
+#pragma unroll
+  for (int i = 0; i < 32; ++i) X[i] = static_cast<unsigned>(rintf(ldexpf(fabsf(x[i]), 23 - e)));  // <= 2^23
+#pragma unroll
+  for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+    for (int p = 0; p < 8; ++p) S[dd] |= (x[kappa(dd, p)] < 0.f ? 8u : 0u) << (4 * p);
+  const int t = e - 24;                     // exponent of digit column 0 (includes A's factor 2)
+  const int ashift = t + 127 < 0 ? t + 127 : 0;
+  const int m = 2 * (beta >> 3) + (beta & 1), g = (beta & 7) >> 1;
+  unsigned char* b = L.b_out;
+  for (int n = 3 * cg; n < 3 * cg + 3; ++n) {
+    unsigned w[4];
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd) {
+      unsigned dg = 0;
+#pragma unroll
+      for (int p = 0; p < 8; ++p) dg |= ((X[kappa(dd, p)] >> (2 * n)) & 3u) << (4 * p);
+      // digit d -> FP4 code 2d - [d == 3] (0, 1.0, 2.0, 3.0), then the sign bit
+      w[dd] = ((dg << 1) - ((dg >> 1) & dg & 0x11111111u)) | S[dd];
+    }
+    *reinterpret_cast<u32x4*>(b + m * kTernaryMfmaBytes + (12 * g + n) * 16) = u32x4{w[0], w[1], w[2], w[3]};
+    b[L.bsc_off + (m >> 2) * 256 + 4 * (16 * g + n) + (m & 3)] = static_cast<unsigned char>(127 + t + 2 * n - ashift);
+  }
+  if (cg == 3)
+    for (int n = 12; n < 16; ++n) b[L.bsc_off + (m >> 2) * 256 + 4 * (16 * g + n) + (m & 3)] = 0;  // 2^-127
+  if (cg == 0) b[L.asc_off + (m >> 2) * 16 + 4 * g + (m & 3)] = static_cast<unsigned char>(127 + ashift);
+}
+
+// Vocabulary input h: wave `sec` converts section sec (256 elements); lane
+// t owns elements 4t .. 4t + 3 of it.
+__device__ void convert_int8(const Level& L, const float* h, int sec, unsigned lane) {
+  const f32x4 v = ((const cg_f32x4*)(h + 256 * sec))[lane];
+  float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+  const int e = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) : 0;
+  const float xv[4] = {v.x, v.y, v.z, v.w};
+  unsigned dw[3] = {0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int X = static_cast<int>(rintf(ldexpf(xv[i], 22 - e)));  // |X| <= 2^22
+    const int d0 = ((X + 128) & 255) - 128;
+    const int X1 = (X - d0) >> 8;
+    const int d1 = ((X1 + 128) & 255) - 128;
+    const int d2 = (X1 - d1) >> 8;
+    dw[0] |= (static_cast<unsigned>(d0) & 255u) << (8 * i);
+    dw[1] |= (static_cast<unsigned>(d1) & 255u) << (8 * i);
+    dw[2] |= (static_cast<unsigned>(d2) & 255u) << (8 * i);
+  }
+  const int m = 4 * sec + static_cast<int>(lane >> 4), g = static_cast<int>((lane & 15u) >> 2), j0 = 4 * static_cast<int>(lane & 3u);
+  unsigned char* b = L.b_out;
+#pragma unroll
+  for (int d = 0; d < 3; ++d) *reinterpret_cast<unsigned*>(b + m * kInt8MfmaBytes + (3 * g + d) * 16 + j0) = dw[d];
+  if (lane == 0) *reinterpret_cast<int*>(b + L.bsc_off + 4 * sec) = e - 22;
+}
+
+// Grid (x, level): level < n_levels converts ternary input blocks, level ==
+// n_levels converts h.  Workgroups beyond a level's work return at once.
+__global__ __launch_bounds__(256) void stream_convert_kernel(const Plan* __restrict__ plan,
+                                                             const Level* __restrict__ levels) {
+  const Plan& P = *plan;
+  const int li = blockIdx.y;
+  const Level& L = levels[li];
+  if (li < P.n_levels) {
+    convert_ternary(L, blockIdx.x * 256 + threadIdx.x);
+  } else {
+    const int sec = blockIdx.x * 4 + static_cast<int>(threadIdx.x >> 6);
+    if (sec < P.hidden / 256) convert_int8(L, P.h, sec, threadIdx.x & 63u);
+  }
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------- host side
+namespace {
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+constexpr int kMaxGrid = 1024;
+
+struct SLayout {
+  size_t plan, partials, arrivals, levels, segs, seg_count, park, regions, total;
+};
+
+size_t region_bytes(const pwg_step_desc* d, int i) {
+  return i < d->n_levels ? ternary_region_bytes(d->levels[i].cols) : int8_region_bytes(d->hidden);
+}
+
+SLayout layout_for(const pwg_step_desc* d) {
+  SLayout L{};
+  L.plan = 0;
+  L.partials = align_up(sizeof(Plan), 256);
+  L.arrivals = L.partials + kMaxGrid * 8;
+  L.levels = align_up(L.arrivals + 256, 256);
+  L.segs = align_up(L.levels + static_cast<size_t>(d->n_levels + 1) * sizeof(Level), 256);
+  L.seg_count = align_up(L.segs + static_cast<size_t>(kMaxGrid) * (d->n_levels + 1) * sizeof(Seg), 256);
+  L.park = align_up(L.seg_count + kMaxGrid * 4, 256);
+  L.regions = L.park + kParkBytes;
+  size_t end = L.regions;
+  for (int i = 0; i <= d->n_levels; ++i) end += align_up(region_bytes(d, i), 256);
+  L.total = end;
+  return L;
+}
+
+Plan* plan_ptr(const pwg_step_desc* d, size_t ws_offset) {
+  const uintptr_t p = reinterpret_cast<uintptr_t>(d->workspace) + ws_offset;
+  return reinterpret_cast<Plan*>(align_up(p, 256));
+}
+
+int grid_size(int* grid) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return fail(PWG_ERR_HIP, "stream step: device query failed: %s", hipGetErrorString(e));
+  *grid = cus < kMaxGrid ? cus : kMaxGrid;
+  return PWG_OK;
+}
+
+// Relative cost of one tile (16 rows x 64 bytes) of each kind.
+constexpr double kTernaryTileCost = 1.0;
+constexpr double kInt8TileCost = 1.0;
+
+// Splits the concatenation of every level's 16-row blocks (then the
+// vocabulary's) into `grid` contiguous ranges of equal cost; each
+// workgroup's ranges are its segments, one per level it touches.
+void partition(const pwg_step_desc* d, int grid, std::vector<std::vector<Seg>>& out) {
+  const int n = d->n_levels;
+  std::vector<long long> blocks(n + 1);
+  std::vector<double> cost(n + 1), start(n + 2);
+  for (int i = 0; i < n; ++i) {
+    blocks[i] = (d->levels[i].rows + 15) / 16;
+    cost[i] = static_cast<double>(d->levels[i].cols / 256) * kTernaryTileCost;
+  }
+  blocks[n] = (d->vocab + 15) / 16;
+  cost[n] = static_cast<double>(d->hidden / 64) * kInt8TileCost;
+  start[0] = 0.0;
+  for (int i = 0; i <= n; ++i) start[i + 1] = start[i] + static_cast<double>(blocks[i]) * cost[i];
+  const double total = start[n + 1];
+  auto pos = [&](double x, int& lv, long long& b) {
+    lv = 0;
+    while (lv < n && x >= start[lv + 1]) ++lv;
+    b = static_cast<long long>(std::llround((x - start[lv]) / cost[lv]));
+    b = b < 0 ? 0 : (b > blocks[lv] ? blocks[lv] : b);
+  };
+  out.assign(grid, {});
+  int lv0 = 0;
+  long long b0 = 0;
+  for (int w = 0; w < grid; ++w) {
+    int lv1;
+    long long b1;
+    if (w + 1 == grid) {
+      lv1 = n;
+      b1 = blocks[n];
+    } else {
+      pos(total * (w + 1) / grid, lv1, b1);
+    }
+    for (int lv = lv0; lv <= lv1; ++lv) {
+      const long long a = lv == lv0 ? b0 : 0;
+      const long long e = lv == lv1 ? b1 : blocks[lv];
+      if (e > a) out[w].push_back(Seg{lv, static_cast<int>(a), static_cast<int>(e), 0});
+    }
+    lv0 = lv1;
+    b0 = b1;
+  }
+}
+
+// Prefetch group: G tiles per register group (two groups per compute wave),
+// 2G dividing every level's tiles per block, so that the register of a tile
+// is known at compile time; 0 (no prefetch) for other shapes.
+int prefetch_depth(const pwg_step_desc* d) {
+  long long gcd = d->hidden / 64;
+  for (int i = 0; i < d->n_levels; ++i) {
+    long long a = gcd, b = d->levels[i].cols / 256;
+    while (b) {
+      const long long t = a % b;
+      a = b;
+      b = t;
+    }
+    gcd = a;
+  }
+  return gcd % 16 == 0 ? 8 : 0;
+}
+
+}  // namespace
+
+int step_stream_check(const pwg_step_desc* d) {
+  for (int i = 0; i < d->n_levels; ++i) {
+    const pwg_level& L = d->levels[i];
+    if (L.cols % 256 != 0 || L.cols > kMaxStreamCols)
+      return fail(PWG_ERR_UNSUPPORTED, "stream schedule: level %d needs cols %% 256 == 0 and cols <= %d (has %lld)", i,
+                  kMaxStreamCols, static_cast<long long>(L.cols));
+    if (L.rows >= (int64_t{1} << 30)) return fail(PWG_ERR_ARG, "stream schedule: level %d has too many rows", i);
+  }
+  if (d->hidden % 256 != 0 || d->hidden > kMaxStreamCols)
+    return fail(PWG_ERR_UNSUPPORTED, "stream schedule: hidden must be a multiple of 256 and at most %d", kMaxStreamCols);
+  if (d->vocab >= (int64_t{1} << 30)) return fail(PWG_ERR_ARG, "stream schedule: vocabulary too large");
+  size_t need = 0;
+  for (int i = 0; i <= d->n_levels; ++i) need = std::max(need, region_bytes(d, i));
+  if (2 * align_up(need, 16) + kFlagBytes > kMaxLds)
+    return fail(PWG_ERR_UNSUPPORTED, "stream schedule: activation operands need %zu bytes of LDS", 2 * need);
+  return PWG_OK;
+}
+
+size_t step_stream_workspace(const pwg_step_desc* d) { return layout_for(d).total + 256; }
+
+int step_stream_plan(const pwg_step_desc* d, size_t ws_offset, void* stream) {
+  TRY(step_stream_check(d));
+  int grid = 0;
+  TRY(grid_size(&grid));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const SLayout lay = layout_for(d);
+  Plan* dplan = plan_ptr(d, ws_offset);
+  char* dbase = reinterpret_cast<char*>(dplan);
+  size_t need = 0;
+  for (int i = 0; i <= d->n_levels; ++i) need = std::max(need, region_bytes(d, i));
+
+  Plan h{};
+  h.n_levels = d->n_levels;
+  h.grid = grid;
+  h.buf_bytes = static_cast<int>(align_up(need, 16));
+  h.vocab = static_cast<int>(d->vocab);
+  h.hidden = static_cast<int>(d->hidden);
+  h.depth = prefetch_depth(d);
+  h.h = d->h;
+  h.emb_table = reinterpret_cast<const u32x4*>(d->emb_table);
+  h.emb_scale = d->emb_scale;
+  h.token_in = d->token_in;
+  h.token_out = d->token_out;
+  h.emb_row_out = reinterpret_cast<u32x4*>(d->emb_row_out);
+  h.emb_scale_out = d->emb_scale_out;
+  h.emb_deq_out = reinterpret_cast<float4*>(d->emb_deq_out);
+  h.park = reinterpret_cast<const unsigned char*>(dbase + lay.park);
+  h.partials = reinterpret_cast<unsigned long long*>(dbase + lay.partials);
+  h.arrivals = reinterpret_cast<unsigned*>(dbase + lay.arrivals);
+  h.status = reinterpret_cast<unsigned*>(dbase + lay.arrivals + 64);
+  h.seg_count = reinterpret_cast<const int*>(dbase + lay.seg_count);
+
+  std::vector<Level> lv(d->n_levels + 1);
+  size_t off = lay.regions;
+  for (int i = 0; i <= d->n_levels; ++i) {
+    Level& L = lv[i];
+    L.b = reinterpret_cast<const unsigned char*>(dbase + off);
+    L.b_out = reinterpret_cast<unsigned char*>(dbase + off);
+    L.b_bytes = static_cast<int>(region_bytes(d, i));
+    if (i < d->n_levels) {
+      const pwg_level& S = d->levels[i];
+      L.w = static_cast<const unsigned char*>(S.w_packed);
+      L.scale = S.row_scale;
+      L.x = S.x;
+      L.y = S.y;
+      L.rows = static_cast<int>(S.rows);
+      L.cols = static_cast<int>(S.cols);
+      L.tiles = static_cast<int>(S.cols / 256);
+      L.kind = kKindTernary;
+      L.bsc_off = static_cast<int>(ternary_bsc_off(S.cols));
+      L.asc_off = static_cast<int>(ternary_asc_off(S.cols));
+    } else {
+      L.w = reinterpret_cast<const unsigned char*>(d->out_table);
+      L.scale = d->out_scale;
+      L.x = d->h;
+      L.y = d->logits_out;
+      L.rows = static_cast<int>(d->vocab);
+      L.cols = static_cast<int>(d->hidden);
+      L.tiles = static_cast<int>(d->hidden / 64);
+      L.kind = kKindInt8;
+      L.bsc_off = static_cast<int>(int8_exp_off(d->hidden));
+      L.asc_off = 0;
+    }
+    off += align_up(region_bytes(d, i), 256);
+  }
+
+  std::vector<std::vector<Seg>> parts;
+  partition(d, grid, parts);
+  int stride = 1;
+  for (const auto& v : parts) stride = std::max(stride, static_cast<int>(v.size()));
+  std::vector<Seg> seg_flat(static_cast<size_t>(grid) * stride, Seg{0, 0, 0, 0});
+  std::vector<int> seg_count(grid);
+  for (int b = 0; b < grid; ++b) {
+    seg_count[b] = static_cast<int>(parts[b].size());
+    for (size_t j = 0; j < parts[b].size(); ++j) seg_flat[static_cast<size_t>(b) * stride + j] = parts[b][j];
+  }
+  h.seg_stride = stride;
+
+  hipError_t e = hipMemsetAsync(dbase, 0, lay.regions, st);  // partials, arrival counter, status, park
+  if (e == hipSuccess) e = hipMemcpyAsync(dplan, &h, sizeof(Plan), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(dbase + lay.levels, lv.data(), lv.size() * sizeof(Level), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(dbase + lay.segs, seg_flat.data(), seg_flat.size() * sizeof(Seg), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(dbase + lay.seg_count, seg_count.data(), seg_count.size() * 4, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(PWG_ERR_HIP, "pwg_step_plan: %s", hipGetErrorString(e));
+  return PWG_OK;
+}
+
+int step_stream_launch(const pwg_step_desc* d, size_t ws_offset, void* stream) {
+  TRY(step_stream_check(d));
+  int grid = 0;
+  TRY(grid_size(&grid));
+  Plan* dplan = plan_ptr(d, ws_offset);
+  char* dbase = reinterpret_cast<char*>(dplan);
+  const SLayout lay = layout_for(d);
+  const Level* lv = reinterpret_cast<const Level*>(dbase + lay.levels);
+  const Seg* segs = reinterpret_cast<const Seg*>(dbase + lay.segs);
+  size_t need = 0;
+  int conv_x = (d->hidden / 256 + 3) / 4;
+  for (int i = 0; i <= d->n_levels; ++i) {
+    need = std::max(need, region_bytes(d, i));
+    if (i < d->n_levels) conv_x = std::max(conv_x, static_cast<int>((d->levels[i].cols / 8 + 255) / 256));
+  }
+  const size_t lds = 2 * align_up(need, 16) + kFlagBytes;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(stream_convert_kernel, dim3(conv_x, d->n_levels + 1), dim3(256), 0, st, dplan, lv);
+  if (prefetch_depth(d) == 8)
+    hipLaunchKernelGGL(stream_step_kernel<8>, dim3(grid), dim3(kThreads), lds, st, dplan, lv, segs);
+  else
+    hipLaunchKernelGGL(stream_step_kernel<0>, dim3(grid), dim3(kThreads), lds, st, dplan, lv, segs);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PWG_ERR_HIP, "stream step launch: %s", hipGetErrorString(e));
+  return PWG_OK;
+}
+
+int step_stream_status(const pwg_step_desc* d, size_t ws_offset, void* stream) {
+  Plan* dplan = plan_ptr(d, ws_offset);
+  const SLayout lay = layout_for(d);
+  unsigned s = 0;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(&s, reinterpret_cast<char*>(dplan) + lay.arrivals + 64, 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(PWG_ERR_HIP, "pwg_step_status: %s", hipGetErrorString(e));
+  if (s == kStatusTimeout) return fail(PWG_ERR_HIP, "stream step: a workgroup's operand wait timed out");
+  return PWG_OK;
+}
+
+}  // namespace pwg

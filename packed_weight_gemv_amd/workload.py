@@ -15,7 +15,8 @@ import torch
 
 import synth
 
-from . import SCHEDULE_LEVELS, StepDesc, pack_weights, step_workspace_bytes
+from . import (LAYOUT_ROWS, LAYOUT_TILED, SCHEDULE_LEVELS, StepDesc, layout_for_schedule, pack_weights,
+               step_workspace_bytes, tile_rows)
 
 LEVEL_NAMES = [name for name, _, _ in synth.LEVELS]
 
@@ -41,6 +42,24 @@ class StepWorkload:
     token0: int = 0
     packed_bytes: int = 0
     scale_bytes: int = 0
+    # device weights per arrangement: {layout: ([w per level], out_table)}
+    weights: dict = field(default_factory=dict)
+
+    def set_schedule(self, schedule: int):
+        """Points the description at the weight arrangement `schedule` takes
+        (both arrangements must have been built) and resizes the workspace."""
+        layout = layout_for_schedule(schedule)
+        ws, out = self.weights[layout]
+        d = self.desc
+        d.levels = [(w,) + tuple(lv[1:]) for w, lv in zip(ws, d.levels)]
+        d.out_table = out
+        d.schedule = schedule
+        d.weight_layout = layout
+        d._c = None
+        need = step_workspace_bytes(d)
+        if d.workspace.numel() < need:
+            d.workspace = torch.zeros(need, dtype=torch.uint8, device=d.workspace.device)
+            d._c = None
 
     def algorithmic_bytes(self) -> dict:
         vocab, hidden = self.out_table.q.shape
@@ -64,9 +83,23 @@ def _level_arrays(workload: int, layer: int, shapes: dict):
 def build_step(n_layers: int = synth.N_LAYERS, shapes: dict | None = None, vocab: int = synth.VOCAB,
                hidden: int = synth.HIDDEN, workload: int = synth.W_STEP, schedule: int = SCHEDULE_LEVELS,
                with_logits: bool = False, sample_rows: int = 64, device: str = "cuda:0",
-               token0: int | None = None, threads: int | None = None) -> StepWorkload:
+               token0: int | None = None, threads: int | None = None, both_layouts: bool = False) -> StepWorkload:
+    """Seeded decode-step workload on the device.  The weights are uploaded in
+    the arrangement `schedule` takes (tiles for the stream schedule, arranged
+    on the device by the library), or in both when `both_layouts`."""
     shapes = shapes or synth.LAYER_SHAPES
     dev = torch.device(device)
+    layout = layout_for_schedule(schedule)
+    layouts = (LAYOUT_ROWS, LAYOUT_TILED) if both_layouts else (layout,)
+    w_by_layout = {lay: [] for lay in layouts}
+
+    def arrange(rows_t, rows, row_bytes):
+        out = {}
+        if LAYOUT_TILED in layouts:
+            out[LAYOUT_TILED] = tile_rows(rows_t, rows, row_bytes)
+        if LAYOUT_ROWS in layouts:
+            out[LAYOUT_ROWS] = rows_t
+        return out
 
     def one_layer(layer):
         levels = _level_arrays(workload, layer, shapes)
@@ -89,7 +122,9 @@ def build_step(n_layers: int = synth.N_LAYERS, shapes: dict | None = None, vocab
         for layer_off, packed in enumerate(batch):
             layer = start + layer_off
             for name, blob, s, x, (r, k), smp in packed:
-                wd = torch.from_numpy(blob).to(dev)
+                for lay, t in arrange(torch.from_numpy(blob).to(dev), r, k // 4).items():
+                    w_by_layout[lay].append(t)
+                wd = w_by_layout[layout][-1]
                 sd = torch.from_numpy(s).to(dev)
                 xd = torch.from_numpy(x).to(dev)
                 yd = torch.empty(r, dtype=torch.float32, device=dev)
@@ -104,9 +139,11 @@ def build_step(n_layers: int = synth.N_LAYERS, shapes: dict | None = None, vocab
     if token0 is None:
         token0 = int(ids[0])
     token = torch.tensor([token0], dtype=torch.int32, device=dev)
+    out_by_layout = arrange(torch.from_numpy(out_t.q).to(dev), vocab, hidden)
+    torch.cuda.synchronize(dev)
     desc = StepDesc(
         levels=levels,
-        out_table=torch.from_numpy(out_t.q).to(dev), out_scale=torch.from_numpy(out_t.scale).to(dev),
+        out_table=out_by_layout[layout], out_scale=torch.from_numpy(out_t.scale).to(dev),
         h=torch.from_numpy(h).to(dev),
         emb_table=torch.from_numpy(emb_t.q).to(dev), emb_scale=torch.from_numpy(emb_t.scale).to(dev),
         token_in=token, token_out=token,
@@ -114,10 +151,11 @@ def build_step(n_layers: int = synth.N_LAYERS, shapes: dict | None = None, vocab
         emb_scale_out=torch.empty(4, dtype=torch.float32, device=dev),
         emb_deq_out=torch.empty(hidden, dtype=torch.float32, device=dev),
         logits_out=torch.empty(vocab, dtype=torch.float32, device=dev) if with_logits else None,
-        schedule=schedule)
+        schedule=schedule, weight_layout=layout, vocab=vocab, hidden=hidden)
     desc.workspace = torch.zeros(1, dtype=torch.uint8, device=dev)   # sized below
     need = step_workspace_bytes(desc)
     desc.workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
     desc._c = None
     return StepWorkload(desc=desc, level_shapes=shapes_out, samples=samples, out_table=out_t, emb_table=emb_t,
-                        h=h, token0=token0, packed_bytes=packed_bytes, scale_bytes=scale_bytes)
+                        h=h, token0=token0, packed_bytes=packed_bytes, scale_bytes=scale_bytes,
+                        weights={lay: (w_by_layout[lay], out_by_layout[lay]) for lay in layouts})

@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_error_string():
-    assert pwg.version() == 1
+    assert pwg.version() == 2
     assert isinstance(pwg.last_error(), str)
 
 
@@ -157,3 +157,53 @@ def test_step_argument_errors():
     lv = (pwg.Level * 1)(pwg.Level(A, A, A, A, 8, 100))
     d.n_levels, d.levels = 1, C.cast(lv, C.POINTER(pwg.Level))
     assert pwg._step(C.byref(d), None) == ERR_ARG and "level 0" in pwg.last_error()
+
+
+def test_step_layout_errors():
+    """Each schedule takes one weight arrangement; the stream schedule also
+    needs widths that are multiples of 256 and at most 12288."""
+    d = pwg._StepDesc()
+    d.vocab, d.hidden = 1000, 4096
+    for name in ("out_table", "out_scale", "h", "emb_table", "emb_scale", "token_in", "token_out",
+                 "emb_row_out", "emb_scale_out", "workspace"):
+        setattr(d, name, A)
+    lv = (pwg.Level * 1)(pwg.Level(A, A, A, A, 64, 4096))
+    d.n_levels, d.levels = 1, C.cast(lv, C.POINTER(pwg.Level))
+    d.weight_layout = 5
+    assert pwg._step(C.byref(d), None) == ERR_ARG and "layout" in pwg.last_error()
+    d.schedule, d.weight_layout = pwg.SCHEDULE_STREAM, pwg.LAYOUT_ROWS
+    assert pwg._step(C.byref(d), None) == ERR_UNSUPPORTED
+    d.schedule, d.weight_layout = pwg.SCHEDULE_PERSISTENT, pwg.LAYOUT_TILED
+    assert pwg._step(C.byref(d), None) == ERR_UNSUPPORTED
+    d.schedule, d.weight_layout = pwg.SCHEDULE_STREAM, pwg.LAYOUT_TILED
+    d.workspace_bytes = pwg._step_ws(C.byref(d))
+    assert d.workspace_bytes > 0
+    lv[0] = pwg.Level(A, A, A, A, 64, 4160)            # not a multiple of 256
+    assert pwg._step(C.byref(d), None) == ERR_UNSUPPORTED and "256" in pwg.last_error()
+    lv[0] = pwg.Level(A, A, A, A, 64, 16384)           # wider than the LDS operand buffers
+    assert pwg._step(C.byref(d), None) == ERR_UNSUPPORTED
+    lv[0] = pwg.Level(A, A, A, A, 64, 4096)
+    d.hidden = 4160
+    assert pwg._step(C.byref(d), None) == ERR_UNSUPPORTED
+
+
+def test_tiled_size():
+    assert pwg.tiled_size(16, 64) == 1024
+    assert pwg.tiled_size(17, 64) == 2048            # rows padded to 16
+    assert pwg.tiled_size(4096, 1024) == 4096 * 1024
+    assert pwg.tiled_size(151936, 4096) == 151936 * 4096
+    for bad in ((0, 64), (16, 0), (16, 32), (16, 100), (-1, 64)):
+        assert pwg.tiled_size(*bad) == 0
+    assert pwg.tiled_size(33, 3072) == 48 * 3072
+
+
+def test_tile_rows_argument_errors():
+    f = pwg._tile_rows
+    need = pwg.tiled_size(17, 128)
+    assert f(None, 17, 128, A, need, None) == ERR_ARG
+    assert f(A, 17, 128, None, need, None) == ERR_ARG
+    assert f(A, 0, 128, A + (1 << 16), need, None) == ERR_ARG
+    assert f(A, 17, 96, A + (1 << 16), need, None) == ERR_ARG
+    assert f(MIS, 17, 128, A + (1 << 16), need, None) == ERR_ALIGN
+    assert f(A, 17, 128, A + (1 << 16), need - 16, None) == ERR_SIZE
+    assert f(A, 17, 128, A + 1024, need, None) == ERR_ARG and "overlap" in pwg.last_error()

@@ -245,3 +245,35 @@ def test_gather_invalid_ids_give_zero_rows_and_nan_scale():
     assert np.array_equal(r[0], tab.q[3]) and np.array_equal(r[3], tab.q[499])
     assert not r[1].any() and not r[2].any() and not d[1].any()
     assert np.isnan(s[1]) and np.isnan(s[2]) and s[0] == tab.scale[3]
+
+
+# ------------------------------------------------------------------ tiled arrangement
+from oracle import packed_format as pf  # noqa: E402
+
+TILE_SHAPES = [(1, 64), (17, 128), (16, 1024), (37, 1024), (1000, 3072), (4096, 1024), (24576, 1024), (1003, 4096)]
+
+
+@pytest.mark.parametrize("shape", TILE_SHAPES, ids=[f"{r}x{b}" for r, b in TILE_SHAPES])
+def test_tile_rows_matches_oracle_bit_for_bit(shape):
+    rows, row_bytes = shape
+    m = np.random.default_rng(rows * 31 + row_bytes).integers(0, 256, size=shape, dtype=np.uint8)
+    out = pwg.tile_rows(dev(m), rows, row_bytes)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()[: pwg.tiled_size(rows, row_bytes)]
+    assert np.array_equal(got, pf.tile16x64(m))
+
+
+def test_tile_rows_full_vocabulary_table_sampled():
+    """The 151,936 x 4,096 int8 output table: sampled tiles against the oracle
+    arrangement of the rows they cover."""
+    rows, cols = 151936, 4096
+    tab = synth.int8_table((106, 0), rows, cols)
+    out = pwg.tile_rows(dev(tab.q.view(np.uint8)), rows, cols)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    tiles_per_block = cols // 64
+    for rb in np.unique(np.concatenate([[0, rows // 16 - 1], rng.integers(0, rows // 16, 24)])):
+        block = tab.q.view(np.uint8)[16 * rb: 16 * rb + 16]
+        want = pf.tile16x64(block)
+        got = out[rb * 16 * cols: (rb + 1) * 16 * cols].cpu().numpy()
+        assert got.size == tiles_per_block * 1024 and np.array_equal(got, want), f"row block {rb}"

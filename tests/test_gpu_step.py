@@ -5,7 +5,7 @@ import pytest
 
 import synth
 from oracle import reference as ref
-from tests.parity import assert_gemv, token_ok
+from tests.parity import assert_gemv, gemv_report, token_ok
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -199,3 +199,78 @@ def test_chained_levels_see_previous_outputs(schedule, size):
         er, _, _ = ref.embed_gather(wl.emb_table.q, wl.emb_table.scale, [token_in])
         assert np.array_equal(out["emb_row"], er[0])
         token_in = out["token"]
+
+
+# ------------------------------------------------------------------ stream schedule edge cases
+RAGGED = {"q": (4000, 4096), "k": (37, 4096), "v": (1, 4096), "o": (4096, 4096),
+          "gate": (100, 4096), "up": (3000, 4096), "down": (1029, 12288)}
+
+
+def test_stream_ragged_rows_prefetch_path():
+    """Row counts that are not multiples of 16 (a one-row level included), a
+    ragged vocabulary, on widths that take the prefetching kernel (tiles per
+    block a multiple of 16)."""
+    wl = build_step(n_layers=2, shapes=RAGGED, vocab=1000, hidden=4096, with_logits=True,
+                    schedule=pwg.SCHEDULE_STREAM)
+    pwg.step_plan(wl.desc)
+    pwg.decode_step_weights(wl.desc)
+    torch.cuda.synchronize()
+    pwg.step_status(wl.desc)
+    out = outputs(wl)
+    for layer in range(2):
+        mats = synth.layer(synth.W_STEP, layer, RAGGED)
+        xs = synth.layer_inputs(synth.W_STEP, layer, hidden=4096, inter=12288)
+        for i, (name, members, _) in enumerate(synth.LEVELS):
+            m = synth.stacked(mats, members)
+            assert_gemv(out["levels"][4 * layer + i], ref.ternary_gemv(m.w, m.scale, xs[name]),
+                        ref.ternary_gemv_magnitude(m.w, m.scale, xs[name]), f"ragged {layer} {name}")
+    check_against_oracle(wl, out, wl.token0, full_levels=False)
+
+
+@pytest.mark.parametrize("kind", ["outlier", "tiny", "huge", "mixed", "zero"])
+def test_stream_activation_ranges(kind):
+    """The matrix-core operands carry one exponent per 32 inputs (ternary) or
+    per 256 (h): outliers, tiny and huge magnitudes, a different magnitude in
+    every block, and all-zero inputs."""
+    wl = build_step(n_layers=1, shapes=SMALL, vocab=1000, hidden=256, with_logits=True,
+                    schedule=pwg.SCHEDULE_STREAM)
+    d = wl.desc
+    xs = {}
+    for i, lv in enumerate(d.levels):
+        x = synth.normal_f32(synth.rng_for(140 + i, 0), lv[5]).astype(np.float64)
+        if kind == "outlier":
+            x[7] = 3000.0
+        elif kind == "tiny":
+            x *= 1e-30
+        elif kind == "huge":
+            x *= 1e30
+        elif kind == "mixed":
+            x *= 10.0 ** np.repeat(np.arange(-8, 8), -(-len(x) // 16))[: len(x)]
+        else:
+            x[:] = 0.0
+        xs[i] = x.astype(np.float32)
+        lv[2].copy_(torch.from_numpy(xs[i]))
+    pwg.step_plan(d)
+    pwg.decode_step_weights(d)
+    torch.cuda.synchronize()
+    pwg.step_status(d)
+    out = outputs(wl)
+    mats = synth.layer(synth.W_STEP, 0, SMALL)
+    for i, (name, members, _) in enumerate(synth.LEVELS):
+        m = synth.stacked(mats, members)
+        y, yr = out["levels"][i], ref.ternary_gemv(m.w, m.scale, xs[i])
+        mag = ref.ternary_gemv_magnitude(m.w, m.scale, xs[i])
+        if kind == "zero":
+            assert not y.any()
+        elif kind == "outlier":
+            # The outlier's 32-element block is rounded relative to 3000, so
+            # that block's terms carry up to 2^-24 * 2^e (2^e <= 2 * block max)
+            # each: the kernel's own error model, plus the float32 floor.
+            rep = gemv_report(y, yr, mag)
+            assert rep["rel_l2"] <= 1e-5, rep
+            rows, cols = m.w.shape
+            bmax = np.abs(xs[i].astype(np.float64)).reshape(-1, 32).max(axis=1)
+            bound = np.abs(m.scale.astype(np.float64)) * (np.abs(m.w).reshape(rows, -1, 32).sum(axis=2) @ bmax) * 2.0 ** -23
+            assert (np.abs(y - yr) <= bound + 1e-6 * mag).all(), name
+        else:
+            assert_gemv(y, yr, mag, f"{kind} {name}")

@@ -189,6 +189,60 @@ def test_t2_round_trip_and_invalid_code():
         pf.packed_nbytes(1, 100)
 
 
+# ---------------------------------------------------------------- tile arrangement
+def _fixture_matrix(rows, row_bytes):
+    r, c = np.meshgrid(np.arange(rows), np.arange(row_bytes), indexing="ij")
+    return ((r * 128 + c) % 251).astype(np.uint8)
+
+
+def test_tile_hand_derived_offsets(golden_dir):
+    import json
+    fx = json.load(open(os.path.join(golden_dir, "tile16x64.json")))
+    rows, rb = fx["matrix"]["rows"], fx["matrix"]["row_bytes"]
+    m = _fixture_matrix(rows, rb)
+    t = pf.tile16x64(m)
+    assert t.size == fx["tiled_bytes"] == pf.tiled_nbytes(rows, rb)
+    for case in fx["cases"]:
+        assert t[case["offset"]] == m[case["row"], case["col"]], case["derivation"]
+    for case in fx["zero_offsets"]:
+        assert t[case["offset"]] == 0, case["derivation"]
+
+
+def test_tile_is_a_permutation_plus_zero_padding_and_inverts():
+    for rows, rb in ((1, 64), (16, 64), (17, 128), (40, 192), (33, 3072)):
+        m = RNG.integers(0, 256, size=(rows, rb), dtype=np.uint8)
+        t = pf.tile16x64(m)
+        pad = t.size - m.size
+        assert pad == (-(-rows // 16) * 16 - rows) * rb
+        assert np.array_equal(np.sort(t), np.sort(np.concatenate([m.reshape(-1), np.zeros(pad, np.uint8)])))
+        assert np.array_equal(pf.untile16x64(t, rows, rb), m)
+
+
+def test_tile_one_kib_tile_holds_one_16_row_block_of_one_window():
+    """Brute force on a matrix whose bytes name their own (row, column):
+    every 1 KiB tile holds exactly the 16 x 64 bytes of one (row block,
+    column window), and every 16-byte unit holds 16 consecutive bytes of one
+    row."""
+    rows, rb = 48, 256
+    ids = np.arange(rows * rb, dtype=np.int64).reshape(rows, rb)
+    lo, hi = (ids % 256).astype(np.uint8), (ids // 256).astype(np.uint8)
+    tl, th = pf.tile16x64(lo), pf.tile16x64(hi)
+    flat_id = th.astype(np.int64) * 256 + tl
+    row, col = flat_id // rb, flat_id % rb
+    for tile in range(flat_id.size // 1024):
+        r, c = row[1024 * tile:1024 * (tile + 1)], col[1024 * tile:1024 * (tile + 1)]
+        assert len(set((r // 16).tolist())) == 1 and len(set((c // 64).tolist())) == 1
+        assert len(set(zip(r.tolist(), c.tolist()))) == 1024
+    units_r, units_c = row.reshape(-1, 16), col.reshape(-1, 16)
+    assert (units_r == units_r[:, :1]).all() and (np.diff(units_c, axis=1) == 1).all()
+
+
+def test_tile_rejects_bad_shapes():
+    for rows, rb in ((0, 64), (4, 32), (4, 100)):
+        with pytest.raises(ValueError):
+            pf.tiled_nbytes(rows, rb)
+
+
 # ---------------------------------------------------------------- decode step
 def test_decode_step_composes_the_parts():
     levels = []
