@@ -16,7 +16,8 @@ constexpr int kInt8MfmaBytes = 4 * 3 * 16;
 constexpr int kSectionMfmas = 4;                  // int8 MFMAs per exponent section (256 values of h)
 constexpr int kMaxStreamCols = 12288;             // two operand buffers of this width fit in LDS
 constexpr size_t kMaxLds = 160 * 1024;
-constexpr size_t kFlagBytes = 128;                // ready word, done words, per-wave argmax keys
+constexpr size_t kFlagBytes = 128;                // ready word, done words, claim counter, per-wave argmax keys
+constexpr int kMaxWgSegs = 32;                    // segments (levels touched) per workgroup
 constexpr size_t kParkBytes = 16 * 1024;          // tiles a wave re-reads after its last one
 enum { kKindTernary = 0, kKindInt8 = 1 };
 

@@ -98,58 +98,60 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
-// Blocks [b0, b1) of segment range [s0, s1) that compute wave k takes.
-__device__ __forceinline__ void wave_blocks(int s0, int s1, int k, int& b0, int& b1) {
-  const int n = s1 - s0;
-  b0 = s0 + (k * n) / kCompute;
-  b1 = s0 + ((k + 1) * n) / kCompute;
-}
-
-// The tile stream of one compute wave: the wave's blocks of every segment of
-// its workgroup, in order, as contiguous runs of 1 KiB tiles.  A run is a
-// whole number of blocks and a block a whole number of load groups, so runs
-// change only between groups.  State is wave-uniform.
-struct TileStream {
+// The producer half of a compute wave: claims 16-row blocks of its
+// workgroup's work, in order, from one counter in LDS (one atomic add per
+// block, so the waves of a workgroup share the blocks dynamically), and
+// issues the 1 KiB tile loads of the claimed block.  Claim f is the f-th
+// block of the concatenated segments; seg_first holds the prefix sums of the
+// segments' block counts.  A claim happens when the loads cross into the
+// next block, so a wave holds at most one block beyond the one it computes
+// on; the claim is left in (mseg, mblk) for the consumer half.  State is
+// wave-uniform and claims are loop-free (a fixed-depth search over at most
+// kMaxWgSegs segments), which keeps the compiler from splitting the tile
+// registers' live ranges around them.
+struct Producer {
   const Seg* segs;
   const Level* levels;
-  int nseg, k;
-  int ps;                     // segment of the current run
+  int* wcnt;                  // LDS claim counter
+  const int* seg_first;       // LDS [nseg + 1] first flat block of each segment
+  int total;                  // blocks of the workgroup
   const unsigned char* ptr;   // this lane's 16 bytes of the next tile
-  const unsigned char* park;  // kParkBytes re-read once the stream is exhausted
-  int left;                   // tiles left in the current run
+  const unsigned char* park;  // kParkBytes re-read once nothing is left
+  int left;                   // tiles of the claimed block still to load
+  int mseg, mblk;             // latest claim (mseg = -1: nothing left)
 
-  // Moves to the next non-empty run from segment ps on (or parks).
-  __device__ __forceinline__ void open(unsigned lane) {
-    while (ps < nseg) {
-      const Seg& s = segs[ps];
-      int b0, b1;
-      wave_blocks(s.b0, s.b1, k, b0, b1);
-      const Level& L = levels[s.level];
-      if (b1 > b0) {
-        ptr = uni(L.w) + (static_cast<size_t>(b0) * L.tiles) * 1024u + lane * 16u;
-        left = uni((b1 - b0) * L.tiles);
-        return;
-      }
-      ps = uni(ps + 1);
+  __device__ __forceinline__ void claim(unsigned lane) {
+    int f = 0;
+    if (lane == 0) f = __hip_atomic_fetch_add(wcnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    f = uni(f);
+    if (f >= total) {
+      ptr = park + lane * 16u;
+      left = 0;
+      mseg = -1;
+      return;
     }
-    ptr = park + lane * 16u;
-    left = 0;
+    int sidx = 0;
+#pragma unroll
+    for (int step = kMaxWgSegs / 2; step >= 1; step >>= 1)
+      if (seg_first[sidx + step] <= f) sidx += step;  // seg_first[s] = total for s >= nseg
+    sidx = uni(sidx);
+    const Seg& s = segs[sidx];
+    const int b = uni(s.b0) + f - uni(seg_first[sidx]);
+    const Level& L = levels[s.level];
+    const int T = uni(L.tiles);
+    ptr = uni(L.w) + static_cast<size_t>(b) * static_cast<size_t>(T) * 1024u + lane * 16u;
+    left = T;
+    mseg = sidx;
+    mblk = b;
   }
-  // Before a group of loads: switch runs at a run's end.
-  __device__ __forceinline__ void refresh(unsigned lane) {
-    if (left == 0) {
-      if (ps < nseg) ps = uni(ps + 1);
-      open(lane);
-    }
-  }
-  __device__ __forceinline__ u32x4 load(int j) const {
-    return __builtin_nontemporal_load((const g_u32x4*)(ptr + 1024 * j));
-  }
-  // After a group of D loads (branch-free, so the loop body stays one basic
-  // block and the scheduling barriers around it hold).
-  template <int D>
-  __device__ __forceinline__ void advance() {
-    const int step = left > 0 ? D : 0;
+  // One group of GR tile loads (claiming the next block first if the
+  // current one is fully loaded), branch-free after the claim.
+  template <int GR>
+  __device__ __forceinline__ void issue(u32x4 (&x)[GR], unsigned lane) {
+    if (left == 0 && mseg >= 0) claim(lane);
+#pragma unroll
+    for (int j = 0; j < GR; ++j) x[j] = __builtin_nontemporal_load((const g_u32x4*)(ptr + 1024 * j));
+    const int step = left > 0 ? GR : 0;
     ptr += step * 1024;
     left = uni(left - step);
   }
@@ -272,9 +274,22 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
   int* ready = reinterpret_cast<int*>(smem + 2 * buf_bytes);  // highest segment whose operands are in LDS
   int* done = ready + 1;                                       // [kWaves]: highest segment a wave finished
   unsigned long long* wkeys = reinterpret_cast<unsigned long long*>(smem + 2 * buf_bytes + 64);
-  if (threadIdx.x == 0) *ready = -1;
+  int* wcnt = ready + 12;                                      // block claims
+  int* seg_first = reinterpret_cast<int*>(smem + 2 * buf_bytes + kFlagBytes);  // [kMaxWgSegs + 1]
+  if (threadIdx.x == 0) {
+    *ready = -1;
+    *wcnt = 0;
+  }
   if (threadIdx.x < kWaves) done[threadIdx.x] = -1;
+  if (threadIdx.x == 64) {  // prefix sums of the segments' block counts (padded with the total)
+    int acc = 0;
+    for (int i = 0; i <= kMaxWgSegs; ++i) {
+      seg_first[i] = acc;
+      if (i < nseg) acc += segs[i].b1 - segs[i].b0;
+    }
+  }
   __syncthreads();
+  const int total_blocks = uni(seg_first[kMaxWgSegs]);
 
   float best = -__builtin_inff();
   unsigned best_idx = 0xFFFFFFFFu;
@@ -309,55 +324,65 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
     if (nseg == 0 && blockIdx.x == 0) embed_row(P, lane);
     if (late && lane == 0) __hip_atomic_store(P.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
-    const int k = static_cast<int>(wave) - 1;
     const unsigned n = lane & 15u, g = lane >> 4;
-    TileStream ts;
-    ts.segs = segs;
-    ts.levels = levels;
-    ts.nseg = nseg;
-    ts.k = k;
-    ts.ps = 0;
-    ts.park = P.park;
-    ts.open(lane);
+    Producer pr;
+    pr.segs = segs;
+    pr.levels = levels;
+    pr.wcnt = wcnt;
+    pr.seg_first = seg_first;
+    pr.total = total_blocks;
+    pr.park = P.park;
+    pr.ptr = P.park + lane * 16u;
+    pr.left = 0;
+    pr.mseg = 0;
+    pr.mblk = 0;
     // Two groups of G tile registers: one group's loads are in flight while
     // the other group is consumed (G == 0: one tile at a time, no prefetch).
     constexpr int GR = G > 0 ? G : 1;
     u32x4 ra[GR], rb[GR];
-    auto issue = [&](u32x4(&x)[GR]) {
-      ts.refresh(lane);
-#pragma unroll
-      for (int j = 0; j < GR; ++j) x[j] = ts.load(j);
-      ts.template advance<GR>();
-    };
-    if (G > 0) issue(ra);
+    if (G > 0) pr.template issue<GR>(ra, lane);  // claims the first block
 
     const unsigned tboff = (12u * g + (n < 12u ? n : n - 12u)) * 16u;  // ternary B entry of this lane
     const unsigned iboff = (3u * g + n % 3u) * 16u;                    // int8 B entry of this lane
     const int icexp = n < 3u ? static_cast<int>(8u * n) : -1000;       // digit weight (columns >= 3 vanish)
     bool late = false;
-    for (int s = 0; s < nseg; ++s) {
-      const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
-      while (uni(lds_acquire(ready)) < s) {
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
-          late = true;
-          break;
+    int cur = -1;  // segment whose operands this wave is using
+    const unsigned char* buf = smem;
+    int T = 0, rows = 0, kind = 0, bsc_off = 0, asc_off = 0;
+    const float* scale = nullptr;
+    float* y = nullptr;
+    for (;;) {
+      if (G == 0) pr.claim(lane);
+      const int s = pr.mseg, blk = pr.mblk;
+      if (s < 0) break;
+      if (s != cur) {
+        lds_publish(&done[wave], s - 1);  // done with every segment before s
+        const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+        while (uni(lds_acquire(ready)) < s) {
+          if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
+            late = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
         }
-        __builtin_amdgcn_s_sleep(1);
+        cur = s;
+        buf = smem + (s & 1) * buf_bytes;
+        const Level& L = levels[segs[s].level];
+        T = uni(L.tiles);
+        rows = uni(L.rows);
+        scale = uni(L.scale);
+        y = uni(L.y);
+        kind = uni(L.kind);
+        bsc_off = uni(L.bsc_off);
+        asc_off = uni(L.asc_off);
       }
-      const unsigned char* buf = smem + (s & 1) * buf_bytes;
-      const Seg& sg = segs[s];
-      const Level& L = levels[sg.level];
-      int b0, b1;
-      wave_blocks(sg.b0, sg.b1, k, b0, b1);
-      const int T = uni(L.tiles);
-      const int rows = uni(L.rows);
-      const float* scale = uni(L.scale);
-      float* y = uni(L.y);
-      if (uni(L.kind) == kKindTernary) {
-        const int bsc_off = uni(L.bsc_off), asc_off = uni(L.asc_off);
-        // G tiles starting at tile t0 (a multiple of G, G even: the parity of
-        // tile t0 + j is that of j)
-        auto group = [&](const u32x4(&x)[GR], int t0, v4f& acc0, v4f& acc1, unsigned& sb, unsigned& sa) {
+      // One block: T tiles, 2 G per iteration; both kinds share the loop so
+      // that the tile registers keep one assignment.
+      v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};  // ternary: two chains; int8: acc0 = sum
+      v4i iacc = {0, 0, 0, 0};
+      unsigned sb = 0, sa = 0;
+      auto group = [&](const u32x4(&x)[GR], int t0) {
+        if (kind == kKindTernary) {
 #pragma unroll
           for (int j = 0; j < GR; ++j) {
             v8i a0, a1;
@@ -367,101 +392,60 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
             if (odd) ternary_mfma<true>(a0, a1, t, buf, bsc_off, asc_off, tboff, lane, g, sb, sa, acc0, acc1);
             else ternary_mfma<false>(a0, a1, t, buf, bsc_off, asc_off, tboff, lane, g, sb, sa, acc0, acc1);
           }
-        };
-        for (int blk = b0; blk < b1; ++blk) {
-          v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-          unsigned sb = 0, sa = 0;
-          if (G > 0) {
-            for (int it = 0; it < T; it += 2 * GR) {
-              issue(rb);
-              __builtin_amdgcn_sched_barrier(0);
-              group(ra, it, acc0, acc1, sb, sa);
-              __builtin_amdgcn_sched_barrier(0);
-              issue(ra);
-              __builtin_amdgcn_sched_barrier(0);
-              group(rb, it + GR, acc0, acc1, sb, sa);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          } else {
-            for (int it = 0; it < T; ++it) {
-              issue(ra);
-              group(ra, it, acc0, acc1, sb, sa);
-            }
-          }
-          v4f a = acc0 + acc1;  // rows 4g + i, digit column n
-          const v4f sc = block_scales(scale, blk, rows, g);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) a[i] = row16_sum(n < 12u ? a[i] : 0.f) * sc[i];
-          const int r0 = blk * 16 + static_cast<int>(4 * g);
-          if (n == 0) {
-            if (r0 + 3 < rows) {
-              *(g_f32x4*)(y + r0) = f32x4{a[0], a[1], a[2], a[3]};
-            } else {
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (r0 + i < rows) ((g_float*)y)[r0 + i] = a[i];
-            }
-          }
-        }
-      } else {
-        const int exp_off = uni(L.bsc_off);
-        // G tiles starting at tile t0; exponent sections of 4 tiles (T and G
-        // are multiples of 4 unless G == 0)
-        auto group = [&](const u32x4(&x)[GR], int t0, v4i& iacc, v4f& facc) {
+        } else {
 #pragma unroll
           for (int j = 0; j < GR; ++j) {
             const int t = t0 + j;
             int8_mfma(x[j], t, buf, iboff, iacc);
+            // exponent sections of 4 tiles (T and G are multiples of 4 unless G == 0)
             const bool end = G > 0 ? (j % kSectionMfmas) == kSectionMfmas - 1 : (t % kSectionMfmas) == kSectionMfmas - 1;
-            if (end) int8_section(t, buf, exp_off, icexp, iacc, facc);
-          }
-        };
-        for (int blk = b0; blk < b1; ++blk) {
-          v4i iacc = {0, 0, 0, 0};
-          v4f facc = {0.f, 0.f, 0.f, 0.f};
-          if (G > 0) {
-            for (int it = 0; it < T; it += 2 * GR) {
-              issue(rb);
-              __builtin_amdgcn_sched_barrier(0);
-              group(ra, it, iacc, facc);
-              __builtin_amdgcn_sched_barrier(0);
-              issue(ra);
-              __builtin_amdgcn_sched_barrier(0);
-              group(rb, it + GR, iacc, facc);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          } else {
-            for (int it = 0; it < T; ++it) {
-              issue(ra);
-              group(ra, it, iacc, facc);
-            }
-          }
-          const v4f sc = block_scales(scale, blk, rows, g);
-          v4f lg;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) lg[i] = row16_sum(facc[i]) * sc[i];
-          const int r0 = blk * 16 + static_cast<int>(4 * g);
-          if (n == 0) {
-            if (y) {
-              if (r0 + 3 < rows) {
-                *(g_f32x4*)(y + r0) = f32x4{lg[0], lg[1], lg[2], lg[3]};
-              } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  if (r0 + i < rows) ((g_float*)y)[r0 + i] = lg[i];
-              }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (r0 + i < rows && lg[i] > best) {  // a lane's rows ascend: ties keep the lower index
-                best = lg[i];
-                best_idx = static_cast<unsigned>(r0 + i);
-              }
+            if (end) int8_section(t, buf, bsc_off, icexp, iacc, acc0);
           }
         }
+      };
+      if (G > 0) {
+        for (int it = 0; it < T; it += 2 * GR) {
+          pr.template issue<GR>(rb, lane);
+          __builtin_amdgcn_sched_barrier(0);
+          group(ra, it);
+          __builtin_amdgcn_sched_barrier(0);
+          pr.template issue<GR>(ra, lane);
+          __builtin_amdgcn_sched_barrier(0);
+          group(rb, it + GR);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        for (int it = 0; it < T; ++it) {
+          pr.template issue<GR>(ra, lane);
+          group(ra, it);
+        }
       }
-      lds_publish(&done[wave], s);  // this wave no longer reads buffer s & 1
+      const v4f sc = block_scales(scale, blk, rows, g);
+      v4f a = kind == kKindTernary ? acc0 + acc1 : acc0;  // rows 4g + i, digit column n
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = row16_sum(kind != kKindTernary || n < 12u ? a[i] : 0.f) * sc[i];
+      const int r0 = blk * 16 + static_cast<int>(4 * g);
+      if (n == 0) {
+        if (y) {
+          if (r0 + 3 < rows) {
+            *(g_f32x4*)(y + r0) = f32x4{a[0], a[1], a[2], a[3]};
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (r0 + i < rows) ((g_float*)y)[r0 + i] = a[i];
+          }
+        }
+        if (kind != kKindTernary) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (r0 + i < rows && a[i] > best) {  // a lane's rows of one block ascend; ties keep the lower index
+              best = a[i];
+              best_idx = static_cast<unsigned>(r0 + i);
+            }
+        }
+      }
     }
+    lds_publish(&done[wave], nseg);  // this wave reads no operand buffer any more
     if (late && lane == 0) __hip_atomic_store(P.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
@@ -628,6 +612,14 @@ SLayout layout_for(const pwg_step_desc* d) {
   return L;
 }
 
+// LDS of the step kernel: two operand buffers, the flag words and the
+// segments' first-block table.
+size_t lds_bytes(const pwg_step_desc* d) {
+  size_t need = 0;
+  for (int i = 0; i <= d->n_levels; ++i) need = std::max(need, region_bytes(d, i));
+  return 2 * align_up(need, 16) + kFlagBytes + align_up(4 * static_cast<size_t>(kMaxWgSegs + 1), 16);
+}
+
 Plan* plan_ptr(const pwg_step_desc* d, size_t ws_offset) {
   const uintptr_t p = reinterpret_cast<uintptr_t>(d->workspace) + ws_offset;
   return reinterpret_cast<Plan*>(align_up(p, 256));
@@ -720,10 +712,8 @@ int step_stream_check(const pwg_step_desc* d) {
   if (d->hidden % 256 != 0 || d->hidden > kMaxStreamCols)
     return fail(PWG_ERR_UNSUPPORTED, "stream schedule: hidden must be a multiple of 256 and at most %d", kMaxStreamCols);
   if (d->vocab >= (int64_t{1} << 30)) return fail(PWG_ERR_ARG, "stream schedule: vocabulary too large");
-  size_t need = 0;
-  for (int i = 0; i <= d->n_levels; ++i) need = std::max(need, region_bytes(d, i));
-  if (2 * align_up(need, 16) + kFlagBytes > kMaxLds)
-    return fail(PWG_ERR_UNSUPPORTED, "stream schedule: activation operands need %zu bytes of LDS", 2 * need);
+  if (lds_bytes(d) > kMaxLds)
+    return fail(PWG_ERR_UNSUPPORTED, "stream schedule: operands and claim counters need %zu bytes of LDS", lds_bytes(d));
   return PWG_OK;
 }
 
@@ -806,6 +796,9 @@ int step_stream_plan(const pwg_step_desc* d, size_t ws_offset, void* stream) {
     for (size_t j = 0; j < parts[b].size(); ++j) seg_flat[static_cast<size_t>(b) * stride + j] = parts[b][j];
   }
   h.seg_stride = stride;
+  if (stride > kMaxWgSegs)
+    return fail(PWG_ERR_UNSUPPORTED, "stream schedule: a workgroup would touch %d levels (at most %d)", stride,
+                kMaxWgSegs);
 
   hipError_t e = hipMemsetAsync(dbase, 0, lay.regions, st);  // partials, arrival counter, status, park
   if (e == hipSuccess) e = hipMemcpyAsync(dplan, &h, sizeof(Plan), hipMemcpyHostToDevice, st);
@@ -835,7 +828,7 @@ int step_stream_launch(const pwg_step_desc* d, size_t ws_offset, void* stream) {
     need = std::max(need, region_bytes(d, i));
     if (i < d->n_levels) conv_x = std::max(conv_x, static_cast<int>((d->levels[i].cols / 8 + 255) / 256));
   }
-  const size_t lds = 2 * align_up(need, 16) + kFlagBytes;
+  const size_t lds = lds_bytes(d);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(stream_convert_kernel, dim3(conv_x, d->n_levels + 1), dim3(256), 0, st, dplan, lv);
   if (prefetch_depth(d) == 8)
