@@ -16,8 +16,22 @@ constexpr int kInt8MfmaBytes = 4 * 3 * 16;
 constexpr int kSectionMfmas = 4;                  // int8 MFMAs per exponent section (256 values of h)
 constexpr int kMaxStreamCols = 12288;             // two operand buffers of this width fit in LDS
 constexpr size_t kMaxLds = 160 * 1024;
-constexpr size_t kFlagBytes = 128;                // ready word, done words, claim counter, per-wave argmax keys
-constexpr int kMaxWgSegs = 32;                    // segments (levels touched) per workgroup
+constexpr int kStreamWaves = 8;                   // waves per workgroup (one control wave)
+constexpr size_t kFlagBytes = 256;                // ready word, claim counters, done words, per-wave argmax keys
+static_assert(kStreamWaves <= 16, "flag words");
+constexpr int kMaxWgSegs = 32;                    // static segments (levels touched) per workgroup
+constexpr int kMaxPoolSegs = 16;                  // levels of the shared pool (the vocabulary first)
+constexpr double kPoolTailShare = 0.04;           // small-block ternary levels that end the pool: this share of the bytes
+constexpr int kRing = 64;                         // pool claims queued per workgroup (ring entries)
+constexpr int kPoolAhead = 6;                     // claims a workgroup keeps ready beyond its pops
+constexpr int kClaimBatch = 8;                    // pool blocks per global atomic ...
+constexpr int kLateClaims = 16;                   // ... until fewer than this many per workgroup remain,
+constexpr int kLateBatch = 4;                     // then this many
+// LDS after the two operand buffers: flag words and argmax keys, the static
+// segments' first-block table, the pool claim ring.
+constexpr size_t kSegFirstOff = kFlagBytes;
+constexpr size_t kRingOff = kSegFirstOff + (4 * (kMaxWgSegs + 1) + 15) / 16 * 16;
+constexpr size_t kLdsTailBytes = kRingOff + 8 * kRing;
 constexpr size_t kParkBytes = 16 * 1024;          // tiles a wave re-reads after its last one
 enum { kKindTernary = 0, kKindInt8 = 1 };
 
@@ -57,6 +71,10 @@ struct Seg {
   int level, b0, b1, pad;
 };
 
+// Work split: every workgroup first takes its static segments (contiguous
+// ranges of the ternary levels), then claims blocks of the shared pool (the
+// vocabulary, then one small-block ternary level) from one global counter,
+// so that workgroups that stream faster take more of the pool.
 struct Plan {
   int n_levels;             // ternary levels; levels[n_levels] is the vocabulary
   int grid;
@@ -64,7 +82,11 @@ struct Plan {
   int buf_bytes;            // one LDS operand buffer
   int vocab, hidden;
   int depth;                // tiles in flight per compute wave
-  int pad;
+  int pool_nseg;            // pool segments (levels), in claim order
+  int pool_total;           // pool blocks
+  int pool_first[kMaxPoolSegs + 1];  // first pool index of each pool segment (then pool_total)
+  Seg pool_segs[kMaxPoolSegs];
+  unsigned* pool_next;      // global claim counter
   const int* seg_count;     // [grid]
   const float* h;
   const dev::u32x4* emb_table;

@@ -51,7 +51,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8;               // wave 0: control; waves 1..7: compute
+constexpr int kWaves = kStreamWaves;     // wave 0: control; the others compute
 constexpr int kCompute = kWaves - 1;
 constexpr int kThreads = kWaves * 64;
 constexpr unsigned kMask = 0xCCCCCCCCu;
@@ -98,64 +98,48 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
-// The producer half of a compute wave: claims 16-row blocks of its
-// workgroup's work, in order, from one counter in LDS (one atomic add per
-// block, so the waves of a workgroup share the blocks dynamically), and
-// issues the 1 KiB tile loads of the claimed block.  Claim f is the f-th
-// block of the concatenated segments; seg_first holds the prefix sums of the
-// segments' block counts.  A claim happens when the loads cross into the
-// next block, so a wave holds at most one block beyond the one it computes
-// on; the claim is left in (mseg, mblk) for the consumer half.  State is
-// wave-uniform and claims are loop-free (a fixed-depth search over at most
-// kMaxWgSegs segments), which keeps the compiler from splitting the tile
-// registers' live ranges around them.
+// The producer half of a compute wave: issues the 1 KiB tile loads of the
+// wave's current block, then of the next block the consumer half has
+// already claimed; parks on a scratch area once nothing is left.  A block's
+// tiles are read starting at tile `rot` (a multiple of the group size) and
+// wrapping around, rot depending on the block index only: the ~1,800 blocks
+// in flight across the chip then do not all read the same offset of their
+// block at the same time.  Loop-free, so the tile loop stays simple enough
+// for the compiler to keep the tile registers in one assignment.  State is
+// wave-uniform.
 struct Producer {
-  const Seg* segs;
-  const Level* levels;
-  int* wcnt;                  // LDS claim counter
-  const int* seg_first;       // LDS [nseg + 1] first flat block of each segment
-  int total;                  // blocks of the workgroup
-  const unsigned char* ptr;   // this lane's 16 bytes of the next tile
-  const unsigned char* park;  // kParkBytes re-read once nothing is left
-  int left;                   // tiles of the claimed block still to load
-  int mseg, mblk;             // latest claim (mseg = -1: nothing left)
+  const unsigned char* base;   // this lane's 16 bytes of tile 0 of the current block
+  int T, rot, pos;             // tiles per block, first tile, tiles issued (T = 0: parked)
+  const unsigned char* nbase;  // the next block (nT = 0: none)
+  int nT, nrot;
 
-  __device__ __forceinline__ void claim(unsigned lane) {
-    int f = 0;
-    if (lane == 0) f = __hip_atomic_fetch_add(wcnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    f = uni(f);
-    if (f >= total) {
-      ptr = park + lane * 16u;
-      left = 0;
-      mseg = -1;
-      return;
+  // Moves to the claimed next block once the current one is fully issued.
+  __device__ __forceinline__ void step_block() {
+    if (pos >= T) {
+      base = nbase;
+      T = nT;
+      rot = nrot;
+      pos = 0;
+      nT = 0;
     }
-    int sidx = 0;
-#pragma unroll
-    for (int step = kMaxWgSegs / 2; step >= 1; step >>= 1)
-      if (seg_first[sidx + step] <= f) sidx += step;  // seg_first[s] = total for s >= nseg
-    sidx = uni(sidx);
-    const Seg& s = segs[sidx];
-    const int b = uni(s.b0) + f - uni(seg_first[sidx]);
-    const Level& L = levels[s.level];
-    const int T = uni(L.tiles);
-    ptr = uni(L.w) + static_cast<size_t>(b) * static_cast<size_t>(T) * 1024u + lane * 16u;
-    left = T;
-    mseg = sidx;
-    mblk = b;
   }
-  // One group of GR tile loads (claiming the next block first if the
-  // current one is fully loaded), branch-free after the claim.
   template <int GR>
-  __device__ __forceinline__ void issue(u32x4 (&x)[GR], unsigned lane) {
-    if (left == 0 && mseg >= 0) claim(lane);
+  __device__ __forceinline__ void issue(u32x4 (&x)[GR]) {
+    step_block();
+    int off = rot + pos;
+    off = off >= T ? off - T : off;
 #pragma unroll
-    for (int j = 0; j < GR; ++j) x[j] = __builtin_nontemporal_load((const g_u32x4*)(ptr + 1024 * j));
-    const int step = left > 0 ? GR : 0;
-    ptr += step * 1024;
-    left = uni(left - step);
+    for (int j = 0; j < GR; ++j) x[j] = __builtin_nontemporal_load((const g_u32x4*)(base + 1024 * (off + j)));
+    pos = uni(pos + (T > 0 ? GR : 0));
   }
 };
+
+// First tile of block `blk` of a level with T tiles per block (groups of G).
+template <int G>
+__device__ __forceinline__ int block_rot(int blk, int T) {
+  if (G == 0) return 0;
+  return ((blk * 5) % (T / G)) * G;
+}
 
 // A operands of one ternary tile slice: FP4 nibbles +2 / -2 / 0 of the 64
 // weights in this lane's 16 bytes (two MFMAs' worth).
@@ -260,6 +244,22 @@ __device__ __forceinline__ void embed_row(const Plan& P, unsigned lane) {
   }
 }
 
+// Segment s of a workgroup: its static segments first, then the pool's.
+__device__ __forceinline__ Seg seg_at(const Seg* segs, int nseg, const Plan& P, int s) {
+  Seg r;
+  if (s < nseg) {
+    r.level = uni(segs[s].level);
+    r.b0 = uni(segs[s].b0);
+    r.b1 = uni(segs[s].b1);
+  } else {
+    r.level = uni(P.pool_segs[s - nseg].level);
+    r.b0 = uni(P.pool_segs[s - nseg].b0);
+    r.b1 = uni(P.pool_segs[s - nseg].b1);
+  }
+  r.pad = 0;
+  return r;
+}
+
 template <int G>
 __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __restrict__ plan,
                                                                    const Level* __restrict__ levels,
@@ -268,20 +268,26 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
   const Plan& P = *plan;
   const unsigned lane = threadIdx.x & 63u;
   const unsigned wave = uni(threadIdx.x >> 6);
-  const int nseg = uni(P.seg_count[blockIdx.x]);
+  const int nseg = uni(P.seg_count[blockIdx.x]);   // static segments
+  const int nall = nseg + uni(P.pool_nseg);         // with the pool's
   const Seg* segs = all_segs + static_cast<size_t>(blockIdx.x) * P.seg_stride;
   const int buf_bytes = P.buf_bytes;
-  int* ready = reinterpret_cast<int*>(smem + 2 * buf_bytes);  // highest segment whose operands are in LDS
-  int* done = ready + 1;                                       // [kWaves]: highest segment a wave finished
-  unsigned long long* wkeys = reinterpret_cast<unsigned long long*>(smem + 2 * buf_bytes + 64);
-  int* wcnt = ready + 12;                                      // block claims
-  int* seg_first = reinterpret_cast<int*>(smem + 2 * buf_bytes + kFlagBytes);  // [kMaxWgSegs + 1]
+  unsigned char* flags = smem + 2 * buf_bytes;
+  int* ready = reinterpret_cast<int*>(flags);        // highest segment whose operands are in LDS
+  int* wcnt = ready + 1;                              // claims of static blocks
+  int* phead = ready + 2;                             // pool claims popped from the ring
+  int* done = ready + 4;                              // [kWaves]: highest segment a wave is done with
+  unsigned long long* wkeys = reinterpret_cast<unsigned long long*>(flags + 128);  // [kWaves]
+  int* seg_first = reinterpret_cast<int*>(flags + kSegFirstOff);               // [kMaxWgSegs + 1]
+  unsigned long long* ring = reinterpret_cast<unsigned long long*>(flags + kRingOff);  // [kRing]
   if (threadIdx.x == 0) {
     *ready = -1;
     *wcnt = 0;
+    *phead = 0;
   }
   if (threadIdx.x < kWaves) done[threadIdx.x] = -1;
-  if (threadIdx.x == 64) {  // prefix sums of the segments' block counts (padded with the total)
+  if (threadIdx.x < kRing) ring[threadIdx.x] = ~0ull;  // tag 0xFFFFFFFF: empty
+  if (threadIdx.x == 64) {  // prefix sums of the static segments' block counts (padded with the total)
     int acc = 0;
     for (int i = 0; i <= kMaxWgSegs; ++i) {
       seg_first[i] = acc;
@@ -294,80 +300,191 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
   float best = -__builtin_inff();
   unsigned best_idx = 0xFFFFFFFFu;
   if (wave == 0) {
-    // Control wave: segment s's operand region into buffer s & 1, once every
-    // compute wave is done with segment s - 2 (the buffer's last user).
+    // Control wave: copies segment s's operand region into buffer s & 1
+    // once every compute wave is done with segment s - 2 (the buffer's last
+    // user), and keeps up to kPoolAhead pool claims queued in the ring
+    // beyond the compute waves' pops (one global atomic per claim; after
+    // the pool runs out, one end marker per compute wave).
     bool late = false;
-    for (int s = 0; s < nseg; ++s) {
-      if (s >= 2) {
-        const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
-        while (true) {
+    int s = 0, tail = 0, ends = 0, batch = kClaimBatch;
+    bool exhausted = false;
+    const int pool_total = uni(P.pool_total);
+    unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    while (s < nall || ends < kCompute) {
+      bool progress = false;
+      if (s < nall) {
+        bool ok = s < 2;
+        if (!ok) {
           const int d = (lane >= 1 && lane < kWaves) ? lds_acquire(&done[lane]) : s;
-          if (__all(d >= s - 2)) break;
-          if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
-            late = true;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
+          ok = __all(d >= s - 2);
+        }
+        if (ok) {
+          const Level& L = levels[seg_at(segs, nseg, P, s).level];
+          const unsigned char* src = uni(L.b);
+          const int bytes = uni(L.b_bytes);
+          unsigned char* dst = smem + (s & 1) * buf_bytes;
+          for (int o = 0; o < bytes; o += 1024)
+            if (o + 16 * static_cast<int>(lane) < bytes)
+              __builtin_amdgcn_global_load_lds(src + o + 16 * lane, PWG_LDS(dst + o), 16, 0, 0);
+          __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed in LDS
+          lds_publish(ready, s);
+          if (s == 0 && blockIdx.x == 0) embed_row(P, lane);
+          s = uni(s + 1);
+          progress = true;
         }
       }
-      const Level& L = levels[segs[s].level];
-      const unsigned char* src = uni(L.b);
-      const int bytes = uni(L.b_bytes);
-      unsigned char* dst = smem + (s & 1) * buf_bytes;
-      for (int o = 0; o < bytes; o += 1024)
-        if (o + 16 * static_cast<int>(lane) < bytes)
-          __builtin_amdgcn_global_load_lds(src + o + 16 * lane, PWG_LDS(dst + o), 16, 0, 0);
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed in LDS
-      lds_publish(ready, s);
-      if (s == 0 && blockIdx.x == 0) embed_row(P, lane);
+      if (ends < kCompute && tail - uni(lds_acquire(phead)) < kPoolAhead) {
+        // claims come in batches of `batch` consecutive pool blocks (one
+        // atomic each; under a full memory load an atomic takes microseconds),
+        // smaller batches once the pool is nearly used up
+        if (!exhausted) {
+          int p = 0;
+          if (lane == 0)
+            p = static_cast<int>(__hip_atomic_fetch_add(P.pool_next, static_cast<unsigned>(batch), __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT));
+          p = uni(p);
+          for (int q = 0; q < batch; ++q) {
+            const int pq = p + q < pool_total ? p + q : -1;
+            if (pq < 0) {
+              exhausted = true;
+              break;
+            }
+            if (lane == 0)
+              __hip_atomic_store(&ring[tail & (kRing - 1)],
+                                 (static_cast<unsigned long long>(static_cast<unsigned>(tail)) << 32) | static_cast<unsigned>(pq),
+                                 __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            tail = uni(tail + 1);
+          }
+          if (pool_total - (p + batch) < kLateClaims * P.grid) batch = kLateBatch;
+        } else {
+          if (lane == 0)
+            __hip_atomic_store(&ring[tail & (kRing - 1)],
+                               (static_cast<unsigned long long>(static_cast<unsigned>(tail)) << 32) | 0xFFFFFFFFull,
+                               __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+          tail = uni(tail + 1);
+          ends = uni(ends + 1);
+        }
+        progress = true;
+      }
+      if (progress) {
+        t0 = __builtin_amdgcn_s_memrealtime();
+      } else {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
+          late = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
     }
-    if (nseg == 0 && blockIdx.x == 0) embed_row(P, lane);
+    if (nall == 0 && blockIdx.x == 0) embed_row(P, lane);
     if (late && lane == 0) __hip_atomic_store(P.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
     const unsigned n = lane & 15u, g = lane >> 4;
+    bool late = false;
+    // Claims the next block: a static block from the workgroup counter (the
+    // segment from a fixed-depth search of the prefix sums), else a pool
+    // block from the ring.  Returns the segment (-1: nothing left).
+    bool static_done = false;
+    auto claim = [&](int& blk) -> int {
+      if (!static_done) {
+        int f = 0;
+        if (lane == 0) f = __hip_atomic_fetch_add(wcnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        f = uni(f);
+        if (f < total_blocks) {
+          int sidx = 0;
+#pragma unroll
+          for (int step = kMaxWgSegs / 2; step >= 1; step >>= 1)
+            if (seg_first[sidx + step] <= f) sidx += step;  // seg_first[i] = total for i >= nseg
+          sidx = uni(sidx);
+          blk = uni(segs[sidx].b0) + f - uni(seg_first[sidx]);
+          return sidx;
+        }
+        static_done = true;
+      }
+      int i = 0;
+      if (lane == 0) i = __hip_atomic_fetch_add(phead, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      i = uni(i);
+      const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+      unsigned long long v;
+      while (true) {
+        v = __hip_atomic_load(&ring[i & (kRing - 1)], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (uni(static_cast<int>(v >> 32)) == i) break;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
+          late = true;
+          return -1;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      const int p = uni(static_cast<int>(static_cast<unsigned>(v)));
+      if (p < 0) return -1;
+      int q = 0;  // pool_first[j] = pool_total for j >= pool_nseg
+#pragma unroll
+      for (int step = kMaxPoolSegs / 2; step >= 1; step >>= 1)
+        if (P.pool_first[q + step] <= p) q += step;
+      q = uni(q);
+      blk = uni(P.pool_segs[q].b0) + p - uni(P.pool_first[q]);
+      return nseg + q;
+    };
+    auto block_at = [&](int sidx, int blk, const unsigned char*& base, int& tiles, int& rot) {
+      const Level& L = levels[seg_at(segs, nseg, P, sidx).level];
+      tiles = uni(L.tiles);
+      base = uni(L.w) + static_cast<size_t>(blk) * static_cast<size_t>(tiles) * 1024u + lane * 16u;
+      rot = block_rot<G>(blk, tiles);
+    };
+
     Producer pr;
-    pr.segs = segs;
-    pr.levels = levels;
-    pr.wcnt = wcnt;
-    pr.seg_first = seg_first;
-    pr.total = total_blocks;
-    pr.park = P.park;
-    pr.ptr = P.park + lane * 16u;
-    pr.left = 0;
-    pr.mseg = 0;
-    pr.mblk = 0;
+    pr.base = P.park + lane * 16u;
+    pr.T = pr.rot = pr.pos = 0;
+    pr.nbase = P.park + lane * 16u;
+    pr.nT = pr.nrot = 0;
+    int cs, cblk = 0;  // the consumer's current block
+    cs = claim(cblk);
+    if (cs >= 0) block_at(cs, cblk, pr.base, pr.T, pr.rot);
     // Two groups of G tile registers: one group's loads are in flight while
     // the other group is consumed (G == 0: one tile at a time, no prefetch).
     constexpr int GR = G > 0 ? G : 1;
     u32x4 ra[GR], rb[GR];
-    if (G > 0) pr.template issue<GR>(ra, lane);  // claims the first block
+    if (G > 0) pr.template issue<GR>(ra);
 
     const unsigned tboff = (12u * g + (n < 12u ? n : n - 12u)) * 16u;  // ternary B entry of this lane
     const unsigned iboff = (3u * g + n % 3u) * 16u;                    // int8 B entry of this lane
     const int icexp = n < 3u ? static_cast<int>(8u * n) : -1000;       // digit weight (columns >= 3 vanish)
-    bool late = false;
     int cur = -1;  // segment whose operands this wave is using
     const unsigned char* buf = smem;
     int T = 0, rows = 0, kind = 0, bsc_off = 0, asc_off = 0;
     const float* scale = nullptr;
     float* y = nullptr;
-    for (;;) {
-      if (G == 0) pr.claim(lane);
-      const int s = pr.mseg, blk = pr.mblk;
-      if (s < 0) break;
-      if (s != cur) {
-        lds_publish(&done[wave], s - 1);  // done with every segment before s
+    while (cs >= 0) {
+      // Without prefetch the loads have not crossed into this block yet:
+      // make it current before the next claim replaces the claimed block.
+      if (G == 0) pr.step_block();
+      // The next block is claimed late, so that a wave holds as little
+      // unstarted work as possible when the pool runs out: just before the
+      // iteration whose loads cross into it (at the start for blocks of one
+      // iteration and without prefetch).
+      int nblk = 0, ns = -1;
+      auto claim_next = [&]() {
+        ns = claim(nblk);
+        if (ns >= 0) {
+          block_at(ns, nblk, pr.nbase, pr.nT, pr.nrot);
+        } else {
+          pr.nbase = P.park + lane * 16u;
+          pr.nT = pr.nrot = 0;
+        }
+      };
+      if (cs != cur) {
+        lds_publish(&done[wave], cs - 1);  // done with every segment before cs
         const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
-        while (uni(lds_acquire(ready)) < s) {
+        while (uni(lds_acquire(ready)) < cs) {
           if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
             late = true;
             break;
           }
           __builtin_amdgcn_s_sleep(1);
         }
-        cur = s;
-        buf = smem + (s & 1) * buf_bytes;
-        const Level& L = levels[segs[s].level];
+        cur = cs;
+        buf = smem + (cs & 1) * buf_bytes;
+        const Level& L = levels[seg_at(segs, nseg, P, cs).level];
         T = uni(L.tiles);
         rows = uni(L.rows);
         scale = uni(L.scale);
@@ -376,8 +493,11 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
         bsc_off = uni(L.bsc_off);
         asc_off = uni(L.asc_off);
       }
-      // One block: T tiles, 2 G per iteration; both kinds share the loop so
-      // that the tile registers keep one assignment.
+      const int blk = cblk;
+      const int rot = block_rot<G>(blk, T);
+      auto wrap = [&](int t) { return t >= T ? t - T : t; };
+      // One block: T tiles from tile rot on, 2 G per iteration; both kinds
+      // share the loop so that the tile registers keep one assignment.
       v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};  // ternary: two chains; int8: acc0 = sum
       v4i iacc = {0, 0, 0, 0};
       unsigned sb = 0, sa = 0;
@@ -404,19 +524,26 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
         }
       };
       if (G > 0) {
-        for (int it = 0; it < T; it += 2 * GR) {
-          pr.template issue<GR>(rb, lane);
-          __builtin_amdgcn_sched_barrier(0);
-          group(ra, it);
-          __builtin_amdgcn_sched_barrier(0);
-          pr.template issue<GR>(ra, lane);
-          __builtin_amdgcn_sched_barrier(0);
-          group(rb, it + GR);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        auto iterations = [&](int from, int to) {
+          for (int it = from; it < to; it += 2 * GR) {
+            pr.template issue<GR>(rb);
+            __builtin_amdgcn_sched_barrier(0);
+            group(ra, wrap(rot + it));
+            __builtin_amdgcn_sched_barrier(0);
+            pr.template issue<GR>(ra);
+            __builtin_amdgcn_sched_barrier(0);
+            group(rb, wrap(rot + it + GR));
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        };
+        const int tc = T - 2 * GR;  // the last iteration's loads cross into the next block
+        iterations(0, tc);
+        claim_next();
+        iterations(tc, T);
       } else {
+        claim_next();
         for (int it = 0; it < T; ++it) {
-          pr.template issue<GR>(ra, lane);
+          pr.template issue<GR>(ra);
           group(ra, it);
         }
       }
@@ -444,8 +571,10 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
             }
         }
       }
+      cs = ns;
+      cblk = nblk;
     }
-    lds_publish(&done[wave], nseg);  // this wave reads no operand buffer any more
+    lds_publish(&done[wave], nall);  // this wave reads no operand buffer any more
     if (late && lane == 0) __hip_atomic_store(P.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
@@ -479,7 +608,9 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
       }
       if (lane == 0) {
         *P.token_out = static_cast<int>(argmax_key_index(m));
-        __hip_atomic_store(P.arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next step
+        // every workgroup has arrived, so nobody claims any more: reset for the next step
+        __hip_atomic_store(P.pool_next, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(P.arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -612,12 +743,12 @@ SLayout layout_for(const pwg_step_desc* d) {
   return L;
 }
 
-// LDS of the step kernel: two operand buffers, the flag words and the
-// segments' first-block table.
+// LDS of the step kernel: two operand buffers, then flags, the segments'
+// first-block table and the pool claim ring.
 size_t lds_bytes(const pwg_step_desc* d) {
   size_t need = 0;
   for (int i = 0; i <= d->n_levels; ++i) need = std::max(need, region_bytes(d, i));
-  return 2 * align_up(need, 16) + kFlagBytes + align_up(4 * static_cast<size_t>(kMaxWgSegs + 1), 16);
+  return 2 * align_up(need, 16) + kLdsTailBytes;
 }
 
 Plan* plan_ptr(const pwg_step_desc* d, size_t ws_offset) {
@@ -634,48 +765,69 @@ int grid_size(int* grid) {
   return PWG_OK;
 }
 
-// Relative cost of one tile (16 rows x 64 bytes) of each kind.
-constexpr double kTernaryTileCost = 1.0;
-constexpr double kInt8TileCost = 1.0;
 
-// Splits the concatenation of every level's 16-row blocks (then the
-// vocabulary's) into `grid` contiguous ranges of equal cost; each
-// workgroup's ranges are its segments, one per level it touches.
-void partition(const pwg_step_desc* d, int grid, std::vector<std::vector<Seg>>& out) {
-  const int n = d->n_levels;
-  std::vector<long long> blocks(n + 1);
-  std::vector<double> cost(n + 1), start(n + 2);
-  for (int i = 0; i < n; ++i) {
-    blocks[i] = (d->levels[i].rows + 15) / 16;
-    cost[i] = static_cast<double>(d->levels[i].cols / 256) * kTernaryTileCost;
+// The ternary levels that end the shared pool: the last levels (in
+// decoder order) with the fewest tiles per block, until they hold
+// kPoolTailShare of the weight bytes.  Small blocks make the last claims
+// even out; the vocabulary's blocks are four times larger.
+std::vector<int> pool_tail_levels(const pwg_step_desc* d) {
+  std::vector<int> out;
+  if (d->n_levels == 0) return out;
+  int64_t min_cols = d->levels[0].cols, total = d->vocab * d->hidden;
+  for (int i = 0; i < d->n_levels; ++i) {
+    min_cols = std::min<int64_t>(min_cols, d->levels[i].cols);
+    total += d->levels[i].rows * d->levels[i].cols / 4;
   }
-  blocks[n] = (d->vocab + 15) / 16;
-  cost[n] = static_cast<double>(d->hidden / 64) * kInt8TileCost;
+  int64_t acc = 0;
+  for (int i = d->n_levels - 1; i >= 0 && static_cast<int>(out.size()) < kMaxPoolSegs - 1; --i) {
+    if (d->levels[i].cols != min_cols) continue;
+    out.insert(out.begin(), i);
+    acc += d->levels[i].rows * d->levels[i].cols / 4;
+    if (static_cast<double>(acc) >= kPoolTailShare * static_cast<double>(total)) break;
+  }
+  return out;
+}
+
+// Splits the concatenation of the ternary levels' 16-row blocks (all but
+// the pool's tail levels) into `grid` contiguous ranges of equal size; each
+// workgroup's ranges are its static segments, one per level it touches.
+void partition(const pwg_step_desc* d, int grid, const std::vector<int>& tail, std::vector<std::vector<Seg>>& out) {
+  std::vector<int> lvl;
+  for (int i = 0; i < d->n_levels; ++i)
+    if (std::find(tail.begin(), tail.end(), i) == tail.end()) lvl.push_back(i);
+  const int n = static_cast<int>(lvl.size());
+  out.assign(grid, {});
+  if (n == 0) return;
+  std::vector<long long> blocks(n);
+  std::vector<double> cost(n), start(n + 1);
+  for (int i = 0; i < n; ++i) {
+    blocks[i] = (d->levels[lvl[i]].rows + 15) / 16;
+    cost[i] = static_cast<double>(d->levels[lvl[i]].cols / 256);
+  }
   start[0] = 0.0;
-  for (int i = 0; i <= n; ++i) start[i + 1] = start[i] + static_cast<double>(blocks[i]) * cost[i];
-  const double total = start[n + 1];
+  for (int i = 0; i < n; ++i) start[i + 1] = start[i] + static_cast<double>(blocks[i]) * cost[i];
+  const double total = start[n];
   auto pos = [&](double x, int& lv, long long& b) {
     lv = 0;
-    while (lv < n && x >= start[lv + 1]) ++lv;
+    while (lv < n - 1 && x >= start[lv + 1]) ++lv;
     b = static_cast<long long>(std::llround((x - start[lv]) / cost[lv]));
     b = b < 0 ? 0 : (b > blocks[lv] ? blocks[lv] : b);
   };
-  out.assign(grid, {});
   int lv0 = 0;
   long long b0 = 0;
   for (int w = 0; w < grid; ++w) {
     int lv1;
     long long b1;
     if (w + 1 == grid) {
-      lv1 = n;
-      b1 = blocks[n];
+      lv1 = n - 1;
+      b1 = blocks[n - 1];
     } else {
       pos(total * (w + 1) / grid, lv1, b1);
     }
     for (int lv = lv0; lv <= lv1; ++lv) {
       const long long a = lv == lv0 ? b0 : 0;
       const long long e = lv == lv1 ? b1 : blocks[lv];
-      if (e > a) out[w].push_back(Seg{lv, static_cast<int>(a), static_cast<int>(e), 0});
+      if (e > a) out[w].push_back(Seg{lvl[lv], static_cast<int>(a), static_cast<int>(e), 0});
     }
     lv0 = lv1;
     b0 = b1;
@@ -785,8 +937,21 @@ int step_stream_plan(const pwg_step_desc* d, size_t ws_offset, void* stream) {
     off += align_up(region_bytes(d, i), 256);
   }
 
+  const std::vector<int> tail = pool_tail_levels(d);
+  h.pool_nseg = 0;
+  h.pool_first[0] = 0;
+  auto add_pool = [&](int level, int blocks) {
+    h.pool_segs[h.pool_nseg] = Seg{level, 0, blocks, 0};
+    h.pool_first[h.pool_nseg + 1] = h.pool_first[h.pool_nseg] + blocks;
+    h.pool_nseg += 1;
+  };
+  add_pool(d->n_levels, static_cast<int>((d->vocab + 15) / 16));
+  for (int t : tail) add_pool(t, static_cast<int>((d->levels[t].rows + 15) / 16));
+  h.pool_total = h.pool_first[h.pool_nseg];
+  for (int i = h.pool_nseg + 1; i <= kMaxPoolSegs; ++i) h.pool_first[i] = h.pool_total;
+  h.pool_next = reinterpret_cast<unsigned*>(dbase + lay.arrivals + 128);
   std::vector<std::vector<Seg>> parts;
-  partition(d, grid, parts);
+  partition(d, grid, tail, parts);
   int stride = 1;
   for (const auto& v : parts) stride = std::max(stride, static_cast<int>(v.size()));
   std::vector<Seg> seg_flat(static_cast<size_t>(grid) * stride, Seg{0, 0, 0, 0});
