@@ -62,10 +62,18 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_sha() -> str:
+# Sources of each schedule's step kernel: the HBM traffic counted for a
+# kernel stays valid while these files are unchanged.
+KERNEL_SOURCES = {
+    "stream": ("step_stream.hip", "step_stream.h", "device_common.h", "pwg_internal.h"),
+    "persistent": ("step_persistent.hip", "t2_rows.h", "device_common.h", "pwg_internal.h"),
+}
+
+
+def kernel_source_sha(schedule: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "packed_weight_gemv_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(KERNEL_SOURCES.get(schedule, os.listdir(csrc))):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -247,9 +255,27 @@ def main():
             src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")   # 1 GiB
             dst = torch.empty_like(src)
             dst.copy_(src)
+            del src, dst
+            # the VALU kernels on the same kinds of work, for the VALU-busy
+            # counters: the row-major ternary GEMV on a 393,216 x 4,096
+            # matrix (402 MB, more than the last-level cache; arbitrary
+            # bytes: the instruction stream does not depend on the values)
+            # and the int8 projection on the output table
+            rows_big, cols_big = 393216, 4096
+            wbig = torch.randint(0, 256, (pwg.packed_size(rows_big, cols_big),), dtype=torch.uint8,
+                                 device="cuda:0")
+            sbig = torch.full((rows_big,), 0.05, dtype=torch.float32, device="cuda:0")
+            xbig = torch.randn(cols_big, dtype=torch.float32, device="cuda:0")
+            ybig = torch.empty(rows_big, dtype=torch.float32, device="cuda:0")
+            table = wl.weights[pwg.LAYOUT_ROWS][1] if pwg.LAYOUT_ROWS in wl.weights else None
+            for _ in range(3):
+                pwg.ternary_gemv(wbig, sbig, rows_big, cols_big, xbig, y=ybig, stream=stream)
+                if table is not None:
+                    pwg.int8_gemv_argmax(table, wl.desc.out_scale, wl.desc.h, stream=stream)
         torch.cuda.synchronize()
         pwg.step_status(wl.desc, stream=stream)
-        log("counter run done: 3 steps + one 1 GiB device-to-device copy")
+        log("counter run done: 3 steps, one 1 GiB device-to-device copy, 3 row-major ternary GEMVs "
+            "(393216x4096) and 3 row-major int8 projections")
         return
 
     def run(desc_schedule):
@@ -345,7 +371,7 @@ def main():
         tfile = os.path.join(ROOT, "profiles", "step_kernel_traffic.json")
         if os.path.exists(tfile):
             t = json.load(open(tfile))
-            if (t.get("kernel_source_sha") == kernel_source_sha() and t.get("layers") == args.layers
+            if (t.get("kernel_source_sha") == kernel_source_sha(args.schedule) and t.get("layers") == args.layers
                     and t.get("schedule") == args.schedule):
                 traffic = t.get("hbm_bytes_per_launch")
         kname = ("step_kernel<ordered> (whole step, one launch)" if schedule == pwg.SCHEDULE_PERSISTENT else
@@ -353,7 +379,7 @@ def main():
         result["roofline"] = {"bound": "hbm", "achieved": achieved_bps / 1e9, "peak": PEAK_HBM_BPS / 1e9,
                               "unit": "GB/s", "frac": achieved_bps / PEAK_HBM_BPS, "traffic": traffic,
                               "kernel": kname, "per_launch_bytes": step_bytes, "avg_launch_us": ms * 1e3}
-    result["kernel_source_sha"] = kernel_source_sha()
+    result["kernel_source_sha"] = kernel_source_sha(args.schedule)
 
     if not args.no_small_batch:
         result["small_batch"] = small_batch(wl, stream)
