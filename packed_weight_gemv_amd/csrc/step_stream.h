@@ -16,7 +16,7 @@ constexpr int kInt8MfmaBytes = 4 * 3 * 16;
 constexpr int kSectionMfmas = 4;                  // int8 MFMAs per exponent section (256 values of h)
 constexpr int kMaxStreamCols = 12288;             // two operand buffers of this width fit in LDS
 constexpr size_t kMaxLds = 160 * 1024;
-constexpr int kStreamWaves = 8;                   // waves per workgroup (one control wave)
+constexpr int kStreamWaves = 8;                   // waves per workgroup (two control waves)
 constexpr size_t kFlagBytes = 256;                // ready word, claim counters, done words, per-wave argmax keys
 static_assert(kStreamWaves <= 16, "flag words");
 constexpr int kMaxWgSegs = 32;                    // static segments (levels touched) per workgroup
@@ -27,11 +27,14 @@ constexpr int kPoolAhead = 6;                     // claims a workgroup keeps re
 constexpr int kClaimBatch = 8;                    // pool blocks per global atomic ...
 constexpr int kLateClaims = 16;                   // ... until fewer than this many per workgroup remain,
 constexpr int kLateBatch = 4;                     // then this many
-// LDS after the two operand buffers: flag words and argmax keys, the static
-// segments' first-block table, the pool claim ring.
+// LDS after the operand regions: flag words and argmax keys, the static
+// segments' first-block table, the pool claim ring, the segments' region
+// offsets.
+constexpr int kMaxSegs = kMaxWgSegs + kMaxPoolSegs;  // segments of one workgroup
 constexpr size_t kSegFirstOff = kFlagBytes;
 constexpr size_t kRingOff = kSegFirstOff + (4 * (kMaxWgSegs + 1) + 15) / 16 * 16;
-constexpr size_t kLdsTailBytes = kRingOff + 8 * kRing;
+constexpr size_t kSegOffOff = kRingOff + 8 * kRing;   // [kMaxSegs][2]: LDS start and end of each segment's operands
+constexpr size_t kLdsTailBytes = kSegOffOff + 8 * kMaxSegs;
 constexpr size_t kParkBytes = 16 * 1024;          // tiles a wave re-reads after its last one
 enum { kKindTernary = 0, kKindInt8 = 1 };
 
@@ -79,7 +82,7 @@ struct Plan {
   int n_levels;             // ternary levels; levels[n_levels] is the vocabulary
   int grid;
   int seg_stride;
-  int buf_bytes;            // one LDS operand buffer
+  int buf_bytes;            // LDS for operand regions (a ring of variable-size regions)
   int vocab, hidden;
   int depth;                // tiles in flight per compute wave
   int pool_nseg;            // pool segments (levels), in claim order

@@ -26,13 +26,16 @@
 // 23-bit fixed point per 256-element section; four instructions accumulate
 // exactly in int32 before one conversion to float per section.
 //
-// Work: 16-row blocks of every level and of the vocabulary, split over the
-// workgroups (one per CU) as contiguous ranges of equal cost, and within a
-// workgroup over 7 compute waves.  Each compute wave streams its tiles through
-// a ring of D registers (D tiles in flight, loads issued D tiles ahead across
-// block, level and segment boundaries).  Wave 0 copies each segment's
-// converted activation operands into one of two LDS buffers, ahead of the
-// compute waves.  The last workgroup to finish reduces the argmax.
+// Work: 16-row blocks of every level and of the vocabulary.  Each workgroup
+// (one per CU) first takes a contiguous range of the ternary levels of equal
+// cost, then claims blocks of a shared pool (the vocabulary, then a few
+// small-block ternary levels) from a global counter.  Inside a workgroup, 6
+// compute waves claim blocks one at a time and stream their tiles through two
+// register groups (one group's loads in flight while the other is consumed,
+// across block, level and segment boundaries).  Wave 0 claims pool blocks
+// ahead into an LDS ring; wave 1 copies each segment's converted activation
+// operands into a ring of LDS regions ahead of the compute waves.  The last
+// workgroup to finish reduces the argmax.
 #include <algorithm>
 #include <cmath>
 #include <vector>
@@ -51,8 +54,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = kStreamWaves;     // wave 0: control; the others compute
-constexpr int kCompute = kWaves - 1;
+constexpr int kWaves = kStreamWaves;     // wave 0 claims pool blocks, wave 1 stages operands, the others compute
+constexpr int kControl = 2;
+constexpr int kCompute = kWaves - kControl;
 constexpr int kThreads = kWaves * 64;
 constexpr unsigned kMask = 0xCCCCCCCCu;
 constexpr unsigned long long kSpinLimit = 50000000ull;  // 0.5 s of the 100 MHz real-time counter
@@ -280,6 +284,7 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
   unsigned long long* wkeys = reinterpret_cast<unsigned long long*>(flags + 128);  // [kWaves]
   int* seg_first = reinterpret_cast<int*>(flags + kSegFirstOff);               // [kMaxWgSegs + 1]
   unsigned long long* ring = reinterpret_cast<unsigned long long*>(flags + kRingOff);  // [kRing]
+  int* seg_pos = reinterpret_cast<int*>(flags + kSegOffOff);                   // [kMaxSegs][2]
   if (threadIdx.x == 0) {
     *ready = -1;
     *wcnt = 0;
@@ -300,40 +305,16 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
   float best = -__builtin_inff();
   unsigned best_idx = 0xFFFFFFFFu;
   if (wave == 0) {
-    // Control wave: copies segment s's operand region into buffer s & 1
-    // once every compute wave is done with segment s - 2 (the buffer's last
-    // user), and keeps up to kPoolAhead pool claims queued in the ring
-    // beyond the compute waves' pops (one global atomic per claim; after
-    // the pool runs out, one end marker per compute wave).
+    // Claim wave: keeps up to kPoolAhead pool claims queued in the claim
+    // ring beyond the compute waves' pops (one global atomic per batch of
+    // claims); after the pool runs out, one end marker per compute wave.
     bool late = false;
-    int s = 0, tail = 0, ends = 0, batch = kClaimBatch;
+    int tail = 0, ends = 0, batch = kClaimBatch;
     bool exhausted = false;
     const int pool_total = uni(P.pool_total);
     unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
-    while (s < nall || ends < kCompute) {
-      bool progress = false;
-      if (s < nall) {
-        bool ok = s < 2;
-        if (!ok) {
-          const int d = (lane >= 1 && lane < kWaves) ? lds_acquire(&done[lane]) : s;
-          ok = __all(d >= s - 2);
-        }
-        if (ok) {
-          const Level& L = levels[seg_at(segs, nseg, P, s).level];
-          const unsigned char* src = uni(L.b);
-          const int bytes = uni(L.b_bytes);
-          unsigned char* dst = smem + (s & 1) * buf_bytes;
-          for (int o = 0; o < bytes; o += 1024)
-            if (o + 16 * static_cast<int>(lane) < bytes)
-              __builtin_amdgcn_global_load_lds(src + o + 16 * lane, PWG_LDS(dst + o), 16, 0, 0);
-          __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed in LDS
-          lds_publish(ready, s);
-          if (s == 0 && blockIdx.x == 0) embed_row(P, lane);
-          s = uni(s + 1);
-          progress = true;
-        }
-      }
-      if (ends < kCompute && tail - uni(lds_acquire(phead)) < kPoolAhead) {
+    while (ends < kCompute) {
+      if (tail - uni(lds_acquire(phead)) < kPoolAhead) {
         // claims come in batches of `batch` consecutive pool blocks (one
         // atomic each; under a full memory load an atomic takes microseconds),
         // smaller batches once the pool is nearly used up
@@ -364,9 +345,59 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
           tail = uni(tail + 1);
           ends = uni(ends + 1);
         }
-        progress = true;
+        t0 = __builtin_amdgcn_s_memrealtime();
+      } else {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
+          late = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
       }
-      if (progress) {
+    }
+    if (late && lane == 0) __hip_atomic_store(P.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (wave == 1) {
+    // Staging wave: copies segment s's operand region into the LDS region
+    // ring as soon as it has room.  The ring is 2 buf_bytes long, buf_bytes
+    // >= the largest region; a region goes right after the previous one,
+    // never straddles the middle, and may not overlap a region a compute
+    // wave may still read (segments after the lowest one every compute wave
+    // is done with).  So small regions are staged several segments ahead,
+    // and a region always fits once only the previous segment is in use.
+    bool late = false;
+    int s = 0, head = 0;
+    unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    while (s < nall) {
+      const Level& L = levels[seg_at(segs, nseg, P, s).level];
+      const int bytes = uni(L.b_bytes);
+      int d = (lane >= kControl && lane < kWaves) ? lds_acquire(&done[lane]) : 0x7FFFFFFF;
+      for (int off = 32; off >= 1; off >>= 1) d = min(d, __shfl_xor(d, off, kWave));
+      const int live0 = uni(d) + 1 > 0 ? uni(d) + 1 : 0;  // regions of segments live0 .. s - 1 may be in use
+      int c = head;
+      if (c < buf_bytes && c + bytes > buf_bytes) c = buf_bytes;
+      if (c + bytes > 2 * buf_bytes) c = 0;
+      int pos = -1;
+      for (int k = 0; k < 3 && pos < 0; ++k) {
+        const int cand = k == 0 ? c : (k == 1 ? 0 : buf_bytes);
+        bool free = true;
+        for (int j = live0; j < s; ++j)
+          if (cand < uni(seg_pos[2 * j + 1]) && uni(seg_pos[2 * j]) < cand + bytes) free = false;
+        if (free) pos = cand;
+      }
+      if (pos >= 0) {
+        const unsigned char* src = uni(L.b);
+        unsigned char* dst = smem + pos;
+        if (lane == 0) {
+          seg_pos[2 * s] = pos;
+          seg_pos[2 * s + 1] = pos + bytes;
+        }
+        head = pos + bytes;
+        for (int o = 0; o < bytes; o += 1024)
+          if (o + 16 * static_cast<int>(lane) < bytes)
+            __builtin_amdgcn_global_load_lds(src + o + 16 * lane, PWG_LDS(dst + o), 16, 0, 0);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed in LDS
+        lds_publish(ready, s);
+        if (s == 0 && blockIdx.x == 0) embed_row(P, lane);
+        s = uni(s + 1);
         t0 = __builtin_amdgcn_s_memrealtime();
       } else {
         if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
@@ -483,7 +514,7 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
           __builtin_amdgcn_s_sleep(1);
         }
         cur = cs;
-        buf = smem + (cs & 1) * buf_bytes;
+        buf = smem + uni(seg_pos[2 * cs]);
         const Level& L = levels[seg_at(segs, nseg, P, cs).level];
         T = uni(L.tiles);
         rows = uni(L.rows);
