@@ -54,20 +54,10 @@ struct DevLevel {
   const float* scale;
   const float* x;
   float* y;
-  unsigned* planes;  // limb planes of x in the workspace (stream schedule)
   int rows;
   int cols;
   int nchunks;  // cols / 64
   int c;        // chunks per lane
-};
-
-// Stream schedule: a contiguous row range of one level (n_levels: the
-// vocabulary), part of one workgroup's share of the step.
-struct Seg {
-  int level;
-  int row_begin;
-  int row_end;
-  int pad;
 };
 
 // Device-side plan, written by pwg_step_plan into the workspace.  It is
@@ -76,12 +66,11 @@ struct Seg {
 // live in the state, counter, flag and partial-key areas that follow it.
 struct alignas(256) Plan {
   unsigned n_levels;
-  unsigned n_barriers;     // barriers per step: n_levels + 1 (ordered) or 1
+  unsigned n_barriers;     // barriers per step: n_levels + 1
   unsigned mode;           // kBarrierL2 or kBarrierFlat
   unsigned grid;
   unsigned per_xcd[8];
   unsigned xcd_mask;
-  unsigned ordered;        // 1: level barriers; 0: levels only ordered within each workgroup
   int vocab, hidden, i8c;
   const u32x4* out_table;
   const float* out_scale;
@@ -94,10 +83,6 @@ struct alignas(256) Plan {
   float* emb_scale_out;
   float4* emb_deq_out;
   float* logits_out;
-  unsigned* vocab_planes;  // int8 limb planes of h in the workspace (stream schedule)
-  const Seg* segs;         // stream schedule: workgroup b's segments are segs[b * seg_stride ...]
-  const int* seg_count;    // stream schedule: segments per workgroup
-  int seg_stride;
   // offsets (bytes from the plan) of the state words, barrier words, partial keys and level table
   unsigned long long state_off, counters_off, flags_off, partials_off, levels_off, calib_off;
 };
@@ -110,9 +95,6 @@ __device__ __forceinline__ unsigned ld_sc(const unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_sc(unsigned* p, unsigned v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_sc(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_sc64(unsigned long long* p, unsigned long long v) {
@@ -213,38 +195,17 @@ struct Barrier {
 // ----------------------------------------------------------------- streaming
 // LDS budget of the step kernel (bytes).
 constexpr int kComputeWaves = kWpb - 1;                 // waves 1..7; wave 0 is the control wave
-constexpr int kRingOrdered = 8;                         // 1 KiB ring slots per compute wave: ordered
-constexpr int kRingStream = 16;                         // and stream schedule
+constexpr int kRing = 8;                                // 1 KiB ring slots per compute wave
 constexpr int kSlotBytes = 1024;                        // 64 lanes x 16 bytes
 constexpr int kMaxT2Cols = 64 * 64 * kMaxC;             // 12288
 constexpr int kMaxWgRows = 640;                         // rows of one level per workgroup
-constexpr size_t kRingBytes = static_cast<size_t>(kComputeWaves) * kRingOrdered * kSlotBytes;        // ordered
-constexpr size_t kRingBytesStream = static_cast<size_t>(kComputeWaves) * kRingStream * kSlotBytes;  // stream
+constexpr size_t kRingBytes = static_cast<size_t>(kComputeWaves) * kRing * kSlotBytes;
 constexpr size_t kStageBytes = kMaxT2Cols * 4;
 constexpr size_t kPlaneBytes = static_cast<size_t>(kMaxT2Cols / 64) * (kT2ChunkDwords + 1) * 4;
 constexpr size_t kScaleBytes = 2 * kMaxWgRows * 4;
-constexpr size_t kOutBytes = kMaxWgRows * 4;              // a level's outputs of the workgroup (ordered)
-// Stream schedule: each compute wave's row scales arrive in blocks of
-// kScaleBlock rows through a ring of kScaleBufs blocks in LDS.
-constexpr int kScaleBlock = 64;
-constexpr int kScaleBufs = 4;
-constexpr size_t kScaleRingBytes = static_cast<size_t>(kComputeWaves) * kScaleBufs * kScaleBlock * 4;
-// Ordered: ring | raw input | planes | 2 x scales | outputs.
-// Stream:  ring | planes (filled by copies of pre-converted planes) | scale rings.
-constexpr size_t kOrderedSmem = kRingBytes + kStageBytes + kPlaneBytes + kScaleBytes + kOutBytes;
-constexpr size_t kStreamSmem = kRingBytesStream + kPlaneBytes + kScaleRingBytes;
-constexpr size_t kStepSmem = kOrderedSmem > kStreamSmem ? kOrderedSmem : kStreamSmem;
-static_assert(kT2ChunkDwords * 4 * (kMaxT2Cols / 64) % 16 == 0, "plane copies move 16-byte units");
-
-// Bytes of the limb planes (with the chunk exponents) of a ternary level's
-// input and of the output projection's input; multiples of 16.
-__host__ __device__ constexpr size_t t2_plane_bytes(int cols) {
-  return (static_cast<size_t>(cols / 64) * (kT2ChunkDwords + 1) * 4 + 15) / 16 * 16;
-}
-__host__ __device__ constexpr size_t i8_plane_bytes(int cols) {
-  return (static_cast<size_t>(cols / 16) * (kI8ChunkDwords + 1) * 4 + 15) / 16 * 16;
-}
-static_assert(t2_plane_bytes(kMaxT2Cols) <= kPlaneBytes, "plane buffer");
+constexpr size_t kOutBytes = kMaxWgRows * 4;              // a level's outputs of the workgroup
+// LDS: ring | raw input | planes | 2 x scales | outputs.
+constexpr size_t kStepSmem = kRingBytes + kStageBytes + kPlaneBytes + kScaleBytes + kOutBytes;
 
 #define PWG_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -255,19 +216,6 @@ __device__ __forceinline__ void dma16(const void* g, void* lds) {
 }
 __device__ __forceinline__ void dma4(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, PWG_LDS(lds), 4, 0, 0);
-}
-
-// Stores v to an LDS word after this wave's earlier LDS reads have
-// completed, without waiting for its outstanding global-to-LDS copies.  The
-// compiler puts a wait for every outstanding copy before any LDS store of a
-// wave that has issued such copies (it cannot tell where they land), so the
-// store is written out here; the flag words are never a copy's destination.
-// LDS operations of a wave complete in order, so the extra one the compiler
-// does not count only makes its later LDS-counter waits longer.
-__device__ __forceinline__ void lds_publish(int* p, int v) {
-  const unsigned addr =
-      static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) int*)p));
-  asm volatile("s_waitcnt lgkmcnt(0)\n\tds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 
 // Waits until at most n of this wave's vector-memory operations are
@@ -326,36 +274,23 @@ __device__ __forceinline__ T* uni(T* p) {
   return reinterpret_cast<T*>((static_cast<unsigned long long>(hi) << 32) | lo);
 }
 
-// Level and workgroup row range [R0, R1) of work item `item`: level `item`
-// split over the workgroups (ordered), or the workgroup's segment `item`.
-__device__ __forceinline__ void item_rows(const Seg* segs, unsigned item, int vocab, const DevLevel* levels,
-                                          unsigned n_levels, unsigned nwg, unsigned& level, long& R0, long& R1) {
-  if (segs) {
-    // written by the plan before the launch and constant during the step:
-    // scalar loads (a vector load would wait behind the ring's copies)
-    typedef const __attribute__((address_space(4))) Seg const_seg;
-    const_seg* cs = (const_seg*)segs;
-    level = uni(static_cast<unsigned>(cs[item].level));
-    R0 = uni(cs[item].row_begin);
-    R1 = uni(cs[item].row_end);
-  } else {
-    level = item;
-    wg_rows(item < n_levels ? uni(levels[item].rows) : vocab, blockIdx.x, nwg, R0, R1);
-  }
+// Workgroup row range [R0, R1) of level `item` (item n_levels: the
+// vocabulary), split evenly over the workgroups.
+__device__ __forceinline__ void item_rows(unsigned item, int vocab, const DevLevel* levels, unsigned n_levels,
+                                          unsigned nwg, long& R0, long& R1) {
+  wg_rows(item < n_levels ? uni(levels[item].rows) : vocab, blockIdx.x, nwg, R0, R1);
 }
 
-// The producer half of a compute wave: walks the wave's rows of every work
-// item and copies each row's slots into its ring of RS slots.  All state is
+// The producer half of a compute wave: walks the wave's rows of every level
+// and copies each row's slots into its ring of RS slots.  All state is
 // wave-uniform.
 template <int RS>
 struct Producer {
   const DevLevel* levels;
-  const Seg* segs;    // this workgroup's segments (stream) or null (ordered: items are levels)
-  unsigned n_items;
+  unsigned n_items;   // levels, then the vocabulary
   unsigned n_levels;
   int vocab, hidden;
   const u32x4* out_table;
-  const float* out_scale;
   unsigned nwg;       // workgroups of the launch
   unsigned k;         // compute-wave index 0..6
   unsigned lane;
@@ -365,36 +300,25 @@ struct Producer {
   int chunk, chunks_per_row, nchunks;
   const u32x4* rowp;  // start of the current row
   unsigned char* ring;
-  // Row scales through the scale ring (stream schedule; sring null: none).
-  // A block of kScaleBlock rows of the item is copied before its first row's
-  // slots, so a wait for a row's slots also covers its scale.
-  float* sring;
-  const float* scale_src;  // the item's scale array
-  long first;              // the item's first row of this wave (rows first + kComputeWaves * i)
-  int count;               // the item's rows of this wave
-  int fast_rows;           // upcoming rows issue_row_fast may issue (see plan_fast)
-  unsigned sb_issued;      // scale blocks issued
-  unsigned sb_consumed;    // scale blocks the consumer is done with
-  unsigned sb_cons_base;   // consumer: scale blocks of the items before the current one
+  long first;         // the item's first row of this wave
+  int count;          // the item's rows of this wave
+  int fast_rows;      // upcoming rows issue_row_fast may issue (see plan_fast)
 
   // Moves to the first item, from `item` on, in which this wave has rows.
   __device__ __forceinline__ void enter_item() {
     item = uni(item);
     while (item < n_items) {
-      unsigned level;
       long R0, R1;
-      item_rows(segs, item, vocab, levels, n_levels, nwg, level, R0, R1);
+      item_rows(item, vocab, levels, n_levels, nwg, R0, R1);
       const u32x4* base;
-      if (level < n_levels) {
-        nchunks = uni(levels[level].nchunks);
-        chunks_per_row = uni(levels[level].c);
-        base = uni(levels[level].w);
-        scale_src = uni(levels[level].scale);
+      if (item < n_levels) {
+        nchunks = uni(levels[item].nchunks);
+        chunks_per_row = uni(levels[item].c);
+        base = uni(levels[item].w);
       } else {
         nchunks = hidden >> 4;
         chunks_per_row = (nchunks + 63) / 64;
         base = out_table;
-        scale_src = out_scale;
       }
       wave_rows(R0, R1, k, item, first, count);
       rows_left = uni(count);
@@ -410,43 +334,23 @@ struct Producer {
   }
 
   // Rows from the next one on that are plain: whole rows of 64-chunk
-  // multiples, not the item's last row, not starting a scale block.  Those
-  // take the straight-line issue_row_fast.
+  // multiples, not the item's last row.  Those take the straight-line
+  // issue_row_fast.
   __device__ __forceinline__ void plan_fast() {
-    const int ri = count - rows_left;  // index of the next row within the item
     int n = rows_left - 1;
     if (chunk != 0 || (nchunks & 63) != 0) n = 0;
-    if (sring) {
-      const int to_block = kScaleBlock - 1 - (ri % kScaleBlock);  // plain rows before the next block start
-      n = ri % kScaleBlock == 0 ? 0 : (n < to_block ? n : to_block);
-    }
     fast_rows = uni(n);
   }
 
   __device__ __forceinline__ bool active() const { return item < n_items; }
 
-  // Whether the next slot may be issued: the ring has room and, when the
-  // slot starts a scale block, the scale ring has a free block.
+  // Whether the next slot may be issued: the ring has room.
   __device__ __forceinline__ bool can_issue(unsigned consumed) const {
-    if (!active() || uni(issued) - uni(consumed) >= static_cast<unsigned>(RS)) return false;
-    if (sring && chunk == 0 && (count - rows_left) % kScaleBlock == 0)
-      return uni(sb_issued) - uni(sb_consumed) < static_cast<unsigned>(kScaleBufs);
-    return true;
+    return active() && uni(issued) - uni(consumed) < static_cast<unsigned>(RS);
   }
 
   // Issues the next slot (the caller checks can_issue()).
   __device__ __forceinline__ void issue() {
-    if (sring && chunk == 0) {
-      const int ri = count - rows_left;  // the row's index within the item
-      if (ri % kScaleBlock == 0) {
-        // scales of rows ri .. ri + 63 (lane i: row ri + i; lanes past the
-        // item's rows copy nothing)
-        if (ri + static_cast<int>(lane) < count)
-          dma4(scale_src + first + static_cast<long>(kRowStride) * (ri + static_cast<int>(lane)),
-               sring + (sb_issued % kScaleBufs) * kScaleBlock);
-        sb_issued = uni(sb_issued + 1);
-      }
-    }
     unsigned c = lane + 64u * static_cast<unsigned>(chunk);
     c = c < static_cast<unsigned>(nchunks) ? c : static_cast<unsigned>(nchunks - 1);
     dma16(rowp + c, ring + (issued % RS) * kSlotBytes);
@@ -515,42 +419,24 @@ __device__ __forceinline__ void take_row(Producer<RS>& pr, unsigned& consumed, c
 }
 
 // Row scale for the tile row this lane stores (tile row row_of<4>(lane >> 4),
-// row index i + that).  kRing: from the wave's scale ring, where the item's
-// scale blocks start at block number sb0; otherwise from the workgroup's LDS
-// copy of the level's scales starting at row R0.
-template <bool kRing, int RS>
-__device__ __forceinline__ float tile_scale(const float* scales, long first, int i, int count, long R0, unsigned lane,
-                                            const Producer<RS>& pr, unsigned sb0) {
+// row index i + that), from the workgroup's LDS copy of the level's scales
+// starting at row R0.
+__device__ __forceinline__ float tile_scale(const float* scales, long first, int i, int count, long R0, unsigned lane) {
   const int t = row_of<4>(static_cast<int>(lane >> 4));
   const int iu = i + t < count ? i + t : i;
-  if constexpr (kRing) {
-    const unsigned blk = sb0 + static_cast<unsigned>(iu / kScaleBlock);
-    return pr.sring[(blk % kScaleBufs) * kScaleBlock + iu % kScaleBlock];
-  } else {
-    return scales[first + static_cast<long>(kRowStride) * iu - R0];
-  }
-}
-
-// After a tile of rows i .. i + 3: the consumer is done with a scale block
-// when the tile ends one (blocks hold kScaleBlock rows, a multiple of 4).
-template <int RS>
-__device__ __forceinline__ void tile_done(Producer<RS>& pr, int i, int count) {
-  if ((i + 4) % kScaleBlock == 0 || i + 4 >= count) pr.sb_consumed = uni(pr.sb_consumed + 1);
+  return scales[first + static_cast<long>(kRowStride) * iu - R0];
 }
 
 // Consumes the wave's rows of one ternary level (C chunks of 64 words per
-// lane and row), four rows per tile reduction.  Results go to y, or to the
-// workgroup's LDS output buffer when `out_buf` is set.
-template <int C, bool kConst, int RS>
+// lane and row), four rows per tile reduction; results go to the
+// workgroup's LDS output buffer (stored to y by the control wave).
+template <int C, int RS>
 __device__ __forceinline__ void t2_consume_level(const DevLevel& L, long first, int count, long R0, const float* scales,
                                                  unsigned lane, Producer<RS>& pr, unsigned& consumed,
                                                  const unsigned char* ring, const unsigned* planes,
-                                                 const int* plane_e, float* out_buf, int* init_flag, int init_val) {
+                                                 const int* plane_e, float* out_buf) {
   T2Lane<C> st;
   t2_lane_init<C>(st, planes, plane_e, L.nchunks, lane);
-  if (init_flag) lds_publish(init_flag, init_val);  // the planes buffer may be refilled
-  const unsigned sb0 = pr.sb_cons_base;              // this item's first scale block
-  if (kConst) pr.sb_cons_base = uni(sb0 + static_cast<unsigned>((count + kScaleBlock - 1) / kScaleBlock));
   for (int i = 0; i < count; i += 4) {
     float p[4];
 #pragma unroll
@@ -571,22 +457,18 @@ __device__ __forceinline__ void t2_consume_level(const DevLevel& L, long first, 
     }
     const int iu = i + row_of<4>(static_cast<int>(lane >> 4));
     const long row = first + static_cast<long>(kRowStride) * iu;
-    const float sc = tile_scale<kConst, RS>(scales, first, i, count, R0, lane, pr, sb0);
-    if (kConst) tile_done(pr, i, count);
+    const float sc = tile_scale(scales, first, i, count, R0, lane);
     const float total = tile_reduce<4>(p);
-    if ((lane & 15u) == 0u && iu < count) {
-      const float v = sc * total;
-      if (out_buf) out_buf[row - R0] = v;  // published by the control wave
-      else L.y[row] = v;
-    }
+    if ((lane & 15u) == 0u && iu < count) out_buf[row - R0] = sc * total;
   }
 }
 
-template <bool kConst, int RS>
+// Consumes the wave's vocabulary rows: logits, and the wave's (max, lowest
+// row) of them.
+template <int RS>
 __device__ __forceinline__ void i8_consume_level(const Plan& P, long first, int count, long R0, const float* scales, unsigned lane,
                                  Producer<RS>& pr, unsigned& consumed, const unsigned char* ring,
-                                 const unsigned* planes, const int* plane_e, float& best, unsigned& best_idx,
-                                 int* init_flag, int init_val) {
+                                 const unsigned* planes, const int* plane_e, float& best, unsigned& best_idx) {
   const int nchunks = P.hidden >> 4;
   unsigned H[kMaxI8C][12];
   int Ec[kMaxI8C];
@@ -602,9 +484,6 @@ __device__ __forceinline__ void i8_consume_level(const Plan& P, long first, int 
       H[c][4 * q] = v.x; H[c][4 * q + 1] = v.y; H[c][4 * q + 2] = v.z; H[c][4 * q + 3] = v.w;
     }
   }
-  if (init_flag) lds_publish(init_flag, init_val);  // the planes buffer may be refilled
-  const unsigned sb0 = pr.sb_cons_base;              // this item's first scale block
-  if (kConst) pr.sb_cons_base = uni(sb0 + static_cast<unsigned>((count + kScaleBlock - 1) / kScaleBlock));
   const int cpr = (nchunks + 63) / 64;  // slots per row (4 for hidden = 4096)
   for (int i = 0; i < count; i += 4) {
     float p[4];
@@ -647,8 +526,7 @@ __device__ __forceinline__ void i8_consume_level(const Plan& P, long first, int 
     }
     const int iu = i + row_of<4>(static_cast<int>(lane >> 4));
     const long row = first + static_cast<long>(kRowStride) * iu;
-    const float sc = tile_scale<kConst, RS>(scales, first, i, count, R0, lane, pr, sb0);
-    if (kConst) tile_done(pr, i, count);
+    const float sc = tile_scale(scales, first, i, count, R0, lane);
     const float total = tile_reduce<4>(p);
     if ((lane & 15u) == 0u && iu < count) {
       const float logit = sc * total;
@@ -684,17 +562,6 @@ __device__ __forceinline__ void stage_scales(const Plan& P, const DevLevel* leve
     if (o + lane < R1) dma4(s + o + lane, scales + (o - R0));
 }
 
-// Control wave: copies level `li`'s pre-converted limb planes (li ==
-// n_levels: those of h) into an LDS plane buffer.
-__device__ __forceinline__ void stage_planes(const Plan& P, const DevLevel* levels, unsigned li, unsigned lane,
-                                             unsigned* buf) {
-  const unsigned char* src = reinterpret_cast<const unsigned char*>(li < P.n_levels ? levels[li].planes : P.vocab_planes);
-  const int bytes = static_cast<int>(li < P.n_levels ? t2_plane_bytes(levels[li].cols) : i8_plane_bytes(P.hidden));
-  unsigned char* dst = reinterpret_cast<unsigned char*>(buf);
-  for (int o = 0; o < bytes; o += 1024)
-    if (o + 16 * static_cast<int>(lane) < bytes) dma16(src + o + 16 * lane, dst + o);
-}
-
 // Embedding row of the previous token (workgroup 0, control wave).
 __device__ __forceinline__ void embed_row(const Plan& P, unsigned lane) {
   const int id = *P.token_in;
@@ -724,32 +591,29 @@ __device__ __forceinline__ void embed_row(const Plan& P, unsigned lane) {
   }
 }
 
-// A compute wave's rows of work item `item` (level li, workgroup rows
-// [R0, R1)); planes: the level's input limbs in LDS.  kConst: `scales` is the
-// level's scale array in global memory, else the workgroup's LDS copy.
-template <bool kConst, int RS>
-__device__ __forceinline__ void consume_item(const Plan& P, const DevLevel* levels, unsigned li, unsigned item, long R0,
-                                             long R1, unsigned k, const float* scales, unsigned lane, Producer<RS>& pr,
+// A compute wave's rows of level li (workgroup rows [R0, R1)); planes: the
+// level's input limbs in LDS; scales: the workgroup's LDS copy of its row
+// scales.
+template <int RS>
+__device__ __forceinline__ void consume_item(const Plan& P, const DevLevel* levels, unsigned li, long R0, long R1,
+                                             unsigned k, const float* scales, unsigned lane, Producer<RS>& pr,
                                              unsigned& consumed, const unsigned char* ring, const unsigned* planes,
-                                             float* out_buf, float& best, unsigned& best_idx, int* init_flag) {
+                                             float* out_buf, float& best, unsigned& best_idx) {
   long first;
   int count;
-  wave_rows(R0, R1, k, item, first, count);
+  wave_rows(R0, R1, k, li, first, count);
   if (li == P.n_levels) {
     const int* plane_e = reinterpret_cast<const int*>(planes + (P.hidden >> 4) * kI8ChunkDwords);
-    i8_consume_level<kConst, RS>(P, first, count, R0, scales, lane, pr, consumed, ring, planes, plane_e, best, best_idx,
-                                 init_flag, static_cast<int>(item));
+    i8_consume_level<RS>(P, first, count, R0, scales, lane, pr, consumed, ring, planes, plane_e, best, best_idx);
     return;
   }
   const DevLevel& L = levels[li];
   const int* plane_e = reinterpret_cast<const int*>(planes + L.nchunks * kT2ChunkDwords);
-  const int iv = static_cast<int>(item);
-  if (L.c == 1) t2_consume_level<1, kConst, RS>(L, first, count, R0, scales, lane, pr, consumed, ring, planes, plane_e, out_buf, init_flag, iv);
-  else if (L.c == 2) t2_consume_level<2, kConst, RS>(L, first, count, R0, scales, lane, pr, consumed, ring, planes, plane_e, out_buf, init_flag, iv);
-  else t2_consume_level<3, kConst, RS>(L, first, count, R0, scales, lane, pr, consumed, ring, planes, plane_e, out_buf, init_flag, iv);
+  if (L.c == 1) t2_consume_level<1, RS>(L, first, count, R0, scales, lane, pr, consumed, ring, planes, plane_e, out_buf);
+  else if (L.c == 2) t2_consume_level<2, RS>(L, first, count, R0, scales, lane, pr, consumed, ring, planes, plane_e, out_buf);
+  else t2_consume_level<3, RS>(L, first, count, R0, scales, lane, pr, consumed, ring, planes, plane_e, out_buf);
 }
 
-template <bool kOrdered>
 __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restrict__ plan,
                                                             const DevLevel* __restrict__ levels, unsigned* state,
                                                             unsigned long long* counters, unsigned* flags,
@@ -758,12 +622,9 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restric
   unsigned char* ring_all = smem;
   // ordered: raw input, one plane buffer, scales, outputs
   float* stage = reinterpret_cast<float*>(smem + kRingBytes);
-  // stream: (larger ring,) one plane buffer
-  unsigned* planes2 = reinterpret_cast<unsigned*>(smem + kRingBytesStream);
   unsigned* planes1 = reinterpret_cast<unsigned*>(smem + kRingBytes + kStageBytes);
-  float* scale_buf = reinterpret_cast<float*>(smem + kRingBytes + (kOrdered ? kStageBytes + kPlaneBytes : 2 * kPlaneBytes));
-  float* out_buf = kOrdered ? reinterpret_cast<float*>(smem + kRingBytes + kStageBytes + kPlaneBytes + kScaleBytes)
-                            : nullptr;
+  float* scale_buf = reinterpret_cast<float*>(smem + kRingBytes + kStageBytes + kPlaneBytes);
+  float* out_buf = reinterpret_cast<float*>(smem + kRingBytes + kStageBytes + kPlaneBytes + kScaleBytes);
 
   const Plan& P = *plan;
   Barrier bar;
@@ -778,13 +639,12 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restric
   const unsigned lane = threadIdx.x & 63u;
   const unsigned wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const unsigned k = wave - 1;  // compute-wave index (unused by wave 0)
-  constexpr int RS = kOrdered ? kRingOrdered : kRingStream;
+  constexpr int RS = kRing;
   unsigned char* ring = ring_all + static_cast<size_t>(wave == 0 ? 0 : k) * RS * kSlotBytes;
 
   Producer<RS> pr;
   pr.levels = levels;
-  pr.segs = kOrdered ? nullptr : P.segs + static_cast<size_t>(blockIdx.x) * P.seg_stride;
-  pr.n_items = kOrdered ? P.n_levels + 1 : static_cast<unsigned>(uni(P.seg_count[blockIdx.x]));
+  pr.n_items = P.n_levels + 1;
   pr.n_levels = P.n_levels;
   pr.vocab = P.vocab;
   pr.hidden = P.hidden;
@@ -795,34 +655,13 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restric
   pr.issued = 0;
   pr.item = 0;
   pr.ring = ring;
-  pr.out_scale = P.out_scale;
-  pr.sring = kOrdered ? nullptr
-                      : reinterpret_cast<float*>(smem + kRingBytesStream + kPlaneBytes) +
-                            static_cast<size_t>(wave == 0 ? 0 : k) * kScaleBufs * kScaleBlock;
-  pr.sb_issued = 0;
-  pr.sb_consumed = 0;
-  pr.sb_cons_base = 0;
   pr.first = 0;
   pr.count = 0;
   unsigned consumed = 0;
 
-  // Stream schedule: the waves synchronise through two LDS words instead of
-  // block barriers (see the level loop).
-  __shared__ int ready_level;            // highest segment whose planes are in LDS
-  __shared__ int done_level[kWpb];       // highest segment each compute wave has finished
-  if (!kOrdered) {
-    if (threadIdx.x == 0) ready_level = -1;
-    if (threadIdx.x < kWpb) done_level[threadIdx.x] = -1;
-    __syncthreads();
-  }
-
   if (wave == 0) {
-    if (kOrdered) {
-      stage_x(P, levels, 0, lane, stage);
-      stage_scales(P, levels, 0, lane, scale_buf);
-    } else if (pr.n_items > 0) {
-      stage_planes(P, levels, static_cast<unsigned>(pr.segs[0].level), lane, planes2);
-    }
+    stage_x(P, levels, 0, lane, stage);
+    stage_scales(P, levels, 0, lane, scale_buf);
     if (blockIdx.x == 0) embed_row(P, lane);
   } else {
     pr.enter_item();
@@ -831,7 +670,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restric
 
   float best = -__builtin_inff();
   unsigned best_idx = 0xFFFFFFFFu;
-  if (kOrdered) {
+  {
     for (unsigned li = 0; li <= P.n_levels; ++li) {
       float* scales = scale_buf + (li & 1u) * kMaxWgRows;
       const bool vocab = li == P.n_levels;
@@ -858,8 +697,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restric
       if (wave == 0) {
         if (li < P.n_levels) stage_scales(P, levels, li + 1, lane, scale_buf + ((li + 1) & 1u) * kMaxWgRows);
       } else {
-        consume_item<false, RS>(P, levels, li, li, R0, R1, k, scales, lane, pr, consumed, ring, planes1, out_buf, best,
-                                best_idx, nullptr);
+        consume_item<RS>(P, levels, li, R0, R1, k, scales, lane, pr, consumed, ring, planes1, out_buf, best, best_idx);
       }
       __syncthreads();  // planes, this level's scales and outputs are complete
       if (!vocab && wave == 0) {
@@ -868,55 +706,6 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restric
           if (o0 + lane < R1 - R0) y[R0 + o0 + lane] = out_buf[o0 + lane];
         bar.arrive_release(li);
       }
-    }
-  } else if (wave == 0) {
-    // Independent levels, split over the workgroups as contiguous row
-    // ranges (segments) of the concatenated levels.  The control wave copies
-    // segment j's pre-converted input planes into the plane buffer as soon
-    // as every compute wave has copied segment j - 1's limbs into registers,
-    // and publishes ready_level = j once the copies have landed.
-    const int n = static_cast<int>(pr.n_items);
-    __builtin_amdgcn_s_waitcnt(0);
-    __hip_atomic_store(&ready_level, 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    for (int j = 1; j < n; ++j) {
-      const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
-      while (true) {
-        const int d = (lane >= 1 && lane < kWpb)
-                          ? __hip_atomic_load(&done_level[lane], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)
-                          : j;
-        if (__all(d >= j - 1)) break;
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {  // scalar read: uniform
-          if (lane == 0) st_sc(&state[kStateStatus], kStatusTimeout);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      stage_planes(P, levels, static_cast<unsigned>(pr.segs[j].level), lane, planes2);
-      __builtin_amdgcn_s_waitcnt(0);
-      __hip_atomic_store(&ready_level, j, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-  } else {
-    // Compute wave: each segment as soon as its planes are in LDS; no block
-    // barrier.  After copying the segment's limbs into registers the wave
-    // publishes done_level = j (the plane buffer may then be refilled).
-    const unsigned n = pr.n_items;
-    for (unsigned j = 0; j < n; ++j) {
-      const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
-      // (the loaded word is the same in every lane; readfirstlane keeps the
-      // loop exit uniform)
-      while (uni(__hip_atomic_load(&ready_level, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) < static_cast<int>(j)) {
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
-          if (lane == 0) st_sc(&state[kStateStatus], kStatusTimeout);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      unsigned li;
-      long R0, R1;
-      item_rows(pr.segs, j, P.vocab, levels, P.n_levels, P.grid, li, R0, R1);
-      const float* scales = li < P.n_levels ? levels[li].scale : P.out_scale;
-      consume_item<true, RS>(P, levels, li, j, R0, R1, k, scales, lane, pr, consumed, ring, planes2, nullptr, best,
-                             best_idx, &done_level[wave]);
     }
   }
 
@@ -936,7 +725,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restric
       st_sc64(&partials[blockIdx.x], m);
     }
   }
-  const unsigned final_barrier = kOrdered ? P.n_levels : 0u;
+  const unsigned final_barrier = P.n_levels;
   bar.arrive(final_barrier);
   if (blockIdx.x == 0) {
     if (bar.wait(final_barrier)) return;
@@ -958,40 +747,18 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restric
   }
 }
 
-// Stream schedule: converts every level's input (and h) into limb planes in
-// the workspace, once per step, before the step kernel.  Workgroup b takes
-// levels b, b + grid, ...; the planes are those the step kernel copies.
-__global__ __launch_bounds__(kThreads) void convert_inputs_kernel(const Plan* __restrict__ plan,
-                                                                  const DevLevel* __restrict__ levels) {
-  const Plan& P = *plan;
-  for (unsigned li = blockIdx.x; li <= P.n_levels; li += gridDim.x) {
-    if (li < P.n_levels) {
-      const DevLevel& L = levels[li];
-      t2_convert_groups(L.x, L.cols, L.planes, reinterpret_cast<int*>(L.planes + L.nchunks * kT2ChunkDwords),
-                        static_cast<int>(threadIdx.x), static_cast<int>(blockDim.x));
-    } else {
-      i8_convert_groups(P.h, P.hidden, P.vocab_planes,
-                        reinterpret_cast<int*>(P.vocab_planes + (P.hidden >> 4) * kI8ChunkDwords),
-                        static_cast<int>(threadIdx.x), static_cast<int>(blockDim.x));
-    }
-  }
-}
-
 __global__ void xcc_calibrate(unsigned* out) {
   if (threadIdx.x == 0) out[blockIdx.x] = xcc_id();
 }
 
 // ----------------------------------------------------------------- host side
 struct Layout {
-  size_t plan = 0, state = 0, counters = 0, flags = 0, partials = 0, levels = 0, calib = 0, planes = 0, segs = 0,
-         seg_count = 0, total = 0;
+  size_t plan = 0, state = 0, counters = 0, flags = 0, partials = 0, levels = 0, calib = 0, total = 0;
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Workspace layout of a step (offsets from the 256-byte aligned plan).  The
-// stream schedule adds the pre-converted limb planes of every level's input
-// and of h (each block 256-byte aligned, in level order).
+// Workspace layout of a step (offsets from the 256-byte aligned plan).
 Layout layout_for(const pwg_step_desc* d) {
   const int n_levels = d->n_levels;
   Layout L;
@@ -1002,68 +769,8 @@ Layout layout_for(const pwg_step_desc* d) {
   L.partials = align_up(L.flags + kFlagsBytes, 256);
   L.levels = align_up(L.partials + kMaxGrid * 8, 256);
   L.calib = align_up(L.levels + static_cast<size_t>(n_levels) * sizeof(DevLevel), 256);
-  L.planes = align_up(L.calib + kMaxGrid * 4, 256);
-  size_t end = L.planes;
-  if (d->schedule == PWG_SCHEDULE_STREAM) {
-    for (int i = 0; i < n_levels; ++i) end += align_up(t2_plane_bytes(static_cast<int>(d->levels[i].cols)), 256);
-    end += align_up(i8_plane_bytes(static_cast<int>(d->hidden)), 256);
-    // segments: at most one per level (and the vocabulary) per workgroup
-    L.segs = align_up(end, 256);
-    L.seg_count = align_up(L.segs + static_cast<size_t>(kMaxGrid) * (n_levels + 1) * sizeof(Seg), 256);
-    end = L.seg_count + kMaxGrid * 4;
-  }
-  L.total = align_up(end, 256);
+  L.total = align_up(L.calib + kMaxGrid * 4, 256);
   return L;
-}
-
-// Relative cost of one 1 KiB slot of the output projection against one of a
-// ternary level (measured: the int8 rows stream at about twice the rate of
-// the ternary rows, whose vector work per byte is about three times larger).
-constexpr double kI8SlotCost = 0.45;
-
-// Stream schedule: splits the concatenation of every level's rows (then the
-// vocabulary rows) into `grid` contiguous ranges of equal cost and returns
-// each workgroup's segments (one per level it touches) in level order.
-void partition_stream(const pwg_step_desc* d, int grid, std::vector<std::vector<Seg>>& out) {
-  const int n = d->n_levels;
-  std::vector<long long> rows(n + 1);
-  std::vector<double> cost(n + 1), start(n + 2);
-  for (int i = 0; i < n; ++i) {
-    rows[i] = d->levels[i].rows;
-    cost[i] = static_cast<double>((d->levels[i].cols / 64 + 63) / 64);
-  }
-  rows[n] = d->vocab;
-  cost[n] = static_cast<double>((d->hidden / 16 + 63) / 64) * kI8SlotCost;
-  start[0] = 0.0;
-  for (int i = 0; i <= n; ++i) start[i + 1] = start[i] + static_cast<double>(rows[i]) * cost[i];
-  const double total = start[n + 1];
-  // position of cost offset x: (level, row), rounded to the nearest row
-  auto pos = [&](double x, int& lv, long long& r) {
-    lv = 0;
-    while (lv < n && x >= start[lv + 1]) ++lv;
-    r = static_cast<long long>(std::llround((x - start[lv]) / cost[lv]));
-    r = r < 0 ? 0 : (r > rows[lv] ? rows[lv] : r);
-  };
-  out.assign(grid, {});
-  int lv0 = 0;
-  long long r0 = 0;
-  for (int b = 0; b < grid; ++b) {
-    int lv1;
-    long long r1;
-    if (b + 1 == grid) {
-      lv1 = n;
-      r1 = rows[n];
-    } else {
-      pos(total * (b + 1) / grid, lv1, r1);
-    }
-    for (int lv = lv0; lv <= lv1; ++lv) {
-      const long long a = lv == lv0 ? r0 : 0;
-      const long long e = lv == lv1 ? r1 : rows[lv];
-      if (e > a) out[b].push_back(Seg{lv, static_cast<int>(a), static_cast<int>(e), 0});
-    }
-    lv0 = lv1;
-    r0 = r1;
-  }
 }
 
 struct GridInfo {
@@ -1079,7 +786,7 @@ int grid_for(const pwg_step_desc* d, GridInfo* gi) {
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   gi->lds = step_lds_bytes(d);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(&step_kernel<true>), kThreads, gi->lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(&step_kernel), kThreads, gi->lds);
   if (e != hipSuccess) return fail(PWG_ERR_HIP, "persistent step: device query failed: %s", hipGetErrorString(e));
   if (occ < 1) return fail(PWG_ERR_UNSUPPORTED, "persistent step: kernel does not fit on a CU");
   gi->grid = cus < static_cast<int>(kMaxGrid) ? cus : static_cast<int>(kMaxGrid);  // one workgroup per CU
@@ -1089,7 +796,7 @@ int grid_for(const pwg_step_desc* d, GridInfo* gi) {
 }  // namespace
 
 size_t step_persistent_workspace(const pwg_step_desc* d) {
-  if (!d || (d->schedule != PWG_SCHEDULE_PERSISTENT && d->schedule != PWG_SCHEDULE_STREAM) || d->n_levels < 0) return 0;
+  if (!d || d->schedule != PWG_SCHEDULE_PERSISTENT || d->n_levels < 0) return 0;
   return layout_for(d).total + 256;  // + 256 for aligning the plan
 }
 
@@ -1102,9 +809,8 @@ int step_persistent_plan(const pwg_step_desc* d, size_t ws_offset, void* stream)
   GridInfo gi0;
   const int rc0 = grid_for(d, &gi0);
   if (rc0 != PWG_OK) return rc0;
-  // the ordered schedule keeps a workgroup's row scales and outputs of a level in LDS
-  const bool ordered = d->schedule == PWG_SCHEDULE_PERSISTENT;
-  auto too_many = [&](int64_t rows) { return ordered && (rows + gi0.grid - 1) / gi0.grid > kMaxWgRows; };
+  // a workgroup keeps its row scales and outputs of a level in LDS
+  auto too_many = [&](int64_t rows) { return (rows + gi0.grid - 1) / gi0.grid > kMaxWgRows; };
   if (too_many(d->vocab))
     return fail(PWG_ERR_UNSUPPORTED, "pwg_step_plan: persistent schedules support up to %d vocabulary rows per CU",
                 kMaxWgRows);
@@ -1147,8 +853,7 @@ int step_persistent_plan(const pwg_step_desc* d, size_t ws_offset, void* stream)
 
   Plan h{};
   h.n_levels = static_cast<unsigned>(d->n_levels);
-  h.ordered = d->schedule == PWG_SCHEDULE_STREAM ? 0u : 1u;
-  h.n_barriers = h.ordered ? h.n_levels + 1 : 1u;  // unordered: only the final (argmax) barrier
+  h.n_barriers = h.n_levels + 1;
   h.mode = uniform && census[0] > 0 ? kBarrierL2 : kBarrierFlat;
   h.grid = static_cast<unsigned>(gi.grid);
   h.xcd_mask = 0;
@@ -1177,7 +882,6 @@ int step_persistent_plan(const pwg_step_desc* d, size_t ws_offset, void* stream)
   h.levels_off = lay.levels;
   h.calib_off = lay.calib;
   std::vector<DevLevel> lv(d->n_levels);
-  size_t plane_off = lay.planes;
   for (int i = 0; i < d->n_levels; ++i) {
     const pwg_level& L = d->levels[i];
     lv[i].w = static_cast<const u32x4*>(L.w_packed);
@@ -1188,41 +892,10 @@ int step_persistent_plan(const pwg_step_desc* d, size_t ws_offset, void* stream)
     lv[i].cols = static_cast<int>(L.cols);
     lv[i].nchunks = static_cast<int>(L.cols / 64);
     lv[i].c = static_cast<int>((L.cols / 64 + 63) / 64);
-    lv[i].planes = nullptr;
-    if (d->schedule == PWG_SCHEDULE_STREAM) {
-      lv[i].planes = reinterpret_cast<unsigned*>(dbase + plane_off);
-      plane_off += align_up(t2_plane_bytes(static_cast<int>(L.cols)), 256);
-    }
-  }
-  h.vocab_planes = d->schedule == PWG_SCHEDULE_STREAM ? reinterpret_cast<unsigned*>(dbase + plane_off) : nullptr;
-  std::vector<Seg> seg_flat;
-  std::vector<int> seg_count;
-  h.segs = nullptr;
-  h.seg_count = nullptr;
-  h.seg_stride = 0;
-  if (d->schedule == PWG_SCHEDULE_STREAM) {
-    std::vector<std::vector<Seg>> parts;
-    partition_stream(d, gi.grid, parts);
-    int stride = 1;
-    for (const auto& v : parts) stride = static_cast<int>(v.size()) > stride ? static_cast<int>(v.size()) : stride;
-    seg_flat.assign(static_cast<size_t>(gi.grid) * stride, Seg{0, 0, 0, 0});
-    seg_count.resize(gi.grid);
-    for (int b = 0; b < gi.grid; ++b) {
-      seg_count[b] = static_cast<int>(parts[b].size());
-      for (size_t j = 0; j < parts[b].size(); ++j) seg_flat[static_cast<size_t>(b) * stride + j] = parts[b][j];
-    }
-    h.segs = reinterpret_cast<const Seg*>(dbase + lay.segs);
-    h.seg_count = reinterpret_cast<const int*>(dbase + lay.seg_count);
-    h.seg_stride = stride;
   }
   e = hipMemcpyAsync(dplan, &h, sizeof(Plan), hipMemcpyHostToDevice, st);
   if (e == hipSuccess && d->n_levels > 0)
     e = hipMemcpyAsync(dbase + lay.levels, lv.data(), lv.size() * sizeof(DevLevel), hipMemcpyHostToDevice, st);
-  if (e == hipSuccess && !seg_flat.empty()) {
-    e = hipMemcpyAsync(dbase + lay.segs, seg_flat.data(), seg_flat.size() * sizeof(Seg), hipMemcpyHostToDevice, st);
-    if (e == hipSuccess)
-      e = hipMemcpyAsync(dbase + lay.seg_count, seg_count.data(), seg_count.size() * 4, hipMemcpyHostToDevice, st);
-  }
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return fail(PWG_ERR_HIP, "pwg_step_plan: %s", hipGetErrorString(e));
   return PWG_OK;
@@ -1241,12 +914,7 @@ int step_persistent_launch(const pwg_step_desc* d, size_t ws_offset, void* strea
   auto* flags = reinterpret_cast<unsigned*>(dbase + lay.flags);
   auto* partials = reinterpret_cast<unsigned long long*>(dbase + lay.partials);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (d->schedule == PWG_SCHEDULE_STREAM) {
-    hipLaunchKernelGGL(convert_inputs_kernel, dim3(gi.grid), dim3(kThreads), 0, st, dplan, lv);
-    hipLaunchKernelGGL(step_kernel<false>, dim3(gi.grid), dim3(kThreads), gi.lds, st, dplan, lv, state, counters, flags, partials);
-  } else {
-    hipLaunchKernelGGL(step_kernel<true>, dim3(gi.grid), dim3(kThreads), gi.lds, st, dplan, lv, state, counters, flags, partials);
-  }
+  hipLaunchKernelGGL(step_kernel, dim3(gi.grid), dim3(kThreads), gi.lds, st, dplan, lv, state, counters, flags, partials);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PWG_ERR_HIP, "persistent step launch: %s", hipGetErrorString(e));
   return PWG_OK;
