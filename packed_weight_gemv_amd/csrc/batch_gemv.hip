@@ -310,6 +310,15 @@ int launch_ternary_gemv_batch(const void* w, const float* s, int64_t rows, int64
   return PWG_OK;
 }
 
+int launch_argmax_reduce_batch(const unsigned long long* partials, int n, size_t nparts, int32_t batch, int32_t* token,
+                               void* stream) {
+  void* args[] = {const_cast<unsigned long long**>(&partials), &n, &nparts, &token};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&argmax_reduce_batch_kernel), dim3(batch), dim3(256),
+                                       args, 0, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PWG_ERR_HIP, "argmax_reduce (batch) launch: %s", hipGetErrorString(e));
+  return PWG_OK;
+}
+
 int launch_int8_gemv_argmax_batch(const int8_t* table, const float* s, int64_t rows, int64_t cols, const float* h,
                                   int32_t batch, void* ws, int32_t* token, float* logits, void* stream) {
   static BatchInstance c1 = {reinterpret_cast<const void*>(&i8_batch_kernel<1, 4, 4>), 4, 0, 0, 0};
@@ -329,11 +338,7 @@ int launch_int8_gemv_argmax_batch(const int8_t* table, const float* s, int64_t r
   void* args[] = {&tp, const_cast<float**>(&s), &r32, &c32, const_cast<float**>(&h), &b32, &logits, &np, &parts};
   hipError_t e = hipLaunchKernel(in.fn, dim3(grid), dim3(kBatchThreads), args, lds, st);
   if (e != hipSuccess) return fail(PWG_ERR_HIP, "int8_gemv_argmax (batch) launch: %s", hipGetErrorString(e));
-  int n = static_cast<int>(grid);
-  void* args2[] = {&parts, &n, &np, &token};
-  e = hipLaunchKernel(reinterpret_cast<const void*>(&argmax_reduce_batch_kernel), dim3(batch), dim3(256), args2, 0, st);
-  if (e != hipSuccess) return fail(PWG_ERR_HIP, "argmax_reduce (batch) launch: %s", hipGetErrorString(e));
-  return PWG_OK;
+  return launch_argmax_reduce_batch(parts, static_cast<int>(grid), np, batch, token, stream);
 }
 
 }  // namespace pwg

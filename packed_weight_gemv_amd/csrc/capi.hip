@@ -45,7 +45,11 @@ int validate_int8(const int8_t* t, const float* s, int64_t rows, int64_t cols, c
   return PWG_OK;
 }
 
-size_t argmax_ws(int64_t rows, int32_t batch) { return int8_partials(rows) * sizeof(unsigned long long) * batch; }
+// Partial (max, index) keys of every vector; for batch > 1 also the operand
+// area of the matrix-core kernel (sized for the widest table).
+size_t argmax_ws(int64_t rows, int32_t batch) {
+  return int8_partials(rows) * sizeof(unsigned long long) * batch + i8b_operand_bytes(batch);
+}
 
 }  // namespace
 

@@ -232,6 +232,12 @@ size_t int8_partials(int64_t rows) {
 
 int launch_int8_gemv_argmax(const int8_t* table, const float* s, int64_t rows, int64_t cols, const float* h,
                             int32_t batch, void* ws, int32_t* token, float* logits, void* stream) {
+  if (batch > 1 && i8b_supported(cols, batch)) {
+    const size_t nparts = int8_partials(rows);
+    auto* parts = static_cast<unsigned long long*>(ws);
+    return launch_i8b(table, s, rows, cols, h, batch, parts, nparts,
+                      static_cast<unsigned char*>(ws) + nparts * sizeof(unsigned long long) * batch, logits, token, stream);
+  }
   if (batch > 1) return launch_int8_gemv_argmax_batch(table, s, rows, cols, h, batch, ws, token, logits, stream);
   I8Instance* in = pick_i8(static_cast<int>(cols));
   const size_t lds = i8_lds_bytes(cols);

@@ -38,6 +38,16 @@ int launch_ternary_gemv_batch(const void* w, const float* s, int64_t rows, int64
 int launch_int8_gemv_argmax_batch(const int8_t* table, const float* s, int64_t rows, int64_t cols,
                                   const float* h, int32_t batch, void* ws, int32_t* token,
                                   float* logits, void* stream);
+int launch_argmax_reduce_batch(const unsigned long long* partials, int n, size_t nparts, int32_t batch, int32_t* token,
+                               void* stream);
+// Matrix-core variant of the batched int8 projection (batch_mfma.hip): for
+// batch 4, 8, 16 and cols a multiple of 1,024 up to kMaxInt8Cols.  Its
+// operands live in the workspace after the partial keys.
+bool i8b_supported(int64_t cols, int32_t batch);
+size_t i8b_operand_bytes(int32_t batch);
+int launch_i8b(const int8_t* table, const float* s, int64_t rows, int64_t cols, const float* h, int32_t batch,
+               unsigned long long* partials, size_t nparts, unsigned char* ops_area, float* logits, int32_t* token,
+               void* stream);
 size_t t2_lds_bytes(int64_t cols);
 size_t i8_lds_bytes(int64_t cols);
 int launch_embed_gather(const int8_t* table, const float* s, int64_t rows, int64_t cols,

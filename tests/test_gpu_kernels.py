@@ -203,7 +203,9 @@ def test_argmax_batch():
         assert_gemv(lg[b], lr[b], ref.int8_logits_magnitude(tab.q, tab.scale, hb[b]), f"batch {b}")
 
 
-I8_BATCH_SHAPES = [(999, 1024, 8), (5000, 4096, 16), (257, 2048, 4), (3, 8192, 4), (70001, 4096, 8)]
+# cols a multiple of 1,024: matrix-core kernel; (777, 768, 4): the VALU kernel
+I8_BATCH_SHAPES = [(999, 1024, 8), (5000, 4096, 16), (257, 2048, 4), (3, 8192, 4), (70001, 4096, 8),
+                   (1000, 1024, 16), (777, 768, 4)]
 
 
 @pytest.mark.parametrize("shape", I8_BATCH_SHAPES, ids=[f"{r}x{c}xB{b}" for r, c, b in I8_BATCH_SHAPES])
@@ -216,6 +218,26 @@ def test_argmax_batch_shapes(shape):
     for b in range(batch):
         assert token_ok(tok[b], lr[b]), f"{shape} vector {b}"
         assert_gemv(lg[b], lr[b], ref.int8_logits_magnitude(tab.q, tab.scale, hb[b]), f"{shape} vector {b}")
+
+
+def test_argmax_batch_vector_ranges():
+    """Vectors of very different magnitudes in one batch (each section of
+    each vector takes its own exponent) and a zero vector."""
+    rows, cols, batch = 5000, 4096, 8
+    tab = synth.int8_table((106, 0), rows, cols)
+    hb = synth.batch_inputs(batch, cols, 13).astype(np.float64)
+    for b in range(batch):
+        hb[b] *= 2.0 ** (12 * (b - 4))
+    hb[5] = 0.0
+    hb = hb.astype(np.float32)
+    tok, lg = run_argmax(tab.q, tab.scale, hb)
+    lr = ref.int8_logits(tab.q, tab.scale, hb)
+    for b in range(batch):
+        if b == 5:
+            assert not lg[b].any() and tok[b] == 0
+            continue
+        assert token_ok(tok[b], lr[b]), f"vector {b}"
+        assert_gemv(lg[b], lr[b], ref.int8_logits_magnitude(tab.q, tab.scale, hb[b]), f"vector {b}")
 
 
 def test_argmax_batch_ties_per_column():
