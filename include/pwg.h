@@ -162,7 +162,10 @@ size_t pwg_tiled_size(int64_t rows, int64_t row_bytes);
 int pwg_tile_rows(const void* src, int64_t rows, int64_t row_bytes,
                   void* dst, size_t dst_bytes, void* stream);
 
-/* Workspace bytes needed by pwg_int8_gemv_argmax for (rows, batch). */
+/* Workspace bytes needed by pwg_int8_gemv_argmax for (rows, batch): the
+ * partial (max, index) keys of every vector and, for batch 4, 8 and 16, the
+ * matrix-core kernel's operand area (the digits of h for a table of up to
+ * 8,192 columns, 4 bytes per value and vector: 512 KiB at batch 16). */
 size_t pwg_argmax_workspace_bytes(int64_t rows, int32_t batch);
 
 /* int8 output projection fused with greedy argmax (page sections "A 104
@@ -177,8 +180,13 @@ size_t pwg_argmax_workspace_bytes(int64_t rows, int32_t batch);
  *                (contents on entry are ignored)
  *   token_out    device, int32[batch]
  *   logits_out   device float32[batch][rows] or NULL (written only if given)
- * Two kernels: a fused GEMV + per-block (max, index), then one block that
- * reduces the pairs.  Deterministic bit for bit.
+ * batch 1: a fused GEMV + per-block (max, index), then one block that
+ * reduces the pairs.  batch 4, 8, 16 with cols a multiple of 1,024: h is
+ * converted into matrix-core operands in the workspace, one kernel computes
+ * every vector's logits on v_mfma_i32_16x16x64_i8 (exact int32 sums per
+ * 256-value section) with the table read once, and one block per vector
+ * reduces its keys; other widths use a VALU kernel.  Deterministic bit for
+ * bit on every path.
  * Errors: PWG_ERR_ARG, PWG_ERR_ALIGN, PWG_ERR_SIZE, PWG_ERR_HIP. */
 int pwg_int8_gemv_argmax(const int8_t* table, const float* row_scale,
                          int64_t rows, int64_t cols,

@@ -120,7 +120,11 @@ def test_ternary_gemv_argument_errors():
 def test_int8_argmax_argument_errors():
     f = pwg._i8argmax
     ws = pwg.argmax_workspace_bytes(1000, 1)
-    assert ws >= 8 and pwg.argmax_workspace_bytes(1000, 4) == 4 * ws
+    # batch > 1: every vector's partial keys plus the operand area of the
+    # matrix-core kernel, sized for the widest table (8,192 columns, one
+    # byte per value and B-operand column, four columns per vector)
+    assert ws >= 8 and pwg.argmax_workspace_bytes(1000, 4) >= 4 * ws + 4 * 8192 * 4
+    assert pwg.argmax_workspace_bytes(1000, 16) >= 16 * ws + 16 * 8192 * 4
     assert pwg.argmax_workspace_bytes(0, 1) == 0 and pwg.argmax_workspace_bytes(10, 3) == 0
     assert f(A, A, 1000, 4096, A, 1, A, ws - 8, A, None, None) == ERR_SIZE
     assert f(A, A, 1000, 4096, A, 1, None, ws, A, None, None) == ERR_ARG
