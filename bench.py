@@ -180,15 +180,19 @@ def cpu_baseline(target_s: float, step_bytes: int):
 def small_batch(wl, stream, reps=50):
     """One 8B-shape layer's four levels and the int8 output projection with
     argmax, applied to B activation vectors per pass (weights stream once per
-    pass whatever B is); one HIP graph per B.  Reports weight bytes per
-    second and effective integer operations per second (2 per weight per
-    vector)."""
+    pass whatever B is); one HIP graph per B.  B = 1: the per-call VALU
+    kernels on row-major weights; B = 4, 8, 16: the batched matrix-core
+    kernels on the tiled arrangement (the one the stream step reads).
+    Reports weight bytes per second and effective integer operations per
+    second (2 per weight per vector)."""
     import torch
 
     import packed_weight_gemv_amd as pwg
     import synth
     rows_w, table = wl.weights[pwg.LAYOUT_ROWS]   # the per-call kernels take row-major weights
     levels = [(w, sc, r, k) for w, (_, sc, _, _, r, k) in zip(rows_w[:4], wl.desc.levels[:4])]
+    tiled = wl.weights.get(pwg.LAYOUT_TILED)
+    tlevels = [(w, sc, r, k) for w, (_, sc, _, _, r, k) in zip(tiled[0][:4], wl.desc.levels[:4])] if tiled else None
     tscale = wl.desc.out_scale
     vocab, hidden = table.shape
     t2_weights = sum(r * k for _, _, r, k in levels)
@@ -200,8 +204,17 @@ def small_batch(wl, stream, reps=50):
         h = torch.from_numpy(synth.batch_inputs(batch, hidden, 30)).to("cuda:0")
         ws = torch.zeros(pwg.argmax_workspace_bytes(vocab, batch), dtype=torch.uint8, device="cuda:0")
         tok = torch.empty(batch, dtype=torch.int32, device="cuda:0")
+        mfma = batch > 1 and tlevels is not None
+        tws = [torch.zeros(max(1, pwg.batch_workspace_bytes(k, batch)), dtype=torch.uint8, device="cuda:0")
+               for _, _, _, k in levels] if mfma else None
 
         def one():
+            if mfma:
+                for (w, sc, r, k), x, y, wsl in zip(tlevels, xs, ys, tws):
+                    pwg.ternary_gemv_tiled(w, sc, r, k, x, y=y, workspace=wsl, stream=stream)
+                pwg.int8_gemv_argmax_tiled(tiled[1], tscale, vocab, hidden, h, workspace=ws, token_out=tok,
+                                           stream=stream)
+                return
             for (w, sc, r, k), x, y in zip(levels, xs, ys):
                 pwg.ternary_gemv(w, sc, r, k, x if batch > 1 else x[0], y=y if batch > 1 else y[0], stream=stream)
             pwg.int8_gemv_argmax(table, tscale, h if batch > 1 else h[0], workspace=ws, token_out=tok, stream=stream)
@@ -209,7 +222,8 @@ def small_batch(wl, stream, reps=50):
         ms = time_graph(g, stream, reps, 5)
         us = ms * 1e3
         ops = 2.0 * (t2_weights + vocab * hidden) * batch
-        out.append({"batch": batch, "us_per_pass": us, "weight_GBps": bytes_ / us / 1e3,
+        out.append({"batch": batch, "kernels": "matrix cores, tiled weights" if mfma else "VALU, row-major weights",
+                    "us_per_pass": us, "weight_GBps": bytes_ / us / 1e3,
                     "pct_of_hbm_peak": 100.0 * bytes_ / (us * 1e-6) / PEAK_HBM_BPS,
                     "effective_Tops": ops / us / 1e6})
         log(f"small batch B={batch}: {us:.1f} us per pass, {bytes_ / us / 1e3:.0f} GB/s, {ops / us / 1e6:.1f} Top/s")

@@ -45,7 +45,7 @@ extern "C" {
 #endif
 #pragma GCC visibility push(default)
 
-#define PWG_VERSION 2
+#define PWG_VERSION 3
 #define PWG_MAX_COLS 16384
 
 enum {
@@ -161,6 +161,50 @@ size_t pwg_tiled_size(int64_t rows, int64_t row_bytes);
  * Errors: PWG_ERR_ARG (null, bad shape), PWG_ERR_ALIGN, PWG_ERR_SIZE, PWG_ERR_HIP. */
 int pwg_tile_rows(const void* src, int64_t rows, int64_t row_bytes,
                   void* dst, size_t dst_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Small batch on the tiled arrangement (page section "The 0.6B model does not
+ * get to decide": several drafted tokens are scored in one batched pass, so
+ * each weight is read once for all of them).  Both calls take the weights as
+ * pwg_tile_rows arranges them (the arrangement the stream step reads), run on
+ * the int8 matrix cores (v_mfma_i32_16x16x64_i8) and form every row sum
+ * exactly in int32 per 256-value section over a fixed-point rounding of the
+ * activations (three balanced base-256 digits of rint(x * 2^(22 - e)), e the
+ * section's exponent); float32 after that.  Asynchronous on `stream`,
+ * capturable, allocate nothing. */
+
+/* Workspace bytes of pwg_ternary_gemv_tiled for (cols, batch): the converted
+ * activations (4 bytes per value and vector) and a few KiB; 0 for an
+ * unsupported shape (cols not a multiple of 2048 in [2048, PWG_MAX_COLS],
+ * batch not 4, 8 or 16). */
+size_t pwg_batch_workspace_bytes(int64_t cols, int32_t batch);
+
+/* Batched ternary GEMV on tiled T2 weights:
+ *     y[b, r] = row_scale[r] * sum_k W[r, k] * x[b, k]
+ *   w_tiled      device, pwg_tiled_size(rows, cols / 4) bytes (pwg_tile_rows
+ *                of the T2 blob)
+ *   row_scale    device, float32[rows]
+ *   x            device, float32[batch][cols]
+ *   y            device, float32[batch][rows] (written)
+ *   workspace    device, >= pwg_batch_workspace_bytes(cols, batch); scratch
+ * batch 4, 8 or 16; cols a multiple of 2048.  The 2-bit codes are expanded
+ * to int8 in registers.
+ * Errors: PWG_ERR_ARG (null, shape, batch), PWG_ERR_ALIGN (pointers are
+ * 16-byte aligned), PWG_ERR_SIZE, PWG_ERR_UNSUPPORTED (cols), PWG_ERR_HIP. */
+int pwg_ternary_gemv_tiled(const void* w_tiled, const float* row_scale, int64_t rows, int64_t cols,
+                           const float* x, int32_t batch, float* y, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Batched int8 projection + per-vector greedy argmax on a tiled table
+ * (pwg_tile_rows of the rows x cols int8 table): the same results as
+ * pwg_int8_gemv_argmax (bit for bit: the same digits and sums), with the
+ * table streamed as contiguous 1 KiB tiles.  batch 4, 8 or 16; cols a
+ * multiple of 1024, at most 8192; workspace >= pwg_argmax_workspace_bytes(rows,
+ * batch).  Errors as pwg_int8_gemv_argmax, plus PWG_ERR_UNSUPPORTED (cols). */
+int pwg_int8_gemv_argmax_tiled(const int8_t* table_tiled, const float* row_scale, int64_t rows,
+                               int64_t cols, const float* h, int32_t batch, void* workspace,
+                               size_t workspace_bytes, int32_t* token_out, float* logits_out,
+                               void* stream);
 
 /* Workspace bytes needed by pwg_int8_gemv_argmax for (rows, batch): the
  * partial (max, index) keys of every vector and, for batch 4, 8 and 16, the

@@ -92,6 +92,9 @@ _tgemv = _sig("pwg_ternary_gemv", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp,
 _argmax_ws = _sig("pwg_argmax_workspace_bytes", _sz, _i64, _i32)
 _i8argmax = _sig("pwg_int8_gemv_argmax", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _sz, _vp, _vp, _vp)
 _gather = _sig("pwg_embed_gather", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _vp)
+_batch_ws = _sig("pwg_batch_workspace_bytes", _sz, _i64, _i32)
+_tgemv_tiled = _sig("pwg_ternary_gemv_tiled", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp, _sz, _vp)
+_i8argmax_tiled = _sig("pwg_int8_gemv_argmax_tiled", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _sz, _vp, _vp, _vp)
 _tiled_size = _sig("pwg_tiled_size", _sz, _i64, _i64)
 _tile_rows = _sig("pwg_tile_rows", C.c_int, _vp, _i64, _i64, _vp, _sz, _vp)
 _step_ws = _sig("pwg_step_workspace_bytes", _sz, C.POINTER(_StepDesc))
@@ -103,7 +106,8 @@ _version = _sig("pwg_version", C.c_int)
 
 EXPORTED = ["pwg_packed_size", "pwg_pack_weights", "pwg_unpack_weights", "pwg_ternary_gemv",
             "pwg_argmax_workspace_bytes", "pwg_int8_gemv_argmax", "pwg_embed_gather",
-            "pwg_tiled_size", "pwg_tile_rows",
+            "pwg_tiled_size", "pwg_tile_rows", "pwg_batch_workspace_bytes", "pwg_ternary_gemv_tiled",
+            "pwg_int8_gemv_argmax_tiled",
             "pwg_step_workspace_bytes", "pwg_step_plan", "pwg_decode_step_weights",
             "pwg_step_status", "pwg_last_error", "pwg_version"]
 
@@ -212,6 +216,40 @@ def embed_gather(table, row_scale, ids, rows_out=None, scales_out=None, deq_out=
 
 
 # ---------------------------------------------------------------- tiled arrangement
+def batch_workspace_bytes(cols: int, batch: int) -> int:
+    return _batch_ws(cols, batch)
+
+
+def ternary_gemv_tiled(w_tiled, row_scale, rows: int, cols: int, x, y=None, workspace=None, stream=None):
+    """y = row_scale * (W @ x.T).T for x of shape (batch, cols), batch 4, 8 or
+    16, W in the tiled arrangement (tile_rows of the T2 blob)."""
+    import torch
+    batch = x.shape[0]
+    if y is None:
+        y = torch.empty((batch, rows), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, _batch_ws(cols, batch)), dtype=torch.uint8, device=x.device)
+    _check(_tgemv_tiled(_ptr(w_tiled), _ptr(row_scale), rows, cols, _ptr(x), batch, _ptr(y), _ptr(workspace),
+                        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return y
+
+
+def int8_gemv_argmax_tiled(table_tiled, row_scale, rows: int, cols: int, h, workspace=None, token_out=None,
+                           logits_out=None, stream=None):
+    """Greedy tokens of logits = row_scale * (Q @ h.T) for h (batch, cols),
+    batch 4, 8 or 16, Q in the tiled arrangement (tile_rows of the table)."""
+    import torch
+    batch = h.shape[0]
+    if workspace is None:
+        workspace = torch.empty(max(1, _argmax_ws(rows, batch)), dtype=torch.uint8, device=h.device)
+    if token_out is None:
+        token_out = torch.empty(batch, dtype=torch.int32, device=h.device)
+    _check(_i8argmax_tiled(_ptr(table_tiled), _ptr(row_scale), rows, cols, _ptr(h), batch, _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _ptr(token_out), _ptr(logits_out),
+                           _stream(stream)))
+    return token_out
+
+
 def tiled_size(rows: int, row_bytes: int) -> int:
     return _tiled_size(rows, row_bytes)
 

@@ -79,6 +79,51 @@ extern "C" int pwg_int8_gemv_argmax(const int8_t* table, const float* row_scale,
   return launch_int8_gemv_argmax(table, row_scale, rows, cols, h, batch, workspace, token_out, logits_out, stream);
 }
 
+extern "C" size_t pwg_batch_workspace_bytes(int64_t cols, int32_t batch) {
+  if (cols < 2048 || cols % 2048 != 0 || cols > PWG_MAX_COLS || !(batch == 4 || batch == 8 || batch == 16)) return 0;
+  return batch_operand_bytes(cols, batch);
+}
+
+extern "C" int pwg_ternary_gemv_tiled(const void* w_tiled, const float* row_scale, int64_t rows, int64_t cols,
+                                      const float* x, int32_t batch, float* y, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  const char* fn = "pwg_ternary_gemv_tiled";
+  TRY(check_shape(rows, cols, fn));
+  if (rows >= (int64_t{1} << 30)) return fail(PWG_ERR_ARG, "%s: too many rows", fn);
+  if (!(batch == 4 || batch == 8 || batch == 16)) return fail(PWG_ERR_ARG, "%s: batch must be 4, 8 or 16 (got %d)", fn, batch);
+  if (cols % 2048 != 0)
+    return fail(PWG_ERR_UNSUPPORTED, "%s: cols must be a multiple of 2048 (got %lld)", fn, static_cast<long long>(cols));
+  TRY(check_ptr(w_tiled, fn, "w_tiled"));
+  TRY(check_ptr(row_scale, fn, "row_scale"));
+  TRY(check_ptr(x, fn, "x"));
+  TRY(check_ptr(y, fn, "y"));
+  TRY(check_ptr(workspace, fn, "workspace"));
+  const size_t need = pwg_batch_workspace_bytes(cols, batch);
+  if (workspace_bytes < need) return fail(PWG_ERR_SIZE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, need);
+  return launch_t2b(w_tiled, row_scale, rows, cols, x, batch, y, workspace, stream);
+}
+
+extern "C" int pwg_int8_gemv_argmax_tiled(const int8_t* table_tiled, const float* row_scale, int64_t rows,
+                                          int64_t cols, const float* h, int32_t batch, void* workspace,
+                                          size_t workspace_bytes, int32_t* token_out, float* logits_out,
+                                          void* stream) {
+  const char* fn = "pwg_int8_gemv_argmax_tiled";
+  TRY(validate_int8(table_tiled, row_scale, rows, cols, fn));
+  if (!(batch == 4 || batch == 8 || batch == 16)) return fail(PWG_ERR_ARG, "%s: batch must be 4, 8 or 16 (got %d)", fn, batch);
+  if (!i8b_supported(cols, batch))
+    return fail(PWG_ERR_UNSUPPORTED, "%s: cols must be a multiple of 1024 (got %lld)", fn, static_cast<long long>(cols));
+  TRY(check_ptr(h, fn, "h"));
+  TRY(check_ptr(workspace, fn, "workspace"));
+  TRY(check_ptr(token_out, fn, "token_out"));
+  if (logits_out && !aligned16(logits_out)) return fail(PWG_ERR_ALIGN, "%s: logits_out is not 16-byte aligned", fn);
+  if (workspace_bytes < argmax_ws(rows, batch))
+    return fail(PWG_ERR_SIZE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, argmax_ws(rows, batch));
+  const size_t nparts = int8_partials(rows);
+  return launch_i8b(table_tiled, true, row_scale, rows, cols, h, batch, static_cast<unsigned long long*>(workspace),
+                    nparts, static_cast<unsigned char*>(workspace) + nparts * sizeof(unsigned long long) * batch,
+                    logits_out, token_out, stream);
+}
+
 extern "C" int pwg_embed_gather(const int8_t* table, const float* row_scale, int64_t rows, int64_t cols,
                                 const int32_t* ids, int32_t n, int8_t* rows_out, float* scales_out, float* deq_out,
                                 void* stream) {

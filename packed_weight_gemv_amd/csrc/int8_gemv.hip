@@ -235,7 +235,7 @@ int launch_int8_gemv_argmax(const int8_t* table, const float* s, int64_t rows, i
   if (batch > 1 && i8b_supported(cols, batch)) {
     const size_t nparts = int8_partials(rows);
     auto* parts = static_cast<unsigned long long*>(ws);
-    return launch_i8b(table, s, rows, cols, h, batch, parts, nparts,
+    return launch_i8b(table, false, s, rows, cols, h, batch, parts, nparts,
                       static_cast<unsigned char*>(ws) + nparts * sizeof(unsigned long long) * batch, logits, token, stream);
   }
   if (batch > 1) return launch_int8_gemv_argmax_batch(table, s, rows, cols, h, batch, ws, token, logits, stream);

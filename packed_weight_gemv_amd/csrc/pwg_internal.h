@@ -45,9 +45,14 @@ int launch_argmax_reduce_batch(const unsigned long long* partials, int n, size_t
 // operands live in the workspace after the partial keys.
 bool i8b_supported(int64_t cols, int32_t batch);
 size_t i8b_operand_bytes(int32_t batch);
-int launch_i8b(const int8_t* table, const float* s, int64_t rows, int64_t cols, const float* h, int32_t batch,
-               unsigned long long* partials, size_t nparts, unsigned char* ops_area, float* logits, int32_t* token,
-               void* stream);
+// Operand area of a batched matrix-core call for up to `cap` values per vector.
+size_t batch_operand_bytes(int64_t cap, int32_t batch);
+// Batched ternary GEMV on tiled T2 weights (batch 4, 8, 16; cols % 2048 == 0).
+int launch_t2b(const void* w_tiled, const float* s, int64_t rows, int64_t cols, const float* x, int32_t batch, float* y,
+               void* ops_area, void* stream);
+int launch_i8b(const int8_t* table, bool tiled, const float* s, int64_t rows, int64_t cols, const float* h,
+               int32_t batch, unsigned long long* partials, size_t nparts, unsigned char* ops_area, float* logits,
+               int32_t* token, void* stream);
 size_t t2_lds_bytes(int64_t cols);
 size_t i8_lds_bytes(int64_t cols);
 int launch_embed_gather(const int8_t* table, const float* s, int64_t rows, int64_t cols,

@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_error_string():
-    assert pwg.version() == 2
+    assert pwg.version() == 3
     assert isinstance(pwg.last_error(), str)
 
 
@@ -115,6 +115,29 @@ def test_ternary_gemv_argument_errors():
     assert f(A, A, 8, 64, MIS, 1, A, None) == ERR_ALIGN
     assert f(A, A, 8, 64, A, 1, None, None) == ERR_ARG
     assert f(A, A, 8, 64, A, 2, A, None) == ERR_ARG and "batch" in pwg.last_error()
+
+
+def test_batch_tiled_argument_errors():
+    """The batched matrix-core entry points validate before launching."""
+    bw = pwg.batch_workspace_bytes
+    assert bw(4096, 16) >= 16 * 4096 * 4 and bw(4096, 4) >= 4 * 4096 * 4
+    assert bw(4096, 1) == 0 and bw(4096, 2) == 0 and bw(1024, 4) == 0 and bw(3072, 4) == 0 and bw(32768, 4) == 0
+    f = pwg._tgemv_tiled
+    ws = bw(4096, 8)
+    assert f(None, A, 64, 4096, A, 8, A, A, ws, None) == ERR_ARG
+    assert f(A, A, 64, 4096, A, 8, A, None, ws, None) == ERR_ARG
+    assert f(MIS, A, 64, 4096, A, 8, A, A, ws, None) == ERR_ALIGN
+    assert f(A, A, 64, 4096, A, 8, A, A, ws - 1, None) == ERR_SIZE
+    assert f(A, A, 64, 4096, A, 2, A, A, ws, None) == ERR_ARG and "batch" in pwg.last_error()
+    assert f(A, A, 64, 1024, A, 8, A, A, ws, None) == ERR_UNSUPPORTED
+    assert f(A, A, 0, 4096, A, 8, A, A, ws, None) == ERR_ARG
+    g = pwg._i8argmax_tiled
+    iw = pwg.argmax_workspace_bytes(1000, 4)
+    assert g(A, A, 1000, 4096, A, 1, A, iw, A, None, None) == ERR_ARG
+    assert g(A, A, 1000, 768, A, 4, A, iw, A, None, None) == ERR_UNSUPPORTED
+    assert g(A, A, 1000, 4096, A, 4, A, iw - 8, A, None, None) == ERR_SIZE
+    assert g(A, A, 1000, 4096, A, 4, A, iw, None, None, None) == ERR_ARG
+    assert g(A, A, 1000, 4096, A, 4, A, iw, A, MIS, None) == ERR_ALIGN
 
 
 def test_int8_argmax_argument_errors():

@@ -299,3 +299,72 @@ def test_tile_rows_full_vocabulary_table_sampled():
         want = pf.tile16x64(block)
         got = out[rb * 16 * cols: (rb + 1) * 16 * cols].cpu().numpy()
         assert got.size == tiles_per_block * 1024 and np.array_equal(got, want), f"row block {rb}"
+
+
+# ------------------------------------------------------------------ batched passes on tiled weights
+def tiled_t2(w):
+    rows, cols = w.shape
+    return pwg.tile_rows(packed_on_gpu(w), rows, cols // 4)
+
+
+TILED_BATCH_SHAPES = [(6144, 4096, 4), (1000, 4096, 16), (4096, 12288, 8), (100, 2048, 16), (24576, 4096, 16),
+                      (17, 16384, 4)]
+
+
+@pytest.mark.parametrize("shape", TILED_BATCH_SHAPES, ids=[f"{r}x{c}xB{b}" for r, c, b in TILED_BATCH_SHAPES])
+def test_ternary_batch_tiled(shape):
+    """Matrix-core batched ternary GEMV: the 8B level shapes, ragged row
+    tails, fewer row blocks than CUs, the widest rows."""
+    rows, cols, batch = shape
+    m = synth.ternary_matrix((107, rows, cols), rows, cols)
+    xb = synth.batch_inputs(batch, cols, 14)
+    y = pwg.ternary_gemv_tiled(tiled_t2(m.w), dev(m.scale), rows, cols, dev(xb))
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    yr = ref.ternary_gemv(m.w, m.scale, xb)
+    for b in range(batch):
+        assert_gemv(y[b], yr[b], ref.ternary_gemv_magnitude(m.w, m.scale, xb[b]), f"{shape} vector {b}")
+
+
+def test_ternary_batch_tiled_vector_ranges():
+    """Vectors of very different magnitudes, a zero vector and a one-hot
+    vector (y = s * W[:, k] exactly) in one batch."""
+    rows, cols, batch = 2000, 4096, 8
+    m = synth.ternary_matrix((108, 0), rows, cols)
+    xb = synth.batch_inputs(batch, cols, 15).astype(np.float64)
+    for b in range(batch):
+        xb[b] *= 2.0 ** (12 * (b - 4))
+    xb[5] = 0.0
+    xb[6] = 0.0
+    xb[6, 777] = 1.0
+    xb = xb.astype(np.float32)
+    y = pwg.ternary_gemv_tiled(tiled_t2(m.w), dev(m.scale), rows, cols, dev(xb)).cpu().numpy()
+    yr = ref.ternary_gemv(m.w, m.scale, xb)
+    assert not y[5].any()
+    assert np.array_equal(y[6], (m.scale * m.w[:, 777]).astype(np.float32))
+    for b in (0, 1, 2, 3, 4, 7):
+        assert_gemv(y[b], yr[b], ref.ternary_gemv_magnitude(m.w, m.scale, xb[b]), f"vector {b}")
+
+
+TILED_I8_SHAPES = [(5000, 4096, 16), (999, 1024, 8), (70001, 4096, 4), (3, 8192, 16)]
+
+
+@pytest.mark.parametrize("shape", TILED_I8_SHAPES, ids=[f"{r}x{c}xB{b}" for r, c, b in TILED_I8_SHAPES])
+def test_argmax_batch_tiled(shape):
+    """The tiled table gives the same tokens and logits, bit for bit, as the
+    row-major table (same digits, same exact sums), and matches the oracle."""
+    rows, cols, batch = shape
+    tab = synth.int8_table((109, rows, cols), rows, cols)
+    hb = synth.batch_inputs(batch, cols, 16)
+    qt = pwg.tile_rows(dev(tab.q.view(np.uint8)), rows, cols)
+    lo_t = torch.empty((batch, rows), dtype=torch.float32, device=DEV)
+    tok_t = pwg.int8_gemv_argmax_tiled(qt, dev(tab.scale), rows, cols, dev(hb), logits_out=lo_t)
+    tok_r, lg_r = run_argmax(tab.q, tab.scale, hb)
+    torch.cuda.synchronize()
+    tok_t, lg_t = tok_t.cpu().numpy(), lo_t.cpu().numpy()
+    assert np.array_equal(tok_t, tok_r)
+    assert np.array_equal(lg_t.view(np.uint32), lg_r.view(np.uint32))
+    lr = ref.int8_logits(tab.q, tab.scale, hb)
+    for b in range(batch):
+        assert token_ok(tok_t[b], lr[b]), f"{shape} vector {b}"
+        assert_gemv(lg_t[b], lr[b], ref.int8_logits_magnitude(tab.q, tab.scale, hb[b]), f"{shape} vector {b}")
