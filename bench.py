@@ -177,61 +177,118 @@ def cpu_baseline(target_s: float, step_bytes: int):
     }
 
 
-def small_batch(wl, stream, reps=50):
-    """One 8B-shape layer's four levels and the int8 output projection with
-    argmax, applied to B activation vectors per pass (weights stream once per
-    pass whatever B is); one HIP graph per B.  B = 1: the per-call VALU
-    kernels on row-major weights; B = 4, 8, 16: the batched matrix-core
-    kernels on the tiled arrangement (the one the stream step reads).
-    Reports weight bytes per second and effective integer operations per
-    second (2 per weight per vector)."""
+def pass_desc(wl, n_layers, batch, seed):
+    """A pass over the first n_layers layers' levels and the output table on
+    the tiled weights: the stream schedule for one vector, the batched pass
+    for 4, 8, 16; seeded inputs of shape (batch, cols) per level."""
     import torch
 
     import packed_weight_gemv_amd as pwg
     import synth
-    rows_w, table = wl.weights[pwg.LAYOUT_ROWS]   # the per-call kernels take row-major weights
+    tw, tq = wl.weights[pwg.LAYOUT_TILED]
+    vocab, hidden = wl.out_table.q.shape
+    dev = "cuda:0"
+    n = 4 * n_layers
+    levels = []
+    for i, (w, (_, sc, _, _, r, k)) in enumerate(zip(tw[:n], wl.desc.levels[:n])):
+        x = torch.from_numpy(synth.batch_inputs(batch, k, seed + i)).to(dev)
+        y = torch.empty((batch, r), dtype=torch.float32, device=dev)
+        levels.append((w, sc, x[0] if batch == 1 else x, y[0] if batch == 1 else y, r, k))
+    h = torch.from_numpy(synth.batch_inputs(batch, hidden, seed + 9999)).to(dev)
+    ids = torch.from_numpy(synth.rng_for(seed, 7).integers(0, vocab, batch).astype("int32")).to(dev)
+    d = pwg.StepDesc(levels=levels, out_table=tq, out_scale=wl.desc.out_scale, h=h[0] if batch == 1 else h,
+                     emb_table=wl.desc.emb_table, emb_scale=wl.desc.emb_scale, token_in=ids,
+                     token_out=torch.empty(batch, dtype=torch.int32, device=dev),
+                     emb_row_out=torch.empty((batch, hidden), dtype=torch.int8, device=dev),
+                     emb_scale_out=torch.empty(batch, dtype=torch.float32, device=dev),
+                     schedule=pwg.SCHEDULE_STREAM, weight_layout=pwg.LAYOUT_TILED, vocab=vocab, hidden=hidden,
+                     batch=batch)
+    d.workspace = torch.zeros(pwg.step_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    d._c = None
+    pwg.step_plan(d)
+    return d
+
+
+def small_batch(wl, stream, reps=50):
+    """One 8B-shape layer's four levels and the int8 output projection with
+    argmax, applied to B activation vectors per pass (the weights stream once
+    per pass whatever B is); one HIP graph per B.  The pass is one call of
+    the decode step on the tiled weights: the stream schedule for B = 1, the
+    batched pass for B = 4, 8, 16.  Also timed: the same products as five
+    separate calls (B = 1: the VALU kernels on row-major weights; B > 1: the
+    per-call matrix-core kernels on tiled weights), and the batched pass over
+    all 36 layers.  Reports weight bytes per second and effective integer
+    operations per second (2 per weight per vector)."""
+    import torch
+
+    import packed_weight_gemv_amd as pwg
+    import synth
+    rows_w, table = wl.weights[pwg.LAYOUT_ROWS]   # the per-call VALU kernels take row-major weights
     levels = [(w, sc, r, k) for w, (_, sc, _, _, r, k) in zip(rows_w[:4], wl.desc.levels[:4])]
-    tiled = wl.weights.get(pwg.LAYOUT_TILED)
-    tlevels = [(w, sc, r, k) for w, (_, sc, _, _, r, k) in zip(tiled[0][:4], wl.desc.levels[:4])] if tiled else None
+    tiled = wl.weights[pwg.LAYOUT_TILED]
+    tlevels = [(w, sc, r, k) for w, (_, sc, _, _, r, k) in zip(tiled[0][:4], wl.desc.levels[:4])]
     tscale = wl.desc.out_scale
     vocab, hidden = table.shape
     t2_weights = sum(r * k for _, _, r, k in levels)
     bytes_ = sum(w.numel() * w.element_size() + sc.numel() * 4 for w, sc, _, _ in levels) + table.numel() + tscale.numel() * 4
+    n_all = len(wl.desc.levels) // 4
+    all_weights = sum(r * k for (_, _, _, _, r, k) in wl.desc.levels) + vocab * hidden
+    all_bytes = wl.algorithmic_bytes()["total"]
     out = []
     for batch in (1, 4, 8, 16):
+        d = pass_desc(wl, 1, batch, 20)
+        g = capture(lambda: pwg.decode_step_weights(d, stream=stream), stream)
+        us = time_graph(g, stream, reps, 5) * 1e3
+        pwg.step_status(d)
+        del g
+
         xs = [torch.from_numpy(synth.batch_inputs(batch, k, 20 + i)).to("cuda:0") for i, (_, _, _, k) in enumerate(levels)]
         ys = [torch.empty((batch, r), dtype=torch.float32, device="cuda:0") for _, _, r, _ in levels]
         h = torch.from_numpy(synth.batch_inputs(batch, hidden, 30)).to("cuda:0")
         ws = torch.zeros(pwg.argmax_workspace_bytes(vocab, batch), dtype=torch.uint8, device="cuda:0")
         tok = torch.empty(batch, dtype=torch.int32, device="cuda:0")
-        mfma = batch > 1 and tlevels is not None
         tws = [torch.zeros(max(1, pwg.batch_workspace_bytes(k, batch)), dtype=torch.uint8, device="cuda:0")
-               for _, _, _, k in levels] if mfma else None
+               for _, _, _, k in levels]
 
-        def one():
-            if mfma:
+        def calls():
+            if batch > 1:
                 for (w, sc, r, k), x, y, wsl in zip(tlevels, xs, ys, tws):
                     pwg.ternary_gemv_tiled(w, sc, r, k, x, y=y, workspace=wsl, stream=stream)
                 pwg.int8_gemv_argmax_tiled(tiled[1], tscale, vocab, hidden, h, workspace=ws, token_out=tok,
                                            stream=stream)
                 return
             for (w, sc, r, k), x, y in zip(levels, xs, ys):
-                pwg.ternary_gemv(w, sc, r, k, x if batch > 1 else x[0], y=y if batch > 1 else y[0], stream=stream)
-            pwg.int8_gemv_argmax(table, tscale, h if batch > 1 else h[0], workspace=ws, token_out=tok, stream=stream)
-        g = capture(one, stream)
-        ms = time_graph(g, stream, reps, 5)
-        us = ms * 1e3
-        ops = 2.0 * (t2_weights + vocab * hidden) * batch
-        out.append({"batch": batch, "kernels": "matrix cores, tiled weights" if mfma else "VALU, row-major weights",
-                    "us_per_pass": us, "weight_GBps": bytes_ / us / 1e3,
-                    "pct_of_hbm_peak": 100.0 * bytes_ / (us * 1e-6) / PEAK_HBM_BPS,
-                    "effective_Tops": ops / us / 1e6})
-        log(f"small batch B={batch}: {us:.1f} us per pass, {bytes_ / us / 1e3:.0f} GB/s, {ops / us / 1e6:.1f} Top/s")
+                pwg.ternary_gemv(w, sc, r, k, x[0], y=y[0], stream=stream)
+            pwg.int8_gemv_argmax(table, tscale, h[0], workspace=ws, token_out=tok, stream=stream)
+        g = capture(calls, stream)
+        us_calls = time_graph(g, stream, reps, 5) * 1e3
         del g
+
+        ops = 2.0 * (t2_weights + vocab * hidden) * batch
+        row = {"batch": batch,
+               "pass": "stream schedule (one kernel pair)" if batch == 1 else "batched pass (one kernel pair)",
+               "us_per_pass": us, "weight_GBps": bytes_ / us / 1e3,
+               "pct_of_hbm_peak": 100.0 * bytes_ / (us * 1e-6) / PEAK_HBM_BPS,
+               "effective_Tops": ops / us / 1e6,
+               "us_per_pass_separate_calls": us_calls,
+               "separate_calls": "VALU, row-major weights" if batch == 1 else "matrix cores, tiled weights"}
+        log(f"small batch B={batch}: {us:.1f} us per pass, {bytes_ / us / 1e3:.0f} GB/s, {ops / us / 1e6:.1f} Top/s"
+            f" (separate calls {us_calls:.1f} us)")
+        if batch > 1:
+            d36 = pass_desc(wl, n_all, batch, 40)
+            g = capture(lambda: pwg.decode_step_weights(d36, stream=stream), stream)
+            us36 = time_graph(g, stream, 20, 3) * 1e3
+            pwg.step_status(d36)
+            del g, d36
+            row["all_layers_us_per_pass"] = us36
+            row["all_layers_weight_GBps"] = all_bytes / us36 / 1e3
+            row["all_layers_effective_Tops"] = 2.0 * all_weights * batch / us36 / 1e6
+            log(f"  all {n_all} layers B={batch}: {us36:.1f} us per pass, {all_bytes / us36 / 1e3:.0f} GB/s")
+        out.append(row)
     return {"config": ("one 8B-shape layer (q|k|v 6144x4096, o 4096x4096, gate|up 24576x4096, down 4096x12288 "
                        "ternary) + int8 output projection 151936x4096 with per-vector argmax, B fp32 N(0,1) "
-                       "vectors per pass, one HIP graph per B"),
-            "weight_bytes_per_pass": bytes_, "results": out}
+                       "vectors per pass, one HIP graph per B; also every layer of the step at B > 1"),
+            "weight_bytes_per_pass": bytes_, "all_layers_weight_bytes_per_pass": all_bytes, "results": out}
 
 
 def main():

@@ -45,7 +45,7 @@ extern "C" {
 #endif
 #pragma GCC visibility push(default)
 
-#define PWG_VERSION 3
+#define PWG_VERSION 4
 #define PWG_MAX_COLS 16384
 
 enum {
@@ -168,9 +168,10 @@ int pwg_tile_rows(const void* src, int64_t rows, int64_t row_bytes,
  * each weight is read once for all of them).  Both calls take the weights as
  * pwg_tile_rows arranges them (the arrangement the stream step reads), run on
  * the int8 matrix cores (v_mfma_i32_16x16x64_i8) and form every row sum
- * exactly in int32 per 256-value section over a fixed-point rounding of the
- * activations (three balanced base-256 digits of rint(x * 2^(22 - e)), e the
- * section's exponent); float32 after that.  Asynchronous on `stream`,
+ * exactly in int32 per 256-value section (int8 tables) or 1,024-value block
+ * (ternary weights) over a fixed-point rounding of the activations (three
+ * balanced base-256 digits of rint(x * 2^(22 - e)), e the exponent of the
+ * section or block); float32 after that.  Asynchronous on `stream`,
  * capturable, allocate nothing. */
 
 /* Workspace bytes of pwg_ternary_gemv_tiled for (cols, batch): the converted
@@ -275,12 +276,26 @@ typedef struct pwg_level {
  * All pointers except `levels` are device pointers; `levels` is a host array
  * read during the call (for the persistent schedule it is read by
  * pwg_step_plan instead).  token_in and token_out may alias (the token then
- * feeds the next step on the device). */
+ * feeds the next step on the device).
+ *
+ * Batched pass (batch = 4, 8 or 16; page section "The 0.6B model does not get
+ * to decide": several drafted tokens scored in one batched forward pass).
+ * Schedule STREAM with tiled weights only; every level's cols a multiple of
+ * 2048 and hidden a multiple of 1024 (PWG_ERR_UNSUPPORTED otherwise).  Every
+ * buffer then holds `batch` rows: x float32[batch][cols], y
+ * float32[batch][rows], h float32[batch][hidden], token_in and token_out
+ * int32[batch], emb_row_out int8[batch][hidden], emb_scale_out
+ * float32[batch], emb_deq_out and logits_out float32[batch][hidden] and
+ * [batch][vocab].  The levels take their given inputs (they do not feed one
+ * another), each weight byte is read once per pass, and the levels' outputs
+ * and tokens are those of pwg_ternary_gemv_tiled and
+ * pwg_int8_gemv_argmax_tiled on the same inputs, bit for bit.  token_in and
+ * token_out may alias. */
 typedef struct pwg_step_desc {
   int32_t n_levels;
   int32_t schedule;              /* PWG_SCHEDULE_* */
   int32_t weight_layout;         /* PWG_LAYOUT_*: of every w_packed and of out_table */
-  int32_t reserved;              /* 0 */
+  int32_t batch;                 /* vectors per step: 0 or 1 (batch-1 step), or 4, 8, 16 */
   const pwg_level* levels;       /* host array [n_levels] */
   const int8_t* out_table;       /* int8 vocab x hidden (arranged as weight_layout says) */
   const float* out_scale;        /* float32[vocab] */
@@ -318,6 +333,9 @@ int pwg_step_plan(const pwg_step_desc* desc, void* stream);
  * Stream schedule: a conversion kernel (every level's input and h into
  * matrix-core operands in the workspace), then one kernel with one workgroup
  * per CU; its only waits are inside a workgroup and are bounded the same way.
+ * Batched pass: a conversion kernel (operands and embedding rows), then one
+ * kernel with one workgroup per CU that claims its work from a counter in the
+ * workspace; its waits are inside a workgroup and bounded the same way.
  * The step's workspace is rewritten by every call: calls that overlap on one
  * workspace race. */
 int pwg_decode_step_weights(const pwg_step_desc* desc, void* stream);

@@ -69,7 +69,7 @@ class Level(C.Structure):
 
 class _StepDesc(C.Structure):
     _fields_ = [
-        ("n_levels", _i32), ("schedule", _i32), ("weight_layout", _i32), ("reserved", _i32),
+        ("n_levels", _i32), ("schedule", _i32), ("weight_layout", _i32), ("batch", _i32),
         ("levels", C.POINTER(Level)),
         ("out_table", _vp), ("out_scale", _vp), ("h", _vp), ("vocab", _i64), ("hidden", _i64),
         ("emb_table", _vp), ("emb_scale", _vp), ("token_in", _vp), ("token_out", _vp),
@@ -286,6 +286,7 @@ class StepDesc:
     weight_layout: int = LAYOUT_ROWS
     vocab: int | None = None        # rows of the output table (when it is stored tiled)
     hidden: int | None = None
+    batch: int = 1                  # 4, 8, 16: batched pass (stream schedule); buffers hold batch rows
     _c: object = field(default=None, repr=False)
     _levels_c: object = field(default=None, repr=False)
 
@@ -299,7 +300,7 @@ class StepDesc:
             hidden = self.hidden if self.hidden is not None else self.out_table.shape[1]
             ws = self.workspace
             self._c = _StepDesc(
-                len(self.levels), self.schedule, self.weight_layout, 0, C.cast(arr, C.POINTER(Level)),
+                len(self.levels), self.schedule, self.weight_layout, self.batch, C.cast(arr, C.POINTER(Level)),
                 _ptr(self.out_table), _ptr(self.out_scale), _ptr(self.h), vocab, hidden,
                 _ptr(self.emb_table), _ptr(self.emb_scale), _ptr(self.token_in), _ptr(self.token_out),
                 _ptr(self.emb_row_out), _ptr(self.emb_scale_out), _ptr(self.emb_deq_out), _ptr(self.logits_out),

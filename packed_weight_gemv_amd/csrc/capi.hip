@@ -166,6 +166,8 @@ extern "C" int pwg_tile_rows(const void* src, int64_t rows, int64_t row_bytes, v
 // ---------------------------------------------------------------------------
 namespace {
 
+bool batched(const pwg_step_desc* d) { return d->batch > 1; }
+
 int validate_step(const pwg_step_desc* d) {
   const char* fn = "pwg_decode_step_weights";
   if (!d) return fail(PWG_ERR_ARG, "%s: desc is null", fn);
@@ -179,6 +181,12 @@ int validate_step(const pwg_step_desc* d) {
   if (d->weight_layout != want)
     return fail(PWG_ERR_UNSUPPORTED, "%s: schedule %d takes weight layout %d (got %d)", fn, d->schedule, want,
                 d->weight_layout);
+  if (d->batch != 0 && d->batch != 1) {
+    if (!(d->batch == 4 || d->batch == 8 || d->batch == 16))
+      return fail(PWG_ERR_ARG, "%s: batch must be 0, 1, 4, 8 or 16 (got %d)", fn, d->batch);
+    if (d->schedule != PWG_SCHEDULE_STREAM)
+      return fail(PWG_ERR_UNSUPPORTED, "%s: batch %d takes the stream schedule", fn, d->batch);
+  }
   if (d->n_levels > 0 && !d->levels) return fail(PWG_ERR_ARG, "%s: levels is null", fn);
   for (int i = 0; i < d->n_levels; ++i) {
     const pwg_level& L = d->levels[i];
@@ -189,7 +197,7 @@ int validate_step(const pwg_step_desc* d) {
     TRY(check_shape(d->vocab, d->hidden, fn));
     TRY(check_ptr(d->out_table, fn, "out_table"));
     TRY(check_ptr(d->out_scale, fn, "out_scale"));
-    TRY(step_stream_check(d));
+    TRY(batched(d) ? step_batch_check(d) : step_stream_check(d));
   } else {
     TRY(validate_int8(d->out_table, d->out_scale, d->vocab, d->hidden, fn));
   }
@@ -210,6 +218,11 @@ int validate_step(const pwg_step_desc* d) {
 
 extern "C" size_t pwg_step_workspace_bytes(const pwg_step_desc* d) {
   if (!d || d->vocab < 1) return 0;
+  if (!(d->batch == 0 || d->batch == 1 || d->batch == 4 || d->batch == 8 || d->batch == 16)) return 0;
+  if (batched(d)) {
+    if (d->schedule != PWG_SCHEDULE_STREAM || d->n_levels < 0 || (d->n_levels > 0 && !d->levels)) return 0;
+    return step_batch_workspace(d);
+  }
   if (d->schedule == PWG_SCHEDULE_STREAM) return step_stream_workspace(d);
   return argmax_ws(d->vocab, 1) + step_persistent_workspace(d);
 }
@@ -219,6 +232,7 @@ extern "C" int pwg_step_plan(const pwg_step_desc* d, void* stream) {
   if (d->workspace_bytes < pwg_step_workspace_bytes(d))
     return fail(PWG_ERR_SIZE, "pwg_step_plan: workspace %zu < %zu bytes", d->workspace_bytes,
                 pwg_step_workspace_bytes(d));
+  if (batched(d)) return step_batch_plan(d, stream);
   if (d->schedule == PWG_SCHEDULE_STREAM) return step_stream_plan(d, 0, stream);
   if (d->schedule != PWG_SCHEDULE_LEVELS) return step_persistent_plan(d, argmax_ws(d->vocab, 1), stream);
   return PWG_OK;
@@ -227,6 +241,7 @@ extern "C" int pwg_step_plan(const pwg_step_desc* d, void* stream) {
 extern "C" int pwg_step_status(const pwg_step_desc* d, void* stream) {
   TRY(validate_step(d));
   if (d->schedule == PWG_SCHEDULE_LEVELS) return PWG_OK;
+  if (batched(d)) return step_batch_status(d, stream);
   if (d->schedule == PWG_SCHEDULE_STREAM) return step_stream_status(d, 0, stream);
   return step_persistent_status(d, argmax_ws(d->vocab, 1), stream);
 }
@@ -236,6 +251,7 @@ extern "C" int pwg_decode_step_weights(const pwg_step_desc* d, void* stream) {
   if (d->workspace_bytes < pwg_step_workspace_bytes(d))
     return fail(PWG_ERR_SIZE, "pwg_decode_step_weights: workspace %zu < %zu bytes", d->workspace_bytes,
                 pwg_step_workspace_bytes(d));
+  if (batched(d)) return step_batch_launch(d, stream);
   if (d->schedule == PWG_SCHEDULE_STREAM) return step_stream_launch(d, 0, stream);
   if (d->schedule != PWG_SCHEDULE_LEVELS) return step_persistent_launch(d, argmax_ws(d->vocab, 1), stream);
   // Levels schedule: embedding row, every level in decoder order, output

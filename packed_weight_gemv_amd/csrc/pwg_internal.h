@@ -73,6 +73,13 @@ int step_stream_plan(const pwg_step_desc* d, size_t ws_offset, void* stream);
 int step_stream_launch(const pwg_step_desc* d, size_t ws_offset, void* stream);
 int step_stream_status(const pwg_step_desc* d, size_t ws_offset, void* stream);
 
+// Batched pass (step_batch.hip): batch 4, 8 or 16, tiled weights.
+int step_batch_check(const pwg_step_desc* d);
+size_t step_batch_workspace(const pwg_step_desc* d);
+int step_batch_plan(const pwg_step_desc* d, void* stream);
+int step_batch_launch(const pwg_step_desc* d, void* stream);
+int step_batch_status(const pwg_step_desc* d, void* stream);
+
 // 16-row x 64-byte tile arrangement (tile.hip).
 size_t tiled_bytes(int64_t rows, int64_t row_bytes);
 int launch_tile_rows(const void* src, int64_t rows, int64_t row_bytes, void* dst, void* stream);

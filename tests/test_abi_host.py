@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_error_string():
-    assert pwg.version() == 3
+    assert pwg.version() == 4
     assert isinstance(pwg.last_error(), str)
 
 
@@ -212,6 +212,47 @@ def test_step_layout_errors():
     lv[0] = pwg.Level(A, A, A, A, 64, 4096)
     d.hidden = 4160
     assert pwg._step(C.byref(d), None) == ERR_UNSUPPORTED
+
+
+def test_batched_step_errors():
+    """A batched pass (batch 4, 8, 16) takes the stream schedule, tiled
+    weights, level widths that are multiples of 2048 and a hidden width that
+    is a multiple of 1024; every call here fails validation before anything
+    is enqueued."""
+    d = pwg._StepDesc()
+    d.vocab, d.hidden = 1000, 4096
+    for name in ("out_table", "out_scale", "h", "emb_table", "emb_scale", "token_in", "token_out",
+                 "emb_row_out", "emb_scale_out", "workspace"):
+        setattr(d, name, A)
+    lv = (pwg.Level * 2)(pwg.Level(A, A, A, A, 64, 4096), pwg.Level(A, A, A, A, 100, 12288))
+    d.n_levels, d.levels = 2, C.cast(lv, C.POINTER(pwg.Level))
+    d.schedule, d.weight_layout = pwg.SCHEDULE_STREAM, pwg.LAYOUT_TILED
+    sizes = {}
+    for b in (4, 8, 16):
+        d.batch = b
+        sizes[b] = pwg._step_ws(C.byref(d))
+    assert 0 < sizes[4] < sizes[8] < sizes[16]
+    d.batch = 16
+    d.workspace_bytes = sizes[16] - 1
+    assert pwg._step(C.byref(d), None) == ERR_SIZE
+    assert pwg._step_plan(C.byref(d), None) == ERR_SIZE
+    d.workspace_bytes = sizes[16]
+    for bad in (2, 3, 5, 32, -1):
+        d.batch = bad
+        assert pwg._step_ws(C.byref(d)) == 0
+        assert pwg._step(C.byref(d), None) == ERR_ARG and "batch" in pwg.last_error()
+    d.batch = 8
+    d.schedule, d.weight_layout = pwg.SCHEDULE_LEVELS, pwg.LAYOUT_ROWS
+    assert pwg._step(C.byref(d), None) == ERR_UNSUPPORTED
+    d.schedule, d.weight_layout = pwg.SCHEDULE_STREAM, pwg.LAYOUT_TILED
+    lv[1] = pwg.Level(A, A, A, A, 100, 1024)           # not a multiple of 2048
+    assert pwg._step(C.byref(d), None) == ERR_UNSUPPORTED and "2048" in pwg.last_error()
+    lv[1] = pwg.Level(A, A, A, A, 100, 12288)
+    d.hidden = 1536                                    # not a multiple of 1024
+    assert pwg._step(C.byref(d), None) == ERR_UNSUPPORTED and "1024" in pwg.last_error()
+    d.hidden = 4096
+    d.h = MIS
+    assert pwg._step(C.byref(d), None) == ERR_ALIGN
 
 
 def test_tiled_size():
