@@ -40,8 +40,7 @@ struct BLevel {
   float* y;                 // output [batch][rows] (vocabulary: logits or null)
   unsigned char* ops;       // operand digits (workspace)
   int* exps;                // section exponents [cols / 256][batch] (workspace)
-  int rows, cols, kind;
-  int unit0;                // first conversion unit: (section, vector) pairs of the levels before
+  int rows, cols, kind, pad;
 };
 
 // Row blocks [rb0, rb1) of one level.
@@ -50,10 +49,11 @@ struct BItem {
 };
 
 struct BPlan {
-  int n_levels, batch, n_items, n_units;
+  int n_levels, batch, n_items, pad0;
   int vocab, hidden, grid, pad;
   const BLevel* levels;           // [n_levels + 1], the vocabulary last
   const BItem* items;             // [n_items], in claim order
+  const int2* conv_wg;            // [conversion workgroups]: (level or -1 for the embedding rows, first unit)
   unsigned* item_next;            // global claim counter
   unsigned* arrivals;
   unsigned* status;
@@ -77,7 +77,6 @@ using namespace bstep;
 
 constexpr int kRing = 8;        // claimed items a workgroup holds (ring in LDS)
 constexpr int kTernarySets = 4; // row-block sets per ternary item and compute wave
-constexpr int kConvertBlocks = 1024;  // conversion workgroups (4 waves each) at most
 constexpr int kMaxGrid = 1024;
 enum : unsigned { kStatusOk = 0, kStatusTimeout = 1 };
 
@@ -109,30 +108,29 @@ __device__ void embed_row(const BPlan& P, int b, unsigned lane) {
 }
 
 // Units: per level, (block, vector) pairs, blocks of 1,024 values (ternary)
-// or 256 (the vocabulary's h), then one embedding row per vector.  Wave w of
-// the grid converts units w, w + W, w + 2 W, ... (W waves in the grid); unit
-// u' of a level (relative to its first unit) is block u' / batch of vector
-// u' % batch.
+// or 256 (the vocabulary's h); unit u of a level is block u / batch of
+// vector u % batch.  Each wave of the grid converts one unit: workgroup w
+// converts units c.y .. c.y + 3 of level c.x (c = conv_wg[w]; units past the
+// level's last are skipped), or, for c.x < 0, the embedding rows of vectors
+// c.y .. c.y + 3.
 __global__ __launch_bounds__(256) void bstep_convert_kernel(const BPlan* __restrict__ plan) {
   const BPlan& P = *plan;
   const unsigned lane = threadIdx.x & 63u;
-  const int nw = static_cast<int>(gridDim.x) * 4;
-  for (int u = uni(static_cast<int>(blockIdx.x * 4 + (threadIdx.x >> 6))); u < P.n_units + P.batch; u += nw) {
-    if (u < P.n_units) {
-      int lo = 0, hi = P.n_levels;  // the last level with unit0 <= u (unit0 ascends)
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (P.levels[mid].unit0 <= u) lo = mid;
-        else hi = mid - 1;
-      }
-      const BLevel& L = P.levels[lo];
-      const int rel = u - L.unit0, blk = rel / P.batch, b = rel % P.batch;
-      const float* xb = L.x + static_cast<size_t>(b) * L.cols;
-      if (L.kind == kKindTernary) convert_ternary_block(xb, blk, b, P.batch / 4, L.ops, L.exps, lane);
-      else convert_int8_section(xb, blk, b, P.batch / 4, L.ops, L.exps, lane);
-    } else {
-      embed_row(P, u - P.n_units, lane);
-    }
+  typedef const __attribute__((address_space(4))) int cint;
+  const cint* cw = (const cint*)P.conv_wg + 2 * blockIdx.x;  // scalar loads
+  const int level = cw[0], u = uni(cw[1] + static_cast<int>(threadIdx.x >> 6));
+  if (level >= 0) {
+    const BLevel& L = P.levels[level];
+    const int cols = uni(L.cols), kind = uni(L.kind), batch = P.batch;
+    unsigned char* ops = uni(L.ops);
+    int* exps = uni(L.exps);
+    const int blk = u / batch, b = u % batch;
+    if (blk >= cols / (kind == kKindTernary ? 1024 : 256)) return;
+    const float* xb = uni(L.x) + static_cast<size_t>(b) * cols;
+    if (kind == kKindTernary) convert_ternary_block(xb, blk, b, batch / 4, ops, exps, lane);
+    else convert_int8_section(xb, blk, b, batch / 4, ops, exps, lane);
+  } else if (u < P.batch) {
+    embed_row(P, u, lane);
   }
 }
 
@@ -449,13 +447,37 @@ __global__ __launch_bounds__(kThreads, 1) void bstep_kernel(const BPlan* __restr
 // ----------------------------------------------------------------- host side
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-constexpr int kVocabItemBlocks = kCW * 2;                  // two row blocks per compute wave
-constexpr int kTernaryItemBlocks = kCW * kTernarySets;     // one per set and compute wave
+// Row blocks per item: kR per compute wave (int8), kR per set and compute
+// wave (ternary).
+constexpr int kVocabItemBlocks = kCW * Compute<1, false>::kR;
+constexpr int kTernaryItemBlocks = kCW * Compute<1, true>::kR * kTernarySets;
 
 struct BLayout {
-  size_t plan, counters, partials, park, levels, items, regions, total;
+  size_t plan, counters, partials, park, levels, items, conv, regions, total;
   int n_items;
 };
+
+// Conversion workgroups (four units each): per level ceil(units / 4), then
+// the embedding rows.
+std::vector<int2> conv_table(const pwg_step_desc* d) {
+  std::vector<int2> out;
+  for (int i = 0; i <= d->n_levels; ++i) {
+    const int64_t cols = i < d->n_levels ? d->levels[i].cols : d->hidden;
+    const int units = static_cast<int>(cols / (i < d->n_levels ? 1024 : 256)) * d->batch;
+    for (int u = 0; u < units; u += 4) out.push_back(make_int2(i, u));
+  }
+  for (int u = 0; u < d->batch; u += 4) out.push_back(make_int2(-1, u));
+  return out;
+}
+
+size_t conv_count(const pwg_step_desc* d) {
+  size_t n = static_cast<size_t>(d->batch + 3) / 4;
+  for (int i = 0; i <= d->n_levels; ++i) {
+    const int64_t cols = i < d->n_levels ? d->levels[i].cols : d->hidden;
+    n += static_cast<size_t>((cols / (i < d->n_levels ? 1024 : 256)) * d->batch + 3) / 4;
+  }
+  return n;
+}
 
 // Claim order: the vocabulary's items, then the ternary levels' items widest
 // K first; the last `grid` ternary-item halves are separate items, so that
@@ -499,7 +521,8 @@ BLayout layout_for(const pwg_step_desc* d) {
   L.park = L.partials + static_cast<size_t>(d->batch) * kMaxGrid * 8;
   L.levels = align_up(L.park + kStepBytes, 256);
   L.items = align_up(L.levels + static_cast<size_t>(d->n_levels + 1) * sizeof(BLevel), 256);
-  L.regions = align_up(L.items + static_cast<size_t>(L.n_items) * sizeof(BItem), 256);
+  L.conv = align_up(L.items + static_cast<size_t>(L.n_items) * sizeof(BItem), 256);
+  L.regions = align_up(L.conv + conv_count(d) * sizeof(int2), 256);
   size_t end = L.regions;
   for (int i = 0; i < d->n_levels; ++i) end += operand_bytes(d->levels[i].cols, d->batch);
   end += operand_bytes(d->hidden, d->batch);
@@ -558,6 +581,7 @@ int step_batch_plan(const pwg_step_desc* d, void* stream) {
   h.grid = grid;
   h.levels = reinterpret_cast<const BLevel*>(dbase + lay.levels);
   h.items = reinterpret_cast<const BItem*>(dbase + lay.items);
+  h.conv_wg = reinterpret_cast<const int2*>(dbase + lay.conv);
   h.item_next = reinterpret_cast<unsigned*>(dbase + lay.counters);
   h.arrivals = reinterpret_cast<unsigned*>(dbase + lay.counters + 64);
   h.status = reinterpret_cast<unsigned*>(dbase + lay.counters + 128);
@@ -573,7 +597,6 @@ int step_batch_plan(const pwg_step_desc* d, void* stream) {
 
   std::vector<BLevel> lv(d->n_levels + 1);
   size_t off = lay.regions;
-  int units = 0;
   for (int i = 0; i <= d->n_levels; ++i) {
     BLevel& L = lv[i];
     const bool vocab = i == d->n_levels;
@@ -588,12 +611,11 @@ int step_batch_plan(const pwg_step_desc* d, void* stream) {
     L.rows = static_cast<int>(vocab ? d->vocab : d->levels[i].rows);
     L.cols = static_cast<int>(cols);
     L.kind = vocab ? kKindInt8 : kKindTernary;
-    L.unit0 = units;
-    units += static_cast<int>(cols / (vocab ? 256 : 1024)) * d->batch;
+    L.pad = 0;
     off += operand_bytes(cols, d->batch);
   }
-  h.n_units = units;
   const std::vector<BItem> items = make_items(d, grid);
+  const std::vector<int2> conv = conv_table(d);
 
   h.n_items = static_cast<int>(items.size());
   hipError_t e = hipMemsetAsync(dbase + lay.counters, 0, lay.levels - lay.counters, st);  // counters, partials, park
@@ -602,6 +624,8 @@ int step_batch_plan(const pwg_step_desc* d, void* stream) {
     e = hipMemcpyAsync(dbase + lay.levels, lv.data(), lv.size() * sizeof(BLevel), hipMemcpyHostToDevice, st);
   if (e == hipSuccess)
     e = hipMemcpyAsync(dbase + lay.items, items.data(), items.size() * sizeof(BItem), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(dbase + lay.conv, conv.data(), conv.size() * sizeof(int2), hipMemcpyHostToDevice, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return fail(PWG_ERR_HIP, "pwg_step_plan: %s", hipGetErrorString(e));
   return PWG_OK;
@@ -612,10 +636,7 @@ int step_batch_launch(const pwg_step_desc* d, void* stream) {
   int grid = 0;
   TRY(grid_size(&grid));
   const BPlan* dplan = plan_ptr(d);
-  int units = 0;
-  for (int i = 0; i < d->n_levels; ++i) units += static_cast<int>(d->levels[i].cols / 1024) * d->batch;
-  units += static_cast<int>(d->hidden / 256) * d->batch;
-  const int conv_blocks = std::min((units + d->batch + 3) / 4, kConvertBlocks);
+  const int conv_blocks = static_cast<int>(conv_count(d));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(bstep_convert_kernel, dim3(conv_blocks), dim3(256), 0, st, dplan);
   if (d->batch == 4)

@@ -66,7 +66,7 @@ struct Level {
   int kind;                 // kKindTernary or kKindInt8
   int bsc_off, asc_off;     // ternary: scale offsets; int8: bsc_off = exponent offset
   int b_bytes;              // region bytes (a multiple of 16)
-  int pad;
+  int conv0;                // first workgroup of the conversion kernel that converts this level's input
 };
 
 // Blocks [b0, b1) of level `level`: one contiguous part of a workgroup's range.
@@ -91,6 +91,7 @@ struct Plan {
   Seg pool_segs[kMaxPoolSegs];
   unsigned* pool_next;      // global claim counter
   const int* seg_count;     // [grid]
+  const int* conv_level;    // [conversion workgroups]: the level each one converts
   const float* h;
   const dev::u32x4* emb_table;
   const float* emb_scale;

@@ -727,17 +727,21 @@ __device__ void convert_int8(const Level& L, const float* h, int sec, unsigned l
   if (lane == 0) *reinterpret_cast<int*>(b + L.bsc_off + 4 * sec) = e - 22;
 }
 
-// Grid (x, level): level < n_levels converts ternary input blocks, level ==
-// n_levels converts h.  Workgroups beyond a level's work return at once.
+// One-dimensional grid: the workgroups of level i are conv0(i) ..
+// conv0(i + 1) - 1 (ternary: 64 blocks of 32 inputs per workgroup; the
+// vocabulary: four 256-value sections of h, one per wave); the plan's table
+// names each workgroup's level.
 __global__ __launch_bounds__(256) void stream_convert_kernel(const Plan* __restrict__ plan,
                                                              const Level* __restrict__ levels) {
   const Plan& P = *plan;
-  const int li = blockIdx.y;
-  const Level& L = levels[li];
-  if (li < P.n_levels) {
-    convert_ternary(L, blockIdx.x * 256 + threadIdx.x);
+  const int wg = static_cast<int>(blockIdx.x);
+  const int lo = ((const __attribute__((address_space(4))) int*)P.conv_level)[wg];  // a scalar load
+  const Level& L = levels[lo];
+  const int local = wg - L.conv0;
+  if (lo < P.n_levels) {
+    convert_ternary(L, local * 256 + static_cast<int>(threadIdx.x));
   } else {
-    const int sec = blockIdx.x * 4 + static_cast<int>(threadIdx.x >> 6);
+    const int sec = local * 4 + static_cast<int>(threadIdx.x >> 6);
     if (sec < P.hidden / 256) convert_int8(L, P.h, sec, threadIdx.x & 63u);
   }
 }
@@ -751,8 +755,15 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 constexpr int kMaxGrid = 1024;
 
 struct SLayout {
-  size_t plan, partials, arrivals, levels, segs, seg_count, park, regions, total;
+  size_t plan, partials, arrivals, levels, segs, seg_count, conv_level, park, regions, total;
 };
+
+// Conversion workgroups of level i (the vocabulary: i == n_levels): 4
+// threads per 32-input ternary block, one wave per 256-value section of h.
+int conv_blocks(const pwg_step_desc* d, int i) {
+  if (i < d->n_levels) return static_cast<int>((d->levels[i].cols / 32 * 4 + 255) / 256);
+  return static_cast<int>((d->hidden / 256 + 3) / 4);
+}
 
 size_t region_bytes(const pwg_step_desc* d, int i) {
   return i < d->n_levels ? ternary_region_bytes(d->levels[i].cols) : int8_region_bytes(d->hidden);
@@ -766,7 +777,10 @@ SLayout layout_for(const pwg_step_desc* d) {
   L.levels = align_up(L.arrivals + 256, 256);
   L.segs = align_up(L.levels + static_cast<size_t>(d->n_levels + 1) * sizeof(Level), 256);
   L.seg_count = align_up(L.segs + static_cast<size_t>(kMaxGrid) * (d->n_levels + 1) * sizeof(Seg), 256);
-  L.park = align_up(L.seg_count + kMaxGrid * 4, 256);
+  int conv = 0;
+  for (int i = 0; i <= d->n_levels; ++i) conv += conv_blocks(d, i);
+  L.conv_level = align_up(L.seg_count + kMaxGrid * 4, 256);
+  L.park = align_up(L.conv_level + static_cast<size_t>(conv) * 4, 256);
   L.regions = L.park + kParkBytes;
   size_t end = L.regions;
   for (int i = 0; i <= d->n_levels; ++i) end += align_up(region_bytes(d, i), 256);
@@ -933,6 +947,7 @@ int step_stream_plan(const pwg_step_desc* d, size_t ws_offset, void* stream) {
   h.arrivals = reinterpret_cast<unsigned*>(dbase + lay.arrivals);
   h.status = reinterpret_cast<unsigned*>(dbase + lay.arrivals + 64);
   h.seg_count = reinterpret_cast<const int*>(dbase + lay.seg_count);
+  h.conv_level = reinterpret_cast<const int*>(dbase + lay.conv_level);
 
   std::vector<Level> lv(d->n_levels + 1);
   size_t off = lay.regions;
@@ -966,6 +981,13 @@ int step_stream_plan(const pwg_step_desc* d, size_t ws_offset, void* stream) {
       L.asc_off = 0;
     }
     off += align_up(region_bytes(d, i), 256);
+  }
+  int conv = 0;
+  std::vector<int> conv_level;
+  for (int i = 0; i <= d->n_levels; ++i) {
+    lv[i].conv0 = conv;
+    conv += conv_blocks(d, i);
+    conv_level.insert(conv_level.end(), conv_blocks(d, i), i);
   }
 
   const std::vector<int> tail = pool_tail_levels(d);
@@ -1004,6 +1026,8 @@ int step_stream_plan(const pwg_step_desc* d, size_t ws_offset, void* stream) {
     e = hipMemcpyAsync(dbase + lay.segs, seg_flat.data(), seg_flat.size() * sizeof(Seg), hipMemcpyHostToDevice, st);
   if (e == hipSuccess)
     e = hipMemcpyAsync(dbase + lay.seg_count, seg_count.data(), seg_count.size() * 4, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(dbase + lay.conv_level, conv_level.data(), conv_level.size() * 4, hipMemcpyHostToDevice, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return fail(PWG_ERR_HIP, "pwg_step_plan: %s", hipGetErrorString(e));
   return PWG_OK;
@@ -1018,15 +1042,11 @@ int step_stream_launch(const pwg_step_desc* d, size_t ws_offset, void* stream) {
   const SLayout lay = layout_for(d);
   const Level* lv = reinterpret_cast<const Level*>(dbase + lay.levels);
   const Seg* segs = reinterpret_cast<const Seg*>(dbase + lay.segs);
-  size_t need = 0;
-  int conv_x = (d->hidden / 256 + 3) / 4;
-  for (int i = 0; i <= d->n_levels; ++i) {
-    need = std::max(need, region_bytes(d, i));
-    if (i < d->n_levels) conv_x = std::max(conv_x, static_cast<int>((d->levels[i].cols / 8 + 255) / 256));
-  }
+  int conv = 0;
+  for (int i = 0; i <= d->n_levels; ++i) conv += conv_blocks(d, i);
   const size_t lds = lds_bytes(d);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(stream_convert_kernel, dim3(conv_x, d->n_levels + 1), dim3(256), 0, st, dplan, lv);
+  hipLaunchKernelGGL(stream_convert_kernel, dim3(conv), dim3(256), 0, st, dplan, lv);
   if (prefetch_depth(d) == 8)
     hipLaunchKernelGGL(stream_step_kernel<8>, dim3(grid), dim3(kThreads), lds, st, dplan, lv, segs);
   else
