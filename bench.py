@@ -433,8 +433,19 @@ def main():
                                                wl.desc.hidden, hb, workspace=iws, stream=stream)
         torch.cuda.synchronize()
         pwg.step_status(wl.desc, stream=stream)
+        # the batched pass over every layer and the output table, 4 and 16 vectors
+        if pwg.LAYOUT_TILED in wl.weights:
+            for B in (4, 16):
+                d = pass_desc(wl, len(wl.desc.levels) // 4, B, 40)
+                with torch.cuda.stream(stream):
+                    for _ in range(3):
+                        pwg.decode_step_weights(d, stream=stream)
+                torch.cuda.synchronize()
+                pwg.step_status(d, stream=stream)
+                del d
         log("counter run done: 3 steps, one 1 GiB device-to-device copy, 3 row-major ternary GEMVs "
-            "(393216x4096), 3 row-major int8 projections and 3 x 4 small-batch calls (16 vectors)")
+            "(393216x4096), 3 row-major int8 projections, 3 x 4 small-batch calls (16 vectors) and 3 batched "
+            "passes over every layer at 4 and at 16 vectors")
         return
 
     def run(desc_schedule):
