@@ -281,6 +281,8 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
   int* wcnt = ready + 1;                              // claims of static blocks
   int* phead = ready + 2;                             // pool claims popped from the ring
   int* done = ready + 4;                              // [kWaves]: highest segment a wave is done with
+  int* pool_mask = ready + 4 + kWaves;                // bit q: this workgroup claimed a block of pool segment q
+  int* pool_past = pool_mask + 1;                     // no later claim of this workgroup falls below pool segment pool_past
   unsigned long long* wkeys = reinterpret_cast<unsigned long long*>(flags + 128);  // [kWaves]
   int* seg_first = reinterpret_cast<int*>(flags + kSegFirstOff);               // [kMaxWgSegs + 1]
   unsigned long long* ring = reinterpret_cast<unsigned long long*>(flags + kRingOff);  // [kRing]
@@ -289,6 +291,8 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
     *ready = -1;
     *wcnt = 0;
     *phead = 0;
+    *pool_mask = 0;
+    *pool_past = 0;
   }
   if (threadIdx.x < kWaves) done[threadIdx.x] = -1;
   if (threadIdx.x < kRing) ring[threadIdx.x] = ~0ull;  // tag 0xFFFFFFFF: empty
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
     // ring beyond the compute waves' pops (one global atomic per batch of
     // claims); after the pool runs out, one end marker per compute wave.
     bool late = false;
-    int tail = 0, ends = 0, batch = kClaimBatch;
+    int tail = 0, ends = 0, batch = kClaimBatch, mask = 0;
     bool exhausted = false;
     const int pool_total = uni(P.pool_total);
     unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
@@ -324,17 +328,32 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
             p = static_cast<int>(__hip_atomic_fetch_add(P.pool_next, static_cast<unsigned>(batch), __ATOMIC_RELAXED,
                                                         __HIP_MEMORY_SCOPE_AGENT));
           p = uni(p);
+          int past = 0;
           for (int q = 0; q < batch; ++q) {
             const int pq = p + q < pool_total ? p + q : -1;
             if (pq < 0) {
               exhausted = true;
               break;
             }
+            // the pool segment of the block: its operands will be needed
+            int sq = 0;  // pool_first[j] = pool_total for j >= pool_nseg
+#pragma unroll
+            for (int step = kMaxPoolSegs / 2; step >= 1; step >>= 1)
+              if (P.pool_first[sq + step] <= pq) sq += step;
+            mask |= 1 << uni(sq);
+            past = uni(sq);
             if (lane == 0)
               __hip_atomic_store(&ring[tail & (kRing - 1)],
                                  (static_cast<unsigned long long>(static_cast<unsigned>(tail)) << 32) | static_cast<unsigned>(pq),
                                  __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             tail = uni(tail + 1);
+          }
+          // claims only move forward through the pool: segments below the
+          // last claimed one will not be claimed again (none at all once the
+          // pool is used up)
+          if (lane == 0) {
+            __hip_atomic_store(pool_mask, mask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_store(pool_past, exhausted ? kMaxPoolSegs : past, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
           }
           if (pool_total - (p + batch) < kLateClaims * P.grid) batch = kLateBatch;
         } else {
@@ -367,6 +386,30 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
     int s = 0, head = 0;
     unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
     while (s < nall) {
+      if (s >= nseg) {
+        // a pool segment: stage it once this workgroup has claimed one of
+        // its blocks; skip it (no region) once the claims have moved past it
+        const int q = s - nseg;
+        const int past = uni(__hip_atomic_load(pool_past, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+        const int mask = uni(__hip_atomic_load(pool_mask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if (!((mask >> q) & 1)) {
+          if (past > q) {
+            if (lane == 0) {
+              seg_pos[2 * s] = 0;
+              seg_pos[2 * s + 1] = 0;  // an empty region overlaps nothing
+            }
+            lds_publish(ready, s);
+            s = uni(s + 1);
+            t0 = __builtin_amdgcn_s_memrealtime();
+          } else if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
+            late = true;
+            break;
+          } else {
+            __builtin_amdgcn_s_sleep(1);
+          }
+          continue;
+        }
+      }
       const Level& L = levels[seg_at(segs, nseg, P, s).level];
       const int bytes = uni(L.b_bytes);
       int d = (lane >= kControl && lane < kWaves) ? lds_acquire(&done[lane]) : 0x7FFFFFFF;
