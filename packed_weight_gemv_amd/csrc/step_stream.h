@@ -23,10 +23,10 @@ constexpr int kMaxWgSegs = 32;                    // static segments (levels tou
 constexpr int kMaxPoolSegs = 16;                  // levels of the shared pool (the vocabulary first)
 constexpr double kPoolTailShare = 0.04;           // small-block ternary levels that end the pool: this share of the bytes
 constexpr int kRing = 64;                         // pool claims queued per workgroup (ring entries)
-constexpr int kPoolAhead = 6;                     // claims a workgroup keeps ready beyond its pops
+constexpr int kPoolAhead = 2;                     // claims a workgroup keeps ready beyond its pops
 constexpr int kClaimBatch = 8;                    // pool blocks per global atomic ...
-constexpr int kLateClaims = 16;                   // ... until fewer than this many per workgroup remain,
-constexpr int kLateBatch = 4;                     // then this many
+constexpr int kLateClaims = 8;                   // ... until fewer than this many per workgroup remain,
+constexpr int kLateBatch = 1;                     // then this many
 // LDS after the operand regions: flag words and argmax keys, the static
 // segments' first-block table, the pool claim ring, the segments' region
 // offsets.
