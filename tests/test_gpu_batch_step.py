@@ -239,3 +239,27 @@ def test_vector_ranges(kind):
         for m, y in zip(p.mats, out["levels"]):
             assert np.array_equal(y[2], (m.scale * m.w[:, 333]).astype(np.float32))
     p.check(out)
+
+
+EDGE = [
+    ([], 4000, 1024, 8),                      # the output table only; hidden of one operand slice
+    ([(1, 2048)], 1, 1024, 16),               # one row everywhere (row blocks padded to 16)
+    ([(33, 16384), (16, 2048)], 777, 8192, 4),  # wide K for both kinds
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=["vocab-only", "one-row", "wide-k"])
+def test_edge_shapes(case):
+    shapes, vocab, hidden, batch = case
+    p = BatchPass(shapes, vocab=vocab, hidden=hidden, batch=batch, seed=8)
+    pwg.step_plan(p.desc)
+    for j in range(2):
+        p.set_inputs(60 + j)
+        out = run(p)
+        p.check(out)
+        if hidden <= 8192:
+            ys, tok, lo = p.per_call()
+            for i, (a, b) in enumerate(zip(out["levels"], ys)):
+                assert same_bits(a, b), f"level {i}"
+            assert np.array_equal(out["tokens"], tok)
+            assert same_bits(out["logits"], lo)
