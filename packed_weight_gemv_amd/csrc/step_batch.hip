@@ -16,7 +16,7 @@
 // or 7 of one ternary level (two or one per compute wave), which the seven
 // compute waves run over K in lock step with the arithmetic of the per-call
 // kernels, while a staging wave claims the next item and copies operand
-// slices into two LDS buffers.  Items come in a fixed order, the vocabulary
+// slices into two or three LDS buffers.  Items come in a fixed order, the vocabulary
 // first and then the ternary levels widest K first, so that the last items
 // are the smallest and the workgroups finish close together.  The last
 // workgroup to arrive reduces the per-workgroup argmax keys into each
@@ -49,7 +49,7 @@ struct BItem {
 };
 
 struct BPlan {
-  int n_levels, batch, n_items, pad0;
+  int n_levels, batch, n_items, n_static;  // items [0, n_static) go round-robin (a multiple of grid)
   int vocab, hidden, grid, pad;
   const BLevel* levels;           // [n_levels + 1], the vocabulary last
   const BItem* items;             // [n_items], in claim order
@@ -134,9 +134,16 @@ __global__ __launch_bounds__(256) void bstep_convert_kernel(const BPlan* __restr
   }
 }
 
+// Operand slice buffers in LDS: three for 4 and 8 vectors (the staging wave
+// runs two slices ahead), two for 16 (three 64 KiB slices would not fit).
+template <int NG>
+constexpr int slice_bufs() {
+  return NG <= 2 ? 3 : 2;
+}
+
 template <int NG>
 constexpr size_t bstep_lds() {
-  return 2 * SliceShape<NG>::kBytes + 64 + 16 * kRing + kW * 4 * NG * 8;
+  return slice_bufs<NG>() * SliceShape<NG>::kBytes + 64 + 16 * kRing + kW * 4 * NG * 8;
 }
 
 // Compute-wave state shared by the two phases (int8 items, then ternary).
@@ -151,6 +158,7 @@ template <int NG>
 struct Pass {
   static constexpr int kB = 4 * NG;
   static constexpr int kSliceBytes = SliceShape<NG>::kBytes;
+  static constexpr int kBufs = slice_bufs<NG>();
   const BPlan& P;
   unsigned char* smem;
   int* ready;        // highest slice staged
@@ -162,10 +170,10 @@ struct Pass {
 
   __device__ __forceinline__ Pass(const BPlan& p, unsigned char* s, unsigned l, int w)
       : P(p), smem(s), lane(l), wave(w) {
-    ready = reinterpret_cast<int*>(smem + 2 * kSliceBytes);
+    ready = reinterpret_cast<int*>(smem + kBufs * kSliceBytes);
     nknown = ready + 1;
     done = ready + 2;
-    ring = reinterpret_cast<int4*>(smem + 2 * kSliceBytes + 64);
+    ring = reinterpret_cast<int4*>(smem + kBufs * kSliceBytes + 64);
   }
 
   // Item i of this workgroup once the staging wave has claimed it.
@@ -186,15 +194,24 @@ struct Pass {
 
   // The staging wave: claims items into the ring and copies each item's
   // operand slices (t counts slices over the items) into buffer t & 1 once
-  // every compute wave is done with slice t - 2.  The item after the current
+  // every compute wave is done with slice t - kBufs.  The item after the current
   // one is claimed before the current one's second-to-last slice, so that
   // the compute waves can issue its first tile loads in time.
   __device__ void stage(bool& late) {
     int claimed = 0;
+    // Claim k of this workgroup: item blockIdx.x + k grid while those are
+    // round-robin items (no atomic: under the full memory load an atomic
+    // takes microseconds, and its wait drains the slice copies in flight),
+    // then the next item of the global counter.
     auto claim = [&]() -> int4 {
       unsigned j = 0;
-      if (lane == 0) j = __hip_atomic_fetch_add(P.item_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      j = static_cast<unsigned>(uni(static_cast<int>(j)));
+      if (claimed < P.n_static / P.grid) {
+        j = blockIdx.x + static_cast<unsigned>(claimed) * static_cast<unsigned>(P.grid);
+      } else {
+        if (lane == 0)
+          j = static_cast<unsigned>(P.n_static) + __hip_atomic_fetch_add(P.item_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        j = static_cast<unsigned>(uni(static_cast<int>(j)));
+      }
       int4 it = make_int4(-1, 0, 0, 0);
       if (j < static_cast<unsigned>(P.n_items)) {
         const BItem& I = P.items[j];
@@ -205,6 +222,7 @@ struct Pass {
       lds_publish(nknown, claimed);  // waits for the ring write first
       return it;
     };
+    constexpr int kOps = SliceShape<NG>::kOps, kEb = SliceShape<NG>::kExpBytes;  // kEb: a multiple of 16
     int4 cur = claim();
     int t = 0;
     while (cur.x >= 0) {
@@ -215,11 +233,11 @@ struct Pass {
       int4 nxt = make_int4(-1, 0, 0, 0);
       for (int j = 0; j < nsl; ++j, ++t) {
         if (j == (nsl > 1 ? nsl - 2 : 0)) nxt = claim();
-        if (t >= 2) {
+        if (t >= kBufs) {
           const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
           while (true) {
             const int d = (lane >= 1 && lane < kW) ? lds_acquire(&done[lane]) : t;
-            if (__all(d >= t - 2)) break;
+            if (__all(d >= t - kBufs)) break;
             if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
               late = true;
               break;
@@ -227,8 +245,7 @@ struct Pass {
             __builtin_amdgcn_s_sleep(1);
           }
         }
-        constexpr int kOps = SliceShape<NG>::kOps, kEb = SliceShape<NG>::kExpBytes;  // kEb: a multiple of 16
-        unsigned char* dst = smem + (t & 1) * kSliceBytes;
+        unsigned char* dst = smem + (t % kBufs) * kSliceBytes;
         const unsigned char* src = ops + static_cast<size_t>(j) * kOps;
         for (int o = 0; o < kOps; o += 1024)
           __builtin_amdgcn_global_load_lds(src + o + 16 * lane, (__attribute__((address_space(3))) void*)(dst + o), 16, 0, 0);
@@ -308,7 +325,7 @@ struct Pass {
         }
         __builtin_amdgcn_s_sleep(1);
       }
-      return smem + (t & 1) * kSliceBytes;
+      return smem + (t % kBufs) * kSliceBytes;
     };
 
     ngroups = set_item(S.cur);
@@ -376,7 +393,7 @@ __global__ __launch_bounds__(kThreads, 1) void bstep_kernel(const BPlan* __restr
   const int wave = uni(static_cast<int>(threadIdx.x >> 6));
   Pass<NG> pass(P, smem, lane, wave);
   unsigned long long* wkeys =
-      reinterpret_cast<unsigned long long*>(smem + 2 * SliceShape<NG>::kBytes + 64 + 16 * kRing);  // [kW][kB]
+      reinterpret_cast<unsigned long long*>(smem + slice_bufs<NG>() * SliceShape<NG>::kBytes + 64 + 16 * kRing);  // [kW][kB]
   if (threadIdx.x == 0) {
     *pass.ready = -1;
     *pass.nknown = 0;
@@ -618,6 +635,8 @@ int step_batch_plan(const pwg_step_desc* d, void* stream) {
   const std::vector<int2> conv = conv_table(d);
 
   h.n_items = static_cast<int>(items.size());
+  // three quarters of the items (whole rounds) round-robin, the rest claimed
+  h.n_static = static_cast<int>((3 * items.size() / 4) / grid) * grid;
   hipError_t e = hipMemsetAsync(dbase + lay.counters, 0, lay.levels - lay.counters, st);  // counters, partials, park
   if (e == hipSuccess) e = hipMemcpyAsync(dplan, &h, sizeof(BPlan), hipMemcpyHostToDevice, st);
   if (e == hipSuccess)
