@@ -16,9 +16,10 @@
 // or 7 of one ternary level (two or one per compute wave), which the seven
 // compute waves run over K in lock step with the arithmetic of the per-call
 // kernels, while a staging wave claims the next item and copies operand
-// slices into two or three LDS buffers.  Items come in a fixed order, the vocabulary
-// first and then the ternary levels widest K first, so that the last items
-// are the smallest and the workgroups finish close together.  The last
+// slices into two or three LDS buffers.  Items come in a fixed order,
+// largest first (ternary levels wider than h, the vocabulary, the other
+// ternary levels widest K first, halves of the last ones), so that the
+// workgroups finish close together.  The last
 // workgroup to arrive reduces the per-workgroup argmax keys into each
 // vector's token and resets the counters for the next pass.
 #include <algorithm>
@@ -415,8 +416,10 @@ __global__ __launch_bounds__(kThreads, 1) void bstep_kernel(const BPlan* __restr
     }
     WaveState S{0, 0, make_int4(-1, 0, 0, 0), false};
     S.cur = pass.wait_item(0, S.late);
-    pass.template phase<false>(wave - 1, S, best, bidx);  // the vocabulary's items come first
-    pass.template phase<true>(wave - 1, S, best, bidx);
+    while (S.cur.x >= 0) {  // runs of items of one kind
+      if (pass.kind_of(S.cur.x) == kKindInt8) pass.template phase<false>(wave - 1, S, best, bidx);
+      else pass.template phase<true>(wave - 1, S, best, bidx);
+    }
     late = S.late;
     lds_publish(&pass.done[wave], 0x7FFFFFFF);
     Compute<NG, false>(lane).wave_keys(best, bidx, wkeys + wave * kB);
@@ -439,18 +442,26 @@ __global__ __launch_bounds__(kThreads, 1) void bstep_kernel(const BPlan* __restr
       last = prev == static_cast<unsigned>(P.grid) - 1u ? 1u : 0u;
     }
     if (uni(static_cast<int>(last))) {
-      for (int b = 0; b < kB; ++b) {
-        unsigned long long m = 0ull;
-        for (int i = static_cast<int>(lane); i < P.grid; i += 64) {
+      // every vector's keys are loaded before any is reduced, so that the
+      // loads' latencies overlap
+      unsigned long long m[kB];
+#pragma unroll
+      for (int b = 0; b < kB; ++b) m[b] = 0ull;
+      for (int i = static_cast<int>(lane); i < P.grid; i += 64) {
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
           const unsigned long long o =
               __hip_atomic_load(&P.partials[static_cast<size_t>(b) * P.grid + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          m = o > m ? o : m;
+          m[b] = o > m[b] ? o : m[b];
         }
+      }
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
         for (int off = 32; off >= 1; off >>= 1) {
-          const unsigned long long o = __shfl_xor(m, off, kWave);
-          m = o > m ? o : m;
+          const unsigned long long o = __shfl_xor(m[b], off, kWave);
+          m[b] = o > m[b] ? o : m[b];
         }
-        if (lane == 0) P.token_out[b] = static_cast<int>(argmax_key_index(m));
+        if (lane == 0) P.token_out[b] = static_cast<int>(argmax_key_index(m[b]));
       }
       if (lane == 0) {
         // every workgroup has arrived, so nobody claims any more: reset for the next pass
@@ -465,9 +476,16 @@ __global__ __launch_bounds__(kThreads, 1) void bstep_kernel(const BPlan* __restr
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Row blocks per item: kR per compute wave (int8), kR per set and compute
-// wave (ternary).
+// wave (ternary).  Ternary items of wide levels take fewer sets, so that
+// every ternary item holds about the same bytes: kTernarySets sets at 4,096
+// columns, scaled by 4,096 / cols, even and at least 2 (the sets of an item
+// fill the compute waves' two register groups).
 constexpr int kVocabItemBlocks = kCW * Compute<1, false>::kR;
-constexpr int kTernaryItemBlocks = kCW * Compute<1, true>::kR * kTernarySets;
+int ternary_item_blocks(int64_t cols) {
+  int sets = static_cast<int>((kTernarySets * int64_t{4096} + cols / 2) / cols);
+  sets = std::max(2, std::min(kTernarySets, sets & ~1));
+  return kCW * Compute<1, true>::kR * sets;
+}
 
 struct BLayout {
   size_t plan, counters, partials, park, levels, items, conv, regions, total;
@@ -496,26 +514,31 @@ size_t conv_count(const pwg_step_desc* d) {
   return n;
 }
 
-// Claim order: the vocabulary's items, then the ternary levels' items widest
-// K first; the last `grid` ternary-item halves are separate items, so that
-// the final claims are small.
+// Claim order, largest items first: the items of ternary levels wider than
+// h (a ternary byte costs the matrix cores more than an int8 byte), the
+// vocabulary's, then the other ternary levels' widest K first; the last
+// `grid` ternary-item halves are separate items, so that the final claims
+// are small.
 std::vector<BItem> make_items(const pwg_step_desc* d, int grid) {
   std::vector<BItem> out;
   auto add = [&](int level, int64_t rows, int per) {
     const int nb = static_cast<int>((rows + 15) / 16);
     for (int b = 0; b < nb; b += per) out.push_back(BItem{level, b, std::min(nb, b + per), 0});
   };
-  add(d->n_levels, d->vocab, kVocabItemBlocks);
-  const size_t first_ternary = out.size();
   std::vector<int> order(d->n_levels);
   for (int i = 0; i < d->n_levels; ++i) order[i] = i;
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return d->levels[a].cols > d->levels[b].cols; });
-  for (int i : order) add(i, d->levels[i].rows, kTernaryItemBlocks);
+  for (int i : order)
+    if (d->levels[i].cols > d->hidden) add(i, d->levels[i].rows, ternary_item_blocks(d->levels[i].cols));
+  add(d->n_levels, d->vocab, kVocabItemBlocks);
+  const size_t first_ternary = out.size();
+  for (int i : order)
+    if (d->levels[i].cols <= d->hidden) add(i, d->levels[i].rows, ternary_item_blocks(d->levels[i].cols));
   const size_t n_split = std::min(out.size() - first_ternary, static_cast<size_t>(grid / 2));
   std::vector<BItem> tail(out.end() - n_split, out.end());
   out.resize(out.size() - n_split);
   for (const BItem& it : tail) {
-    const int mid = std::min(it.rb1, it.rb0 + kTernaryItemBlocks / 2);
+    const int mid = std::min(it.rb1, it.rb0 + ternary_item_blocks(d->levels[it.level].cols) / 2);
     out.push_back(BItem{it.level, it.rb0, mid, 0});
     if (mid < it.rb1) out.push_back(BItem{it.level, mid, it.rb1, 0});
   }
@@ -525,7 +548,8 @@ std::vector<BItem> make_items(const pwg_step_desc* d, int grid) {
 size_t count_items(const pwg_step_desc* d) {
   size_t n = static_cast<size_t>((d->vocab + 15) / 16 + kVocabItemBlocks - 1) / kVocabItemBlocks;
   for (int i = 0; i < d->n_levels; ++i)
-    n += static_cast<size_t>((d->levels[i].rows + 15) / 16 + kTernaryItemBlocks - 1) / kTernaryItemBlocks;
+    n += static_cast<size_t>((d->levels[i].rows + 15) / 16 + ternary_item_blocks(d->levels[i].cols) - 1) /
+         ternary_item_blocks(d->levels[i].cols);
   return 2 * n;  // an upper bound: items split in two at the end
 }
 
