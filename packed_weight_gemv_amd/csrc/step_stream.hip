@@ -33,9 +33,10 @@
 // compute waves claim blocks one at a time and stream their tiles through two
 // register groups (one group's loads in flight while the other is consumed,
 // across block, level and segment boundaries).  Wave 0 claims pool blocks
-// ahead into an LDS ring; wave 1 copies each segment's converted activation
-// operands into a ring of LDS regions ahead of the compute waves.  The last
-// workgroup to finish reduces the argmax.
+// ahead into an LDS ring and records which pool segments its claims fall
+// in; wave 1 copies the converted activation operands of each static
+// segment and of each claimed pool segment into a ring of LDS regions ahead
+// of the compute waves.  The last workgroup to finish reduces the argmax.
 #include <algorithm>
 #include <cmath>
 #include <vector>
