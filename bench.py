@@ -474,6 +474,13 @@ def main():
     ms_direct = time_direct(step_fn, stream, args.steps, args.warmup)
     pwg.step_status(wl.desc, stream=stream)
     log(f"{args.schedule} without a graph: {ms_direct * 1e3:.1f} us/step")
+    # four consecutive steps in one graph (each step's token feeds the next
+    # step's embedding row): the per-replay launch cost spread over four steps
+    graph4 = capture(lambda: [step_fn() for _ in range(4)], stream)
+    ms4 = time_graph(graph4, stream, max(1, args.steps // 4), max(1, args.warmup // 4)) / 4
+    del graph4
+    pwg.step_status(wl.desc, stream=stream)
+    log(f"{args.schedule}, four steps per graph: {ms4 * 1e3:.1f} us/step")
     kernels_per_step = {pwg.SCHEDULE_PERSISTENT: 1, pwg.SCHEDULE_STREAM: 2}.get(schedule, len(wl.desc.levels) + 3)
 
     extra = {}
@@ -536,6 +543,7 @@ def main():
     result.update(extra)
 
     result["us_per_step_without_graph"] = ms_direct * 1e3
+    result["us_per_step_four_steps_per_graph"] = ms4 * 1e3
     result["graph_replay_overhead_us"] = (ms - ms_direct) * 1e3
 
     # roofline of the dominant kernel: the step kernel moves every
