@@ -476,16 +476,9 @@ __global__ __launch_bounds__(kThreads, 1) void bstep_kernel(const BPlan* __restr
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Row blocks per item: kR per compute wave (int8), kR per set and compute
-// wave (ternary).  Ternary items of wide levels take fewer sets, so that
-// every ternary item holds about the same bytes: kTernarySets sets at 4,096
-// columns, scaled by 4,096 / cols, even and at least 2 (the sets of an item
-// fill the compute waves' two register groups).
+// wave (ternary).
 constexpr int kVocabItemBlocks = kCW * Compute<1, false>::kR;
-int ternary_item_blocks(int64_t cols) {
-  int sets = static_cast<int>((kTernarySets * int64_t{4096} + cols / 2) / cols);
-  sets = std::max(2, std::min(kTernarySets, sets & ~1));
-  return kCW * Compute<1, true>::kR * sets;
-}
+constexpr int kTernaryItemBlocks = kCW * Compute<1, true>::kR * kTernarySets;
 
 struct BLayout {
   size_t plan, counters, partials, park, levels, items, conv, regions, total;
@@ -529,16 +522,16 @@ std::vector<BItem> make_items(const pwg_step_desc* d, int grid) {
   for (int i = 0; i < d->n_levels; ++i) order[i] = i;
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return d->levels[a].cols > d->levels[b].cols; });
   for (int i : order)
-    if (d->levels[i].cols > d->hidden) add(i, d->levels[i].rows, ternary_item_blocks(d->levels[i].cols));
+    if (d->levels[i].cols > d->hidden) add(i, d->levels[i].rows, kTernaryItemBlocks);
   add(d->n_levels, d->vocab, kVocabItemBlocks);
   const size_t first_ternary = out.size();
   for (int i : order)
-    if (d->levels[i].cols <= d->hidden) add(i, d->levels[i].rows, ternary_item_blocks(d->levels[i].cols));
+    if (d->levels[i].cols <= d->hidden) add(i, d->levels[i].rows, kTernaryItemBlocks);
   const size_t n_split = std::min(out.size() - first_ternary, static_cast<size_t>(grid / 2));
   std::vector<BItem> tail(out.end() - n_split, out.end());
   out.resize(out.size() - n_split);
   for (const BItem& it : tail) {
-    const int mid = std::min(it.rb1, it.rb0 + ternary_item_blocks(d->levels[it.level].cols) / 2);
+    const int mid = std::min(it.rb1, it.rb0 + kTernaryItemBlocks / 2);
     out.push_back(BItem{it.level, it.rb0, mid, 0});
     if (mid < it.rb1) out.push_back(BItem{it.level, mid, it.rb1, 0});
   }
@@ -548,8 +541,7 @@ std::vector<BItem> make_items(const pwg_step_desc* d, int grid) {
 size_t count_items(const pwg_step_desc* d) {
   size_t n = static_cast<size_t>((d->vocab + 15) / 16 + kVocabItemBlocks - 1) / kVocabItemBlocks;
   for (int i = 0; i < d->n_levels; ++i)
-    n += static_cast<size_t>((d->levels[i].rows + 15) / 16 + ternary_item_blocks(d->levels[i].cols) - 1) /
-         ternary_item_blocks(d->levels[i].cols);
+    n += static_cast<size_t>((d->levels[i].rows + 15) / 16 + kTernaryItemBlocks - 1) / kTernaryItemBlocks;
   return 2 * n;  // an upper bound: items split in two at the end
 }
 
