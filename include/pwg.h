@@ -45,7 +45,7 @@ extern "C" {
 #endif
 #pragma GCC visibility push(default)
 
-#define PWG_VERSION 4
+#define PWG_VERSION 5
 #define PWG_MAX_COLS 16384
 
 enum {
@@ -257,6 +257,55 @@ int pwg_embed_gather(const int8_t* table, const float* row_scale,
                      int8_t* rows_out, float* scales_out, float* deq_out,
                      void* stream);
 
+/* How a level's input vector is formed when the level starts (chained step).
+ * Page "The Neutrino Engine", section "A 104 microsecond floor inside a 694
+ * microsecond step": a decoder layer applies its projections to the current
+ * activations, so each projection depends on the ones before it.  The pages
+ * do not give the operations between projections; these are the pre-norm
+ * decoder layer's (RMSNorm with a gain, grouped-query attention taken at the
+ * first position of a sequence, SwiGLU, residual adds).
+ *
+ * With any op other than PWG_INPUT_GIVEN the library WRITES the formed
+ * vector to the level's x (float32[cols]), then the level multiplies it;
+ * `src`, `resid` and `gamma` are device float32 vectors read during the
+ * step, `resid_out` (nullable) receives the residual sum.  In the formulas
+ * n = the level's cols:
+ *   PWG_INPUT_RMSNORM:        h = resid + src (src NULL: h = resid);
+ *                             x = gamma * h / sqrt(mean(h^2) + eps);
+ *   PWG_INPUT_EMBED_RMSNORM:  h = the step's dequantised embedding row of
+ *                             *token_in (emb_table[id][k] * emb_scale[id]),
+ *                             then as RMSNORM; resid and src unused;
+ *   PWG_INPUT_ATTN1:          x[i] = src[(i / (head_dim*group))*head_dim + i % head_dim]
+ *                             (each of n/head_dim query heads reads the value
+ *                             vector of key/value head (i/head_dim)/group:
+ *                             attention over one cached position, whose
+ *                             softmax weight is 1);
+ *   PWG_INPUT_SWIGLU:         x[i] = silu(src[i]) * src[n + i], silu(g) = g / (1 + e^-g)
+ *                             (src: the stacked gate|up output, gate first).
+ * Buffers may not overlap: x, resid_out, src, resid and gamma are distinct
+ * (PWG_ERR_ARG where pointers are equal).  Only the ordered schedules
+ * (LEVELS, PERSISTENT) at batch 1 take such levels (PWG_ERR_UNSUPPORTED
+ * otherwise).  Arithmetic is float32: the mean of squares is a float32 sum,
+ * the root and the quotient IEEE float32. */
+enum {
+  PWG_INPUT_GIVEN = 0,
+  PWG_INPUT_RMSNORM = 1,
+  PWG_INPUT_EMBED_RMSNORM = 2,
+  PWG_INPUT_ATTN1 = 3,
+  PWG_INPUT_SWIGLU = 4
+};
+
+typedef struct pwg_input {
+  int32_t op;            /* PWG_INPUT_* (0: x is used as given) */
+  int32_t head_dim;      /* ATTN1: values per head (n % (head_dim*group) == 0) */
+  int32_t group;         /* ATTN1: query heads per key/value head */
+  float eps;             /* RMSNORM, EMBED_RMSNORM: added to the mean of squares (>= 0) */
+  const float* src;      /* RMSNORM (nullable), ATTN1, SWIGLU (2n values) */
+  const float* resid;    /* RMSNORM: the residual stream, float32[n] */
+  const float* gamma;    /* RMSNORM, EMBED_RMSNORM: the gain, float32[n] */
+  float* resid_out;      /* RMSNORM, EMBED_RMSNORM: receives h (nullable) */
+} pwg_input;
+
 /* One ternary GEMV level of a decode step (matrices that share an input are
  * stacked by rows: q|k|v and gate|up). */
 typedef struct pwg_level {
@@ -266,6 +315,7 @@ typedef struct pwg_level {
   float* y;                /* device, float32[rows] */
   int64_t rows;
   int64_t cols;
+  pwg_input in;            /* how x is formed (zero-filled: x as given) */
 } pwg_level;
 
 /* Whole batch-1 decode step over the weights (page section "A 104
@@ -312,6 +362,8 @@ typedef struct pwg_step_desc {
   float* logits_out;             /* float32[vocab] or NULL */
   void* workspace;               /* >= pwg_step_workspace_bytes(desc) */
   size_t workspace_bytes;
+  pwg_input h_in;                /* how h is formed (zero-filled: h as given); with
+                                    another op the library writes h (hidden values) */
 } pwg_step_desc;
 
 /* Workspace bytes for a step description (depends on shapes and schedule). */

@@ -21,7 +21,8 @@ __all__ = [
     "argmax_workspace_bytes", "int8_gemv_argmax", "embed_gather", "Level", "StepDesc",
     "step_workspace_bytes", "step_plan", "decode_step_weights", "step_status", "last_error", "version",
     "tiled_size", "tile_rows", "SCHEDULE_LEVELS", "SCHEDULE_PERSISTENT", "SCHEDULE_STREAM",
-    "LAYOUT_ROWS", "LAYOUT_TILED", "layout_for_schedule", "LIB_PATH",
+    "LAYOUT_ROWS", "LAYOUT_TILED", "layout_for_schedule", "LIB_PATH", "InputOp", "INPUT_GIVEN",
+    "INPUT_RMSNORM", "INPUT_EMBED_RMSNORM", "INPUT_ATTN1", "INPUT_SWIGLU",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpwg.so")
@@ -34,6 +35,8 @@ SCHEDULE_PERSISTENT = 1
 SCHEDULE_STREAM = 2
 LAYOUT_ROWS = 0
 LAYOUT_TILED = 1
+# how a level's input is formed in a chained step (pwg.h, pwg_input)
+INPUT_GIVEN, INPUT_RMSNORM, INPUT_EMBED_RMSNORM, INPUT_ATTN1, INPUT_SWIGLU = 0, 1, 2, 3, 4
 
 
 def layout_for_schedule(schedule: int) -> int:
@@ -63,8 +66,14 @@ lib = C.CDLL(LIB_PATH)
 _i64, _i32, _sz, _vp = C.c_int64, C.c_int32, C.c_size_t, C.c_void_p
 
 
+class _Input(C.Structure):
+    _fields_ = [("op", _i32), ("head_dim", _i32), ("group", _i32), ("eps", C.c_float),
+                ("src", _vp), ("resid", _vp), ("gamma", _vp), ("resid_out", _vp)]
+
+
 class Level(C.Structure):
-    _fields_ = [("w_packed", _vp), ("row_scale", _vp), ("x", _vp), ("y", _vp), ("rows", _i64), ("cols", _i64)]
+    _fields_ = [("w_packed", _vp), ("row_scale", _vp), ("x", _vp), ("y", _vp), ("rows", _i64), ("cols", _i64),
+                ("input", _Input)]
 
 
 class _StepDesc(C.Structure):
@@ -74,7 +83,7 @@ class _StepDesc(C.Structure):
         ("out_table", _vp), ("out_scale", _vp), ("h", _vp), ("vocab", _i64), ("hidden", _i64),
         ("emb_table", _vp), ("emb_scale", _vp), ("token_in", _vp), ("token_out", _vp),
         ("emb_row_out", _vp), ("emb_scale_out", _vp), ("emb_deq_out", _vp), ("logits_out", _vp),
-        ("workspace", _vp), ("workspace_bytes", _sz),
+        ("workspace", _vp), ("workspace_bytes", _sz), ("h_in", _Input),
     ]
 
 
@@ -267,9 +276,27 @@ def tile_rows(src, rows: int, row_bytes: int, dst=None, stream=None):
 
 # ---------------------------------------------------------------- decode step
 @dataclass
+class InputOp:
+    """How a level's input (or h) is formed in a chained step; keeps its
+    tensors alive.  op: INPUT_*; see pwg.h for each op's formula."""
+    op: int
+    src: object = None
+    resid: object = None
+    gamma: object = None
+    resid_out: object = None
+    eps: float = 1e-6
+    head_dim: int = 0
+    group: int = 0
+
+    def c(self):
+        return _Input(self.op, self.head_dim, self.group, self.eps, _ptr(self.src), _ptr(self.resid),
+                      _ptr(self.gamma), _ptr(self.resid_out))
+
+
+@dataclass
 class StepDesc:
     """Python-side description of a decode step; keeps every tensor alive."""
-    levels: list            # [(w_packed, row_scale, x, y, rows, cols)]
+    levels: list            # [(w_packed, row_scale, x, y, rows, cols[, InputOp])]
     out_table: object
     out_scale: object
     h: object
@@ -287,14 +314,16 @@ class StepDesc:
     vocab: int | None = None        # rows of the output table (when it is stored tiled)
     hidden: int | None = None
     batch: int = 1                  # 4, 8, 16: batched pass (stream schedule); buffers hold batch rows
+    h_in: object = None             # InputOp forming h (chained step), or None: h as given
     _c: object = field(default=None, repr=False)
     _levels_c: object = field(default=None, repr=False)
 
     def c(self):
         if self._c is None:
             arr = (Level * max(1, len(self.levels)))()
-            for i, (w, s, x, y, r, k) in enumerate(self.levels):
-                arr[i] = Level(_ptr(w), _ptr(s), _ptr(x), _ptr(y), r, k)
+            for i, lv in enumerate(self.levels):
+                w, s, x, y, r, k = lv[:6]
+                arr[i] = Level(_ptr(w), _ptr(s), _ptr(x), _ptr(y), r, k, lv[6].c() if len(lv) > 6 else _Input())
             self._levels_c = arr
             vocab = self.vocab if self.vocab is not None else self.out_table.shape[0]
             hidden = self.hidden if self.hidden is not None else self.out_table.shape[1]
@@ -304,7 +333,8 @@ class StepDesc:
                 _ptr(self.out_table), _ptr(self.out_scale), _ptr(self.h), vocab, hidden,
                 _ptr(self.emb_table), _ptr(self.emb_scale), _ptr(self.token_in), _ptr(self.token_out),
                 _ptr(self.emb_row_out), _ptr(self.emb_scale_out), _ptr(self.emb_deq_out), _ptr(self.logits_out),
-                _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size())
+                _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                self.h_in.c() if self.h_in is not None else _Input())
         return self._c
 
 

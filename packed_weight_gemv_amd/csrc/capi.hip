@@ -168,6 +168,36 @@ namespace {
 
 bool batched(const pwg_step_desc* d) { return d->batch > 1; }
 
+bool chained(const pwg_input& in) { return in.op != PWG_INPUT_GIVEN; }
+
+constexpr int64_t kMaxFormedInput = 12288;
+
+// A level input op (pwg.h, pwg_input): n is the level's cols (hidden for h).
+int validate_input(const pwg_input& in, int64_t n, const float* x, const char* fn, const char* what) {
+  if (in.op == PWG_INPUT_GIVEN) return PWG_OK;
+  if (in.op < PWG_INPUT_GIVEN || in.op > PWG_INPUT_SWIGLU)
+    return fail(PWG_ERR_ARG, "%s: %s: unknown input op %d", fn, what, in.op);
+  if (n > kMaxFormedInput)
+    return fail(PWG_ERR_UNSUPPORTED, "%s: %s: formed inputs hold at most %d values", fn, what, kMaxFormedInput);
+  const void* bufs[5] = {x, in.resid_out, in.src, in.resid, in.gamma};
+  for (int a = 0; a < 5; ++a)
+    for (int b = a + 1; b < 5; ++b)
+      if (bufs[a] && bufs[a] == bufs[b]) return fail(PWG_ERR_ARG, "%s: %s: input buffers overlap", fn, what);
+  if (in.op == PWG_INPUT_RMSNORM || in.op == PWG_INPUT_EMBED_RMSNORM) {
+    if (!(in.eps >= 0.f) || in.eps > 1e30f) return fail(PWG_ERR_ARG, "%s: %s: eps must be >= 0", fn, what);
+    TRY(check_ptr(in.gamma, fn, "gamma"));
+    if (in.op == PWG_INPUT_RMSNORM) TRY(check_ptr(in.resid, fn, "resid"));
+  } else {
+    TRY(check_ptr(in.src, fn, "src"));
+    if (in.op == PWG_INPUT_ATTN1) {
+      if (in.head_dim < 1 || in.group < 1 || n % (static_cast<int64_t>(in.head_dim) * in.group) != 0)
+        return fail(PWG_ERR_ARG, "%s: %s: %lld values are not whole groups of %d heads of %d", fn, what,
+                    static_cast<long long>(n), in.group, in.head_dim);
+    }
+  }
+  return PWG_OK;
+}
+
 int validate_step(const pwg_step_desc* d) {
   const char* fn = "pwg_decode_step_weights";
   if (!d) return fail(PWG_ERR_ARG, "%s: desc is null", fn);
@@ -188,11 +218,18 @@ int validate_step(const pwg_step_desc* d) {
       return fail(PWG_ERR_UNSUPPORTED, "%s: batch %d takes the stream schedule", fn, d->batch);
   }
   if (d->n_levels > 0 && !d->levels) return fail(PWG_ERR_ARG, "%s: levels is null", fn);
+  bool any_chained = chained(d->h_in);
   for (int i = 0; i < d->n_levels; ++i) {
     const pwg_level& L = d->levels[i];
-    const int rc = validate_ternary(L.w_packed, L.row_scale, L.rows, L.cols, L.x, 1, L.y, fn);
+    int rc = validate_ternary(L.w_packed, L.row_scale, L.rows, L.cols, L.x, 1, L.y, fn);
+    if (rc == PWG_OK) rc = validate_input(L.in, L.cols, L.x, fn, "level input");
     if (rc != PWG_OK) return fail(rc, "%s (level %d)", pwg_last_error(), i);
+    any_chained = any_chained || chained(L.in);
   }
+  TRY(validate_input(d->h_in, d->hidden, d->h, fn, "h"));
+  if (any_chained && (d->schedule == PWG_SCHEDULE_STREAM || batched(d)))
+    return fail(PWG_ERR_UNSUPPORTED, "%s: formed level inputs need an ordered schedule (levels or persistent) at batch 1",
+                fn);
   if (d->schedule == PWG_SCHEDULE_STREAM) {
     TRY(check_shape(d->vocab, d->hidden, fn));
     TRY(check_ptr(d->out_table, fn, "out_table"));
@@ -260,8 +297,10 @@ extern "C" int pwg_decode_step_weights(const pwg_step_desc* d, void* stream) {
                           d->emb_scale_out, d->emb_deq_out, stream));
   for (int i = 0; i < d->n_levels; ++i) {
     const pwg_level& L = d->levels[i];
+    if (chained(L.in)) TRY(launch_chain_input(L.in, L.cols, const_cast<float*>(L.x), d, stream));
     TRY(launch_ternary_gemv(L.w_packed, L.row_scale, L.rows, L.cols, L.x, 1, L.y, stream));
   }
+  if (chained(d->h_in)) TRY(launch_chain_input(d->h_in, d->hidden, const_cast<float*>(d->h), d, stream));
   return launch_int8_gemv_argmax(d->out_table, d->out_scale, d->vocab, d->hidden, d->h, 1, d->workspace,
                                  d->token_out, d->logits_out, stream);
 }

@@ -55,6 +55,9 @@ int launch_i8b(const int8_t* table, bool tiled, const float* s, int64_t rows, in
                int32_t* token, void* stream);
 size_t t2_lds_bytes(int64_t cols);
 size_t i8_lds_bytes(int64_t cols);
+// Chained step, levels schedule (chain.hip): forms one level's input into x.
+int launch_chain_input(const pwg_input& in, int64_t n, float* x, const pwg_step_desc* d, void* stream);
+
 int launch_embed_gather(const int8_t* table, const float* s, int64_t rows, int64_t cols,
                         const int32_t* ids, int32_t n, int8_t* rows_out, float* scales_out,
                         float* deq_out, void* stream);

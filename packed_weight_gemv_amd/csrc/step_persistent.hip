@@ -26,6 +26,7 @@
 #include <cmath>
 #include <vector>
 
+#include "chain_input.h"
 #include "device_common.h"
 #include "pwg_internal.h"
 #include "t2_rows.h"
@@ -58,6 +59,7 @@ struct DevLevel {
   int cols;
   int nchunks;  // cols / 64
   int c;        // chunks per lane
+  chain::DevInput in;  // how x is formed (op 0: x as given)
 };
 
 // Device-side plan, written by pwg_step_plan into the workspace.  It is
@@ -83,6 +85,7 @@ struct alignas(256) Plan {
   float* emb_scale_out;
   float4* emb_deq_out;
   float* logits_out;
+  chain::DevInput h_in;  // how h is formed (op 0: h as given)
   // offsets (bytes from the plan) of the state words, barrier words, partial keys and level table
   unsigned long long state_off, counters_off, flags_off, partials_off, levels_off, calib_off;
 };
@@ -204,8 +207,9 @@ constexpr size_t kStageBytes = kMaxT2Cols * 4;
 constexpr size_t kPlaneBytes = static_cast<size_t>(kMaxT2Cols / 64) * (kT2ChunkDwords + 1) * 4;
 constexpr size_t kScaleBytes = 2 * kMaxWgRows * 4;
 constexpr size_t kOutBytes = kMaxWgRows * 4;              // a level's outputs of the workgroup
-// LDS: ring | raw input | planes | 2 x scales | outputs.
-constexpr size_t kStepSmem = kRingBytes + kStageBytes + kPlaneBytes + kScaleBytes + kOutBytes;
+constexpr size_t kRedBytes = 64;                          // input formation: per-wave partial sums
+// LDS: ring | raw input | planes | 2 x scales | outputs | partial sums.
+constexpr size_t kStepSmem = kRingBytes + kStageBytes + kPlaneBytes + kScaleBytes + kOutBytes + kRedBytes;
 
 #define PWG_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -625,6 +629,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restric
   unsigned* planes1 = reinterpret_cast<unsigned*>(smem + kRingBytes + kStageBytes);
   float* scale_buf = reinterpret_cast<float*>(smem + kRingBytes + kStageBytes + kPlaneBytes);
   float* out_buf = reinterpret_cast<float*>(smem + kRingBytes + kStageBytes + kPlaneBytes + kScaleBytes);
+  float* red = out_buf + kMaxWgRows;
 
   const Plan& P = *plan;
   Barrier bar;
@@ -659,8 +664,13 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restric
   pr.count = 0;
   unsigned consumed = 0;
 
+  // how each level's input is formed (op 0: staged as given); a formed
+  // input reads earlier outputs, so it is formed after the level barrier
+  auto input_of = [&](unsigned li) -> const chain::DevInput& { return li < P.n_levels ? levels[li].in : P.h_in; };
+  const chain::EmbedSrc emb{reinterpret_cast<const int8_t*>(P.emb_table), P.emb_scale, P.token_in,
+                            static_cast<long>(P.vocab)};
   if (wave == 0) {
-    stage_x(P, levels, 0, lane, stage);
+    if (input_of(0).op == PWG_INPUT_GIVEN) stage_x(P, levels, 0, lane, stage);
     stage_scales(P, levels, 0, lane, scale_buf);
     if (blockIdx.x == 0) embed_row(P, lane);
   } else {
@@ -683,12 +693,18 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restric
         if (bar.wait(li - 1)) return;
         if (wave == 0) {
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-          stage_x(P, levels, li, lane, stage);
+          if (input_of(li).op == PWG_INPUT_GIVEN) stage_x(P, levels, li, lane, stage);
         }
       }
       if (wave == 0) __builtin_amdgcn_s_waitcnt(0);  // this level's input and scales have landed
       __syncthreads();
       const int cols = vocab ? P.hidden : levels[li].cols;
+      // A formed input: every wave reads the sources after the barrier
+      // (the control wave's acquire above has invalidated this CU's and
+      // this XCD's stale lines before the workgroup barrier), and the
+      // workgroup forms the vector in the staging buffer.
+      const chain::DevInput& fin = input_of(li);
+      if (fin.op != PWG_INPUT_GIVEN) chain::form_input<kThreads>(fin, cols, stage, red, emb);
       int* plane_e = reinterpret_cast<int*>(planes1 + (vocab ? (cols >> 4) * kI8ChunkDwords : (cols >> 6) * kT2ChunkDwords));
       if (vocab) i8_prepare_x(stage, cols, planes1, plane_e);
       else t2_convert_staged(stage, cols, planes1, plane_e);
@@ -696,6 +712,11 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restric
       // functions; the planes are rewritten only after the block barrier below
       if (wave == 0) {
         if (li < P.n_levels) stage_scales(P, levels, li + 1, lane, scale_buf + ((li + 1) & 1u) * kMaxWgRows);
+        // workgroup 0 writes the formed input (and the residual sum); the
+        // release at this level's arrival publishes them
+        if (fin.op != PWG_INPUT_GIVEN && blockIdx.x == 0)
+          chain::store_formed(fin, cols, stage, const_cast<float*>(li < P.n_levels ? levels[li].x : P.h), emb,
+                              static_cast<int>(lane), 64);
       } else {
         consume_item<RS>(P, levels, li, R0, R1, k, scales, lane, pr, consumed, ring, planes1, out_buf, best, best_idx);
       }
@@ -875,6 +896,7 @@ int step_persistent_plan(const pwg_step_desc* d, size_t ws_offset, void* stream)
   h.emb_scale_out = d->emb_scale_out;
   h.emb_deq_out = reinterpret_cast<float4*>(d->emb_deq_out);
   h.logits_out = d->logits_out;
+  h.h_in = chain::from_abi(d->h_in);
   h.state_off = lay.state;
   h.counters_off = lay.counters;
   h.flags_off = lay.flags;
@@ -892,6 +914,7 @@ int step_persistent_plan(const pwg_step_desc* d, size_t ws_offset, void* stream)
     lv[i].cols = static_cast<int>(L.cols);
     lv[i].nchunks = static_cast<int>(L.cols / 64);
     lv[i].c = static_cast<int>((L.cols / 64 + 63) / 64);
+    lv[i].in = chain::from_abi(L.in);
   }
   e = hipMemcpyAsync(dplan, &h, sizeof(Plan), hipMemcpyHostToDevice, st);
   if (e == hipSuccess && d->n_levels > 0)

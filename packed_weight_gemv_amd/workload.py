@@ -15,8 +15,9 @@ import torch
 
 import synth
 
-from . import (LAYOUT_ROWS, LAYOUT_TILED, SCHEDULE_LEVELS, StepDesc, layout_for_schedule, pack_weights,
-               step_workspace_bytes, tile_rows)
+from . import (INPUT_ATTN1, INPUT_EMBED_RMSNORM, INPUT_RMSNORM, INPUT_SWIGLU, LAYOUT_ROWS, LAYOUT_TILED,
+               SCHEDULE_LEVELS, InputOp, StepDesc, layout_for_schedule, pack_weights, step_workspace_bytes,
+               tile_rows)
 
 LEVEL_NAMES = [name for name, _, _ in synth.LEVELS]
 
@@ -159,3 +160,80 @@ def build_step(n_layers: int = synth.N_LAYERS, shapes: dict | None = None, vocab
     return StepWorkload(desc=desc, level_shapes=shapes_out, samples=samples, out_table=out_t, emb_table=emb_t,
                         h=h, token0=token0, packed_bytes=packed_bytes, scale_bytes=scale_bytes,
                         weights={lay: (w_by_layout[lay], out_by_layout[lay]) for lay in layouts})
+
+
+@dataclass
+class ChainStep:
+    """A chained decode step over a StepWorkload's weights: every level's
+    input is formed from earlier outputs (pre-norm decoder layer, attention
+    at the first position).  Buffers are per level and per layer so every
+    intermediate can be read back."""
+    desc: StepDesc
+    x: list                 # formed input of each level (device)
+    y: list                 # output of each level (device)
+    h: list                 # per layer (h entering the layer, h after attention) (device)
+    h_final: object         # residual stream after the last layer (device)
+    gains: list             # per layer (attention gain, feed-forward gain) (host float32)
+    g_final: np.ndarray
+    head_dim: int
+    group: int
+    eps: float
+
+
+def make_chained(wl: StepWorkload, schedule: int = SCHEDULE_LEVELS, head_dim: int = synth.HEAD_DIM,
+                 eps: float = 1e-6, workload: int = synth.W_STEP) -> ChainStep:
+    """Chained step on the row-major weights of `wl` (levels qkv, o, gate_up,
+    down per layer).  The query rows are o's input width; the key and value
+    rows split the rest of qkv equally."""
+    d0 = wl.desc
+    dev = d0.out_scale.device
+    ws_rows, out_rows = wl.weights[LAYOUT_ROWS]
+    hidden = d0.hidden
+    n_layers = len(d0.levels) // 4
+    f32 = dict(dtype=torch.float32, device=dev)
+    levels, xs, ys, hs, gains = [], [], [], [], []
+    prev_mid = prev_down = None
+    for layer in range(n_layers):
+        lv = [d0.levels[4 * layer + j] for j in range(4)]
+        qkv_rows, q_rows, inter = lv[0][4], lv[1][5], lv[3][5]
+        kv_rows = (qkv_rows - q_rows) // 2
+        ga = synth.norm_gain(workload, layer, synth.GAIN_ATTN, hidden)
+        gm = synth.norm_gain(workload, layer, synth.GAIN_MLP, hidden)
+        gains.append((ga, gm))
+        x = [torch.empty(lv[j][5], **f32) for j in range(4)]
+        y = [torch.empty(lv[j][4], **f32) for j in range(4)]
+        h_l, h_mid = torch.empty(hidden, **f32), torch.empty(hidden, **f32)
+        g_attn, g_mlp = torch.from_numpy(ga).to(dev), torch.from_numpy(gm).to(dev)
+        if layer == 0:
+            op0 = InputOp(INPUT_EMBED_RMSNORM, gamma=g_attn, resid_out=h_l, eps=eps)
+        else:
+            op0 = InputOp(INPUT_RMSNORM, src=prev_down, resid=prev_mid, gamma=g_attn, resid_out=h_l, eps=eps)
+        ops = [op0,
+               InputOp(INPUT_ATTN1, src=y[0][q_rows + kv_rows:], head_dim=head_dim, group=q_rows // kv_rows),
+               InputOp(INPUT_RMSNORM, src=y[1], resid=h_l, gamma=g_mlp, resid_out=h_mid, eps=eps),
+               InputOp(INPUT_SWIGLU, src=y[2])]
+        assert y[2].numel() == 2 * inter
+        for j in range(4):
+            levels.append((ws_rows[4 * layer + j], lv[j][1], x[j], y[j], lv[j][4], lv[j][5], ops[j]))
+        xs.extend(x)
+        ys.extend(y)
+        hs.append((h_l, h_mid))
+        prev_mid, prev_down = h_mid, y[3]
+    gf = synth.norm_gain(workload, -1, synth.GAIN_FINAL, hidden)
+    h_final = torch.empty(hidden, **f32)
+    h_out = torch.empty(hidden, **f32)
+    desc = StepDesc(
+        levels=levels, out_table=out_rows, out_scale=d0.out_scale, h=h_out, emb_table=d0.emb_table,
+        emb_scale=d0.emb_scale, token_in=torch.tensor([wl.token0], dtype=torch.int32, device=dev),
+        token_out=None, emb_row_out=torch.empty(hidden, dtype=torch.int8, device=dev),
+        emb_scale_out=torch.empty(4, **f32), emb_deq_out=torch.empty(hidden, **f32),
+        logits_out=torch.empty(d0.vocab, **f32) if d0.logits_out is not None else None,
+        schedule=schedule, weight_layout=LAYOUT_ROWS, vocab=d0.vocab, hidden=hidden,
+        h_in=InputOp(INPUT_RMSNORM, src=prev_down, resid=prev_mid, gamma=torch.from_numpy(gf).to(dev),
+                     resid_out=h_final, eps=eps))
+    desc.token_out = desc.token_in
+    desc.workspace = torch.zeros(1, dtype=torch.uint8, device=dev)
+    desc.workspace = torch.zeros(max(step_workspace_bytes(desc), 16), dtype=torch.uint8, device=dev)
+    desc._c = None
+    return ChainStep(desc=desc, x=xs, y=ys, h=hs, h_final=h_final, gains=gains, g_final=gf,
+                     head_dim=head_dim, group=levels[4][6].group if n_layers else 1, eps=eps)

@@ -61,6 +61,9 @@ LEVELS = (
 
 # Workload ids used as the first element of every seed key.
 W_SINGLE, W_LAYER, W_VOCAB, W_STEP, W_BATCH = 1, 2, 3, 4, 5
+# Item ids of the chained step's RMSNorm gains: 200 (attention norm), 201
+# (feed-forward norm) inside a layer; the final norm is layer -1's item 202.
+GAIN_ATTN, GAIN_MLP, GAIN_FINAL = 200, 201, 202
 
 # Item ids inside a layer: 0..6 are the matrices, 100+i the level inputs.
 X_ITEM_BASE = 100
@@ -167,3 +170,9 @@ def parallel_map(fn, items):
     GIL for most of the drawing); results keep the order of ``items``."""
     with ThreadPoolExecutor(n_workers()) as ex:
         return list(ex.map(fn, items))
+
+
+def norm_gain(workload: int, layer: int, item: int, n: int) -> np.ndarray:
+    """RMSNorm gain of a chained step: float32 U[0.5, 1.5] (the pages give
+    none; trained gains sit around 1)."""
+    return uniform_f32(rng_for(workload, layer if layer >= 0 else 1_000_000, item), n, 0.5, 1.5)

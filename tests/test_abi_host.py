@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_error_string():
-    assert pwg.version() == 4
+    assert pwg.version() == 5
     assert isinstance(pwg.last_error(), str)
 
 
@@ -275,3 +275,55 @@ def test_tile_rows_argument_errors():
     assert f(MIS, 17, 128, A + (1 << 16), need, None) == ERR_ALIGN
     assert f(A, 17, 128, A + (1 << 16), need - 16, None) == ERR_SIZE
     assert f(A, 17, 128, A + 1024, need, None) == ERR_ARG and "overlap" in pwg.last_error()
+
+
+def test_chained_input_errors():
+    """Level inputs formed from earlier outputs (pwg_input): unknown ops,
+    missing sources, overlapping buffers, bad head grouping, a negative eps,
+    over-long inputs and the schedules that cannot order levels are refused
+    before anything is enqueued (every call here fails validation)."""
+    P = [A + 256 * k for k in range(8)]
+    d = pwg._StepDesc()
+    d.vocab, d.hidden = 1000, 4096
+    for name in ("out_table", "out_scale", "h", "emb_table", "emb_scale", "token_in", "token_out",
+                 "emb_row_out", "emb_scale_out", "workspace"):
+        setattr(d, name, A)
+    d.schedule, d.weight_layout = pwg.SCHEDULE_LEVELS, pwg.LAYOUT_ROWS
+    d.workspace_bytes = 1 << 30
+    lv = (pwg.Level * 1)(pwg.Level(P[0], P[1], P[2], P[3], 64, 4096))
+    d.n_levels, d.levels = 1, C.cast(lv, C.POINTER(pwg.Level))
+
+    def check(inp, code, text, level=True):
+        if level:
+            lv[0].input = inp
+        else:
+            d.h_in = inp
+        try:
+            assert pwg._step(C.byref(d), None) == code
+            assert text in pwg.last_error()
+            assert pwg._step_plan(C.byref(d), None) == code
+        finally:
+            lv[0].input = pwg._Input()
+            d.h_in = pwg._Input()
+
+    I = pwg._Input
+    check(I(9), ERR_ARG, "unknown input op")
+    check(I(-1), ERR_ARG, "unknown input op", level=False)
+    check(I(pwg.INPUT_RMSNORM, 0, 0, 1e-6, None, P[4], None, None), ERR_ARG, "gamma")
+    check(I(pwg.INPUT_RMSNORM, 0, 0, 1e-6, None, None, P[5], None), ERR_ARG, "resid")
+    check(I(pwg.INPUT_RMSNORM, 0, 0, -1.0, None, P[4], P[5], None), ERR_ARG, "eps")
+    check(I(pwg.INPUT_RMSNORM, 0, 0, float("nan"), None, P[4], P[5], None), ERR_ARG, "eps")
+    check(I(pwg.INPUT_RMSNORM, 0, 0, 1e-6, None, P[4], P[5], P[2]), ERR_ARG, "overlap")   # resid_out == x
+    check(I(pwg.INPUT_EMBED_RMSNORM, 0, 0, 1e-6, None, None, P[5], P[5]), ERR_ARG, "overlap")
+    check(I(pwg.INPUT_SWIGLU, 0, 0, 0.0, None, None, None, None), ERR_ARG, "src")
+    check(I(pwg.INPUT_ATTN1, 0, 4, 0.0, P[6], None, None, None), ERR_ARG, "heads")
+    check(I(pwg.INPUT_ATTN1, 128, 3, 0.0, P[6], None, None, None), ERR_ARG, "heads")    # 384 does not divide 4096
+    check(I(pwg.INPUT_ATTN1, 128, 4, 0.0, P[2], None, None, None), ERR_ARG, "overlap")  # src == x
+    # ordered schedules only, batch 1 only
+    d.schedule, d.weight_layout = pwg.SCHEDULE_STREAM, pwg.LAYOUT_TILED
+    d.workspace_bytes = 1 << 40
+    check(I(pwg.INPUT_SWIGLU, 0, 0, 0.0, P[6], None, None, None), ERR_UNSUPPORTED, "ordered schedule")
+    check(I(pwg.INPUT_RMSNORM, 0, 0, 1e-6, None, P[4], P[5], None), ERR_UNSUPPORTED, "ordered schedule", level=False)
+    d.schedule, d.weight_layout = pwg.SCHEDULE_PERSISTENT, pwg.LAYOUT_ROWS
+    lv[0] = pwg.Level(P[0], P[1], P[2], P[3], 64, 16384)
+    check(I(pwg.INPUT_SWIGLU, 0, 0, 0.0, P[6], None, None, None), ERR_UNSUPPORTED, "at most 12288")
