@@ -369,7 +369,7 @@ def main():
 
     import packed_weight_gemv_amd as pwg
     from oracle import reference as ref
-    from packed_weight_gemv_amd.workload import build_step
+    from packed_weight_gemv_amd.workload import build_step, make_chained
 
     assert torch.cuda.is_available(), "bench needs a GPU"
     schedule = {"persistent": pwg.SCHEDULE_PERSISTENT, "levels": pwg.SCHEDULE_LEVELS,
@@ -507,6 +507,33 @@ def main():
         ms_null = time_graph(gnull, stream, args.steps, args.warmup)
         extra["null_graph_us"] = ms_null * 1e3
         extra["null_graph_kernels"] = n_null
+        # chained step: every level's input formed from earlier outputs
+        # (RMSNorm, one-position attention, SwiGLU, residual sums) on the two
+        # ordered schedules, the dependency chain the stream step leaves out
+        cs = make_chained(wl, schedule=pwg.SCHEDULE_LEVELS)
+        for sched_c in (pwg.SCHEDULE_LEVELS, pwg.SCHEDULE_PERSISTENT):
+            cs.desc.schedule = sched_c
+            cs.desc._c = None
+            need = pwg.step_workspace_bytes(cs.desc)
+            if cs.desc.workspace.numel() < need:
+                cs.desc.workspace = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+                cs.desc._c = None
+            pwg.step_plan(cs.desc, stream=stream)
+            chain_fn = lambda: pwg.decode_step_weights(cs.desc, stream=stream)  # noqa: E731
+            with torch.cuda.stream(stream):
+                chain_fn()
+                stream.synchronize()
+            pwg.step_status(cs.desc, stream=stream)
+            tok = int(cs.desc.token_out.cpu()[0])
+            if not (0 <= tok < wl.desc.vocab and bool(torch.isfinite(cs.desc.h).all())):
+                raise SystemExit(f"chained step produced token {tok} / non-finite hidden state")
+            g3 = capture(chain_fn, stream)
+            ms_chain = time_graph(g3, stream, args.steps, args.warmup)
+            pwg.step_status(cs.desc, stream=stream)
+            del g3
+            extra[f"chained_{names[sched_c]}_us"] = ms_chain * 1e3
+            log(f"chained step, {names[sched_c]} schedule: {ms_chain * 1e3:.1f} us/step")
+        del cs
         run(schedule)  # restore the timed schedule's plan
 
     achieved_bps = step_bytes / (ms * 1e-3)

@@ -1,4 +1,4 @@
-// Input formation of a chained step on the levels schedule: one workgroup
+// Input formation of a chained step on the levels schedule: a small kernel
 // forms a level's input (RMSNorm with a gain, one-position grouped-query
 // attention or SwiGLU, with the residual sum) and writes it to the level's x
 // before the level's GEMV runs (page "The Neutrino Engine", section "A 104
@@ -13,12 +13,16 @@ namespace {
 
 constexpr int kChainThreads = 512;  // the persistent kernel's workgroup size: both schedules reduce in one order
 
+// Workgroup b writes elements [b * kChainThreads, (b + 1) * kChainThreads)
+// of the formed vector; for a norm it forms all of it (the sum of squares
+// needs every element), for the other ops only its own elements.
 __global__ __launch_bounds__(kChainThreads) void chain_input_kernel(chain::DevInput in, int n, float* x,
                                                                     chain::EmbedSrc e) {
   extern __shared__ __align__(16) float v[];
   float* red = v + n;
-  chain::form_input<kChainThreads>(in, n, v, red, e);
-  chain::store_formed(in, n, v, x, e, threadIdx.x, kChainThreads);
+  const int lo = blockIdx.x * kChainThreads, hi = lo + kChainThreads < n ? lo + kChainThreads : n;
+  chain::form_input<kChainThreads>(in, n, v, red, e, lo, hi);
+  chain::store_formed(in, n, v, x, e, lo, hi, threadIdx.x, kChainThreads);
 }
 
 }  // namespace
@@ -27,7 +31,8 @@ int launch_chain_input(const pwg_input& in, int64_t n, float* x, const pwg_step_
   const chain::DevInput di = chain::from_abi(in);
   const chain::EmbedSrc e{d->emb_table, d->emb_scale, d->token_in, static_cast<long>(d->vocab)};
   const size_t lds = static_cast<size_t>(n) * 4 + (kChainThreads / 64 + 1) * 4;
-  hipLaunchKernelGGL(chain_input_kernel, dim3(1), dim3(kChainThreads), lds, reinterpret_cast<hipStream_t>(stream), di,
+  const unsigned grid = static_cast<unsigned>((n + kChainThreads - 1) / kChainThreads);
+  hipLaunchKernelGGL(chain_input_kernel, dim3(grid), dim3(kChainThreads), lds, reinterpret_cast<hipStream_t>(stream), di,
                      static_cast<int>(n), x, e);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(PWG_ERR_HIP, "chain input launch: %s", hipGetErrorString(err));

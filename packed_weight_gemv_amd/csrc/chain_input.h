@@ -63,33 +63,95 @@ __device__ __forceinline__ void embed_row(const EmbedSrc& e, int n, const int8_t
 
 // Every thread of the workgroup (T threads) calls this; `v` is LDS
 // float[n], `red` LDS float[T / 64 + 1].  On return (after a workgroup
-// barrier) v holds the formed input.
+// barrier) v holds the formed input: all of it for the norm ops (whose sum
+// of squares needs every element), elements [lo, hi) for the others.  Loads are issued in batches of kU per
+// thread before any of them is used, so a batch costs one memory round trip
+// (the sources were just written by other CUs and come from HBM).
+constexpr int kU = 8;
+
 template <int T>
-__device__ __forceinline__ void form_input(const DevInput& in, int n, float* v, float* red, const EmbedSrc& e) {
+__device__ __forceinline__ void form_input(const DevInput& in, int n, float* v, float* red, const EmbedSrc& e,
+                                           int lo, int hi) {
   const int tid = threadIdx.x;
   if (in.op == PWG_INPUT_ATTN1) {
     const int span = in.head_dim * in.group;
-    for (int i = tid; i < n; i += T) v[i] = in.src[(i / span) * in.head_dim + i % in.head_dim];
-    __syncthreads();
-    return;
-  }
-  if (in.op == PWG_INPUT_SWIGLU) {
-    for (int i = tid; i < n; i += T) {
-      const float g = in.src[i];
-      v[i] = g / (1.0f + expf(-g)) * in.src[n + i];
+    for (int base = lo; base < hi; base += kU * T) {
+      float a[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = base + u * T + tid;
+        a[u] = i < hi ? in.src[(i / span) * in.head_dim + i % in.head_dim] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = base + u * T + tid;
+        if (i < hi) v[i] = a[u];
+      }
     }
     __syncthreads();
     return;
   }
-  // RMSNORM / EMBED_RMSNORM
+  if (in.op == PWG_INPUT_SWIGLU) {
+    for (int base = lo; base < hi; base += kU * T) {
+      float g[kU], up[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = base + u * T + tid;
+        g[u] = i < hi ? in.src[i] : 0.f;
+        up[u] = i < hi ? in.src[n + i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = base + u * T + tid;
+        if (i < hi) v[i] = g[u] / (1.0f + expf(-g[u])) * up[u];
+      }
+    }
+    __syncthreads();
+    return;
+  }
+  // RMSNORM / EMBED_RMSNORM: v holds gamma * h until the sum of squares of
+  // h is known, then the product is scaled by 1 / sqrt(mean + eps).
   const int8_t* row = nullptr;
   float s = 0.f;
   if (in.op == PWG_INPUT_EMBED_RMSNORM) embed_row(e, n, row, s);
   float acc = 0.f;
-  for (int i = tid; i < n; i += T) {
-    const float h = norm_value(in, i, row, s);
-    v[i] = h;
-    acc = fmaf(h, h, acc);
+  for (int base = 0; base < n; base += kU * T) {
+    float h[kU], gm[kU];
+    if (in.op == PWG_INPUT_EMBED_RMSNORM) {
+      int q[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = base + u * T + tid;
+        q[u] = (i < n && row) ? static_cast<int>(row[i]) : 0;
+        gm[u] = i < n ? in.gamma[i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) h[u] = static_cast<float>(q[u]) * s;
+    } else if (in.src) {
+      float r[kU], a[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = base + u * T + tid;
+        r[u] = i < n ? in.resid[i] : 0.f;
+        a[u] = i < n ? in.src[i] : 0.f;
+        gm[u] = i < n ? in.gamma[i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) h[u] = r[u] + a[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = base + u * T + tid;
+        h[u] = i < n ? in.resid[i] : 0.f;
+        gm[u] = i < n ? in.gamma[i] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = base + u * T + tid;
+      if (i < n) v[i] = gm[u] * h[u];
+      acc = fmaf(h[u], h[u], acc);  // lanes past the end add 0
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
@@ -102,21 +164,35 @@ __device__ __forceinline__ void form_input(const DevInput& in, int n, float* v, 
   }
   __syncthreads();
   const float inv = red[T / 64];
-  for (int i = tid; i < n; i += T) v[i] = in.gamma[i] * v[i] * inv;
+  for (int i = tid; i < n; i += T) v[i] *= inv;
   __syncthreads();
 }
 
-// Writes the formed input v (LDS) to x and, for the norm ops, h to
-// resid_out.  Called by `nt` threads with index t (a whole workgroup, or one
-// wave); h is recomputed from its sources, which form_input only read.
+// Writes elements [lo, hi) of the formed input v (LDS) to x and, for the
+// norm ops, of h to resid_out.  Called by `nt` threads with index t; h is
+// recomputed from its sources (form_input only read them), with each
+// thread's loads of a batch issued before its stores.
 __device__ __forceinline__ void store_formed(const DevInput& in, int n, const float* v, float* x, const EmbedSrc& e,
-                                             int t, int nt) {
-  for (int i = t; i < n; i += nt) x[i] = v[i];
-  if ((in.op == PWG_INPUT_RMSNORM || in.op == PWG_INPUT_EMBED_RMSNORM) && in.resid_out) {
-    const int8_t* row = nullptr;
-    float s = 0.f;
-    if (in.op == PWG_INPUT_EMBED_RMSNORM) embed_row(e, n, row, s);
-    for (int i = t; i < n; i += nt) in.resid_out[i] = norm_value(in, i, row, s);
+                                             int lo, int hi, int t, int nt) {
+  const bool norm = (in.op == PWG_INPUT_RMSNORM || in.op == PWG_INPUT_EMBED_RMSNORM) && in.resid_out;
+  const int8_t* row = nullptr;
+  float s = 0.f;
+  if (norm && in.op == PWG_INPUT_EMBED_RMSNORM) embed_row(e, n, row, s);
+  for (int base = lo; base < hi; base += kU * nt) {
+    float h[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = base + u * nt + t;
+      h[u] = (norm && i < hi) ? norm_value(in, i, row, s) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = base + u * nt + t;
+      if (i < hi) {
+        x[i] = v[i];
+        if (norm) in.resid_out[i] = h[u];
+      }
+    }
   }
 }
 

@@ -704,7 +704,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restric
       // this XCD's stale lines before the workgroup barrier), and the
       // workgroup forms the vector in the staging buffer.
       const chain::DevInput& fin = input_of(li);
-      if (fin.op != PWG_INPUT_GIVEN) chain::form_input<kThreads>(fin, cols, stage, red, emb);
+      if (fin.op != PWG_INPUT_GIVEN) chain::form_input<kThreads>(fin, cols, stage, red, emb, 0, cols);
       int* plane_e = reinterpret_cast<int*>(planes1 + (vocab ? (cols >> 4) * kI8ChunkDwords : (cols >> 6) * kT2ChunkDwords));
       if (vocab) i8_prepare_x(stage, cols, planes1, plane_e);
       else t2_convert_staged(stage, cols, planes1, plane_e);
@@ -712,10 +712,12 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(const Plan* __restric
       // functions; the planes are rewritten only after the block barrier below
       if (wave == 0) {
         if (li < P.n_levels) stage_scales(P, levels, li + 1, lane, scale_buf + ((li + 1) & 1u) * kMaxWgRows);
-        // workgroup 0 writes the formed input (and the residual sum); the
-        // release at this level's arrival publishes them
-        if (fin.op != PWG_INPUT_GIVEN && blockIdx.x == 0)
+        // every workgroup writes its slice of the formed input (and of the
+        // residual sum); the release at this level's arrival publishes them
+        if (fin.op != PWG_INPUT_GIVEN)
           chain::store_formed(fin, cols, stage, const_cast<float*>(li < P.n_levels ? levels[li].x : P.h), emb,
+                              static_cast<int>(blockIdx.x * static_cast<unsigned>(cols) / P.grid),
+                              static_cast<int>((blockIdx.x + 1) * static_cast<unsigned>(cols) / P.grid),
                               static_cast<int>(lane), 64);
       } else {
         consume_item<RS>(P, levels, li, R0, R1, k, scales, lane, pr, consumed, ring, planes1, out_buf, best, best_idx);
