@@ -11,6 +11,8 @@ specification for the packed-byte decoder/encoder:
 * ``reference``       - ternary GEMV with row scales, int8 vocabulary GEMV,
                         greedy argmax, embedding-row gather, the decode-step
                         composition;
+* ``attention``       - grouped-query decode attention over a bfloat16
+                        key/value cache;
 * ``chain``           - the chained decode step: RMSNorm, one-position
                         grouped-query attention, SwiGLU and residual adds
                         between the projections;
@@ -22,4 +24,4 @@ Parity status of each function is stated in its module.  One part is
 name it but never specify it), so the build's 2-bit format is pinned only by
 its own specification and round trips, not by the pages.
 """
-from . import accounting, chain, packed_format, reference  # noqa: F401
+from . import accounting, attention, chain, packed_format, reference  # noqa: F401

@@ -176,3 +176,24 @@ def norm_gain(workload: int, layer: int, item: int, n: int) -> np.ndarray:
     """RMSNorm gain of a chained step: float32 U[0.5, 1.5] (the pages give
     none; trained gains sit around 1)."""
     return uniform_f32(rng_for(workload, layer if layer >= 0 else 1_000_000, item), n, 0.5, 1.5)
+
+
+W_ATTN = 6  # workload id of the decode-attention inputs
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest even (input
+    generation only; finite inputs)."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def kv_cache(layer: int, ctx: int, n_kv: int = KV_HEADS, head_dim: int = HEAD_DIM, seed: int = 0):
+    """One layer's bfloat16 key and value caches [ctx, n_kv, head_dim] of
+    N(0,1) values, and an N(0,1) float32 query for 4 query heads per
+    key/value head."""
+    rng = rng_for(W_ATTN, seed, layer)
+    k = bf16_bits(rng.standard_normal((ctx, n_kv, head_dim)).astype(np.float32))
+    v = bf16_bits(rng.standard_normal((ctx, n_kv, head_dim)).astype(np.float32))
+    q = rng.standard_normal(4 * n_kv * head_dim).astype(np.float32)
+    return q, k, v
