@@ -45,7 +45,7 @@ extern "C" {
 #endif
 #pragma GCC visibility push(default)
 
-#define PWG_VERSION 5
+#define PWG_VERSION 6
 #define PWG_MAX_COLS 16384
 
 enum {
@@ -399,6 +399,30 @@ int pwg_step_status(const pwg_step_desc* desc, void* stream);
 
 /* Thread-local message of the last failed call on this thread ("" if none). */
 const char* pwg_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Grouped-query decode attention over a bfloat16 key/value cache (one layer,
+ * one new token).  Page "The Neutrino Engine", KV-cache section: 8 key/value
+ * heads of 128 values per layer, 2 bytes per value for keys and for values;
+ * every cached position is read once per token.
+ *   out[j*head_dim + d] = sum_t p_jt * V[t][j/group][d],
+ *   p_jt = softmax over t of scale * sum_d q[j*head_dim + d] * K[t][j/group][d],
+ * for query heads j < n_heads, group = n_heads / n_kv.
+ *   k_cache, v_cache: device bfloat16 bit patterns (the upper half of a
+ *       float32), position-major [ctx][n_kv][head_dim];
+ *   q: device float32[n_heads*head_dim]; out: device float32[n_heads*head_dim];
+ *   workspace: device, >= pwg_attention_workspace_bytes(...) bytes, ZERO-FILLED
+ *       before its first use; each call leaves it zero-filled again (its
+ *       arrival counters), so calls on one workspace must not overlap.
+ * Every pointer is 16-byte aligned (PWG_ERR_ALIGN), none null (PWG_ERR_ARG).
+ * Accumulation is float32 (online softmax in base 2, partial results per
+ * range of positions merged at the end).  Supported: head_dim 64 or 128 and
+ * group 1, 2 or 4 (PWG_ERR_UNSUPPORTED otherwise); ctx >= 1 (PWG_ERR_ARG);
+ * scale finite. */
+size_t pwg_attention_workspace_bytes(int32_t n_heads, int32_t n_kv, int32_t head_dim, int64_t ctx);
+int pwg_gqa_decode_attention(const uint16_t* k_cache, const uint16_t* v_cache, const float* q,
+                             int32_t n_heads, int32_t n_kv, int32_t head_dim, int64_t ctx, float scale,
+                             float* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* PWG_VERSION of the built library. */
 int pwg_version(void);

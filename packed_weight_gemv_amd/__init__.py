@@ -22,7 +22,8 @@ __all__ = [
     "step_workspace_bytes", "step_plan", "decode_step_weights", "step_status", "last_error", "version",
     "tiled_size", "tile_rows", "SCHEDULE_LEVELS", "SCHEDULE_PERSISTENT", "SCHEDULE_STREAM",
     "LAYOUT_ROWS", "LAYOUT_TILED", "layout_for_schedule", "LIB_PATH", "InputOp", "INPUT_GIVEN",
-    "INPUT_RMSNORM", "INPUT_EMBED_RMSNORM", "INPUT_ATTN1", "INPUT_SWIGLU",
+    "INPUT_RMSNORM", "INPUT_EMBED_RMSNORM", "INPUT_ATTN1", "INPUT_SWIGLU", "attention_workspace_bytes",
+    "gqa_decode_attention",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpwg.so")
@@ -97,6 +98,9 @@ def _sig(name, restype, *argtypes):
 _packed_size = _sig("pwg_packed_size", _sz, _i64, _i64)
 _pack = _sig("pwg_pack_weights", C.c_int, _vp, _i64, _i64, _vp, _sz, C.POINTER(_sz))
 _unpack = _sig("pwg_unpack_weights", C.c_int, _vp, _i64, _i64, _vp)
+_attn_ws = _sig("pwg_attention_workspace_bytes", _sz, _i32, _i32, _i32, _i64)
+_attn = _sig("pwg_gqa_decode_attention", C.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _i64, C.c_float, _vp, _vp, _sz,
+             _vp)
 _tgemv = _sig("pwg_ternary_gemv", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp)
 _argmax_ws = _sig("pwg_argmax_workspace_bytes", _sz, _i64, _i32)
 _i8argmax = _sig("pwg_int8_gemv_argmax", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _sz, _vp, _vp, _vp)
@@ -118,7 +122,8 @@ EXPORTED = ["pwg_packed_size", "pwg_pack_weights", "pwg_unpack_weights", "pwg_te
             "pwg_tiled_size", "pwg_tile_rows", "pwg_batch_workspace_bytes", "pwg_ternary_gemv_tiled",
             "pwg_int8_gemv_argmax_tiled",
             "pwg_step_workspace_bytes", "pwg_step_plan", "pwg_decode_step_weights",
-            "pwg_step_status", "pwg_last_error", "pwg_version"]
+            "pwg_step_status", "pwg_last_error", "pwg_version", "pwg_attention_workspace_bytes",
+            "pwg_gqa_decode_attention"]
 
 
 def last_error() -> str:
@@ -222,6 +227,29 @@ def embed_gather(table, row_scale, ids, rows_out=None, scales_out=None, deq_out=
     _check(_gather(_ptr(table), _ptr(row_scale), rows, cols, _ptr(ids), n, _ptr(rows_out), _ptr(scales_out),
                    _ptr(deq_out) if dequant else None, _stream(stream)))
     return rows_out, scales_out[:n], (deq_out if dequant else None)
+
+
+# ---------------------------------------------------------------- decode attention
+def attention_workspace_bytes(n_heads: int, n_kv: int, head_dim: int, ctx: int) -> int:
+    return _attn_ws(n_heads, n_kv, head_dim, ctx)
+
+
+def gqa_decode_attention(k_cache, v_cache, q, n_heads: int, n_kv: int, head_dim: int, scale: float, out=None,
+                         workspace=None, stream=None):
+    """One layer's grouped-query decode attention; k_cache, v_cache: int16 or
+    uint16 tensors of bfloat16 bits [ctx, n_kv, head_dim] on the device.  A
+    workspace passed in must be zero-filled before its first use (each call
+    leaves it so)."""
+    import torch
+    ctx = k_cache.shape[0]
+    if out is None:
+        out = torch.empty(n_heads * head_dim, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.zeros(max(16, attention_workspace_bytes(n_heads, n_kv, head_dim, ctx)), dtype=torch.uint8,
+                                device=q.device)
+    _check(_attn(_ptr(k_cache), _ptr(v_cache), _ptr(q), n_heads, n_kv, head_dim, ctx, scale, _ptr(out),
+                 _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
 
 
 # ---------------------------------------------------------------- tiled arrangement

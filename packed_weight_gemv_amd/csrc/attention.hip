@@ -1,0 +1,268 @@
+// Grouped-query decode attention over a bfloat16 key/value cache.
+//
+// Page "The Neutrino Engine", KV-cache section: per layer the cache holds 8
+// key/value heads of 128 values, 2 bytes each for keys and values, and every
+// cached position is read once per generated token, so at long contexts the
+// cache, not the weights, is the larger stream.  One call is one layer:
+// out_j = sum_t softmax_t(scale * q_j . k_t) v_t for every query head j,
+// query head j reading key/value head j / group.
+//
+// The kernel is an HBM stream over K and V: workgroup (split, kv) takes a
+// contiguous range of positions of one key/value head; inside it 16-byte
+// lane loads cover 8 values of one position's key (or value) row, HD/8 lanes
+// a row, so one wave load reads 64/(HD/8) positions.  Each lane group keeps
+// a running maximum, normaliser and weighted value sum per query head of the
+// group (online softmax in base 2, the query pre-scaled by scale * log2 e),
+// taking U positions per step so the K and V loads of U positions are in
+// flight together.  The lane groups are merged through LDS, each workgroup
+// writes one partial (maximum, normaliser, sum) per query head, and the last
+// workgroup of a key/value head (an arrival counter in the workspace, reset
+// by that workgroup) merges the splits into the output.
+#include <cmath>
+
+#include "device_common.h"
+#include "pwg_internal.h"
+
+namespace pwg {
+namespace {
+
+constexpr int kAttnThreads = 256;
+constexpr int kAttnU = 4;  // positions per lane group per step
+
+struct AttnArgs {
+  const dev::u32x4* k;
+  const dev::u32x4* v;
+  const float* q;
+  float* out;
+  float* part;            // [n_heads][splits][HD] weighted sums
+  float2* part_ml;        // [n_heads][splits] (maximum, normaliser)
+  unsigned* arrivals;     // [n_kv]
+  int n_kv, splits, per;  // positions per split
+  long ctx;
+  float qscale;           // scale * log2(e)
+};
+
+__device__ __forceinline__ float lo_bf16(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(unsigned w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int HD, int G>
+__global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnArgs a) {
+  constexpr int L = HD / 8;                   // lanes per row
+  constexpr int P = 64 / L;                   // rows per wave load
+  constexpr int NGR = (kAttnThreads / 64) * P;  // lane groups per workgroup
+  __shared__ float sm_ml[NGR][G][2];
+  __shared__ float sm_acc[NGR][G][HD];
+  __shared__ int sm_last;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane % L, r = wave * P + lane / L;
+  const int split = blockIdx.x, kvh = blockIdx.y;
+  const long t0 = static_cast<long>(split) * a.per;
+  const long t1 = t0 + a.per < a.ctx ? t0 + a.per : a.ctx;
+  const long npos = t1 - t0;
+
+  float q[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[g][i] = a.q[(kvh * G + g) * HD + 8 * sub + i] * a.qscale;
+
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
+  }
+
+  const long row_stride = static_cast<long>(a.n_kv) * L;  // uint4 per position
+  const long trips = (npos + NGR * kAttnU - 1) / (NGR * kAttnU);  // uniform over the workgroup
+  for (long it = 0; it < trips; ++it) {
+    dev::u32x4 kw[kAttnU], vw[kAttnU];
+    bool valid[kAttnU];
+#pragma unroll
+    for (int u = 0; u < kAttnU; ++u) {
+      const long t = t0 + (it * kAttnU + u) * NGR + r;
+      valid[u] = t < t1;
+      // positions past the range read row 0 (in bounds) and are discarded
+      const long idx = (valid[u] ? t * row_stride : 0) + static_cast<long>(kvh) * L + sub;
+      const dev::u32x4 zero = {0u, 0u, 0u, 0u};
+      const dev::u32x4 kl = __builtin_nontemporal_load(a.k + idx);
+      const dev::u32x4 vl = __builtin_nontemporal_load(a.v + idx);
+      kw[u] = valid[u] ? kl : zero;
+      vw[u] = valid[u] ? vl : zero;
+    }
+    float s[G][kAttnU];
+#pragma unroll
+    for (int u = 0; u < kAttnU; ++u) {
+      const unsigned w[4] = {kw[u].x, kw[u].y, kw[u].z, kw[u].w};
+      float kf[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kf[2 * i] = lo_bf16(w[i]);
+        kf[2 * i + 1] = hi_bf16(w[i]);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float d = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d = fmaf(q[g][i], kf[i], d);
+#pragma unroll
+        for (int o = L / 2; o > 0; o >>= 1) d += __shfl_xor(d, o, 64);
+        s[g][u] = valid[u] ? d : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mx = m[g];
+#pragma unroll
+      for (int u = 0; u < kAttnU; ++u) mx = fmaxf(mx, s[g][u]);
+      const float corr = mx == -INFINITY ? 1.f : exp2f(m[g] - mx);
+      l[g] *= corr;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[g][i] *= corr;
+#pragma unroll
+      for (int u = 0; u < kAttnU; ++u) {
+        const float p = valid[u] ? exp2f(s[g][u] - mx) : 0.f;
+        l[g] += p;
+        const unsigned w[4] = {vw[u].x, vw[u].y, vw[u].z, vw[u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[g][2 * i] = fmaf(p, lo_bf16(w[i]), acc[g][2 * i]);
+          acc[g][2 * i + 1] = fmaf(p, hi_bf16(w[i]), acc[g][2 * i + 1]);
+        }
+      }
+      m[g] = mx;
+    }
+  }
+
+  // merge the lane groups of the workgroup
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (sub == 0) {
+      sm_ml[r][g][0] = m[g];
+      sm_ml[r][g][1] = l[g];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sm_acc[r][g][8 * sub + i] = acc[g][i];
+  }
+  __syncthreads();
+  for (int o = threadIdx.x; o < G * HD; o += kAttnThreads) {
+    const int g = o / HD, d = o % HD;
+    float M = -INFINITY;
+    for (int j = 0; j < NGR; ++j) M = fmaxf(M, sm_ml[j][g][0]);
+    float A = 0.f, Z = 0.f;
+    for (int j = 0; j < NGR; ++j) {
+      const float mj = sm_ml[j][g][0];
+      const float w = mj == -INFINITY ? 0.f : exp2f(mj - M);
+      A = fmaf(sm_acc[j][g][d], w, A);
+      Z = fmaf(sm_ml[j][g][1], w, Z);
+    }
+    const int head = kvh * G + g;
+    a.part[(static_cast<long>(head) * a.splits + split) * HD + d] = A;
+    if (d == 0) a.part_ml[static_cast<long>(head) * a.splits + split] = make_float2(M, Z);
+  }
+
+  // the last workgroup of this key/value head merges the splits
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = atomicAdd(&a.arrivals[kvh], 1u);
+    sm_last = prev == static_cast<unsigned>(a.splits) - 1u;
+  }
+  __syncthreads();
+  if (!sm_last) return;
+  __threadfence();
+  for (int o = threadIdx.x; o < G * HD; o += kAttnThreads) {
+    const int g = o / HD, d = o % HD;
+    const int head = kvh * G + g;
+    const float2* ml = a.part_ml + static_cast<long>(head) * a.splits;
+    const float* pa = a.part + static_cast<long>(head) * a.splits * HD + d;
+    float M = -INFINITY;
+    for (int j = 0; j < a.splits; ++j) M = fmaxf(M, ml[j].x);
+    float A = 0.f, Z = 0.f;
+    for (int j = 0; j < a.splits; ++j) {
+      const float mj = ml[j].x;
+      const float w = mj == -INFINITY ? 0.f : exp2f(mj - M);
+      A = fmaf(pa[static_cast<long>(j) * HD], w, A);
+      Z = fmaf(ml[j].y, w, Z);
+    }
+    a.out[head * HD + d] = A / Z;
+  }
+  if (threadIdx.x == 0) atomicExch(&a.arrivals[kvh], 0u);  // ready for the next call
+}
+
+struct Shape {
+  int splits, per;
+};
+
+Shape split_for(int n_kv, long ctx) {
+  // about 128 positions per workgroup, at most ~1024 workgroups in all
+  long splits = (ctx + 127) / 128;
+  const long cap = 1024 / n_kv > 0 ? 1024 / n_kv : 1;
+  if (splits > cap) splits = cap;
+  if (splits < 1) splits = 1;
+  const long per = (ctx + splits - 1) / splits;
+  return Shape{static_cast<int>((ctx + per - 1) / per), static_cast<int>(per)};
+}
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+template <int HD, int G>
+const void* kernel_for() {
+  return reinterpret_cast<const void*>(&attn_decode_kernel<HD, G>);
+}
+
+const void* pick(int hd, int g) {
+  // group sizes up to 4 (the per-workgroup merge buffer is G * 16 KiB)
+  if (hd == 128) {
+    if (g == 1) return kernel_for<128, 1>();
+    if (g == 2) return kernel_for<128, 2>();
+    if (g == 4) return kernel_for<128, 4>();
+  } else if (hd == 64) {
+    if (g == 1) return kernel_for<64, 1>();
+    if (g == 2) return kernel_for<64, 2>();
+    if (g == 4) return kernel_for<64, 4>();
+  }
+  return nullptr;
+}
+
+}  // namespace
+
+bool attention_supported(int n_heads, int n_kv, int head_dim) {
+  return n_kv >= 1 && n_heads >= n_kv && n_heads % n_kv == 0 && pick(head_dim, n_heads / n_kv) != nullptr;
+}
+
+size_t attention_workspace(int n_heads, int n_kv, int head_dim, long ctx) {
+  const Shape s = split_for(n_kv, ctx);
+  return align256(static_cast<size_t>(n_kv) * 4) + align256(static_cast<size_t>(n_heads) * s.splits * 8) +
+         static_cast<size_t>(n_heads) * s.splits * head_dim * 4;
+}
+
+int launch_attention(const uint16_t* k, const uint16_t* v, const float* q, int n_heads, int n_kv, int head_dim,
+                     long ctx, float scale, float* out, void* workspace, void* stream) {
+  const Shape s = split_for(n_kv, ctx);
+  char* ws = static_cast<char*>(workspace);
+  AttnArgs a;
+  a.k = reinterpret_cast<const dev::u32x4*>(k);
+  a.v = reinterpret_cast<const dev::u32x4*>(v);
+  a.q = q;
+  a.out = out;
+  a.arrivals = reinterpret_cast<unsigned*>(ws);
+  a.part_ml = reinterpret_cast<float2*>(ws + align256(static_cast<size_t>(n_kv) * 4));
+  a.part = reinterpret_cast<float*>(ws + align256(static_cast<size_t>(n_kv) * 4) +
+                                    align256(static_cast<size_t>(n_heads) * s.splits * 8));
+  a.n_kv = n_kv;
+  a.splits = s.splits;
+  a.per = s.per;
+  a.ctx = ctx;
+  a.qscale = scale * 1.4426950408889634f;
+  void* args[] = {&a};
+  const hipError_t e = hipLaunchKernel(pick(head_dim, n_heads / n_kv), dim3(s.splits, n_kv), dim3(kAttnThreads),
+                                       args, 0, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PWG_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
+  return PWG_OK;
+}
+
+}  // namespace pwg

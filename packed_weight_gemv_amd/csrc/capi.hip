@@ -2,6 +2,8 @@
 // allocates or synchronises except pwg_step_plan (documented as such).
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "pwg_internal.h"
 
 using namespace pwg;
@@ -303,4 +305,34 @@ extern "C" int pwg_decode_step_weights(const pwg_step_desc* d, void* stream) {
   if (chained(d->h_in)) TRY(launch_chain_input(d->h_in, d->hidden, const_cast<float*>(d->h), d, stream));
   return launch_int8_gemv_argmax(d->out_table, d->out_scale, d->vocab, d->hidden, d->h, 1, d->workspace,
                                  d->token_out, d->logits_out, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Decode attention
+// ---------------------------------------------------------------------------
+extern "C" size_t pwg_attention_workspace_bytes(int32_t n_heads, int32_t n_kv, int32_t head_dim, int64_t ctx) {
+  if (ctx < 1 || ctx > (int64_t{1} << 31) || !attention_supported(n_heads, n_kv, head_dim)) return 0;
+  return attention_workspace(n_heads, n_kv, head_dim, static_cast<long>(ctx));
+}
+
+extern "C" int pwg_gqa_decode_attention(const uint16_t* k_cache, const uint16_t* v_cache, const float* q,
+                                        int32_t n_heads, int32_t n_kv, int32_t head_dim, int64_t ctx, float scale,
+                                        float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "pwg_gqa_decode_attention";
+  if (n_heads < 1 || n_kv < 1 || head_dim < 1 || n_heads % n_kv != 0)
+    return fail(PWG_ERR_ARG, "%s: %d query heads are not a multiple of %d key/value heads", fn, n_heads, n_kv);
+  if (ctx < 1 || ctx > (int64_t{1} << 31)) return fail(PWG_ERR_ARG, "%s: ctx must be in [1, 2^31]", fn);
+  if (!std::isfinite(scale)) return fail(PWG_ERR_ARG, "%s: scale is not finite", fn);
+  if (!attention_supported(n_heads, n_kv, head_dim))
+    return fail(PWG_ERR_UNSUPPORTED, "%s: head_dim %d with %d query heads per key/value head", fn, head_dim,
+                n_heads / n_kv);
+  TRY(check_ptr(k_cache, fn, "k_cache"));
+  TRY(check_ptr(v_cache, fn, "v_cache"));
+  TRY(check_ptr(q, fn, "q"));
+  TRY(check_ptr(out, fn, "out"));
+  TRY(check_ptr(workspace, fn, "workspace"));
+  const size_t need = attention_workspace(n_heads, n_kv, head_dim, static_cast<long>(ctx));
+  if (workspace_bytes < need) return fail(PWG_ERR_SIZE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, need);
+  return launch_attention(k_cache, v_cache, q, n_heads, n_kv, head_dim, static_cast<long>(ctx), scale, out,
+                          workspace, stream);
 }

@@ -55,6 +55,12 @@ int launch_i8b(const int8_t* table, bool tiled, const float* s, int64_t rows, in
                int32_t* token, void* stream);
 size_t t2_lds_bytes(int64_t cols);
 size_t i8_lds_bytes(int64_t cols);
+// Decode attention over a bfloat16 KV cache (attention.hip).
+bool attention_supported(int n_heads, int n_kv, int head_dim);
+size_t attention_workspace(int n_heads, int n_kv, int head_dim, long ctx);
+int launch_attention(const uint16_t* k, const uint16_t* v, const float* q, int n_heads, int n_kv, int head_dim,
+                     long ctx, float scale, float* out, void* workspace, void* stream);
+
 // Chained step, levels schedule (chain.hip): forms one level's input into x.
 int launch_chain_input(const pwg_input& in, int64_t n, float* x, const pwg_step_desc* d, void* stream);
 

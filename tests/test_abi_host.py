@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_error_string():
-    assert pwg.version() == 5
+    assert pwg.version() == 6
     assert isinstance(pwg.last_error(), str)
 
 
@@ -327,3 +327,27 @@ def test_chained_input_errors():
     d.schedule, d.weight_layout = pwg.SCHEDULE_PERSISTENT, pwg.LAYOUT_ROWS
     lv[0] = pwg.Level(P[0], P[1], P[2], P[3], 64, 16384)
     check(I(pwg.INPUT_SWIGLU, 0, 0, 0.0, P[6], None, None, None), ERR_UNSUPPORTED, "at most 12288")
+
+
+def test_attention_errors():
+    """Unsupported head sizes and groups, empty caches, bad scales, null or
+    misaligned pointers and short workspaces are refused before anything is
+    enqueued (every call here fails validation)."""
+    P = [A + 256 * k for k in range(5)]
+    assert pwg.attention_workspace_bytes(32, 8, 128, 4096) > 0
+    assert pwg.attention_workspace_bytes(32, 8, 96, 4096) == 0
+    assert pwg.attention_workspace_bytes(64, 8, 128, 4096) == 0   # group 8
+    assert pwg.attention_workspace_bytes(32, 8, 128, 0) == 0
+    ws = pwg.attention_workspace_bytes(32, 8, 128, 100)
+
+    def call(*, k=P[0], v=P[1], q=P[2], heads=32, kv=8, hd=128, ctx=100, scale=0.1, out=P[3], w=P[4], wb=ws):
+        return pwg._attn(k, v, q, heads, kv, hd, ctx, scale, out, w, wb, None)
+
+    assert call(hd=96) == ERR_UNSUPPORTED
+    assert call(heads=64) == ERR_UNSUPPORTED
+    assert call(heads=30) == ERR_ARG
+    assert call(ctx=0) == ERR_ARG
+    assert call(scale=float("inf")) == ERR_ARG
+    assert call(k=None) == ERR_ARG
+    assert call(q=MIS) == ERR_ALIGN
+    assert call(wb=ws - 1) == ERR_SIZE
