@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--no-compare", action="store_true", help="skip the levels-schedule and null-graph timings")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-small-batch", action="store_true", help="skip the small-batch (B = 1, 4, 8, 16) timings")
+    p.add_argument("--attention-only", action="store_true",
+                   help="only the decode-attention leg (one 8B-shape layer at 4,096 and 32,768 cached positions; "
+                        "parity, then timing); prints its JSON object")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle's timed sample")
     p.add_argument("--counters", action="store_true",
                    help="counter-collection run: 3 eager steps of the timed schedule plus a 1 GiB device copy "
@@ -276,6 +279,49 @@ def pass_desc(wl, n_layers, batch, seed):
     return d
 
 
+def decode_attention(stream, contexts=(4096, 32768), reps=200):
+    """One layer of grouped-query decode attention at the 8B shape (32 query
+    heads over 8 key/value heads of 128, bfloat16 cache) per context length:
+    parity of the timed call against the oracle, then HIP-event time per call
+    and the rate over the cache bytes read (keys and values)."""
+    import math
+
+    import numpy as np
+    import torch
+
+    import packed_weight_gemv_amd as pwg
+    import synth
+    from oracle import attention as at
+    out = {}
+    n_heads, n_kv, hd = 32, 8, synth.HEAD_DIM
+    for ctx in contexts:
+        q, k, v = synth.kv_cache(0, ctx)
+        dev = torch.device("cuda:0")
+        qd = torch.from_numpy(q).to(dev)
+        kd, vd = torch.from_numpy(k.view(np.int16)).to(dev), torch.from_numpy(v.view(np.int16)).to(dev)
+        ws = torch.zeros(pwg.attention_workspace_bytes(n_heads, n_kv, hd, ctx), dtype=torch.uint8, device=dev)
+        o = torch.empty(n_heads * hd, dtype=torch.float32, device=dev)
+        scale = 1 / math.sqrt(hd)
+        fn = lambda: pwg.gqa_decode_attention(kd, vd, qd, n_heads, n_kv, hd, scale, out=o, workspace=ws,  # noqa: E731
+                                              stream=stream)
+        with torch.cuda.stream(stream):
+            fn()
+        stream.synchronize()
+        ref = at.gqa_decode(q, k, v, n_heads, n_kv, hd, scale)
+        got = o.cpu().numpy().astype(np.float64)
+        rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        if not rel <= 1e-5:
+            raise SystemExit(f"decode attention parity failed at {ctx} positions: rel L2 {rel}")
+        ms = time_direct(fn, stream, reps, 20)
+        nbytes = 2 * ctx * n_kv * hd * 2
+        out[str(ctx)] = {"us_per_layer": ms * 1e3, "cache_bytes": nbytes, "GB_per_s": nbytes / (ms * 1e-3) / 1e9,
+                         "frac_of_8TBps": nbytes / (ms * 1e-3) / PEAK_HBM_BPS, "rel_l2_vs_oracle": rel}
+        log(f"decode attention, {ctx} positions: {ms * 1e3:.2f} us per layer, "
+            f"{nbytes / (ms * 1e-3) / 1e9:.0f} GB/s (rel L2 {rel:.1e})")
+        del kd, vd, ws
+    return out
+
+
 def small_batch(wl, stream, reps=50):
     """One 8B-shape layer's four levels and the int8 output projection with
     argmax, applied to B activation vectors per pass (the weights stream once
@@ -372,6 +418,9 @@ def main():
     from packed_weight_gemv_amd.workload import build_step, make_chained
 
     assert torch.cuda.is_available(), "bench needs a GPU"
+    if args.attention_only:
+        print(json.dumps({"decode_attention": decode_attention(torch.cuda.Stream())}), flush=True)
+        return
     schedule = {"persistent": pwg.SCHEDULE_PERSISTENT, "levels": pwg.SCHEDULE_LEVELS,
                 "stream": pwg.SCHEDULE_STREAM}[args.schedule]
     t0 = time.time()
@@ -596,6 +645,8 @@ def main():
 
     if not args.no_small_batch:
         result["small_batch"] = small_batch(wl, stream)
+    if not args.no_compare:
+        result["decode_attention"] = decode_attention(stream)
 
     # 5. oracle CPU baseline (bounded sample)
     if not args.no_cpu_baseline:

@@ -411,9 +411,9 @@ const char* pwg_last_error(void);
  *   k_cache, v_cache: device bfloat16 bit patterns (the upper half of a
  *       float32), position-major [ctx][n_kv][head_dim];
  *   q: device float32[n_heads*head_dim]; out: device float32[n_heads*head_dim];
- *   workspace: device, >= pwg_attention_workspace_bytes(...) bytes, ZERO-FILLED
- *       before its first use; each call leaves it zero-filled again (its
- *       arrival counters), so calls on one workspace must not overlap.
+ *   workspace: device, >= pwg_attention_workspace_bytes(...) bytes (partial
+ *       results per range of positions); calls on one workspace must not
+ *       overlap.  Two kernels on `stream`.
  * Every pointer is 16-byte aligned (PWG_ERR_ALIGN), none null (PWG_ERR_ARG).
  * Accumulation is float32 (online softmax in base 2, partial results per
  * range of positions merged at the end).  Supported: head_dim 64 or 128 and

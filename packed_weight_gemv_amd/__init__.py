@@ -237,15 +237,13 @@ def attention_workspace_bytes(n_heads: int, n_kv: int, head_dim: int, ctx: int) 
 def gqa_decode_attention(k_cache, v_cache, q, n_heads: int, n_kv: int, head_dim: int, scale: float, out=None,
                          workspace=None, stream=None):
     """One layer's grouped-query decode attention; k_cache, v_cache: int16 or
-    uint16 tensors of bfloat16 bits [ctx, n_kv, head_dim] on the device.  A
-    workspace passed in must be zero-filled before its first use (each call
-    leaves it so)."""
+    uint16 tensors of bfloat16 bits [ctx, n_kv, head_dim] on the device."""
     import torch
     ctx = k_cache.shape[0]
     if out is None:
         out = torch.empty(n_heads * head_dim, dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = torch.zeros(max(16, attention_workspace_bytes(n_heads, n_kv, head_dim, ctx)), dtype=torch.uint8,
+        workspace = torch.empty(max(16, attention_workspace_bytes(n_heads, n_kv, head_dim, ctx)), dtype=torch.uint8,
                                 device=q.device)
     _check(_attn(_ptr(k_cache), _ptr(v_cache), _ptr(q), n_heads, n_kv, head_dim, ctx, scale, _ptr(out),
                  _ptr(workspace), workspace.numel(), _stream(stream)))

@@ -15,9 +15,9 @@
 // group (online softmax in base 2, the query pre-scaled by scale * log2 e),
 // taking U positions per step so the K and V loads of U positions are in
 // flight together.  The lane groups are merged through LDS, each workgroup
-// writes one partial (maximum, normaliser, sum) per query head, and the last
-// workgroup of a key/value head (an arrival counter in the workspace, reset
-// by that workgroup) merges the splits into the output.
+// writes one partial (maximum, normaliser, sum) per query head to the
+// workspace, and a second kernel (one workgroup per query head) merges the
+// splits into the output.
 #include <cmath>
 
 #include "device_common.h"
@@ -27,7 +27,9 @@ namespace pwg {
 namespace {
 
 constexpr int kAttnThreads = 256;
-constexpr int kAttnU = 4;  // positions per lane group per step
+constexpr int kAttnU = 8;  // positions per lane group per step
+constexpr int kMergeBatch = 16;  // split partials loaded together by the merging workgroup
+constexpr int kMaxSplits = 512;  // splits per key/value head (workgroups in all <= ~512)
 
 struct AttnArgs {
   const dev::u32x4* k;
@@ -36,7 +38,6 @@ struct AttnArgs {
   float* out;
   float* part;            // [n_heads][splits][HD] weighted sums
   float2* part_ml;        // [n_heads][splits] (maximum, normaliser)
-  unsigned* arrivals;     // [n_kv]
   int n_kv, splits, per;  // positions per split
   long ctx;
   float qscale;           // scale * log2(e)
@@ -52,7 +53,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnArgs a) {
   constexpr int NGR = (kAttnThreads / 64) * P;  // lane groups per workgroup
   __shared__ float sm_ml[NGR][G][2];
   __shared__ float sm_acc[NGR][G][HD];
-  __shared__ int sm_last;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % L, r = wave * P + lane / L;
@@ -164,33 +164,39 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnArgs a) {
     if (d == 0) a.part_ml[static_cast<long>(head) * a.splits + split] = make_float2(M, Z);
   }
 
-  // the last workgroup of this key/value head merges the splits
-  __threadfence();
+}
+
+// Merge of the split partials: workgroup `head`, one thread per value index.
+// The partials are complete (stream order after the split kernel); each
+// thread loads kMergeBatch splits' sums before using them.
+template <int HD>
+__global__ __launch_bounds__(HD) void attn_merge_kernel(AttnArgs a) {
+  __shared__ float2 sm[kMaxSplits];
+  const int head = blockIdx.x, d = threadIdx.x;
+  const float2* ml = a.part_ml + static_cast<long>(head) * a.splits;
+  const float* pa = a.part + static_cast<long>(head) * a.splits * HD + d;
+  for (int j = d; j < a.splits; j += HD) sm[j] = ml[j];  // one load per thread and round
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(&a.arrivals[kvh], 1u);
-    sm_last = prev == static_cast<unsigned>(a.splits) - 1u;
-  }
-  __syncthreads();
-  if (!sm_last) return;
-  __threadfence();
-  for (int o = threadIdx.x; o < G * HD; o += kAttnThreads) {
-    const int g = o / HD, d = o % HD;
-    const int head = kvh * G + g;
-    const float2* ml = a.part_ml + static_cast<long>(head) * a.splits;
-    const float* pa = a.part + static_cast<long>(head) * a.splits * HD + d;
-    float M = -INFINITY;
-    for (int j = 0; j < a.splits; ++j) M = fmaxf(M, ml[j].x);
-    float A = 0.f, Z = 0.f;
-    for (int j = 0; j < a.splits; ++j) {
-      const float mj = ml[j].x;
-      const float w = mj == -INFINITY ? 0.f : exp2f(mj - M);
-      A = fmaf(pa[static_cast<long>(j) * HD], w, A);
-      Z = fmaf(ml[j].y, w, Z);
+  float M = -INFINITY;
+  for (int j = 0; j < a.splits; ++j) M = fmaxf(M, sm[j].x);
+  float A = 0.f, Z = 0.f;
+  for (int j0 = 0; j0 < a.splits; j0 += kMergeBatch) {
+    float pv[kMergeBatch];
+    float2 mv[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const bool in = j0 + u < a.splits;
+      pv[u] = in ? pa[static_cast<long>(j0 + u) * HD] : 0.f;
+      mv[u] = in ? sm[j0 + u] : make_float2(-INFINITY, 0.f);
     }
-    a.out[head * HD + d] = A / Z;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const float w = mv[u].x == -INFINITY ? 0.f : exp2f(mv[u].x - M);
+      A = fmaf(pv[u], w, A);
+      Z = fmaf(mv[u].y, w, Z);
+    }
   }
-  if (threadIdx.x == 0) atomicExch(&a.arrivals[kvh], 0u);  // ready for the next call
+  a.out[head * HD + d] = A / Z;
 }
 
 struct Shape {
@@ -198,9 +204,11 @@ struct Shape {
 };
 
 Shape split_for(int n_kv, long ctx) {
-  // about 128 positions per workgroup, at most ~1024 workgroups in all
+  // one step of every lane group (16 lane groups x 8 positions for heads of
+  // 128) per
+  // split at short contexts, at most ~512 workgroups in all at long ones
   long splits = (ctx + 127) / 128;
-  const long cap = 1024 / n_kv > 0 ? 1024 / n_kv : 1;
+  const long cap = kMaxSplits / n_kv > 0 ? kMaxSplits / n_kv : 1;
   if (splits > cap) splits = cap;
   if (splits < 1) splits = 1;
   const long per = (ctx + splits - 1) / splits;
@@ -236,8 +244,7 @@ bool attention_supported(int n_heads, int n_kv, int head_dim) {
 
 size_t attention_workspace(int n_heads, int n_kv, int head_dim, long ctx) {
   const Shape s = split_for(n_kv, ctx);
-  return align256(static_cast<size_t>(n_kv) * 4) + align256(static_cast<size_t>(n_heads) * s.splits * 8) +
-         static_cast<size_t>(n_heads) * s.splits * head_dim * 4;
+  return align256(static_cast<size_t>(n_heads) * s.splits * 8) + static_cast<size_t>(n_heads) * s.splits * head_dim * 4;
 }
 
 int launch_attention(const uint16_t* k, const uint16_t* v, const float* q, int n_heads, int n_kv, int head_dim,
@@ -249,18 +256,21 @@ int launch_attention(const uint16_t* k, const uint16_t* v, const float* q, int n
   a.v = reinterpret_cast<const dev::u32x4*>(v);
   a.q = q;
   a.out = out;
-  a.arrivals = reinterpret_cast<unsigned*>(ws);
-  a.part_ml = reinterpret_cast<float2*>(ws + align256(static_cast<size_t>(n_kv) * 4));
-  a.part = reinterpret_cast<float*>(ws + align256(static_cast<size_t>(n_kv) * 4) +
-                                    align256(static_cast<size_t>(n_heads) * s.splits * 8));
+  a.part_ml = reinterpret_cast<float2*>(ws);
+  a.part = reinterpret_cast<float*>(ws + align256(static_cast<size_t>(n_heads) * s.splits * 8));
   a.n_kv = n_kv;
   a.splits = s.splits;
   a.per = s.per;
   a.ctx = ctx;
   a.qscale = scale * 1.4426950408889634f;
   void* args[] = {&a};
-  const hipError_t e = hipLaunchKernel(pick(head_dim, n_heads / n_kv), dim3(s.splits, n_kv), dim3(kAttnThreads),
-                                       args, 0, reinterpret_cast<hipStream_t>(stream));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipLaunchKernel(pick(head_dim, n_heads / n_kv), dim3(s.splits, n_kv), dim3(kAttnThreads), args, 0, st);
+  if (e == hipSuccess) {
+    const void* merge = head_dim == 128 ? reinterpret_cast<const void*>(&attn_merge_kernel<128>)
+                                        : reinterpret_cast<const void*>(&attn_merge_kernel<64>);
+    e = hipLaunchKernel(merge, dim3(n_heads), dim3(head_dim), args, 0, st);
+  }
   if (e != hipSuccess) return fail(PWG_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
   return PWG_OK;
 }
