@@ -43,12 +43,27 @@ struct AttnArgs {
   float qscale;           // scale * log2(e)
 };
 
+// Sum over the L lanes of a row group (L = 8 or 16, aligned), every lane
+// receiving the sum: DPP lane exchanges inside 16-lane rows (xor 1 and xor
+// 2 within quads, then mirrors of 8 and of 16 lanes), full-rate VALU
+// operands instead of LDS-crossbar shuffles.
+template <int L>
+__device__ __forceinline__ float row_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));  // quad [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));  // quad [2,3,0,1]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // row half mirror
+  if constexpr (L == 16)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row mirror
+  return v;
+}
+
 __device__ __forceinline__ float lo_bf16(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(unsigned w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 template <int HD, int G>
 __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnArgs a) {
   constexpr int L = HD / 8;                   // lanes per row
+  static_assert(L == 8 || L == 16, "row sums cover 8 or 16 lanes");
   constexpr int P = 64 / L;                   // rows per wave load
   constexpr int NGR = (kAttnThreads / 64) * P;  // lane groups per workgroup
   __shared__ float sm_ml[NGR][G][2];
@@ -108,8 +123,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnArgs a) {
         float d = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) d = fmaf(q[g][i], kf[i], d);
-#pragma unroll
-        for (int o = L / 2; o > 0; o >>= 1) d += __shfl_xor(d, o, 64);
+        d = row_sum<L>(d);
         s[g][u] = valid[u] ? d : -INFINITY;
       }
     }
