@@ -13,6 +13,7 @@ specification for the packed-byte decoder/encoder:
                         composition;
 * ``attention``       - grouped-query decode attention over a bfloat16
                         key/value cache;
+* ``verify``          - the speculative verify step's acceptance rule;
 * ``chain``           - the chained decode step: RMSNorm, one-position
                         grouped-query attention, SwiGLU and residual adds
                         between the projections;
@@ -24,4 +25,4 @@ Parity status of each function is stated in its module.  One part is
 name it but never specify it), so the build's 2-bit format is pinned only by
 its own specification and round trips, not by the pages.
 """
-from . import accounting, attention, chain, packed_format, reference  # noqa: F401
+from . import accounting, attention, chain, packed_format, reference, verify  # noqa: F401
