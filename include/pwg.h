@@ -45,7 +45,7 @@ extern "C" {
 #endif
 #pragma GCC visibility push(default)
 
-#define PWG_VERSION 6
+#define PWG_VERSION 7
 #define PWG_MAX_COLS 16384
 
 enum {
@@ -423,6 +423,21 @@ size_t pwg_attention_workspace_bytes(int32_t n_heads, int32_t n_kv, int32_t head
 int pwg_gqa_decode_attention(const uint16_t* k_cache, const uint16_t* v_cache, const float* q,
                              int32_t n_heads, int32_t n_kv, int32_t head_dim, int64_t ctx, float scale,
                              float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Acceptance of drafted tokens after a batched verify pass (page "The
+ * Neutrino Engine", section "The 0.6B model does not get to decide": the
+ * large model scores the drafts in one batched pass and keeps them only while
+ * its greedy choice agrees).  Device int32 arrays: tokens_in[0] = the last
+ * accepted token, tokens_in[1..n_drafts] = the drafts (the batched pass's
+ * token_in); targets[i] = the large model's greedy token after position i
+ * (the batched pass's token_out).  Writes *accepted = k, the largest k <=
+ * n_drafts with targets[i] == tokens_in[i+1] for all i < k, and *next_token =
+ * targets[k]; the step emits drafts 1..k, then *next_token.  Positions past
+ * n_drafts (padding up to the pass's batch) are ignored.  0 <= n_drafts <= 15
+ * (PWG_ERR_ARG); pointers 16-byte aligned.  One small kernel on `stream`. */
+int pwg_verify_accept(const int32_t* tokens_in, const int32_t* targets, int32_t n_drafts, int32_t* accepted,
+                      int32_t* next_token, void* stream);
 
 /* PWG_VERSION of the built library. */
 int pwg_version(void);

@@ -23,7 +23,7 @@ __all__ = [
     "tiled_size", "tile_rows", "SCHEDULE_LEVELS", "SCHEDULE_PERSISTENT", "SCHEDULE_STREAM",
     "LAYOUT_ROWS", "LAYOUT_TILED", "layout_for_schedule", "LIB_PATH", "InputOp", "INPUT_GIVEN",
     "INPUT_RMSNORM", "INPUT_EMBED_RMSNORM", "INPUT_ATTN1", "INPUT_SWIGLU", "attention_workspace_bytes",
-    "gqa_decode_attention",
+    "gqa_decode_attention", "verify_accept",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpwg.so")
@@ -101,6 +101,7 @@ _unpack = _sig("pwg_unpack_weights", C.c_int, _vp, _i64, _i64, _vp)
 _attn_ws = _sig("pwg_attention_workspace_bytes", _sz, _i32, _i32, _i32, _i64)
 _attn = _sig("pwg_gqa_decode_attention", C.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _i64, C.c_float, _vp, _vp, _sz,
              _vp)
+_verify = _sig("pwg_verify_accept", C.c_int, _vp, _vp, _i32, _vp, _vp, _vp)
 _tgemv = _sig("pwg_ternary_gemv", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp)
 _argmax_ws = _sig("pwg_argmax_workspace_bytes", _sz, _i64, _i32)
 _i8argmax = _sig("pwg_int8_gemv_argmax", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _sz, _vp, _vp, _vp)
@@ -123,7 +124,7 @@ EXPORTED = ["pwg_packed_size", "pwg_pack_weights", "pwg_unpack_weights", "pwg_te
             "pwg_int8_gemv_argmax_tiled",
             "pwg_step_workspace_bytes", "pwg_step_plan", "pwg_decode_step_weights",
             "pwg_step_status", "pwg_last_error", "pwg_version", "pwg_attention_workspace_bytes",
-            "pwg_gqa_decode_attention"]
+            "pwg_gqa_decode_attention", "pwg_verify_accept"]
 
 
 def last_error() -> str:
@@ -248,6 +249,20 @@ def gqa_decode_attention(k_cache, v_cache, q, n_heads: int, n_kv: int, head_dim:
     _check(_attn(_ptr(k_cache), _ptr(v_cache), _ptr(q), n_heads, n_kv, head_dim, ctx, scale, _ptr(out),
                  _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+# ---------------------------------------------------------------- verify pass
+def verify_accept(tokens_in, targets, n_drafts: int, accepted=None, next_token=None, stream=None):
+    """Accepted-draft count and next token after a batched verify pass
+    (device int32 tensors); returns (accepted, next_token) device tensors."""
+    import torch
+    dev = tokens_in.device
+    if accepted is None:
+        accepted = torch.empty(4, dtype=torch.int32, device=dev)
+    if next_token is None:
+        next_token = torch.empty(4, dtype=torch.int32, device=dev)
+    _check(_verify(_ptr(tokens_in), _ptr(targets), n_drafts, _ptr(accepted), _ptr(next_token), _stream(stream)))
+    return accepted, next_token
 
 
 # ---------------------------------------------------------------- tiled arrangement

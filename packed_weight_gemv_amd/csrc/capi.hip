@@ -336,3 +336,17 @@ extern "C" int pwg_gqa_decode_attention(const uint16_t* k_cache, const uint16_t*
   return launch_attention(k_cache, v_cache, q, n_heads, n_kv, head_dim, static_cast<long>(ctx), scale, out,
                           workspace, stream);
 }
+
+// ---------------------------------------------------------------------------
+// Verify-pass acceptance
+// ---------------------------------------------------------------------------
+extern "C" int pwg_verify_accept(const int32_t* tokens_in, const int32_t* targets, int32_t n_drafts,
+                                 int32_t* accepted, int32_t* next_token, void* stream) {
+  const char* fn = "pwg_verify_accept";
+  if (n_drafts < 0 || n_drafts > 15) return fail(PWG_ERR_ARG, "%s: n_drafts must be in [0, 15] (got %d)", fn, n_drafts);
+  TRY(check_ptr(tokens_in, fn, "tokens_in"));
+  TRY(check_ptr(targets, fn, "targets"));
+  TRY(check_ptr(accepted, fn, "accepted"));
+  TRY(check_ptr(next_token, fn, "next_token"));
+  return launch_verify_accept(tokens_in, targets, n_drafts, accepted, next_token, stream);
+}

@@ -61,6 +61,10 @@ size_t attention_workspace(int n_heads, int n_kv, int head_dim, long ctx);
 int launch_attention(const uint16_t* k, const uint16_t* v, const float* q, int n_heads, int n_kv, int head_dim,
                      long ctx, float scale, float* out, void* workspace, void* stream);
 
+// Verify-pass acceptance (verify.hip).
+int launch_verify_accept(const int32_t* tokens_in, const int32_t* targets, int32_t n_drafts, int32_t* accepted,
+                         int32_t* next_token, void* stream);
+
 // Chained step, levels schedule (chain.hip): forms one level's input into x.
 int launch_chain_input(const pwg_input& in, int64_t n, float* x, const pwg_step_desc* d, void* stream);
 

@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_error_string():
-    assert pwg.version() == 6
+    assert pwg.version() == 7
     assert isinstance(pwg.last_error(), str)
 
 
@@ -351,3 +351,13 @@ def test_attention_errors():
     assert call(k=None) == ERR_ARG
     assert call(q=MIS) == ERR_ALIGN
     assert call(wb=ws - 1) == ERR_SIZE
+
+
+def test_verify_accept_errors():
+    """Draft counts outside [0, 15] and null or misaligned pointers are
+    refused before anything is enqueued."""
+    P = [A + 256 * k for k in range(4)]
+    assert pwg._verify(P[0], P[1], 16, P[2], P[3], None) == ERR_ARG
+    assert pwg._verify(P[0], P[1], -1, P[2], P[3], None) == ERR_ARG
+    assert pwg._verify(None, P[1], 3, P[2], P[3], None) == ERR_ARG
+    assert pwg._verify(P[0], MIS, 3, P[2], P[3], None) == ERR_ALIGN
