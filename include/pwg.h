@@ -428,10 +428,10 @@ int pwg_gqa_decode_attention(const uint16_t* k_cache, const uint16_t* v_cache, c
  * Acceptance of drafted tokens after a batched verify pass (page "The
  * Neutrino Engine", section "The 0.6B model does not get to decide": the
  * large model scores the drafts in one batched pass and keeps them only while
- * its greedy choice agrees).  Device int32 arrays: tokens_in[0] = the last
- * accepted token, tokens_in[1..n_drafts] = the drafts (the batched pass's
- * token_in); targets[i] = the large model's greedy token after position i
- * (the batched pass's token_out).  Writes *accepted = k, the largest k <=
+ * its greedy choice agrees).  Device int32 arrays of at least n_drafts + 1
+ * entries: tokens_in[0] = the last accepted token, tokens_in[1..n_drafts] =
+ * the drafts (the batched pass's token_in); targets[i] = the large model's
+ * greedy token after position i (the batched pass's token_out).  Writes *accepted = k, the largest k <=
  * n_drafts with targets[i] == tokens_in[i+1] for all i < k, and *next_token =
  * targets[k]; the step emits drafts 1..k, then *next_token.  Positions past
  * n_drafts (padding up to the pass's batch) are ignored.  0 <= n_drafts <= 15
