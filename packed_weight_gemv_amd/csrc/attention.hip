@@ -27,7 +27,7 @@ namespace pwg {
 namespace {
 
 constexpr int kAttnThreads = 256;
-constexpr int kAttnU = 8;  // positions per lane group per step
+constexpr int kAttnU = 4;  // positions per lane group per step
 constexpr int kMergeBatch = 16;  // split partials loaded together by the merging workgroup
 constexpr int kMaxSplits = 512;  // splits per key/value head (workgroups in all <= ~512)
 
@@ -218,9 +218,9 @@ struct Shape {
 };
 
 Shape split_for(int n_kv, long ctx) {
-  // one step of every lane group (16 lane groups x 8 positions for heads of
-  // 128) per
-  // split at short contexts, at most ~512 workgroups in all at long ones
+  // ~128 positions per split at short contexts (two steps of 16 lane
+  // groups x 4 positions for heads of 128), at most ~512 workgroups in all
+  // at long ones
   long splits = (ctx + 127) / 128;
   const long cap = kMaxSplits / n_kv > 0 ? kMaxSplits / n_kv : 1;
   if (splits > cap) splits = cap;
