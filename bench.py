@@ -15,10 +15,9 @@ weights we did not train": identity is checked before any timing):
   3. warm up W graph replays, time K replays (HIP events on the replay stream)
      of the timed schedule: by default the stream schedule, which computes
      the step over its fixed per-level inputs with no waits between levels;
-  4. the same for the other schedules (the ordered persistent kernel, with a
-     device-wide barrier between levels as a chained step needs, and one
-     kernel per level) and for a null graph with as many empty kernels, to
-     split dependency and launch overhead from DRAM time;
+  4. the same for the other schedule (one kernel per level, in decoder
+     order, as a chained step needs) and for a null graph with as many empty
+     kernels, to split dependency and launch overhead from DRAM time;
   5. the oracle timed on a bounded sample of the same workload (rank 0).
 Prints one JSON line.
 """
@@ -43,10 +42,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=256)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--schedule", choices=["stream", "persistent", "levels"], default="stream",
-                   help="timed schedule: stream (the step over its fixed level inputs, no dependency waits), "
-                        "persistent (ordered: a device-wide barrier between levels, as a chained step needs) or "
-                        "levels (one kernel per level); the other two are timed alongside")
+    p.add_argument("--schedule", choices=["stream", "levels"], default="stream",
+                   help="timed schedule: stream (the step over its fixed level inputs, no dependency waits) or "
+                        "levels (one kernel per level, in decoder order); the other is timed alongside")
     p.add_argument("--layers", type=int, default=36)
     p.add_argument("--no-compare", action="store_true", help="skip the levels-schedule and null-graph timings")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -68,8 +66,7 @@ def log(msg):
 # Sources of each schedule's step kernel: the HBM traffic counted for a
 # kernel stays valid while these files are unchanged.
 KERNEL_SOURCES = {
-    "stream": ("step_stream.hip", "step_stream.h", "device_common.h", "pwg_internal.h"),
-    "persistent": ("step_persistent.hip", "t2_rows.h", "device_common.h", "pwg_internal.h"),
+    "stream": ("step_stream.hip", "step_stream.h", "operands.h", "device_common.h", "pwg_internal.h"),
 }
 
 
@@ -328,7 +325,7 @@ def small_batch(wl, stream, reps=50):
     per pass whatever B is); one HIP graph per B.  The pass is one call of
     the decode step on the tiled weights: the stream schedule for B = 1, the
     batched pass for B = 4, 8, 16.  Also timed: the same products as five
-    separate calls (B = 1: the VALU kernels on row-major weights; B > 1: the
+    separate calls (B = 1: the per-call kernels on row-major weights; B > 1: the
     per-call matrix-core kernels on tiled weights), and the batched pass over
     all 36 layers.  Reports weight bytes per second and effective integer
     operations per second (2 per weight per vector)."""
@@ -336,7 +333,7 @@ def small_batch(wl, stream, reps=50):
 
     import packed_weight_gemv_amd as pwg
     import synth
-    rows_w, table = wl.weights[pwg.LAYOUT_ROWS]   # the per-call VALU kernels take row-major weights
+    rows_w, table = wl.weights[pwg.LAYOUT_ROWS]   # the batch-1 per-call kernels take row-major weights
     levels = [(w, sc, r, k) for w, (_, sc, _, _, r, k) in zip(rows_w[:4], wl.desc.levels[:4])]
     tiled = wl.weights[pwg.LAYOUT_TILED]
     tlevels = [(w, sc, r, k) for w, (_, sc, _, _, r, k) in zip(tiled[0][:4], wl.desc.levels[:4])]
@@ -384,7 +381,7 @@ def small_batch(wl, stream, reps=50):
                "pct_of_hbm_peak": 100.0 * bytes_ / (us * 1e-6) / PEAK_HBM_BPS,
                "effective_Tops": ops / us / 1e6,
                "us_per_pass_separate_calls": us_calls,
-               "separate_calls": "VALU, row-major weights" if batch == 1 else "matrix cores, tiled weights"}
+               "separate_calls": "matrix cores, row-major weights" if batch == 1 else "matrix cores, tiled weights"}
         log(f"small batch B={batch}: {us:.1f} us per pass, {bytes_ / us / 1e3:.0f} GB/s, {ops / us / 1e6:.1f} Top/s"
             f" (separate calls {us_calls:.1f} us)")
         if batch > 1:
@@ -421,8 +418,7 @@ def main():
     if args.attention_only:
         print(json.dumps({"decode_attention": decode_attention(torch.cuda.Stream())}), flush=True)
         return
-    schedule = {"persistent": pwg.SCHEDULE_PERSISTENT, "levels": pwg.SCHEDULE_LEVELS,
-                "stream": pwg.SCHEDULE_STREAM}[args.schedule]
+    schedule = {"levels": pwg.SCHEDULE_LEVELS, "stream": pwg.SCHEDULE_STREAM}[args.schedule]
     t0 = time.time()
     # both weight arrangements when other schedules or the small-batch
     # kernels (row-major) run next to a tiled stream step
@@ -530,12 +526,12 @@ def main():
     del graph4
     pwg.step_status(wl.desc, stream=stream)
     log(f"{args.schedule}, four steps per graph: {ms4 * 1e3:.1f} us/step")
-    kernels_per_step = {pwg.SCHEDULE_PERSISTENT: 1, pwg.SCHEDULE_STREAM: 2}.get(schedule, len(wl.desc.levels) + 3)
+    kernels_per_step = {pwg.SCHEDULE_STREAM: 2}.get(schedule, len(wl.desc.levels) + 3)
 
     extra = {}
     if not args.no_compare:
-        names = {pwg.SCHEDULE_LEVELS: "levels", pwg.SCHEDULE_PERSISTENT: "persistent", pwg.SCHEDULE_STREAM: "stream"}
-        for other in (pwg.SCHEDULE_LEVELS, pwg.SCHEDULE_PERSISTENT, pwg.SCHEDULE_STREAM):
+        names = {pwg.SCHEDULE_LEVELS: "levels", pwg.SCHEDULE_STREAM: "stream"}
+        for other in (pwg.SCHEDULE_LEVELS, pwg.SCHEDULE_STREAM):
             if other == schedule:
                 continue
             other_fn = run(other)
@@ -557,10 +553,10 @@ def main():
         extra["null_graph_us"] = ms_null * 1e3
         extra["null_graph_kernels"] = n_null
         # chained step: every level's input formed from earlier outputs
-        # (RMSNorm, one-position attention, SwiGLU, residual sums) on the two
-        # ordered schedules, the dependency chain the stream step leaves out
+        # (RMSNorm, one-position attention, SwiGLU, residual sums) on the
+        # ordered schedule, the dependency chain the stream step leaves out
         cs = make_chained(wl, schedule=pwg.SCHEDULE_LEVELS)
-        for sched_c in (pwg.SCHEDULE_LEVELS, pwg.SCHEDULE_PERSISTENT):
+        for sched_c in (pwg.SCHEDULE_LEVELS,):
             cs.desc.schedule = sched_c
             cs.desc._c = None
             need = pwg.step_workspace_bytes(cs.desc)
@@ -602,9 +598,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("ternary FP4 x FP4-digit block-scaled MFMA (exact products, f32 sums) / int8 x int8-digit MFMA "
-                  "(i32 exact), f32 scale" if schedule == pwg.SCHEDULE_STREAM else
-                  "ternary x int4-limb dot (i32 exact) / int8 x int8-limb dot (i32 exact), f32 scale"),
+        "dtype": ("f32: ternary FP4 x six e4m3 pieces of x (block-scaled MFMA, exact products, f32 sums); "
+                  "int8 x six int8 digits of h (MFMA, exact i32 sums per section); f32 row scales"),
         "data": "synthetic seeded (ternary iid p=1/3, int8 U[-127,127], activations N(0,1))",
         "config": {
             "workload": (f"8B-shape batch-1 decode step: embedding row + {args.layers} layers x (q|k|v 6144x4096, "
@@ -627,7 +622,7 @@ def main():
     # launches without a graph, measured with HIP events on the launch
     # stream (for the stream schedule that includes the input-conversion
     # kernel before it, about 7 us)
-    if schedule in (pwg.SCHEDULE_PERSISTENT, pwg.SCHEDULE_STREAM):
+    if schedule == pwg.SCHEDULE_STREAM:
         traffic = None
         tfile = os.path.join(ROOT, "profiles", "step_kernel_traffic.json")
         if os.path.exists(tfile):
@@ -635,8 +630,7 @@ def main():
             if (t.get("kernel_source_sha") == kernel_source_sha(args.schedule) and t.get("layers") == args.layers
                     and t.get("schedule") == args.schedule):
                 traffic = t.get("hbm_bytes_per_launch")
-        kname = ("step_kernel<ordered> (whole step, one launch)" if schedule == pwg.SCHEDULE_PERSISTENT else
-                 "stream_step_kernel<8> (whole step; timed with its input-conversion kernel)")
+        kname = "stream_step_kernel<8> (whole step; timed with its input-conversion kernel)"
         kernel_bps = step_bytes / (ms_direct * 1e-3)
         result["roofline"] = {"bound": "hbm", "achieved": kernel_bps / 1e9, "peak": PEAK_HBM_BPS / 1e9,
                               "unit": "GB/s", "frac": kernel_bps / PEAK_HBM_BPS, "traffic": traffic,

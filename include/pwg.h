@@ -61,9 +61,8 @@ enum {
 /* Step schedules for pwg_decode_step_weights. */
 enum {
   PWG_SCHEDULE_LEVELS = 0,      /* one kernel per dependency level, in decoder order */
-  PWG_SCHEDULE_PERSISTENT = 1,  /* one persistent kernel; a device-wide barrier after
-                                   every level, so level L+1 starts only when all of
-                                   level L is done (the dependency of a chained step) */
+  PWG_SCHEDULE_PERSISTENT = 1,  /* reserved: not available in this build
+                                   (PWG_ERR_UNSUPPORTED) */
   PWG_SCHEDULE_STREAM = 2       /* one matrix-core kernel (after a small input
                                    conversion kernel) without level barriers: the
                                    16-row blocks of all levels and of the vocabulary
@@ -78,7 +77,7 @@ enum {
 /* Weight arrangements of a step description (pwg_step_desc.weight_layout). */
 enum {
   PWG_LAYOUT_ROWS = 0,   /* T2 blobs and the int8 output table row-major
-                            (schedules LEVELS and PERSISTENT) */
+                            (schedule LEVELS) */
   PWG_LAYOUT_TILED = 1   /* the same bytes in 16-row x 64-byte tiles, see
                             pwg_tile_rows (schedule STREAM) */
 };
@@ -124,9 +123,12 @@ int pwg_unpack_weights(const void* packed_host, int64_t rows, int64_t cols,
  *   row_scale    device, float32[rows]
  *   x            device, float32[batch][cols] row-major
  *   y            device, float32[batch][rows] row-major (written, not accumulated)
- * Accuracy: float32-class.  The sum is formed exactly in integers over a
- * 22-bit fixed-point rounding of x with one exponent per vector, then scaled
- * in float32; see the design notes for the error bound.
+ * Arithmetic: the matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4), the
+ * weights as FP4 and x as six e4m3 pieces per value with a shared E8M0 scale
+ * per 32 values; the pieces sum to x to within 2^-24 of each value (2^-30 of
+ * its 32-value block's maximum at worst), every product is exact and the
+ * sums are float32: the accuracy of a float32 GEMV, outliers included.
+ * batch > 1 runs one pass over the weights per vector.
  * Errors: PWG_ERR_ARG, PWG_ERR_ALIGN, PWG_ERR_HIP. */
 int pwg_ternary_gemv(const void* w_packed, const float* row_scale,
                      int64_t rows, int64_t cols,
@@ -169,10 +171,10 @@ int pwg_tile_rows(const void* src, int64_t rows, int64_t row_bytes,
  * pwg_tile_rows arranges them (the arrangement the stream step reads), run on
  * the int8 matrix cores (v_mfma_i32_16x16x64_i8) and form every row sum
  * exactly in int32 per 256-value section (int8 tables) or 1,024-value block
- * (ternary weights) over a fixed-point rounding of the activations (three
- * balanced base-256 digits of rint(x * 2^(22 - e)), e the exponent of the
- * section or block); float32 after that.  Asynchronous on `stream`,
- * capturable, allocate nothing. */
+ * (ternary weights) over a fixed-point rounding of the activations (four
+ * balanced base-256 digits of rint(x * 2^(30 - e)), e the exponent of the
+ * section or block: at most 2^(e - 31) per value); float32 after that.
+ * Asynchronous on `stream`, capturable, allocate nothing. */
 
 /* Workspace bytes of pwg_ternary_gemv_tiled for (cols, batch): the converted
  * activations (4 bytes per value and vector) and a few KiB; 0 for an
@@ -226,12 +228,15 @@ size_t pwg_argmax_workspace_bytes(int64_t rows, int32_t batch);
  *   token_out    device, int32[batch]
  *   logits_out   device float32[batch][rows] or NULL (written only if given)
  * batch 1: a fused GEMV + per-block (max, index), then one block that
- * reduces the pairs.  batch 4, 8, 16 with cols a multiple of 1,024: h is
- * converted into matrix-core operands in the workspace, one kernel computes
- * every vector's logits on v_mfma_i32_16x16x64_i8 (exact int32 sums per
- * 256-value section) with the table read once, and one block per vector
- * reduces its keys; other widths use a VALU kernel.  Deterministic bit for
- * bit on every path.
+ * reduces the pairs; h is rounded to five int8 limbs per value (39-bit fixed
+ * point per 16-value chunk: at most 2^(e - 39) per value, e the exponent of
+ * the chunk maximum) and each limb's sum is exact in int32 (v_dot4_i32_i8).
+ * batch 4, 8, 16 with cols a multiple of 1,024: h is converted into
+ * matrix-core operands in the workspace, one kernel computes every vector's
+ * logits on v_mfma_i32_16x16x64_i8 (exact int32 sums per 256-value section
+ * over four digits, as pwg_ternary_gemv_tiled) with the table read once, and
+ * one block per vector reduces its keys; other widths run the batch-1 kernel
+ * per vector.  Deterministic bit for bit on every path.
  * Errors: PWG_ERR_ARG, PWG_ERR_ALIGN, PWG_ERR_SIZE, PWG_ERR_HIP. */
 int pwg_int8_gemv_argmax(const int8_t* table, const float* row_scale,
                          int64_t rows, int64_t cols,
@@ -284,8 +289,7 @@ int pwg_embed_gather(const int8_t* table, const float* row_scale,
  *                             (src: the stacked gate|up output, gate first).
  * Buffers may not overlap: x, resid_out, src, resid and gamma are distinct
  * (PWG_ERR_ARG where pointers are equal).  Only the ordered schedules
- * (LEVELS, PERSISTENT) at batch 1 take such levels (PWG_ERR_UNSUPPORTED
- * otherwise).  Arithmetic is float32: the mean of squares is a float32 sum,
+ * (LEVELS) at batch 1 takes such levels (PWG_ERR_UNSUPPORTED otherwise).  Arithmetic is float32: the mean of squares is a float32 sum,
  * the root and the quotient IEEE float32. */
 enum {
   PWG_INPUT_GIVEN = 0,
@@ -323,9 +327,10 @@ typedef struct pwg_level {
  * projections in decoder order, the output projection and the greedy token):
  *   embedding gather of *token_in -> levels[0 .. n_levels-1] in order ->
  *   int8 output projection of h + argmax -> *token_out.
- * All pointers except `levels` are device pointers; `levels` is a host array
- * read during the call (for the persistent schedule it is read by
- * pwg_step_plan instead).  token_in and token_out may alias (the token then
+ * All pointers except `levels` are device pointers; `levels` is a host
+ * array: the levels schedule reads it during each call, the stream schedule
+ * and the batched pass read it in pwg_step_plan (their device plan then holds
+ * the pointers and shapes).  token_in and token_out may alias (the token then
  * feeds the next step on the device).
  *
  * Batched pass (batch = 4, 8 or 16; page section "The 0.6B model does not get
@@ -370,8 +375,8 @@ typedef struct pwg_step_desc {
 size_t pwg_step_workspace_bytes(const pwg_step_desc* desc);
 
 /* Prepare the workspace of a step: validates the description and, for the
- * persistent and stream schedules, writes the device-side level table and
- * work split and resets the barrier and status words.  Synchronous (it waits
+ * stream schedule and the batched pass, writes the device-side level table
+ * and work split and resets the claim counters and status words.  Synchronous (it waits
  * for its own copies); call it once per set of buffers, outside stream
  * capture, before pwg_decode_step_weights.
  * Errors: PWG_ERR_ARG, PWG_ERR_ALIGN, PWG_ERR_SIZE, PWG_ERR_HIP,
@@ -379,12 +384,13 @@ size_t pwg_step_workspace_bytes(const pwg_step_desc* desc);
 int pwg_step_plan(const pwg_step_desc* desc, void* stream);
 
 /* Enqueue one step on `stream` (capturable; no allocation, no sync).
- * Persistent schedule: one kernel with one workgroup per CU; every level
- * barrier wait is bounded (about 0.5 s), after which the kernel records a
- * timeout and ends instead of hanging; pwg_step_status reports it.
+ * Levels schedule: one kernel per level (and one per formed input), the
+ * output projection and the argmax reduction, in decoder order.
  * Stream schedule: a conversion kernel (every level's input and h into
  * matrix-core operands in the workspace), then one kernel with one workgroup
- * per CU; its only waits are inside a workgroup and are bounded the same way.
+ * per CU; its only waits are inside a workgroup and are bounded (about
+ * 0.5 s), after which the kernel records a timeout and ends instead of
+ * hanging; pwg_step_status reports it.
  * Batched pass: a conversion kernel (operands and embedding rows), then one
  * kernel with one workgroup per CU that claims its work from a counter in the
  * workspace; its waits are inside a workgroup and bounded the same way.
@@ -392,8 +398,8 @@ int pwg_step_plan(const pwg_step_desc* desc, void* stream);
  * workspace race. */
 int pwg_decode_step_weights(const pwg_step_desc* desc, void* stream);
 
-/* Synchronously reads the step's status word (persistent and stream
- * schedules; always PWG_OK for the levels schedule): PWG_ERR_HIP with a
+/* Synchronously reads the step's status word (stream schedule and batched
+ * pass; always PWG_OK for the levels schedule): PWG_ERR_HIP with a
  * message if a bounded wait timed out.  Not for the hot path. */
 int pwg_step_status(const pwg_step_desc* desc, void* stream);
 

@@ -5,13 +5,14 @@
 //
 // Operands.  Each vector's input is rounded per 256-value section (int8
 // tables) or 1,024-value block (ternary levels) to fixed point,
-// X = rint(x * 2^(22 - e)) with max|x| < 2^e in the section or block
-// (|X| <= 2^22), and X is written as three balanced base-256 digits (int8).
-// Four vectors share the 16 columns of one v_mfma_i32_16x16x64_i8 B operand:
-// column 4 j + d holds digit d of vector j of the group, column 4 j + 3 is
-// zero.  The instructions of a section or block sum exactly in int32
-// (|sum| <= 2^17); one fused multiply-add by the column's power of two per
-// section or block moves the sum into a float32 accumulator.
+// X = rint(x * 2^(30 - e)) with max|x| < 2^e in the section or block
+// (|X| <= 2^30, a rounding of at most 2^(e - 31) per value), and X is
+// written as four balanced base-256 digits (int8).  Four vectors share the
+// 16 columns of one v_mfma_i32_16x16x64_i8 B operand: column 4 j + d holds
+// digit d of vector j of the group.  The instructions of a section or block
+// sum exactly in int32 (|sum| <= 2^23); one fused multiply-add by the
+// column's power of two per section or block moves the sum into a float32
+// accumulator.
 //
 // Operand area of one input (per 64-value K-step m and group G of four
 // vectors, 1 KiB: 64 lanes x 16 bytes) and the section exponents
@@ -77,20 +78,24 @@ __device__ __forceinline__ int lds_acquire(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+constexpr int kDigits = 4;       // balanced base-256 digits per value
+constexpr int kFixedBits = 30;   // |X| <= 2^30
+
 // Balanced base-256 digits of the fixed-point values of xv (exponent e of the
-// section): dw[d] byte i = digit d of value i.
-__device__ __forceinline__ void section_digits(const float (&xv)[4], int e, unsigned (&dw)[3]) {
-  dw[0] = dw[1] = dw[2] = 0u;
+// section): dw[d] byte i = digit d of value i.  |xv * 2^(30 - e)| < 2^30 is
+// an exact float32, so the rounding to an integer is the only one.
+__device__ __forceinline__ void section_digits(const float (&xv)[4], int e, unsigned (&dw)[kDigits]) {
+#pragma unroll
+  for (int d = 0; d < kDigits; ++d) dw[d] = 0u;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int X = static_cast<int>(rintf(ldexpf(xv[i], 22 - e)));  // |X| <= 2^22
-    const int d0 = ((X + 128) & 255) - 128;
-    const int X1 = (X - d0) >> 8;
-    const int d1 = ((X1 + 128) & 255) - 128;
-    const int d2 = (X1 - d1) >> 8;
-    dw[0] |= (static_cast<unsigned>(d0) & 255u) << (8 * i);
-    dw[1] |= (static_cast<unsigned>(d1) & 255u) << (8 * i);
-    dw[2] |= (static_cast<unsigned>(d2) & 255u) << (8 * i);
+    int X = static_cast<int>(rintf(ldexpf(xv[i], kFixedBits - e)));
+#pragma unroll
+    for (int d = 0; d < kDigits; ++d) {
+      const int dg = d < kDigits - 1 ? ((X + 128) & 255) - 128 : X;
+      X = (X - dg) >> 8;
+      dw[d] |= (static_cast<unsigned>(dg) & 255u) << (8 * i);
+    }
   }
 }
 
@@ -107,15 +112,15 @@ __device__ __forceinline__ void convert_int8_section(const float* xb, int sec, i
   const float4 v = reinterpret_cast<const float4*>(xb + 256 * sec)[lane];
   const int e = section_exponent(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
   const float xv[4] = {v.x, v.y, v.z, v.w};
-  unsigned dw[3];
+  unsigned dw[kDigits];
   section_digits(xv, e, dw);
   const int m = 4 * sec + static_cast<int>(lane >> 4), g = static_cast<int>((lane & 15u) >> 2);
   const int j0 = 4 * static_cast<int>(lane & 3u);
   const int G = b >> 2, n0 = 4 * (b & 3);
   unsigned char* base = ops + (static_cast<size_t>(m) * ngroups + G) * kStepBytes + (16 * g + n0) * 16 + j0;
 #pragma unroll
-  for (int d = 0; d < 4; ++d) *(g_u32*)(base + d * 16) = d < 3 ? dw[d] : 0u;
-  if (lane == 0) exps[sec * 4 * ngroups + b] = e - 22;
+  for (int d = 0; d < kDigits; ++d) *(g_u32*)(base + d * 16) = dw[d];
+  if (lane == 0) exps[sec * 4 * ngroups + b] = e - kFixedBits;
 }
 
 // Ternary levels: the same digits with one exponent per 1,024-value block
@@ -149,13 +154,13 @@ __device__ __forceinline__ void convert_ternary_block(const float* xb, int blk, 
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int sec = 4 * blk + q;
-    unsigned dw[3];
+    unsigned dw[kDigits];
     section_digits(xv[q], e, dw);
     const int m = 4 * sec + j, G = b >> 2, n0 = 4 * (b & 3);
     unsigned char* base = ops + (static_cast<size_t>(m) * ngroups + G) * kStepBytes + (16 * g + n0) * 16 + 4 * sq;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) *(g_u32*)(base + d * 16) = d < 3 ? dw[d] : 0u;
-    if (t == 0) exps[sec * 4 * ngroups + b] = e - 22;
+    for (int d = 0; d < kDigits; ++d) *(g_u32*)(base + d * 16) = dw[d];
+    if (t == 0) exps[sec * 4 * ngroups + b] = e - kFixedBits;
   }
 }
 
@@ -204,16 +209,15 @@ struct Compute {
   }
 
   // End of a 256-value section of the slice in `buf`: the exact sums scaled
-  // by this column's exponent, 2^(e + 8 d) for digit column d (the fourth
-  // column is zero, so its scale is 0).  float(sum) * 2^(e + 8 d) is exact,
-  // so the fused multiply-add rounds once, as an add of the scaled sum would.
+  // by this column's exponent, 2^(e + 8 d) for digit column d.
+  // float(sum) * 2^(e + 8 d) is exact (|sum| < 2^24), so the fused
+  // multiply-add rounds once, as an add of the scaled sum would.
   __device__ __forceinline__ void section_end(const unsigned char* buf, int sec_in_slice, v4i (&iacc)[kR][NG],
                                               v4f (&facc)[kR][NG]) const {
     const int* ex = reinterpret_cast<const int*>(buf + kOps) + sec_in_slice * kB;
-    const float keep = digit < 3 ? 1.0f : 0.0f;
 #pragma unroll
     for (int G = 0; G < NG; ++G) {
-      const float sc = ldexpf(keep, ex[4 * G + vec_in_group] + 8 * digit);
+      const float sc = ldexpf(1.0f, ex[4 * G + vec_in_group] + 8 * digit);
 #pragma unroll
       for (int r = 0; r < kR; ++r) {
         facc[r][G].x = fmaf(static_cast<float>(iacc[r][G].x), sc, facc[r][G].x);

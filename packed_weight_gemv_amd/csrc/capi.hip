@@ -206,6 +206,8 @@ int validate_step(const pwg_step_desc* d) {
   if (d->schedule != PWG_SCHEDULE_LEVELS && d->schedule != PWG_SCHEDULE_PERSISTENT &&
       d->schedule != PWG_SCHEDULE_STREAM)
     return fail(PWG_ERR_ARG, "%s: unknown schedule %d", fn, d->schedule);
+  if (d->schedule == PWG_SCHEDULE_PERSISTENT)
+    return fail(PWG_ERR_UNSUPPORTED, "%s: the persistent schedule is not available in this build", fn);
   if (d->n_levels < 0 || d->n_levels > 4096) return fail(PWG_ERR_ARG, "%s: n_levels out of range", fn);
   if (d->weight_layout != PWG_LAYOUT_ROWS && d->weight_layout != PWG_LAYOUT_TILED)
     return fail(PWG_ERR_ARG, "%s: unknown weight layout %d", fn, d->weight_layout);
@@ -263,7 +265,8 @@ extern "C" size_t pwg_step_workspace_bytes(const pwg_step_desc* d) {
     return step_batch_workspace(d);
   }
   if (d->schedule == PWG_SCHEDULE_STREAM) return step_stream_workspace(d);
-  return argmax_ws(d->vocab, 1) + step_persistent_workspace(d);
+  if (d->schedule != PWG_SCHEDULE_LEVELS) return 0;
+  return argmax_ws(d->vocab, 1);
 }
 
 extern "C" int pwg_step_plan(const pwg_step_desc* d, void* stream) {
@@ -273,7 +276,6 @@ extern "C" int pwg_step_plan(const pwg_step_desc* d, void* stream) {
                 pwg_step_workspace_bytes(d));
   if (batched(d)) return step_batch_plan(d, stream);
   if (d->schedule == PWG_SCHEDULE_STREAM) return step_stream_plan(d, 0, stream);
-  if (d->schedule != PWG_SCHEDULE_LEVELS) return step_persistent_plan(d, argmax_ws(d->vocab, 1), stream);
   return PWG_OK;
 }
 
@@ -281,8 +283,7 @@ extern "C" int pwg_step_status(const pwg_step_desc* d, void* stream) {
   TRY(validate_step(d));
   if (d->schedule == PWG_SCHEDULE_LEVELS) return PWG_OK;
   if (batched(d)) return step_batch_status(d, stream);
-  if (d->schedule == PWG_SCHEDULE_STREAM) return step_stream_status(d, 0, stream);
-  return step_persistent_status(d, argmax_ws(d->vocab, 1), stream);
+  return step_stream_status(d, 0, stream);
 }
 
 extern "C" int pwg_decode_step_weights(const pwg_step_desc* d, void* stream) {
@@ -292,7 +293,6 @@ extern "C" int pwg_decode_step_weights(const pwg_step_desc* d, void* stream) {
                 pwg_step_workspace_bytes(d));
   if (batched(d)) return step_batch_launch(d, stream);
   if (d->schedule == PWG_SCHEDULE_STREAM) return step_stream_launch(d, 0, stream);
-  if (d->schedule != PWG_SCHEDULE_LEVELS) return step_persistent_launch(d, argmax_ws(d->vocab, 1), stream);
   // Levels schedule: embedding row, every level in decoder order, output
   // projection + argmax, all on one stream.
   TRY(launch_embed_gather(d->emb_table, d->emb_scale, d->vocab, d->hidden, d->token_in, 1, d->emb_row_out,

@@ -103,7 +103,13 @@ __device__ __forceinline__ void form_input(const DevInput& in, int n, float* v, 
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int i = base + u * T + tid;
-        if (i < hi) v[i] = g[u] / (1.0f + expf(-g[u])) * up[u];
+        if (i < hi) {
+          // silu(g) = g * sigmoid(g), with sigmoid from e^-|g| in (0, 1]: no
+          // overflow for very negative g (g / (1 + e^-g) would give 0 there)
+          const float gv = g[u], ez = expf(-fabsf(gv));
+          const float sig = gv >= 0.f ? 1.0f / (1.0f + ez) : ez / (1.0f + ez);
+          v[i] = gv * sig * up[u];
+        }
       }
     }
     __syncthreads();

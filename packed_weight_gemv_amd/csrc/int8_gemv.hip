@@ -9,8 +9,9 @@
 //
 // Stage 1 (one kernel): every wave streams a contiguous range of table rows
 // (64 lanes x 16 B = 1 KiB per load instruction, four per 4,096-byte row),
-// forms each logit exactly in integers with v_dot4_i32_i8 against three int8
-// limbs of the fixed-point hidden state, keeps a running (max, lowest index),
+// forms each logit with v_dot4_i32_i8 against five int8 limbs of the hidden
+// state rounded to 39-bit fixed point per 16-element chunk (exact integer
+// sums per limb and chunk, then float32), keeps a running (max, lowest index),
 // and each workgroup writes one 64-bit key.  Stage 2 (one workgroup) reduces
 // the keys.  Both stages use a fixed reduction order, so the token is
 // reproducible bit for bit.
@@ -34,7 +35,7 @@ __global__ __launch_bounds__(WPB * 64) void int8_gemv_argmax_kernel(const u32x4*
   i8_prepare_x(h, cols, lds, lds_e);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  unsigned H[C][12];
+  unsigned H[C][kI8ChunkDwords];
   int Ec[C];  // -E_c
 #pragma unroll
   for (int c = 0; c < C; ++c) {
@@ -43,13 +44,13 @@ __global__ __launch_bounds__(WPB * 64) void int8_gemv_argmax_kernel(const u32x4*
     if (chunk < nchunks) {
       const u32x4* src = reinterpret_cast<const u32x4*>(lds + chunk * kI8ChunkDwords);
 #pragma unroll
-      for (int q = 0; q < 3; ++q) {
+      for (int q = 0; q < kI8Limbs; ++q) {
         const u32x4 v = src[q];
         H[c][4 * q + 0] = v.x; H[c][4 * q + 1] = v.y; H[c][4 * q + 2] = v.z; H[c][4 * q + 3] = v.w;
       }
     } else {
 #pragma unroll
-      for (int q = 0; q < 12; ++q) H[c][q] = 0u;
+      for (int q = 0; q < kI8ChunkDwords; ++q) H[c][q] = 0u;
     }
   }
 
@@ -78,16 +79,19 @@ __global__ __launch_bounds__(WPB * 64) void int8_gemv_argmax_kernel(const u32x4*
       float part = 0.f;
 #pragma unroll
       for (int c = 0; c < C; ++c) {
-        int a0 = 0, a1 = 0, a2 = 0;
+        int a[kI8Limbs];
         const unsigned qd[4] = {Q[u][c].x, Q[u][c].y, Q[u][c].z, Q[u][c].w};
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          a0 = dot4(qd[g], H[c][3 * g + 0], a0);
-          a1 = dot4(qd[g], H[c][3 * g + 1], a1);
-          a2 = dot4(qd[g], H[c][3 * g + 2], a2);
+        for (int l = 0; l < kI8Limbs; ++l) {
+          a[l] = 0;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) a[l] = dot4(qd[g], H[c][4 * l + g], a[l]);
         }
-        // each limb sum is exact in float32 (|a| <= 16*127*128 < 2^24); the shifts are exact
-        const float p = fmaf(static_cast<float>(a2), 65536.0f, fmaf(static_cast<float>(a1), 256.0f, static_cast<float>(a0)));
+        // each limb sum is exact in float32 (|a| <= 16*127*128 < 2^24) and so
+        // is its scaling; the float32 sum of the scaled limbs rounds
+        float p = static_cast<float>(a[kI8Limbs - 1]);
+#pragma unroll
+        for (int l = kI8Limbs - 2; l >= 0; --l) p = fmaf(p, 256.0f, static_cast<float>(a[l]));
         part += ldexpf(p, Ec[c]);
       }
       const float total = group_sum<64>(part);
@@ -144,6 +148,29 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const unsigned long 
     unsigned long long m = wk[0];
     for (int i = 1; i < 4; ++i) m = wk[i] > m ? wk[i] : m;
     token[0] = static_cast<int32_t>(argmax_key_index(m));
+  }
+}
+
+// Stage 2 for several vectors: block b reduces vector b's keys.
+__global__ __launch_bounds__(256) void argmax_reduce_batch_kernel(const unsigned long long* __restrict__ partials,
+                                                                  int n, size_t nparts, int32_t* __restrict__ token) {
+  const unsigned long long* pb = partials + static_cast<size_t>(blockIdx.x) * nparts;
+  unsigned long long k = 0ull;
+  for (int i0 = 0; i0 < n; i0 += 256) {
+    const int i = i0 + static_cast<int>(threadIdx.x);
+    if (i < n) k = pb[i] > k ? pb[i] : k;
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned long long o = __shfl_xor(k, off, kWave);
+    k = o > k ? o : k;
+  }
+  __shared__ unsigned long long wk[4];
+  if ((threadIdx.x & 63) == 0) wk[threadIdx.x >> 6] = k;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long m = wk[0];
+    for (int i = 1; i < 4; ++i) m = wk[i] > m ? wk[i] : m;
+    token[blockIdx.x] = static_cast<int32_t>(argmax_key_index(m));
   }
 }
 
@@ -238,7 +265,6 @@ int launch_int8_gemv_argmax(const int8_t* table, const float* s, int64_t rows, i
     return launch_i8b(table, false, s, rows, cols, h, batch, parts, nparts,
                       static_cast<unsigned char*>(ws) + nparts * sizeof(unsigned long long) * batch, logits, token, stream);
   }
-  if (batch > 1) return launch_int8_gemv_argmax_batch(table, s, rows, cols, h, batch, ws, token, logits, stream);
   I8Instance* in = pick_i8(static_cast<int>(cols));
   const size_t lds = i8_lds_bytes(cols);
   unsigned grid = i8_grid(in, rows, lds);
@@ -261,6 +287,15 @@ int launch_int8_gemv_argmax(const int8_t* table, const float* s, int64_t rows, i
     e = hipLaunchKernel(reinterpret_cast<const void*>(&argmax_reduce_kernel), dim3(1), dim3(256), args2, 0, st);
     if (e != hipSuccess) return fail(PWG_ERR_HIP, "argmax_reduce launch: %s", hipGetErrorString(e));
   }
+  return PWG_OK;
+}
+
+int launch_argmax_reduce_batch(const unsigned long long* partials, int n, size_t nparts, int32_t batch, int32_t* token,
+                               void* stream) {
+  void* args[] = {const_cast<unsigned long long**>(&partials), &n, &nparts, &token};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&argmax_reduce_batch_kernel), dim3(batch), dim3(256),
+                                       args, 0, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PWG_ERR_HIP, "argmax_reduce (batch) launch: %s", hipGetErrorString(e));
   return PWG_OK;
 }
 

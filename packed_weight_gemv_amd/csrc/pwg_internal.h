@@ -21,8 +21,8 @@ void clear_error();
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool valid_batch(int32_t b) { return b == 1 || b == 4 || b == 8 || b == 16; }
 inline bool valid_cols(int64_t cols) { return cols >= 64 && cols % 64 == 0 && cols <= PWG_MAX_COLS; }
-// The int8 kernels keep 48 dwords of activation limbs per 4,096 columns in
-// VGPRs; beyond 8,192 columns they would spill.
+// The VALU int8 kernel keeps 80 dwords of activation limbs per 4,096 columns
+// in VGPRs; beyond 8,192 columns they would spill.
 constexpr int64_t kMaxInt8Cols = 8192;
 
 // Launchers (asynchronous, arguments already validated).
@@ -32,12 +32,9 @@ int launch_int8_gemv_argmax(const int8_t* table, const float* s, int64_t rows, i
                             const float* h, int32_t batch, void* ws, int32_t* token,
                             float* logits, void* stream);
 size_t int8_partials(int64_t rows);
-// Weight-stationary variants for batch > 1 (batch_gemv.hip).
-int launch_ternary_gemv_batch(const void* w, const float* s, int64_t rows, int64_t cols,
-                              const float* x, int32_t batch, float* y, void* stream);
-int launch_int8_gemv_argmax_batch(const int8_t* table, const float* s, int64_t rows, int64_t cols,
-                                  const float* h, int32_t batch, void* ws, int32_t* token,
-                                  float* logits, void* stream);
+// Batch-1 ternary GEMV on the tiled arrangement (gemv_mfma.hip).
+int launch_ternary_gemv_tiled1(const void* w, const float* s, int64_t rows, int64_t cols, const float* x, float* y,
+                               void* stream);
 int launch_argmax_reduce_batch(const unsigned long long* partials, int n, size_t nparts, int32_t batch, int32_t* token,
                                void* stream);
 // Matrix-core variant of the batched int8 projection (batch_mfma.hip): for
@@ -53,7 +50,6 @@ int launch_t2b(const void* w_tiled, const float* s, int64_t rows, int64_t cols, 
 int launch_i8b(const int8_t* table, bool tiled, const float* s, int64_t rows, int64_t cols, const float* h,
                int32_t batch, unsigned long long* partials, size_t nparts, unsigned char* ops_area, float* logits,
                int32_t* token, void* stream);
-size_t t2_lds_bytes(int64_t cols);
 size_t i8_lds_bytes(int64_t cols);
 // Decode attention over a bfloat16 KV cache (attention.hip).
 bool attention_supported(int n_heads, int n_kv, int head_dim);
@@ -72,12 +68,6 @@ int launch_embed_gather(const int8_t* table, const float* s, int64_t rows, int64
                         const int32_t* ids, int32_t n, int8_t* rows_out, float* scales_out,
                         float* deq_out, void* stream);
 
-// Persistent (single-kernel) step schedule.  `ws_offset` is where its part of
-// the step workspace starts (the argmax partials come first).
-size_t step_persistent_workspace(const pwg_step_desc* d);
-int step_persistent_plan(const pwg_step_desc* d, size_t ws_offset, void* stream);
-int step_persistent_launch(const pwg_step_desc* d, size_t ws_offset, void* stream);
-int step_persistent_status(const pwg_step_desc* d, size_t ws_offset, void* stream);
 
 // Stream schedule on the matrix cores (step_stream.hip): tiled weights.
 int step_stream_check(const pwg_step_desc* d);

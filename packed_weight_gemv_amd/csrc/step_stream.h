@@ -5,15 +5,14 @@
 #include <cstdint>
 
 #include "device_common.h"
+#include "operands.h"
 
 namespace pwg {
 namespace stream {
 
-// Operand bytes of one MFMA: ternary B = 4 lane groups x 12 digit columns x
-// 16 bytes (32 FP4 nibbles); int8 B = 4 lane groups x 3 digit columns x 16 bytes.
-constexpr int kTernaryMfmaBytes = 4 * 12 * 16;
-constexpr int kInt8MfmaBytes = 4 * 3 * 16;
-constexpr int kSectionMfmas = 4;                  // int8 MFMAs per exponent section (256 values of h)
+using ops::kTernaryMfmaBytes;
+using ops::kInt8MfmaBytes;
+using ops::kSectionMfmas;
 constexpr int kMaxStreamCols = 12288;             // two operand buffers of this width fit in LDS
 constexpr size_t kMaxLds = 160 * 1024;
 constexpr int kStreamWaves = 8;                   // waves per workgroup (two control waves)
@@ -38,19 +37,15 @@ constexpr size_t kLdsTailBytes = kSegOffOff + 8 * kMaxSegs;
 constexpr size_t kParkBytes = 16 * 1024;          // tiles a wave re-reads after its last one
 enum { kKindTernary = 0, kKindInt8 = 1 };
 
-// Ternary level region (per K = cols): B digits of every MFMA, then the B
-// scale dwords (per group of 4 MFMAs, one per lane), then the A scale dwords
-// (per group of 4 MFMAs, one per lane group).  One scale byte per MFMA.
-__host__ __device__ constexpr size_t ternary_mfmas(int64_t cols) { return static_cast<size_t>(cols / 128); }
-__host__ __device__ constexpr size_t ternary_quads(int64_t cols) { return (ternary_mfmas(cols) + 3) / 4; }
-__host__ __device__ constexpr size_t ternary_bsc_off(int64_t cols) { return ternary_mfmas(cols) * kTernaryMfmaBytes; }
-__host__ __device__ constexpr size_t ternary_asc_off(int64_t cols) { return ternary_bsc_off(cols) + ternary_quads(cols) * 256; }
-__host__ __device__ constexpr size_t ternary_region_bytes(int64_t cols) { return ternary_asc_off(cols) + ternary_quads(cols) * 16; }
-// int8 (h) region: B digits of every MFMA, then one int32 exponent per section.
-__host__ __device__ constexpr size_t int8_exp_off(int64_t hidden) { return static_cast<size_t>(hidden / 64) * kInt8MfmaBytes; }
-__host__ __device__ constexpr size_t int8_region_bytes(int64_t hidden) {
-  return (int8_exp_off(hidden) + static_cast<size_t>((hidden / 64 + kSectionMfmas - 1) / kSectionMfmas) * 4 + 15) / 16 * 16;
-}
+// Operand regions (operands.h): the ternary levels' FP8 pieces of x and the
+// vocabulary's base-256 digits of h.
+using ops::ternary_mfmas;
+using ops::ternary_quads;
+using ops::ternary_bsc_off;
+using ops::ternary_asc_off;
+using ops::ternary_region_bytes;
+using ops::int8_exp_off;
+using ops::int8_region_bytes;
 static_assert(ternary_region_bytes(kMaxStreamCols) % 16 == 0, "regions are copied in 16-byte units");
 
 // One ternary level or (last entry) the vocabulary.

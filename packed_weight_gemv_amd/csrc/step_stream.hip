@@ -9,22 +9,24 @@
 // the stored values for the device at load time: here, 16-row x 64-byte
 // tiles, one 1 KiB tile per wave load instruction).
 //
-// Ternary levels run on v_mfma_scale_f32_16x16x128_f8f6f4 with both operands
-// in FP4 (e2m1).  Operand A is 16 weight rows x 128 weights: masking a T2
-// word with 0xCCCCCCCC, and again after a 2-bit left shift, leaves nibbles
-// 0b0100 / 0b1100 / 0 for w = +1 / -1 / 0, which are the FP4 values +2, -2
-// and 0, so a 16-byte tile slice becomes the A operands of two instructions
-// with three VALU operations per word.  Operand B is 128 x 16: column n holds
-// base-4 digit n (n < 12) of the activations rounded to 23-bit fixed point per
-// 32-element block, with the sign applied; the E8M0 block scales (one per 32
-// K-values and operand lane) carry the block exponent and the digit weight.
-// Digits and weights are small integers, so every product is exact; the
-// instruction sums in float32.
+// Ternary levels run on v_mfma_scale_f32_16x16x128_f8f6f4 with A in FP4
+// (e2m1) and B in FP8 (e4m3).  Operand A is 16 weight rows x 128 weights:
+// masking a T2 word with 0xCCCCCCCC, and again after a 2-bit left shift,
+// leaves nibbles 0b0100 / 0b1100 / 0 for w = +1 / -1 / 0, which are the FP4
+// values +2, -2 and 0, so a 16-byte tile slice becomes the A operands of two
+// instructions with three VALU operations per word.  Operand B is 128 x 16:
+// column j < 6 holds e4m3 piece j of the activations (operands.h: six pieces
+// of four significant bits, each with its own exponent per value, that sum to
+// x exactly); the E8M0 block scales (one per 32 K-values and column) carry
+// the block exponent and the piece's weight.  Every product is exact; the
+// instruction sums in float32.  The instruction's destination must not share
+// registers with its A or B operands (with an FP8 operand that gives wrong
+// sums on gfx950), so every operand stays live past its instruction.
 //
 // The int8 output projection runs on v_mfma_i32_16x16x64_i8: A is the tile
-// as stored, B's columns are three balanced base-256 digits of h rounded to
-// 23-bit fixed point per 256-element section; four instructions accumulate
-// exactly in int32 before one conversion to float per section.
+// as stored, B's columns are six balanced base-256 digits of h rounded to
+// 47-bit fixed point per 256-element section; four instructions accumulate
+// exactly in int32 before one conversion to float per section and column.
 //
 // Work: 16-row blocks of every level and of the vocabulary.  Each workgroup
 // (one per CU) first takes a contiguous range of the ternary levels of equal
@@ -42,6 +44,7 @@
 #include <vector>
 
 #include "device_common.h"
+#include "operands.h"
 #include "pwg_internal.h"
 #include "step_stream.h"
 
@@ -50,6 +53,9 @@ namespace {
 
 using namespace dev;
 using namespace stream;
+using ops::block_scales;
+using ops::row16_sum;
+using ops::ternary_unpack;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -59,7 +65,6 @@ constexpr int kWaves = kStreamWaves;     // wave 0 claims pool blocks, wave 1 st
 constexpr int kControl = 2;
 constexpr int kCompute = kWaves - kControl;
 constexpr int kThreads = kWaves * 64;
-constexpr unsigned kMask = 0xCCCCCCCCu;
 constexpr unsigned long long kSpinLimit = 50000000ull;  // 0.5 s of the 100 MHz real-time counter
 enum : unsigned { kStatusOk = 0, kStatusTimeout = 1 };
 
@@ -92,15 +97,6 @@ __device__ __forceinline__ void lds_publish(int* p, int v) {
 }
 __device__ __forceinline__ int lds_acquire(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
-// Sum over the 16 lanes of a DPP row; every lane ends with the same total.
-__device__ __forceinline__ float row16_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // lane ^ 1
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // lane ^ 2
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // half mirror
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // mirror
-  return v;
 }
 
 // The producer half of a compute wave: issues the 1 KiB tile loads of the
@@ -146,37 +142,33 @@ __device__ __forceinline__ int block_rot(int blk, int T) {
   return ((blk * 5) % (T / G)) * G;
 }
 
-// A operands of one ternary tile slice: FP4 nibbles +2 / -2 / 0 of the 64
-// weights in this lane's 16 bytes (two MFMAs' worth).
-__device__ __forceinline__ void ternary_unpack(const u32x4 v, v8i& a0, v8i& a1) {
-  a0 = v8i{static_cast<int>(v.x & kMask), static_cast<int>((v.x << 2) & kMask), static_cast<int>(v.y & kMask),
-           static_cast<int>((v.y << 2) & kMask), 0, 0, 0, 0};
-  a1 = v8i{static_cast<int>(v.z & kMask), static_cast<int>((v.z << 2) & kMask), static_cast<int>(v.w & kMask),
-           static_cast<int>((v.w << 2) & kMask), 0, 0, 0, 0};
-}
-
-// Two FP4 MFMAs over K-values 256 t .. 256 t + 255 of a ternary block.
+// Two FP4 x FP8 MFMAs over K-values 256 t .. 256 t + 255 of a ternary block.
 // buf: the level's operand region in LDS; kOdd: t is odd (the scale bytes of
 // MFMAs 2t, 2t + 1 are then bytes 2 and 3 of the dwords read at t - 1).
 template <bool kOdd>
 __device__ __forceinline__ void ternary_mfma(const v8i& a0, const v8i& a1, int t, const unsigned char* buf,
                                              int bsc_off, int asc_off, unsigned boff, unsigned lane, unsigned g,
                                              unsigned& sb, unsigned& sa, v4f& acc0, v4f& acc1) {
-  const u32x4 b0 = *reinterpret_cast<const u32x4*>(buf + (2 * t) * kTernaryMfmaBytes + boff);
-  const u32x4 b1 = *reinterpret_cast<const u32x4*>(buf + (2 * t + 1) * kTernaryMfmaBytes + boff);
+  const u32x4* p0 = reinterpret_cast<const u32x4*>(buf + (2 * t) * kTernaryMfmaBytes + boff);
+  const u32x4* p1 = reinterpret_cast<const u32x4*>(buf + (2 * t + 1) * kTernaryMfmaBytes + boff);
+  const u32x4 b0 = p0[0], b0h = p0[1], b1 = p1[0], b1h = p1[1];
   if (!kOdd) {  // scales of MFMAs 2t .. 2t + 3 (one byte each)
     sb = *reinterpret_cast<const unsigned*>(buf + bsc_off + (t >> 1) * 256 + lane * 4);
     sa = *reinterpret_cast<const unsigned*>(buf + asc_off + (t >> 1) * 16 + g * 4);
   }
-  const v8i B0 = {static_cast<int>(b0.x), static_cast<int>(b0.y), static_cast<int>(b0.z), static_cast<int>(b0.w), 0, 0, 0, 0};
-  const v8i B1 = {static_cast<int>(b1.x), static_cast<int>(b1.y), static_cast<int>(b1.z), static_cast<int>(b1.w), 0, 0, 0, 0};
+  const v8i B0 = {static_cast<int>(b0.x), static_cast<int>(b0.y), static_cast<int>(b0.z), static_cast<int>(b0.w),
+                  static_cast<int>(b0h.x), static_cast<int>(b0h.y), static_cast<int>(b0h.z), static_cast<int>(b0h.w)};
+  const v8i B1 = {static_cast<int>(b1.x), static_cast<int>(b1.y), static_cast<int>(b1.z), static_cast<int>(b1.w),
+                  static_cast<int>(b1h.x), static_cast<int>(b1h.y), static_cast<int>(b1h.z), static_cast<int>(b1h.w)};
   if (kOdd) {
-    acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, B0, acc0, 4, 4, 2, static_cast<int>(sa), 2, static_cast<int>(sb));
-    acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, B1, acc1, 4, 4, 3, static_cast<int>(sa), 3, static_cast<int>(sb));
+    acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, B0, acc0, 4, 0, 2, static_cast<int>(sa), 2, static_cast<int>(sb));
+    acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, B1, acc1, 4, 0, 3, static_cast<int>(sa), 3, static_cast<int>(sb));
   } else {
-    acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, B0, acc0, 4, 4, 0, static_cast<int>(sa), 0, static_cast<int>(sb));
-    acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, B1, acc1, 4, 4, 1, static_cast<int>(sa), 1, static_cast<int>(sb));
+    acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, B0, acc0, 4, 0, 0, static_cast<int>(sa), 0, static_cast<int>(sb));
+    acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, B1, acc1, 4, 0, 1, static_cast<int>(sa), 1, static_cast<int>(sb));
   }
+  // operands live past the instructions: no destination shares their registers
+  asm volatile("" ::"v"(a0), "v"(a1), "v"(B0), "v"(B1));
 }
 
 // One int8 MFMA over K-values 64 t .. 64 t + 63 of a vocabulary block.
@@ -191,35 +183,12 @@ __device__ __forceinline__ void int8_mfma(const u32x4 v, int t, const unsigned c
 __device__ __forceinline__ void int8_section(int t, const unsigned char* buf, int exp_off, int cexp, v4i& iacc,
                                              v4f& facc) {
   const int e = *reinterpret_cast<const int*>(buf + exp_off + (t / kSectionMfmas) * 4) + cexp;
-  // |iacc| <= 4 * 64 * 127 * 128 < 2^24: the conversion is exact
+  // |iacc| <= 4 * 64 * 127 * 128 < 2^23: the conversion is exact
   facc.x += ldexpf(static_cast<float>(iacc.x), e);
   facc.y += ldexpf(static_cast<float>(iacc.y), e);
   facc.z += ldexpf(static_cast<float>(iacc.z), e);
   facc.w += ldexpf(static_cast<float>(iacc.w), e);
   iacc = v4i{0, 0, 0, 0};
-}
-
-// The 16 row scales of block `blk` (rows 16 blk .. 16 blk + 15, clamped to
-// rows - 1) through scalar loads; returns the scale of row 4 g + i.
-__device__ __forceinline__ v4f block_scales(const float* scale, int blk, int rows, unsigned g) {
-  cfloat* s = (cfloat*)scale;
-  float r[16];
-  const int base = blk * 16;
-  if (base + 16 <= rows) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) r[i] = s[base + i];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) r[i] = s[base + i < rows ? base + i : rows - 1];
-  }
-  // (readfirstlane keeps the values in scalar registers: otherwise the
-  // per-lane choice below becomes a per-lane vector load)
-#pragma unroll
-  for (int i = 0; i < 16; ++i) r[i] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(r[i])));
-  v4f out;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) out[i] = g == 0 ? r[i] : g == 1 ? r[4 + i] : g == 2 ? r[8 + i] : r[12 + i];
-  return out;
 }
 
 // Embedding row of the previous token (workgroup 0, control wave).
@@ -521,9 +490,9 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
     u32x4 ra[GR], rb[GR];
     if (G > 0) pr.template issue<GR>(ra);
 
-    const unsigned tboff = (12u * g + (n < 12u ? n : n - 12u)) * 16u;  // ternary B entry of this lane
-    const unsigned iboff = (3u * g + n % 3u) * 16u;                    // int8 B entry of this lane
-    const int icexp = n < 3u ? static_cast<int>(8u * n) : -1000;       // digit weight (columns >= 3 vanish)
+    const unsigned tboff = ops::ternary_b_entry(n, g);                 // ternary B entry of this lane
+    const unsigned iboff = ops::int8_b_entry(n, g);                    // int8 B entry of this lane
+    const int icexp = n < static_cast<unsigned>(ops::kInt8Digits) ? static_cast<int>(8u * n) : -1000;  // digit weight (other columns vanish)
     int cur = -1;  // segment whose operands this wave is using
     const unsigned char* buf = smem;
     int T = 0, rows = 0, kind = 0, bsc_off = 0, asc_off = 0;
@@ -625,7 +594,8 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
       const v4f sc = block_scales(scale, blk, rows, g);
       v4f a = kind == kKindTernary ? acc0 + acc1 : acc0;  // rows 4g + i, digit column n
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = row16_sum(kind != kKindTernary || n < 12u ? a[i] : 0.f) * sc[i];
+      for (int i = 0; i < 4; ++i)
+        a[i] = row16_sum(kind != kKindTernary || n < static_cast<unsigned>(ops::kSplits) ? a[i] : 0.f) * sc[i];
       const int r0 = blk * 16 + static_cast<int>(4 * g);
       if (n == 0) {
         if (y) {
@@ -692,56 +662,24 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
 }
 
 // --------------------------------------------------------------- conversion
-// Bit offset of weight-in-block κ's nibble: the T2 word masks deliver, in A
-// dword dd, nibble p = the weight with index κ(dd, p) of the 32-weight block
-// (dd = 0, 2: the odd weights of a nibble pair; dd = 1, 3: the even ones).
-__device__ __forceinline__ int kappa(int dd, int p) { return 16 * (dd >> 1) + 8 * (p & 1) + 2 * (p >> 1) + (1 - (dd & 1)); }
-
-// Ternary level input: thread (β, cg) of level L converts 32-element block β
-// (digit columns 3 cg .. 3 cg + 2) into the B operand entries of MFMA
-// m = 2 (β / 8) + β % 2, lane group g = (β % 8) / 2, and their scale bytes.
-__device__ void convert_ternary(const Level& L, int tid) {
-  const int beta = tid >> 2, cg = tid & 3;
-  if (beta >= L.cols / 32) return;
-  const cg_f32x4* xs = (const cg_f32x4*)(L.x + 32 * beta);
-  float x[32];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const f32x4 v = xs[q];
-    x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
-  }
+// Ternary level input: thread (beta, h) of level L converts half h of the
+// 32-element block beta (operands.h); the two halves of a block are adjacent
+// lanes and share the block exponent.
+__device__ void convert_ternary(const Level& L, int tid, unsigned lane) {
+  const int beta = tid >> 1, h = tid & 1;
+  const bool ok = beta < L.cols / 32;
+  float xs[16];
   float amax = 0.f;
+  const cg_f32x4* src = (const cg_f32x4*)(L.x + 32 * (ok ? beta : 0) + 16 * h);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  const int e = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) : 0;  // amax < 2^e
-  unsigned X[32];
-  unsigned S[4] = {0u, 0u, 0u, 0u};  // sign bits (bit 3 of each nibble) in A nibble order
-#pragma unroll
-  for (int i = 0; i < 32; ++i) X[i] = static_cast<unsigned>(rintf(ldexpf(fabsf(x[i]), 23 - e)));  // <= 2^23
-#pragma unroll
-  for (int dd = 0; dd < 4; ++dd)
-#pragma unroll
-    for (int p = 0; p < 8; ++p) S[dd] |= (x[kappa(dd, p)] < 0.f ? 8u : 0u) << (4 * p);
-  const int t = e - 24;                     // exponent of digit column 0 (includes A's factor 2)
-  const int ashift = t + 127 < 0 ? t + 127 : 0;
-  const int m = 2 * (beta >> 3) + (beta & 1), g = (beta & 7) >> 1;
-  unsigned char* b = L.b_out;
-  for (int n = 3 * cg; n < 3 * cg + 3; ++n) {
-    unsigned w[4];
-#pragma unroll
-    for (int dd = 0; dd < 4; ++dd) {
-      unsigned dg = 0;
-#pragma unroll
-      for (int p = 0; p < 8; ++p) dg |= ((X[kappa(dd, p)] >> (2 * n)) & 3u) << (4 * p);
-      // digit d -> FP4 code 2d - [d == 3] (0, 1.0, 2.0, 3.0), then the sign bit
-      w[dd] = ((dg << 1) - ((dg >> 1) & dg & 0x11111111u)) | S[dd];
-    }
-    *reinterpret_cast<u32x4*>(b + m * kTernaryMfmaBytes + (12 * g + n) * 16) = u32x4{w[0], w[1], w[2], w[3]};
-    b[L.bsc_off + (m >> 2) * 256 + 4 * (16 * g + n) + (m & 3)] = static_cast<unsigned char>(127 + t + 2 * n - ashift);
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 v = ok ? src[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+    xs[4 * q] = v.x; xs[4 * q + 1] = v.y; xs[4 * q + 2] = v.z; xs[4 * q + 3] = v.w;
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
   }
-  if (cg == 3)
-    for (int n = 12; n < 16; ++n) b[L.bsc_off + (m >> 2) * 256 + 4 * (16 * g + n) + (m & 3)] = 0;  // 2^-127
-  if (cg == 0) b[L.asc_off + (m >> 2) * 16 + 4 * g + (m & 3)] = static_cast<unsigned char>(127 + ashift);
+  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+  (void)lane;
+  if (ok) ops::write_ternary_half(L.b_out, L.bsc_off, L.asc_off, beta, h, xs, ops::block_exponent(amax));
 }
 
 // Vocabulary input h: wave `sec` converts section sec (256 elements); lane
@@ -750,31 +688,22 @@ __device__ void convert_int8(const Level& L, const float* h, int sec, unsigned l
   const f32x4 v = ((const cg_f32x4*)(h + 256 * sec))[lane];
   float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
-  const int e = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) : 0;
-  const float xv[4] = {v.x, v.y, v.z, v.w};
-  unsigned dw[3] = {0u, 0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int X = static_cast<int>(rintf(ldexpf(xv[i], 22 - e)));  // |X| <= 2^22
-    const int d0 = ((X + 128) & 255) - 128;
-    const int X1 = (X - d0) >> 8;
-    const int d1 = ((X1 + 128) & 255) - 128;
-    const int d2 = (X1 - d1) >> 8;
-    dw[0] |= (static_cast<unsigned>(d0) & 255u) << (8 * i);
-    dw[1] |= (static_cast<unsigned>(d1) & 255u) << (8 * i);
-    dw[2] |= (static_cast<unsigned>(d2) & 255u) << (8 * i);
-  }
+  const int e = ops::block_exponent(amax);
+  const float hv[4] = {v.x, v.y, v.z, v.w};
+  unsigned dw[ops::kInt8Digits];
+  ops::int8_digits4(hv, e, dw);
   const int m = 4 * sec + static_cast<int>(lane >> 4), g = static_cast<int>((lane & 15u) >> 2), j0 = 4 * static_cast<int>(lane & 3u);
   unsigned char* b = L.b_out;
 #pragma unroll
-  for (int d = 0; d < 3; ++d) *reinterpret_cast<unsigned*>(b + m * kInt8MfmaBytes + (3 * g + d) * 16 + j0) = dw[d];
-  if (lane == 0) *reinterpret_cast<int*>(b + L.bsc_off + 4 * sec) = e - 22;
+  for (int d = 0; d < ops::kInt8Digits; ++d)
+    *reinterpret_cast<unsigned*>(b + m * kInt8MfmaBytes + ops::int8_b_entry(d, g) + j0) = dw[d];
+  if (lane == 0) *reinterpret_cast<int*>(b + L.bsc_off + 4 * sec) = e - ops::kInt8FixedBits;
 }
 
 // One-dimensional grid: the workgroups of level i are conv0(i) ..
-// conv0(i + 1) - 1 (ternary: 64 blocks of 32 inputs per workgroup; the
-// vocabulary: four 256-value sections of h, one per wave); the plan's table
-// names each workgroup's level.
+// conv0(i + 1) - 1 (ternary: 128 blocks of 32 inputs per workgroup, two
+// threads per block; the vocabulary: four 256-value sections of h, one per
+// wave); the plan's table names each workgroup's level.
 __global__ __launch_bounds__(256) void stream_convert_kernel(const Plan* __restrict__ plan,
                                                              const Level* __restrict__ levels) {
   const Plan& P = *plan;
@@ -783,7 +712,7 @@ __global__ __launch_bounds__(256) void stream_convert_kernel(const Plan* __restr
   const Level& L = levels[lo];
   const int local = wg - L.conv0;
   if (lo < P.n_levels) {
-    convert_ternary(L, local * 256 + static_cast<int>(threadIdx.x));
+    convert_ternary(L, local * 256 + static_cast<int>(threadIdx.x), threadIdx.x & 63u);
   } else {
     const int sec = local * 4 + static_cast<int>(threadIdx.x >> 6);
     if (sec < P.hidden / 256) convert_int8(L, P.h, sec, threadIdx.x & 63u);
@@ -802,10 +731,10 @@ struct SLayout {
   size_t plan, partials, arrivals, levels, segs, seg_count, conv_level, park, regions, total;
 };
 
-// Conversion workgroups of level i (the vocabulary: i == n_levels): 4
+// Conversion workgroups of level i (the vocabulary: i == n_levels): 2
 // threads per 32-input ternary block, one wave per 256-value section of h.
 int conv_blocks(const pwg_step_desc* d, int i) {
-  if (i < d->n_levels) return static_cast<int>((d->levels[i].cols / 32 * 4 + 255) / 256);
+  if (i < d->n_levels) return static_cast<int>((d->levels[i].cols / 32 * 2 + 255) / 256);
   return static_cast<int>((d->hidden / 256 + 3) / 4);
 }
 

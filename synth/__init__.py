@@ -197,3 +197,30 @@ def kv_cache(layer: int, ctx: int, n_kv: int = KV_HEADS, head_dim: int = HEAD_DI
     v = bf16_bits(rng.standard_normal((ctx, n_kv, head_dim)).astype(np.float32))
     q = rng.standard_normal(4 * n_kv * head_dim).astype(np.float32)
     return q, k, v
+
+
+W_OUTLIER = 7  # workload id of the outlier activation vectors
+
+
+def outlier_vector(n: int, seed: int, background: str = "normal", n_outliers: int = 6, n_quiet: int = 2) -> np.ndarray:
+    """An activation vector with massive outliers, as decoder hidden states
+    carry them: a background of N(0, 1) values ("normal") or of N(0, 1) x 1e-3
+    values ("small"); `n_outliers` positions set to +-3e3 or +-1e4; and
+    `n_quiet` aligned 64-value stretches whose values are U(-1e-3, 1e-3)
+    except one +-1e4 outlier at a random place inside (an outlier among small
+    values).  float32; drawn in float64."""
+    rng = rng_for(W_OUTLIER, n, seed)
+    x = rng.standard_normal(n)
+    if background == "small":
+        x *= 1e-3
+    elif background != "normal":
+        raise ValueError(background)
+    stretches = n // 64
+    quiet = rng.choice(stretches, size=min(n_quiet, stretches), replace=False) if stretches else []
+    for s in quiet:
+        x[64 * s:64 * s + 64] = rng.uniform(-1e-3, 1e-3, size=64)
+        x[64 * s + rng.integers(0, 64)] = rng.choice([-1e4, 1e4])
+    free = np.setdiff1d(np.arange(n), np.concatenate([np.arange(64 * s, 64 * s + 64) for s in quiet]) if len(quiet) else [])
+    pos = rng.choice(free, size=min(n_outliers, len(free)), replace=False)
+    x[pos] = rng.choice([-1e4, -3e3, 3e3, 1e4], size=len(pos))
+    return x.astype(np.float32)

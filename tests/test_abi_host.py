@@ -324,7 +324,7 @@ def test_chained_input_errors():
     d.workspace_bytes = 1 << 40
     check(I(pwg.INPUT_SWIGLU, 0, 0, 0.0, P[6], None, None, None), ERR_UNSUPPORTED, "ordered schedule")
     check(I(pwg.INPUT_RMSNORM, 0, 0, 1e-6, None, P[4], P[5], None), ERR_UNSUPPORTED, "ordered schedule", level=False)
-    d.schedule, d.weight_layout = pwg.SCHEDULE_PERSISTENT, pwg.LAYOUT_ROWS
+    d.schedule, d.weight_layout = pwg.SCHEDULE_LEVELS, pwg.LAYOUT_ROWS
     lv[0] = pwg.Level(P[0], P[1], P[2], P[3], 64, 16384)
     check(I(pwg.INPUT_SWIGLU, 0, 0, 0.0, P[6], None, None, None), ERR_UNSUPPORTED, "at most 12288")
 

@@ -208,10 +208,13 @@ def test_no_logits_no_deq_and_token_aliasing():
     p.check(out)
 
 
-@pytest.mark.parametrize("kind", ["zero", "onehot", "ranges"])
+@pytest.mark.parametrize("kind", ["zero", "onehot", "ranges", "outliers"])
 def test_vector_ranges(kind):
     """A zero vector gives exact zeros, a one-hot vector gives s * W[:, k]
-    exactly, vectors 2^-48 .. 2^36 apart in size stay within the bound."""
+    exactly, vectors 2^-48 .. 2^36 apart in size stay within the bound, and
+    vectors with massive outliers inside them (+-3e3 and +-1e4 at several
+    places, and outliers among values near 1e-3) meet the same criteria, for
+    the ternary levels and for h."""
     p = BatchPass([(500, 4096), (100, 2048)], vocab=1500, hidden=1024, batch=8, seed=7)
     pwg.step_plan(p.desc)
     p.set_inputs(5)
@@ -223,10 +226,16 @@ def test_vector_ranges(kind):
         for x in xs:
             x[2] = 0.0
             x[2, 333] = 1.0
-    else:
+    elif kind == "ranges":
         for x in xs:
             for b in range(8):
                 x[b] *= 2.0 ** (12 * (b - 4))
+    else:
+        for i, x in enumerate(xs):
+            for b in range(8):
+                x[b] = synth.outlier_vector(x.shape[1], 100 * i + b)
+        p.h = np.stack([synth.outlier_vector(p.hidden, 900 + b) for b in range(8)])
+        p.desc.h.copy_(torch.from_numpy(p.h))
     p.xs = [x.astype(np.float32) for x in xs]
     for lv, x in zip(p.desc.levels, p.xs):
         lv[2].copy_(torch.from_numpy(x))

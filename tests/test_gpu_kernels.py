@@ -7,7 +7,7 @@ import pytest
 
 import synth
 from oracle import reference as ref
-from tests.parity import assert_gemv, gemv_report, token_ok
+from tests.parity import assert_gemv, token_ok
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -61,35 +61,50 @@ def test_ternary_zero_input_gives_exact_zero():
     assert not y.any()
 
 
-@pytest.mark.parametrize("kind", ["outlier", "tiny", "huge", "mixed_scales"])
-def test_ternary_activation_ranges(kind):
-    rows, cols = 513, 4096
-    m = synth.ternary_matrix((93, 0), rows, cols)
-    x = synth.normal_f32(synth.rng_for(94, 0), cols).astype(np.float64)
+def activation_case(kind, cols, seed):
+    """Activation vectors that stress a rounding of x relative to a block
+    maximum: massive outliers on an N(0, 1) or a 1e-3 background (with
+    outliers among values near 1e-3), one outlier, tiny and huge vectors, a
+    different magnitude in every 64-element stretch."""
+    if kind == "outliers":
+        return synth.outlier_vector(cols, seed)
+    if kind == "outliers_small":
+        return synth.outlier_vector(cols, seed, background="small")
+    x = synth.normal_f32(synth.rng_for(94, seed), cols).astype(np.float64)
     if kind == "outlier":
-        x[1234] = 3000.0
+        x[min(1234, cols - 1)] = 3000.0
     elif kind == "tiny":
         x *= 1e-30
     elif kind == "huge":
         x *= 1e30
-    else:   # a different magnitude in every 64-element chunk
-        x *= 10.0 ** np.repeat(np.arange(-8, 8), 256)
-    x = x.astype(np.float32)
+    elif kind == "mixed_scales":
+        x *= 10.0 ** np.repeat(np.arange(-8, 8), -(-cols // 16))[:cols]
+    else:
+        raise ValueError(kind)
+    return x.astype(np.float32)
+
+
+ACT_KINDS = ["outlier", "outliers", "outliers_small", "tiny", "huge", "mixed_scales"]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("kind", ACT_KINDS)
+def test_ternary_activation_ranges(kind, seed):
+    rows, cols = 513, 4096
+    m = synth.ternary_matrix((93, 0), rows, cols)
+    x = activation_case(kind, cols, seed)
     y = run_ternary(m.w, m.scale, x)
-    yr, mag = ref.ternary_gemv(m.w, m.scale, x), ref.ternary_gemv_magnitude(m.w, m.scale, x)
-    if kind != "outlier":
-        assert_gemv(y, yr, mag, kind)
-        return
-    # One element 3000x the others: its 64-element chunk is quantised relative
-    # to 3000, so that chunk's terms carry up to 2^-23 * 3000 each.  The
-    # aggregate bound still holds; each element must meet the kernel's own
-    # error model (2^-22 of the chunk maximum per nonzero term, twice the
-    # rounding half-ulp, plus the float32 magnitude floor).
-    rep = gemv_report(y, yr, mag)
-    assert rep["rel_l2"] <= 1e-5, rep
-    chunk_max = np.abs(x.astype(np.float64)).reshape(-1, 64).max(axis=1)
-    bound = np.abs(m.scale.astype(np.float64)) * (np.abs(m.w).reshape(rows, -1, 64).sum(axis=2) @ chunk_max) * 2.0 ** -22
-    assert (np.abs(y - yr) <= bound + 1e-6 * mag).all()
+    assert_gemv(y, ref.ternary_gemv(m.w, m.scale, x), ref.ternary_gemv_magnitude(m.w, m.scale, x), f"{kind} {seed}")
+
+
+@pytest.mark.parametrize("shape", [(24576, 4096), (4096, 12288), (1000, 16384)], ids=["gate_up", "down", "widest"])
+def test_ternary_outliers_level_shapes(shape):
+    rows, cols = shape
+    m = synth.ternary_matrix((93, rows, cols), rows, cols)
+    for bg in ("normal", "small"):
+        x = synth.outlier_vector(cols, 5, background=bg)
+        y = run_ternary(m.w, m.scale, x)
+        assert_gemv(y, ref.ternary_gemv(m.w, m.scale, x), ref.ternary_gemv_magnitude(m.w, m.scale, x), f"{shape} {bg}")
 
 
 def test_ternary_extreme_weights():
@@ -120,8 +135,8 @@ BATCH_SHAPES = [(5, 64, 4), (1536, 4096, 16), (257, 8192, 8), (1000, 12288, 4), 
 
 @pytest.mark.parametrize("shape", BATCH_SHAPES, ids=[f"{r}x{c}xB{b}" for r, c, b in BATCH_SHAPES])
 def test_ternary_batch_weights_read_once(shape):
-    """The weight-stationary batch kernels (every chunks-per-lane instance,
-    ragged row tails, batch not a multiple of the vector group)."""
+    """Row-major batches (one matrix-core pass per vector): every width class,
+    ragged row tails, widths that are not a multiple of 256."""
     rows, cols, batch = shape
     m = synth.ternary_matrix((103, rows, cols), rows, cols)
     xb = synth.batch_inputs(batch, cols, 3)
@@ -159,6 +174,18 @@ def test_int8_argmax_shapes(shape):
     tok, lg = run_argmax(tab.q, tab.scale, h)
     lr = ref.int8_logits(tab.q, tab.scale, h)
     assert_gemv(lg, lr, ref.int8_logits_magnitude(tab.q, tab.scale, h), str(shape))
+    assert token_ok(tok[0], lr)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("kind", ACT_KINDS)
+def test_int8_activation_ranges(kind, seed):
+    rows, cols = 3000, 4096
+    tab = synth.int8_table((99, 7), rows, cols)
+    h = activation_case(kind, cols, seed)
+    tok, lg = run_argmax(tab.q, tab.scale, h)
+    lr = ref.int8_logits(tab.q, tab.scale, h)
+    assert_gemv(lg, lr, ref.int8_logits_magnitude(tab.q, tab.scale, h), f"{kind} {seed}")
     assert token_ok(tok[0], lr)
 
 
@@ -203,7 +230,7 @@ def test_argmax_batch():
         assert_gemv(lg[b], lr[b], ref.int8_logits_magnitude(tab.q, tab.scale, hb[b]), f"batch {b}")
 
 
-# cols a multiple of 1,024: matrix-core kernel; (777, 768, 4): the VALU kernel
+# cols a multiple of 1,024: matrix-core kernel; (777, 768, 4): the VALU kernel per vector
 I8_BATCH_SHAPES = [(999, 1024, 8), (5000, 4096, 16), (257, 2048, 4), (3, 8192, 4), (70001, 4096, 8),
                    (1000, 1024, 16), (777, 768, 4)]
 
@@ -344,6 +371,32 @@ def test_ternary_batch_tiled_vector_ranges():
     assert np.array_equal(y[6], (m.scale * m.w[:, 777]).astype(np.float32))
     for b in (0, 1, 2, 3, 4, 7):
         assert_gemv(y[b], yr[b], ref.ternary_gemv_magnitude(m.w, m.scale, xb[b]), f"vector {b}")
+
+
+@pytest.mark.parametrize("batch", [4, 8, 16])
+def test_ternary_batch_tiled_outliers(batch):
+    """Massive outliers inside every vector (N(0, 1) background, outliers
+    among values near 1e-3): the batched pass rounds each vector to 31 bits
+    per 1,024-value block."""
+    rows, cols = 3000, 4096
+    m = synth.ternary_matrix((108, 1), rows, cols)
+    xb = np.stack([synth.outlier_vector(cols, 20 + b) for b in range(batch)])
+    y = pwg.ternary_gemv_tiled(tiled_t2(m.w), dev(m.scale), rows, cols, dev(xb)).cpu().numpy()
+    yr = ref.ternary_gemv(m.w, m.scale, xb)
+    for b in range(batch):
+        assert_gemv(y[b], yr[b], ref.ternary_gemv_magnitude(m.w, m.scale, xb[b]), f"vector {b}")
+
+
+@pytest.mark.parametrize("batch", [4, 16])
+def test_argmax_batch_outliers(batch):
+    rows, cols = 5000, 4096
+    tab = synth.int8_table((106, 1), rows, cols)
+    hb = np.stack([synth.outlier_vector(cols, 40 + b) for b in range(batch)])
+    tok, lg = run_argmax(tab.q, tab.scale, hb)
+    lr = ref.int8_logits(tab.q, tab.scale, hb)
+    for b in range(batch):
+        assert token_ok(tok[b], lr[b]), f"vector {b}"
+        assert_gemv(lg[b], lr[b], ref.int8_logits_magnitude(tab.q, tab.scale, hb[b]), f"vector {b}")
 
 
 TILED_I8_SHAPES = [(5000, 4096, 16), (999, 1024, 8), (70001, 4096, 4), (3, 8192, 16)]
