@@ -392,5 +392,6 @@ def decode_step_weights(desc: StepDesc, stream=None):
 
 
 def step_status(desc: StepDesc, stream=None):
-    """Raises if a persistent step recorded a barrier timeout (synchronous)."""
+    """Raises if a stream step or batched pass recorded a timeout of one of
+    its bounded waits (synchronous)."""
     _check(_step_status(C.byref(desc.c()), _stream(stream)))

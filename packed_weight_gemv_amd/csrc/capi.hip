@@ -252,6 +252,7 @@ int validate_step(const pwg_step_desc* d) {
   if (d->emb_deq_out && !aligned16(d->emb_deq_out)) return fail(PWG_ERR_ALIGN, "%s: emb_deq_out misaligned", fn);
   if (d->logits_out && !aligned16(d->logits_out)) return fail(PWG_ERR_ALIGN, "%s: logits_out misaligned", fn);
   TRY(check_ptr(d->workspace, fn, "workspace"));
+  if (d->schedule == PWG_SCHEDULE_STREAM) TRY(check_unordered_aliasing(d, fn));
   return PWG_OK;
 }
 
@@ -274,8 +275,10 @@ extern "C" int pwg_step_plan(const pwg_step_desc* d, void* stream) {
   if (d->workspace_bytes < pwg_step_workspace_bytes(d))
     return fail(PWG_ERR_SIZE, "pwg_step_plan: workspace %zu < %zu bytes", d->workspace_bytes,
                 pwg_step_workspace_bytes(d));
-  if (batched(d)) return step_batch_plan(d, stream);
-  if (d->schedule == PWG_SCHEDULE_STREAM) return step_stream_plan(d, 0, stream);
+  if (d->schedule != PWG_SCHEDULE_STREAM) return PWG_OK;
+  plan_forget(d);
+  TRY(batched(d) ? step_batch_plan(d, stream) : step_stream_plan(d, 0, stream));
+  plan_record(d);
   return PWG_OK;
 }
 
@@ -291,8 +294,11 @@ extern "C" int pwg_decode_step_weights(const pwg_step_desc* d, void* stream) {
   if (d->workspace_bytes < pwg_step_workspace_bytes(d))
     return fail(PWG_ERR_SIZE, "pwg_decode_step_weights: workspace %zu < %zu bytes", d->workspace_bytes,
                 pwg_step_workspace_bytes(d));
-  if (batched(d)) return step_batch_launch(d, stream);
-  if (d->schedule == PWG_SCHEDULE_STREAM) return step_stream_launch(d, 0, stream);
+  if (d->schedule == PWG_SCHEDULE_STREAM) {
+    // the kernels take every pointer and shape from the device plan
+    TRY(plan_check(d, "pwg_decode_step_weights"));
+    return batched(d) ? step_batch_launch(d, stream) : step_stream_launch(d, 0, stream);
+  }
   // Levels schedule: embedding row, every level in decoder order, output
   // projection + argmax, all on one stream.
   TRY(launch_embed_gather(d->emb_table, d->emb_scale, d->vocab, d->hidden, d->token_in, 1, d->emb_row_out,

@@ -83,6 +83,17 @@ int step_batch_plan(const pwg_step_desc* d, void* stream);
 int step_batch_launch(const pwg_step_desc* d, void* stream);
 int step_batch_status(const pwg_step_desc* d, void* stream);
 
+// Host-only checks of a step description (validate.cpp).
+// PWG_ERR_UNSUPPORTED when a level input or h overlaps a buffer the step
+// writes (schedules that run levels in no fixed order).
+int check_unordered_aliasing(const pwg_step_desc* d, const char* fn);
+uint64_t step_fingerprint(const pwg_step_desc* d);
+// The fingerprint of the description a workspace was last planned for.
+void plan_record(const pwg_step_desc* d);
+void plan_forget(const pwg_step_desc* d);
+// PWG_ERR_ARG unless `d` is the description its workspace was planned for.
+int plan_check(const pwg_step_desc* d, const char* fn);
+
 // 16-row x 64-byte tile arrangement (tile.hip).
 size_t tiled_bytes(int64_t rows, int64_t row_bytes);
 int launch_tile_rows(const void* src, int64_t rows, int64_t row_bytes, void* dst, void* stream);

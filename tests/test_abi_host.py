@@ -219,12 +219,14 @@ def test_batched_step_errors():
     weights, level widths that are multiples of 2048 and a hidden width that
     is a multiple of 1024; every call here fails validation before anything
     is enqueued."""
+    P = lambda k: (1 << 36) + k * (1 << 24)  # noqa: E731  (distinct buffers)
     d = pwg._StepDesc()
     d.vocab, d.hidden = 1000, 4096
-    for name in ("out_table", "out_scale", "h", "emb_table", "emb_scale", "token_in", "token_out",
-                 "emb_row_out", "emb_scale_out", "workspace"):
-        setattr(d, name, A)
-    lv = (pwg.Level * 2)(pwg.Level(A, A, A, A, 64, 4096), pwg.Level(A, A, A, A, 100, 12288))
+    for i, name in enumerate(("out_table", "out_scale", "h", "emb_table", "emb_scale", "token_in", "token_out",
+                              "emb_row_out", "emb_scale_out", "workspace")):
+        setattr(d, name, P(i))
+    lv = (pwg.Level * 2)(pwg.Level(P(20), P(21), P(22), P(23), 64, 4096),
+                         pwg.Level(P(24), P(25), P(26), P(27), 100, 12288))
     d.n_levels, d.levels = 2, C.cast(lv, C.POINTER(pwg.Level))
     d.schedule, d.weight_layout = pwg.SCHEDULE_STREAM, pwg.LAYOUT_TILED
     sizes = {}
@@ -245,14 +247,97 @@ def test_batched_step_errors():
     d.schedule, d.weight_layout = pwg.SCHEDULE_LEVELS, pwg.LAYOUT_ROWS
     assert pwg._step(C.byref(d), None) == ERR_UNSUPPORTED
     d.schedule, d.weight_layout = pwg.SCHEDULE_STREAM, pwg.LAYOUT_TILED
-    lv[1] = pwg.Level(A, A, A, A, 100, 1024)           # not a multiple of 2048
+    lv[1].cols = 1024                                  # not a multiple of 2048
     assert pwg._step(C.byref(d), None) == ERR_UNSUPPORTED and "2048" in pwg.last_error()
-    lv[1] = pwg.Level(A, A, A, A, 100, 12288)
+    lv[1].cols = 12288
     d.hidden = 1536                                    # not a multiple of 1024
     assert pwg._step(C.byref(d), None) == ERR_UNSUPPORTED and "1024" in pwg.last_error()
     d.hidden = 4096
     d.h = MIS
     assert pwg._step(C.byref(d), None) == ERR_ALIGN
+
+
+def distinct_desc(batch=0):
+    """A stream-schedule description whose buffers are all distinct (16 MiB
+    apart, 16-byte aligned): it passes validation, and the launch then stops
+    at the missing plan."""
+    P = lambda k: (1 << 36) + k * (1 << 24)  # noqa: E731
+    d = pwg._StepDesc()
+    d.vocab, d.hidden, d.batch = 1000, 4096, batch
+    for i, name in enumerate(("out_table", "out_scale", "h", "emb_table", "emb_scale", "token_in", "token_out",
+                              "emb_row_out", "emb_scale_out", "workspace")):
+        setattr(d, name, P(i))
+    lv = (pwg.Level * 2)(pwg.Level(P(20), P(21), P(22), P(23), 64, 4096), pwg.Level(P(24), P(25), P(26), P(27), 64, 4096))
+    d.n_levels, d.levels = 2, C.cast(lv, C.POINTER(pwg.Level))
+    d.schedule, d.weight_layout = pwg.SCHEDULE_STREAM, pwg.LAYOUT_TILED
+    d.workspace_bytes = pwg._step_ws(C.byref(d))
+    assert d.workspace_bytes > 0
+    return d, lv, P
+
+
+@pytest.mark.parametrize("batch", [0, 4])
+def test_unordered_schedules_reject_aliased_inputs(batch):
+    """The stream schedule and the batched pass run levels in no fixed order,
+    so an input (a level's x, or h) that shares memory with anything the step
+    writes (a level's y, the logits, the embedding outputs) would be read
+    before or after the write at random: PWG_ERR_UNSUPPORTED, for equal and
+    for partly overlapping ranges, with the ranges scaled by the batch."""
+    d, lv, P = distinct_desc(batch)
+    assert pwg._step(C.byref(d), None) == ERR_ARG and "plan" in pwg.last_error()
+    nb = max(batch, 1)
+
+    def refused(what):
+        rc = pwg._step(C.byref(d), None)
+        assert rc == ERR_UNSUPPORTED and "overlaps" in pwg.last_error(), (what, rc, pwg.last_error())
+
+    lv[1].x = lv[0].y                                   # level 1 reads level 0's output
+    refused("x1 = y0")
+    lv[1].x = P(23) + 64 * 4 * nb - 16                  # starts in y0's last 16 bytes
+    refused("x1 inside y0")
+    lv[1].x = P(23) + 64 * 4 * nb                       # right after y0: no overlap
+    assert pwg._step(C.byref(d), None) == ERR_ARG
+    lv[1].x = P(26)
+    lv[0].x = lv[0].y                                   # a level reading its own output
+    refused("x0 = y0")
+    lv[0].x = P(22)
+    d.h = lv[1].y                                       # h is a level output
+    refused("h = y1")
+    d.h = P(2)
+    d.logits_out = P(30)
+    lv[0].x = P(30) + 400                               # inside the logits
+    refused("x0 in logits")
+    lv[0].x = P(22)
+    d.emb_deq_out = P(31)
+    d.h = P(31)                                         # h is the dequantised embedding row
+    refused("h = emb_deq_out")
+    d.h = P(2)
+    lv[0].x = d.emb_row_out                             # x0 is the gathered int8 row
+    refused("x0 = emb_row_out")
+    lv[0].x = P(22)
+    assert pwg._step(C.byref(d), None) == ERR_ARG and "plan" in pwg.last_error()
+
+
+def test_levels_schedule_takes_chained_pointers():
+    """The levels schedule runs levels in decoder order: a level may read the
+    previous level's output (validation passes; on this host the launch then
+    fails only for want of a device)."""
+    d, lv, P = distinct_desc()
+    d.schedule, d.weight_layout = pwg.SCHEDULE_LEVELS, pwg.LAYOUT_ROWS
+    d.workspace_bytes = pwg._step_ws(C.byref(d))
+    lv[1].x = lv[0].y
+    rc = pwg._step(C.byref(d), None)
+    assert rc not in (ERR_UNSUPPORTED, ERR_ARG, ERR_ALIGN, ERR_SIZE), (rc, pwg.last_error())
+
+
+def test_stream_launch_needs_a_plan_for_this_description():
+    """The stream kernels take every pointer and shape from the device plan
+    that pwg_step_plan writes into the workspace: a launch on a workspace that
+    holds no plan is refused before anything is enqueued (a launch after a
+    changed description is covered on the GPU, where a plan can be made)."""
+    for batch in (0, 8):
+        d, lv, P = distinct_desc(batch)
+        rc = pwg._step(C.byref(d), None)
+        assert rc == ERR_ARG and "no plan" in pwg.last_error()
 
 
 def test_tiled_size():

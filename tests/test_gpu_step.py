@@ -144,6 +144,32 @@ def test_many_steps_stay_identical(schedule):
     assert np.array_equal(first["logits"], last["logits"]) and first["token"] == last["token"]
 
 
+def test_stream_launch_after_changed_description_is_refused():
+    """The stream kernels read every pointer and shape from the device plan:
+    after a level's input buffer is replaced, a launch without a new plan is
+    refused (nothing is enqueued), and after planning again the step reads the
+    new buffer."""
+    wl = build_step(n_layers=1, shapes=SMALL, vocab=1000, hidden=256, with_logits=True, schedule=pwg.SCHEDULE_STREAM)
+    d = wl.desc
+    pwg.step_plan(d)
+    pwg.decode_step_weights(d)
+    torch.cuda.synchronize()
+    lv = [list(t) for t in d.levels]
+    x_new = synth.normal_f32(synth.rng_for(150, 0), lv[1][5])
+    lv[1][2] = torch.from_numpy(x_new).to("cuda:0")
+    d.levels = [tuple(t) for t in lv]
+    d._c = None
+    with pytest.raises(pwg.PwgError, match="planned"):
+        pwg.decode_step_weights(d)
+    pwg.step_plan(d)
+    pwg.decode_step_weights(d)
+    torch.cuda.synchronize()
+    pwg.step_status(d)
+    m = synth.stacked(synth.layer(synth.W_STEP, 0, SMALL), synth.LEVELS[1][1])
+    assert_gemv(d.levels[1][3].cpu().numpy(), ref.ternary_gemv(m.w, m.scale, x_new),
+                ref.ternary_gemv_magnitude(m.w, m.scale, x_new), "o after re-plan")
+
+
 def chain_levels(wl):
     """Rewires a built step so that every level reads a prefix of the previous
     level's output and h is the last level's output: a chained step, in which

@@ -114,6 +114,41 @@ def test_int8_one_hot_reads_a_column():
     assert np.array_equal(ref.int8_logits(q, t, h), t.astype(np.float64) * q[:, 17])
 
 
+def test_int8_magnitude_is_the_sum_of_absolute_terms():
+    """The cancellation floor of the logits comparison:
+    |t_v| * sum_k |Q_vk| * |h_k|, pinned against a scalar-loop fsum, against
+    the logit itself where no term cancels, and at the int8 minimum -128
+    (whose absolute value does not fit in int8)."""
+    rng = np.random.default_rng(11)
+    q = rng.integers(-128, 128, size=(7, 9), dtype=np.int8)
+    q[0, 0] = -128
+    t = rng.uniform(-0.01, 0.01, size=7).astype(np.float32)
+    h = rng.standard_normal(9).astype(np.float32)
+    mag = ref.int8_logits_magnitude(q, t, h)
+    for v in range(7):
+        want = abs(float(t[v])) * math.fsum(abs(int(q[v, k])) * abs(float(h[k])) for k in range(9))
+        assert mag[v] == pytest.approx(want, rel=1e-15)
+    assert (mag >= np.abs(ref.int8_logits(q, t, h)) * (1 - 1e-15)).all()
+    # no cancellation: every term of a row has the same sign
+    qp = np.abs(q.astype(np.int16)).clip(0, 127).astype(np.int8)
+    hp = np.abs(h)
+    assert np.allclose(ref.int8_logits_magnitude(qp, t, hp), np.abs(ref.int8_logits(qp, t, hp)), rtol=1e-15, atol=0)
+    # a row whose terms cancel exactly: logit 0, magnitude the full sum
+    qc = np.array([[1, -1, 2, -2]], np.int8)
+    hc = np.array([3.0, 3.0, -0.5, -0.5], np.float32)
+    assert ref.int8_logits(qc, np.ones(1, np.float32), hc)[0] == 0.0
+    assert ref.int8_logits_magnitude(qc, np.ones(1, np.float32), hc)[0] == 8.0
+    # -128 and a negative scale: 128 * |h| * |t|
+    m1 = ref.int8_logits_magnitude(np.array([[-128]], np.int8), np.array([-0.5], np.float32), np.array([-2.0], np.float32))
+    assert m1[0] == 128.0
+    # invariant under negating h or the table
+    assert np.array_equal(ref.int8_logits_magnitude(q, t, -h), mag)
+    qn = (-q.astype(np.int16)).clip(-127, 127).astype(np.int8)
+    qs = q.copy()
+    qs[q == -128] = -127
+    assert np.array_equal(ref.int8_logits_magnitude(qn, t, h), ref.int8_logits_magnitude(qs, t, h))
+
+
 def test_planted_maximum_is_found():
     v, k = 1000, 64
     q = RNG.integers(-100, 101, size=(v, k), dtype=np.int8)
