@@ -245,6 +245,27 @@ int pwg_int8_gemv_argmax(const int8_t* table, const float* row_scale,
                          int32_t* token_out, float* logits_out,
                          void* stream);
 
+/* pwg_int8_gemv_argmax for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and results, bit for bit, with no
+ * workspace argument.  Its scratch (the per-workgroup (max, index) keys and,
+ * for batch 4, 8, 16, the matrix-core operands of h) is a fixed device array
+ * of this library, 1 MiB per GPU, held by each GPU the library runs on until
+ * the process ends; the call allocates and frees nothing.  Requests needing
+ * more than 1 MiB (pwg_argmax_workspace_bytes(rows, batch) > 1 MiB, e.g.
+ * batch 16 over more than about 4,000 rows) fail with PWG_ERR_SIZE.  Every
+ * call on one GPU shares that GPU's array and leaves its contents behind
+ * (nothing in it needs to start at zero): calls that overlap on one GPU
+ * (other streams, other threads) race.  The first call on a device looks up
+ * the array's address (hipGetSymbolAddress), so make it outside stream
+ * capture.  Arguments and errors as pwg_int8_gemv_argmax, plus PWG_ERR_SIZE
+ * for the limit. */
+int pwg_int8_gemv_argmax_noalloc(const int8_t* table, const float* row_scale,
+                                 int64_t rows, int64_t cols,
+                                 const float* h, int32_t batch,
+                                 int32_t* token_out, float* logits_out,
+                                 void* stream);
+
 /* Embedding-row gather (page section "The file is not the traffic": only the
  * selected input rows are read):
  *     rows_out[i, :] = table[ids[i], :]; scales_out[i] = row_scale[ids[i]];

@@ -18,7 +18,7 @@ import numpy as np
 
 __all__ = [
     "PwgError", "lib", "packed_size", "pack_weights", "unpack_weights", "ternary_gemv",
-    "argmax_workspace_bytes", "int8_gemv_argmax", "embed_gather", "Level", "StepDesc",
+    "argmax_workspace_bytes", "int8_gemv_argmax", "int8_gemv_argmax_noalloc", "embed_gather", "Level", "StepDesc",
     "step_workspace_bytes", "step_plan", "decode_step_weights", "step_status", "last_error", "version",
     "tiled_size", "tile_rows", "SCHEDULE_LEVELS", "SCHEDULE_PERSISTENT", "SCHEDULE_STREAM",
     "LAYOUT_ROWS", "LAYOUT_TILED", "layout_for_schedule", "LIB_PATH", "InputOp", "INPUT_GIVEN",
@@ -105,6 +105,7 @@ _verify = _sig("pwg_verify_accept", C.c_int, _vp, _vp, _i32, _vp, _vp, _vp)
 _tgemv = _sig("pwg_ternary_gemv", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp)
 _argmax_ws = _sig("pwg_argmax_workspace_bytes", _sz, _i64, _i32)
 _i8argmax = _sig("pwg_int8_gemv_argmax", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _sz, _vp, _vp, _vp)
+_i8argmax_na = _sig("pwg_int8_gemv_argmax_noalloc", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp)
 _gather = _sig("pwg_embed_gather", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _vp)
 _batch_ws = _sig("pwg_batch_workspace_bytes", _sz, _i64, _i32)
 _tgemv_tiled = _sig("pwg_ternary_gemv_tiled", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp, _sz, _vp)
@@ -124,7 +125,7 @@ EXPORTED = ["pwg_packed_size", "pwg_pack_weights", "pwg_unpack_weights", "pwg_te
             "pwg_int8_gemv_argmax_tiled",
             "pwg_step_workspace_bytes", "pwg_step_plan", "pwg_decode_step_weights",
             "pwg_step_status", "pwg_last_error", "pwg_version", "pwg_attention_workspace_bytes",
-            "pwg_gqa_decode_attention", "pwg_verify_accept"]
+            "pwg_gqa_decode_attention", "pwg_verify_accept", "pwg_int8_gemv_argmax_noalloc"]
 
 
 def last_error() -> str:
@@ -210,6 +211,20 @@ def int8_gemv_argmax(table, row_scale, h, workspace=None, token_out=None, logits
     _check(_i8argmax(_ptr(table), _ptr(row_scale), rows, cols, _ptr(h), batch, _ptr(workspace),
                      workspace.numel() * workspace.element_size(), _ptr(token_out), _ptr(logits_out),
                      _stream(stream)))
+    return token_out
+
+
+def int8_gemv_argmax_noalloc(table, row_scale, h, token_out=None, logits_out=None, stream=None):
+    """int8_gemv_argmax with the library's fixed scratch array instead of a
+    workspace (nothing is allocated by the call; token_out must be given to
+    keep the binding allocation-free too)."""
+    import torch
+    rows, cols = table.shape
+    batch = 1 if h.dim() == 1 else h.shape[0]
+    if token_out is None:
+        token_out = torch.empty(batch, dtype=torch.int32, device=h.device)
+    _check(_i8argmax_na(_ptr(table), _ptr(row_scale), rows, cols, _ptr(h), batch, _ptr(token_out), _ptr(logits_out),
+                        _stream(stream)))
     return token_out
 
 

@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libpwg.so")
 ARCH = os.environ.get("PWG_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["errors.cpp", "pack.cpp", "validate.cpp", "capi.hip", "gemv_mfma.hip", "int8_gemv.hip", "step_stream.hip", "tile.hip",
-           "batch_mfma.hip", "step_batch.hip", "chain.hip", "attention.hip", "verify.hip"]
+           "batch_mfma.hip", "step_batch.hip", "chain.hip", "attention.hip", "verify.hip", "noalloc.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function"]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
