@@ -8,17 +8,25 @@ resident in HBM before the timed region starts.
 
 Order of work (the release-gate policy of the page "The Neutrino Engine",
 sections "One changed token fails the release" and "The engine also runs
-weights we did not train": identity is checked before any timing):
+weights we did not train": identity is checked before any timing, and timing
+is done in interleaved rounds):
   1. build the seeded synthetic workload and upload it;
   2. parity: sampled rows of every level, the full logits' argmax and the
      embedding row against the CPU oracle; abort on any failure;
-  3. warm up W graph replays, time K replays (HIP events on the replay stream)
-     of the timed schedule: by default the stream schedule, which computes
-     the step over its fixed per-level inputs with no waits between levels;
-  4. the same for the other schedule (one kernel per level, in decoder
-     order, as a chained step needs) and for a null graph with as many empty
-     kernels, to split dependency and launch overhead from DRAM time;
-  5. the oracle timed on a bounded sample of the same workload (rank 0).
+  3. the timed schedule (by default the stream schedule, which computes the
+     step over its fixed per-level inputs with no waits between levels) in
+     one HIP graph: untimed replays for --prewarm seconds, --warmup untimed
+     replays, exactly --steps timed replays (HIP events on the replay
+     stream), then --rounds more rounds of --steps for the median and
+     p10 / p90; the same step without a graph (the roofline time) and four
+     steps per graph;
+  4. the levels schedule (one kernel per level, in decoder order, as a
+     chained step needs), a null graph with as many empty kernels, and the
+     chained step, to split dependency and launch overhead from DRAM time;
+  5. configurations 1-3 as units of their own, the packing against the
+     pages' slab, the small-batch passes and decode attention;
+  6. the oracle on a bounded sample of the same workload, each sample round
+     right after a GPU timing round of the step, and on one thread.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -53,6 +61,10 @@ def parse():
                    help="only the decode-attention leg (one 8B-shape layer at 4,096 and 32,768 cached positions; "
                         "parity, then timing); prints its JSON object")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle's timed sample")
+    p.add_argument("--prewarm", type=float, default=0.3,
+                   help="seconds of untimed graph replays before the counted warm-up (steady clocks)")
+    p.add_argument("--rounds", type=int, default=15, help="extra timing rounds of --steps replays (median, p10, p90)")
+    p.add_argument("--no-units", action="store_true", help="skip configurations 1-3 as standalone units")
     p.add_argument("--counters", action="store_true",
                    help="counter-collection run: 3 eager steps of the timed schedule plus a 1 GiB device copy "
                         "(the known-size reference for FETCH_SIZE / WRITE_SIZE); prints nothing else")
@@ -94,6 +106,56 @@ def time_graph(graph, stream, steps, warmup):
     e1.synchronize()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps  # ms per replay
+
+
+def prewarm(graph, stream, seconds):
+    """Replays `graph` untimed for about `seconds` so that clocks and caches
+    are in their steady state before the counted warm-up and timed replays
+    (the number of those is fixed by the command line; this is not)."""
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            graph.replay()
+        n += 16
+        stream.synchronize()
+    return n
+
+
+def time_rounds(graph, stream, steps, rounds):
+    """ms per replay over `rounds` rounds of `steps` replays each (HIP events
+    on the replay stream, one pair per round)."""
+    import torch
+    out = []
+    with torch.cuda.stream(stream):
+        for _ in range(rounds):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                graph.replay()
+            e1.record(stream)
+            e1.synchronize()
+            out.append(e0.elapsed_time(e1) / steps)
+    return out
+
+
+def spread(ms_list):
+    """Median and 10th / 90th percentiles (us) of per-round ms values."""
+    import numpy as np
+    a = np.asarray(ms_list, dtype=np.float64) * 1e3
+    return {"median_us": float(np.median(a)), "p10_us": float(np.percentile(a, 10)),
+            "p90_us": float(np.percentile(a, 90)), "rounds": int(a.size)}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 class HipGraph:
@@ -207,41 +269,190 @@ def torch_index(rows):
     return torch.from_numpy(rows).to("cuda:0")
 
 
-def cpu_baseline(target_s: float, step_bytes: int):
-    """The oracle, as it stands, on the first layers of the same seeded
-    workload (as many as fit in about target_s seconds, at least one) and the
-    full output projection; the per-layer mean is scaled to 36 layers."""
+def cpu_baseline(target_s: float, step_bytes: int, gpu_round=None):
+    """The oracle, as it stands (float64 numpy), on a bounded sample of the
+    same seeded workload, in rounds interleaved with GPU timing rounds of the
+    step: round r times the GPU step (`gpu_round()`, ms per step), then the
+    oracle's four levels of layer r, until about target_s seconds of oracle
+    time; then the full output projection and argmax.  The per-layer mean is
+    scaled to the step's 36 layers.  All host threads (BLAS threads as the
+    library sets them), and one layer again on one thread."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import synth
     from oracle import reference as ref
-    layer_s = []
-    for layer in range(synth.N_LAYERS):
-        if layer_s and sum(layer_s) + float(np.mean(layer_s)) > target_s:
-            break
+
+    def one_layer(layer):
         mats = synth.layer(synth.W_STEP, layer)
         xs = synth.layer_inputs(synth.W_STEP, layer)
-        levels = [(synth.stacked(mats, members), xs[name]) for name, members, _ in synth.LEVELS]
+        return [(synth.stacked(mats, members), xs[name]) for name, members, _ in synth.LEVELS]
+
+    def run_layer(levels):
         t0 = time.perf_counter()
         for m, x in levels:
             ref.ternary_gemv(m.w, m.scale, x)
-        layer_s.append(time.perf_counter() - t0)
-        del mats, levels
+        return time.perf_counter() - t0
+
+    layer_s, gpu_ms = [], []
+    for layer in range(synth.N_LAYERS):
+        if layer_s and sum(layer_s) + float(np.mean(layer_s)) > target_s:
+            break
+        levels = one_layer(layer)          # generation is not timed
+        if gpu_round is not None:
+            gpu_ms.append(gpu_round())
+        layer_s.append(run_layer(levels))
+        del levels
     out_t, _, _, h = synth.vocab_workload(n_ids=1, workload=synth.W_STEP)
     t0 = time.perf_counter()
     lg = ref.int8_logits(out_t.q, out_t.scale, h)
     ref.greedy_token(lg)
     vocab_s = time.perf_counter() - t0
+    del out_t, lg
     step_s = float(np.mean(layer_s)) * synth.N_LAYERS + vocab_s
     threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    return {
+    levels = one_layer(0)
+    with threadpool_limits(limits=1):
+        one_s = run_layer(levels)
+    del levels
+    # one thread: the layer time scaled by the step's bytes over the layer's
+    layer_bytes = sum(r * k // 4 + 4 * r for r, k in ((6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)))
+    one_step_s = one_s * step_bytes / layer_bytes
+    out = {
         "value": step_bytes / step_s / 1e9, "unit": "GB/s",
-        "us_per_step": step_s * 1e6, "cores": int(threads), "kind": "oracle",
-        "sample": (f"{len(layer_s)} of 36 layers (all 4 levels each, float64 numpy) plus the full "
-                   f"151936x4096 output projection and argmax, timed once; the per-layer mean is scaled to 36 layers"),
+        "us_per_step": step_s * 1e6, "cores": int(threads), "kind": "oracle", "cpu_model": cpu_model(),
+        "sample": (f"{len(layer_s)} of 36 layers (all 4 levels each, float64 numpy), each timed right after a GPU "
+                   f"timing round of the step, plus the full 151936x4096 output projection and argmax; the "
+                   f"per-layer mean is scaled to 36 layers"),
         "sample_seconds": float(sum(layer_s) + vocab_s),
+        "one_core": {"value": step_bytes / one_step_s / 1e9, "unit": "GB/s", "cores": 1,
+                     "us_per_step": one_step_s * 1e6,
+                     "sample": "layer 0 (4 levels) on one BLAS thread, scaled to the step by algorithmic bytes",
+                     "sample_seconds": one_s},
     }
+    if gpu_ms:
+        out["interleaved_gpu_rounds"] = spread(gpu_ms)
+    return out
+
+
+def packing_report(wl):
+    """Bytes per weight of the packed ternary lane against the pages' per-layer
+    slab (72,351,744 bytes for the 8B shape's 192,937,984 weights)."""
+    lv = wl.desc.levels[:4]
+    weights = sum(r * k for (_, _, _, _, r, k) in lv)
+    packed = sum(r * k // 4 for (_, _, _, _, r, k) in lv)
+    scales = sum(4 * r for (_, _, _, _, r, k) in lv)
+    slab = 72351744
+    return {"format": "T2 (2 bits per weight, row scales float32 apart)", "weights_per_layer": weights,
+            "packed_bytes_per_layer": packed, "scale_bytes_per_layer": scales,
+            "bytes_per_weight": packed / weights, "pages_slab_bytes_per_layer": slab,
+            "pages_slab_bytes_per_weight": slab / weights, "ratio_to_pages_slab": packed / slab}
+
+
+def standalone_units(wl, stream, reps=20):
+    """Configurations 1-3 as units of their own, each after a parity check:
+    the 1024 x 1024 ternary GEMV (per call, resident, and rotated over 1,100
+    copies so that the copies exceed the last-level cache); one 8B-shape
+    layer's four levels through the per-call GEMV, rotated over the step's 36
+    layers; the int8 output projection + argmax over the 151,936 x 4,096
+    table, and the gather of 64 embedding rows."""
+    import numpy as np
+    import torch
+
+    import packed_weight_gemv_amd as pwg
+    import synth
+    from oracle import reference as ref
+    from tests.parity import assert_gemv, token_ok
+    dev = "cuda:0"
+    out = {}
+    # configuration 1
+    w, s_, x = synth.single_gemv()
+    blob = torch.from_numpy(pwg.pack_weights(w)).to(dev)
+    sd, xd = torch.from_numpy(s_).to(dev), torch.from_numpy(x).to(dev)
+    yd = torch.empty(1024, dtype=torch.float32, device=dev)
+    pwg.ternary_gemv(blob, sd, 1024, 1024, xd, y=yd, stream=stream)
+    stream.synchronize()
+    assert_gemv(yd.cpu().numpy(), ref.ternary_gemv(w, s_, x), ref.ternary_gemv_magnitude(w, s_, x), "config 1")
+    unit_bytes = 1024 * 1024 // 4 + 4 * 1024
+    copies = 1100
+    wr = blob.repeat(copies).view(copies, -1)
+    sr, xr = sd.repeat(copies).view(copies, -1), xd.repeat(copies).view(copies, -1)
+    yr = torch.empty((copies, 1024), dtype=torch.float32, device=dev)
+    g_res = capture(lambda: [pwg.ternary_gemv(blob, sd, 1024, 1024, xd, y=yd, stream=stream) for _ in range(copies)],
+                    stream)
+    prewarm(g_res, stream, 0.05)
+    us_res = time_graph(g_res, stream, 5, 1) * 1e3 / copies
+    del g_res
+    g_rot = capture(lambda: [pwg.ternary_gemv(wr[i], sr[i], 1024, 1024, xr[i], y=yr[i], stream=stream)
+                             for i in range(copies)], stream)
+    prewarm(g_rot, stream, 0.05)
+    us_rot = time_graph(g_rot, stream, 5, 1) * 1e3 / copies
+    del g_rot
+    us_call = time_direct(lambda: pwg.ternary_gemv(blob, sd, 1024, 1024, xd, y=yd, stream=stream), stream, 2000, 200) * 1e3
+    out["config1_1024x1024_gemv"] = {
+        "us_per_call_launched": us_call, "us_per_call_in_graph_resident": us_res,
+        "us_per_call_in_graph_rotated_1100_copies": us_rot, "bytes_per_call": unit_bytes,
+        "rotated_GBps": unit_bytes / (us_rot * 1e-6) / 1e9, "floor_us": unit_bytes / PEAK_HBM_BPS * 1e6,
+        "note": "latency-bound: each call is one kernel launch; graph node boundaries included"}
+    log(f"config 1: {us_call:.2f} us per launched call, {us_res:.2f} us per call in a graph (resident), "
+        f"{us_rot:.2f} us rotated over {copies} copies ({unit_bytes / (us_rot * 1e-6) / 1e9:.0f} GB/s)")
+    del wr, sr, xr, yr
+    # configuration 2: the per-call GEMV over every level of every layer (one graph)
+    rows_w = wl.weights[pwg.LAYOUT_ROWS][0]
+    lv = wl.desc.levels
+    n_layers = len(lv) // 4
+    calls = [(w_, sc, x_, y_, r, k) for w_, (_, sc, x_, y_, r, k) in zip(rows_w, lv)]
+    g2 = capture(lambda: [pwg.ternary_gemv(w_, sc, r, k, x_, y=y_, stream=stream) for w_, sc, x_, y_, r, k in calls],
+                 stream)
+    prewarm(g2, stream, 0.1)
+    ms2 = time_graph(g2, stream, reps, 2)
+    del g2
+    smp = wl.samples[4]
+    yv = lv[4][3][torch.from_numpy(smp.rows).to(dev)].cpu().numpy()
+    assert_gemv(yv, ref.ternary_gemv(smp.w, smp.scale, smp.x), ref.ternary_gemv_magnitude(smp.w, smp.scale, smp.x),
+                "config 2 sample")
+    layer_bytes = sum(r * k // 4 + 4 * r for (_, _, _, _, r, k) in lv[:4])
+    us_layer = ms2 * 1e3 / n_layers
+    out["config2_8b_layer_per_call_gemvs"] = {
+        "us_per_layer": us_layer, "bytes_per_layer": layer_bytes, "GBps": layer_bytes / (us_layer * 1e-6) / 1e9,
+        "floor_us": layer_bytes / PEAK_HBM_BPS * 1e6, "layers_rotated": n_layers,
+        "note": "four pwg_ternary_gemv calls per layer on row-major T2, one graph over all layers"}
+    log(f"config 2: {us_layer:.1f} us per layer through per-call GEMVs ({layer_bytes / (us_layer * 1e-6) / 1e9:.0f} GB/s)")
+    # configuration 3: int8 projection + argmax, and 64 embedding rows
+    table = wl.weights[pwg.LAYOUT_ROWS][1]
+    vocab, hidden = table.shape
+    ws = torch.zeros(pwg.argmax_workspace_bytes(vocab, 1), dtype=torch.uint8, device=dev)
+    tok = torch.empty(1, dtype=torch.int32, device=dev)
+    g3 = capture(lambda: pwg.int8_gemv_argmax(table, wl.desc.out_scale, wl.desc.h, workspace=ws, token_out=tok,
+                                              stream=stream), stream)
+    prewarm(g3, stream, 0.1)
+    ms3 = time_graph(g3, stream, reps, 2)
+    del g3
+    lr = ref.int8_logits(wl.out_table.q, wl.out_table.scale, wl.h)
+    if not token_ok(int(tok.cpu()[0]), lr):
+        raise SystemExit("config 3 parity failed: token")
+    vbytes = vocab * hidden + 4 * vocab
+    ids = torch.from_numpy(synth.rng_for(synth.W_VOCAB, 2).integers(0, vocab, size=64).astype(np.int32)).to(dev)
+    ro = torch.empty((64, hidden), dtype=torch.int8, device=dev)
+    so = torch.empty(64, dtype=torch.float32, device=dev)
+    do = torch.empty((64, hidden), dtype=torch.float32, device=dev)
+    gfn = lambda: pwg.embed_gather(wl.desc.emb_table, wl.desc.emb_scale, ids, rows_out=ro, scales_out=so,  # noqa: E731
+                                   deq_out=do, stream=stream)
+    g4 = capture(gfn, stream)
+    prewarm(g4, stream, 0.05)
+    ms4 = time_graph(g4, stream, 200, 10)
+    del g4
+    er, _, _ = ref.embed_gather(wl.emb_table.q, wl.emb_table.scale, ids.cpu().numpy())
+    if not np.array_equal(ro.cpu().numpy(), er):
+        raise SystemExit("config 3 parity failed: gathered rows")
+    out["config3_int8_projection_argmax"] = {
+        "us_per_call": ms3 * 1e3, "bytes_per_call": vbytes, "GBps": vbytes / (ms3 * 1e-3) / 1e9,
+        "floor_us": vbytes / PEAK_HBM_BPS * 1e6, "kernel": "VALU int8 x five int8 limbs of h, row-major table"}
+    out["config3_gather_64_rows"] = {"us_per_call": ms4 * 1e3, "bytes_per_call": 64 * (hidden + 4),
+                                     "note": "int8 rows, scales and float32 dequantised rows of 64 ids"}
+    log(f"config 3: int8 projection + argmax {ms3 * 1e3:.1f} us ({vbytes / (ms3 * 1e-3) / 1e9:.0f} GB/s), "
+        f"gather of 64 rows {ms4 * 1e3:.2f} us")
+    return out
 
 
 def pass_desc(wl, n_layers, batch, seed):
@@ -511,11 +722,16 @@ def main():
     par = parity(wl, ref, token1)
     log(f"parity ok: {par}")
 
-    # 3. timed graph replays
+    # 3. timed graph replays: a time-based pre-warm (clocks settle whatever
+    #    --warmup says), the --warmup untimed replays, then exactly --steps
+    #    timed replays; then repeated rounds of --steps replays for the spread
     graph = capture(step_fn, stream)
+    n_pre = prewarm(graph, stream, args.prewarm)
     ms = time_graph(graph, stream, args.steps, args.warmup)
+    rounds = time_rounds(graph, stream, args.steps, args.rounds)
     pwg.step_status(wl.desc, stream=stream)
-    log(f"{args.schedule}: {ms * 1e3:.1f} us/step")
+    log(f"{args.schedule}: {ms * 1e3:.1f} us/step (after {n_pre} pre-warm replays); over {args.rounds} more rounds "
+        f"of {args.steps}: {spread(rounds)}")
     ms_direct = time_direct(step_fn, stream, args.steps, args.warmup)
     pwg.step_status(wl.desc, stream=stream)
     log(f"{args.schedule} without a graph: {ms_direct * 1e3:.1f} us/step")
@@ -610,6 +826,9 @@ def main():
             "algorithmic_bytes_per_step": bytes_,
         },
         "parity": par,
+        "timing": {"prewarm_replays": n_pre, "prewarm_s": args.prewarm, "warmup_replays": args.warmup,
+                   "timed_replays": args.steps, "spread_over_rounds": spread(rounds)},
+        "packing": packing_report(wl),
     }
     result.update(extra)
 
@@ -637,16 +856,26 @@ def main():
                               "kernel": kname, "per_launch_bytes": step_bytes, "avg_launch_us": ms_direct * 1e3}
     result["kernel_source_sha"] = kernel_source_sha(args.schedule)
 
+    if not args.no_units and pwg.LAYOUT_ROWS in wl.weights:
+        result["units"] = standalone_units(wl, stream)
     if not args.no_small_batch:
         result["small_batch"] = small_batch(wl, stream)
     if not args.no_compare:
         result["decode_attention"] = decode_attention(stream)
 
-    # 5. oracle CPU baseline (bounded sample)
+    # 5. oracle CPU baseline (bounded sample), in rounds interleaved with GPU
+    #    rounds of the timed step
     if not args.no_cpu_baseline:
         t0 = time.time()
-        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds, step_bytes)
-        log(f"cpu baseline in {time.time() - t0:.1f}s")
+        run(schedule)
+        g_cpu = capture(step_fn, stream)
+        prewarm(g_cpu, stream, 0.05)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds, step_bytes,
+                                              gpu_round=lambda: time_rounds(g_cpu, stream, args.steps, 1)[0])
+        del g_cpu
+        log(f"cpu baseline in {time.time() - t0:.1f}s: {result['cpu_baseline']['us_per_step'] / 1e6:.1f} s per step "
+            f"on {result['cpu_baseline']['cores']} threads, {result['cpu_baseline']['one_core']['us_per_step'] / 1e6:.1f}"
+            f" s on one ({result['cpu_baseline']['cpu_model']})")
     print(json.dumps(result), flush=True)
 
 

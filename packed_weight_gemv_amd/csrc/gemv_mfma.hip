@@ -12,13 +12,19 @@
 // A operands, a T2 word masked into FP4 nibbles +2 / -2 / 0 with three VALU
 // operations.  Products are exact and the instruction adds in float32.
 //
-// Work: 16-row blocks, contiguous ranges per wave (every wave of the grid
-// takes about the same number).  A block is cols / 256 tiles of 16 rows x 64
-// bytes; one wave load instruction moves one tile (lane 16 q + i: row i,
-// bytes 64 t + 16 q .. + 15), from the tiled arrangement (one contiguous KiB)
-// or straight from the row-major blob (16 pieces of 64 bytes).  Each wave
-// keeps two groups of kG tile loads in flight: one group's loads are issued
-// before the other group is multiplied.
+// Work: each workgroup (8 waves, one per CU) takes a contiguous range of
+// 16-row blocks, in batches that its LDS partial slots hold.  Every block's
+// K range is cut into KW chunks (KW = the largest power of two <= 8 that is
+// at most the block's tiles) and the 8 waves take one chunk of 8 / KW blocks
+// each at a time, so all waves stream even when the matrix has few rows.  A
+// chunk's partial 16 x 16 result goes to an LDS slot; at the end of a batch
+// one wave per block adds its KW partials in a fixed order (results do not
+// depend on timing), sums the piece columns, scales and stores.  A tile is
+// 16 rows x 64 bytes; one wave load instruction moves one tile (lane 16 q + i:
+// row i, bytes 64 t + 16 q .. + 15), from the tiled arrangement (one
+// contiguous KiB) or straight from the row-major blob (16 pieces of 64 bytes).
+// Each wave keeps two groups of kG tile loads in flight across chunk and
+// batch boundaries; the first group is issued before x is converted.
 #include "device_common.h"
 #include "operands.h"
 #include "pwg_internal.h"
@@ -69,22 +75,52 @@ __device__ __forceinline__ void convert_x(const float* __restrict__ x, int cols,
   __syncthreads();
 }
 
+constexpr int kMaxSlots = 96;                  // LDS partial slots (1 KiB each)
+constexpr size_t kLdsBudget = 160 * 1024;
+
+// Position of a wave in its sequence of tiles: batch b, block j of the
+// batch, tile t of the wave's chunk [t0, t1).  b == nbatch: done.
+struct Seq {
+  int b, j, t;
+};
+
 template <bool kTiled>
 __global__ __launch_bounds__(kThreads) void t2_mfma_gemv_kernel(const unsigned char* __restrict__ w,
                                                                  const float* __restrict__ scale, int rows, int cols,
-                                                                 const float* __restrict__ x, float* __restrict__ y) {
+                                                                 const float* __restrict__ x, float* __restrict__ y,
+                                                                 int kw, int nbb) {
   extern __shared__ __align__(16) unsigned char smem[];
-  convert_x(x, cols, smem);
-
   const unsigned lane = threadIdx.x & 63u, n = lane & 15u, g = lane >> 4;
   const int wave = uni(static_cast<int>(threadIdx.x >> 6));
   const int T = (cols + 255) >> 8;
   const int row_bytes = cols >> 2;
+  const size_t region = ops::ternary_region_bytes(cols);
+  unsigned char* slots = smem + region;
   const int bsc_off = static_cast<int>(ops::ternary_bsc_off(cols)), asc_off = static_cast<int>(ops::ternary_asc_off(cols));
   const long nb = (static_cast<long>(rows) + 15) / 16;
-  const long gw = static_cast<long>(blockIdx.x) * kWaves + wave, nw = static_cast<long>(gridDim.x) * kWaves;
-  const long b0 = gw * nb / nw, b1 = (gw + 1) * nb / nw;
+  const long bw0 = static_cast<long>(blockIdx.x) * nb / gridDim.x, bw1 = (static_cast<long>(blockIdx.x) + 1) * nb / gridDim.x;
+  const int nblk = static_cast<int>(bw1 - bw0);
+  const int nbatch = (nblk + nbb - 1) / nbb;
+  const int P = kWaves / kw;                // blocks in progress at a time
+  const int c = wave % kw, s0 = wave / kw;  // this wave's chunk and first block slot
+  const int t0 = c * T / kw, t1 = (c + 1) * T / kw;
   const unsigned tboff = ops::ternary_b_entry(n, g);
+  auto blocks_in = [&](int b) { return min(nbb, nblk - b * nbb); };
+  auto norm = [&](Seq& q) {
+    while (q.b < nbatch) {
+      if (q.j < blocks_in(q.b) && q.t < t1) return;
+      if (q.t >= t1) {
+        q.j += P;
+        q.t = t0;
+      }
+      if (q.j >= blocks_in(q.b)) {
+        ++q.b;
+        q.j = s0;
+        q.t = t0;
+      }
+    }
+  };
+  auto block_of = [&](const Seq& q) { return bw0 + static_cast<long>(q.b) * nbb + q.j; };
 
   // tile (blk, t) of this lane; tiles past the matrix read as zero
   auto load = [&](long blk, int t) -> u32x4 {
@@ -94,44 +130,59 @@ __global__ __launch_bounds__(kThreads) void t2_mfma_gemv_kernel(const unsigned c
     if (r >= rows || off >= row_bytes) return u32x4{0u, 0u, 0u, 0u};
     return __builtin_nontemporal_load((g_u32x4*)(w + static_cast<size_t>(r) * row_bytes + off));
   };
-
-  long lblk = b0, cblk = b0;
-  int lt = 0, ct = 0;
+  Seq ld{0, s0, t0}, cs{0, s0, t0};
+  norm(ld);
+  norm(cs);
   auto load_group = [&](u32x4 (&r)[kG]) {
 #pragma unroll
     for (int j = 0; j < kG; ++j) {
-      if (lblk < b1) r[j] = load(lblk, lt);
-      if (++lt == T) {
-        lt = 0;
-        ++lblk;
+      if (ld.b < nbatch) {
+        r[j] = load(block_of(ld), ld.t);
+        ++ld.t;
+        norm(ld);
       }
     }
   };
+  u32x4 ra[kG], rb[kG];
+  load_group(ra);  // the first loads do not wait for x
+  convert_x(x, cols, smem);
+
+  // End of batch bb: one wave per block adds the block's chunk partials (in
+  // chunk order), sums the piece columns, scales and stores.
+  int done_b = 0;
+  auto end_batch = [&]() {
+    __syncthreads();
+    const int nbl = blocks_in(done_b);
+    for (int j = wave; j < nbl; j += kWaves) {
+      v4f a = {0.f, 0.f, 0.f, 0.f};
+      for (int cc = 0; cc < kw; ++cc) a += *reinterpret_cast<const v4f*>(slots + (j * kw + cc) * 1024 + 16 * lane);
+      const long blk = bw0 + static_cast<long>(done_b) * nbb + j;
+      const v4f sc = ops::block_scales(scale, blk, rows, g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = ops::row16_sum(n < static_cast<unsigned>(ops::kSplits) ? a[i] : 0.f) * sc[i];
+      const long r0 = blk * 16 + 4 * g;
+      if (n == 0) {
+        if (r0 + 3 < rows) {
+          *(g_f32x4*)(y + r0) = f32x4{a[0], a[1], a[2], a[3]};
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (r0 + i < rows) ((g_float*)y)[r0 + i] = a[i];
+        }
+      }
+    }
+    __syncthreads();
+    ++done_b;
+  };
+
   v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  auto finish = [&]() {
-    const v4f sc = ops::block_scales(scale, cblk, rows, g);
-    v4f a = acc0 + acc1;  // rows 4 g + i, column n
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = ops::row16_sum(n < static_cast<unsigned>(ops::kSplits) ? a[i] : 0.f) * sc[i];
-    const long r0 = cblk * 16 + 4 * g;
-    if (n == 0) {
-      if (r0 + 3 < rows) {
-        *(g_f32x4*)(y + r0) = f32x4{a[0], a[1], a[2], a[3]};
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (r0 + i < rows) ((g_float*)y)[r0 + i] = a[i];
-      }
-    }
-    acc0 = v4f{0.f, 0.f, 0.f, 0.f};
-    acc1 = v4f{0.f, 0.f, 0.f, 0.f};
-  };
   auto compute_group = [&](const u32x4 (&r)[kG]) {
 #pragma unroll
-    for (int j = 0; j < kG; ++j) {
-      if (cblk < b1) {
+    for (int jj = 0; jj < kG; ++jj) {
+      if (cs.b < nbatch) {
         v8i a0, a1;
-        ops::ternary_unpack(r[j], a0, a1);
+        ops::ternary_unpack(r[jj], a0, a1);
+        const int ct = cs.t;
         const unsigned char* bp = smem + static_cast<size_t>(2 * ct) * ops::kTernaryMfmaBytes + tboff;
         const u32x4 b0l = *reinterpret_cast<const u32x4*>(bp), b0h = *reinterpret_cast<const u32x4*>(bp + 16);
         const u32x4 b1l = *reinterpret_cast<const u32x4*>(bp + ops::kTernaryMfmaBytes);
@@ -151,23 +202,26 @@ __global__ __launch_bounds__(kThreads) void t2_mfma_gemv_kernel(const unsigned c
         }
         // operands live past the instructions: no destination shares their registers
         asm volatile("" ::"v"(a0), "v"(a1), "v"(B0), "v"(B1));
-        if (++ct == T) {
-          finish();
-          ct = 0;
-          ++cblk;
+        if (ct + 1 == t1) {  // end of this wave's chunk of the block: its partial to the block's slot
+          *reinterpret_cast<v4f*>(slots + (cs.j * kw + c) * 1024 + 16 * lane) = acc0 + acc1;
+          acc0 = v4f{0.f, 0.f, 0.f, 0.f};
+          acc1 = v4f{0.f, 0.f, 0.f, 0.f};
         }
+        const int b_before = cs.b;
+        ++cs.t;
+        norm(cs);
+        for (int bb = b_before; bb < cs.b; ++bb) end_batch();
       }
     }
   };
 
-  u32x4 ra[kG], rb[kG];
-  load_group(ra);
-  while (cblk < b1) {
+  while (cs.b < nbatch) {
     load_group(rb);
     compute_group(ra);
     load_group(ra);
     compute_group(rb);
   }
+  while (done_b < nbatch) end_batch();  // batches in which this wave had no chunk
 }
 
 struct Instance {
@@ -188,7 +242,14 @@ int device_cus() {
 
 int launch(Instance& in, const void* w, const float* s, int64_t rows, int64_t cols, const float* x, int32_t batch,
            float* y, void* stream) {
-  const size_t lds = ops::ternary_region_bytes(cols);
+  const size_t region = (ops::ternary_region_bytes(cols) + 1023) / 1024 * 1024;
+  const int T = static_cast<int>((cols + 255) / 256);
+  int kw = 8;
+  while (kw > T) kw >>= 1;
+  int slots = static_cast<int>((kLdsBudget - region) / 1024);
+  slots = slots < kMaxSlots ? slots : kMaxSlots;
+  int nbb = slots / kw;
+  const size_t lds = region + static_cast<size_t>(nbb) * kw * 1024;
   if (in.max_active == 0 || in.lds != lds) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, in.fn, kThreads, lds) != hipSuccess || n < 1) n = 1;
@@ -204,7 +265,7 @@ int launch(Instance& in, const void* w, const float* s, int64_t rows, int64_t co
   for (int b = 0; b < batch; ++b) {
     const float* xb = x + static_cast<size_t>(b) * cols;
     float* yb = y + static_cast<size_t>(b) * rows;
-    void* args[] = {&wp, const_cast<float**>(&s), &r32, &c32, &xb, &yb};
+    void* args[] = {&wp, const_cast<float**>(&s), &r32, &c32, &xb, &yb, &kw, &nbb};
     const hipError_t e = hipLaunchKernel(in.fn, dim3(grid), dim3(kThreads), args, lds, st);
     if (e != hipSuccess) return fail(PWG_ERR_HIP, "ternary GEMV launch: %s", hipGetErrorString(e));
   }

@@ -775,10 +775,16 @@ Plan* plan_ptr(const pwg_step_desc* d, size_t ws_offset) {
 }
 
 int grid_size(int* grid) {
+  static int cus_of[64] = {};  // CUs per device, queried once
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return fail(PWG_ERR_HIP, "stream step: device query failed: %s", hipGetErrorString(e));
+  if (e == hipSuccess && dev >= 0 && dev < 64 && cus_of[dev] > 0) {
+    cus = cus_of[dev];
+  } else {
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail(PWG_ERR_HIP, "stream step: device query failed: %s", hipGetErrorString(e));
+    if (dev >= 0 && dev < 64) cus_of[dev] = cus;
+  }
   *grid = cus < kMaxGrid ? cus : kMaxGrid;
   return PWG_OK;
 }
@@ -1007,8 +1013,7 @@ int step_stream_plan(const pwg_step_desc* d, size_t ws_offset, void* stream) {
 }
 
 int step_stream_launch(const pwg_step_desc* d, size_t ws_offset, void* stream) {
-  TRY(step_stream_check(d));
-  int grid = 0;
+  int grid = 0;  // (the description was checked by the caller)
   TRY(grid_size(&grid));
   Plan* dplan = plan_ptr(d, ws_offset);
   char* dbase = reinterpret_cast<char*>(dplan);

@@ -2,6 +2,7 @@
 // HIP): buffer aliasing on the schedules that do not order their levels, and
 // the fingerprint that ties a workspace's device plan to the description it
 // was planned for.
+#include <algorithm>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -24,16 +25,17 @@ Range range_of(const void* p, size_t bytes, const char* what, int index) {
   return Range{a, a + bytes, what, index};
 }
 
-bool overlaps(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
-
-// FNV-1a over the bytes of each field.
+// A 64-bit mix of every field (each field zero-extended to 8 bytes).
 struct Hasher {
   uint64_t h = 1469598103934665603ull;
   template <typename T>
   void add(const T& v) {
-    unsigned char b[sizeof(T)];
-    std::memcpy(b, &v, sizeof(T));
-    for (unsigned char c : b) h = (h ^ c) * 1099511628211ull;
+    static_assert(sizeof(T) <= 8, "one word per field");
+    uint64_t u = 0;
+    std::memcpy(&u, &v, sizeof(T));
+    h ^= u + 0x9E3779B97F4A7C15ull + (h << 6) + (h >> 2);
+    h *= 0xFF51AFD7ED558CCDull;
+    h ^= h >> 33;
   }
   void add_input(const pwg_input& in) {
     add(in.op);
@@ -72,17 +74,36 @@ int check_unordered_aliasing(const pwg_step_desc* d, const char* fn) {
     if (r.index >= 0) std::snprintf(buf, n, "%s of level %d", r.what, r.index);
     else std::snprintf(buf, n, "%s", r.what);
   };
-  for (const Range& a : in)
-    for (const Range& b : out)
-      if (overlaps(a, b)) {
-        char na[48], nb2[48];
-        name(a, na, sizeof na);
-        name(b, nb2, sizeof nb2);
-        return fail(PWG_ERR_UNSUPPORTED,
-                    "%s: %s overlaps %s; this schedule runs levels in no fixed order, so an input may not share "
-                    "memory with anything the step writes (use the levels schedule for chained levels)",
-                    fn, na, nb2);
-      }
+  // sweep over the ranges by start address: an input overlaps an output iff
+  // one of them starts before the other ends; keep the output (and the
+  // input) that reaches furthest so far
+  struct Ev {
+    Range r;
+    bool input;
+  };
+  std::vector<Ev> ev;
+  ev.reserve(in.size() + out.size());
+  for (const Range& r : in)
+    if (r.lo != r.hi) ev.push_back({r, true});
+  for (const Range& r : out)
+    if (r.lo != r.hi) ev.push_back({r, false});
+  std::sort(ev.begin(), ev.end(), [](const Ev& a, const Ev& b) { return a.r.lo < b.r.lo; });
+  const Range* far_in = nullptr;
+  const Range* far_out = nullptr;
+  for (const Ev& e : ev) {
+    const Range* other = e.input ? far_out : far_in;
+    if (other && other->hi > e.r.lo) {
+      char na[48], nb2[48];
+      name(e.input ? e.r : *other, na, sizeof na);
+      name(e.input ? *other : e.r, nb2, sizeof nb2);
+      return fail(PWG_ERR_UNSUPPORTED,
+                  "%s: %s overlaps %s; this schedule runs levels in no fixed order, so an input may not share "
+                  "memory with anything the step writes (use the levels schedule for chained levels)",
+                  fn, na, nb2);
+    }
+    const Range*& far = e.input ? far_in : far_out;
+    if (!far || e.r.hi > far->hi) far = &e.r;
+  }
   return PWG_OK;
 }
 
