@@ -650,11 +650,11 @@ def main():
             dst = torch.empty_like(src)
             dst.copy_(src)
             del src, dst
-            # the VALU kernels on the same kinds of work, for the VALU-busy
-            # counters: the row-major ternary GEMV on a 393,216 x 4,096
-            # matrix (402 MB, more than the last-level cache; arbitrary
-            # bytes: the instruction stream does not depend on the values)
-            # and the int8 projection on the output table
+            # the per-call kernels on the same kinds of work, for the VALU / MFMA
+            # busy counters: the row-major ternary GEMV (matrix cores) on a
+            # 393,216 x 4,096 matrix (402 MB, more than the last-level cache;
+            # arbitrary bytes: the instruction stream does not depend on the
+            # values) and the VALU int8 projection on the output table
             rows_big, cols_big = 393216, 4096
             wbig = torch.randint(0, 256, (pwg.packed_size(rows_big, cols_big),), dtype=torch.uint8,
                                  device="cuda:0")
@@ -666,25 +666,19 @@ def main():
                 pwg.ternary_gemv(wbig, sbig, rows_big, cols_big, xbig, y=ybig, stream=stream)
                 if table is not None:
                     pwg.int8_gemv_argmax(table, wl.desc.out_scale, wl.desc.h, stream=stream)
-            # small batch (16 vectors), VALU against matrix cores on the same
-            # kinds of work: the gate|up level (24576 x 4096) row-major (VALU)
-            # and tiled (matrix cores); an int8 table of 3840 columns (VALU:
-            # not a multiple of 1024) and the output table tiled (matrix cores)
-            if pwg.LAYOUT_TILED in wl.weights and pwg.LAYOUT_ROWS in wl.weights:
+            # small batch (16 vectors) on the per-call matrix-core kernels: the
+            # gate|up level (24576 x 4096) and the output table, tiled
+            if pwg.LAYOUT_TILED in wl.weights:
                 B = 16
-                wr, wt = wl.weights[pwg.LAYOUT_ROWS][0][2], wl.weights[pwg.LAYOUT_TILED][0][2]
+                wt = wl.weights[pwg.LAYOUT_TILED][0][2]
                 _, sc, _, _, r, k = wl.desc.levels[2]
                 xb = torch.randn(B, k, device="cuda:0")
                 yb = torch.empty(B, r, device="cuda:0")
                 tws = torch.empty(pwg.batch_workspace_bytes(k, B), dtype=torch.uint8, device="cuda:0")
-                q3840 = torch.randint(-127, 128, (wl.desc.vocab, 3840), dtype=torch.int8, device="cuda:0")
-                h3840 = torch.randn(B, 3840, device="cuda:0")
                 hb = torch.randn(B, wl.desc.hidden, device="cuda:0")
                 iws = torch.empty(pwg.argmax_workspace_bytes(wl.desc.vocab, B), dtype=torch.uint8, device="cuda:0")
                 for _ in range(3):
-                    pwg.ternary_gemv(wr, sc, r, k, xb, y=yb, stream=stream)
                     pwg.ternary_gemv_tiled(wt, sc, r, k, xb, y=yb, workspace=tws, stream=stream)
-                    pwg.int8_gemv_argmax(q3840, wl.desc.out_scale, h3840, workspace=iws, stream=stream)
                     pwg.int8_gemv_argmax_tiled(wl.weights[pwg.LAYOUT_TILED][1], wl.desc.out_scale, wl.desc.vocab,
                                                wl.desc.hidden, hb, workspace=iws, stream=stream)
         torch.cuda.synchronize()
@@ -700,8 +694,8 @@ def main():
                 pwg.step_status(d, stream=stream)
                 del d
         log("counter run done: 3 steps, one 1 GiB device-to-device copy, 3 row-major ternary GEMVs "
-            "(393216x4096), 3 row-major int8 projections, 3 x 4 small-batch calls (16 vectors) and 3 batched "
-            "passes over every layer at 4 and at 16 vectors")
+            "(393216x4096), 3 row-major int8 projections, 3 x 2 tiled small-batch calls (16 vectors) and 3 "
+            "batched passes over every layer at 4 and at 16 vectors")
         return
 
     def run(desc_schedule):

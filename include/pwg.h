@@ -177,9 +177,10 @@ int pwg_tile_rows(const void* src, int64_t rows, int64_t row_bytes,
  * Asynchronous on `stream`, capturable, allocate nothing. */
 
 /* Workspace bytes of pwg_ternary_gemv_tiled for (cols, batch): the converted
- * activations (4 bytes per value and vector) and a few KiB; 0 for an
- * unsupported shape (cols not a multiple of 2048 in [2048, PWG_MAX_COLS],
- * batch not 4, 8 or 16). */
+ * activations (4 bytes per value and vector) and a few KiB; 16 (unused) for
+ * batch 1; 0 for an unsupported shape (batch 1: cols not a multiple of 256 in
+ * [256, PWG_MAX_COLS]; batch 4, 8, 16: cols not a multiple of 2048 in [2048,
+ * PWG_MAX_COLS]; other batches). */
 size_t pwg_batch_workspace_bytes(int64_t cols, int32_t batch);
 
 /* Batched ternary GEMV on tiled T2 weights:
@@ -190,8 +191,10 @@ size_t pwg_batch_workspace_bytes(int64_t cols, int32_t batch);
  *   x            device, float32[batch][cols]
  *   y            device, float32[batch][rows] (written)
  *   workspace    device, >= pwg_batch_workspace_bytes(cols, batch); scratch
- * batch 4, 8 or 16; cols a multiple of 2048.  The 2-bit codes are expanded
- * to int8 in registers.
+ * batch 1 (cols a multiple of 256): the matrix-core kernel of
+ * pwg_ternary_gemv on the tiled weights (FP8 pieces of x, float32-accurate;
+ * the workspace is not used).  batch 4, 8 or 16 (cols a multiple of 2048):
+ * the digits above, the 2-bit codes expanded to int8 in registers.
  * Errors: PWG_ERR_ARG (null, shape, batch), PWG_ERR_ALIGN (pointers are
  * 16-byte aligned), PWG_ERR_SIZE, PWG_ERR_UNSUPPORTED (cols), PWG_ERR_HIP. */
 int pwg_ternary_gemv_tiled(const void* w_tiled, const float* row_scale, int64_t rows, int64_t cols,

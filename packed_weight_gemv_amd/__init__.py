@@ -286,10 +286,13 @@ def batch_workspace_bytes(cols: int, batch: int) -> int:
 
 
 def ternary_gemv_tiled(w_tiled, row_scale, rows: int, cols: int, x, y=None, workspace=None, stream=None):
-    """y = row_scale * (W @ x.T).T for x of shape (batch, cols), batch 4, 8 or
-    16, W in the tiled arrangement (tile_rows of the T2 blob)."""
+    """y = row_scale * (W @ x.T).T for x of shape (batch, cols), batch 1, 4, 8
+    or 16 (x of shape (cols,) for one vector), W in the tiled arrangement
+    (tile_rows of the T2 blob)."""
     import torch
-    batch = x.shape[0]
+    batch = 1 if x.dim() == 1 else x.shape[0]
+    if x.dim() == 1 and y is None:
+        y = torch.empty(rows, dtype=torch.float32, device=x.device)
     if y is None:
         y = torch.empty((batch, rows), dtype=torch.float32, device=x.device)
     if workspace is None:

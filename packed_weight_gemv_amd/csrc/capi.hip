@@ -82,6 +82,7 @@ extern "C" int pwg_int8_gemv_argmax(const int8_t* table, const float* row_scale,
 }
 
 extern "C" size_t pwg_batch_workspace_bytes(int64_t cols, int32_t batch) {
+  if (batch == 1) return (cols >= 256 && cols % 256 == 0 && cols <= PWG_MAX_COLS) ? 16 : 0;  // no scratch used
   if (cols < 2048 || cols % 2048 != 0 || cols > PWG_MAX_COLS || !(batch == 4 || batch == 8 || batch == 16)) return 0;
   return batch_operand_bytes(cols, batch);
 }
@@ -92,9 +93,11 @@ extern "C" int pwg_ternary_gemv_tiled(const void* w_tiled, const float* row_scal
   const char* fn = "pwg_ternary_gemv_tiled";
   TRY(check_shape(rows, cols, fn));
   if (rows >= (int64_t{1} << 30)) return fail(PWG_ERR_ARG, "%s: too many rows", fn);
-  if (!(batch == 4 || batch == 8 || batch == 16)) return fail(PWG_ERR_ARG, "%s: batch must be 4, 8 or 16 (got %d)", fn, batch);
-  if (cols % 2048 != 0)
-    return fail(PWG_ERR_UNSUPPORTED, "%s: cols must be a multiple of 2048 (got %lld)", fn, static_cast<long long>(cols));
+  if (!(batch == 1 || batch == 4 || batch == 8 || batch == 16))
+    return fail(PWG_ERR_ARG, "%s: batch must be 1, 4, 8 or 16 (got %d)", fn, batch);
+  if (cols % (batch == 1 ? 256 : 2048) != 0)
+    return fail(PWG_ERR_UNSUPPORTED, "%s: cols must be a multiple of %d at batch %d (got %lld)", fn,
+                batch == 1 ? 256 : 2048, batch, static_cast<long long>(cols));
   TRY(check_ptr(w_tiled, fn, "w_tiled"));
   TRY(check_ptr(row_scale, fn, "row_scale"));
   TRY(check_ptr(x, fn, "x"));
@@ -102,6 +105,7 @@ extern "C" int pwg_ternary_gemv_tiled(const void* w_tiled, const float* row_scal
   TRY(check_ptr(workspace, fn, "workspace"));
   const size_t need = pwg_batch_workspace_bytes(cols, batch);
   if (workspace_bytes < need) return fail(PWG_ERR_SIZE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, need);
+  if (batch == 1) return launch_ternary_gemv_tiled1(w_tiled, row_scale, rows, cols, x, y, stream);
   return launch_t2b(w_tiled, row_scale, rows, cols, x, batch, y, workspace, stream);
 }
 

@@ -12,19 +12,25 @@
 // A operands, a T2 word masked into FP4 nibbles +2 / -2 / 0 with three VALU
 // operations.  Products are exact and the instruction adds in float32.
 //
-// Work: each workgroup (8 waves, one per CU) takes a contiguous range of
-// 16-row blocks, in batches that its LDS partial slots hold.  Every block's
-// K range is cut into KW chunks (KW = the largest power of two <= 8 that is
-// at most the block's tiles) and the 8 waves take one chunk of 8 / KW blocks
-// each at a time, so all waves stream even when the matrix has few rows.  A
-// chunk's partial 16 x 16 result goes to an LDS slot; at the end of a batch
-// one wave per block adds its KW partials in a fixed order (results do not
-// depend on timing), sums the piece columns, scales and stores.  A tile is
-// 16 rows x 64 bytes; one wave load instruction moves one tile (lane 16 q + i:
-// row i, bytes 64 t + 16 q .. + 15), from the tiled arrangement (one
-// contiguous KiB) or straight from the row-major blob (16 pieces of 64 bytes).
-// Each wave keeps two groups of kG tile loads in flight across chunk and
-// batch boundaries; the first group is issued before x is converted.
+// Work: each workgroup (8 waves) takes a contiguous range of 16-row blocks,
+// in batches that its LDS slots hold.  When the workgroup has at least two
+// blocks per wave, each wave streams whole blocks; with fewer, every block's
+// K range is cut into KW chunks (a power of two <= 8) so that all waves
+// stream even when the matrix has few rows.  At the end of its chunk a wave
+// sums the piece columns and writes the chunk's 16 row sums to an LDS slot;
+// at the end of a batch one wave per block adds the block's KW sums in chunk
+// order (results do not depend on timing), scales and stores.  Two slot
+// buffers alternate between batches, so a batch is reduced after the load
+// group that crossed its end.  A tile is 16 rows x 64 bytes; one wave load
+// instruction moves one tile (lane 16 q + i: row i, bytes 64 t + 16 q ..
+// + 15), from the tiled arrangement (one contiguous KiB) or straight from
+// the row-major blob (16 pieces of 64 bytes).  Loads go through a raw buffer
+// resource over the workgroup's range: lanes past the matrix and loads past
+// a wave's work read zeros without touching memory, so every load is issued
+// unconditionally and the compiler waits only for the group being
+// multiplied.  Each wave keeps two groups of kG tile loads in flight across
+// chunk and batch boundaries; x is loaded first, then the first group, and
+// the conversion waits for x alone.
 #include "device_common.h"
 #include "operands.h"
 #include "pwg_internal.h"
@@ -38,51 +44,95 @@ using ops::v8i;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kG = 4;  // tile loads per register group (two groups in flight per wave)
+constexpr int kG = 8;  // tile loads per register group (two groups in flight per wave)
 
-typedef const __attribute__((address_space(1))) u32x4 g_u32x4;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef const __attribute__((address_space(1))) f32x4 cg_f32x4;
 typedef __attribute__((address_space(1))) float g_float;
-typedef __attribute__((address_space(1))) f32x4 g_f32x4;
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Writes the operands of x (cols values, cols % 64 == 0) into the LDS region
-// `ops_lds`: thread (beta, h) converts half h of 32-value block beta; blocks
-// past cols (the rest of the last 256-value tile) are zero.  All threads of
-// the workgroup take part (uniform trip count: the half-block partners
-// exchange their maxima with a lane shuffle).
-__device__ __forceinline__ void convert_x(const float* __restrict__ x, int cols, unsigned char* ops_lds) {
-  const int T = (cols + 255) >> 8;
-  const int nhalf = T * 16;
-  const size_t bsc_off = ops::ternary_bsc_off(cols), asc_off = ops::ternary_asc_off(cols);
-  for (int t0 = 0; t0 < nhalf; t0 += kThreads) {
-    const int tid = t0 + static_cast<int>(threadIdx.x);
-    const int beta = tid >> 1, h = tid & 1, k0 = 32 * beta + 16 * h;
-    float xs[16];
-    float amax = 0.f;
-    const bool in = tid < nhalf && k0 < cols;  // cols % 16 == 0: a half is all in or all out
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 v = in ? ((cg_f32x4*)(x + k0))[q] : f32x4{0.f, 0.f, 0.f, 0.f};
-      xs[4 * q] = v.x; xs[4 * q + 1] = v.y; xs[4 * q + 2] = v.z; xs[4 * q + 3] = v.w;
-      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-    }
-    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-    if (tid < nhalf) ops::write_ternary_half(ops_lds, bsc_off, asc_off, beta, h, xs, ops::block_exponent(amax));
-  }
-  __syncthreads();
+// Raw buffer resource over [base, base + bytes): a lane whose offset lies
+// past the end reads zeros and moves no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+constexpr unsigned kOff = 0x80000000u;  // an offset past every resource: the load returns zero
+constexpr int kNt = 2;                  // streaming (non-temporal) cache policy
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNt));
 }
 
-constexpr int kMaxSlots = 96;                  // LDS partial slots (1 KiB each)
+// One conversion round of x: thread (beta, h) of round t0 holds half h of
+// 32-value block beta (zeros past cols).
+struct XRound {
+  u32x4 v[4];
+};
+__device__ __forceinline__ XRound load_x_round(__amdgpu_buffer_rsrc_t xr, int cols, int t0) {
+  const int tid = t0 + static_cast<int>(threadIdx.x);
+  const int k0 = 16 * tid;  // = 32 beta + 16 h
+  XRound q;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q.v[i] = buffer_load16(xr, k0 < cols ? 4u * static_cast<unsigned>(k0 + 4 * i) : kOff);
+  return q;
+}
+
+// Converts one round into the LDS operand region (cols % 64 == 0, so a half
+// block is all in or all out; blocks past cols up to the 256-value tile end
+// are written as zero).  Every thread takes part: the half-block partners
+// exchange their maxima with a lane shuffle.
+__device__ __forceinline__ void convert_x_round(const XRound& q, int cols, int t0, unsigned char* ops_lds) {
+  const int T = (cols + 255) >> 8;
+  const int nhalf = T * 16;
+  const int tid = t0 + static_cast<int>(threadIdx.x);
+  const int beta = tid >> 1, h = tid & 1;
+  float xs[16];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xs[4 * i + e] = __uint_as_float(q.v[i][e]);
+      amax = fmaxf(amax, fabsf(xs[4 * i + e]));
+    }
+  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+  if (tid < nhalf)
+    ops::write_ternary_half(ops_lds, ops::ternary_bsc_off(cols), ops::ternary_asc_off(cols), beta, h, xs,
+                            ops::block_exponent(amax));
+}
+
 constexpr size_t kLdsBudget = 160 * 1024;
+constexpr int kSlotBytes = 64;         // 16 float row sums of one (block, chunk)
+constexpr size_t kSlotBudget = 64 * 1024;
 
 // Position of a wave in its sequence of tiles: batch b, block j of the
 // batch, tile t of the wave's chunk [t0, t1).  b == nbatch: done.
 struct Seq {
   int b, j, t;
 };
+
+// The 16 row scales of block blk through scalar loads (they count on the
+// scalar memory counter, so waiting for them never waits for weight loads);
+// lane i < 16 gets row 16 blk + i.
+__device__ __forceinline__ float lane_row_scale(const float* scale, long blk, long rows, unsigned lane) {
+  typedef const __attribute__((address_space(4))) float cfloat;
+  cfloat* s = (cfloat*)scale;
+  const long base = blk * 16;
+  float r[16];
+  if (base + 16 <= rows) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = s[base + i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = s[base + i < rows ? base + i : rows - 1];
+  }
+  float out = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    out = lane == static_cast<unsigned>(i) ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(r[i]))) : out;
+  return out;
+}
 
 template <bool kTiled>
 __global__ __launch_bounds__(kThreads) void t2_mfma_gemv_kernel(const unsigned char* __restrict__ w,
@@ -94,8 +144,9 @@ __global__ __launch_bounds__(kThreads) void t2_mfma_gemv_kernel(const unsigned c
   const int wave = uni(static_cast<int>(threadIdx.x >> 6));
   const int T = (cols + 255) >> 8;
   const int row_bytes = cols >> 2;
-  const size_t region = ops::ternary_region_bytes(cols);
+  const int region = static_cast<int>((ops::ternary_region_bytes(cols) + 1023) / 1024 * 1024);
   unsigned char* slots = smem + region;
+  const int slot_buf = nbb * kw * kSlotBytes;  // one of two batch buffers
   const int bsc_off = static_cast<int>(ops::ternary_bsc_off(cols)), asc_off = static_cast<int>(ops::ternary_asc_off(cols));
   const long nb = (static_cast<long>(rows) + 15) / 16;
   const long bw0 = static_cast<long>(blockIdx.x) * nb / gridDim.x, bw1 = (static_cast<long>(blockIdx.x) + 1) * nb / gridDim.x;
@@ -120,56 +171,64 @@ __global__ __launch_bounds__(kThreads) void t2_mfma_gemv_kernel(const unsigned c
       }
     }
   };
-  auto block_of = [&](const Seq& q) { return bw0 + static_cast<long>(q.b) * nbb + q.j; };
+  auto block_of = [&](const Seq& q) { return static_cast<long>(q.b) * nbb + q.j; };  // relative to bw0
 
-  // tile (blk, t) of this lane; tiles past the matrix read as zero
-  auto load = [&](long blk, int t) -> u32x4 {
-    if (kTiled) return __builtin_nontemporal_load((g_u32x4*)(w + (static_cast<size_t>(blk) * T + t) * 1024u + 16u * lane));
-    const long r = blk * 16 + n;
+  // This workgroup's weights as one buffer resource; offsets are relative to
+  // its first block.  Rows past the matrix lie past the resource.
+  const __amdgpu_buffer_rsrc_t wr =
+      kTiled ? buffer_over(w + static_cast<size_t>(bw0) * T * 1024u, static_cast<unsigned>(nblk) * T * 1024u)
+             : buffer_over(w + static_cast<size_t>(bw0) * 16 * row_bytes,
+                           static_cast<unsigned>(min(static_cast<long>(rows), bw1 * 16) - bw0 * 16) * row_bytes);
+  auto offset = [&](long blk, int t) -> unsigned {
+    if (kTiled) return static_cast<unsigned>((blk * T + t) * 1024 + 16 * lane);
     const int off = 64 * t + 16 * static_cast<int>(g);
-    if (r >= rows || off >= row_bytes) return u32x4{0u, 0u, 0u, 0u};
-    return __builtin_nontemporal_load((g_u32x4*)(w + static_cast<size_t>(r) * row_bytes + off));
+    return off < row_bytes ? static_cast<unsigned>((blk * 16 + n) * row_bytes + off) : kOff;
   };
   Seq ld{0, s0, t0}, cs{0, s0, t0};
   norm(ld);
   norm(cs);
+  // kG loads per group, all issued (a load past the wave's sequence reads
+  // nothing), so the compiler counts them and waits only for the group it
+  // multiplies
   auto load_group = [&](u32x4 (&r)[kG]) {
 #pragma unroll
     for (int j = 0; j < kG; ++j) {
-      if (ld.b < nbatch) {
-        r[j] = load(block_of(ld), ld.t);
-        ++ld.t;
-        norm(ld);
-      }
+      r[j] = buffer_load16(wr, ld.b < nbatch ? offset(block_of(ld), ld.t) : kOff);
+      ++ld.t;  // past the end norm() leaves b == nbatch
+      norm(ld);
     }
   };
+  const __amdgpu_buffer_rsrc_t xr = buffer_over(x, static_cast<unsigned>(cols) * 4u);
+  // row scales of the first block this wave reduces (block `wave` of the
+  // first batch), loaded before anything else so that the reduction does not
+  // wait a memory latency for them
+  const float sc_first = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+      buffer_over(scale, static_cast<unsigned>(rows) * 4u),
+      lane < 16u && wave < nblk ? static_cast<unsigned>(((bw0 + wave) * 16 + lane) * 4) : kOff, 0, 0));
   u32x4 ra[kG], rb[kG];
-  load_group(ra);  // the first loads do not wait for x
-  convert_x(x, cols, smem);
-
-  // End of batch bb: one wave per block adds the block's chunk partials (in
-  // chunk order), sums the piece columns, scales and stores.
-  int done_b = 0;
-  auto end_batch = [&]() {
+  {
+    const XRound q = load_x_round(xr, cols, 0);  // x first: its wait leaves the weight loads in flight
+    load_group(ra);
+    convert_x_round(q, cols, 0, smem);
+    for (int r0 = kThreads; r0 < T * 16; r0 += kThreads) convert_x_round(load_x_round(xr, cols, r0), cols, r0, smem);
     __syncthreads();
+  }
+
+  // End of batch b: all partials of the batch are in slot buffer b & 1; wave
+  // j (step kWaves) adds block j's kw chunk sums in chunk order, scales and
+  // stores its 16 rows.  The second barrier frees the buffer for batch b + 2.
+  int done_b = 0;
+  auto reduce_batch = [&]() {
+    __syncthreads();
+    const float* sl = reinterpret_cast<const float*>(slots + (done_b & 1) * slot_buf);
     const int nbl = blocks_in(done_b);
     for (int j = wave; j < nbl; j += kWaves) {
-      v4f a = {0.f, 0.f, 0.f, 0.f};
-      for (int cc = 0; cc < kw; ++cc) a += *reinterpret_cast<const v4f*>(slots + (j * kw + cc) * 1024 + 16 * lane);
       const long blk = bw0 + static_cast<long>(done_b) * nbb + j;
-      const v4f sc = ops::block_scales(scale, blk, rows, g);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = ops::row16_sum(n < static_cast<unsigned>(ops::kSplits) ? a[i] : 0.f) * sc[i];
-      const long r0 = blk * 16 + 4 * g;
-      if (n == 0) {
-        if (r0 + 3 < rows) {
-          *(g_f32x4*)(y + r0) = f32x4{a[0], a[1], a[2], a[3]};
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (r0 + i < rows) ((g_float*)y)[r0 + i] = a[i];
-        }
-      }
+      float v = 0.f;
+      for (int cc = 0; cc < kw; ++cc) v += sl[(j * kw + cc) * 16 + (lane & 15u)];
+      v *= done_b == 0 && j == wave ? sc_first : lane_row_scale(scale, blk, rows, lane);
+      const long r = blk * 16 + lane;
+      if (lane < 16u && r < rows) ((g_float*)y)[r] = v;
     }
     __syncthreads();
     ++done_b;
@@ -180,9 +239,9 @@ __global__ __launch_bounds__(kThreads) void t2_mfma_gemv_kernel(const unsigned c
 #pragma unroll
     for (int jj = 0; jj < kG; ++jj) {
       if (cs.b < nbatch) {
+        const int ct = cs.t;
         v8i a0, a1;
         ops::ternary_unpack(r[jj], a0, a1);
-        const int ct = cs.t;
         const unsigned char* bp = smem + static_cast<size_t>(2 * ct) * ops::kTernaryMfmaBytes + tboff;
         const u32x4 b0l = *reinterpret_cast<const u32x4*>(bp), b0h = *reinterpret_cast<const u32x4*>(bp + 16);
         const u32x4 b1l = *reinterpret_cast<const u32x4*>(bp + ops::kTernaryMfmaBytes);
@@ -202,26 +261,34 @@ __global__ __launch_bounds__(kThreads) void t2_mfma_gemv_kernel(const unsigned c
         }
         // operands live past the instructions: no destination shares their registers
         asm volatile("" ::"v"(a0), "v"(a1), "v"(B0), "v"(B1));
-        if (ct + 1 == t1) {  // end of this wave's chunk of the block: its partial to the block's slot
-          *reinterpret_cast<v4f*>(slots + (cs.j * kw + c) * 1024 + 16 * lane) = acc0 + acc1;
+        if (ct + 1 == t1) {  // end of this wave's chunk of the block: the piece columns summed, to its slot
+          v4f a = acc0 + acc1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a[i] = ops::row16_sum(n < static_cast<unsigned>(ops::kSplits) ? a[i] : 0.f);
+          if (n == 0)
+            *reinterpret_cast<v4f*>(slots + (cs.b & 1) * slot_buf + (cs.j * kw + c) * kSlotBytes + 16 * g) = a;
           acc0 = v4f{0.f, 0.f, 0.f, 0.f};
           acc1 = v4f{0.f, 0.f, 0.f, 0.f};
         }
-        const int b_before = cs.b;
         ++cs.t;
         norm(cs);
-        for (int bb = b_before; bb < cs.b; ++bb) end_batch();
       }
     }
   };
 
+  // A group crosses at most one batch boundary (the host sizes batches so
+  // that every wave has at least kG tiles in each full batch), so the
+  // reduction of a batch can wait until the group ends: the next batch
+  // writes the other slot buffer.
   while (cs.b < nbatch) {
     load_group(rb);
     compute_group(ra);
+    while (done_b < cs.b) reduce_batch();
     load_group(ra);
     compute_group(rb);
+    while (done_b < cs.b) reduce_batch();
   }
-  while (done_b < nbatch) end_batch();  // batches in which this wave had no chunk
+  while (done_b < nbatch) reduce_batch();  // batches in which this wave had no chunk
 }
 
 struct Instance {
@@ -244,12 +311,10 @@ int launch(Instance& in, const void* w, const float* s, int64_t rows, int64_t co
            float* y, void* stream) {
   const size_t region = (ops::ternary_region_bytes(cols) + 1023) / 1024 * 1024;
   const int T = static_cast<int>((cols + 255) / 256);
-  int kw = 8;
-  while (kw > T) kw >>= 1;
-  int slots = static_cast<int>((kLdsBudget - region) / 1024);
-  slots = slots < kMaxSlots ? slots : kMaxSlots;
-  int nbb = slots / kw;
-  const size_t lds = region + static_cast<size_t>(nbb) * kw * 1024;
+  // the slot room is fixed, so the LDS footprint (and the occupancy) does
+  // not depend on how blocks are cut
+  const size_t slot_room = kLdsBudget - region < kSlotBudget ? kLdsBudget - region : kSlotBudget;
+  const size_t lds = region + slot_room;
   if (in.max_active == 0 || in.lds != lds) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, in.fn, kThreads, lds) != hipSuccess || n < 1) n = 1;
@@ -259,6 +324,21 @@ int launch(Instance& in, const void* w, const float* s, int64_t rows, int64_t co
   const long nb = (rows + 15) / 16;
   const long cap = static_cast<long>(device_cus()) * in.max_active;
   const unsigned grid = static_cast<unsigned>(nb < cap ? nb : cap);
+  const long wg_blocks = (nb + grid - 1) / grid;
+  // a workgroup's weights are addressed with 32-bit offsets
+  if (wg_blocks * 16 * (cols / 4) >= (1L << 31))
+    return fail(PWG_ERR_UNSUPPORTED, "ternary GEMV: %lld rows exceed the per-workgroup addressing", static_cast<long long>(rows));
+  // K chunks per block: a wave streams whole blocks when the workgroup has
+  // at least two blocks per wave; with fewer, the K range is cut so that
+  // every wave has tiles
+  int kw = 1;
+  while (kw < kWaves && 2 * kw <= T && wg_blocks * kw < 2 * kWaves) kw *= 2;
+  // two slot buffers of nbb blocks x kw chunks; every wave needs at least kG
+  // tiles in a full batch: nbb / P blocks of at least T / kw tiles each
+  int nbb = static_cast<int>(slot_room / (2 * static_cast<size_t>(kw) * kSlotBytes));
+  const int P = kWaves / kw;
+  const int need = P * ((kG + T / kw - 1) / (T / kw));
+  if (nbb < need) return fail(PWG_ERR_UNSUPPORTED, "ternary GEMV: %lld columns leave too little LDS", static_cast<long long>(cols));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   int r32 = static_cast<int>(rows), c32 = static_cast<int>(cols);
   const unsigned char* wp = static_cast<const unsigned char*>(w);

@@ -121,7 +121,8 @@ def test_batch_tiled_argument_errors():
     """The batched matrix-core entry points validate before launching."""
     bw = pwg.batch_workspace_bytes
     assert bw(4096, 16) >= 16 * 4096 * 4 and bw(4096, 4) >= 4 * 4096 * 4
-    assert bw(4096, 1) == 0 and bw(4096, 2) == 0 and bw(1024, 4) == 0 and bw(3072, 4) == 0 and bw(32768, 4) == 0
+    assert bw(4096, 1) == 16 and bw(1024, 1) == 16 and bw(4160, 1) == 0      # batch 1: no scratch, cols % 256
+    assert bw(4096, 2) == 0 and bw(1024, 4) == 0 and bw(3072, 4) == 0 and bw(32768, 4) == 0
     f = pwg._tgemv_tiled
     ws = bw(4096, 8)
     assert f(None, A, 64, 4096, A, 8, A, A, ws, None) == ERR_ARG
@@ -131,6 +132,7 @@ def test_batch_tiled_argument_errors():
     assert f(A, A, 64, 4096, A, 2, A, A, ws, None) == ERR_ARG and "batch" in pwg.last_error()
     assert f(A, A, 64, 1024, A, 8, A, A, ws, None) == ERR_UNSUPPORTED
     assert f(A, A, 0, 4096, A, 8, A, A, ws, None) == ERR_ARG
+    assert f(A, A, 64, 4160, A, 1, A, A, 16, None) == ERR_UNSUPPORTED and "256" in pwg.last_error()
     g = pwg._i8argmax_tiled
     iw = pwg.argmax_workspace_bytes(1000, 4)
     assert g(A, A, 1000, 4096, A, 1, A, iw, A, None, None) == ERR_ARG

@@ -373,6 +373,23 @@ def test_ternary_batch_tiled_vector_ranges():
         assert_gemv(y[b], yr[b], ref.ternary_gemv_magnitude(m.w, m.scale, xb[b]), f"vector {b}")
 
 
+TILED1_SHAPES = [(1, 256), (37, 1024), (6144, 4096), (4096, 12288), (1000, 16384), (24576, 4096)]
+
+
+@pytest.mark.parametrize("shape", TILED1_SHAPES, ids=[f"{r}x{c}" for r, c in TILED1_SHAPES])
+def test_ternary_tiled_batch1_matches_oracle_and_row_major(shape):
+    """Batch 1 on the tiled arrangement: the same kernel as the row-major
+    blob (the same tile slices reach the same lanes), so the outputs are
+    identical bit for bit; both meet the oracle criterion, outliers included."""
+    rows, cols = shape
+    m = synth.ternary_matrix((110, rows, cols), rows, cols)
+    for x in (synth.normal_f32(synth.rng_for(111, rows), cols), synth.outlier_vector(cols, 3)):
+        yt = pwg.ternary_gemv_tiled(tiled_t2(m.w), dev(m.scale), rows, cols, dev(x)).cpu().numpy()
+        yr = run_ternary(m.w, m.scale, x)
+        assert np.array_equal(yt.view(np.uint32), yr.view(np.uint32))
+        assert_gemv(yt, ref.ternary_gemv(m.w, m.scale, x), ref.ternary_gemv_magnitude(m.w, m.scale, x), str(shape))
+
+
 @pytest.mark.parametrize("batch", [4, 8, 16])
 def test_ternary_batch_tiled_outliers(batch):
     """Massive outliers inside every vector (N(0, 1) background, outliers
