@@ -18,11 +18,14 @@ specification for the packed-byte decoder/encoder:
                         grouped-query attention, SwiGLU and residual adds
                         between the projections;
 * ``packed_format``   - encoder/decoder of the 2-bit packed ternary format;
+* ``base3_format``    - encoder/decoder and device arrangement of the
+                        base-3 format (five weights per byte);
 * ``accounting``      - byte accounting of the 8B shape and the KV cache.
 
 Parity status of each function is stated in its module.  One part is
 "parity unpinned": the internals of the pages' own packed format (the pages
-name it but never specify it), so the build's 2-bit format is pinned only by
-its own specification and round trips, not by the pages.
+name it but never specify it), so the library's 2-bit and base-3 formats are
+pinned only by their own specifications, hand-derived bytes and round trips,
+not by the pages.
 """
-from . import accounting, attention, chain, packed_format, reference, verify  # noqa: F401
+from . import accounting, attention, base3_format, chain, packed_format, reference, verify  # noqa: F401

@@ -128,3 +128,38 @@ def draft_cycle_fraction(draft_steps: int = 6, draft_ratio: float = 1 / 12) -> f
     """Bytes of `draft_steps` draft steps plus one verify pass, relative to
     draft_steps + 1 plain steps (page section on speculative decoding)."""
     return (draft_steps * draft_ratio + 1) / (draft_steps + 1)
+
+
+# ---------------------------------------------------------------- base-3 packing
+# Five ternary weights per byte (3^5 = 243 <= 256): a row of c weights stores
+# ceil(c / 5) bytes.  Its device arrangement cuts a row into 30-weight groups
+# of 6 bytes and pads it to whole windows of 8 groups (48 bytes).
+B3_TRITS = 5
+B3_GROUP_BYTES = 6
+B3_WINDOW_GROUPS = 8
+
+
+def b3_row_bytes(cols: int) -> int:
+    return -(-cols // B3_TRITS)
+
+
+def b3_device_row_bytes(cols: int) -> int:
+    groups = -(-b3_row_bytes(cols) // B3_GROUP_BYTES)
+    return -(-groups // B3_WINDOW_GROUPS) * B3_WINDOW_GROUPS * B3_GROUP_BYTES
+
+
+def b3_layer_bytes(device: bool = False) -> int:
+    """Packed bytes of one layer's seven projections (row scales apart):
+    stored form, or the device arrangement the kernels stream."""
+    per_row = b3_device_row_bytes if device else b3_row_bytes
+    return sum(r * per_row(c) for r, c in LAYER_SHAPES.values())
+
+
+def b3_step_bytes(device: bool = False, n_layers: int = N_LAYERS) -> dict:
+    """step_bytes() with the projections in the base-3 format."""
+    w = n_layers * b3_layer_bytes(device)
+    s = n_layers * rows_per_layer() * SCALE_BYTES
+    out_table = VOCAB * HIDDEN + VOCAB * SCALE_BYTES
+    emb_row = HIDDEN + SCALE_BYTES
+    return {"ternary_weights": w, "ternary_scales": s, "output_table": out_table,
+            "embedding_row": emb_row, "total": w + s + out_table + emb_row}
