@@ -455,6 +455,94 @@ def standalone_units(wl, stream, reps=20):
     return out
 
 
+def base3_lane(wl, stream, reps=10):
+    """The step's ternary lane in the base-3 format (five weights per byte),
+    measured against its own bytes/bandwidth floor and against tiled T2 on
+    the same shapes: every 4,096-column row of the 36 layers stacked into one
+    1,253,376 x 4,096 matrix and every down row into one 147,456 x 12,288
+    matrix (one activation vector per width class; the same bytes per weight
+    as the step's 144 levels), one per-call GEMV each, then the int8 output
+    projection + argmax; one graph.  Random valid codes generated on the
+    device (the instruction stream does not depend on the values); sampled
+    rows are checked against the oracle before timing."""
+    import numpy as np
+    import torch
+
+    import packed_weight_gemv_amd as pwg
+    from oracle import base3_format as b3
+    from oracle import reference as ref
+    from tests.parity import assert_gemv
+    dev = "cuda:0"
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    n_layers = len(wl.desc.levels) // 4
+    shapes = [(n_layers * (4096 + 1024 + 1024 + 4096 + 12288 + 12288), 4096), (n_layers * 4096, 12288)]
+    mats = []
+    # every tensor is made and used on `stream` (generation, arrangement,
+    # frees), so no work on another stream can race with it
+    with torch.cuda.stream(stream):
+        for rows, cols in shapes:
+            raw = torch.randint(0, 243, (pwg.b3_packed_size(rows, cols),), dtype=torch.uint8, device=dev, generator=g)
+            t2 = torch.randint(0, 256, (rows * cols // 4,), dtype=torch.uint8, device=dev, generator=g) & 0x55  # codes 00 / 01
+            s_ = torch.empty(rows, dtype=torch.float32, device=dev).uniform_(0.01, 0.1, generator=g)
+            x_ = torch.randn(cols, dtype=torch.float32, device=dev, generator=g)
+            mats.append({"rows": rows, "cols": cols, "b3": pwg.tile_b3(raw, rows, cols, stream=stream),
+                         "t2": pwg.tile_rows(t2, rows, cols // 4, stream=stream), "s": s_, "x": x_,
+                         "y": torch.empty(rows, dtype=torch.float32, device=dev)})
+            stream.synchronize()
+            # parity on sampled rows: the oracle decodes the stored bytes of those rows
+            pick = np.sort(np.random.default_rng(rows).choice(rows, 256, replace=False))
+            B = pwg.b3_packed_size(1, cols)
+            rb = raw.view(rows, B)[torch.from_numpy(pick).to(dev)].cpu().numpy()
+            w = b3.decode(rb.reshape(-1), len(pick), cols)
+            m = mats[-1]
+            pwg.ternary_gemv_b3(m["b3"], m["s"], rows, cols, m["x"], y=m["y"], stream=stream)
+            stream.synchronize()
+            sv, xv = m["s"].cpu().numpy()[pick], m["x"].cpu().numpy()
+            assert_gemv(m["y"].cpu().numpy()[pick], ref.ternary_gemv(w, sv, xv), ref.ternary_gemv_magnitude(w, sv, xv),
+                        f"base-3 {rows}x{cols} sample")
+            del raw, t2
+    table = wl.weights[pwg.LAYOUT_ROWS][1]  # the row-major int8 table (pwg_int8_gemv_argmax's input)
+    ws = torch.zeros(pwg.argmax_workspace_bytes(wl.desc.vocab, 1), dtype=torch.uint8, device=dev)
+    tok = torch.empty(1, dtype=torch.int32, device=dev)
+
+    def lane(kind):
+        def fn():
+            for m in mats:
+                if kind == "b3":
+                    pwg.ternary_gemv_b3(m["b3"], m["s"], m["rows"], m["cols"], m["x"], y=m["y"], stream=stream)
+                else:
+                    pwg.ternary_gemv_tiled(m["t2"], m["s"], m["rows"], m["cols"], m["x"], y=m["y"], stream=stream)
+            pwg.int8_gemv_argmax(table, wl.desc.out_scale, wl.desc.h, workspace=ws, token_out=tok, stream=stream)
+        return fn
+    out = {}
+    vocab_bytes = wl.desc.vocab * wl.desc.hidden + 4 * wl.desc.vocab
+    for kind in ("b3", "t2"):
+        gr = capture(lane(kind), stream)
+        prewarm(gr, stream, 0.1)
+        rounds = time_rounds(gr, stream, reps, 5)
+        del gr
+        us = float(np.median(rounds)) * 1e3
+        if kind == "b3":
+            wbytes = sum(pwg.b3_tiled_size(m["rows"], m["cols"]) for m in mats)
+            stored = sum(pwg.b3_packed_size(m["rows"], m["cols"]) for m in mats)
+        else:
+            wbytes = stored = sum(m["rows"] * m["cols"] // 4 for m in mats)
+        total = wbytes + sum(4 * m["rows"] for m in mats) + vocab_bytes
+        total_stored = stored + sum(4 * m["rows"] for m in mats) + vocab_bytes
+        out[kind] = {"us": us, "spread": spread(rounds), "bytes_streamed": total, "GBps": total / (us * 1e-6) / 1e9,
+                     "floor_us": total / PEAK_HBM_BPS * 1e6, "floor_us_stored_bytes": total_stored / PEAK_HBM_BPS * 1e6,
+                     "frac_of_floor": total / PEAK_HBM_BPS * 1e6 / us}
+    out["kernels"] = "pwg_ternary_gemv_b3 / pwg_ternary_gemv_tiled per width class, then pwg_int8_gemv_argmax"
+    out["note"] = ("the step's ternary lane stacked per width class (one activation vector each); base-3 bytes as "
+                   "arranged for the device (30-weight groups in 48-byte windows) and as stored (0.2 B/weight)")
+    log(f"base-3 lane: {out['b3']['us']:.1f} us ({out['b3']['GBps']:.0f} GB/s, floor {out['b3']['floor_us']:.1f} us "
+        f"as arranged, {out['b3']['floor_us_stored_bytes']:.1f} us stored); T2 on the same shapes: "
+        f"{out['t2']['us']:.1f} us ({out['t2']['GBps']:.0f} GB/s, floor {out['t2']['floor_us']:.1f} us)")
+    del mats
+    return out
+
+
 def pass_desc(wl, n_layers, batch, seed):
     """A pass over the first n_layers layers' levels and the output table on
     the tiled weights: the stream schedule for one vector, the batched pass
@@ -666,6 +754,15 @@ def main():
                 pwg.ternary_gemv(wbig, sbig, rows_big, cols_big, xbig, y=ybig, stream=stream)
                 if table is not None:
                     pwg.int8_gemv_argmax(table, wl.desc.out_scale, wl.desc.h, stream=stream)
+            # the same matrix shape tiled (T2) and in the base-3 device arrangement
+            wt2 = pwg.tile_rows(wbig, rows_big, cols_big // 4, stream=stream)
+            del wbig
+            wb3 = pwg.tile_b3(torch.randint(0, 243, (pwg.b3_packed_size(rows_big, cols_big),), dtype=torch.uint8,
+                                            device="cuda:0"), rows_big, cols_big, stream=stream)
+            for _ in range(3):
+                pwg.ternary_gemv_tiled(wt2, sbig, rows_big, cols_big, xbig, y=ybig, stream=stream)
+                pwg.ternary_gemv_b3(wb3, sbig, rows_big, cols_big, xbig, y=ybig, stream=stream)
+            del wt2, wb3
             # small batch (16 vectors) on the per-call matrix-core kernels: the
             # gate|up level (24576 x 4096) and the output table, tiled
             if pwg.LAYOUT_TILED in wl.weights:
@@ -694,7 +791,8 @@ def main():
                 pwg.step_status(d, stream=stream)
                 del d
         log("counter run done: 3 steps, one 1 GiB device-to-device copy, 3 row-major ternary GEMVs "
-            "(393216x4096), 3 row-major int8 projections, 3 x 2 tiled small-batch calls (16 vectors) and 3 "
+            "(393216x4096), 3 row-major int8 projections, 3 tiled and 3 base-3 ternary GEMVs of the same shape, "
+            "3 x 2 tiled small-batch calls (16 vectors) and 3 "
             "batched passes over every layer at 4 and at 16 vectors")
         return
 
@@ -854,6 +952,8 @@ def main():
         result["units"] = standalone_units(wl, stream)
     if not args.no_small_batch:
         result["small_batch"] = small_batch(wl, stream)
+    if not args.no_units and pwg.LAYOUT_ROWS in wl.weights:
+        result["base3_lane"] = base3_lane(wl, stream)
     if not args.no_compare:
         result["decode_attention"] = decode_attention(stream)
 

@@ -165,6 +165,77 @@ int pwg_tile_rows(const void* src, int64_t rows, int64_t row_bytes,
                   void* dst, size_t dst_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Base-3 packed ternary format "B3" (five weights per byte, 0.2 bytes per
+ * weight against T2's 0.25).  Page "The Neutrino Engine", section "A 104
+ * microsecond floor inside a 694 microsecond step": weight bytes over memory
+ * bandwidth bound a batch-1 step, and a smaller artifact lowers that bound on
+ * every backend; section "The file is not the traffic": the page's own
+ * 72,351,744-byte layer slab (3 bits per weight).  The pages do not specify
+ * their format; this is the library's:
+ *   - logical W in {-1,0,+1}^(rows x cols), 1 <= cols <= PWG_MAX_COLS;
+ *   - row-major: row r is bytes [r*B, (r+1)*B), B = ceil(cols/5);
+ *   - byte m of a row holds weights k = 5m + i (i = 0..4) as base-3 digits
+ *     d_i = w_k + 1, least significant first:
+ *         byte = d_0 + 3 d_1 + 9 d_2 + 27 d_3 + 81 d_4;
+ *     weights past the row end are 0 (digit 1); bytes 243..255 never occur;
+ *   - no header; row scales are separate float32 arrays.
+ * One layer of the 8B shape is 38,617,088 bytes (0.534 of the slab).
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of a B3 blob: rows * ceil(cols / 5); 0 for an invalid shape (rows <
+ * 1, cols outside [1, PWG_MAX_COLS]).  Pure host function. */
+size_t pwg_b3_packed_size(int64_t rows, int64_t cols);
+
+/* Pack a logical ternary matrix into B3 on the host (multi-threaded):
+ *   w_host       host, int8 rows x cols row-major, values in {-1, 0, 1}
+ *   out_host     host, >= pwg_b3_packed_size(rows, cols) bytes
+ *   out_bytes    may be NULL; receives the blob size
+ * Errors: PWG_ERR_ARG (null / bad shape), PWG_ERR_SIZE (capacity too small),
+ * PWG_ERR_VALUE (a value outside {-1,0,1}; out_host contents unspecified). */
+int pwg_pack_weights_b3(const int8_t* w_host, int64_t rows, int64_t cols,
+                        void* out_host, size_t out_capacity, size_t* out_bytes);
+
+/* Inverse of pwg_pack_weights_b3 (host).  PWG_ERR_VALUE on a byte > 242. */
+int pwg_unpack_weights_b3(const void* packed_host, int64_t rows, int64_t cols,
+                          int8_t* w_out_host);
+
+/* Bytes of the device arrangement of a B3 blob: ceil(rows/16) 16-row blocks
+ * of W = ceil(ceil(ceil(cols/5)/6)/8) windows of 768 bytes (40,304,640 bytes
+ * for one layer of the 8B shape); 0 for an invalid shape. */
+size_t pwg_b3_tiled_size(int64_t rows, int64_t cols);
+
+/* Load-time device arrangement of a B3 blob (page section "The same weights
+ * take four execution paths": the loader arranges the same stored values for
+ * the device).  Each row's bytes are cut into 30-weight groups of 6 bytes and
+ * padded with the zero-weight byte 121 to whole windows of 8 groups; rows are
+ * padded to a multiple of 16 with zero-weight rows.  Window tile (rb, t) is
+ * the (rb * W + t)-th 768 bytes; its 12 bytes at offset 12 L (L = 16 g + i)
+ * are group 8t+g and then group 8t+4+g of row 16 rb + i: one lane's A
+ * operands of two matrix-core instructions.
+ *   src          device, the B3 blob (no alignment needed)
+ *   dst          device, >= pwg_b3_tiled_size(rows, cols) bytes, 16-byte
+ *                aligned, not overlapping src
+ * Asynchronous on `stream`.  Errors: PWG_ERR_ARG (null, bad shape, overlap),
+ * PWG_ERR_ALIGN, PWG_ERR_SIZE, PWG_ERR_HIP. */
+int pwg_tile_b3(const void* src, int64_t rows, int64_t cols,
+                void* dst, size_t dst_bytes, void* stream);
+
+/* Ternary GEMV on B3 weights in their device arrangement:
+ *     y[b, r] = row_scale[r] * sum_k W[r, k] * x[b, k]
+ *   w_b3_tiled   device, pwg_tile_b3 output for rows x cols
+ *   row_scale    device, float32[rows]
+ *   x            device, float32[batch][cols]
+ *   y            device, float32[batch][rows] (written)
+ * The same arithmetic and accuracy as pwg_ternary_gemv (six e4m3 pieces of x
+ * per value, FP4 weights, float32 sums; one E8M0 exponent per 30-value group
+ * of x).  Each byte becomes five FP4 weights through a 256-entry table in
+ * LDS (bytes 243..255 read as zero weights).  batch > 1 runs one pass per
+ * vector.  Errors: PWG_ERR_ARG (null, shape, batch), PWG_ERR_ALIGN
+ * (pointers are 16-byte aligned), PWG_ERR_HIP. */
+int pwg_ternary_gemv_b3(const void* w_b3_tiled, const float* row_scale, int64_t rows, int64_t cols,
+                        const float* x, int32_t batch, float* y, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Small batch on the tiled arrangement (page section "The 0.6B model does not
  * get to decide": several drafted tokens are scored in one batched pass, so
  * each weight is read once for all of them).  Both calls take the weights as

@@ -112,6 +112,12 @@ _tgemv_tiled = _sig("pwg_ternary_gemv_tiled", C.c_int, _vp, _vp, _i64, _i64, _vp
 _i8argmax_tiled = _sig("pwg_int8_gemv_argmax_tiled", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _sz, _vp, _vp, _vp)
 _tiled_size = _sig("pwg_tiled_size", _sz, _i64, _i64)
 _tile_rows = _sig("pwg_tile_rows", C.c_int, _vp, _i64, _i64, _vp, _sz, _vp)
+_b3_packed_size = _sig("pwg_b3_packed_size", _sz, _i64, _i64)
+_pack_b3 = _sig("pwg_pack_weights_b3", C.c_int, _vp, _i64, _i64, _vp, _sz, C.POINTER(_sz))
+_unpack_b3 = _sig("pwg_unpack_weights_b3", C.c_int, _vp, _i64, _i64, _vp)
+_b3_tiled_size = _sig("pwg_b3_tiled_size", _sz, _i64, _i64)
+_tile_b3 = _sig("pwg_tile_b3", C.c_int, _vp, _i64, _i64, _vp, _sz, _vp)
+_tgemv_b3 = _sig("pwg_ternary_gemv_b3", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp)
 _step_ws = _sig("pwg_step_workspace_bytes", _sz, C.POINTER(_StepDesc))
 _step_plan = _sig("pwg_step_plan", C.c_int, C.POINTER(_StepDesc), _vp)
 _step = _sig("pwg_decode_step_weights", C.c_int, C.POINTER(_StepDesc), _vp)
@@ -125,7 +131,9 @@ EXPORTED = ["pwg_packed_size", "pwg_pack_weights", "pwg_unpack_weights", "pwg_te
             "pwg_int8_gemv_argmax_tiled",
             "pwg_step_workspace_bytes", "pwg_step_plan", "pwg_decode_step_weights",
             "pwg_step_status", "pwg_last_error", "pwg_version", "pwg_attention_workspace_bytes",
-            "pwg_gqa_decode_attention", "pwg_verify_accept", "pwg_int8_gemv_argmax_noalloc"]
+            "pwg_gqa_decode_attention", "pwg_verify_accept", "pwg_int8_gemv_argmax_noalloc",
+            "pwg_b3_packed_size", "pwg_pack_weights_b3", "pwg_unpack_weights_b3", "pwg_b3_tiled_size",
+            "pwg_tile_b3", "pwg_ternary_gemv_b3"]
 
 
 def last_error() -> str:
@@ -181,6 +189,33 @@ def unpack_weights(blob: np.ndarray, rows: int, cols: int) -> np.ndarray:
     if blob.size < _packed_size(rows, cols):
         raise ValueError("blob too small")
     _check(_unpack(blob.ctypes.data, rows, cols, out.ctypes.data))
+    return out
+
+
+def b3_packed_size(rows: int, cols: int) -> int:
+    return _b3_packed_size(rows, cols)
+
+
+def pack_weights_b3(w: np.ndarray) -> np.ndarray:
+    """Pack an int8 (rows, cols) ternary matrix into a uint8 base-3 blob
+    (five weights per byte; host)."""
+    w = np.ascontiguousarray(w, dtype=np.int8)
+    if w.ndim != 2:
+        raise ValueError("w must be 2-D")
+    rows, cols = w.shape
+    n = _b3_packed_size(rows, cols)
+    out = np.empty(max(n, 1), dtype=np.uint8)
+    written = _sz(0)
+    _check(_pack_b3(w.ctypes.data, rows, cols, out.ctypes.data, out.nbytes if n else 0, C.byref(written)))
+    return out[:written.value]
+
+
+def unpack_weights_b3(blob: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    out = np.empty((rows, cols), dtype=np.int8)
+    if blob.size < _b3_packed_size(rows, cols):
+        raise ValueError("blob too small")
+    _check(_unpack_b3(blob.ctypes.data, rows, cols, out.ctypes.data))
     return out
 
 
@@ -331,6 +366,32 @@ def tile_rows(src, rows: int, row_bytes: int, dst=None, stream=None):
         dst = torch.empty(max(need, 16), dtype=torch.uint8, device=src.device)
     _check(_tile_rows(_ptr(src), rows, row_bytes, _ptr(dst), dst.numel() * dst.element_size(), _stream(stream)))
     return dst
+
+
+def b3_tiled_size(rows: int, cols: int) -> int:
+    return _b3_tiled_size(rows, cols)
+
+
+def tile_b3(src, rows: int, cols: int, dst=None, stream=None):
+    """Device arrangement of a base-3 blob on the device (768-byte windows of
+    30-weight groups)."""
+    import torch
+    need = _b3_tiled_size(rows, cols)
+    if dst is None:
+        dst = torch.empty(max(need, 16), dtype=torch.uint8, device=src.device)
+    _check(_tile_b3(_ptr(src), rows, cols, _ptr(dst), dst.numel() * dst.element_size(), _stream(stream)))
+    return dst
+
+
+def ternary_gemv_b3(w_b3_tiled, row_scale, rows: int, cols: int, x, y=None, stream=None):
+    """y = row_scale * (W @ x) on base-3 weights as tile_b3 arranges them; x
+    of shape (cols,) or (batch, cols)."""
+    import torch
+    batch = 1 if x.dim() == 1 else x.shape[0]
+    if y is None:
+        y = torch.empty((rows,) if x.dim() == 1 else (batch, rows), dtype=torch.float32, device=x.device)
+    _check(_tgemv_b3(_ptr(w_b3_tiled), _ptr(row_scale), rows, cols, _ptr(x), batch, _ptr(y), _stream(stream)))
+    return y
 
 
 # ---------------------------------------------------------------- decode step

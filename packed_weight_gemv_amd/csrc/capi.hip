@@ -4,6 +4,7 @@
 
 #include <cmath>
 
+#include "operands.h"
 #include "pwg_internal.h"
 
 using namespace pwg;
@@ -165,6 +166,46 @@ extern "C" int pwg_tile_rows(const void* src, int64_t rows, int64_t row_bytes, v
   const size_t src_bytes = static_cast<size_t>(rows) * static_cast<size_t>(row_bytes);
   if (s0 < d0 + need && d0 < s0 + src_bytes) return fail(PWG_ERR_ARG, "%s: src and dst overlap", fn);
   return launch_tile_rows(src, rows, row_bytes, dst, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Base-3 weights
+// ---------------------------------------------------------------------------
+namespace {
+int check_b3_shape(int64_t rows, int64_t cols, const char* fn) {
+  if (rows < 1 || rows > (int64_t{1} << 30))
+    return fail(PWG_ERR_ARG, "%s: rows must be in [1, 2^30] (got %lld)", fn, (long long)rows);
+  if (cols < 1 || cols > PWG_MAX_COLS)
+    return fail(PWG_ERR_ARG, "%s: cols must be in [1, %d] (got %lld)", fn, PWG_MAX_COLS, (long long)cols);
+  return PWG_OK;
+}
+}  // namespace
+
+extern "C" size_t pwg_b3_tiled_size(int64_t rows, int64_t cols) { return b3_tiled_bytes(rows, cols); }
+
+extern "C" int pwg_tile_b3(const void* src, int64_t rows, int64_t cols, void* dst, size_t dst_bytes, void* stream) {
+  const char* fn = "pwg_tile_b3";
+  TRY(check_b3_shape(rows, cols, fn));
+  if (src == nullptr) return fail(PWG_ERR_ARG, "%s: src is null", fn);
+  TRY(check_ptr(dst, fn, "dst"));
+  const size_t need = b3_tiled_bytes(rows, cols);
+  if (dst_bytes < need) return fail(PWG_ERR_SIZE, "%s: dst has %zu bytes, needs %zu", fn, dst_bytes, need);
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  const size_t src_bytes = static_cast<size_t>(rows) * static_cast<size_t>(ops::b3_row_bytes(cols));
+  if (s0 < d0 + need && d0 < s0 + src_bytes) return fail(PWG_ERR_ARG, "%s: src and dst overlap", fn);
+  return launch_tile_b3(src, rows, cols, dst, stream);
+}
+
+extern "C" int pwg_ternary_gemv_b3(const void* w_b3_tiled, const float* row_scale, int64_t rows, int64_t cols,
+                                   const float* x, int32_t batch, float* y, void* stream) {
+  const char* fn = "pwg_ternary_gemv_b3";
+  TRY(check_b3_shape(rows, cols, fn));
+  if (!valid_batch(batch)) return fail(PWG_ERR_ARG, "%s: batch must be 1, 4, 8 or 16 (got %d)", fn, batch);
+  TRY(check_ptr(w_b3_tiled, fn, "w_b3_tiled"));
+  TRY(check_ptr(row_scale, fn, "row_scale"));
+  TRY(check_ptr(x, fn, "x"));
+  TRY(check_ptr(y, fn, "y"));
+  return launch_ternary_gemv_b3(w_b3_tiled, row_scale, rows, cols, x, batch, y, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -44,7 +44,7 @@ using ops::v8i;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kG = 8;  // tile loads per register group (two groups in flight per wave)
+
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) float g_float;
@@ -64,47 +64,76 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, unsigne
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNt));
 }
 
+enum Fmt { kT2Rows, kT2Tiled, kB3Tiled };
+
+// Tile loads per register group (two groups in flight per wave).  Base-3
+// tiles take more registers to decode; with shorter groups the kernel fits
+// in 80 registers and three workgroups share a CU.
+__host__ __device__ constexpr int group_tiles(int fmt) { return fmt == kB3Tiled ? 4 : 8; }
+// Resident workgroups per CU the LDS sizing aims at for large matrices.
+__host__ __device__ constexpr int target_residency(int fmt) { return fmt == kB3Tiled ? 3 : 2; }
+
+__device__ __forceinline__ int fmt_windows(int fmt, int cols) {
+  return fmt == kB3Tiled ? static_cast<int>(ops::b3_windows(cols)) : (cols + 255) >> 8;
+}
+
 // One conversion round of x: thread (beta, h) of round t0 holds half h of
-// 32-value block beta (zeros past cols).
+// 32-value block beta (T2: x[32 beta + 16 h + i]; base-3: group beta,
+// x[30 beta + 16 h + i] for 16 h + i < 30), zeros past cols.
 struct XRound {
-  u32x4 v[4];
+  float v[16];
 };
+template <int kFmt>
 __device__ __forceinline__ XRound load_x_round(__amdgpu_buffer_rsrc_t xr, int cols, int t0) {
   const int tid = t0 + static_cast<int>(threadIdx.x);
-  const int k0 = 16 * tid;  // = 32 beta + 16 h
+  const int beta = tid >> 1, h = tid & 1;
   XRound q;
+  if (kFmt == kB3Tiled) {
+    const int k0 = ops::kB3GroupWeights * beta + 16 * h;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) q.v[i] = buffer_load16(xr, k0 < cols ? 4u * static_cast<unsigned>(k0 + 4 * i) : kOff);
+    for (int i = 0; i < 16; ++i) {
+      const bool in = 16 * h + i < ops::kB3GroupWeights && k0 + i < cols;
+      q.v[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, in ? 4u * static_cast<unsigned>(k0 + i) : kOff, 0, 0));
+    }
+  } else {
+    const int k0 = 16 * tid;  // = 32 beta + 16 h; cols % 16 == 0: a half is all in or all out
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 v = buffer_load16(xr, k0 < cols ? 4u * static_cast<unsigned>(k0 + 4 * i) : kOff);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q.v[4 * i + e] = __uint_as_float(v[e]);
+    }
+  }
   return q;
 }
 
-// Converts one round into the LDS operand region (cols % 64 == 0, so a half
-// block is all in or all out; blocks past cols up to the 256-value tile end
-// are written as zero).  Every thread takes part: the half-block partners
-// exchange their maxima with a lane shuffle.
-__device__ __forceinline__ void convert_x_round(const XRound& q, int cols, int t0, unsigned char* ops_lds) {
-  const int T = (cols + 255) >> 8;
+// Converts one round into the LDS operand region (blocks past cols up to the
+// last window are written as zero).  Every thread takes part: the half-block
+// partners exchange their maxima with a lane shuffle.
+template <int kFmt>
+__device__ __forceinline__ void convert_x_round(XRound& q, int cols, int t0, unsigned char* ops_lds) {
+  const int T = fmt_windows(kFmt, cols);
   const int nhalf = T * 16;
   const int tid = t0 + static_cast<int>(threadIdx.x);
   const int beta = tid >> 1, h = tid & 1;
-  float xs[16];
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      xs[4 * i + e] = __uint_as_float(q.v[i][e]);
-      amax = fmaxf(amax, fabsf(xs[4 * i + e]));
-    }
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(q.v[i]));
   amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-  if (tid < nhalf)
-    ops::write_ternary_half(ops_lds, ops::ternary_bsc_off(cols), ops::ternary_asc_off(cols), beta, h, xs,
-                            ops::block_exponent(amax));
+  if (tid < nhalf) {
+    const size_t mf = static_cast<size_t>(2 * T);
+    if (kFmt == kB3Tiled)
+      ops::write_b3_half(ops_lds, ops::operand_bsc_off(mf), ops::operand_asc_off(mf), beta, h, q.v, ops::block_exponent(amax));
+    else
+      ops::write_ternary_half(ops_lds, ops::operand_bsc_off(mf), ops::operand_asc_off(mf), beta, h, q.v,
+                              ops::block_exponent(amax));
+  }
 }
 
 constexpr size_t kLdsBudget = 160 * 1024;
 constexpr int kSlotBytes = 64;         // 16 float row sums of one (block, chunk)
 constexpr size_t kSlotBudget = 64 * 1024;
+constexpr size_t kSlotMin = 16 * 1024;
 
 // Position of a wave in its sequence of tiles: batch b, block j of the
 // batch, tile t of the wave's chunk [t0, t1).  b == nbatch: done.
@@ -134,7 +163,15 @@ __device__ __forceinline__ float lane_row_scale(const float* scale, long blk, lo
   return out;
 }
 
-template <bool kTiled>
+// LDS: the operand region (rounded to 1 KiB), the base-3 nibble table
+// (1 KiB, base-3 only), then the two slot buffers.
+__host__ __device__ constexpr size_t fmt_region(int fmt, int64_t cols) {
+  return (ops::operand_region_bytes(fmt == kB3Tiled ? ops::b3_mfmas(cols) : ops::ternary_mfmas(cols)) + 1023) / 1024 *
+             1024 +
+         (fmt == kB3Tiled ? 1024 : 0);
+}
+
+template <int kFmt>
 __global__ __launch_bounds__(kThreads) void t2_mfma_gemv_kernel(const unsigned char* __restrict__ w,
                                                                  const float* __restrict__ scale, int rows, int cols,
                                                                  const float* __restrict__ x, float* __restrict__ y,
@@ -142,12 +179,16 @@ __global__ __launch_bounds__(kThreads) void t2_mfma_gemv_kernel(const unsigned c
   extern __shared__ __align__(16) unsigned char smem[];
   const unsigned lane = threadIdx.x & 63u, n = lane & 15u, g = lane >> 4;
   const int wave = uni(static_cast<int>(threadIdx.x >> 6));
-  const int T = (cols + 255) >> 8;
-  const int row_bytes = cols >> 2;
-  const int region = static_cast<int>((ops::ternary_region_bytes(cols) + 1023) / 1024 * 1024);
+  constexpr bool kTiled = kFmt != kT2Rows;
+  const int T = fmt_windows(kFmt, cols);
+  constexpr int kTileBytes = kFmt == kB3Tiled ? ops::kB3TileBytes : 1024;
+  constexpr int kLaneBytes = kTileBytes / 64;
+  const int row_bytes = cols >> 2;  // T2 row-major only
+  const int region = static_cast<int>(fmt_region(kFmt, cols));
   unsigned char* slots = smem + region;
+  const unsigned* lut = reinterpret_cast<const unsigned*>(smem + region - 1024);  // base-3 only
   const int slot_buf = nbb * kw * kSlotBytes;  // one of two batch buffers
-  const int bsc_off = static_cast<int>(ops::ternary_bsc_off(cols)), asc_off = static_cast<int>(ops::ternary_asc_off(cols));
+  const int bsc_off = static_cast<int>(ops::operand_bsc_off(2 * T)), asc_off = static_cast<int>(ops::operand_asc_off(2 * T));
   const long nb = (static_cast<long>(rows) + 15) / 16;
   const long bw0 = static_cast<long>(blockIdx.x) * nb / gridDim.x, bw1 = (static_cast<long>(blockIdx.x) + 1) * nb / gridDim.x;
   const int nblk = static_cast<int>(bw1 - bw0);
@@ -176,11 +217,11 @@ __global__ __launch_bounds__(kThreads) void t2_mfma_gemv_kernel(const unsigned c
   // This workgroup's weights as one buffer resource; offsets are relative to
   // its first block.  Rows past the matrix lie past the resource.
   const __amdgpu_buffer_rsrc_t wr =
-      kTiled ? buffer_over(w + static_cast<size_t>(bw0) * T * 1024u, static_cast<unsigned>(nblk) * T * 1024u)
+      kTiled ? buffer_over(w + static_cast<size_t>(bw0) * T * kTileBytes, static_cast<unsigned>(nblk) * T * kTileBytes)
              : buffer_over(w + static_cast<size_t>(bw0) * 16 * row_bytes,
                            static_cast<unsigned>(min(static_cast<long>(rows), bw1 * 16) - bw0 * 16) * row_bytes);
   auto offset = [&](long blk, int t) -> unsigned {
-    if (kTiled) return static_cast<unsigned>((blk * T + t) * 1024 + 16 * lane);
+    if (kTiled) return static_cast<unsigned>((blk * T + t) * kTileBytes + kLaneBytes * lane);
     const int off = 64 * t + 16 * static_cast<int>(g);
     return off < row_bytes ? static_cast<unsigned>((blk * 16 + n) * row_bytes + off) : kOff;
   };
@@ -190,10 +231,17 @@ __global__ __launch_bounds__(kThreads) void t2_mfma_gemv_kernel(const unsigned c
   // kG loads per group, all issued (a load past the wave's sequence reads
   // nothing), so the compiler counts them and waits only for the group it
   // multiplies
+  constexpr int kG = group_tiles(kFmt);
   auto load_group = [&](u32x4 (&r)[kG]) {
 #pragma unroll
     for (int j = 0; j < kG; ++j) {
-      r[j] = buffer_load16(wr, ld.b < nbatch ? offset(block_of(ld), ld.t) : kOff);
+      const unsigned off = ld.b < nbatch ? offset(block_of(ld), ld.t) : kOff;
+      if (kFmt == kB3Tiled) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b96(wr, off, 0, kNt);
+        r[j] = u32x4{static_cast<unsigned>(v[0]), static_cast<unsigned>(v[1]), static_cast<unsigned>(v[2]), 0u};
+      } else {
+        r[j] = buffer_load16(wr, off);
+      }
       ++ld.t;  // past the end norm() leaves b == nbatch
       norm(ld);
     }
@@ -207,10 +255,15 @@ __global__ __launch_bounds__(kThreads) void t2_mfma_gemv_kernel(const unsigned c
       lane < 16u && wave < nblk ? static_cast<unsigned>(((bw0 + wave) * 16 + lane) * 4) : kOff, 0, 0));
   u32x4 ra[kG], rb[kG];
   {
-    const XRound q = load_x_round(xr, cols, 0);  // x first: its wait leaves the weight loads in flight
+    XRound q = load_x_round<kFmt>(xr, cols, 0);  // x first: its wait leaves the weight loads in flight
     load_group(ra);
-    convert_x_round(q, cols, 0, smem);
-    for (int r0 = kThreads; r0 < T * 16; r0 += kThreads) convert_x_round(load_x_round(xr, cols, r0), cols, r0, smem);
+    if (kFmt == kB3Tiled && threadIdx.x < 256u)
+      const_cast<unsigned*>(lut)[threadIdx.x] = ops::b3_nibbles(threadIdx.x);
+    convert_x_round<kFmt>(q, cols, 0, smem);
+    for (int r0 = kThreads; r0 < T * 16; r0 += kThreads) {
+      XRound qn = load_x_round<kFmt>(xr, cols, r0);
+      convert_x_round<kFmt>(qn, cols, r0, smem);
+    }
     __syncthreads();
   }
 
@@ -241,7 +294,10 @@ __global__ __launch_bounds__(kThreads) void t2_mfma_gemv_kernel(const unsigned c
       if (cs.b < nbatch) {
         const int ct = cs.t;
         v8i a0, a1;
-        ops::ternary_unpack(r[jj], a0, a1);
+        if (kFmt == kB3Tiled)
+          ops::b3_unpack(lut, r[jj][0], r[jj][1], r[jj][2], a0, a1);
+        else
+          ops::ternary_unpack(r[jj], a0, a1);
         const unsigned char* bp = smem + static_cast<size_t>(2 * ct) * ops::kTernaryMfmaBytes + tboff;
         const u32x4 b0l = *reinterpret_cast<const u32x4*>(bp), b0h = *reinterpret_cast<const u32x4*>(bp + 16);
         const u32x4 b1l = *reinterpret_cast<const u32x4*>(bp + ops::kTernaryMfmaBytes);
@@ -293,8 +349,21 @@ __global__ __launch_bounds__(kThreads) void t2_mfma_gemv_kernel(const unsigned c
 
 struct Instance {
   const void* fn;
-  int max_active;  // resident workgroups per CU for the LDS of the last query
-  size_t lds;
+  int fmt;
+  // resident workgroups per CU for the last two LDS footprints queried
+  size_t lds[2];
+  int max_active[2];
+  int occupancy(size_t bytes) {
+    for (int i = 0; i < 2; ++i)
+      if (lds[i] == bytes && max_active[i] > 0) return max_active[i];
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, bytes) != hipSuccess || n < 1) n = 1;
+    lds[1] = lds[0];
+    max_active[1] = max_active[0];
+    lds[0] = bytes;
+    max_active[0] = n;
+    return n;
+  }
 };
 
 int device_cus() {
@@ -309,24 +378,25 @@ int device_cus() {
 
 int launch(Instance& in, const void* w, const float* s, int64_t rows, int64_t cols, const float* x, int32_t batch,
            float* y, void* stream) {
-  const size_t region = (ops::ternary_region_bytes(cols) + 1023) / 1024 * 1024;
-  const int T = static_cast<int>((cols + 255) / 256);
-  // the slot room is fixed, so the LDS footprint (and the occupancy) does
-  // not depend on how blocks are cut
-  const size_t slot_room = kLdsBudget - region < kSlotBudget ? kLdsBudget - region : kSlotBudget;
-  const size_t lds = region + slot_room;
-  if (in.max_active == 0 || in.lds != lds) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, in.fn, kThreads, lds) != hipSuccess || n < 1) n = 1;
-    in.max_active = n;
-    in.lds = lds;
-  }
+  const size_t region = fmt_region(in.fmt, cols);
+  const int T = static_cast<int>(in.fmt == kB3Tiled ? ops::b3_windows(cols) : (cols + 255) / 256);
+  // slots: all the LDS the operand region leaves (capped); or, for a matrix
+  // with at least two blocks per wave at k workgroups per CU, room for k
+  // resident workgroups (more waves to hide the load and LDS latencies)
   const long nb = (rows + 15) / 16;
-  const long cap = static_cast<long>(device_cus()) * in.max_active;
+  size_t slot_room = kLdsBudget - region < kSlotBudget ? kLdsBudget - region : kSlotBudget;
+  for (int k = target_residency(in.fmt); k >= 2; --k) {
+    if (kLdsBudget / k >= region + kSlotMin && nb >= static_cast<long>(k) * device_cus() * 2 * kWaves) {
+      slot_room = kLdsBudget / k - region < slot_room ? kLdsBudget / k - region : slot_room;
+      break;
+    }
+  }
+  const size_t lds = region + slot_room;
+  const long cap = static_cast<long>(device_cus()) * in.occupancy(lds);
   const unsigned grid = static_cast<unsigned>(nb < cap ? nb : cap);
   const long wg_blocks = (nb + grid - 1) / grid;
   // a workgroup's weights are addressed with 32-bit offsets
-  if (wg_blocks * 16 * (cols / 4) >= (1L << 31))
+  if (wg_blocks * T * 1024 >= (1L << 31))
     return fail(PWG_ERR_UNSUPPORTED, "ternary GEMV: %lld rows exceed the per-workgroup addressing", static_cast<long long>(rows));
   // K chunks per block: a wave streams whole blocks when the workgroup has
   // at least two blocks per wave; with fewer, the K range is cut so that
@@ -337,6 +407,7 @@ int launch(Instance& in, const void* w, const float* s, int64_t rows, int64_t co
   // tiles in a full batch: nbb / P blocks of at least T / kw tiles each
   int nbb = static_cast<int>(slot_room / (2 * static_cast<size_t>(kw) * kSlotBytes));
   const int P = kWaves / kw;
+  const int kG = group_tiles(in.fmt);
   const int need = P * ((kG + T / kw - 1) / (T / kw));
   if (nbb < need) return fail(PWG_ERR_UNSUPPORTED, "ternary GEMV: %lld columns leave too little LDS", static_cast<long long>(cols));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -357,15 +428,23 @@ int launch(Instance& in, const void* w, const float* s, int64_t rows, int64_t co
 // Row-major T2 blob; batch > 1 runs one pass per vector.
 int launch_ternary_gemv(const void* w, const float* s, int64_t rows, int64_t cols, const float* x, int32_t batch,
                         float* y, void* stream) {
-  static Instance rowmajor{reinterpret_cast<const void*>(&t2_mfma_gemv_kernel<false>), 0, 0};
+  static Instance rowmajor{reinterpret_cast<const void*>(&t2_mfma_gemv_kernel<kT2Rows>), kT2Rows, {0, 0}, {0, 0}};
   return launch(rowmajor, w, s, rows, cols, x, batch, y, stream);
 }
 
 // Tiled T2 (cols % 256 == 0), batch 1.
 int launch_ternary_gemv_tiled1(const void* w, const float* s, int64_t rows, int64_t cols, const float* x, float* y,
                                void* stream) {
-  static Instance tiled{reinterpret_cast<const void*>(&t2_mfma_gemv_kernel<true>), 0, 0};
+  static Instance tiled{reinterpret_cast<const void*>(&t2_mfma_gemv_kernel<kT2Tiled>), kT2Tiled, {0, 0}, {0, 0}};
   return launch(tiled, w, s, rows, cols, x, 1, y, stream);
+}
+
+// Base-3 weights in their device arrangement; batch > 1 runs one pass per
+// vector.
+int launch_ternary_gemv_b3(const void* w, const float* s, int64_t rows, int64_t cols, const float* x, int32_t batch,
+                           float* y, void* stream) {
+  static Instance b3{reinterpret_cast<const void*>(&t2_mfma_gemv_kernel<kB3Tiled>), kB3Tiled, {0, 0}, {0, 0}};
+  return launch(b3, w, s, rows, cols, x, batch, y, stream);
 }
 
 }  // namespace pwg

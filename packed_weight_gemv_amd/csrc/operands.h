@@ -55,12 +55,29 @@ constexpr int kSectionMfmas = 4;        // int8 instructions per exponent sectio
 // one per lane: byte m % 4 for instruction m), then the A scale dwords (per
 // group of 4 instructions, one per lane group).
 __host__ __device__ constexpr size_t ternary_mfmas(int64_t cols) { return static_cast<size_t>((cols + 255) / 256) * 2; }
-__host__ __device__ constexpr size_t ternary_quads(int64_t cols) { return (ternary_mfmas(cols) + 3) / 4; }
-__host__ __device__ constexpr size_t ternary_bsc_off(int64_t cols) { return ternary_mfmas(cols) * kTernaryMfmaBytes; }
-__host__ __device__ constexpr size_t ternary_asc_off(int64_t cols) { return ternary_bsc_off(cols) + ternary_quads(cols) * 256; }
-__host__ __device__ constexpr size_t ternary_region_bytes(int64_t cols) {
-  return (ternary_asc_off(cols) + ternary_quads(cols) * 16 + 15) / 16 * 16;
+// The same layout for any instruction count (both weight formats).
+__host__ __device__ constexpr size_t operand_quads(size_t mfmas) { return (mfmas + 3) / 4; }
+__host__ __device__ constexpr size_t operand_bsc_off(size_t mfmas) { return mfmas * kTernaryMfmaBytes; }
+__host__ __device__ constexpr size_t operand_asc_off(size_t mfmas) { return operand_bsc_off(mfmas) + operand_quads(mfmas) * 256; }
+__host__ __device__ constexpr size_t operand_region_bytes(size_t mfmas) {
+  return (operand_asc_off(mfmas) + operand_quads(mfmas) * 16 + 15) / 16 * 16;
 }
+__host__ __device__ constexpr size_t ternary_quads(int64_t cols) { return operand_quads(ternary_mfmas(cols)); }
+__host__ __device__ constexpr size_t ternary_bsc_off(int64_t cols) { return operand_bsc_off(ternary_mfmas(cols)); }
+__host__ __device__ constexpr size_t ternary_asc_off(int64_t cols) { return operand_asc_off(ternary_mfmas(cols)); }
+__host__ __device__ constexpr size_t ternary_region_bytes(int64_t cols) { return operand_region_bytes(ternary_mfmas(cols)); }
+
+// Base-3 weights (five per byte, base-3 digits w + 1, first weight least
+// significant), arranged in 30-weight groups of 6 bytes, 8 groups to a
+// 768-byte tile window: lane (i, g) of window t holds group 8 t + g (the A
+// operand of instruction 2 t, lane group g) and group 8 t + 4 + g
+// (instruction 2 t + 1).  A lane group's 32 K values are the group's 30
+// weights in order and two zeros.
+constexpr int kB3GroupWeights = 30;
+constexpr int kB3TileBytes = 768;
+__host__ __device__ constexpr int64_t b3_row_bytes(int64_t cols) { return (cols + 4) / 5; }
+__host__ __device__ constexpr int64_t b3_windows(int64_t cols) { return ((b3_row_bytes(cols) + 5) / 6 + 7) / 8; }
+__host__ __device__ constexpr size_t b3_mfmas(int64_t cols) { return static_cast<size_t>(b3_windows(cols)) * 2; }
 // int8 (h) region: B digits of every instruction, then one int32 exponent per section.
 __host__ __device__ constexpr size_t int8_exp_off(int64_t hidden) { return static_cast<size_t>(hidden / 64) * kInt8MfmaBytes; }
 __host__ __device__ constexpr size_t int8_region_bytes(int64_t hidden) {
@@ -135,6 +152,29 @@ __device__ __forceinline__ int block_exponent(float amax) {
   return amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) : 0;
 }
 
+// Writes 16 values in K order (r[j] multiplies K value 16 h + j of A lane
+// group ga of instruction m; e = the exponent of that lane group's whole
+// 32-value block) into the operand region `b` (any address space, aligned to
+// 16): B lane group 2 (ga % 2) + h at byte 16 (ga / 2).  Half 0 also writes
+// the block's scale bytes (columns >= kSplits: 0, i.e. 2^-127).  r is
+// consumed.
+__device__ __forceinline__ void write_operand_half(unsigned char* b, size_t bsc_off, size_t asc_off, int m, int ga,
+                                                   int h, float (&r)[16], int e) {
+  unsigned q[kSplits][4];
+  fp8_splits16(r, e, q);
+  const unsigned g = 2u * static_cast<unsigned>(ga & 1) + static_cast<unsigned>(h);
+  unsigned char* base = b + static_cast<size_t>(m) * kTernaryMfmaBytes + 16 * (ga >> 1);
+#pragma unroll
+  for (int s = 0; s < kSplits; ++s)
+    *reinterpret_cast<uint4*>(base + ternary_b_entry(static_cast<unsigned>(s), g)) = make_uint4(q[s][0], q[s][1], q[s][2], q[s][3]);
+  if (h == 0) {
+    unsigned char* sb = b + bsc_off + static_cast<size_t>(m >> 2) * 256 + (m & 3);
+#pragma unroll
+    for (int n = 0; n < 16; ++n) sb[4 * (16 * ga + n)] = n < kSplits ? static_cast<unsigned char>(split_b_scale(e, n)) : 0;
+    b[asc_off + static_cast<size_t>(m >> 2) * 16 + 4 * ga + (m & 3)] = static_cast<unsigned char>(split_a_scale(e));
+  }
+}
+
 // Converts half h of 32-value block `beta` of a ternary input (values at
 // xs[0..15] = x[32 beta + 16 h .. + 15], absent values zero; e = the whole
 // block's exponent) into the operand region `b` (any address space, aligned
@@ -147,20 +187,15 @@ __device__ __forceinline__ void write_ternary_half(unsigned char* b, size_t bsc_
   float r[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) r[j] = xs[lambda16(j)];
-  unsigned q[kSplits][4];
-  fp8_splits16(r, e, q);
-  const int m = 2 * (beta >> 3) + (beta & 1), ga = (beta & 7) >> 1;
-  const unsigned g = 2u * static_cast<unsigned>(ga & 1) + static_cast<unsigned>(h);
-  unsigned char* base = b + static_cast<size_t>(m) * kTernaryMfmaBytes + 16 * (ga >> 1);
-#pragma unroll
-  for (int s = 0; s < kSplits; ++s)
-    *reinterpret_cast<uint4*>(base + ternary_b_entry(static_cast<unsigned>(s), g)) = make_uint4(q[s][0], q[s][1], q[s][2], q[s][3]);
-  if (h == 0) {
-    unsigned char* sb = b + bsc_off + static_cast<size_t>(m >> 2) * 256 + (m & 3);
-#pragma unroll
-    for (int n = 0; n < 16; ++n) sb[4 * (16 * ga + n)] = n < kSplits ? static_cast<unsigned char>(split_b_scale(e, n)) : 0;
-    b[asc_off + static_cast<size_t>(m >> 2) * 16 + 4 * ga + (m & 3)] = static_cast<unsigned char>(split_a_scale(e));
-  }
+  write_operand_half(b, bsc_off, asc_off, 2 * (beta >> 3) + (beta & 1), (beta & 7) >> 1, h, r, e);
+}
+
+// Converts half h of base-3 group q (xs[i] = x[30 q + 16 h + i] for
+// 16 h + i < 30, else zero; e = the group's exponent): the group is A lane
+// group q % 4 of instruction 2 (q / 8) + (q / 4) % 2.
+__device__ __forceinline__ void write_b3_half(unsigned char* b, size_t bsc_off, size_t asc_off, int q, int h,
+                                              float (&xs)[16], int e) {
+  write_operand_half(b, bsc_off, asc_off, 2 * (q >> 3) + ((q >> 2) & 1), q & 3, h, xs, e);
 }
 
 // Balanced base-256 digits of X = rint(h * 2^(46 - e)) for four values:
@@ -194,6 +229,33 @@ __device__ __forceinline__ void ternary_unpack(const u32x4_t v, v8i& a0, v8i& a1
            static_cast<int>((v.y << 2) & kMask), 0, 0, 0, 0};
   a1 = v8i{static_cast<int>(v.z & kMask), static_cast<int>((v.z << 2) & kMask), static_cast<int>(v.w & kMask),
            static_cast<int>((v.w << 2) & kMask), 0, 0, 0, 0};
+}
+
+// FP4 nibbles of one base-3 byte: weight i (digit d_i of the byte) at bits
+// 4 i .. 4 i + 3 as +2 (0b0100, w = +1), -2 (0b1100, w = -1) or 0; the
+// bytes 243..255 (never written by the packer) decode to zero weights.
+__host__ __device__ constexpr unsigned b3_nibbles(unsigned byte) {
+  unsigned out = 0, v = byte;
+  for (int i = 0; i < 5; ++i) {
+    const unsigned d = v % 3;
+    v /= 3;
+    out |= (d == 2 ? 0x4u : d == 0 ? 0xCu : 0u) << (4 * i);
+  }
+  return byte < 243 ? out : 0u;
+}
+
+// A operands of one base-3 lane slice (12 bytes: group g, then group g + 4
+// of the window) through the 256-entry nibble table `lut` in LDS: each
+// group's six 20-bit table entries fill nibbles 0..29 of four dwords.
+__device__ __forceinline__ void b3_group(const unsigned* lut, unsigned b0, unsigned b1, unsigned b2, unsigned b3,
+                                         unsigned b4, unsigned b5, v8i& a) {
+  const unsigned l0 = lut[b0], l1 = lut[b1], l2 = lut[b2], l3 = lut[b3], l4 = lut[b4], l5 = lut[b5];
+  a = v8i{static_cast<int>(l0 | (l1 << 20)), static_cast<int>((l1 >> 12) | (l2 << 8) | (l3 << 28)),
+          static_cast<int>((l3 >> 4) | (l4 << 16)), static_cast<int>((l4 >> 16) | (l5 << 4)), 0, 0, 0, 0};
+}
+__device__ __forceinline__ void b3_unpack(const unsigned* lut, unsigned v0, unsigned v1, unsigned v2, v8i& a0, v8i& a1) {
+  b3_group(lut, v0 & 255u, (v0 >> 8) & 255u, (v0 >> 16) & 255u, v0 >> 24, v1 & 255u, (v1 >> 8) & 255u, a0);
+  b3_group(lut, (v1 >> 16) & 255u, v1 >> 24, v2 & 255u, (v2 >> 8) & 255u, (v2 >> 16) & 255u, v2 >> 24, a1);
 }
 
 // Sum over the 16 lanes of a DPP row (one lane group: the columns of one

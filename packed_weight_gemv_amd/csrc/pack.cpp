@@ -8,9 +8,13 @@
 // 8+2b, 9+2b in its high nibble, two bits each, lower index in lower bits;
 // the code is w in 2-bit two's complement.
 //
-// The nibble interleave exists for the GEMV kernel: masking a word with
-// 0xCCCCCCCC (and, after a 2-bit left shift, again) yields eight signed 4-bit
-// lanes holding 4*w, which feed v_dot8_i32_i4 directly.
+// The nibble interleave exists for the GEMV kernels: masking a word with
+// 0xCCCCCCCC (and, after a 2-bit left shift, again) leaves eight 4-bit lanes
+// holding 0b0100 / 0b1100 / 0 for w = +1 / -1 / 0, the FP4 (e2m1) values
+// +2 / -2 / 0 that the matrix-core instructions take as their A operand.
+//
+// Also here: the base-3 format (five weights per byte), packed and unpacked
+// on the host; its device arrangement is tile.hip's.
 #include <algorithm>
 #include <cstring>
 #include <thread>
@@ -90,6 +94,48 @@ int64_t parallel_rows(int64_t rows, int64_t cols, F&& fn) {
 
 bool valid_shape(int64_t rows, int64_t cols) { return rows >= 1 && cols >= 64 && cols % 64 == 0; }
 
+// Base-3: row r is ceil(cols / 5) bytes; byte m holds weights 5 m + i as
+// digits w + 1 (first weight least significant); padding weights are 0.
+int64_t b3_row(int64_t cols) { return (cols + 4) / 5; }
+bool b3_valid_shape(int64_t rows, int64_t cols) { return rows >= 1 && cols >= 1 && cols <= PWG_MAX_COLS; }
+
+int64_t pack_rows_b3(const int8_t* w, int64_t cols, int64_t r0, int64_t r1, uint8_t* out) {
+  const int64_t B = b3_row(cols);
+  for (int64_t r = r0; r < r1; ++r) {
+    const int8_t* row = w + r * cols;
+    uint8_t* dst = out + r * B;
+    for (int64_t m = 0; m < B; ++m) {
+      unsigned code = 0, place = 1;
+      for (int i = 0; i < 5; ++i, place *= 3) {
+        const int64_t k = 5 * m + i;
+        const int v = k < cols ? row[k] : 0;
+        if (v < -1 || v > 1) return r * cols + k;
+        code += static_cast<unsigned>(v + 1) * place;
+      }
+      dst[m] = static_cast<uint8_t>(code);
+    }
+  }
+  return -1;
+}
+
+// Returns the flat index (row * B + byte) of the first invalid byte or -1.
+int64_t unpack_rows_b3(const uint8_t* in, int64_t cols, int64_t r0, int64_t r1, int8_t* w) {
+  const int64_t B = b3_row(cols);
+  for (int64_t r = r0; r < r1; ++r) {
+    const uint8_t* src = in + r * B;
+    int8_t* row = w + r * cols;
+    for (int64_t m = 0; m < B; ++m) {
+      unsigned code = src[m];
+      if (code > 242) return r * B + m;
+      for (int i = 0; i < 5; ++i, code /= 3) {
+        const int64_t k = 5 * m + i;
+        if (k < cols) row[k] = static_cast<int8_t>(static_cast<int>(code % 3) - 1);
+      }
+    }
+  }
+  return -1;
+}
+
 }  // namespace
 
 extern "C" size_t pwg_packed_size(int64_t rows, int64_t cols) {
@@ -130,5 +176,49 @@ extern "C" int pwg_unpack_weights(const void* packed_host, int64_t rows, int64_t
   if (bad >= 0)
     return fail(PWG_ERR_VALUE, "pwg_unpack_weights: invalid code 0b10 at (row %lld, col %lld)",
                 (long long)(bad / cols), (long long)(bad % cols));
+  return PWG_OK;
+}
+
+extern "C" size_t pwg_b3_packed_size(int64_t rows, int64_t cols) {
+  if (!b3_valid_shape(rows, cols)) return 0;
+  return static_cast<size_t>(rows) * static_cast<size_t>(b3_row(cols));
+}
+
+extern "C" int pwg_pack_weights_b3(const int8_t* w_host, int64_t rows, int64_t cols, void* out_host,
+                                   size_t out_capacity, size_t* out_bytes) {
+  using pwg::fail;
+  const char* fn = "pwg_pack_weights_b3";
+  if (!w_host || !out_host) return fail(PWG_ERR_ARG, "%s: null pointer", fn);
+  if (!b3_valid_shape(rows, cols))
+    return fail(PWG_ERR_ARG, "%s: need rows >= 1 and cols in [1, %d] (got %lld x %lld)", fn, PWG_MAX_COLS,
+                (long long)rows, (long long)cols);
+  const size_t need = pwg_b3_packed_size(rows, cols);
+  if (out_capacity < need) return fail(PWG_ERR_SIZE, "%s: output capacity %zu < %zu bytes", fn, out_capacity, need);
+  uint8_t* out = static_cast<uint8_t*>(out_host);
+  const int64_t bad = parallel_rows(rows, cols, [&](int64_t r0, int64_t r1) {
+    return pack_rows_b3(w_host, cols, r0, r1, out);
+  });
+  if (bad >= 0)
+    return fail(PWG_ERR_VALUE, "%s: value %d at (row %lld, col %lld) is not in {-1, 0, 1}", fn, (int)w_host[bad],
+                (long long)(bad / cols), (long long)(bad % cols));
+  if (out_bytes) *out_bytes = need;
+  return PWG_OK;
+}
+
+extern "C" int pwg_unpack_weights_b3(const void* packed_host, int64_t rows, int64_t cols, int8_t* w_out_host) {
+  using pwg::fail;
+  const char* fn = "pwg_unpack_weights_b3";
+  if (!packed_host || !w_out_host) return fail(PWG_ERR_ARG, "%s: null pointer", fn);
+  if (!b3_valid_shape(rows, cols))
+    return fail(PWG_ERR_ARG, "%s: need rows >= 1 and cols in [1, %d] (got %lld x %lld)", fn, PWG_MAX_COLS,
+                (long long)rows, (long long)cols);
+  const uint8_t* in = static_cast<const uint8_t*>(packed_host);
+  const int64_t B = b3_row(cols);
+  const int64_t bad = parallel_rows(rows, cols, [&](int64_t r0, int64_t r1) {
+    return unpack_rows_b3(in, cols, r0, r1, w_out_host);
+  });
+  if (bad >= 0)
+    return fail(PWG_ERR_VALUE, "%s: byte %u at (row %lld, byte %lld) is not a base-3 code (0..242)", fn,
+                (unsigned)in[bad], (long long)(bad / B), (long long)(bad % B));
   return PWG_OK;
 }

@@ -33,6 +33,8 @@ int launch_int8_gemv_argmax(const int8_t* table, const float* s, int64_t rows, i
                             float* logits, void* stream);
 size_t int8_partials(int64_t rows);
 // Batch-1 ternary GEMV on the tiled arrangement (gemv_mfma.hip).
+int launch_ternary_gemv_b3(const void* w, const float* s, int64_t rows, int64_t cols, const float* x, int32_t batch,
+                           float* y, void* stream);
 int launch_ternary_gemv_tiled1(const void* w, const float* s, int64_t rows, int64_t cols, const float* x, float* y,
                                void* stream);
 int launch_argmax_reduce_batch(const unsigned long long* partials, int n, size_t nparts, int32_t batch, int32_t* token,
@@ -97,5 +99,7 @@ int plan_check(const pwg_step_desc* d, const char* fn);
 // 16-row x 64-byte tile arrangement (tile.hip).
 size_t tiled_bytes(int64_t rows, int64_t row_bytes);
 int launch_tile_rows(const void* src, int64_t rows, int64_t row_bytes, void* dst, void* stream);
+size_t b3_tiled_bytes(int64_t rows, int64_t cols);
+int launch_tile_b3(const void* src, int64_t rows, int64_t cols, void* dst, void* stream);
 
 }  // namespace pwg

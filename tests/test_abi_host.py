@@ -448,3 +448,72 @@ def test_verify_accept_errors():
     assert pwg._verify(P[0], P[1], -1, P[2], P[3], None) == ERR_ARG
     assert pwg._verify(None, P[1], 3, P[2], P[3], None) == ERR_ARG
     assert pwg._verify(P[0], MIS, 3, P[2], P[3], None) == ERR_ALIGN
+
+
+# ---------------------------------------------------------------- base-3 format
+def test_b3_sizes():
+    from oracle import base3_format as b3
+    assert pwg.b3_packed_size(4096, 4096) == 4096 * 820
+    assert pwg.b3_packed_size(1, 1) == 1 and pwg.b3_packed_size(2, 12288) == 2 * 2458
+    for bad in ((0, 5), (1, 0), (-1, 5), (1, 16385)):
+        assert pwg.b3_packed_size(*bad) == 0
+        assert pwg.b3_tiled_size(*bad) == 0
+    for rows, cols in ((1, 1), (16, 240), (17, 60), (4096, 4096), (4096, 12288), (33, 1001)):
+        assert pwg.b3_tiled_size(rows, cols) == b3.tiled_nbytes(rows, cols)
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (3, 7), (37, 1001), (5, 4100), (2048, 4096), (3, 12288)])
+def test_b3_pack_matches_oracle_encoder_bit_for_bit(shape):
+    from oracle import base3_format as b3
+    rng = np.random.default_rng(shape[0] * 11 + shape[1])
+    w = rng.integers(-1, 2, size=shape, dtype=np.int8)
+    blob = pwg.pack_weights_b3(w)
+    assert blob.size == b3.packed_nbytes(*shape)
+    assert np.array_equal(blob, b3.encode(w))
+    assert np.array_equal(pwg.unpack_weights_b3(blob, *shape), w)
+
+
+def test_b3_pack_hand_fixture(golden_dir):
+    import json
+    for case in json.load(open(os.path.join(golden_dir, "b3_bytes.json")))["cases"]:
+        w = np.array(case["weights"], np.int8)
+        assert pwg.pack_weights_b3(w).tobytes() == bytes.fromhex(case["bytes_hex"]), case["derivation"]
+
+
+def test_b3_pack_and_unpack_errors():
+    w = np.zeros((4, 11), np.int8)
+    w[2, 7] = 2
+    with pytest.raises(pwg.PwgError) as e:
+        pwg.pack_weights_b3(w)
+    assert e.value.code == ERR_VALUE and "row 2" in str(e.value) and "col 7" in str(e.value)
+    out = np.zeros(16, np.uint8)
+    n = C.c_size_t(0)
+    ok = np.zeros((2, 11), np.int8)
+    assert pwg._pack_b3(None, 2, 11, out.ctypes.data, 16, C.byref(n)) == ERR_ARG
+    assert pwg._pack_b3(ok.ctypes.data, 2, 0, out.ctypes.data, 16, C.byref(n)) == ERR_ARG
+    assert pwg._pack_b3(ok.ctypes.data, 2, 11, out.ctypes.data, 5, C.byref(n)) == ERR_SIZE
+    assert pwg._pack_b3(ok.ctypes.data, 2, 11, out.ctypes.data, 6, C.byref(n)) == 0 and n.value == 6
+    blob = pwg.pack_weights_b3(np.zeros((3, 12), np.int8))
+    blob[7] = 243
+    with pytest.raises(pwg.PwgError) as e:
+        pwg.unpack_weights_b3(blob, 3, 12)
+    assert e.value.code == ERR_VALUE and "row 2" in str(e.value) and "byte 1" in str(e.value)
+
+
+def test_b3_tile_and_gemv_argument_errors():
+    t = pwg._tile_b3
+    need = pwg.b3_tiled_size(17, 60)
+    assert t(None, 17, 60, A, need, None) == ERR_ARG
+    assert t(A, 0, 60, A + (1 << 16), need, None) == ERR_ARG
+    assert t(A, 17, 16385, A + (1 << 16), need, None) == ERR_ARG
+    assert t(A + 3, 17, 60, MIS + (1 << 16), need, None) == ERR_ALIGN   # dst alignment; src needs none
+    assert t(A, 17, 60, A + (1 << 16), need - 1, None) == ERR_SIZE
+    assert t(A, 17, 60, A + 16, need, None) == ERR_ARG and "overlap" in pwg.last_error()
+    g = pwg._tgemv_b3
+    assert g(None, A, 8, 60, A, 1, A, None) == ERR_ARG
+    assert g(A, A, 0, 60, A, 1, A, None) == ERR_ARG
+    assert g(A, A, 8, 0, A, 1, A, None) == ERR_ARG
+    assert g(A, A, 8, 16385, A, 1, A, None) == ERR_ARG
+    assert g(A, A, 8, 60, A, 3, A, None) == ERR_ARG and "batch" in pwg.last_error()
+    assert g(A, A, 8, 60, MIS, 1, A, None) == ERR_ALIGN
+    assert g(A, A, 8, 60, A, 1, None, None) == ERR_ARG
