@@ -3,8 +3,10 @@
 One step = embedding row of the previous token, 36 layers x 4 ternary levels
 (q|k|v 6144x4096, o 4096x4096, gate|up 24576x4096, down 4096x12288) in
 decoder order, the int8 output projection (151,936 x 4,096) and the greedy
-argmax.  The step is captured once into a HIP graph and replayed; inputs are
-resident in HBM before the timed region starts.
+argmax.  Steps are captured into HIP graphs (by default four consecutive
+steps per graph, each step's token feeding the next step's embedding row on
+the device) and replayed; inputs are resident in HBM before the timed region
+starts.
 
 Order of work (the release-gate policy of the page "The Neutrino Engine",
 sections "One changed token fails the release" and "The engine also runs
@@ -16,10 +18,10 @@ is done in interleaved rounds):
   3. the timed schedule (by default the stream schedule, which computes the
      step over its fixed per-level inputs with no waits between levels) in
      one HIP graph: untimed replays for --prewarm seconds, --warmup untimed
-     replays, exactly --steps timed replays (HIP events on the replay
-     stream), then --rounds more rounds of --steps for the median and
-     p10 / p90; the same step without a graph (the roofline time) and four
-     steps per graph;
+     steps, exactly --steps timed steps (HIP events on the replay stream;
+     graphs of --steps-per-graph chained steps), then --rounds more rounds
+     of --steps for the median and p10 / p90; the same step with one step
+     per graph and without a graph;
   4. the levels schedule (one kernel per level, in decoder order, as a
      chained step needs), a null graph with as many empty kernels, and the
      chained step, to split dependency and launch overhead from DRAM time;
@@ -63,7 +65,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle's timed sample")
     p.add_argument("--prewarm", type=float, default=0.3,
                    help="seconds of untimed graph replays before the counted warm-up (steady clocks)")
-    p.add_argument("--rounds", type=int, default=15, help="extra timing rounds of --steps replays (median, p10, p90)")
+    p.add_argument("--rounds", type=int, default=15, help="extra timing rounds of --steps steps (median, p10, p90)")
+    p.add_argument("--steps-per-graph", type=int, default=4,
+                   help="consecutive decode steps captured in one graph for the timed replays (each step's token "
+                        "feeds the next step's embedding row on the device)")
     p.add_argument("--no-units", action="store_true", help="skip configurations 1-3 as standalone units")
     p.add_argument("--counters", action="store_true",
                    help="counter-collection run: 3 eager steps of the timed schedule plus a 1 GiB device copy "
@@ -133,6 +138,32 @@ def time_rounds(graph, stream, steps, rounds):
             e0.record(stream)
             for _ in range(steps):
                 graph.replay()
+            e1.record(stream)
+            e1.synchronize()
+            out.append(e0.elapsed_time(e1) / steps)
+    return out
+
+
+def time_steps(graph_s, graph_1, s, stream, steps, warmup, rounds=1):
+    """ms per step over exactly `steps` steps: steps // s replays of the
+    s-step graph and steps % s replays of the one-step graph, after `warmup`
+    untimed steps done the same way; `rounds` timed rounds (HIP events on the
+    replay stream, one pair per round)."""
+    import torch
+
+    def run(n):
+        for _ in range(n // s):
+            graph_s.replay()
+        for _ in range(n % s):
+            graph_1.replay()
+    with torch.cuda.stream(stream):
+        run(warmup)
+        stream.synchronize()
+        out = []
+        for _ in range(rounds):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run(steps)
             e1.record(stream)
             e1.synchronize()
             out.append(e0.elapsed_time(e1) / steps)
@@ -814,26 +845,32 @@ def main():
     par = parity(wl, ref, token1)
     log(f"parity ok: {par}")
 
-    # 3. timed graph replays: a time-based pre-warm (clocks settle whatever
-    #    --warmup says), the --warmup untimed replays, then exactly --steps
-    #    timed replays; then repeated rounds of --steps replays for the spread
+    # 3. timed graph replays.  A graph holds S = --steps-per-graph consecutive
+    #    steps (each step's token feeds the next step's embedding row on the
+    #    device, so the S steps are a decode loop; one graph launch per S
+    #    steps).  A time-based pre-warm (clocks settle whatever --warmup
+    #    says), --warmup untimed steps, then exactly --steps timed steps
+    #    (steps // S replays of the S-step graph, steps % S of the one-step
+    #    graph); then repeated rounds of --steps steps for the spread.  The
+    #    one-step graph (a graph launch per step) and launches without a
+    #    graph are timed too.
+    S = max(1, args.steps_per_graph)
     graph = capture(step_fn, stream)
-    n_pre = prewarm(graph, stream, args.prewarm)
-    ms = time_graph(graph, stream, args.steps, args.warmup)
-    rounds = time_rounds(graph, stream, args.steps, args.rounds)
+    graph_s = capture(lambda: [step_fn() for _ in range(S)], stream) if S > 1 else graph
+    n_pre = prewarm(graph_s, stream, args.prewarm)
+    ms = time_steps(graph_s, graph, S, stream, args.steps, args.warmup)[0]
+    rounds = time_steps(graph_s, graph, S, stream, args.steps, 0, args.rounds)
     pwg.step_status(wl.desc, stream=stream)
-    log(f"{args.schedule}: {ms * 1e3:.1f} us/step (after {n_pre} pre-warm replays); over {args.rounds} more rounds "
-        f"of {args.steps}: {spread(rounds)}")
+    log(f"{args.schedule}: {ms * 1e3:.1f} us/step, {S} steps per graph (after {n_pre} pre-warm replays); over "
+        f"{args.rounds} more rounds of {args.steps}: {spread(rounds)}")
+    prewarm(graph, stream, 0.1)
+    ms1 = time_graph(graph, stream, args.steps, args.warmup)
+    pwg.step_status(wl.desc, stream=stream)
+    log(f"{args.schedule}, one step per graph: {ms1 * 1e3:.1f} us/step")
     ms_direct = time_direct(step_fn, stream, args.steps, args.warmup)
     pwg.step_status(wl.desc, stream=stream)
     log(f"{args.schedule} without a graph: {ms_direct * 1e3:.1f} us/step")
-    # four consecutive steps in one graph (each step's token feeds the next
-    # step's embedding row): the per-replay launch cost spread over four steps
-    graph4 = capture(lambda: [step_fn() for _ in range(4)], stream)
-    ms4 = time_graph(graph4, stream, max(1, args.steps // 4), max(1, args.warmup // 4)) / 4
-    del graph4
-    pwg.step_status(wl.desc, stream=stream)
-    log(f"{args.schedule}, four steps per graph: {ms4 * 1e3:.1f} us/step")
+    del graph_s
     kernels_per_step = {pwg.SCHEDULE_STREAM: 2}.get(schedule, len(wl.desc.levels) + 3)
 
     extra = {}
@@ -912,27 +949,26 @@ def main():
         "config": {
             "workload": (f"8B-shape batch-1 decode step: embedding row + {args.layers} layers x (q|k|v 6144x4096, "
                          "o 4096x4096, gate|up 24576x4096, down 4096x12288) ternary T2 + int8 output projection "
-                         "151936x4096 + greedy argmax, one HIP graph per step"),
+                         f"151936x4096 + greedy argmax; HIP graphs of {S} chained steps"),
             "schedule": args.schedule,
             "kernels_per_step": kernels_per_step,
             "algorithmic_bytes_per_step": bytes_,
         },
         "parity": par,
-        "timing": {"prewarm_replays": n_pre, "prewarm_s": args.prewarm, "warmup_replays": args.warmup,
-                   "timed_replays": args.steps, "spread_over_rounds": spread(rounds)},
+        "timing": {"steps_per_graph": S, "prewarm_replays": n_pre, "prewarm_s": args.prewarm,
+                   "warmup_steps": args.warmup, "timed_steps": args.steps, "spread_over_rounds": spread(rounds)},
         "packing": packing_report(wl),
     }
     result.update(extra)
 
+    result["us_per_step_one_step_per_graph"] = ms1 * 1e3
     result["us_per_step_without_graph"] = ms_direct * 1e3
-    result["us_per_step_four_steps_per_graph"] = ms4 * 1e3
-    result["graph_replay_overhead_us"] = (ms - ms_direct) * 1e3
+    result["graph_launch_us_per_replay"] = (ms1 - ms) * 1e3 * S / max(1, S - 1) if S > 1 else None
 
     # roofline of the dominant kernel: the step kernel moves every
-    # algorithmic byte of the step; its time is taken from back-to-back
-    # launches without a graph, measured with HIP events on the launch
-    # stream (for the stream schedule that includes the input-conversion
-    # kernel before it, about 7 us)
+    # algorithmic byte of the step; its time is the per-step time of the
+    # S-step graph (HIP events on the replay stream), i.e. the step kernel
+    # and its input-conversion kernel (about 7 us) back to back
     if schedule == pwg.SCHEDULE_STREAM:
         traffic = None
         tfile = os.path.join(ROOT, "profiles", "step_kernel_traffic.json")
@@ -942,10 +978,10 @@ def main():
                     and t.get("schedule") == args.schedule):
                 traffic = t.get("hbm_bytes_per_launch")
         kname = "stream_step_kernel<8> (whole step; timed with its input-conversion kernel)"
-        kernel_bps = step_bytes / (ms_direct * 1e-3)
+        kernel_bps = step_bytes / (ms * 1e-3)
         result["roofline"] = {"bound": "hbm", "achieved": kernel_bps / 1e9, "peak": PEAK_HBM_BPS / 1e9,
                               "unit": "GB/s", "frac": kernel_bps / PEAK_HBM_BPS, "traffic": traffic,
-                              "kernel": kname, "per_launch_bytes": step_bytes, "avg_launch_us": ms_direct * 1e3}
+                              "kernel": kname, "per_launch_bytes": step_bytes, "avg_launch_us": ms * 1e3}
     result["kernel_source_sha"] = kernel_source_sha(args.schedule)
 
     if not args.no_units and pwg.LAYOUT_ROWS in wl.weights:

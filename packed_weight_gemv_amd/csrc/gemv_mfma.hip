@@ -77,26 +77,30 @@ __device__ __forceinline__ int fmt_windows(int fmt, int cols) {
   return fmt == kB3Tiled ? static_cast<int>(ops::b3_windows(cols)) : (cols + 255) >> 8;
 }
 
-// One conversion round of x: thread (beta, h) of round t0 holds half h of
-// 32-value block beta (T2: x[32 beta + 16 h + i]; base-3: group beta,
-// x[30 beta + 16 h + i] for 16 h + i < 30), zeros past cols.
+// One conversion round of x: thread (beta, h, G) of round t0 converts
+// summation group G of half h of 32-value block beta.  T2: it holds the
+// half's 16 values x[32 beta + 16 h + i]; base-3 (block = 30-value group
+// beta): its own 8 values x[30 beta + 16 h + 8 G + i] for 16 h + 8 G + i <
+// 30.  Zeros past cols.
 struct XRound {
   float v[16];
 };
 template <int kFmt>
 __device__ __forceinline__ XRound load_x_round(__amdgpu_buffer_rsrc_t xr, int cols, int t0) {
   const int tid = t0 + static_cast<int>(threadIdx.x);
-  const int beta = tid >> 1, h = tid & 1;
+  const int beta = tid >> 2, h = (tid >> 1) & 1, G = tid & 1;
   XRound q;
   if (kFmt == kB3Tiled) {
-    const int k0 = ops::kB3GroupWeights * beta + 16 * h;
+    const int j0 = 16 * h + 8 * G, k0 = ops::kB3GroupWeights * beta + j0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const bool in = 16 * h + i < ops::kB3GroupWeights && k0 + i < cols;
+    for (int i = 0; i < 8; ++i) {
+      const bool in = j0 + i < ops::kB3GroupWeights && k0 + i < cols;
       q.v[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, in ? 4u * static_cast<unsigned>(k0 + i) : kOff, 0, 0));
     }
+#pragma unroll
+    for (int i = 8; i < 16; ++i) q.v[i] = 0.f;
   } else {
-    const int k0 = 16 * tid;  // = 32 beta + 16 h; cols % 16 == 0: a half is all in or all out
+    const int k0 = 32 * beta + 16 * h;  // cols % 16 == 0: a half is all in or all out
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const u32x4 v = buffer_load16(xr, k0 < cols ? 4u * static_cast<unsigned>(k0 + 4 * i) : kOff);
@@ -108,25 +112,31 @@ __device__ __forceinline__ XRound load_x_round(__amdgpu_buffer_rsrc_t xr, int co
 }
 
 // Converts one round into the LDS operand region (blocks past cols up to the
-// last window are written as zero).  Every thread takes part: the half-block
-// partners exchange their maxima with a lane shuffle.
+// last window are written as zero).  Every thread takes part: the quarters
+// of a block exchange their maxima with lane shuffles.
 template <int kFmt>
 __device__ __forceinline__ void convert_x_round(XRound& q, int cols, int t0, unsigned char* ops_lds) {
   const int T = fmt_windows(kFmt, cols);
-  const int nhalf = T * 16;
+  const int nquarter = T * 32;
   const int tid = t0 + static_cast<int>(threadIdx.x);
-  const int beta = tid >> 1, h = tid & 1;
+  const int beta = tid >> 2, h = (tid >> 1) & 1, G = tid & 1;
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(q.v[i]));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-  if (tid < nhalf) {
+  if (kFmt == kB3Tiled) amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));  // T2 quarters hold their whole half
+  amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+  if (tid < nquarter) {
     const size_t mf = static_cast<size_t>(2 * T);
-    if (kFmt == kB3Tiled)
-      ops::write_b3_half(ops_lds, ops::operand_bsc_off(mf), ops::operand_asc_off(mf), beta, h, q.v, ops::block_exponent(amax));
-    else
-      ops::write_ternary_half(ops_lds, ops::operand_bsc_off(mf), ops::operand_asc_off(mf), beta, h, q.v,
-                              ops::block_exponent(amax));
+    if (kFmt == kB3Tiled) {
+      float r[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) r[i] = q.v[i];
+      ops::write_b3_quarter(ops_lds, ops::operand_bsc_off(mf), ops::operand_asc_off(mf), beta, h, G, r,
+                            ops::block_exponent(amax));
+    } else {
+      ops::write_ternary_quarter(ops_lds, ops::operand_bsc_off(mf), ops::operand_asc_off(mf), beta, h, G, q.v,
+                                 ops::block_exponent(amax));
+    }
   }
 }
 
@@ -260,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void t2_mfma_gemv_kernel(const unsigned c
     if (kFmt == kB3Tiled && threadIdx.x < 256u)
       const_cast<unsigned*>(lut)[threadIdx.x] = ops::b3_nibbles(threadIdx.x);
     convert_x_round<kFmt>(q, cols, 0, smem);
-    for (int r0 = kThreads; r0 < T * 16; r0 += kThreads) {
+    for (int r0 = kThreads; r0 < T * 32; r0 += kThreads) {
       XRound qn = load_x_round<kFmt>(xr, cols, r0);
       convert_x_round<kFmt>(qn, cols, r0, smem);
     }

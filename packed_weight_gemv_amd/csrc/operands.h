@@ -111,29 +111,25 @@ __device__ __forceinline__ unsigned split_a_scale(int e) { return static_cast<un
 
 constexpr int kDeferBits = 8;  // a residual below 2^-8 of its group's largest waits for a later split
 
-// Splits 16 values (r[j] = value 16 h + lambda16(j) of the block, i.e. in
-// operand order: r[0..7] and r[8..15] are the two 8-value summation groups of
-// the instruction) into out[s][d]: bytes 4 d .. 4 d + 3 of piece s, e4m3
-// codes in operand order.  r is consumed (left holding the final residuals).
-__device__ __forceinline__ void fp8_splits16(float (&r)[16], int e, unsigned (&out)[kSplits][4]) {
+// Splits the 8 values of one summation group of the instruction (r[j]: K
+// value j of the group) into out[s][d]: bytes 4 d .. 4 d + 3 of piece s,
+// e4m3 codes in operand order.  r is consumed (left holding the final
+// residuals).
+__device__ __forceinline__ void fp8_splits8(float (&r)[8], int e, unsigned (&out)[kSplits][2]) {
 #pragma unroll
   for (int s = 0; s < kSplits; ++s) {
     const int sc = e - 8 - 4 * s;
-    float thr[2];
+    float m = 0.f;
 #pragma unroll
-    for (int G = 0; G < 2; ++G) {
-      float m = 0.f;
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(r[j]));
+    const float thr = ldexpf(m, -kDeferBits);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(r[8 * G + j]));
-      thr[G] = ldexpf(m, -kDeferBits);
-    }
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int d = 0; d < 2; ++d) {
       float v[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float rv = r[4 * d + q];
-        v[q] = fabsf(rv) >= thr[d >> 1] ? ldexpf(rv, -sc) : 0.f;
+        v[q] = fabsf(rv) >= thr ? ldexpf(rv, -sc) : 0.f;
       }
       unsigned w = static_cast<unsigned>(__builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false));
       w = static_cast<unsigned>(__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], static_cast<int>(w), true));
@@ -144,6 +140,25 @@ __device__ __forceinline__ void fp8_splits16(float (&r)[16], int e, unsigned (&o
       r[4 * d + 2] -= ldexpf(__builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), 2), sc);
       r[4 * d + 3] -= ldexpf(__builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), 3), sc);
     }
+  }
+}
+
+// The same for 16 values (two summation groups, which split independently).
+__device__ __forceinline__ void fp8_splits16(float (&r)[16], int e, unsigned (&out)[kSplits][4]) {
+#pragma unroll
+  for (int G = 0; G < 2; ++G) {
+    float g8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) g8[j] = r[8 * G + j];
+    unsigned o[kSplits][2];
+    fp8_splits8(g8, e, o);
+#pragma unroll
+    for (int s = 0; s < kSplits; ++s) {
+      out[s][2 * G] = o[s][0];
+      out[s][2 * G + 1] = o[s][1];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[8 * G + j] = g8[j];
   }
 }
 
@@ -173,6 +188,54 @@ __device__ __forceinline__ void write_operand_half(unsigned char* b, size_t bsc_
     for (int n = 0; n < 16; ++n) sb[4 * (16 * ga + n)] = n < kSplits ? static_cast<unsigned char>(split_b_scale(e, n)) : 0;
     b[asc_off + static_cast<size_t>(m >> 2) * 16 + 4 * ga + (m & 3)] = static_cast<unsigned char>(split_a_scale(e));
   }
+}
+
+// One summation group of the same: r[j] multiplies K value 16 h + 8 G + j
+// of A lane group ga of instruction m; the 8 bytes of each piece go to byte
+// 16 (ga / 2) + 8 G of B lane group 2 (ga % 2) + h.  Quarter (h, G) = (0, 0)
+// also writes the block's scale bytes.
+__device__ __forceinline__ void write_operand_quarter(unsigned char* b, size_t bsc_off, size_t asc_off, int m, int ga,
+                                                      int h, int G, float (&r)[8], int e) {
+  unsigned q[kSplits][2];
+  fp8_splits8(r, e, q);
+  const unsigned g = 2u * static_cast<unsigned>(ga & 1) + static_cast<unsigned>(h);
+  unsigned char* base = b + static_cast<size_t>(m) * kTernaryMfmaBytes + 16 * (ga >> 1) + 8 * G;
+#pragma unroll
+  for (int s = 0; s < kSplits; ++s)
+    *reinterpret_cast<uint2*>(base + ternary_b_entry(static_cast<unsigned>(s), g)) = make_uint2(q[s][0], q[s][1]);
+  if (h == 0 && G == 0) {
+    unsigned char* sb = b + bsc_off + static_cast<size_t>(m >> 2) * 256 + (m & 3);
+#pragma unroll
+    for (int n = 0; n < 16; ++n) sb[4 * (16 * ga + n)] = n < kSplits ? static_cast<unsigned char>(split_b_scale(e, n)) : 0;
+    b[asc_off + static_cast<size_t>(m >> 2) * 16 + 4 * ga + (m & 3)] = static_cast<unsigned char>(split_a_scale(e));
+  }
+}
+
+// a where the mask bits are set, b elsewhere (v_bfi_b32).  Written as an
+// instruction: a choice between two elements of one array would otherwise be
+// folded into a computed index, which moves the array to scratch memory.
+__device__ __forceinline__ float pick(unsigned mask, float a, float b) {
+  float out;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(out) : "v"(mask), "v"(a), "v"(b));
+  return out;
+}
+
+// Quarter (h, G) of 32-value T2 block beta: xs = the half's 16 values
+// (x[32 beta + 16 h + i]); in K order the group holds xs[lambda16(8 G + j)].
+__device__ __forceinline__ void write_ternary_quarter(unsigned char* b, size_t bsc_off, size_t asc_off, int beta, int h,
+                                                      int G, const float (&xs)[16], int e) {
+  const unsigned first = G ? 0u : ~0u;
+  float r[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = pick(first, xs[lambda16(j)], xs[lambda16(8 + j)]);
+  write_operand_quarter(b, bsc_off, asc_off, 2 * (beta >> 3) + (beta & 1), (beta & 7) >> 1, h, G, r, e);
+}
+
+// Quarter (h, G) of base-3 group q: r[j] = x[30 q + 16 h + 8 G + j] (zero
+// past the group's 30 values or past cols).
+__device__ __forceinline__ void write_b3_quarter(unsigned char* b, size_t bsc_off, size_t asc_off, int q, int h, int G,
+                                                 float (&r)[8], int e) {
+  write_operand_quarter(b, bsc_off, asc_off, 2 * (q >> 3) + ((q >> 2) & 1), q & 3, h, G, r, e);
 }
 
 // Converts half h of 32-value block `beta` of a ternary input (values at

@@ -662,11 +662,11 @@ __global__ __launch_bounds__(kThreads, 1) void stream_step_kernel(const Plan* __
 }
 
 // --------------------------------------------------------------- conversion
-// Ternary level input: thread (beta, h) of level L converts half h of the
-// 32-element block beta (operands.h); the two halves of a block are adjacent
-// lanes and share the block exponent.
+// Ternary level input: thread (beta, h, G) of level L converts summation
+// group G of half h of the 32-element block beta (operands.h); the four
+// quarters of a block are adjacent lanes and share the block exponent.
 __device__ void convert_ternary(const Level& L, int tid, unsigned lane) {
-  const int beta = tid >> 1, h = tid & 1;
+  const int beta = tid >> 2, h = (tid >> 1) & 1, G = tid & 1;
   const bool ok = beta < L.cols / 32;
   float xs[16];
   float amax = 0.f;
@@ -677,9 +677,9 @@ __device__ void convert_ternary(const Level& L, int tid, unsigned lane) {
     xs[4 * q] = v.x; xs[4 * q + 1] = v.y; xs[4 * q + 2] = v.z; xs[4 * q + 3] = v.w;
     amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
   }
-  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));  // the other half of the block
   (void)lane;
-  if (ok) ops::write_ternary_half(L.b_out, L.bsc_off, L.asc_off, beta, h, xs, ops::block_exponent(amax));
+  if (ok) ops::write_ternary_quarter(L.b_out, L.bsc_off, L.asc_off, beta, h, G, xs, ops::block_exponent(amax));
 }
 
 // Vocabulary input h: wave `sec` converts section sec (256 elements); lane
@@ -701,7 +701,7 @@ __device__ void convert_int8(const Level& L, const float* h, int sec, unsigned l
 }
 
 // One-dimensional grid: the workgroups of level i are conv0(i) ..
-// conv0(i + 1) - 1 (ternary: 128 blocks of 32 inputs per workgroup, two
+// conv0(i + 1) - 1 (ternary: 64 blocks of 32 inputs per workgroup, four
 // threads per block; the vocabulary: four 256-value sections of h, one per
 // wave); the plan's table names each workgroup's level.
 __global__ __launch_bounds__(256) void stream_convert_kernel(const Plan* __restrict__ plan,
@@ -731,10 +731,10 @@ struct SLayout {
   size_t plan, partials, arrivals, levels, segs, seg_count, conv_level, park, regions, total;
 };
 
-// Conversion workgroups of level i (the vocabulary: i == n_levels): 2
+// Conversion workgroups of level i (the vocabulary: i == n_levels): 4
 // threads per 32-input ternary block, one wave per 256-value section of h.
 int conv_blocks(const pwg_step_desc* d, int i) {
-  if (i < d->n_levels) return static_cast<int>((d->levels[i].cols / 32 * 2 + 255) / 256);
+  if (i < d->n_levels) return static_cast<int>((d->levels[i].cols / 32 * 4 + 255) / 256);
   return static_cast<int>((d->hidden / 256 + 3) / 4);
 }
 
