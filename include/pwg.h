@@ -540,6 +540,60 @@ int pwg_gqa_decode_attention(const uint16_t* k_cache, const uint16_t* v_cache, c
 int pwg_verify_accept(const int32_t* tokens_in, const int32_t* targets, int32_t n_drafts, int32_t* accepted,
                       int32_t* next_token, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Packed-blob header (page "The Neutrino Engine", sections "The same weights
+ * take four execution paths" and "What ships": every path reads the same
+ * stored values, and a converted pack must match the engine before it is
+ * used).  A 64-byte little-endian header that a loader writes in front of a
+ * packed payload and checks before use: format version, layout, shape, the
+ * payload size and a checksum of the LOGICAL values, FNV-1a 64 (Fowler, Noll,
+ * Vo: h = 14695981039346656037, then h = (h ^ byte) * 1099511628211 mod 2^64)
+ * over W as int8, row-major.  The 2-bit and base-3 packings of one matrix,
+ * stored or arranged for the device, carry the same checksum.  Host
+ * functions; the library's kernels take payloads without headers.
+ * ------------------------------------------------------------------------- */
+#define PWG_BLOB_MAGIC 0x42475750u /* "PWGB" */
+#define PWG_BLOB_VERSION 1
+
+enum {
+  PWG_BLOB_T2 = 1,        /* T2, row-major (pwg_pack_weights); cols % 64 == 0 */
+  PWG_BLOB_T2_TILED = 2,  /* T2 in 16-row x 64-byte tiles (pwg_tile_rows); cols % 256 == 0 */
+  PWG_BLOB_B3 = 3,        /* base-3, stored (pwg_pack_weights_b3) */
+  PWG_BLOB_B3_TILED = 4   /* base-3, device arrangement (pwg_tile_b3) */
+};
+
+typedef struct pwg_blob_header {
+  uint32_t magic;          /* PWG_BLOB_MAGIC */
+  uint16_t version;        /* PWG_BLOB_VERSION */
+  uint16_t layout;         /* PWG_BLOB_* */
+  int64_t rows;            /* >= 1 */
+  int64_t cols;            /* >= 1, <= PWG_MAX_COLS */
+  uint64_t payload_bytes;  /* size of the payload that follows */
+  uint64_t logical_fnv1a;  /* FNV-1a 64 of W (int8, row-major, rows * cols bytes) */
+  uint64_t header_fnv1a;   /* FNV-1a 64 of the 40 bytes above */
+  uint64_t reserved[2];    /* zero */
+} pwg_blob_header;
+
+/* Payload bytes of `layout` for rows x cols; 0 for an invalid combination. */
+size_t pwg_blob_payload_bytes(int32_t layout, int64_t rows, int64_t cols);
+
+/* Fills *out for the logical matrix w_host (host int8 rows x cols, values in
+ * {-1, 0, 1}) in `layout`.  Errors: PWG_ERR_ARG (null, layout / shape),
+ * PWG_ERR_VALUE (a value outside {-1, 0, 1}). */
+int pwg_blob_header_init(int32_t layout, const int8_t* w_host, int64_t rows, int64_t cols, pwg_blob_header* out);
+
+/* Checks a header without reading the payload: magic, version, header
+ * checksum, reserved words, layout and shape, and that its payload size is
+ * the layout's and equals payload_bytes.  Errors: PWG_ERR_ARG (null),
+ * PWG_ERR_VALUE (a malformed header), PWG_ERR_SIZE (payload size). */
+int pwg_blob_header_check(const pwg_blob_header* h, size_t payload_bytes);
+
+/* pwg_blob_header_check, then decodes every weight of the host payload in
+ * its layout and compares the logical checksum.  Errors as the check, plus
+ * PWG_ERR_ARG (null payload) and PWG_ERR_VALUE (an invalid code, or a
+ * payload whose logical values differ from the header's). */
+int pwg_blob_verify(const pwg_blob_header* h, const void* payload_host, size_t payload_bytes);
+
 /* PWG_VERSION of the built library. */
 int pwg_version(void);
 

@@ -20,6 +20,8 @@ specification for the packed-byte decoder/encoder:
 * ``packed_format``   - encoder/decoder of the 2-bit packed ternary format;
 * ``base3_format``    - encoder/decoder and device arrangement of the
                         base-3 format (five weights per byte);
+* ``blob_header``     - the packed-blob header and its FNV-1a checksum of
+                        the logical values;
 * ``accounting``      - byte accounting of the 8B shape and the KV cache.
 
 Parity status of each function is stated in its module.  One part is
@@ -28,4 +30,4 @@ name it but never specify it), so the library's 2-bit and base-3 formats are
 pinned only by their own specifications, hand-derived bytes and round trips,
 not by the pages.
 """
-from . import accounting, attention, base3_format, chain, packed_format, reference, verify  # noqa: F401
+from . import accounting, attention, base3_format, blob_header, chain, packed_format, reference, verify  # noqa: F401

@@ -88,6 +88,12 @@ class _StepDesc(C.Structure):
     ]
 
 
+class BlobHeader(C.Structure):
+    _fields_ = [("magic", C.c_uint32), ("version", C.c_uint16), ("layout", C.c_uint16), ("rows", _i64),
+                ("cols", _i64), ("payload_bytes", C.c_uint64), ("logical_fnv1a", C.c_uint64),
+                ("header_fnv1a", C.c_uint64), ("reserved", C.c_uint64 * 2)]
+
+
 def _sig(name, restype, *argtypes):
     f = getattr(lib, name)
     f.restype = restype
@@ -118,6 +124,10 @@ _unpack_b3 = _sig("pwg_unpack_weights_b3", C.c_int, _vp, _i64, _i64, _vp)
 _b3_tiled_size = _sig("pwg_b3_tiled_size", _sz, _i64, _i64)
 _tile_b3 = _sig("pwg_tile_b3", C.c_int, _vp, _i64, _i64, _vp, _sz, _vp)
 _tgemv_b3 = _sig("pwg_ternary_gemv_b3", C.c_int, _vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp)
+_blob_payload = _sig("pwg_blob_payload_bytes", _sz, _i32, _i64, _i64)
+_blob_init = _sig("pwg_blob_header_init", C.c_int, _i32, _vp, _i64, _i64, C.POINTER(BlobHeader))
+_blob_check = _sig("pwg_blob_header_check", C.c_int, C.POINTER(BlobHeader), _sz)
+_blob_verify = _sig("pwg_blob_verify", C.c_int, C.POINTER(BlobHeader), _vp, _sz)
 _step_ws = _sig("pwg_step_workspace_bytes", _sz, C.POINTER(_StepDesc))
 _step_plan = _sig("pwg_step_plan", C.c_int, C.POINTER(_StepDesc), _vp)
 _step = _sig("pwg_decode_step_weights", C.c_int, C.POINTER(_StepDesc), _vp)
@@ -133,7 +143,8 @@ EXPORTED = ["pwg_packed_size", "pwg_pack_weights", "pwg_unpack_weights", "pwg_te
             "pwg_step_status", "pwg_last_error", "pwg_version", "pwg_attention_workspace_bytes",
             "pwg_gqa_decode_attention", "pwg_verify_accept", "pwg_int8_gemv_argmax_noalloc",
             "pwg_b3_packed_size", "pwg_pack_weights_b3", "pwg_unpack_weights_b3", "pwg_b3_tiled_size",
-            "pwg_tile_b3", "pwg_ternary_gemv_b3"]
+            "pwg_tile_b3", "pwg_ternary_gemv_b3", "pwg_blob_payload_bytes", "pwg_blob_header_init",
+            "pwg_blob_header_check", "pwg_blob_verify"]
 
 
 def last_error() -> str:
@@ -217,6 +228,33 @@ def unpack_weights_b3(blob: np.ndarray, rows: int, cols: int) -> np.ndarray:
         raise ValueError("blob too small")
     _check(_unpack_b3(blob.ctypes.data, rows, cols, out.ctypes.data))
     return out
+
+
+# ---------------------------------------------------------------- packed-blob header
+BLOB_T2, BLOB_T2_TILED, BLOB_B3, BLOB_B3_TILED = 1, 2, 3, 4
+
+
+def blob_payload_bytes(layout: int, rows: int, cols: int) -> int:
+    return _blob_payload(layout, rows, cols)
+
+
+def blob_header(layout: int, w: np.ndarray) -> bytes:
+    """The 64-byte header of the logical matrix w (int8) in `layout`."""
+    w = np.ascontiguousarray(w, dtype=np.int8)
+    h = BlobHeader()
+    _check(_blob_init(layout, w.ctypes.data, w.shape[0], w.shape[1], C.byref(h)))
+    return bytes(h)
+
+
+def blob_verify(header: bytes, payload: np.ndarray, check_only: bool = False):
+    """Checks a header (and, unless check_only, the payload's logical values
+    against it); raises PwgError."""
+    h = BlobHeader.from_buffer_copy(header)
+    payload = np.ascontiguousarray(payload, dtype=np.uint8)
+    if check_only:
+        _check(_blob_check(C.byref(h), payload.nbytes))
+    else:
+        _check(_blob_verify(C.byref(h), payload.ctypes.data, payload.nbytes))
 
 
 # ---------------------------------------------------------------- GPU entry points

@@ -50,6 +50,49 @@ static void pack_round_trips() {
   CHECK(pwg_unpack_weights(nullptr, 1, 64, &one) == PWG_ERR_ARG);
 }
 
+// Base-3 packing and the blob header on exactly sized buffers.
+static void base3_and_header_checks() {
+  std::mt19937 rng(11);
+  const int64_t shapes[][2] = {{1, 1}, {3, 7}, {17, 240}, {5, 1001}, {33, 4096}, {2, 12288}, {3, 16384}};
+  for (const auto& sh : shapes) {
+    const int64_t rows = sh[0], cols = sh[1];
+    std::vector<int8_t> w(static_cast<size_t>(rows * cols));
+    for (auto& v : w) v = static_cast<int8_t>(static_cast<int>(rng() % 3) - 1);
+    const size_t need = pwg_b3_packed_size(rows, cols);
+    CHECK(need == static_cast<size_t>(rows * ((cols + 4) / 5)));
+    std::vector<unsigned char> blob(need);
+    size_t wrote = 0;
+    CHECK(pwg_pack_weights_b3(w.data(), rows, cols, blob.data(), need, &wrote) == PWG_OK && wrote == need);
+    std::vector<int8_t> back(w.size());
+    CHECK(pwg_unpack_weights_b3(blob.data(), rows, cols, back.data()) == PWG_OK);
+    CHECK(std::memcmp(back.data(), w.data(), w.size()) == 0);
+    CHECK(pwg_pack_weights_b3(w.data(), rows, cols, blob.data(), need - 1, nullptr) == PWG_ERR_SIZE);
+    pwg_blob_header h;
+    CHECK(pwg_blob_header_init(PWG_BLOB_B3, w.data(), rows, cols, &h) == PWG_OK);
+    CHECK(pwg_blob_verify(&h, blob.data(), need) == PWG_OK);
+    CHECK(pwg_blob_verify(&h, blob.data(), need - 1) == PWG_ERR_SIZE);
+    blob[need - 1] = 243;  // not a base-3 code
+    CHECK(pwg_unpack_weights_b3(blob.data(), rows, cols, back.data()) == PWG_ERR_VALUE);
+    CHECK(pwg_blob_verify(&h, blob.data(), need) == PWG_ERR_VALUE);
+    if (cols % 64 == 0) {  // the same matrix as T2 carries the same logical checksum
+      std::vector<unsigned char> t2(pwg_packed_size(rows, cols));
+      CHECK(pwg_pack_weights(w.data(), rows, cols, t2.data(), t2.size(), nullptr) == PWG_OK);
+      pwg_blob_header h2;
+      CHECK(pwg_blob_header_init(PWG_BLOB_T2, w.data(), rows, cols, &h2) == PWG_OK);
+      CHECK(h2.logical_fnv1a == h.logical_fnv1a);
+      CHECK(pwg_blob_verify(&h2, t2.data(), t2.size()) == PWG_OK);
+    }
+  }
+  pwg_blob_header h;
+  int8_t one = 1;
+  CHECK(pwg_blob_header_init(PWG_BLOB_T2, &one, 1, 1, &h) == PWG_ERR_ARG);
+  CHECK(pwg_blob_header_init(7, &one, 1, 1, &h) == PWG_ERR_ARG);
+  CHECK(pwg_blob_header_init(PWG_BLOB_B3, &one, 1, 1, &h) == PWG_OK);
+  h.header_fnv1a ^= 1u;
+  CHECK(pwg_blob_header_check(&h, 1) == PWG_ERR_VALUE);
+  CHECK(pwg_blob_header_check(nullptr, 1) == PWG_ERR_ARG);
+}
+
 static uintptr_t slot(int k) { return (uintptr_t{1} << 36) + static_cast<uintptr_t>(k) * (uintptr_t{1} << 24); }
 template <typename T>
 static T* P(int k) { return reinterpret_cast<T*>(slot(k)); }
@@ -115,6 +158,7 @@ static void step_checks() {
 
 int main() {
   pack_round_trips();
+  base3_and_header_checks();
   step_checks();
   std::printf("host checks ok\n");
   return 0;

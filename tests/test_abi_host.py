@@ -517,3 +517,47 @@ def test_b3_tile_and_gemv_argument_errors():
     assert g(A, A, 8, 60, A, 3, A, None) == ERR_ARG and "batch" in pwg.last_error()
     assert g(A, A, 8, 60, MIS, 1, A, None) == ERR_ALIGN
     assert g(A, A, 8, 60, A, 1, None, None) == ERR_ARG
+
+
+# ---------------------------------------------------------------- packed-blob header
+def test_blob_header_matches_the_oracle_and_verifies_every_layout():
+    from oracle import base3_format as b3
+    from oracle import blob_header as bh
+    rng = np.random.default_rng(17)
+    w = rng.integers(-1, 2, size=(37, 512)).astype(np.int8)
+    payloads = {pwg.BLOB_T2: pf.encode(w), pwg.BLOB_T2_TILED: pf.tile16x64(pf.encode(w).reshape(37, 128)),
+                pwg.BLOB_B3: b3.encode(w), pwg.BLOB_B3_TILED: b3.tile(b3.encode(w), 37, 512)}
+    for layout, p in payloads.items():
+        head = pwg.blob_header(layout, w)
+        assert head == bh.make(layout, w)                      # byte for byte, every field
+        assert pwg.blob_payload_bytes(layout, 37, 512) == p.size
+        pwg.blob_verify(head, p)
+        bad = p.copy()
+        bad[p.size // 2] ^= 0x01                               # one code changed
+        with pytest.raises(pwg.PwgError) as e:
+            pwg.blob_verify(head, bad)
+        assert e.value.code == ERR_VALUE
+        with pytest.raises(pwg.PwgError) as e:
+            pwg.blob_verify(head, p[:-1], check_only=True)
+        assert e.value.code == ERR_SIZE
+    # the header names the matrix, not the packing: every layout carries one checksum
+    assert len({bh.parse(pwg.blob_header(l, w))["logical_fnv1a"] for l in payloads}) == 1
+
+
+def test_blob_header_rejects_malformed_headers():
+    w = np.zeros((2, 64), np.int8)
+    head = bytearray(pwg.blob_header(pwg.BLOB_T2, w))
+    p = np.zeros(32, np.uint8)
+    for off, what in ((0, "magic"), (4, "version"), (20, "cols"), (40, "checksum"), (50, "reserved")):
+        h = bytearray(head)
+        h[off] ^= 0x10
+        with pytest.raises(pwg.PwgError) as e:
+            pwg.blob_verify(bytes(h), p, check_only=True)
+        assert e.value.code == ERR_VALUE, what
+    with pytest.raises(pwg.PwgError) as e:
+        pwg.blob_header(pwg.BLOB_T2, np.zeros((2, 60), np.int8))   # T2 needs cols % 64 == 0
+    assert e.value.code == ERR_ARG
+    with pytest.raises(pwg.PwgError) as e:
+        pwg.blob_header(pwg.BLOB_B3, np.full((1, 3), 2, np.int8))
+    assert e.value.code == ERR_VALUE
+    assert pwg.blob_payload_bytes(9, 1, 64) == 0 and pwg.blob_payload_bytes(pwg.BLOB_T2_TILED, 1, 64) == 0

@@ -19,7 +19,8 @@ def test_host_code_under_asan_and_ubsan(tmp_path):
     cmd = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
            "-fno-sanitize-recover=all", "-I" + CSRC,
            os.path.join(ROOT, "tests", "native", "host_sanitize.cpp"),
-           os.path.join(CSRC, "pack.cpp"), os.path.join(CSRC, "errors.cpp"), os.path.join(CSRC, "validate.cpp"),
+           os.path.join(CSRC, "pack.cpp"), os.path.join(CSRC, "blob.cpp"), os.path.join(CSRC, "errors.cpp"),
+           os.path.join(CSRC, "validate.cpp"),
            "-o", str(exe), "-lpthread"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
