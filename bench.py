@@ -875,8 +875,8 @@ def main():
 
     extra = {}
     if not args.no_compare:
-        names = {pwg.SCHEDULE_LEVELS: "levels", pwg.SCHEDULE_STREAM: "stream"}
-        for other in (pwg.SCHEDULE_LEVELS, pwg.SCHEDULE_STREAM):
+        names = {pwg.SCHEDULE_LEVELS: "levels", pwg.SCHEDULE_STREAM: "stream", pwg.SCHEDULE_PERSISTENT: "persistent"}
+        for other in (pwg.SCHEDULE_LEVELS, pwg.SCHEDULE_STREAM, pwg.SCHEDULE_PERSISTENT):
             if other == schedule:
                 continue
             other_fn = run(other)
@@ -899,15 +899,9 @@ def main():
         extra["null_graph_kernels"] = n_null
         # chained step: every level's input formed from earlier outputs
         # (RMSNorm, one-position attention, SwiGLU, residual sums) on the
-        # ordered schedule, the dependency chain the stream step leaves out
-        cs = make_chained(wl, schedule=pwg.SCHEDULE_LEVELS)
-        for sched_c in (pwg.SCHEDULE_LEVELS,):
-            cs.desc.schedule = sched_c
-            cs.desc._c = None
-            need = pwg.step_workspace_bytes(cs.desc)
-            if cs.desc.workspace.numel() < need:
-                cs.desc.workspace = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
-                cs.desc._c = None
+        # ordered schedules, the dependency chain the stream step leaves out
+        for sched_c in (pwg.SCHEDULE_LEVELS, pwg.SCHEDULE_PERSISTENT):
+            cs = make_chained(wl, schedule=sched_c)
             pwg.step_plan(cs.desc, stream=stream)
             chain_fn = lambda: pwg.decode_step_weights(cs.desc, stream=stream)  # noqa: E731
             with torch.cuda.stream(stream):
@@ -923,7 +917,7 @@ def main():
             del g3
             extra[f"chained_{names[sched_c]}_us"] = ms_chain * 1e3
             log(f"chained step, {names[sched_c]} schedule: {ms_chain * 1e3:.1f} us/step")
-        del cs
+            del cs
         run(schedule)  # restore the timed schedule's plan
 
     achieved_bps = step_bytes / (ms * 1e-3)

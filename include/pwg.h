@@ -61,8 +61,14 @@ enum {
 /* Step schedules for pwg_decode_step_weights. */
 enum {
   PWG_SCHEDULE_LEVELS = 0,      /* one kernel per dependency level, in decoder order */
-  PWG_SCHEDULE_PERSISTENT = 1,  /* reserved: not available in this build
-                                   (PWG_ERR_UNSUPPORTED) */
+  PWG_SCHEDULE_PERSISTENT = 1,  /* one resident matrix-core kernel that runs the
+                                   levels in decoder order, separated by device-wide
+                                   barriers; each workgroup's weight tiles of a level
+                                   are loaded before that level's input is ready.
+                                   Honours every dependency (chained inputs allowed).
+                                   Needs PWG_LAYOUT_TILED weights, batch 1, hidden and
+                                   every level's cols a multiple of 256 and at most
+                                   12288; pwg_step_plan before the first call */
   PWG_SCHEDULE_STREAM = 2       /* one matrix-core kernel (after a small input
                                    conversion kernel) without level barriers: the
                                    16-row blocks of all levels and of the vocabulary
@@ -79,7 +85,7 @@ enum {
   PWG_LAYOUT_ROWS = 0,   /* T2 blobs and the int8 output table row-major
                             (schedule LEVELS) */
   PWG_LAYOUT_TILED = 1   /* the same bytes in 16-row x 64-byte tiles, see
-                            pwg_tile_rows (schedule STREAM) */
+                            pwg_tile_rows (schedules STREAM and PERSISTENT) */
 };
 
 /* ---------------------------------------------------------------------------
@@ -384,7 +390,8 @@ int pwg_embed_gather(const int8_t* table, const float* row_scale,
  *                             (src: the stacked gate|up output, gate first).
  * Buffers may not overlap: x, resid_out, src, resid and gamma are distinct
  * (PWG_ERR_ARG where pointers are equal).  Only the ordered schedules
- * (LEVELS) at batch 1 takes such levels (PWG_ERR_UNSUPPORTED otherwise).  Arithmetic is float32: the mean of squares is a float32 sum,
+ * (LEVELS, PERSISTENT) at batch 1 take such levels (PWG_ERR_UNSUPPORTED
+ * otherwise).  Arithmetic is float32: the mean of squares is a float32 sum,
  * the root and the quotient IEEE float32. */
 enum {
   PWG_INPUT_GIVEN = 0,
@@ -423,9 +430,9 @@ typedef struct pwg_level {
  *   embedding gather of *token_in -> levels[0 .. n_levels-1] in order ->
  *   int8 output projection of h + argmax -> *token_out.
  * All pointers except `levels` are device pointers; `levels` is a host
- * array: the levels schedule reads it during each call, the stream schedule
- * and the batched pass read it in pwg_step_plan (their device plan then holds
- * the pointers and shapes).  token_in and token_out may alias (the token then
+ * array: the levels schedule reads it during each call, the stream and
+ * persistent schedules and the batched pass read it in pwg_step_plan (their
+ * device plan then holds the pointers and shapes).  token_in and token_out may alias (the token then
  * feeds the next step on the device).
  *
  * Batched pass (batch = 4, 8 or 16; page section "The 0.6B model does not get
@@ -470,8 +477,9 @@ typedef struct pwg_step_desc {
 size_t pwg_step_workspace_bytes(const pwg_step_desc* desc);
 
 /* Prepare the workspace of a step: validates the description and, for the
- * stream schedule and the batched pass, writes the device-side level table
- * and work split and resets the claim counters and status words.  Synchronous (it waits
+ * stream and persistent schedules and the batched pass, writes the
+ * device-side level table and work split and resets the claim counters,
+ * barrier counters and status words.  Synchronous (it waits
  * for its own copies); call it once per set of buffers, outside stream
  * capture, before pwg_decode_step_weights.
  * Errors: PWG_ERR_ARG, PWG_ERR_ALIGN, PWG_ERR_SIZE, PWG_ERR_HIP,
@@ -486,6 +494,11 @@ int pwg_step_plan(const pwg_step_desc* desc, void* stream);
  * per CU; its only waits are inside a workgroup and are bounded (about
  * 0.5 s), after which the kernel records a timeout and ends instead of
  * hanging; pwg_step_status reports it.
+ * Persistent schedule: one kernel with one workgroup per CU (all resident at
+ * once); the levels run in order, separated by device-wide barriers whose
+ * waits are bounded the same way (a timed-out wait ends the kernel and
+ * pwg_step_status reports it).  Level outputs, formed inputs and h are
+ * written and read at device scope inside the launch.
  * Batched pass: a conversion kernel (operands and embedding rows), then one
  * kernel with one workgroup per CU that claims its work from a counter in the
  * workspace; its waits are inside a workgroup and bounded the same way.
@@ -493,8 +506,8 @@ int pwg_step_plan(const pwg_step_desc* desc, void* stream);
  * workspace race. */
 int pwg_decode_step_weights(const pwg_step_desc* desc, void* stream);
 
-/* Synchronously reads the step's status word (stream schedule and batched
- * pass; always PWG_OK for the levels schedule): PWG_ERR_HIP with a
+/* Synchronously reads the step's status word (stream and persistent
+ * schedules and batched pass; always PWG_OK for the levels schedule): PWG_ERR_HIP with a
  * message if a bounded wait timed out.  Not for the hot path. */
 int pwg_step_status(const pwg_step_desc* desc, void* stream);
 

@@ -42,7 +42,7 @@ INPUT_GIVEN, INPUT_RMSNORM, INPUT_EMBED_RMSNORM, INPUT_ATTN1, INPUT_SWIGLU = 0, 
 
 def layout_for_schedule(schedule: int) -> int:
     """Weight arrangement a schedule takes (the stream schedule runs on tiles)."""
-    return LAYOUT_TILED if schedule == SCHEDULE_STREAM else LAYOUT_ROWS
+    return LAYOUT_ROWS if schedule == SCHEDULE_LEVELS else LAYOUT_TILED
 
 
 class PwgError(RuntimeError):

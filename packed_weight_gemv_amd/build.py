@@ -18,7 +18,7 @@ BUILD = os.path.join(os.path.dirname(PKG), "_build")
 LIB = os.path.join(PKG, "libpwg.so")
 ARCH = os.environ.get("PWG_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["errors.cpp", "pack.cpp", "blob.cpp", "validate.cpp", "capi.hip", "gemv_mfma.hip", "int8_gemv.hip", "step_stream.hip", "tile.hip",
+SOURCES = ["errors.cpp", "pack.cpp", "blob.cpp", "validate.cpp", "capi.hip", "gemv_mfma.hip", "int8_gemv.hip", "step_stream.hip", "step_ordered.hip", "tile.hip",
            "batch_mfma.hip", "step_batch.hip", "chain.hip", "attention.hip", "verify.hip", "noalloc.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function"]

@@ -251,12 +251,10 @@ int validate_step(const pwg_step_desc* d) {
   if (d->schedule != PWG_SCHEDULE_LEVELS && d->schedule != PWG_SCHEDULE_PERSISTENT &&
       d->schedule != PWG_SCHEDULE_STREAM)
     return fail(PWG_ERR_ARG, "%s: unknown schedule %d", fn, d->schedule);
-  if (d->schedule == PWG_SCHEDULE_PERSISTENT)
-    return fail(PWG_ERR_UNSUPPORTED, "%s: the persistent schedule is not available in this build", fn);
   if (d->n_levels < 0 || d->n_levels > 4096) return fail(PWG_ERR_ARG, "%s: n_levels out of range", fn);
   if (d->weight_layout != PWG_LAYOUT_ROWS && d->weight_layout != PWG_LAYOUT_TILED)
     return fail(PWG_ERR_ARG, "%s: unknown weight layout %d", fn, d->weight_layout);
-  const int want = d->schedule == PWG_SCHEDULE_STREAM ? PWG_LAYOUT_TILED : PWG_LAYOUT_ROWS;
+  const int want = d->schedule == PWG_SCHEDULE_LEVELS ? PWG_LAYOUT_ROWS : PWG_LAYOUT_TILED;
   if (d->weight_layout != want)
     return fail(PWG_ERR_UNSUPPORTED, "%s: schedule %d takes weight layout %d (got %d)", fn, d->schedule, want,
                 d->weight_layout);
@@ -284,6 +282,11 @@ int validate_step(const pwg_step_desc* d) {
     TRY(check_ptr(d->out_table, fn, "out_table"));
     TRY(check_ptr(d->out_scale, fn, "out_scale"));
     TRY(batched(d) ? step_batch_check(d) : step_stream_check(d));
+  } else if (d->schedule == PWG_SCHEDULE_PERSISTENT) {
+    TRY(check_shape(d->vocab, d->hidden, fn));
+    TRY(check_ptr(d->out_table, fn, "out_table"));
+    TRY(check_ptr(d->out_scale, fn, "out_scale"));
+    TRY(step_ordered_check(d, fn));
   } else {
     TRY(validate_int8(d->out_table, d->out_scale, d->vocab, d->hidden, fn));
   }
@@ -311,6 +314,7 @@ extern "C" size_t pwg_step_workspace_bytes(const pwg_step_desc* d) {
     return step_batch_workspace(d);
   }
   if (d->schedule == PWG_SCHEDULE_STREAM) return step_stream_workspace(d);
+  if (d->schedule == PWG_SCHEDULE_PERSISTENT) return step_ordered_workspace(d);
   if (d->schedule != PWG_SCHEDULE_LEVELS) return 0;
   return argmax_ws(d->vocab, 1);
 }
@@ -320,9 +324,10 @@ extern "C" int pwg_step_plan(const pwg_step_desc* d, void* stream) {
   if (d->workspace_bytes < pwg_step_workspace_bytes(d))
     return fail(PWG_ERR_SIZE, "pwg_step_plan: workspace %zu < %zu bytes", d->workspace_bytes,
                 pwg_step_workspace_bytes(d));
-  if (d->schedule != PWG_SCHEDULE_STREAM) return PWG_OK;
+  if (d->schedule == PWG_SCHEDULE_LEVELS) return PWG_OK;
   plan_forget(d);
-  TRY(batched(d) ? step_batch_plan(d, stream) : step_stream_plan(d, 0, stream));
+  if (d->schedule == PWG_SCHEDULE_PERSISTENT) TRY(step_ordered_plan(d, stream));
+  else TRY(batched(d) ? step_batch_plan(d, stream) : step_stream_plan(d, 0, stream));
   plan_record(d);
   return PWG_OK;
 }
@@ -330,6 +335,7 @@ extern "C" int pwg_step_plan(const pwg_step_desc* d, void* stream) {
 extern "C" int pwg_step_status(const pwg_step_desc* d, void* stream) {
   TRY(validate_step(d));
   if (d->schedule == PWG_SCHEDULE_LEVELS) return PWG_OK;
+  if (d->schedule == PWG_SCHEDULE_PERSISTENT) return step_ordered_status(d, stream);
   if (batched(d)) return step_batch_status(d, stream);
   return step_stream_status(d, 0, stream);
 }
@@ -339,9 +345,10 @@ extern "C" int pwg_decode_step_weights(const pwg_step_desc* d, void* stream) {
   if (d->workspace_bytes < pwg_step_workspace_bytes(d))
     return fail(PWG_ERR_SIZE, "pwg_decode_step_weights: workspace %zu < %zu bytes", d->workspace_bytes,
                 pwg_step_workspace_bytes(d));
-  if (d->schedule == PWG_SCHEDULE_STREAM) {
+  if (d->schedule != PWG_SCHEDULE_LEVELS) {
     // the kernels take every pointer and shape from the device plan
     TRY(plan_check(d, "pwg_decode_step_weights"));
+    if (d->schedule == PWG_SCHEDULE_PERSISTENT) return step_ordered_launch(d, stream);
     return batched(d) ? step_batch_launch(d, stream) : step_stream_launch(d, 0, stream);
   }
   // Levels schedule: embedding row, every level in decoder order, output

@@ -9,8 +9,8 @@
 // form_input() is called by every thread of a workgroup of T threads and
 // leaves the formed float32 vector in LDS; store_formed() writes it, and the
 // residual sum, to memory.  The ordered step schedules call both: the levels
-// schedule from a one-workgroup kernel before the level's GEMV, the
-// persistent schedule in every workgroup after the level barrier.
+// schedule from a small kernel before the level's GEMV, the persistent
+// schedule in every workgroup after the level barrier.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -43,11 +43,21 @@ struct EmbedSrc {
   long vocab;
 };
 
+// A load of a value another workgroup of the same launch may have written:
+// kCoherent reads it at device scope (past this XCD's L2, which may hold a
+// stale line), so the kernel needs no cache invalidation.
+template <bool kCoherent>
+__device__ __forceinline__ float ld(const float* p) {
+  if (kCoherent) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return *p;
+}
+
 // Residual-stream value h[i] of a norm op (the dequantised embedding entry,
 // or resid + src); `row`/`s` describe the embedding row (s = 0: invalid id).
+template <bool kCoherent = false>
 __device__ __forceinline__ float norm_value(const DevInput& in, int i, const int8_t* row, float s) {
   if (in.op == PWG_INPUT_EMBED_RMSNORM) return row ? static_cast<float>(row[i]) * s : 0.f;
-  return in.src ? in.resid[i] + in.src[i] : in.resid[i];
+  return in.src ? ld<kCoherent>(in.resid + i) + ld<kCoherent>(in.src + i) : ld<kCoherent>(in.resid + i);
 }
 
 __device__ __forceinline__ void embed_row(const EmbedSrc& e, int n, const int8_t*& row, float& s) {
@@ -69,7 +79,7 @@ __device__ __forceinline__ void embed_row(const EmbedSrc& e, int n, const int8_t
 // (the sources were just written by other CUs and come from HBM).
 constexpr int kU = 8;
 
-template <int T>
+template <int T, bool kCoherent = false>
 __device__ __forceinline__ void form_input(const DevInput& in, int n, float* v, float* red, const EmbedSrc& e,
                                            int lo, int hi) {
   const int tid = threadIdx.x;
@@ -80,7 +90,7 @@ __device__ __forceinline__ void form_input(const DevInput& in, int n, float* v, 
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int i = base + u * T + tid;
-        a[u] = i < hi ? in.src[(i / span) * in.head_dim + i % in.head_dim] : 0.f;
+        a[u] = i < hi ? ld<kCoherent>(in.src + (i / span) * in.head_dim + i % in.head_dim) : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
@@ -97,8 +107,8 @@ __device__ __forceinline__ void form_input(const DevInput& in, int n, float* v, 
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int i = base + u * T + tid;
-        g[u] = i < hi ? in.src[i] : 0.f;
-        up[u] = i < hi ? in.src[n + i] : 0.f;
+        g[u] = i < hi ? ld<kCoherent>(in.src + i) : 0.f;
+        up[u] = i < hi ? ld<kCoherent>(in.src + n + i) : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
@@ -138,8 +148,8 @@ __device__ __forceinline__ void form_input(const DevInput& in, int n, float* v, 
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int i = base + u * T + tid;
-        r[u] = i < n ? in.resid[i] : 0.f;
-        a[u] = i < n ? in.src[i] : 0.f;
+        r[u] = i < n ? ld<kCoherent>(in.resid + i) : 0.f;
+        a[u] = i < n ? ld<kCoherent>(in.src + i) : 0.f;
         gm[u] = i < n ? in.gamma[i] : 0.f;
       }
 #pragma unroll
@@ -148,7 +158,7 @@ __device__ __forceinline__ void form_input(const DevInput& in, int n, float* v, 
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int i = base + u * T + tid;
-        h[u] = i < n ? in.resid[i] : 0.f;
+        h[u] = i < n ? ld<kCoherent>(in.resid + i) : 0.f;
         gm[u] = i < n ? in.gamma[i] : 0.f;
       }
     }
@@ -178,6 +188,9 @@ __device__ __forceinline__ void form_input(const DevInput& in, int n, float* v, 
 // norm ops, of h to resid_out.  Called by `nt` threads with index t; h is
 // recomputed from its sources (form_input only read them), with each
 // thread's loads of a batch issued before its stores.
+// kCoherent: agent-scope stores that reach memory past this XCD's L2, for a
+// kernel whose other workgroups read the residual sum later in the same launch.
+template <bool kCoherent = false>
 __device__ __forceinline__ void store_formed(const DevInput& in, int n, const float* v, float* x, const EmbedSrc& e,
                                              int lo, int hi, int t, int nt) {
   const bool norm = (in.op == PWG_INPUT_RMSNORM || in.op == PWG_INPUT_EMBED_RMSNORM) && in.resid_out;
@@ -189,14 +202,19 @@ __device__ __forceinline__ void store_formed(const DevInput& in, int n, const fl
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int i = base + u * nt + t;
-      h[u] = (norm && i < hi) ? norm_value(in, i, row, s) : 0.f;
+      h[u] = (norm && i < hi) ? norm_value<kCoherent>(in, i, row, s) : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int i = base + u * nt + t;
       if (i < hi) {
-        x[i] = v[i];
-        if (norm) in.resid_out[i] = h[u];
+        if (kCoherent) {
+          __hip_atomic_store(&x[i], v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (norm) __hip_atomic_store(&in.resid_out[i], h[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          x[i] = v[i];
+          if (norm) in.resid_out[i] = h[u];
+        }
       }
     }
   }

@@ -79,6 +79,13 @@ int step_stream_launch(const pwg_step_desc* d, size_t ws_offset, void* stream);
 int step_stream_status(const pwg_step_desc* d, size_t ws_offset, void* stream);
 
 // Batched pass (step_batch.hip): batch 4, 8 or 16, tiled weights.
+// The ordered (persistent) step on the matrix cores: step_ordered.hip.
+size_t step_ordered_workspace(const pwg_step_desc* d);
+int step_ordered_check(const pwg_step_desc* d, const char* fn);
+int step_ordered_plan(const pwg_step_desc* d, void* stream);
+int step_ordered_launch(const pwg_step_desc* d, void* stream);
+int step_ordered_status(const pwg_step_desc* d, void* stream);
+
 int step_batch_check(const pwg_step_desc* d);
 size_t step_batch_workspace(const pwg_step_desc* d);
 int step_batch_plan(const pwg_step_desc* d, void* stream);

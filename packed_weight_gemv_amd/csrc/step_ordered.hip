@@ -1,0 +1,804 @@
+// Ordered decode step on the CDNA4 matrix cores: one persistent kernel runs
+// the embedding row, every level in decoder order and the output projection
+// with greedy argmax, for chained levels (each input formed from earlier
+// outputs) as well as given ones.
+//
+// Page "The Neutrino Engine", section "A 104 microsecond floor inside a 694
+// microsecond step" and Fig. 1: each projection waits for the activations of
+// the one before it; most of a measured step went to kernel boundaries and
+// dependency waits, and a fused kernel with software barriers replaced the
+// launches with similar waits.  What this kernel does about the waits:
+//  * weights do not depend on activations, so while level L is computed the
+//    compute waves already have their level-L+1 tiles in flight (one
+//    register buffer per level parity), and HBM streams through the barrier;
+//  * every workgroup forms the whole input of a level itself, straight from
+//    its sources (previous outputs, the residual stream, the embedding row
+//    in the table), so one barrier per level orders everything;
+//  * outputs leave through device-coherent stores (past the XCD's L2) from
+//    a control wave that has no loads in flight, and the barrier is
+//    hierarchical over the 8 XCDs: an atomic in each XCD's L2 counts that
+//    XCD's arrivals, the last one publishes the XCD's arrival to 8
+//    replicated flag lines, and waiters poll their XCD's replica.
+// Arithmetic: the stream step's (operands.h): FP4 weights x six e4m3 pieces
+// of x on v_mfma_scale_f32_16x16x128_f8f6f4, the int8 table x six digits of
+// h on v_mfma_i32_16x16x64_i8; weights in the 16-row x 64-byte tiled
+// arrangement.
+//
+// Work: one workgroup of 8 waves per CU (the kernel asks for more than half
+// of a CU's LDS, so all workgroups are resident at once).  Workgroup w takes
+// 16-row blocks [w nb / G, (w + 1) nb / G) of every level; its 7 compute
+// waves split the workgroup's tiles (block-major) into contiguous ranges,
+// sum piece columns at each block end into 64-byte LDS slots, and the
+// control wave adds each block's slots in wave order (results do not depend
+// on timing), scales, stores and arrives.  The vocabulary is split the same
+// way in whole blocks per compute wave and streamed through both register
+// buffers; the last workgroup to finish reduces the argmax keys.  Every wait
+// is bounded (~0.5 s): a broken schedule ends with a status, never a hang.
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "chain_input.h"
+#include "device_common.h"
+#include "operands.h"
+#include "pwg_internal.h"
+
+namespace pwg {
+namespace {
+
+using namespace dev;
+using ops::v4f;
+using ops::v8i;
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kCompute = kWaves - 1;   // waves 1..7; wave 0 controls
+constexpr int kMaxT = 16;              // tiles per compute wave in one register buffer
+constexpr int kMaxCols = 12288;
+constexpr int kMaxBlk = 16;            // 16-row blocks of one level per workgroup
+constexpr int kReplicas = 8;
+constexpr unsigned long long kSpinLimit = 50000000ull;  // 0.5 s of the 100 MHz real-time counter
+enum : unsigned { kBarrierL2 = 0, kBarrierFlat = 1 };
+enum : unsigned { kStatusOk = 0, kStatusTimeout = 1 };
+enum : unsigned { kStateStatus = 0, kStateGen = 1 };
+
+// LDS: the formed input (float), the operand region, the partial slots,
+// the norm reduction and the waves' argmax keys.
+constexpr size_t kStageBytes = kMaxCols * 4;
+constexpr size_t kRegionBytes = 80256;  // ternary operands of 12,288 columns (int8 of 12,288: 73,920)
+static_assert(kRegionBytes >= ops::ternary_region_bytes(kMaxCols) && kRegionBytes >= ops::int8_region_bytes(kMaxCols),
+              "operand region");
+constexpr size_t kSlotsBytes = static_cast<size_t>(kMaxBlk) * kCompute * 64;
+constexpr size_t kMiscBytes = 256;
+constexpr size_t kLds = kStageBytes + kRegionBytes + kSlotsBytes + kMiscBytes;
+static_assert(kLds > 80 * 1024 && kLds <= 160 * 1024, "one resident workgroup per CU");
+
+struct OLevel {
+  const unsigned char* w;  // tiled T2
+  const float* scale;
+  const float* x;          // given input, or where the formed input is written
+  float* y;
+  int rows, cols, T, nb;   // T = cols / 256 tiles per block, nb = 16-row blocks
+  chain::DevInput in;
+};
+
+struct alignas(256) OPlan {
+  unsigned n_levels, n_barriers, grid, mode;
+  unsigned per_xcd[8];
+  unsigned xcd_mask;
+  int vocab, hidden;
+  const unsigned char* out_table;  // tiled int8
+  const float* out_scale;
+  const float* h;
+  const int8_t* emb_table;
+  const float* emb_scale;
+  const int* token_in;
+  int* token_out;
+  int8_t* emb_row_out;
+  float* emb_scale_out;
+  float* emb_deq_out;
+  float* logits_out;
+  chain::DevInput h_in;
+};
+
+constexpr size_t kMaxGrid = 1024;
+constexpr size_t kStateBytes = 256;
+constexpr size_t kCountersBytes = 8 * 128;               // one 64-bit counter per 128-byte line
+constexpr size_t kFlagsBytes = kReplicas * 256 + 4096;   // 8 XCD flags per replica line (+ flat mode)
+
+struct OLayout {
+  size_t plan, state, counters, flags, partials, arrivals, levels, calib, total;
+};
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+OLayout olayout(int n_levels) {
+  OLayout L{};
+  L.plan = 0;
+  L.state = align_up(sizeof(OPlan), 256);
+  L.counters = L.state + kStateBytes;
+  L.flags = L.counters + kCountersBytes;
+  L.partials = L.flags + kFlagsBytes;
+  L.arrivals = L.partials + kMaxGrid * 8;
+  L.levels = L.arrivals + 256;
+  L.calib = align_up(L.levels + static_cast<size_t>(n_levels) * sizeof(OLevel), 256);
+  L.total = align_up(L.calib + kMaxGrid * 4, 256);
+  return L;
+}
+
+// ------------------------------------------------------------------ device
+__device__ __forceinline__ unsigned ld_sc(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_sc(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool reached(unsigned f, unsigned e) { return static_cast<int>(f - e) >= 0; }
+__device__ __forceinline__ unsigned xcc_id() { return __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 7u; }
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <typename T>
+__device__ __forceinline__ T* uni_ptr(T* p) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
+  const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<int>(v >> 32)));
+  return reinterpret_cast<T*>((static_cast<unsigned long long>(hi) << 32) | lo);
+}
+
+struct Barrier {
+  const OPlan* plan;
+  unsigned* state;
+  unsigned long long* counters;
+  unsigned* flags;
+  unsigned xcd;
+  unsigned base;  // gen * n_barriers
+
+  // Arrival of the workgroup at barrier j, by its control wave once its
+  // device-coherent stores of the level have completed.  Everything another
+  // workgroup reads from this launch is stored and loaded at device scope,
+  // so no L2 write-back (or invalidation) is needed: those are cache-wide
+  // operations, and every workgroup of an XCD would run them each level.
+  __device__ __forceinline__ void arrive(unsigned j) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores have completed
+    if ((threadIdx.x & 63u) == 0) {
+      const unsigned epoch = base + j + 1;
+      if (plan->mode == kBarrierL2) {
+        // workgroup scope: the atomic executes in this XCD's L2, shared by its CUs
+        const unsigned long long old =
+            __hip_atomic_fetch_add(&counters[xcd * 16], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const unsigned long long target = static_cast<unsigned long long>(epoch) * plan->per_xcd[xcd];
+        if (old + 1 == target)
+          for (int r = 0; r < kReplicas; ++r) st_sc(&flags[r * 64 + xcd], epoch);
+      } else {
+        st_sc(&flags[kReplicas * 64 + blockIdx.x], epoch);
+      }
+    }
+  }
+
+  // Wait (control wave) until every workgroup has arrived at barrier j;
+  // true when the wait timed out (uniform).
+  __device__ __forceinline__ bool wait(unsigned j) {
+    const unsigned epoch = base + j + 1;
+    const unsigned lane = threadIdx.x & 63u;
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    bool late = false;
+    while (true) {
+      bool ok = true;
+      if (plan->mode == kBarrierL2) {
+        if (lane < 8 && ((plan->xcd_mask >> lane) & 1u)) ok = reached(ld_sc(&flags[xcd * 64 + lane]), epoch);
+      } else {
+        for (unsigned b0 = 0; b0 < plan->grid; b0 += 64)
+          if (b0 + lane < plan->grid) ok = ok && reached(ld_sc(&flags[kReplicas * 64 + b0 + lane]), epoch);
+      }
+      if (__all(ok)) break;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
+        late = true;
+        break;
+      }
+    }
+    if (late && lane == 0) st_sc(&state[kStateStatus], kStatusTimeout);
+    return late;
+  }
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+constexpr unsigned kOff = 0x80000000u;  // past every resource: the load returns zero and moves nothing
+
+// Tiles [s, e) of a block-major sequence of 1 KiB tiles (T per block, first
+// block b0 of a matrix of nb blocks): this lane's 16 bytes of tile s + j go
+// to r[j]; the slots past e read nothing.
+__device__ __forceinline__ void load_tiles(u32x4 (&r)[kMaxT], const unsigned char* w, int nb, int T, int b0, int s,
+                                           int e) {
+  const __amdgpu_buffer_rsrc_t rs = buffer_over(w, static_cast<unsigned>(nb) * static_cast<unsigned>(T) * 1024u);
+  const unsigned lane = threadIdx.x & 63u;
+  int blk = s / T, t = s - blk * T;
+#pragma unroll
+  for (int j = 0; j < kMaxT; ++j) {
+    const unsigned off = s + j < e ? static_cast<unsigned>(((b0 + blk) * T + t) * 1024) + 16u * lane : kOff;
+    r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2));
+    const int wrap = t + 1 == T;  // selects, not branches: the loads stay in one basic block
+    t = wrap ? 0 : t + 1;
+    blk += wrap;
+  }
+}
+
+// Ternary tiles [s, e) (at most kMaxT, the ones in r) of a compute wave's
+// range that ends at e_all: two MFMAs per tile against the operand region;
+// at a block's last tile, or the range's end, the piece columns are summed
+// and the block's 16 row sums go to slot (block, wave).
+__device__ __forceinline__ void ternary_tiles(const u32x4 (&r)[kMaxT], int T, int s, int e, int e_all,
+                                              const unsigned char* region, int bsc_off, int asc_off, float* slots,
+                                              int k, v4f& acc0, v4f& acc1) {
+  const unsigned lane = threadIdx.x & 63u, n = lane & 15u, g = lane >> 4;
+  const unsigned tboff = ops::ternary_b_entry(n, g);
+  int blk = s / T, t = s - blk * T;
+#pragma unroll
+  for (int j = 0; j < kMaxT; ++j) {
+    if (s + j < e) {
+      v8i a0, a1;
+      ops::ternary_unpack(r[j], a0, a1);
+      const unsigned char* bp = region + static_cast<size_t>(2 * t) * ops::kTernaryMfmaBytes + tboff;
+      const u32x4 b0l = *reinterpret_cast<const u32x4*>(bp), b0h = *reinterpret_cast<const u32x4*>(bp + 16);
+      const u32x4 b1l = *reinterpret_cast<const u32x4*>(bp + ops::kTernaryMfmaBytes);
+      const u32x4 b1h = *reinterpret_cast<const u32x4*>(bp + ops::kTernaryMfmaBytes + 16);
+      const int sb = *reinterpret_cast<const int*>(region + bsc_off + (t >> 1) * 256 + 4 * lane);
+      const int sa = *reinterpret_cast<const int*>(region + asc_off + (t >> 1) * 16 + 4 * g);
+      const v8i B0 = {static_cast<int>(b0l.x), static_cast<int>(b0l.y), static_cast<int>(b0l.z), static_cast<int>(b0l.w),
+                      static_cast<int>(b0h.x), static_cast<int>(b0h.y), static_cast<int>(b0h.z), static_cast<int>(b0h.w)};
+      const v8i B1 = {static_cast<int>(b1l.x), static_cast<int>(b1l.y), static_cast<int>(b1l.z), static_cast<int>(b1l.w),
+                      static_cast<int>(b1h.x), static_cast<int>(b1h.y), static_cast<int>(b1h.z), static_cast<int>(b1h.w)};
+      if (t & 1) {  // instructions 2 t, 2 t + 1: scale bytes 2 and 3 of their quad's dwords
+        acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, B0, acc0, 4, 0, 2, sa, 2, sb);
+        acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, B1, acc1, 4, 0, 3, sa, 3, sb);
+      } else {
+        acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, B0, acc0, 4, 0, 0, sa, 0, sb);
+        acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, B1, acc1, 4, 0, 1, sa, 1, sb);
+      }
+      // operands live past the instructions: no destination shares their registers
+      asm volatile("" ::"v"(a0), "v"(a1), "v"(B0), "v"(B1));
+      if (t == T - 1 || s + j == e_all - 1) {
+        v4f a = acc0 + acc1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = ops::row16_sum(n < static_cast<unsigned>(ops::kSplits) ? a[i] : 0.f);
+        if (n == 0) *reinterpret_cast<v4f*>(slots + (blk * kCompute + k) * 16 + 4 * g) = a;
+        acc0 = v4f{0.f, 0.f, 0.f, 0.f};
+        acc1 = v4f{0.f, 0.f, 0.f, 0.f};
+      }
+      const int wrap = t + 1 == T;
+      t = wrap ? 0 : t + 1;
+      blk += wrap;
+    }
+  }
+}
+
+// One round of the vocabulary: tiles t0 .. t0 + kMaxT - 1 of one block (t0
+// a multiple of kMaxT, so the exponent sections of 4 tiles fall at fixed
+// places): one MFMA per tile, exact int32 sums per section moved into float
+// with the section's power of two.
+__device__ __forceinline__ void int8_round(const u32x4 (&r)[kMaxT], int t0, const unsigned char* region, int exp_off,
+                                           v4i& iacc, v4f& facc) {
+  const unsigned lane = threadIdx.x & 63u, n = lane & 15u, g = lane >> 4;
+  const unsigned iboff = ops::int8_b_entry(n, g);
+  const int cexp = n < static_cast<unsigned>(ops::kInt8Digits) ? static_cast<int>(8u * n) : -1000;
+#pragma unroll
+  for (int j = 0; j < kMaxT; ++j) {
+    const int t = t0 + j;
+    const u32x4 b = *reinterpret_cast<const u32x4*>(region + t * ops::kInt8MfmaBytes + iboff);
+    const v4i A = {static_cast<int>(r[j].x), static_cast<int>(r[j].y), static_cast<int>(r[j].z), static_cast<int>(r[j].w)};
+    const v4i B = {static_cast<int>(b.x), static_cast<int>(b.y), static_cast<int>(b.z), static_cast<int>(b.w)};
+    iacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, iacc, 0, 0, 0);
+    if ((j % ops::kSectionMfmas) == ops::kSectionMfmas - 1) {
+      const int ex = *reinterpret_cast<const int*>(region + exp_off + (t / ops::kSectionMfmas) * 4) + cexp;
+      // |iacc| <= 4 * 64 * 127 * 128 < 2^23: the conversion is exact
+      facc.x += ldexpf(static_cast<float>(iacc.x), ex);
+      facc.y += ldexpf(static_cast<float>(iacc.y), ex);
+      facc.z += ldexpf(static_cast<float>(iacc.z), ex);
+      facc.w += ldexpf(static_cast<float>(iacc.w), ex);
+      iacc = v4i{0, 0, 0, 0};
+    }
+  }
+}
+
+// End of vocabulary block blk: the digit columns summed and scaled, the
+// logits stored (through a resource that is empty when none are wanted, so
+// the store is not a branch) and the lane's running (max, lowest row)
+// updated.
+__device__ __forceinline__ void int8_block_end(long blk, const OPlan& P, __amdgpu_buffer_rsrc_t lr, v4f& facc,
+                                               float& best, unsigned& best_idx) {
+  const unsigned lane = threadIdx.x & 63u, n = lane & 15u, g = lane >> 4;
+  const v4f sc = ops::block_scales(P.out_scale, blk, P.vocab, g);
+  const long r0 = blk * 16 + 4 * g;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = ops::row16_sum(n < static_cast<unsigned>(ops::kInt8Digits) ? facc[i] : 0.f) * sc[i];
+    const bool mine = n == 0 && r0 + i < P.vocab;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), lr, mine ? static_cast<unsigned>(4 * (r0 + i)) : kOff, 0, 0);
+    if (mine && a > best) {  // a lane's rows ascend; ties keep the lower index
+      best = a;
+      best_idx = static_cast<unsigned>(r0 + i);
+    }
+  }
+  facc = v4f{0.f, 0.f, 0.f, 0.f};
+}
+
+// Any vocabulary width (T a multiple of 4): the wave's n tiles from block
+// b0 on, one load per tile as it is used.  For widths that are not a
+// multiple of 64 kMaxT values (never the 8B shape): no prefetch, few
+// registers.
+__device__ __noinline__ unsigned long long int8_tiles_any(const OPlan& P, int T, int nbv, long b0, int n,
+                                                          const unsigned char* region, int exp_off,
+                                                          __amdgpu_buffer_rsrc_t lr) {
+  float best = -__builtin_inff();
+  unsigned best_idx = 0xFFFFFFFFu;
+  const unsigned lane = threadIdx.x & 63u, nl = lane & 15u, g = lane >> 4;
+  const unsigned iboff = ops::int8_b_entry(nl, g);
+  const int cexp = nl < static_cast<unsigned>(ops::kInt8Digits) ? static_cast<int>(8u * nl) : -1000;
+  const __amdgpu_buffer_rsrc_t rs = buffer_over(P.out_table, static_cast<unsigned>(nbv) * static_cast<unsigned>(T) * 1024u);
+  v4i iacc = {0, 0, 0, 0};
+  v4f facc = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < n; ++i) {
+    const int blk = i / T, t = i - blk * T;
+    const u32x4 v = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<unsigned>(((b0 + blk) * T + t) * 1024) + 16u * lane, 0, 2));
+    const u32x4 b = *reinterpret_cast<const u32x4*>(region + t * ops::kInt8MfmaBytes + iboff);
+    const v4i A = {static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w)};
+    const v4i B = {static_cast<int>(b.x), static_cast<int>(b.y), static_cast<int>(b.z), static_cast<int>(b.w)};
+    iacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, iacc, 0, 0, 0);
+    if ((t % ops::kSectionMfmas) == ops::kSectionMfmas - 1) {
+      const int ex = *reinterpret_cast<const int*>(region + exp_off + (t / ops::kSectionMfmas) * 4) + cexp;
+      facc.x += ldexpf(static_cast<float>(iacc.x), ex);
+      facc.y += ldexpf(static_cast<float>(iacc.y), ex);
+      facc.z += ldexpf(static_cast<float>(iacc.z), ex);
+      facc.w += ldexpf(static_cast<float>(iacc.w), ex);
+      iacc = v4i{0, 0, 0, 0};
+    }
+    if (t == T - 1) int8_block_end(b0 + blk, P, lr, facc, best, best_idx);
+  }
+  return best_idx == 0xFFFFFFFFu ? 0ull : argmax_key(best, best_idx);  // this lane's (max, lowest row)
+}
+
+// Converts the formed input in `stage` (cols values) into the ternary
+// operand region: four threads per 32-value block, one summation group each.
+__device__ __forceinline__ void convert_ternary(const float* stage, int cols, unsigned char* region) {
+  const int T = cols >> 8;
+  const size_t mf = static_cast<size_t>(2 * T);
+  const size_t bsc = ops::operand_bsc_off(mf), asc = ops::operand_asc_off(mf);
+  for (int t0 = 0; t0 < T * 32; t0 += kThreads) {  // uniform trip count (shuffles below)
+    const int tid = t0 + static_cast<int>(threadIdx.x);
+    const int beta = tid >> 2, h = (tid >> 1) & 1, G = tid & 1;
+    const bool in = tid < T * 32;
+    float xs[16];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      xs[i] = in ? stage[32 * beta + 16 * h + i] : 0.f;
+      amax = fmaxf(amax, fabsf(xs[i]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));  // the other half of the block
+    if (in) ops::write_ternary_quarter(region, bsc, asc, beta, h, G, xs, ops::block_exponent(amax));
+  }
+}
+
+// Converts h (stage, hidden values) into the int8 operand region: one wave
+// per 256-value section, lane t owning values 4t .. 4t + 3.
+__device__ __forceinline__ void convert_int8(const float* stage, int hidden, unsigned char* region) {
+  const unsigned lane = threadIdx.x & 63u;
+  const int exp_off = static_cast<int>(ops::int8_exp_off(hidden));
+  for (int sec = static_cast<int>(threadIdx.x >> 6); sec < hidden / 256; sec += kWaves) {
+    const float* v = stage + 256 * sec + 4 * lane;
+    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+    const int e = ops::block_exponent(amax);
+    const float hv[4] = {v[0], v[1], v[2], v[3]};
+    unsigned dw[ops::kInt8Digits];
+    ops::int8_digits4(hv, e, dw);
+    const int m = 4 * sec + static_cast<int>(lane >> 4), g = static_cast<int>((lane & 15u) >> 2),
+              j0 = 4 * static_cast<int>(lane & 3u);
+#pragma unroll
+    for (int d = 0; d < ops::kInt8Digits; ++d)
+      *reinterpret_cast<unsigned*>(region + m * ops::kInt8MfmaBytes + ops::int8_b_entry(d, g) + j0) = dw[d];
+    if (lane == 0) *reinterpret_cast<int*>(region + exp_off + 4 * sec) = e - ops::kInt8FixedBits;
+  }
+}
+
+// The input of level `li` (li == n_levels: h) in `stage`, by every thread.
+__device__ __forceinline__ void form_level_input(const OPlan& P, const OLevel* levels, unsigned li, float* stage,
+                                                 float* red, const chain::EmbedSrc& emb) {
+  const bool vocab = li == P.n_levels;
+  const chain::DevInput& in = vocab ? P.h_in : levels[li].in;
+  const int n = vocab ? P.hidden : levels[li].cols;
+  if (in.op == PWG_INPUT_GIVEN) {  // a given input may be an earlier level's output: device-scope loads
+    const float* x = vocab ? P.h : levels[li].x;
+    for (int i = static_cast<int>(threadIdx.x); i < n; i += kThreads)
+      stage[i] = __hip_atomic_load(x + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+  } else {
+    chain::form_input<kThreads, true>(in, n, stage, red, emb, 0, n);
+  }
+}
+
+// Embedding row of the step's token (control wave of workgroup 0).
+__device__ __forceinline__ void embed_outputs(const OPlan& P) {
+  const unsigned lane = threadIdx.x & 63u;
+  const int id = *P.token_in;
+  const bool ok = id >= 0 && id < P.vocab;
+  const float s = ok ? P.emb_scale[id] : __builtin_nanf("");
+  if (lane == 0) *P.emb_scale_out = s;
+  for (int i = static_cast<int>(lane); i < P.hidden; i += 64) {
+    const int8_t q = ok ? P.emb_table[static_cast<long>(id) * P.hidden + i] : static_cast<int8_t>(0);
+    P.emb_row_out[i] = q;
+    if (P.emb_deq_out) P.emb_deq_out[i] = ok ? static_cast<float>(q) * s : 0.f;
+  }
+}
+
+// Tiles [s, e) of compute wave k of a workgroup with nblk blocks of T tiles.
+__device__ __forceinline__ void wave_range(int nblk, int T, int k, int& s, int& e) {
+  const int n = nblk * T;
+  s = k * n / kCompute;
+  e = (k + 1) * n / kCompute;
+}
+
+__global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* __restrict__ plan,
+                                                                   const OLevel* __restrict__ levels, unsigned* state,
+                                                                   unsigned long long* counters, unsigned* flags,
+                                                                   unsigned long long* partials, unsigned* arrivals) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* stage = reinterpret_cast<float*>(smem);
+  unsigned char* region = smem + kStageBytes;
+  float* slots = reinterpret_cast<float*>(smem + kStageBytes + kRegionBytes);
+  float* red = reinterpret_cast<float*>(smem + kStageBytes + kRegionBytes + kSlotsBytes);
+  unsigned long long* wkeys = reinterpret_cast<unsigned long long*>(red + 16);
+
+  const OPlan& P = *plan;
+  const unsigned lane = threadIdx.x & 63u;
+  const int wave = uni(static_cast<int>(threadIdx.x >> 6));
+  const int k = wave - 1;  // compute-wave index (wave 0: -1)
+  const unsigned G = P.grid, wg = blockIdx.x;
+  const unsigned nl = P.n_levels;
+  Barrier bar{plan, state, counters, flags, xcc_id(), 0};
+  bar.base = ld_sc(&state[kStateGen]) * P.n_barriers;
+  const chain::EmbedSrc emb{P.emb_table, P.emb_scale, P.token_in, static_cast<long>(P.vocab)};
+
+  // rows of level li owned by this workgroup: blocks [b0, b1)
+  auto wg_blocks = [&](unsigned li, int& b0, int& b1) {
+    const int nb = li < nl ? uni(levels[li].nb) : (P.vocab + 15) / 16;
+    b0 = static_cast<int>(static_cast<long>(wg) * nb / G);
+    b1 = static_cast<int>(static_cast<long>(wg + 1) * nb / G);
+  };
+  // tiles of level li (li == nl: the vocabulary's first kMaxT; past it:
+  // none) for this compute wave.  The parameters are chosen first and the
+  // loads issued from one place, so the compiler counts them and the compute
+  // that follows waits only for the tiles it uses.
+  auto prefetch = [&](u32x4 (&r)[kMaxT], unsigned li) {
+    int b0 = 0, b1 = 0, s = 0, e = 0, nb = 1, T = 1;
+    const unsigned char* w = P.out_table;
+    if (li <= nl) wg_blocks(li, b0, b1);
+    if (li < nl) {
+      const OLevel& L = levels[li];
+      w = uni_ptr(L.w);
+      nb = uni(L.nb);
+      T = uni(L.T);
+      wave_range(b1 - b0, T, k, s, e);
+    } else if (li == nl) {
+      T = P.hidden / 64;
+      nb = (P.vocab + 15) / 16;
+      const int w0 = b0 + k * (b1 - b0) / kCompute, w1 = b0 + (k + 1) * (b1 - b0) / kCompute;
+      b0 = w0;
+      e = (w1 - w0) * T;
+    }
+    load_tiles(r, w, nb, T, b0, s, e < s + kMaxT ? e : s + kMaxT);
+  };
+
+  u32x4 ra[kMaxT], rb[kMaxT];
+  if (wave == 0) {
+    if (wg == 0) embed_outputs(P);
+  } else {
+    prefetch(ra, 0);
+  }
+
+  // One level: its tiles are in `cur` (loaded a level earlier), the next
+  // level's go into `nxt` before the compute.
+  auto level = [&](unsigned li, u32x4(&cur)[kMaxT], u32x4(&nxt)[kMaxT]) -> bool {
+    if (li > 0) {
+      bool late = false;
+      if (wave == 0) late = bar.wait(li - 1);
+      if (wave == 0 && lane == 0) red[15] = late ? 1.f : 0.f;
+      __syncthreads();
+      if (red[15] != 0.f) return true;
+    }
+    const OLevel& L = levels[li];
+    const int T = uni(L.T), cols = uni(L.cols), rows = uni(L.rows);
+    int b0, b1;
+    wg_blocks(li, b0, b1);
+    form_level_input(P, levels, li, stage, red, emb);
+    convert_ternary(stage, cols, region);
+    if (wave == 0 && L.in.op != PWG_INPUT_GIVEN)
+      chain::store_formed<true>(L.in, cols, stage, const_cast<float*>(L.x), emb,
+                                static_cast<int>(static_cast<long>(wg) * cols / G),
+                                static_cast<int>(static_cast<long>(wg + 1) * cols / G), static_cast<int>(lane), 64);
+    __syncthreads();  // the operand region is complete
+    if (wave > 0) {
+      // every load issued so far has completed (the formation waited for
+      // its own, issued after this level's tiles); saying so lets the
+      // compiler count the prefetch below instead of draining it
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      prefetch(nxt, li + 1);
+      int s, e;
+      wave_range(b1 - b0, T, k, s, e);
+      const size_t mf = static_cast<size_t>(2 * T);
+      const int bsc = static_cast<int>(ops::operand_bsc_off(mf)), asc = static_cast<int>(ops::operand_asc_off(mf));
+      v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+      // the first round's tiles arrived before the formation; rounds past it
+      // (levels wider than 7 x kMaxT tiles per workgroup) load on demand
+      ternary_tiles(cur, T, s, e < s + kMaxT ? e : s + kMaxT, e, region, bsc, asc, slots, k, acc0, acc1);
+      for (int r0 = s + kMaxT; r0 < e; r0 += kMaxT) {
+        load_tiles(cur, uni_ptr(L.w), uni(L.nb), T, b0, r0, e < r0 + kMaxT ? e : r0 + kMaxT);
+        ternary_tiles(cur, T, r0, e < r0 + kMaxT ? e : r0 + kMaxT, e, region, bsc, asc, slots, k, acc0, acc1);
+      }
+    }
+    __syncthreads();  // every slot of the level is written
+    if (wave == 0) {
+      // rows of the workgroup: block bl's sum over the compute waves that
+      // touched it, in wave order
+      const int nrow = (b1 - b0) * 16;
+      for (int r0 = 0; r0 < nrow; r0 += 64) {
+        const int rr = r0 + static_cast<int>(lane);
+        if (rr < nrow) {
+          const int bl = rr >> 4, i = rr & 15;
+          float v = 0.f;
+          for (int kk = 0; kk < kCompute; ++kk) {
+            int s, e;
+            wave_range(b1 - b0, T, kk, s, e);
+            if (s < e && s < (bl + 1) * T && e > bl * T) v += slots[(bl * kCompute + kk) * 16 + i];
+          }
+          const long row = static_cast<long>(b0 + bl) * 16 + i;
+          if (row < rows) __hip_atomic_store(&L.y[row], v * L.scale[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      bar.arrive(li);
+    }
+    return false;
+  };
+
+  // levels in pairs, so that each buffer has one static role per call
+  for (unsigned li = 0; li < nl; li += 2) {
+    if (level(li, ra, rb)) return;
+    if (li + 1 < nl && level(li + 1, rb, ra)) return;
+  }
+  const bool vocab_in_a = (nl & 1u) == 0;  // the vocabulary's first tiles: prefetched into ra for even nl
+
+  // Output projection: h formed after the last level, then every compute
+  // wave streams its whole vocabulary blocks through both buffers.
+  if (nl > 0) {
+    bool late = false;
+    if (wave == 0) late = bar.wait(nl - 1);
+    if (wave == 0 && lane == 0) red[15] = late ? 1.f : 0.f;
+    __syncthreads();
+    if (red[15] != 0.f) return;
+  }
+  form_level_input(P, levels, nl, stage, red, emb);
+  convert_int8(stage, P.hidden, region);
+  if (wave == 0 && P.h_in.op != PWG_INPUT_GIVEN)
+    chain::store_formed<true>(P.h_in, P.hidden, stage, const_cast<float*>(P.h), emb,
+                               static_cast<int>(static_cast<long>(wg) * P.hidden / G),
+                               static_cast<int>(static_cast<long>(wg + 1) * P.hidden / G), static_cast<int>(lane), 64);
+  __syncthreads();
+  float best = -__builtin_inff();
+  unsigned best_idx = 0xFFFFFFFFu;
+  unsigned long long key_any = 0ull;  // the any-width path's key
+  if (wave > 0) {
+    int b0, b1;
+    wg_blocks(nl, b0, b1);
+    const int T = P.hidden / 64, nbv = (P.vocab + 15) / 16;
+    const int w0 = b0 + k * (b1 - b0) / kCompute, w1 = b0 + (k + 1) * (b1 - b0) / kCompute;
+    const int n = (w1 - w0) * T;
+    const int exp_off = static_cast<int>(ops::int8_exp_off(P.hidden));
+    v4i iacc = {0, 0, 0, 0};
+    v4f facc = {0.f, 0.f, 0.f, 0.f};
+    const __amdgpu_buffer_rsrc_t lr =
+        buffer_over(P.logits_out, P.logits_out ? static_cast<unsigned>(P.vocab) * 4u : 0u);
+    const int rpb = T / kMaxT;  // rounds per block (T is a multiple of kMaxT)
+    auto stream = [&](u32x4(&a)[kMaxT], u32x4(&b)[kMaxT]) {
+      if (T % kMaxT != 0) {  // any width: tiles loaded one at a time (the prefetched round is not used)
+        key_any = int8_tiles_any(P, T, nbv, w0, n, region, exp_off, lr);
+        return;
+      }
+      // a holds round 0 (prefetched); rounds alternate between the buffers
+      for (int r0 = 0; r0 < n; r0 += 2 * kMaxT) {
+        load_tiles(b, P.out_table, nbv, T, w0, r0 + kMaxT, n < r0 + 2 * kMaxT ? n : r0 + 2 * kMaxT);
+        int8_round(a, r0 % T, region, exp_off, iacc, facc);
+        if ((r0 / kMaxT) % rpb == rpb - 1) int8_block_end(w0 + r0 / T, P, lr, facc, best, best_idx);
+        if (r0 + kMaxT >= n) break;
+        load_tiles(a, P.out_table, nbv, T, w0, r0 + 2 * kMaxT, n < r0 + 3 * kMaxT ? n : r0 + 3 * kMaxT);
+        int8_round(b, (r0 + kMaxT) % T, region, exp_off, iacc, facc);
+        if ((r0 / kMaxT + 1) % rpb == rpb - 1) int8_block_end(w0 + (r0 + kMaxT) / T, P, lr, facc, best, best_idx);
+      }
+    };
+    if (vocab_in_a) stream(ra, rb);
+    else stream(rb, ra);
+  }
+
+  // Workgroup (max, lowest index), then the last workgroup to arrive reduces
+  // every workgroup's key into the token and starts the next step's epoch.
+  unsigned long long key = best_idx == 0xFFFFFFFFu ? 0ull : argmax_key(best, best_idx);
+  key = key_any > key ? key_any : key;
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned long long o = __shfl_xor(key, off, kWave);
+    key = o > key ? o : key;
+  }
+  if (lane == 0) wkeys[wave] = key;
+  __syncthreads();
+  if (wave == 0) {
+    unsigned last = 0;
+    if (lane == 0) {
+      unsigned long long m = 0ull;
+      for (int i = 0; i < kWaves; ++i) m = wkeys[i] > m ? wkeys[i] : m;
+      __hip_atomic_store(&partials[wg], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned prev = __hip_atomic_fetch_add(arrivals, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      last = prev == G - 1u ? 1u : 0u;
+    }
+    if (uni(static_cast<int>(last))) {
+      unsigned long long m = 0ull;
+      for (unsigned b = lane; b < G; b += 64) {
+        const unsigned long long o = __hip_atomic_load(&partials[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        m = o > m ? o : m;
+      }
+      for (int off = 32; off >= 1; off >>= 1) {
+        const unsigned long long o = __shfl_xor(m, off, kWave);
+        m = o > m ? o : m;
+      }
+      if (lane == 0) {
+        *P.token_out = static_cast<int>(argmax_key_index(m));
+        __hip_atomic_store(arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        st_sc(&state[kStateGen], ld_sc(&state[kStateGen]) + 1u);
+      }
+    }
+  }
+}
+
+__global__ void xcc_census_kernel(unsigned* out) {
+  if (threadIdx.x == 0) out[blockIdx.x] = xcc_id();
+}
+
+int ordered_grid() {
+  int dev = 0, cus = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return -1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&ordered_step_kernel), kThreads,
+                                                   kLds) != hipSuccess || n != 1)
+    return -1;
+  return cus;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------- host
+size_t step_ordered_workspace(const pwg_step_desc* d) { return olayout(d->n_levels).total; }
+
+int step_ordered_check(const pwg_step_desc* d, const char* fn) {
+  if (d->weight_layout != PWG_LAYOUT_TILED)
+    return fail(PWG_ERR_UNSUPPORTED, "%s: the persistent schedule reads tiled weights (PWG_LAYOUT_TILED)", fn);
+  if (d->batch > 1) return fail(PWG_ERR_UNSUPPORTED, "%s: the persistent schedule runs one vector", fn);
+  if (d->hidden < 256 || d->hidden % 256 != 0 || d->hidden > kMaxCols)
+    return fail(PWG_ERR_UNSUPPORTED, "%s: hidden must be a multiple of 256 in [256, %d] on the persistent schedule", fn,
+                kMaxCols);
+  for (int i = 0; i < d->n_levels; ++i) {
+    const pwg_level& L = d->levels[i];
+    if (L.cols % 256 != 0 || L.cols > kMaxCols)
+      return fail(PWG_ERR_UNSUPPORTED, "%s: level %d: cols must be a multiple of 256 in [256, %d] on the persistent "
+                  "schedule", fn, i, kMaxCols);
+  }
+  return PWG_OK;
+}
+
+namespace {
+OLayout layout_of(const pwg_step_desc* d) { return olayout(d->n_levels); }
+unsigned char* ws_base(const pwg_step_desc* d) { return static_cast<unsigned char*>(d->workspace); }
+}  // namespace
+
+int step_ordered_plan(const pwg_step_desc* d, void* stream) {
+  const char* fn = "pwg_step_plan";
+  TRY(step_ordered_check(d, fn));
+  const int G = ordered_grid();
+  if (G < 1 || G > static_cast<int>(kMaxGrid))
+    return fail(PWG_ERR_UNSUPPORTED, "%s: the persistent kernel needs one resident workgroup on every CU", fn);
+  const OLayout lay = layout_of(d);
+  std::vector<OLevel> lv(static_cast<size_t>(d->n_levels));
+  for (int i = 0; i < d->n_levels; ++i) {
+    const pwg_level& L = d->levels[i];
+    OLevel& o = lv[i];
+    o.w = static_cast<const unsigned char*>(L.w_packed);
+    o.scale = L.row_scale;
+    o.x = L.x;
+    o.y = L.y;
+    o.rows = static_cast<int>(L.rows);
+    o.cols = static_cast<int>(L.cols);
+    o.T = static_cast<int>(L.cols / 256);
+    o.nb = static_cast<int>((L.rows + 15) / 16);
+    o.in = chain::from_abi(L.in);
+    if ((o.nb + G - 1) / G > kMaxBlk)
+      return fail(PWG_ERR_UNSUPPORTED, "%s: level %d has more than %d rows per CU", fn, i, kMaxBlk * 16);
+    if (static_cast<long>(o.nb) * o.T * 1024 >= (1L << 32))
+      return fail(PWG_ERR_UNSUPPORTED, "%s: level %d is larger than 4 GiB", fn, i);
+  }
+  if ((d->vocab + 15) / 16 * (d->hidden / 64) * 1024 >= (int64_t{1} << 32))
+    return fail(PWG_ERR_UNSUPPORTED, "%s: the output table is larger than 4 GiB", fn);
+  OPlan h;
+  std::memset(&h, 0, sizeof h);
+  h.n_levels = static_cast<unsigned>(d->n_levels);
+  h.n_barriers = static_cast<unsigned>(d->n_levels > 0 ? d->n_levels : 1);
+  h.grid = static_cast<unsigned>(G);
+  h.vocab = static_cast<int>(d->vocab);
+  h.hidden = static_cast<int>(d->hidden);
+  h.out_table = static_cast<const unsigned char*>(static_cast<const void*>(d->out_table));
+  h.out_scale = d->out_scale;
+  h.h = d->h;
+  h.emb_table = d->emb_table;
+  h.emb_scale = d->emb_scale;
+  h.token_in = d->token_in;
+  h.token_out = d->token_out;
+  h.emb_row_out = d->emb_row_out;
+  h.emb_scale_out = d->emb_scale_out;
+  h.emb_deq_out = d->emb_deq_out;
+  h.logits_out = d->logits_out;
+  h.h_in = chain::from_abi(d->h_in);
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  unsigned char* base = ws_base(d);
+  // XCD census: one workgroup per CU (the step kernel's LDS request); the
+  // barrier counts per XCD when every XCD holds the same number of them
+  hipLaunchKernelGGL(xcc_census_kernel, dim3(G), dim3(kThreads), kLds, st, reinterpret_cast<unsigned*>(base + lay.calib));
+  std::vector<unsigned> xcc(static_cast<size_t>(G));
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = hipMemcpyAsync(xcc.data(), base + lay.calib, static_cast<size_t>(G) * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(PWG_ERR_HIP, "%s: XCD census: %s", fn, hipGetErrorString(e));
+  unsigned census[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int b = 0; b < G; ++b) census[xcc[b] & 7u] += 1;
+  bool uniform = true;
+  for (int x = 1; x < 8; ++x) uniform = uniform && (census[x] == census[0] || census[x] == 0);
+  h.mode = uniform ? kBarrierL2 : kBarrierFlat;
+  for (int x = 0; x < 8; ++x) {
+    h.per_xcd[x] = census[x];
+    if (census[x]) h.xcd_mask |= 1u << x;
+  }
+  e = hipMemcpyAsync(base + lay.plan, &h, sizeof h, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess && !lv.empty())
+    e = hipMemcpyAsync(base + lay.levels, lv.data(), lv.size() * sizeof(OLevel), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipMemsetAsync(base + lay.state, 0, lay.levels - lay.state, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(PWG_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  return PWG_OK;
+}
+
+int step_ordered_launch(const pwg_step_desc* d, void* stream) {
+  const OLayout lay = layout_of(d);
+  static int grid = -1;
+  if (grid < 0) grid = ordered_grid();
+  if (grid < 1) return fail(PWG_ERR_UNSUPPORTED, "persistent step: no resident grid");
+  unsigned char* base = ws_base(d);
+  hipLaunchKernelGGL(ordered_step_kernel, dim3(grid), dim3(kThreads), kLds, reinterpret_cast<hipStream_t>(stream),
+                     reinterpret_cast<const OPlan*>(base + lay.plan), reinterpret_cast<const OLevel*>(base + lay.levels),
+                     reinterpret_cast<unsigned*>(base + lay.state), reinterpret_cast<unsigned long long*>(base + lay.counters),
+                     reinterpret_cast<unsigned*>(base + lay.flags), reinterpret_cast<unsigned long long*>(base + lay.partials),
+                     reinterpret_cast<unsigned*>(base + lay.arrivals));
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PWG_ERR_HIP, "persistent step launch: %s", hipGetErrorString(e));
+  return PWG_OK;
+}
+
+int step_ordered_status(const pwg_step_desc* d, void* stream) {
+  const OLayout lay = layout_of(d);
+  unsigned s = 0;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(&s, ws_base(d) + lay.state + 4 * kStateStatus, 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(PWG_ERR_HIP, "pwg_step_status: %s", hipGetErrorString(e));
+  if (s == kStatusTimeout) return fail(PWG_ERR_HIP, "persistent step: a level barrier timed out (re-plan the step)");
+  return PWG_OK;
+}
+
+}  // namespace pwg

@@ -182,12 +182,19 @@ class ChainStep:
 
 def make_chained(wl: StepWorkload, schedule: int = SCHEDULE_LEVELS, head_dim: int = synth.HEAD_DIM,
                  eps: float = 1e-6, workload: int = synth.W_STEP) -> ChainStep:
-    """Chained step on the row-major weights of `wl` (levels qkv, o, gate_up,
-    down per layer).  The query rows are o's input width; the key and value
-    rows split the rest of qkv equally."""
+    """Chained step on the weights of `wl` (levels qkv, o, gate_up, down per
+    layer) in the arrangement `schedule` takes (tiled copies are made on the
+    device when `wl` holds only the row-major blobs).  The query rows are o's
+    input width; the key and value rows split the rest of qkv equally."""
     d0 = wl.desc
     dev = d0.out_scale.device
-    ws_rows, out_rows = wl.weights[LAYOUT_ROWS]
+    layout = layout_for_schedule(schedule)
+    if layout not in wl.weights:
+        rws, rout = wl.weights[LAYOUT_ROWS]
+        tws = [tile_rows(w, lv[4], lv[5] // 4) for w, lv in zip(rws, d0.levels)]
+        wl.weights[layout] = (tws, tile_rows(rout, rout.shape[0], rout.shape[1]))
+        torch.cuda.synchronize(dev)
+    ws_rows, out_rows = wl.weights[layout]
     hidden = d0.hidden
     n_layers = len(d0.levels) // 4
     f32 = dict(dtype=torch.float32, device=dev)
@@ -228,7 +235,7 @@ def make_chained(wl: StepWorkload, schedule: int = SCHEDULE_LEVELS, head_dim: in
         token_out=None, emb_row_out=torch.empty(hidden, dtype=torch.int8, device=dev),
         emb_scale_out=torch.empty(4, **f32), emb_deq_out=torch.empty(hidden, **f32),
         logits_out=torch.empty(d0.vocab, **f32) if d0.logits_out is not None else None,
-        schedule=schedule, weight_layout=LAYOUT_ROWS, vocab=d0.vocab, hidden=hidden,
+        schedule=schedule, weight_layout=layout, vocab=d0.vocab, hidden=hidden,
         h_in=InputOp(INPUT_RMSNORM, src=prev_down, resid=prev_mid, gamma=torch.from_numpy(gf).to(dev),
                      resid_out=h_final, eps=eps))
     desc.token_out = desc.token_in

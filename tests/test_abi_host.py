@@ -189,8 +189,8 @@ def test_step_argument_errors():
 
 
 def test_step_layout_errors():
-    """Each schedule takes one weight arrangement; the stream schedule also
-    needs widths that are multiples of 256 and at most 12288."""
+    """Each schedule takes one weight arrangement; the stream and persistent
+    schedules also need widths that are multiples of 256 and at most 12288."""
     d = pwg._StepDesc()
     d.vocab, d.hidden = 1000, 4096
     for name in ("out_table", "out_scale", "h", "emb_table", "emb_scale", "token_in", "token_out",
@@ -202,8 +202,17 @@ def test_step_layout_errors():
     assert pwg._step(C.byref(d), None) == ERR_ARG and "layout" in pwg.last_error()
     d.schedule, d.weight_layout = pwg.SCHEDULE_STREAM, pwg.LAYOUT_ROWS
     assert pwg._step(C.byref(d), None) == ERR_UNSUPPORTED
-    d.schedule, d.weight_layout = pwg.SCHEDULE_PERSISTENT, pwg.LAYOUT_TILED
+    d.schedule, d.weight_layout = pwg.SCHEDULE_PERSISTENT, pwg.LAYOUT_ROWS
     assert pwg._step(C.byref(d), None) == ERR_UNSUPPORTED
+    d.weight_layout = pwg.LAYOUT_TILED
+    d.workspace_bytes = pwg._step_ws(C.byref(d))
+    assert d.workspace_bytes > 0
+    lv[0] = pwg.Level(A, A, A, A, 64, 4160)            # not a multiple of 256
+    assert pwg._step(C.byref(d), None) == ERR_UNSUPPORTED and "256" in pwg.last_error()
+    lv[0] = pwg.Level(A, A, A, A, 64, 4096)
+    d.batch = 4                                        # the persistent step is batch 1 only
+    assert pwg._step(C.byref(d), None) == ERR_UNSUPPORTED
+    d.batch = 0
     d.schedule, d.weight_layout = pwg.SCHEDULE_STREAM, pwg.LAYOUT_TILED
     d.workspace_bytes = pwg._step_ws(C.byref(d))
     assert d.workspace_bytes > 0

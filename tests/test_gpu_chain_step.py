@@ -40,8 +40,8 @@ CHAIN_REL_L2 = 1e-4
 # 4 query heads over 1 key/value head of 128, or 8 over 2 of 64
 CHAIN_SMALL = {"q": (512, 512), "k": (128, 512), "v": (128, 512), "o": (512, 512),
                "gate": (1536, 512), "up": (1536, 512), "down": (512, 1536)}
-SCHEDULES = [pwg.SCHEDULE_LEVELS]
-SCHED_IDS = ["levels"]
+SCHEDULES = [pwg.SCHEDULE_LEVELS, pwg.SCHEDULE_PERSISTENT]
+SCHED_IDS = ["levels", "persistent"]
 
 
 def run(cs):

@@ -56,10 +56,10 @@ def check_against_oracle(wl, out, token_in, full_levels):
     assert np.array_equal(out["emb_deq"], ed[0])
 
 
-SCHEDULES = [pwg.SCHEDULE_LEVELS, pwg.SCHEDULE_STREAM]
-SCHED_IDS = ["levels", "stream"]
-ORDERED = [pwg.SCHEDULE_LEVELS]
-ORDERED_IDS = ["levels"]
+SCHEDULES = [pwg.SCHEDULE_LEVELS, pwg.SCHEDULE_STREAM, pwg.SCHEDULE_PERSISTENT]
+SCHED_IDS = ["levels", "stream", "persistent"]
+ORDERED = [pwg.SCHEDULE_LEVELS, pwg.SCHEDULE_PERSISTENT]
+ORDERED_IDS = ["levels", "persistent"]
 
 
 @pytest.mark.parametrize("schedule", SCHEDULES, ids=SCHED_IDS)
@@ -179,7 +179,7 @@ def chain_levels(wl):
     for i in range(1, len(lv)):
         lv[i][2] = lv[i - 1][3][: lv[i][5]]
     d.levels = [tuple(t) for t in lv]
-    d.h = lv[-1][3][: d.out_table.shape[1]]
+    d.h = lv[-1][3][: d.hidden]
     d._c = None
     return lv[0][2]
 
