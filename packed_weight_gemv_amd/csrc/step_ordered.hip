@@ -70,9 +70,18 @@ constexpr size_t kRegionBytes = 80256;  // ternary operands of 12,288 columns (i
 static_assert(kRegionBytes >= ops::ternary_region_bytes(kMaxCols) && kRegionBytes >= ops::int8_region_bytes(kMaxCols),
               "operand region");
 constexpr size_t kSlotsBytes = static_cast<size_t>(kMaxBlk) * kCompute * 64;
-constexpr size_t kMiscBytes = 256;
+constexpr int kMaxSlice = 256;           // formed values one workgroup writes back
+constexpr int kMaxNormCols = 9984;       // RMSNORM: source and gain staged in the operand region
+constexpr size_t kLevelBytes = 96;       // one level descriptor (OLevel)
+// red[16], wkeys[8], hsave[kMaxSlice], two level descriptors
+constexpr size_t kMiscBytes = 128 + 4 * kMaxSlice + 2 * kLevelBytes;
 constexpr size_t kLds = kStageBytes + kRegionBytes + kSlotsBytes + kMiscBytes;
 static_assert(kLds > 80 * 1024 && kLds <= 160 * 1024, "one resident workgroup per CU");
+// formation staging in the operand region: two float rows, or an int8 row
+// (rounded to KiB) and a float row
+static_assert(kRegionBytes >= 4 * kMaxCols && kRegionBytes >= (kMaxCols + 1023) / 1024 * 1024 + 4 * kMaxCols &&
+                  kRegionBytes >= 8 * kMaxNormCols,
+              "formation staging");
 
 struct OLevel {
   const unsigned char* w;  // tiled T2
@@ -82,6 +91,8 @@ struct OLevel {
   int rows, cols, T, nb;   // T = cols / 256 tiles per block, nb = 16-row blocks
   chain::DevInput in;
 };
+
+static_assert(sizeof(OLevel) == kLevelBytes && kLevelBytes % 4 == 0, "level descriptor size");
 
 struct alignas(256) OPlan {
   unsigned n_levels, n_barriers, grid, mode;
@@ -207,22 +218,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* base, 
 }
 constexpr unsigned kOff = 0x80000000u;  // past every resource: the load returns zero and moves nothing
 
-// Tiles [s, e) of a block-major sequence of 1 KiB tiles (T per block, first
-// block b0 of a matrix of nb blocks): this lane's 16 bytes of tile s + j go
-// to r[j]; the slots past e read nothing.
-__device__ __forceinline__ void load_tiles(u32x4 (&r)[kMaxT], const unsigned char* w, int nb, int T, int b0, int s,
-                                           int e) {
-  const __amdgpu_buffer_rsrc_t rs = buffer_over(w, static_cast<unsigned>(nb) * static_cast<unsigned>(T) * 1024u);
-  const unsigned lane = threadIdx.x & 63u;
-  int blk = s / T, t = s - blk * T;
+// Tiles [s, e) (e - s <= kMaxT) of a block-major sequence of 1 KiB tiles (T
+// per block, first block b0): consecutive tiles of the sequence are
+// consecutive KiB of the arrangement, so this lane's 16 bytes of tile s + j
+// are at KiB b0 T + s + j, byte 16 lane.  The resource ends after tile e - 1:
+// the slots past it read zeros and move nothing.  Every slot's load is
+// issued, so the compiler can count them.
+__device__ __forceinline__ void load_tiles(u32x4 (&r)[kMaxT], const unsigned char* w, int T, int b0, int s, int e) {
+  const long first = static_cast<long>(b0) * T + s;
+  const __amdgpu_buffer_rsrc_t rs = buffer_over(w + first * 1024, e > s ? static_cast<unsigned>(e - s) * 1024u : 0u);
+  const unsigned off = 16u * (threadIdx.x & 63u);
 #pragma unroll
-  for (int j = 0; j < kMaxT; ++j) {
-    const unsigned off = s + j < e ? static_cast<unsigned>(((b0 + blk) * T + t) * 1024) + 16u * lane : kOff;
-    r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2));
-    const int wrap = t + 1 == T;  // selects, not branches: the loads stay in one basic block
-    t = wrap ? 0 : t + 1;
-    blk += wrap;
-  }
+  for (int j = 0; j < kMaxT; ++j)
+    r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 1024u * j, 0, 2));
+}
+
+// The same for a prefetch whose registers are not read until every load of
+// the wave has completed: only the tiles that exist are loaded (a load
+// past the end still costs the wave an address-unit slot).
+__device__ __forceinline__ void prefetch_tiles(u32x4 (&r)[kMaxT], const unsigned char* w, int T, int b0, int s, int e) {
+  const long first = static_cast<long>(b0) * T + s;
+  const int n = e - s;
+  const __amdgpu_buffer_rsrc_t rs = buffer_over(w + first * 1024, n > 0 ? static_cast<unsigned>(n) * 1024u : 0u);
+  const unsigned off = 16u * (threadIdx.x & 63u);
+#pragma unroll
+  for (int j = 0; j < kMaxT; ++j)
+    if (j < n) r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 1024u * j, 0, 2));
 }
 
 // Ternary tiles [s, e) (at most kMaxT, the ones in r) of a compute wave's
@@ -360,9 +381,209 @@ __device__ __noinline__ unsigned long long int8_tiles_any(const OPlan& P, int T,
   return best_idx == 0xFFFFFFFFu ? 0ull : argmax_key(best, best_idx);  // this lane's (max, lowest row)
 }
 
-// Converts the formed input in `stage` (cols values) into the ternary
-// operand region: four threads per 32-value block, one summation group each.
-__device__ __forceinline__ void convert_ternary(const float* stage, int cols, unsigned char* region) {
+// A level descriptor held in LDS, read as wave-uniform (scalar) values.
+__device__ __forceinline__ OLevel uni_level(const OLevel* p) {
+  constexpr int kDw = static_cast<int>(kLevelBytes / 4);
+  int w[kDw];
+  __builtin_memcpy(w, p, kLevelBytes);
+#pragma unroll
+  for (int i = 0; i < kDw; ++i) w[i] = __builtin_amdgcn_readfirstlane(w[i]);
+  OLevel o;
+  __builtin_memcpy(&o, w, kLevelBytes);
+  return o;
+}
+
+// ------------------------------------------------------------ formation
+// A level's input is formed in three steps: the control wave copies its
+// sources into LDS with device-coherent loads (no registers, one memory round
+// trip; the sources that do not depend on the previous level are copied
+// before its barrier), every thread then forms the values element by element
+// (the norm's sum of squares, SwiGLU), and every thread converts the result
+// into the matrix-core operand region.  The arithmetic is chain_input.h's:
+// same element order, same reductions.
+constexpr int kSc1 = 16;  // cache-policy bits of a device-coherent (SC1) load
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// LDS-destination load: lane l's 16 bytes at byte `off` of rs go to lds + 16 l.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, unsigned off, unsigned char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)lds, 16, off, 0, 0, kSc1);
+}
+
+// One wave copies bytes [0, bytes) of p to LDS at dst, 1 KiB per instruction
+// (lanes past the end read zeros).
+__device__ __forceinline__ void lds_copy(const void* p, unsigned bytes, unsigned char* dst) {
+  const __amdgpu_buffer_rsrc_t rs = buffer_over(p, bytes);
+  const unsigned lane = threadIdx.x & 63u;
+  for (unsigned o = 0; o < bytes; o += 1024u) lds_load16(rs, o + 16u * lane, dst + o);
+}
+
+__device__ __forceinline__ bool is_norm(int op) { return op == PWG_INPUT_RMSNORM || op == PWG_INPUT_EMBED_RMSNORM; }
+__device__ __forceinline__ int embed_gamma_off(int n) { return (n + 1023) / 1024 * 1024; }
+
+// LDS use while forming (raw = the operand region, free until conversion):
+//   GIVEN          x -> stage
+//   RMSNORM        resid -> stage, src -> raw[0, n), gamma -> raw[n, 2n)
+//                  (n <= kMaxNormCols)
+//   EMBED_RMSNORM  int8 row -> raw bytes [0, n), gamma -> raw bytes from
+//                  embed_gamma_off(n) (past the row copy's last KiB)
+//   ATTN1          gathered value rows -> stage
+//   SWIGLU         gate -> raw[0, n), up -> stage
+// Control wave, any time after the previous level's operands were used: the
+// sources that are constant in the launch.
+__device__ __forceinline__ void issue_static_sources(const chain::DevInput& in, int n, unsigned char* raw,
+                                                     const chain::EmbedSrc& e, float* red) {
+  const unsigned nb = static_cast<unsigned>(n) * 4u;
+  if (in.op == PWG_INPUT_RMSNORM) lds_copy(in.gamma, nb, raw + nb);
+  if (in.op == PWG_INPUT_EMBED_RMSNORM) {
+    const int id = *e.token_in;
+    const bool valid = id >= 0 && id < e.vocab;
+    if (valid) lds_copy(e.table + static_cast<long>(id) * n, static_cast<unsigned>(n), raw);
+    lds_copy(in.gamma, nb, raw + embed_gamma_off(n));
+    if ((threadIdx.x & 63u) == 0) {
+      red[12] = valid ? e.scale[id] : 0.f;
+      red[13] = valid ? 1.f : 0.f;
+    }
+  }
+}
+
+// Control wave, after the previous level's barrier: the sources written
+// earlier in this launch.
+__device__ __forceinline__ void issue_dynamic_sources(const chain::DevInput& in, int n, const float* x, float* stage,
+                                                      unsigned char* raw) {
+  const unsigned nb = static_cast<unsigned>(n) * 4u;
+  unsigned char* st = reinterpret_cast<unsigned char*>(stage);
+  if (in.op == PWG_INPUT_GIVEN) {
+    lds_copy(x, nb, st);
+  } else if (in.op == PWG_INPUT_RMSNORM) {
+    lds_copy(in.resid, nb, st);
+    if (in.src) lds_copy(in.src, nb, raw);
+  } else if (in.op == PWG_INPUT_SWIGLU) {
+    lds_copy(in.src, nb, raw);
+    lds_copy(in.src + n, nb, st);
+  } else if (in.op == PWG_INPUT_ATTN1) {
+    // element i is value element i % head_dim of key/value head i / span;
+    // a lane's 4 elements lie in one head (head_dim is a multiple of 4)
+    const int span = in.head_dim * in.group;
+    const unsigned src_bytes = static_cast<unsigned>(((n - 1) / span + 1) * in.head_dim) * 4u;
+    const __amdgpu_buffer_rsrc_t rs = buffer_over(in.src, src_bytes);
+    const int lane = static_cast<int>(threadIdx.x & 63u);
+    for (int i0 = 0; i0 < n; i0 += 256) {
+      const int i = i0 + 4 * lane;
+      lds_load16(rs, static_cast<unsigned>((i / span) * in.head_dim + i % in.head_dim) * 4u, st + 4 * i0);
+    }
+  }
+}
+
+// Element-wise formation by every thread: element i = base + kThreads u +
+// tid, kU per thread per round, every LDS read of a round issued before the
+// first use, indices clamped so that the reads need no branch.
+constexpr int kU = 8;
+
+__device__ __forceinline__ void form_swiglu(int n, float* stage, const float* gate) {
+  const int tid = static_cast<int>(threadIdx.x);
+  for (int base = 0; base < n; base += kU * kThreads) {
+    float g[kU], up[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = min(base + u * kThreads + tid, n - 1);
+      g[u] = gate[i];
+      up[u] = stage[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      // silu(g) = g * sigmoid(g), sigmoid from e^-|g| (no overflow)
+      const float gv = g[u], ez = expf(-fabsf(gv));
+      const float sig = gv >= 0.f ? 1.0f / (1.0f + ez) : ez / (1.0f + ez);
+      const float v = gv * sig * up[u];
+      const int i = base + u * kThreads + tid;
+      if (i < n) stage[i] = v;
+    }
+  }
+}
+
+// RMSNORM (kEmbed: of the embedding row q * s, else of resid + src): gamma *
+// h to stage, h of elements [s0, s1) to hsave, and the thread's sum of
+// squares (elements past n add 0), in chain_input.h's order.
+template <bool kEmbed, bool kSrc>
+__device__ __forceinline__ float form_norm(int n, float* stage, const float* src, const int8_t* q, float s,
+                                           const float* gamma, float* hsave, int s0, int s1) {
+  const int tid = static_cast<int>(threadIdx.x);
+  float acc = 0.f;
+  for (int base = 0; base < n; base += kU * kThreads) {
+    float h[kU], gm[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = min(base + u * kThreads + tid, n - 1);
+      if (kEmbed) h[u] = static_cast<float>(q[i]) * s;
+      else h[u] = kSrc ? stage[i] + src[i] : stage[i];
+      gm[u] = gamma[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = base + u * kThreads + tid;
+      const float hv = i < n ? h[u] : 0.f;
+      if (i < n) stage[i] = gm[u] * hv;
+      if (static_cast<unsigned>(i - s0) < static_cast<unsigned>(s1 - s0)) hsave[i - s0] = hv;
+      acc = fmaf(hv, hv, acc);
+    }
+  }
+  return acc;
+}
+
+// Every thread: the formed input (before the norm's scale) in stage, the
+// waves' sums of squares in red[0, 8) (norm ops) and the residual-stream
+// values of elements [s0, s1) in hsave.  EMBED_RMSNORM: red[12] holds the
+// row's scale and red[13] whether the token id was valid.  True when it
+// wrote LDS.
+__device__ __forceinline__ bool form_elementwise(const chain::DevInput& in, int n, float* stage,
+                                                 const unsigned char* raw, float* red, float* hsave, int s0, int s1) {
+  const float* rawf = reinterpret_cast<const float*>(raw);
+  if (in.op == PWG_INPUT_SWIGLU) {
+    form_swiglu(n, stage, rawf);
+    return true;
+  }
+  if (!is_norm(in.op)) return false;
+  float acc;
+  if (in.op == PWG_INPUT_EMBED_RMSNORM) {
+    // an invalid id gathers a zero row (scale 0)
+    const float s = red[13] != 0.f ? red[12] : 0.f;
+    acc = form_norm<true, false>(n, stage, nullptr, reinterpret_cast<const int8_t*>(raw), s,
+                                 reinterpret_cast<const float*>(raw + embed_gamma_off(n)), hsave, s0, s1);
+  } else if (in.src) {
+    acc = form_norm<false, true>(n, stage, rawf, nullptr, 0.f, rawf + n, hsave, s0, s1);
+  } else {
+    acc = form_norm<false, false>(n, stage, nullptr, nullptr, 0.f, rawf + n, hsave, s0, s1);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+  if ((threadIdx.x & 63u) == 0) red[threadIdx.x >> 6] = acc;
+  return true;
+}
+
+// The norm's scale 1 / sqrt(mean + eps) from the waves' sums (fixed order),
+// or 1 for the other ops.
+__device__ __forceinline__ float norm_scale(const chain::DevInput& in, int n, const float* red) {
+  if (!is_norm(in.op)) return 1.f;
+  float sum = 0.f;
+  for (int w = 0; w < kWaves; ++w) sum += red[w];
+  return 1.0f / sqrtf(sum / static_cast<float>(n) + in.eps);
+}
+
+// Control wave: the formed input's elements [s0, s1) to x and, for the norm
+// ops, the residual-stream values to resid_out (device scope).
+__device__ __forceinline__ void store_slice(const chain::DevInput& in, const float* stage, const float* hsave,
+                                            float inv, float* x, int s0, int s1) {
+  if (in.op == PWG_INPUT_GIVEN) return;
+  const bool norm = is_norm(in.op) && in.resid_out;
+  for (int i = s0 + static_cast<int>(threadIdx.x & 63u); i < s1; i += 64) {
+    __hip_atomic_store(&x[i], stage[i] * inv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (norm) __hip_atomic_store(&in.resid_out[i], hsave[i - s0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Converts stage * sc (cols values) into the ternary operand region: four
+// threads per 32-value block, one summation group each.
+__device__ __forceinline__ void convert_ternary(const float* stage, int cols, unsigned char* region, float sc) {
   const int T = cols >> 8;
   const size_t mf = static_cast<size_t>(2 * T);
   const size_t bsc = ops::operand_bsc_off(mf), asc = ops::operand_asc_off(mf);
@@ -372,27 +593,33 @@ __device__ __forceinline__ void convert_ternary(const float* stage, int cols, un
     const bool in = tid < T * 32;
     float xs[16];
     float amax = 0.f;
+    const float4* src = reinterpret_cast<const float4*>(stage + 32 * (in ? beta : 0) + 16 * h);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      xs[i] = in ? stage[32 * beta + 16 * h + i] : 0.f;
-      amax = fmaxf(amax, fabsf(xs[i]));
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = src[q];
+      xs[4 * q + 0] = in ? v.x * sc : 0.f;
+      xs[4 * q + 1] = in ? v.y * sc : 0.f;
+      xs[4 * q + 2] = in ? v.z * sc : 0.f;
+      xs[4 * q + 3] = in ? v.w * sc : 0.f;
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xs[i]));
     amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));  // the other half of the block
     if (in) ops::write_ternary_quarter(region, bsc, asc, beta, h, G, xs, ops::block_exponent(amax));
   }
 }
 
-// Converts h (stage, hidden values) into the int8 operand region: one wave
+// Converts stage * sc (hidden values) into the int8 operand region: one wave
 // per 256-value section, lane t owning values 4t .. 4t + 3.
-__device__ __forceinline__ void convert_int8(const float* stage, int hidden, unsigned char* region) {
+__device__ __forceinline__ void convert_int8(const float* stage, int hidden, unsigned char* region, float sc) {
   const unsigned lane = threadIdx.x & 63u;
   const int exp_off = static_cast<int>(ops::int8_exp_off(hidden));
   for (int sec = static_cast<int>(threadIdx.x >> 6); sec < hidden / 256; sec += kWaves) {
-    const float* v = stage + 256 * sec + 4 * lane;
-    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    const float4 v4 = *reinterpret_cast<const float4*>(stage + 256 * sec + 4 * lane);
+    const float hv[4] = {v4.x * sc, v4.y * sc, v4.z * sc, v4.w * sc};
+    float amax = fmaxf(fmaxf(fabsf(hv[0]), fabsf(hv[1])), fmaxf(fabsf(hv[2]), fabsf(hv[3])));
     for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
     const int e = ops::block_exponent(amax);
-    const float hv[4] = {v[0], v[1], v[2], v[3]};
     unsigned dw[ops::kInt8Digits];
     ops::int8_digits4(hv, e, dw);
     const int m = 4 * sec + static_cast<int>(lane >> 4), g = static_cast<int>((lane & 15u) >> 2),
@@ -401,22 +628,6 @@ __device__ __forceinline__ void convert_int8(const float* stage, int hidden, uns
     for (int d = 0; d < ops::kInt8Digits; ++d)
       *reinterpret_cast<unsigned*>(region + m * ops::kInt8MfmaBytes + ops::int8_b_entry(d, g) + j0) = dw[d];
     if (lane == 0) *reinterpret_cast<int*>(region + exp_off + 4 * sec) = e - ops::kInt8FixedBits;
-  }
-}
-
-// The input of level `li` (li == n_levels: h) in `stage`, by every thread.
-__device__ __forceinline__ void form_level_input(const OPlan& P, const OLevel* levels, unsigned li, float* stage,
-                                                 float* red, const chain::EmbedSrc& emb) {
-  const bool vocab = li == P.n_levels;
-  const chain::DevInput& in = vocab ? P.h_in : levels[li].in;
-  const int n = vocab ? P.hidden : levels[li].cols;
-  if (in.op == PWG_INPUT_GIVEN) {  // a given input may be an earlier level's output: device-scope loads
-    const float* x = vocab ? P.h : levels[li].x;
-    for (int i = static_cast<int>(threadIdx.x); i < n; i += kThreads)
-      stage[i] = __hip_atomic_load(x + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-  } else {
-    chain::form_input<kThreads, true>(in, n, stage, red, emb, 0, n);
   }
 }
 
@@ -451,6 +662,8 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
   float* slots = reinterpret_cast<float*>(smem + kStageBytes + kRegionBytes);
   float* red = reinterpret_cast<float*>(smem + kStageBytes + kRegionBytes + kSlotsBytes);
   unsigned long long* wkeys = reinterpret_cast<unsigned long long*>(red + 16);
+  float* hsave = red + 32;
+  OLevel* ring = reinterpret_cast<OLevel*>(hsave + kMaxSlice);  // descriptors of levels li & 1
 
   const OPlan& P = *plan;
   const unsigned lane = threadIdx.x & 63u;
@@ -461,91 +674,135 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
   Barrier bar{plan, state, counters, flags, xcc_id(), 0};
   bar.base = ld_sc(&state[kStateGen]) * P.n_barriers;
   const chain::EmbedSrc emb{P.emb_table, P.emb_scale, P.token_in, static_cast<long>(P.vocab)};
+  constexpr int kDw = static_cast<int>(kLevelBytes / 4);
 
-  // rows of level li owned by this workgroup: blocks [b0, b1)
-  auto wg_blocks = [&](unsigned li, int& b0, int& b1) {
-    const int nb = li < nl ? uni(levels[li].nb) : (P.vocab + 15) / 16;
+  // 16-row blocks [b0, b1) of a matrix of nb blocks owned by this workgroup
+  auto wg_blocks = [&](int nb, int& b0, int& b1) {
     b0 = static_cast<int>(static_cast<long>(wg) * nb / G);
     b1 = static_cast<int>(static_cast<long>(wg + 1) * nb / G);
   };
-  // tiles of level li (li == nl: the vocabulary's first kMaxT; past it:
-  // none) for this compute wave.  The parameters are chosen first and the
-  // loads issued from one place, so the compiler counts them and the compute
-  // that follows waits only for the tiles it uses.
-  auto prefetch = [&](u32x4 (&r)[kMaxT], unsigned li) {
+  // elements of a formed input of n values this workgroup writes back
+  auto wg_slice = [&](int n, int& s0, int& s1) {
+    s0 = static_cast<int>(static_cast<long>(wg) * n / G);
+    s1 = static_cast<int>(static_cast<long>(wg + 1) * n / G);
+  };
+  // tiles of level li (descriptor L; li == nl: the vocabulary's first kMaxT;
+  // past it: none) for this compute wave; every load of the wave completes
+  // before they are read
+  auto prefetch = [&](u32x4 (&r)[kMaxT], unsigned li, const OLevel& L) {
     int b0 = 0, b1 = 0, s = 0, e = 0, nb = 1, T = 1;
     const unsigned char* w = P.out_table;
-    if (li <= nl) wg_blocks(li, b0, b1);
     if (li < nl) {
-      const OLevel& L = levels[li];
-      w = uni_ptr(L.w);
-      nb = uni(L.nb);
-      T = uni(L.T);
+      w = L.w;
+      nb = L.nb;
+      T = L.T;
+      wg_blocks(nb, b0, b1);
       wave_range(b1 - b0, T, k, s, e);
     } else if (li == nl) {
       T = P.hidden / 64;
       nb = (P.vocab + 15) / 16;
+      wg_blocks(nb, b0, b1);
       const int w0 = b0 + k * (b1 - b0) / kCompute, w1 = b0 + (k + 1) * (b1 - b0) / kCompute;
       b0 = w0;
       e = (w1 - w0) * T;
     }
-    load_tiles(r, w, nb, T, b0, s, e < s + kMaxT ? e : s + kMaxT);
+    prefetch_tiles(r, w, T, b0, s, e < s + kMaxT ? e : s + kMaxT);
+  };
+  // control wave: the row scales of a level (lane + 64 j of the workgroup's rows)
+  float rsc[4] = {0.f, 0.f, 0.f, 0.f};
+  auto load_scales = [&](const OLevel& L) {
+    int b0, b1;
+    wg_blocks(L.nb, b0, b1);
+    const __amdgpu_buffer_rsrc_t rs = buffer_over(L.scale, static_cast<unsigned>(L.rows) * 4u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rr = static_cast<int>(lane) + 64 * j, row = b0 * 16 + rr;
+      const unsigned off = rr < (b1 - b0) * 16 && row < L.rows ? static_cast<unsigned>(row) * 4u : kOff;
+      rsc[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+    }
   };
 
   u32x4 ra[kMaxT], rb[kMaxT];
   if (wave == 0) {
     if (wg == 0) embed_outputs(P);
+    if (nl > 0 && lane < kDw)  // level 0's descriptor
+      reinterpret_cast<int*>(ring)[lane] = reinterpret_cast<const int*>(levels)[lane];
   } else {
-    prefetch(ra, 0);
+    prefetch(ra, 0, levels[0]);
   }
 
-  // One level: its tiles are in `cur` (loaded a level earlier), the next
-  // level's go into `nxt` before the compute.
-  auto level = [&](unsigned li, u32x4(&cur)[kMaxT], u32x4(&nxt)[kMaxT]) -> bool {
-    if (li > 0) {
+  // The sources of level li's input (li == nl: h) in LDS, after the previous
+  // level's barrier, and level li + 1's descriptor in the ring; true
+  // (uniform) when the wait timed out.
+  auto gather = [&](unsigned li) -> bool {
+    const bool vocab = li == nl;
+    if (wave == 0) {
+      const OLevel L = vocab ? OLevel{} : uni_level(&ring[li & 1]);
+      const chain::DevInput in = vocab ? P.h_in : L.in;
+      const int n = vocab ? P.hidden : L.cols;
+      int next_dw = 0;
+      if (li + 1 < nl && lane < kDw) next_dw = reinterpret_cast<const int*>(levels + li + 1)[lane];
+      if (!vocab) load_scales(L);
+      issue_static_sources(in, n, region, emb, red);
       bool late = false;
-      if (wave == 0) late = bar.wait(li - 1);
-      if (wave == 0 && lane == 0) red[15] = late ? 1.f : 0.f;
-      __syncthreads();
-      if (red[15] != 0.f) return true;
+      if (li > 0) late = bar.wait(li - 1);
+      if (!late) issue_dynamic_sources(in, n, vocab ? P.h : L.x, stage, region);
+      if (li + 1 < nl && lane < kDw) reinterpret_cast<int*>(&ring[(li + 1) & 1])[lane] = next_dw;
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the sources are in LDS
+      if (lane == 0) red[15] = late ? 1.f : 0.f;
     }
-    const OLevel& L = levels[li];
-    const int T = uni(L.T), cols = uni(L.cols), rows = uni(L.rows);
-    int b0, b1;
-    wg_blocks(li, b0, b1);
-    form_level_input(P, levels, li, stage, red, emb);
-    convert_ternary(stage, cols, region);
-    if (wave == 0 && L.in.op != PWG_INPUT_GIVEN)
-      chain::store_formed<true>(L.in, cols, stage, const_cast<float*>(L.x), emb,
-                                static_cast<int>(static_cast<long>(wg) * cols / G),
-                                static_cast<int>(static_cast<long>(wg + 1) * cols / G), static_cast<int>(lane), 64);
+    __syncthreads();
+    return red[15] != 0.f;
+  };
+
+  // One level: its tiles are in `cur` (loaded during the previous level's
+  // conversion and products); the next level's go into `nxt` as soon as this
+  // level's sources are in LDS, so the weight stream overlaps the conversion
+  // and the products and stays off the paths of the level's inputs and
+  // outputs.
+  auto level = [&](unsigned li, u32x4(&cur)[kMaxT], u32x4(&nxt)[kMaxT]) -> bool {
+    if (gather(li)) return true;
+    const OLevel L = uni_level(&ring[li & 1]);
+    const int T = L.T, cols = L.cols, rows = L.rows;
+    int b0, b1, s0, s1;
+    wg_blocks(L.nb, b0, b1);
+    wg_slice(cols, s0, s1);
+    // every earlier load (this level's tiles) has completed; saying so on
+    // every path lets the compiler count the prefetch below instead of
+    // draining it before the products
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    if (wave > 0) {
+      const OLevel Ln = uni_level(&ring[(li + 1) & 1]);  // not read past the last level
+      prefetch(nxt, li + 1, Ln);
+    }
+    if (form_elementwise(L.in, cols, stage, region, red, hsave, s0, s1)) __syncthreads();
+    const float inv = norm_scale(L.in, cols, red);
+    convert_ternary(stage, cols, region, inv);
     __syncthreads();  // the operand region is complete
     if (wave > 0) {
-      // every load issued so far has completed (the formation waited for
-      // its own, issued after this level's tiles); saying so lets the
-      // compiler count the prefetch below instead of draining it
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      prefetch(nxt, li + 1);
       int s, e;
       wave_range(b1 - b0, T, k, s, e);
       const size_t mf = static_cast<size_t>(2 * T);
       const int bsc = static_cast<int>(ops::operand_bsc_off(mf)), asc = static_cast<int>(ops::operand_asc_off(mf));
       v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-      // the first round's tiles arrived before the formation; rounds past it
-      // (levels wider than 7 x kMaxT tiles per workgroup) load on demand
+      // rounds past the first (levels wider than 7 x kMaxT tiles per
+      // workgroup) load on demand
       ternary_tiles(cur, T, s, e < s + kMaxT ? e : s + kMaxT, e, region, bsc, asc, slots, k, acc0, acc1);
       for (int r0 = s + kMaxT; r0 < e; r0 += kMaxT) {
-        load_tiles(cur, uni_ptr(L.w), uni(L.nb), T, b0, r0, e < r0 + kMaxT ? e : r0 + kMaxT);
+        load_tiles(cur, L.w, T, b0, r0, e < r0 + kMaxT ? e : r0 + kMaxT);
         ternary_tiles(cur, T, r0, e < r0 + kMaxT ? e : r0 + kMaxT, e, region, bsc, asc, slots, k, acc0, acc1);
       }
+    } else {
+      store_slice(L.in, stage, hsave, inv, const_cast<float*>(L.x), s0, s1);
     }
     __syncthreads();  // every slot of the level is written
     if (wave == 0) {
       // rows of the workgroup: block bl's sum over the compute waves that
       // touched it, in wave order
       const int nrow = (b1 - b0) * 16;
-      for (int r0 = 0; r0 < nrow; r0 += 64) {
-        const int rr = r0 + static_cast<int>(lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = static_cast<int>(lane) + 64 * j;
         if (rr < nrow) {
           const int bl = rr >> 4, i = rr & 15;
           float v = 0.f;
@@ -555,7 +812,7 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
             if (s < e && s < (bl + 1) * T && e > bl * T) v += slots[(bl * kCompute + kk) * 16 + i];
           }
           const long row = static_cast<long>(b0 + bl) * 16 + i;
-          if (row < rows) __hip_atomic_store(&L.y[row], v * L.scale[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (row < rows) __hip_atomic_store(&L.y[row], v * rsc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
       bar.arrive(li);
@@ -568,31 +825,27 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
     if (level(li, ra, rb)) return;
     if (li + 1 < nl && level(li + 1, rb, ra)) return;
   }
-  const bool vocab_in_a = (nl & 1u) == 0;  // the vocabulary's first tiles: prefetched into ra for even nl
+  const bool vocab_in_a = (nl & 1u) == 0;  // the vocabulary's first round: prefetched into ra for even nl
 
   // Output projection: h formed after the last level, then every compute
-  // wave streams its whole vocabulary blocks through both buffers.
-  if (nl > 0) {
-    bool late = false;
-    if (wave == 0) late = bar.wait(nl - 1);
-    if (wave == 0 && lane == 0) red[15] = late ? 1.f : 0.f;
+  // wave streams its whole vocabulary blocks through both register buffers.
+  if (gather(nl)) return;
+  {
+    int s0, s1;
+    wg_slice(P.hidden, s0, s1);
+    if (form_elementwise(P.h_in, P.hidden, stage, region, red, hsave, s0, s1)) __syncthreads();
+    const float inv = norm_scale(P.h_in, P.hidden, red);
+    convert_int8(stage, P.hidden, region, inv);
     __syncthreads();
-    if (red[15] != 0.f) return;
+    if (wave == 0) store_slice(P.h_in, stage, hsave, inv, const_cast<float*>(P.h), s0, s1);
   }
-  form_level_input(P, levels, nl, stage, red, emb);
-  convert_int8(stage, P.hidden, region);
-  if (wave == 0 && P.h_in.op != PWG_INPUT_GIVEN)
-    chain::store_formed<true>(P.h_in, P.hidden, stage, const_cast<float*>(P.h), emb,
-                               static_cast<int>(static_cast<long>(wg) * P.hidden / G),
-                               static_cast<int>(static_cast<long>(wg + 1) * P.hidden / G), static_cast<int>(lane), 64);
-  __syncthreads();
   float best = -__builtin_inff();
   unsigned best_idx = 0xFFFFFFFFu;
   unsigned long long key_any = 0ull;  // the any-width path's key
   if (wave > 0) {
-    int b0, b1;
-    wg_blocks(nl, b0, b1);
     const int T = P.hidden / 64, nbv = (P.vocab + 15) / 16;
+    int b0, b1;
+    wg_blocks(nbv, b0, b1);
     const int w0 = b0 + k * (b1 - b0) / kCompute, w1 = b0 + (k + 1) * (b1 - b0) / kCompute;
     const int n = (w1 - w0) * T;
     const int exp_off = static_cast<int>(ops::int8_exp_off(P.hidden));
@@ -601,18 +854,19 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
     const __amdgpu_buffer_rsrc_t lr =
         buffer_over(P.logits_out, P.logits_out ? static_cast<unsigned>(P.vocab) * 4u : 0u);
     const int rpb = T / kMaxT;  // rounds per block (T is a multiple of kMaxT)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the first round has arrived
     auto stream = [&](u32x4(&a)[kMaxT], u32x4(&b)[kMaxT]) {
       if (T % kMaxT != 0) {  // any width: tiles loaded one at a time (the prefetched round is not used)
         key_any = int8_tiles_any(P, T, nbv, w0, n, region, exp_off, lr);
         return;
       }
-      // a holds round 0 (prefetched); rounds alternate between the buffers
+      // a holds round 0; rounds alternate between the buffers
       for (int r0 = 0; r0 < n; r0 += 2 * kMaxT) {
-        load_tiles(b, P.out_table, nbv, T, w0, r0 + kMaxT, n < r0 + 2 * kMaxT ? n : r0 + 2 * kMaxT);
+        load_tiles(b, P.out_table, T, w0, r0 + kMaxT, n < r0 + 2 * kMaxT ? n : r0 + 2 * kMaxT);
         int8_round(a, r0 % T, region, exp_off, iacc, facc);
         if ((r0 / kMaxT) % rpb == rpb - 1) int8_block_end(w0 + r0 / T, P, lr, facc, best, best_idx);
         if (r0 + kMaxT >= n) break;
-        load_tiles(a, P.out_table, nbv, T, w0, r0 + 2 * kMaxT, n < r0 + 3 * kMaxT ? n : r0 + 3 * kMaxT);
+        load_tiles(a, P.out_table, T, w0, r0 + 2 * kMaxT, n < r0 + 3 * kMaxT ? n : r0 + 3 * kMaxT);
         int8_round(b, (r0 + kMaxT) % T, region, exp_off, iacc, facc);
         if ((r0 / kMaxT + 1) % rpb == rpb - 1) int8_block_end(w0 + (r0 + kMaxT) / T, P, lr, facc, best, best_idx);
       }
@@ -678,6 +932,21 @@ int ordered_grid() {
 // ------------------------------------------------------------------- host
 size_t step_ordered_workspace(const pwg_step_desc* d) { return olayout(d->n_levels).total; }
 
+namespace {
+// The control wave copies a level's sources into LDS 16 bytes per lane.
+int check_sources(const pwg_input& in, int64_t n, const float* x, const char* fn, const char* what) {
+  const void* ptrs[4] = {in.op == PWG_INPUT_GIVEN ? static_cast<const void*>(x) : nullptr, in.src, in.resid, in.gamma};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(PWG_ERR_ALIGN, "%s: %s: sources must be 16-byte aligned", fn, what);
+  if (in.op == PWG_INPUT_ATTN1 && in.head_dim % 4 != 0)
+    return fail(PWG_ERR_UNSUPPORTED, "%s: %s: head_dim must be a multiple of 4 on the persistent schedule", fn, what);
+  if (in.op == PWG_INPUT_RMSNORM && n > kMaxNormCols)
+    return fail(PWG_ERR_UNSUPPORTED, "%s: %s: RMSNORM over more than %d values is not on the persistent schedule", fn,
+                what, kMaxNormCols);
+  return PWG_OK;
+}
+}  // namespace
+
 int step_ordered_check(const pwg_step_desc* d, const char* fn) {
   if (d->weight_layout != PWG_LAYOUT_TILED)
     return fail(PWG_ERR_UNSUPPORTED, "%s: the persistent schedule reads tiled weights (PWG_LAYOUT_TILED)", fn);
@@ -690,7 +959,9 @@ int step_ordered_check(const pwg_step_desc* d, const char* fn) {
     if (L.cols % 256 != 0 || L.cols > kMaxCols)
       return fail(PWG_ERR_UNSUPPORTED, "%s: level %d: cols must be a multiple of 256 in [256, %d] on the persistent "
                   "schedule", fn, i, kMaxCols);
+    TRY(check_sources(L.in, L.cols, L.x, fn, "level input"));
   }
+  TRY(check_sources(d->h_in, d->hidden, d->h, fn, "h"));
   return PWG_OK;
 }
 
@@ -705,6 +976,8 @@ int step_ordered_plan(const pwg_step_desc* d, void* stream) {
   const int G = ordered_grid();
   if (G < 1 || G > static_cast<int>(kMaxGrid))
     return fail(PWG_ERR_UNSUPPORTED, "%s: the persistent kernel needs one resident workgroup on every CU", fn);
+  if ((kMaxCols + G - 1) / G > kMaxSlice)
+    return fail(PWG_ERR_UNSUPPORTED, "%s: %d CUs are too few for the persistent kernel", fn, G);
   const OLayout lay = layout_of(d);
   std::vector<OLevel> lv(static_cast<size_t>(d->n_levels));
   for (int i = 0; i < d->n_levels; ++i) {
