@@ -72,7 +72,7 @@ static_assert(kRegionBytes >= ops::ternary_region_bytes(kMaxCols) && kRegionByte
 constexpr size_t kSlotsBytes = static_cast<size_t>(kMaxBlk) * kCompute * 64;
 constexpr int kMaxSlice = 256;           // formed values one workgroup writes back
 constexpr int kMaxNormCols = 9984;       // RMSNORM: source and gain staged in the operand region
-constexpr size_t kLevelBytes = 96;       // one level descriptor (OLevel)
+constexpr size_t kLevelBytes = 160;      // one level descriptor (OLevel)
 // red[16], wkeys[8], hsave[kMaxSlice], two level descriptors
 constexpr size_t kMiscBytes = 128 + 4 * kMaxSlice + 2 * kLevelBytes;
 constexpr size_t kLds = kStageBytes + kRegionBytes + kSlotsBytes + kMiscBytes;
@@ -83,6 +83,16 @@ static_assert(kRegionBytes >= 4 * kMaxCols && kRegionBytes >= (kMaxCols + 1023) 
                   kRegionBytes >= 8 * kMaxNormCols,
               "formation staging");
 
+// A level input formed by the previous level (its producer) from its own
+// outputs: the input op kInputPrenorm takes src = gamma h, written by the
+// producer, and the producer's per-workgroup sums of h^2 (`part`); the
+// consumer only applies the norm's scale.
+constexpr int kInputPrenorm = 100;
+// What a level's control wave forms from the level's outputs for the next
+// consumer (the next level, or h): nothing, RMSNORM's gamma h and h (with
+// the sums of h^2), or SwiGLU's input (rows assigned as gate/up block pairs).
+enum : int { kEpiNone = 0, kEpiNorm = 1, kEpiSwiglu = 2 };
+
 struct OLevel {
   const unsigned char* w;  // tiled T2
   const float* scale;
@@ -90,12 +100,22 @@ struct OLevel {
   float* y;
   int rows, cols, T, nb;   // T = cols / 256 tiles per block, nb = 16-row blocks
   chain::DevInput in;
+  int epi;                 // kEpi*
+  int seg;                 // 1: block j of the first half paired with block j of the second
+  int pad0, pad1;
+  const float* part;       // in.op == kInputPrenorm: the producer's sums of h^2, one per workgroup
+  float* e_out;            // kEpiNorm: gamma h; kEpiSwiglu: the consumer's input
+  const float* e_resid;    // kEpiNorm: the residual stream added to y
+  const float* e_gamma;
+  float* e_resid_out;      // kEpiNorm: h (or null)
+  float* e_part;           // kEpiNorm: this launch's per-workgroup sums of h^2
 };
 
 static_assert(sizeof(OLevel) == kLevelBytes && kLevelBytes % 4 == 0, "level descriptor size");
 
 struct alignas(256) OPlan {
   unsigned n_levels, n_barriers, grid, mode;
+  unsigned long long grid_magic;  // ceil(2^40 / grid): x / grid = x grid_magic >> 40 for x < 2^26
   unsigned per_xcd[8];
   unsigned xcd_mask;
   int vocab, hidden;
@@ -111,6 +131,7 @@ struct alignas(256) OPlan {
   float* emb_deq_out;
   float* logits_out;
   chain::DevInput h_in;
+  const float* h_part;     // h_in.op == kInputPrenorm: the producer's sums of h^2
 };
 
 constexpr size_t kMaxGrid = 1024;
@@ -119,7 +140,7 @@ constexpr size_t kCountersBytes = 8 * 128;               // one 64-bit counter p
 constexpr size_t kFlagsBytes = kReplicas * 256 + 4096;   // 8 XCD flags per replica line (+ flat mode)
 
 struct OLayout {
-  size_t plan, state, counters, flags, partials, arrivals, levels, calib, total;
+  size_t plan, state, counters, flags, partials, arrivals, levels, calib, uvec, sums, total;
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -134,7 +155,9 @@ OLayout olayout(int n_levels) {
   L.arrivals = L.partials + kMaxGrid * 8;
   L.levels = L.arrivals + 256;
   L.calib = align_up(L.levels + static_cast<size_t>(n_levels) * sizeof(OLevel), 256);
-  L.total = align_up(L.calib + kMaxGrid * 4, 256);
+  L.uvec = align_up(L.calib + kMaxGrid * 4, 256);        // two vectors of gamma h (consumer parity)
+  L.sums = L.uvec + 2 * kMaxCols * 4;                     // two arrays of per-workgroup sums of h^2
+  L.total = align_up(L.sums + 2 * kMaxGrid * 4, 256);
   return L;
 }
 
@@ -233,17 +256,42 @@ __device__ __forceinline__ void load_tiles(u32x4 (&r)[kMaxT], const unsigned cha
     r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 1024u * j, 0, 2));
 }
 
-// The same for a prefetch whose registers are not read until every load of
-// the wave has completed: only the tiles that exist are loaded (a load
-// past the end still costs the wave an address-unit slot).
-__device__ __forceinline__ void prefetch_tiles(u32x4 (&r)[kMaxT], const unsigned char* w, int T, int b0, int s, int e) {
-  const long first = static_cast<long>(b0) * T + s;
+// A workgroup's tiles of a level: tile idx of the workgroup's block-major
+// sequence is tile a0 + idx of the matrix below `split`, b0 + idx - split
+// from there (rows assigned as two segments; split = the first segment's
+// tiles).  Tile t is KiB t of the arrangement.
+struct TileMap {
+  int a0, b0, split;
+};
+__device__ __forceinline__ unsigned tile_byte(const TileMap& m, int idx) {
+  return static_cast<unsigned>(idx < m.split ? m.a0 + idx : m.b0 + (idx - m.split)) * 1024u;
+}
+
+// Tiles [s, e) (e - s <= kMaxT) of the sequence, for a prefetch whose
+// registers are not read until every load of the wave has completed: only
+// the tiles that exist are loaded (a load past the end still costs the wave
+// an address-unit slot).  `bytes`: the matrix's size.
+__device__ __forceinline__ void prefetch_tiles(u32x4 (&r)[kMaxT], const unsigned char* w, unsigned bytes,
+                                               const TileMap& m, int s, int e) {
+  const __amdgpu_buffer_rsrc_t rs = buffer_over(w, bytes);
+  const unsigned lo = 16u * (threadIdx.x & 63u);
   const int n = e - s;
-  const __amdgpu_buffer_rsrc_t rs = buffer_over(w + first * 1024, n > 0 ? static_cast<unsigned>(n) * 1024u : 0u);
-  const unsigned off = 16u * (threadIdx.x & 63u);
 #pragma unroll
   for (int j = 0; j < kMaxT; ++j)
-    if (j < n) r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 1024u * j, 0, 2));
+    if (j < n) r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, tile_byte(m, s + j) + lo, 0, 2));
+}
+
+// The same with every slot's load issued (slots past e read zeros), for
+// tiles used right after: the compiler counts the loads.
+__device__ __forceinline__ void load_tiles_map(u32x4 (&r)[kMaxT], const unsigned char* w, unsigned bytes,
+                                               const TileMap& m, int s, int e) {
+  const __amdgpu_buffer_rsrc_t rs = buffer_over(w, bytes);
+  const unsigned lo = 16u * (threadIdx.x & 63u);
+#pragma unroll
+  for (int j = 0; j < kMaxT; ++j) {
+    const unsigned off = s + j < e ? tile_byte(m, s + j) + lo : kOff;
+    r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2));
+  }
 }
 
 // Ternary tiles [s, e) (at most kMaxT, the ones in r) of a compute wave's
@@ -428,6 +476,8 @@ __device__ __forceinline__ int embed_gamma_off(int n) { return (n + 1023) / 1024
 //                  embed_gamma_off(n) (past the row copy's last KiB)
 //   ATTN1          gathered value rows -> stage
 //   SWIGLU         gate -> raw[0, n), up -> stage
+//   kInputPrenorm  gamma h -> stage, the producer's sums of h^2 -> sums
+//                  (the slot area, free until the products)
 // Control wave, any time after the previous level's operands were used: the
 // sources that are constant in the launch.
 __device__ __forceinline__ void issue_static_sources(const chain::DevInput& in, int n, unsigned char* raw,
@@ -449,11 +499,14 @@ __device__ __forceinline__ void issue_static_sources(const chain::DevInput& in, 
 // Control wave, after the previous level's barrier: the sources written
 // earlier in this launch.
 __device__ __forceinline__ void issue_dynamic_sources(const chain::DevInput& in, int n, const float* x, float* stage,
-                                                      unsigned char* raw) {
+                                                      unsigned char* raw, const float* part, int grid, float* sums) {
   const unsigned nb = static_cast<unsigned>(n) * 4u;
   unsigned char* st = reinterpret_cast<unsigned char*>(stage);
   if (in.op == PWG_INPUT_GIVEN) {
     lds_copy(x, nb, st);
+  } else if (in.op == kInputPrenorm) {
+    lds_copy(in.src, nb, st);
+    lds_copy(part, static_cast<unsigned>(grid) * 4u, reinterpret_cast<unsigned char*>(sums));
   } else if (in.op == PWG_INPUT_RMSNORM) {
     lds_copy(in.resid, nb, st);
     if (in.src) lds_copy(in.src, nb, raw);
@@ -562,7 +615,17 @@ __device__ __forceinline__ bool form_elementwise(const chain::DevInput& in, int 
 
 // The norm's scale 1 / sqrt(mean + eps) from the waves' sums (fixed order),
 // or 1 for the other ops.
-__device__ __forceinline__ float norm_scale(const chain::DevInput& in, int n, const float* red) {
+__device__ __forceinline__ float norm_scale(const chain::DevInput& in, int n, const float* red, const float* sums,
+                                            int grid) {
+  if (in.op == kInputPrenorm) {
+    // the producer's sums: lane l adds sums l, l + 64, ... in order, then a
+    // fixed tree over the lanes; every wave of every workgroup gets the same
+    float v = 0.f;
+    for (int w = static_cast<int>(threadIdx.x & 63u); w < grid; w += 64) v += sums[w];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return 1.0f / sqrtf(v / static_cast<float>(n) + in.eps);
+  }
   if (!is_norm(in.op)) return 1.f;
   float sum = 0.f;
   for (int w = 0; w < kWaves; ++w) sum += red[w];
@@ -676,49 +739,79 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
   const chain::EmbedSrc emb{P.emb_table, P.emb_scale, P.token_in, static_cast<long>(P.vocab)};
   constexpr int kDw = static_cast<int>(kLevelBytes / 4);
 
-  // 16-row blocks [b0, b1) of a matrix of nb blocks owned by this workgroup
-  auto wg_blocks = [&](int nb, int& b0, int& b1) {
-    b0 = static_cast<int>(static_cast<long>(wg) * nb / G);
-    b1 = static_cast<int>(static_cast<long>(wg + 1) * nb / G);
+  // [b0, b1) of a range of n units owned by this workgroup
+  auto wg_split = [&](int n, int& b0, int& b1) {
+    const unsigned long long m = P.grid_magic;
+    b0 = static_cast<int>((static_cast<unsigned long long>(wg * static_cast<unsigned>(n)) * m) >> 40);
+    b1 = static_cast<int>((static_cast<unsigned long long>((wg + 1) * static_cast<unsigned>(n)) * m) >> 40);
   };
+  // The workgroup's 16-row blocks of a level: local block lb is block
+  // a0 + lb below na, c0 + lb - na from there (seg: block j of the first half
+  // paired with block j of the second).
+  struct WgRows {
+    int a0, na, c0, nblk;
+    __device__ int block(int lb) const { return lb < na ? a0 + lb : c0 + (lb - na); }
+  };
+  auto wg_rows = [&](const OLevel& L) -> WgRows {
+    int b0, b1;
+    if (L.seg) {
+      const int half = L.nb / 2;
+      wg_split(half, b0, b1);
+      return WgRows{b0, b1 - b0, half + b0, 2 * (b1 - b0)};
+    }
+    wg_split(L.nb, b0, b1);
+    return WgRows{b0, b1 - b0, 0, b1 - b0};
+  };
+  auto tile_map = [&](const WgRows& R, int T) { return TileMap{R.a0 * T, R.c0 * T, R.na * T}; };
   // elements of a formed input of n values this workgroup writes back
-  auto wg_slice = [&](int n, int& s0, int& s1) {
-    s0 = static_cast<int>(static_cast<long>(wg) * n / G);
-    s1 = static_cast<int>(static_cast<long>(wg + 1) * n / G);
-  };
+  auto wg_slice = [&](int n, int& s0, int& s1) { wg_split(n, s0, s1); };
   // tiles of level li (descriptor L; li == nl: the vocabulary's first kMaxT;
   // past it: none) for this compute wave; every load of the wave completes
   // before they are read
   auto prefetch = [&](u32x4 (&r)[kMaxT], unsigned li, const OLevel& L) {
-    int b0 = 0, b1 = 0, s = 0, e = 0, nb = 1, T = 1;
+    int s = 0, e = 0;
+    unsigned bytes = 0;
     const unsigned char* w = P.out_table;
+    TileMap m{0, 0, 0};
     if (li < nl) {
+      const WgRows R = wg_rows(L);
       w = L.w;
-      nb = L.nb;
-      T = L.T;
-      wg_blocks(nb, b0, b1);
-      wave_range(b1 - b0, T, k, s, e);
+      bytes = static_cast<unsigned>(L.nb) * static_cast<unsigned>(L.T) * 1024u;
+      m = tile_map(R, L.T);
+      wave_range(R.nblk, L.T, k, s, e);
     } else if (li == nl) {
-      T = P.hidden / 64;
-      nb = (P.vocab + 15) / 16;
-      wg_blocks(nb, b0, b1);
+      const int T = P.hidden / 64, nbv = (P.vocab + 15) / 16;
+      int b0, b1;
+      wg_split(nbv, b0, b1);
       const int w0 = b0 + k * (b1 - b0) / kCompute, w1 = b0 + (k + 1) * (b1 - b0) / kCompute;
-      b0 = w0;
+      bytes = static_cast<unsigned>(nbv) * static_cast<unsigned>(T) * 1024u;
+      m = TileMap{w0 * T, 0, 1 << 30};
       e = (w1 - w0) * T;
     }
-    prefetch_tiles(r, w, T, b0, s, e < s + kMaxT ? e : s + kMaxT);
+    prefetch_tiles(r, w, bytes, m, s, e < s + kMaxT ? e : s + kMaxT);
   };
-  // control wave: the row scales of a level (lane + 64 j of the workgroup's rows)
-  float rsc[4] = {0.f, 0.f, 0.f, 0.f};
-  auto load_scales = [&](const OLevel& L) {
-    int b0, b1;
-    wg_blocks(L.nb, b0, b1);
-    const __amdgpu_buffer_rsrc_t rs = buffer_over(L.scale, static_cast<unsigned>(L.rows) * 4u);
+  // control wave: per row lane + 64 j of the workgroup's rows of a level, its
+  // scale and, for a norm epilogue, the gain and the residual stream there
+  // (`dynamic`: the residual stream only, after the previous level's barrier,
+  // since the previous level may have written it)
+  float rsc[4] = {0.f, 0.f, 0.f, 0.f}, rres[4] = {0.f, 0.f, 0.f, 0.f}, rgam[4] = {0.f, 0.f, 0.f, 0.f};
+  auto load_rows = [&](const OLevel& L, bool dynamic) {
+    const WgRows R = wg_rows(L);
+    const unsigned nb = static_cast<unsigned>(L.rows) * 4u;
+    const __amdgpu_buffer_rsrc_t rs = buffer_over(L.scale, nb);
+    const __amdgpu_buffer_rsrc_t rr_res = buffer_over(L.e_resid, L.epi == kEpiNorm ? nb : 0u);
+    const __amdgpu_buffer_rsrc_t rr_gam = buffer_over(L.e_gamma, L.epi == kEpiNorm ? nb : 0u);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int rr = static_cast<int>(lane) + 64 * j, row = b0 * 16 + rr;
-      const unsigned off = rr < (b1 - b0) * 16 && row < L.rows ? static_cast<unsigned>(row) * 4u : kOff;
-      rsc[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+      const int rr = static_cast<int>(lane) + 64 * j, row = R.block(rr >> 4) * 16 + (rr & 15);
+      const unsigned off = rr < R.nblk * 16 && row < L.rows ? static_cast<unsigned>(row) * 4u : kOff;
+      if (dynamic) {
+        // written earlier in this launch: device scope
+        rres[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr_res, off, 0, kSc1));
+      } else {
+        rsc[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+        rgam[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr_gam, off, 0, 0));
+      }
     }
   };
 
@@ -742,11 +835,15 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
       const int n = vocab ? P.hidden : L.cols;
       int next_dw = 0;
       if (li + 1 < nl && lane < kDw) next_dw = reinterpret_cast<const int*>(levels + li + 1)[lane];
-      if (!vocab) load_scales(L);
+      if (!vocab) load_rows(L, false);
       issue_static_sources(in, n, region, emb, red);
       bool late = false;
       if (li > 0) late = bar.wait(li - 1);
-      if (!late) issue_dynamic_sources(in, n, vocab ? P.h : L.x, stage, region);
+      if (!late) {
+        issue_dynamic_sources(in, n, vocab ? P.h : L.x, stage, region, vocab ? P.h_part : L.part,
+                              static_cast<int>(G), slots);
+        if (!vocab && L.epi == kEpiNorm) load_rows(L, true);
+      }
       if (li + 1 < nl && lane < kDw) reinterpret_cast<int*>(&ring[(li + 1) & 1])[lane] = next_dw;
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the sources are in LDS
       if (lane == 0) red[15] = late ? 1.f : 0.f;
@@ -764,8 +861,8 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
     if (gather(li)) return true;
     const OLevel L = uni_level(&ring[li & 1]);
     const int T = L.T, cols = L.cols, rows = L.rows;
-    int b0, b1, s0, s1;
-    wg_blocks(L.nb, b0, b1);
+    const WgRows R = wg_rows(L);
+    int s0, s1;
     wg_slice(cols, s0, s1);
     // every earlier load (this level's tiles) has completed; saying so on
     // every path lets the compiler count the prefetch below instead of
@@ -776,12 +873,12 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
       prefetch(nxt, li + 1, Ln);
     }
     if (form_elementwise(L.in, cols, stage, region, red, hsave, s0, s1)) __syncthreads();
-    const float inv = norm_scale(L.in, cols, red);
+    const float inv = norm_scale(L.in, cols, red, slots, static_cast<int>(G));
     convert_ternary(stage, cols, region, inv);
     __syncthreads();  // the operand region is complete
     if (wave > 0) {
       int s, e;
-      wave_range(b1 - b0, T, k, s, e);
+      wave_range(R.nblk, T, k, s, e);
       const size_t mf = static_cast<size_t>(2 * T);
       const int bsc = static_cast<int>(ops::operand_bsc_off(mf)), asc = static_cast<int>(ops::operand_asc_off(mf));
       v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -789,7 +886,8 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
       // workgroup) load on demand
       ternary_tiles(cur, T, s, e < s + kMaxT ? e : s + kMaxT, e, region, bsc, asc, slots, k, acc0, acc1);
       for (int r0 = s + kMaxT; r0 < e; r0 += kMaxT) {
-        load_tiles(cur, L.w, T, b0, r0, e < r0 + kMaxT ? e : r0 + kMaxT);
+        load_tiles_map(cur, L.w, static_cast<unsigned>(L.nb) * static_cast<unsigned>(T) * 1024u, tile_map(R, T), r0,
+                       e < r0 + kMaxT ? e : r0 + kMaxT);
         ternary_tiles(cur, T, r0, e < r0 + kMaxT ? e : r0 + kMaxT, e, region, bsc, asc, slots, k, acc0, acc1);
       }
     } else {
@@ -798,8 +896,10 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
     __syncthreads();  // every slot of the level is written
     if (wave == 0) {
       // rows of the workgroup: block bl's sum over the compute waves that
-      // touched it, in wave order
-      const int nrow = (b1 - b0) * 16;
+      // touched it, in wave order; then what the rows form for the next
+      // consumer
+      const int nrow = R.nblk * 16;
+      float hh = 0.f;  // kEpiNorm: this lane's sum of h^2
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int rr = static_cast<int>(lane) + 64 * j;
@@ -808,11 +908,41 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
           float v = 0.f;
           for (int kk = 0; kk < kCompute; ++kk) {
             int s, e;
-            wave_range(b1 - b0, T, kk, s, e);
+            wave_range(R.nblk, T, kk, s, e);
             if (s < e && s < (bl + 1) * T && e > bl * T) v += slots[(bl * kCompute + kk) * 16 + i];
           }
-          const long row = static_cast<long>(b0 + bl) * 16 + i;
-          if (row < rows) __hip_atomic_store(&L.y[row], v * rsc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const int row = R.block(bl) * 16 + i;
+          const float y = v * rsc[j];
+          if (row < rows) {
+            __hip_atomic_store(&L.y[row], y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (L.epi == kEpiNorm) {
+              // chain_input.h's h = resid + src, then gamma h
+              const float h = rres[j] + y;
+              if (L.e_resid_out) __hip_atomic_store(&L.e_resid_out[row], h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_store(&L.e_out[row], rgam[j] * h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              hh = fmaf(h, h, hh);
+            }
+          }
+          if (L.epi == kEpiSwiglu) hsave[rr] = y;
+        }
+      }
+      if (L.epi == kEpiNorm) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) hh += __shfl_xor(hh, o, kWave);
+        if (lane == 0) __hip_atomic_store(&L.e_part[wg], hh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else if (L.epi == kEpiSwiglu) {
+        // gate row g of local block bl < na pairs with up row g + rows / 2 of
+        // local block bl + na; SwiGLU as chain_input.h forms it
+        const int ng = R.na * 16;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int rr = static_cast<int>(lane) + 64 * j;
+          if (rr < ng) {
+            const float gv = hsave[rr], up = hsave[rr + ng], ez = expf(-fabsf(gv));
+            const float sig = gv >= 0.f ? 1.0f / (1.0f + ez) : ez / (1.0f + ez);
+            __hip_atomic_store(&L.e_out[(R.a0 + (rr >> 4)) * 16 + (rr & 15)], gv * sig * up, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          }
         }
       }
       bar.arrive(li);
@@ -834,7 +964,7 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
     int s0, s1;
     wg_slice(P.hidden, s0, s1);
     if (form_elementwise(P.h_in, P.hidden, stage, region, red, hsave, s0, s1)) __syncthreads();
-    const float inv = norm_scale(P.h_in, P.hidden, red);
+    const float inv = norm_scale(P.h_in, P.hidden, red, slots, static_cast<int>(G));
     convert_int8(stage, P.hidden, region, inv);
     __syncthreads();
     if (wave == 0) store_slice(P.h_in, stage, hsave, inv, const_cast<float*>(P.h), s0, s1);
@@ -845,7 +975,7 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
   if (wave > 0) {
     const int T = P.hidden / 64, nbv = (P.vocab + 15) / 16;
     int b0, b1;
-    wg_blocks(nbv, b0, b1);
+    wg_split(nbv, b0, b1);
     const int w0 = b0 + k * (b1 - b0) / kCompute, w1 = b0 + (k + 1) * (b1 - b0) / kCompute;
     const int n = (w1 - w0) * T;
     const int exp_off = static_cast<int>(ops::int8_exp_off(P.hidden));
@@ -999,11 +1129,16 @@ int step_ordered_plan(const pwg_step_desc* d, void* stream) {
   }
   if ((d->vocab + 15) / 16 * (d->hidden / 64) * 1024 >= (int64_t{1} << 32))
     return fail(PWG_ERR_UNSUPPORTED, "%s: the output table is larger than 4 GiB", fn);
+  if (d->vocab > (int64_t{1} << 20))  // 16-row blocks split over the grid by multiply-shift
+    return fail(PWG_ERR_UNSUPPORTED, "%s: vocab above 2^20 on the persistent schedule", fn);
   OPlan h;
   std::memset(&h, 0, sizeof h);
   h.n_levels = static_cast<unsigned>(d->n_levels);
   h.n_barriers = static_cast<unsigned>(d->n_levels > 0 ? d->n_levels : 1);
   h.grid = static_cast<unsigned>(G);
+  // x / G for x < 2^26: x ceil(2^40 / G) / 2^40 exceeds x / G by less than
+  // 2^-14 < 1 / G, which cannot carry past the next integer
+  h.grid_magic = ((1ull << 40) + static_cast<unsigned long long>(G) - 1) / static_cast<unsigned long long>(G);
   h.vocab = static_cast<int>(d->vocab);
   h.hidden = static_cast<int>(d->hidden);
   h.out_table = static_cast<const unsigned char*>(static_cast<const void*>(d->out_table));
@@ -1021,6 +1156,43 @@ int step_ordered_plan(const pwg_step_desc* d, void* stream) {
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   unsigned char* base = ws_base(d);
+
+  // Producer epilogues: where a consumer (the next level, or h) forms its
+  // input from the previous level's output alone, that level's control wave
+  // forms it as it writes the output (RMSNORM: h, gamma h and the sums of
+  // h^2, the consumer applying the scale; SwiGLU: the input itself, with the
+  // gate and up rows of one index in one workgroup).  Buffers alternate with
+  // the consumer's parity: a consumer reads them before its barrier, the
+  // next writer of the same buffer runs after it.
+  float* uvec = reinterpret_cast<float*>(base + lay.uvec);
+  float* sums = reinterpret_cast<float*>(base + lay.sums);
+  auto link = [&](OLevel& p, chain::DevInput& in, int n, float* cons_x, const float** cons_part, int parity,
+                  bool level_consumer) {
+    if (in.op == PWG_INPUT_RMSNORM && in.src == p.y && n == p.rows && n <= kMaxNormCols) {
+      p.epi = kEpiNorm;
+      p.e_out = uvec + static_cast<size_t>(parity) * kMaxCols;
+      p.e_resid = in.resid;
+      p.e_gamma = in.gamma;
+      p.e_resid_out = in.resid_out;
+      p.e_part = sums + static_cast<size_t>(parity) * kMaxGrid;
+      in.op = kInputPrenorm;
+      in.src = p.e_out;
+      in.resid = nullptr;
+      in.gamma = nullptr;
+      in.resid_out = nullptr;
+      *cons_part = p.e_part;
+    } else if (level_consumer && in.op == PWG_INPUT_SWIGLU && in.src == p.y && p.rows == 2 * n && n % 16 == 0 &&
+               (p.nb / 2 + G - 1) / G * 2 <= kMaxBlk) {
+      p.epi = kEpiSwiglu;
+      p.seg = 1;
+      p.e_out = cons_x;
+      in.op = PWG_INPUT_GIVEN;
+    }
+  };
+  for (int i = 0; i + 1 < d->n_levels; ++i)
+    link(lv[i], lv[i + 1].in, lv[i + 1].cols, const_cast<float*>(lv[i + 1].x), &lv[i + 1].part, (i + 1) & 1, true);
+  if (d->n_levels > 0)
+    link(lv[d->n_levels - 1], h.h_in, h.hidden, const_cast<float*>(h.h), &h.h_part, d->n_levels & 1, false);
   // XCD census: one workgroup per CU (the step kernel's LDS request); the
   // barrier counts per XCD when every XCD holds the same number of them
   hipLaunchKernelGGL(xcc_census_kernel, dim3(G), dim3(kThreads), kLds, st, reinterpret_cast<unsigned*>(base + lay.calib));
