@@ -55,6 +55,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kCompute = kWaves - 1;   // waves 1..7; wave 0 controls
 constexpr int kMaxT = 16;              // tiles per compute wave in one register buffer
+constexpr int kPrefetchFirst = 8;      // tiles of the next level loaded before a level's conversion
 constexpr int kMaxCols = 12288;
 constexpr int kMaxBlk = 16;            // 16-row blocks of one level per workgroup
 constexpr int kReplicas = 8;
@@ -271,13 +272,15 @@ __device__ __forceinline__ unsigned tile_byte(const TileMap& m, int idx) {
 // registers are not read until every load of the wave has completed: only
 // the tiles that exist are loaded (a load past the end still costs the wave
 // an address-unit slot).  `bytes`: the matrix's size.
+// Slots [J0, J1) only: a large prefetch is issued in two parts.
+template <int J0, int J1>
 __device__ __forceinline__ void prefetch_tiles(u32x4 (&r)[kMaxT], const unsigned char* w, unsigned bytes,
                                                const TileMap& m, int s, int e) {
   const __amdgpu_buffer_rsrc_t rs = buffer_over(w, bytes);
   const unsigned lo = 16u * (threadIdx.x & 63u);
   const int n = e - s;
 #pragma unroll
-  for (int j = 0; j < kMaxT; ++j)
+  for (int j = J0; j < J1; ++j)
     if (j < n) r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, tile_byte(m, s + j) + lo, 0, 2));
 }
 
@@ -768,7 +771,7 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
   // tiles of level li (descriptor L; li == nl: the vocabulary's first kMaxT;
   // past it: none) for this compute wave; every load of the wave completes
   // before they are read
-  auto prefetch = [&](u32x4 (&r)[kMaxT], unsigned li, const OLevel& L) {
+  auto prefetch = [&](u32x4 (&r)[kMaxT], unsigned li, const OLevel& L, int part) {
     int s = 0, e = 0;
     unsigned bytes = 0;
     const unsigned char* w = P.out_table;
@@ -788,7 +791,8 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
       m = TileMap{w0 * T, 0, 1 << 30};
       e = (w1 - w0) * T;
     }
-    prefetch_tiles(r, w, bytes, m, s, e < s + kMaxT ? e : s + kMaxT);
+    if (part == 0) prefetch_tiles<0, kPrefetchFirst>(r, w, bytes, m, s, e < s + kMaxT ? e : s + kMaxT);
+    if (part != 0) prefetch_tiles<kPrefetchFirst, kMaxT>(r, w, bytes, m, s, e < s + kMaxT ? e : s + kMaxT);
   };
   // control wave: per row lane + 64 j of the workgroup's rows of a level, its
   // scale and, for a norm epilogue, the gain and the residual stream there
@@ -821,7 +825,8 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
     if (nl > 0 && lane < kDw)  // level 0's descriptor
       reinterpret_cast<int*>(ring)[lane] = reinterpret_cast<const int*>(levels)[lane];
   } else {
-    prefetch(ra, 0, levels[0]);
+    prefetch(ra, 0, levels[0], 0);
+    prefetch(ra, 0, levels[0], 1);
   }
 
   // The sources of level li's input (li == nl: h) in LDS, after the previous
@@ -868,10 +873,11 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
     // every path lets the compiler count the prefetch below instead of
     // draining it before the products
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    if (wave > 0) {
-      const OLevel Ln = uni_level(&ring[(li + 1) & 1]);  // not read past the last level
-      prefetch(nxt, li + 1, Ln);
-    }
+    // the first kPrefetchFirst tiles of the next level now; the rest after
+    // this level's products, so that a large next level holds up neither the
+    // conversion nor the products alone
+    const OLevel Ln = uni_level(&ring[(li + 1) & 1]);  // not read past the last level
+    if (wave > 0) prefetch(nxt, li + 1, Ln, 0);
     if (form_elementwise(L.in, cols, stage, region, red, hsave, s0, s1)) __syncthreads();
     const float inv = norm_scale(L.in, cols, red, slots, static_cast<int>(G));
     convert_ternary(stage, cols, region, inv);
@@ -890,6 +896,7 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
                        e < r0 + kMaxT ? e : r0 + kMaxT);
         ternary_tiles(cur, T, r0, e < r0 + kMaxT ? e : r0 + kMaxT, e, region, bsc, asc, slots, k, acc0, acc1);
       }
+      prefetch(nxt, li + 1, Ln, 1);
     } else {
       store_slice(L.in, stage, hsave, inv, const_cast<float*>(L.x), s0, s1);
     }
