@@ -511,6 +511,29 @@ int pwg_decode_step_weights(const pwg_step_desc* desc, void* stream);
  * message if a bounded wait timed out.  Not for the hot path. */
 int pwg_step_status(const pwg_step_desc* desc, void* stream);
 
+/* Level trace of the persistent schedule (page "The Neutrino Engine",
+ * section "A 104 microsecond floor inside a 694 microsecond step" and Fig. 1:
+ * where a step's time goes between its dependent levels).
+ * pwg_step_trace_bytes: bytes of a trace buffer for the description (0 for
+ * the other schedules, or where no device is present).
+ * pwg_step_set_trace, after pwg_step_plan (synchronous): later calls of
+ * pwg_decode_step_weights on this workspace record, for every level and the
+ * output projection (index n_levels) and every workgroup, eight uint64
+ * stamps of the GPU's 100 MHz real-time counter, laid out
+ * [level][workgroup][event]:
+ *   0 the control wave starts waiting for the previous level's barrier,
+ *   1 the barrier has passed, 2 the level's sources are in LDS, 3 every wave
+ *   is past them, 4 the operands are converted, 5 the products are done,
+ *   6 the control wave has arrived (its stores complete), 7 unused.
+ * Events a level does not reach keep their previous contents.
+ * trace: device, 16-byte aligned, >= pwg_step_trace_bytes(desc) bytes; NULL
+ * turns tracing off, and so does pwg_step_plan.  Each event adds a store by
+ * one thread: tracing lengthens the step it measures.
+ * Errors: PWG_ERR_UNSUPPORTED (another schedule), PWG_ERR_ARG (no plan for
+ * this description), PWG_ERR_SIZE, PWG_ERR_ALIGN, PWG_ERR_HIP. */
+size_t pwg_step_trace_bytes(const pwg_step_desc* desc);
+int pwg_step_set_trace(const pwg_step_desc* desc, void* trace, size_t trace_bytes, void* stream);
+
 /* Thread-local message of the last failed call on this thread ("" if none). */
 const char* pwg_last_error(void);
 

@@ -132,6 +132,8 @@ _step_ws = _sig("pwg_step_workspace_bytes", _sz, C.POINTER(_StepDesc))
 _step_plan = _sig("pwg_step_plan", C.c_int, C.POINTER(_StepDesc), _vp)
 _step = _sig("pwg_decode_step_weights", C.c_int, C.POINTER(_StepDesc), _vp)
 _step_status = _sig("pwg_step_status", C.c_int, C.POINTER(_StepDesc), _vp)
+_step_trace_bytes = _sig("pwg_step_trace_bytes", _sz, C.POINTER(_StepDesc))
+_step_set_trace = _sig("pwg_step_set_trace", C.c_int, C.POINTER(_StepDesc), _vp, _sz, _vp)
 _last_error = _sig("pwg_last_error", C.c_char_p)
 _version = _sig("pwg_version", C.c_int)
 
@@ -144,7 +146,7 @@ EXPORTED = ["pwg_packed_size", "pwg_pack_weights", "pwg_unpack_weights", "pwg_te
             "pwg_gqa_decode_attention", "pwg_verify_accept", "pwg_int8_gemv_argmax_noalloc",
             "pwg_b3_packed_size", "pwg_pack_weights_b3", "pwg_unpack_weights_b3", "pwg_b3_tiled_size",
             "pwg_tile_b3", "pwg_ternary_gemv_b3", "pwg_blob_payload_bytes", "pwg_blob_header_init",
-            "pwg_blob_header_check", "pwg_blob_verify"]
+            "pwg_blob_header_check", "pwg_blob_verify", "pwg_step_trace_bytes", "pwg_step_set_trace"]
 
 
 def last_error() -> str:
@@ -506,6 +508,22 @@ def step_plan(desc: StepDesc, stream=None):
 
 def decode_step_weights(desc: StepDesc, stream=None):
     _check(_step(C.byref(desc.c()), _stream(stream)))
+
+
+TRACE_EVENTS = 8
+TRACE_EVENT_NAMES = ("wait", "passed", "sources", "start", "converted", "products", "arrived", "unused")
+
+
+def step_trace_bytes(desc: StepDesc) -> int:
+    return _step_trace_bytes(C.byref(desc.c()))
+
+
+def step_set_trace(desc: StepDesc, trace=None, stream=None):
+    """Records the persistent schedule's level trace into `trace` (a device
+    uint8/int64 tensor of step_trace_bytes(desc) bytes) on later steps; None
+    turns it off.  Synchronous; after step_plan."""
+    ptr, nbytes = (None, 0) if trace is None else (trace.data_ptr(), trace.numel() * trace.element_size())
+    _check(_step_set_trace(C.byref(desc.c()), ptr, nbytes, _stream(stream)))
 
 
 def step_status(desc: StepDesc, stream=None):

@@ -340,6 +340,25 @@ extern "C" int pwg_step_status(const pwg_step_desc* d, void* stream) {
   return step_stream_status(d, 0, stream);
 }
 
+extern "C" size_t pwg_step_trace_bytes(const pwg_step_desc* d) {
+  if (!d || d->schedule != PWG_SCHEDULE_PERSISTENT || d->n_levels < 0 || d->n_levels > 4096) return 0;
+  return step_ordered_trace_bytes(d);
+}
+
+extern "C" int pwg_step_set_trace(const pwg_step_desc* d, void* trace, size_t trace_bytes, void* stream) {
+  const char* fn = "pwg_step_set_trace";
+  TRY(validate_step(d));
+  if (d->schedule != PWG_SCHEDULE_PERSISTENT)
+    return fail(PWG_ERR_UNSUPPORTED, "%s: only the persistent schedule records a level trace", fn);
+  TRY(plan_check(d, fn));
+  if (trace) {
+    const size_t need = pwg_step_trace_bytes(d);
+    if (trace_bytes < need) return fail(PWG_ERR_SIZE, "%s: trace buffer %zu < %zu bytes", fn, trace_bytes, need);
+    if (!aligned16(trace)) return fail(PWG_ERR_ALIGN, "%s: trace buffer is not 16-byte aligned", fn);
+  }
+  return step_ordered_set_trace(d, trace, stream);
+}
+
 extern "C" int pwg_decode_step_weights(const pwg_step_desc* d, void* stream) {
   TRY(validate_step(d));
   if (d->workspace_bytes < pwg_step_workspace_bytes(d))

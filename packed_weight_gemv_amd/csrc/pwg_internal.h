@@ -85,6 +85,8 @@ int step_ordered_check(const pwg_step_desc* d, const char* fn);
 int step_ordered_plan(const pwg_step_desc* d, void* stream);
 int step_ordered_launch(const pwg_step_desc* d, void* stream);
 int step_ordered_status(const pwg_step_desc* d, void* stream);
+size_t step_ordered_trace_bytes(const pwg_step_desc* d);
+int step_ordered_set_trace(const pwg_step_desc* d, void* trace, void* stream);
 
 int step_batch_check(const pwg_step_desc* d);
 size_t step_batch_workspace(const pwg_step_desc* d);

@@ -35,6 +35,7 @@
 // buffers; the last workgroup to finish reduces the argmax keys.  Every wait
 // is bounded (~0.5 s): a broken schedule ends with a status, never a hang.
 #include <algorithm>
+#include <cstddef>
 #include <cstring>
 #include <vector>
 
@@ -63,6 +64,14 @@ constexpr unsigned long long kSpinLimit = 50000000ull;  // 0.5 s of the 100 MHz 
 enum : unsigned { kBarrierL2 = 0, kBarrierFlat = 1 };
 enum : unsigned { kStatusOk = 0, kStatusTimeout = 1 };
 enum : unsigned { kStateStatus = 0, kStateGen = 1 };
+// Level trace events (100 MHz real-time counter), per level and workgroup:
+// control wave before its barrier wait, after it, with the level's sources
+// in LDS; every wave past the sources' barrier, past the converted operands,
+// past the products; control wave after its arrival.
+enum : int {
+  kEvWait = 0, kEvPassed = 1, kEvSources = 2, kEvStart = 3, kEvConverted = 4, kEvProducts = 5, kEvArrived = 6,
+  kTraceEvents = 8
+};
 
 // LDS: the formed input (float), the operand region, the partial slots,
 // the norm reduction and the waves' argmax keys.
@@ -133,6 +142,7 @@ struct alignas(256) OPlan {
   float* logits_out;
   chain::DevInput h_in;
   const float* h_part;     // h_in.op == kInputPrenorm: the producer's sums of h^2
+  unsigned long long* trace;  // null, or [n_levels + 1][grid][kTraceEvents] real-time stamps
 };
 
 constexpr size_t kMaxGrid = 1024;
@@ -741,6 +751,11 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
   bar.base = ld_sc(&state[kStateGen]) * P.n_barriers;
   const chain::EmbedSrc emb{P.emb_table, P.emb_scale, P.token_in, static_cast<long>(P.vocab)};
   constexpr int kDw = static_cast<int>(kLevelBytes / 4);
+  unsigned long long* const trace = P.trace;
+  auto stamp = [&](unsigned li, int ev) {
+    if (trace && threadIdx.x == 0)
+      trace[(static_cast<size_t>(li) * G + wg) * kTraceEvents + ev] = __builtin_amdgcn_s_memrealtime();
+  };
 
   // [b0, b1) of a range of n units owned by this workgroup
   auto wg_split = [&](int n, int& b0, int& b1) {
@@ -842,8 +857,10 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
       if (li + 1 < nl && lane < kDw) next_dw = reinterpret_cast<const int*>(levels + li + 1)[lane];
       if (!vocab) load_rows(L, false);
       issue_static_sources(in, n, region, emb, red);
+      stamp(li, kEvWait);
       bool late = false;
       if (li > 0) late = bar.wait(li - 1);
+      stamp(li, kEvPassed);
       if (!late) {
         issue_dynamic_sources(in, n, vocab ? P.h : L.x, stage, region, vocab ? P.h_part : L.part,
                               static_cast<int>(G), slots);
@@ -851,9 +868,11 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
       }
       if (li + 1 < nl && lane < kDw) reinterpret_cast<int*>(&ring[(li + 1) & 1])[lane] = next_dw;
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the sources are in LDS
+      stamp(li, kEvSources);
       if (lane == 0) red[15] = late ? 1.f : 0.f;
     }
     __syncthreads();
+    stamp(li, kEvStart);
     return red[15] != 0.f;
   };
 
@@ -882,6 +901,7 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
     const float inv = norm_scale(L.in, cols, red, slots, static_cast<int>(G));
     convert_ternary(stage, cols, region, inv);
     __syncthreads();  // the operand region is complete
+    stamp(li, kEvConverted);
     if (wave > 0) {
       int s, e;
       wave_range(R.nblk, T, k, s, e);
@@ -901,6 +921,7 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
       store_slice(L.in, stage, hsave, inv, const_cast<float*>(L.x), s0, s1);
     }
     __syncthreads();  // every slot of the level is written
+    stamp(li, kEvProducts);
     if (wave == 0) {
       // rows of the workgroup: block bl's sum over the compute waves that
       // touched it, in wave order; then what the rows form for the next
@@ -953,6 +974,7 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
         }
       }
       bar.arrive(li);
+      stamp(li, kEvArrived);
     }
     return false;
   };
@@ -974,6 +996,7 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
     const float inv = norm_scale(P.h_in, P.hidden, red, slots, static_cast<int>(G));
     convert_int8(stage, P.hidden, region, inv);
     __syncthreads();
+    stamp(nl, kEvConverted);
     if (wave == 0) store_slice(P.h_in, stage, hsave, inv, const_cast<float*>(P.h), s0, s1);
   }
   float best = -__builtin_inff();
@@ -1022,6 +1045,7 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
   }
   if (lane == 0) wkeys[wave] = key;
   __syncthreads();
+  stamp(nl, kEvProducts);
   if (wave == 0) {
     unsigned last = 0;
     if (lane == 0) {
@@ -1239,6 +1263,22 @@ int step_ordered_launch(const pwg_step_desc* d, void* stream) {
                      reinterpret_cast<unsigned*>(base + lay.arrivals));
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PWG_ERR_HIP, "persistent step launch: %s", hipGetErrorString(e));
+  return PWG_OK;
+}
+
+size_t step_ordered_trace_bytes(const pwg_step_desc* d) {
+  const int G = ordered_grid();
+  if (G < 1 || d->n_levels < 0) return 0;
+  return static_cast<size_t>(d->n_levels + 1) * static_cast<size_t>(G) * kTraceEvents * 8;
+}
+
+int step_ordered_set_trace(const pwg_step_desc* d, void* trace, void* stream) {
+  const OLayout lay = layout_of(d);
+  unsigned long long* t = static_cast<unsigned long long*>(trace);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(ws_base(d) + lay.plan + offsetof(OPlan, trace), &t, sizeof t, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(PWG_ERR_HIP, "pwg_step_set_trace: %s", hipGetErrorString(e));
   return PWG_OK;
 }
 

@@ -188,6 +188,23 @@ def test_step_argument_errors():
     assert pwg._step(C.byref(d), None) == ERR_ARG and "level 0" in pwg.last_error()
 
 
+def test_step_trace_host_errors():
+    """The level trace belongs to the persistent schedule: another schedule is
+    refused, and without a device no trace buffer size is reported."""
+    d = pwg._StepDesc()
+    d.vocab, d.hidden = 1000, 4096
+    for name in ("out_table", "out_scale", "h", "emb_table", "emb_scale", "token_in", "token_out",
+                 "emb_row_out", "emb_scale_out", "workspace"):
+        setattr(d, name, A)
+    lv = (pwg.Level * 1)(pwg.Level(A, A, A, A, 64, 4096))
+    d.n_levels, d.levels = 1, C.cast(lv, C.POINTER(pwg.Level))
+    d.schedule, d.weight_layout = pwg.SCHEDULE_STREAM, pwg.LAYOUT_TILED
+    assert pwg._step_trace_bytes(C.byref(d)) == 0
+    assert pwg._step_set_trace(C.byref(d), None, 0, None) == ERR_UNSUPPORTED
+    d.schedule = pwg.SCHEDULE_PERSISTENT
+    assert pwg._step_trace_bytes(C.byref(d)) == 0   # no device here
+
+
 def test_step_layout_errors():
     """Each schedule takes one weight arrangement; the stream and persistent
     schedules also need widths that are multiples of 256 and at most 12288."""

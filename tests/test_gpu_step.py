@@ -123,6 +123,46 @@ def test_graph_replay_matches_eager(schedule):
     check_against_oracle(wl, got, eager["token"], full_levels=True)
 
 
+def test_persistent_level_trace():
+    """The persistent schedule's level trace: a traced step computes what an
+    untraced one does, bit for bit, and each workgroup's stamps of a level
+    come in event order, each level's start after the previous level's
+    arrivals of every workgroup (the barrier), and every one is written."""
+    wl = build_step(n_layers=2, shapes=SMALL, vocab=1000, hidden=256, with_logits=True,
+                    schedule=pwg.SCHEDULE_PERSISTENT)
+    pwg.step_plan(wl.desc)
+    pwg.decode_step_weights(wl.desc)
+    torch.cuda.synchronize()
+    plain = outputs(wl)
+    nbytes = pwg.step_trace_bytes(wl.desc)
+    nl = len(wl.desc.levels)
+    assert nbytes > 0 and nbytes % ((nl + 1) * pwg.TRACE_EVENTS * 8) == 0
+    grid = nbytes // ((nl + 1) * pwg.TRACE_EVENTS * 8)
+    trace = torch.zeros(nbytes // 8, dtype=torch.int64, device="cuda:0")
+    pwg.step_set_trace(wl.desc, trace)
+    wl.desc.token_in.fill_(int(wl.token0))
+    pwg.decode_step_weights(wl.desc)
+    torch.cuda.synchronize()
+    pwg.step_status(wl.desc)
+    traced = outputs(wl)
+    for a, b in zip(traced["levels"], plain["levels"]):
+        assert np.array_equal(a, b)
+    assert np.array_equal(traced["logits"], plain["logits"]) and traced["token"] == plain["token"]
+    t = trace.cpu().numpy().reshape(nl + 1, grid, pwg.TRACE_EVENTS)
+    ev = {n: i for i, n in enumerate(pwg.TRACE_EVENT_NAMES)}
+    order = ["wait", "passed", "sources", "start", "converted", "products", "arrived"]
+    for li in range(nl):
+        for a, b in zip(order, order[1:]):
+            assert (t[li, :, ev[a]] <= t[li, :, ev[b]]).all(), (li, a, b)
+        assert (t[li, :, ev["arrived"]] > 0).all()
+        if li > 0:   # nobody starts a level before every workgroup arrived at the one before
+            assert t[li, :, ev["passed"]].min() >= t[li - 1, :, ev["arrived"]].max(), li
+    for a, b in zip(order[:5], order[1:6]):
+        assert (t[nl, :, ev[a]] <= t[nl, :, ev[b]]).all(), ("projection", a, b)
+    assert t[nl, :, ev["passed"]].min() >= t[nl - 1, :, ev["arrived"]].max()
+    pwg.step_set_trace(wl.desc, None)
+
+
 @pytest.mark.parametrize("schedule", [pwg.SCHEDULE_STREAM], ids=["stream"])
 def test_many_steps_stay_identical(schedule):
     """Claim counters are reset by every step's last workgroup; 50
