@@ -109,16 +109,24 @@ __device__ __forceinline__ unsigned split_b_scale(int e, int j) {
 }
 __device__ __forceinline__ unsigned split_a_scale(int e) { return static_cast<unsigned>(126 + split_ashift(e)); }
 
+typedef short v2s16 __attribute__((ext_vector_type(2)));
 constexpr int kDeferBits = 8;  // a residual below 2^-8 of its group's largest waits for a later split
 
 // Splits the 8 values of one summation group of the instruction (r[j]: K
 // value j of the group) into out[s][d]: bytes 4 d .. 4 d + 3 of piece s,
-// e4m3 codes in operand order.  r is consumed (left holding the final
-// residuals).
+// e4m3 codes in operand order.  Piece s holds the residual at scale
+// 2^(e - 8 - 4 s).  The residuals are kept in units of the first piece's
+// scale (one exact power-of-two scaling per value: the kept residuals stay
+// far above float32's normal range), so that each piece needs no per-value
+// scaling: the gfx950 scaled conversion divides by 2^-4s on the way to e4m3,
+// and one fused multiply-add by 2^-4s takes the piece back off, exactly.
+// r is consumed.
 __device__ __forceinline__ void fp8_splits8(float (&r)[8], int e, unsigned (&out)[kSplits][2]) {
 #pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = ldexpf(r[j], 8 - e);
+#pragma unroll
   for (int s = 0; s < kSplits; ++s) {
-    const int sc = e - 8 - 4 * s;
+    const float down = __builtin_bit_cast(float, static_cast<unsigned>(127 - 4 * s) << 23);  // 2^-4s
     float m = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(r[j]));
@@ -129,16 +137,20 @@ __device__ __forceinline__ void fp8_splits8(float (&r)[8], int e, unsigned (&out
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float rv = r[4 * d + q];
-        v[q] = fabsf(rv) >= thr ? ldexpf(rv, -sc) : 0.f;
+        v[q] = fabsf(rv) >= thr ? rv : 0.f;
       }
-      unsigned w = static_cast<unsigned>(__builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false));
-      w = static_cast<unsigned>(__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], static_cast<int>(w), true));
+      v2s16 w2 = {0, 0};
+      w2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w2, v[0], v[1], down, false);
+      w2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w2, v[2], v[3], down, true);
+      const unsigned w = __builtin_bit_cast(unsigned, w2);
       out[s][d] = w;
-      // the piece's value, exactly; the residual is exact in float32
-      r[4 * d + 0] -= ldexpf(__builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), 0), sc);
-      r[4 * d + 1] -= ldexpf(__builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), 1), sc);
-      r[4 * d + 2] -= ldexpf(__builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), 2), sc);
-      r[4 * d + 3] -= ldexpf(__builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), 3), sc);
+      if (s + 1 < kSplits) {
+        // the piece's value, exactly; the residual is exact in float32
+        r[4 * d + 0] = fmaf(-__builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), 0), down, r[4 * d + 0]);
+        r[4 * d + 1] = fmaf(-__builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), 1), down, r[4 * d + 1]);
+        r[4 * d + 2] = fmaf(-__builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), 2), down, r[4 * d + 2]);
+        r[4 * d + 3] = fmaf(-__builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), 3), down, r[4 * d + 3]);
+      }
     }
   }
 }
@@ -157,8 +169,6 @@ __device__ __forceinline__ void fp8_splits16(float (&r)[16], int e, unsigned (&o
       out[s][2 * G] = o[s][0];
       out[s][2 * G + 1] = o[s][1];
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) r[8 * G + j] = g8[j];
   }
 }
 
