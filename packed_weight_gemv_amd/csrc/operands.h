@@ -110,6 +110,7 @@ __device__ __forceinline__ unsigned split_b_scale(int e, int j) {
 __device__ __forceinline__ unsigned split_a_scale(int e) { return static_cast<unsigned>(126 + split_ashift(e)); }
 
 typedef short v2s16 __attribute__((ext_vector_type(2)));
+typedef float v2f32 __attribute__((ext_vector_type(2)));
 constexpr int kDeferBits = 8;  // a residual below 2^-8 of its group's largest waits for a later split
 
 // Splits the 8 values of one summation group of the instruction (r[j]: K
@@ -146,10 +147,12 @@ __device__ __forceinline__ void fp8_splits8(float (&r)[8], int e, unsigned (&out
       out[s][d] = w;
       if (s + 1 < kSplits) {
         // the piece's value, exactly; the residual is exact in float32
-        r[4 * d + 0] = fmaf(-__builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), 0), down, r[4 * d + 0]);
-        r[4 * d + 1] = fmaf(-__builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), 1), down, r[4 * d + 1]);
-        r[4 * d + 2] = fmaf(-__builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), 2), down, r[4 * d + 2]);
-        r[4 * d + 3] = fmaf(-__builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), 3), down, r[4 * d + 3]);
+        const v2f32 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+        const v2f32 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+        r[4 * d + 0] = fmaf(-lo.x, down, r[4 * d + 0]);
+        r[4 * d + 1] = fmaf(-lo.y, down, r[4 * d + 1]);
+        r[4 * d + 2] = fmaf(-hi.x, down, r[4 * d + 2]);
+        r[4 * d + 3] = fmaf(-hi.y, down, r[4 * d + 3]);
       }
     }
   }

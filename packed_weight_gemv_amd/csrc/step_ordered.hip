@@ -532,10 +532,15 @@ __device__ __forceinline__ void issue_dynamic_sources(const chain::DevInput& in,
     const int span = in.head_dim * in.group;
     const unsigned src_bytes = static_cast<unsigned>(((n - 1) / span + 1) * in.head_dim) * 4u;
     const __amdgpu_buffer_rsrc_t rs = buffer_over(in.src, src_bytes);
-    const int lane = static_cast<int>(threadIdx.x & 63u);
+    // i / head_dim and its quotient by group through multiply-high by
+    // ceil(2^32 / d): exact, since i d < n^2 < 2^32 (the host bounds n)
+    const unsigned hd = static_cast<unsigned>(in.head_dim), grp = static_cast<unsigned>(in.group);
+    const unsigned m_hd = 0xFFFFFFFFu / hd + 1u, m_grp = grp > 1 ? 0xFFFFFFFFu / grp + 1u : 0u;
+    const unsigned lane = threadIdx.x & 63u;
     for (int i0 = 0; i0 < n; i0 += 256) {
-      const int i = i0 + 4 * lane;
-      lds_load16(rs, static_cast<unsigned>((i / span) * in.head_dim + i % in.head_dim) * 4u, st + 4 * i0);
+      const unsigned i = static_cast<unsigned>(i0) + 4u * lane;
+      const unsigned q = __umulhi(i, m_hd), kv = grp > 1 ? __umulhi(q, m_grp) : q;
+      lds_load16(rs, (kv * hd + (i - q * hd)) * 4u, st + 4 * i0);
     }
   }
 }
