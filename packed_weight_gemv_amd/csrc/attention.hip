@@ -57,6 +57,10 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
+// 2^x for x <= 0 by the hardware instruction alone: a result below 2^-126
+// (flushed to zero) weighs less than 2^-126 against the running maximum's 1.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float lo_bf16(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(unsigned w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -132,13 +136,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnArgs a) {
       float mx = m[g];
 #pragma unroll
       for (int u = 0; u < kAttnU; ++u) mx = fmaxf(mx, s[g][u]);
-      const float corr = mx == -INFINITY ? 1.f : exp2f(m[g] - mx);
+      const float corr = mx == -INFINITY ? 1.f : fast_exp2(m[g] - mx);
       l[g] *= corr;
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[g][i] *= corr;
 #pragma unroll
       for (int u = 0; u < kAttnU; ++u) {
-        const float p = valid[u] ? exp2f(s[g][u] - mx) : 0.f;
+        const float p = valid[u] ? fast_exp2(s[g][u] - mx) : 0.f;
         l[g] += p;
         const unsigned w[4] = {vw[u].x, vw[u].y, vw[u].z, vw[u].w};
 #pragma unroll
