@@ -28,7 +28,7 @@ namespace {
 
 constexpr int kAttnThreads = 256;
 constexpr int kAttnU = 4;  // positions per lane group per step
-constexpr int kMergeBatch = 16;  // split partials loaded together by the merging workgroup
+constexpr int kMergeBatch = 32;  // split partials loaded together by the merging workgroup
 constexpr int kMaxSplits = 512;  // splits per key/value head (workgroups in all <= ~512)
 
 struct AttnArgs {
@@ -185,34 +185,40 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnArgs a) {
 }
 
 // Merge of the split partials: workgroup `head`, one thread per value index.
-// The partials are complete (stream order after the split kernel); each
-// thread loads kMergeBatch splits' sums before using them.
+// The partials are complete (stream order after the split kernel).  Each
+// round of up to kMergeBatch splits issues every load it needs at once (the
+// threads' value sums, and the splits' (maximum, normaliser) pairs shared
+// through LDS), so that a round waits for one round trip; a running maximum
+// rescales across rounds.
 template <int HD>
 __global__ __launch_bounds__(HD) void attn_merge_kernel(AttnArgs a) {
-  __shared__ float2 sm[kMaxSplits];
+  __shared__ float2 sm[kMergeBatch];
   const int head = blockIdx.x, d = threadIdx.x;
   const float2* ml = a.part_ml + static_cast<long>(head) * a.splits;
   const float* pa = a.part + static_cast<long>(head) * a.splits * HD + d;
-  for (int j = d; j < a.splits; j += HD) sm[j] = ml[j];  // one load per thread and round
-  __syncthreads();
-  float M = -INFINITY;
-  for (int j = 0; j < a.splits; ++j) M = fmaxf(M, sm[j].x);
-  float A = 0.f, Z = 0.f;
+  float M = -INFINITY, A = 0.f, Z = 0.f;
   for (int j0 = 0; j0 < a.splits; j0 += kMergeBatch) {
+    const int nb = a.splits - j0 < kMergeBatch ? a.splits - j0 : kMergeBatch;
     float pv[kMergeBatch];
-    float2 mv[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) pv[u] = u < nb ? pa[static_cast<long>(j0 + u) * HD] : 0.f;
+    for (int u = d; u < kMergeBatch; u += HD) sm[u] = u < nb ? ml[j0 + u] : make_float2(-INFINITY, 0.f);
+    __syncthreads();
+    float mb = M;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) mb = fmaxf(mb, sm[u].x);
+    const float c = M == -INFINITY ? 0.f : exp2f(M - mb);
+    A *= c;
+    Z *= c;
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      const bool in = j0 + u < a.splits;
-      pv[u] = in ? pa[static_cast<long>(j0 + u) * HD] : 0.f;
-      mv[u] = in ? sm[j0 + u] : make_float2(-INFINITY, 0.f);
-    }
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) {
-      const float w = mv[u].x == -INFINITY ? 0.f : exp2f(mv[u].x - M);
+      const float2 mz = sm[u];
+      const float w = mz.x == -INFINITY ? 0.f : exp2f(mz.x - mb);
       A = fmaf(pv[u], w, A);
-      Z = fmaf(mv[u].y, w, Z);
+      Z = fmaf(mz.y, w, Z);
     }
+    M = mb;
+    __syncthreads();  // sm is rewritten by the next round
   }
   a.out[head * HD + d] = A / Z;
 }
