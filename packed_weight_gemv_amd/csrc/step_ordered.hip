@@ -921,12 +921,13 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
                        e < r0 + kMaxT ? e : r0 + kMaxT);
         ternary_tiles(cur, T, r0, e < r0 + kMaxT ? e : r0 + kMaxT, e, region, bsc, asc, slots, k, acc0, acc1);
       }
-      prefetch(nxt, li + 1, Ln, 1);
     } else {
       store_slice(L.in, stage, hsave, inv, const_cast<float*>(L.x), s0, s1);
     }
     __syncthreads();  // every slot of the level is written
     stamp(li, kEvProducts);
+    // the rest of the next level's tiles, while the control wave publishes
+    if (wave > 0) prefetch(nxt, li + 1, Ln, 1);
     if (wave == 0) {
       // rows of the workgroup: block bl's sum over the compute waves that
       // touched it, in wave order; then what the rows form for the next
