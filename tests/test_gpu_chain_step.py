@@ -151,6 +151,29 @@ def test_small_chained_steps_match_oracle(schedule, head_dim):
         token = new
 
 
+@pytest.mark.parametrize("kv_rows,head_dim", [(512, 64), (256, 64), (128, 32)], ids=["group1", "group2", "hd32"])
+@pytest.mark.parametrize("schedule", SCHEDULES, ids=SCHED_IDS)
+def test_chained_attention_groupings(schedule, kv_rows, head_dim):
+    """One-position attention with every query head on its own key/value head
+    (group 1), two per key/value head, and heads of 32 values: the gather of
+    value rows into the o projection's input against the oracle."""
+    n_layers = 2
+    shapes = dict(CHAIN_SMALL, k=(kv_rows, 512), v=(kv_rows, 512))
+    wl = build_step(n_layers=n_layers, shapes=shapes, vocab=3000, hidden=512, with_logits=True,
+                    schedule=pwg.SCHEDULE_LEVELS)
+    cs = make_chained(wl, schedule=schedule, head_dim=head_dim)
+    weights = level_weights(wl, shapes, n_layers)
+    shape = ch.ChainShape(512, 1536, 512 // head_dim, kv_rows // head_dim, head_dim)
+    token = wl.token0
+    run(cs)
+    new = check_teacher_forced(wl, cs, token, weights)
+    r = oracle_chain(wl, cs, weights, shape, token)
+    h = cs.h_final.cpu().numpy().astype(np.float64)
+    rel = np.linalg.norm(h - r["h_final"]) / np.linalg.norm(r["h_final"])
+    assert rel <= CHAIN_REL_L2, f"final residual rel L2 {rel}"
+    assert token_ok(new, r["logits"])
+
+
 @pytest.mark.parametrize("schedule", SCHEDULES, ids=SCHED_IDS)
 def test_schedules_form_the_first_input_alike(schedule):
     """Both ordered schedules form vectors with workgroups of 512 threads in
