@@ -791,7 +791,15 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
   // tiles of level li (descriptor L; li == nl: the vocabulary's first kMaxT;
   // past it: none) for this compute wave; every load of the wave completes
   // before they are read
-  auto prefetch = [&](u32x4 (&r)[kMaxT], unsigned li, const OLevel& L, int part) {
+  // A prefetch of level li's tiles (li == nl: the output table's first
+  // round) for this compute wave: where the tiles are, then the loads.
+  struct Pref {
+    const unsigned char* w;
+    unsigned bytes;
+    TileMap m;
+    int s, e;
+  };
+  auto pref_plan = [&](unsigned li, const OLevel& L) -> Pref {
     int s = 0, e = 0;
     unsigned bytes = 0;
     const unsigned char* w = P.out_table;
@@ -811,8 +819,12 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
       m = TileMap{w0 * T, 0, 1 << 30};
       e = (w1 - w0) * T;
     }
-    if (part == 0) prefetch_tiles<0, kPrefetchFirst>(r, w, bytes, m, s, e < s + kMaxT ? e : s + kMaxT);
-    if (part != 0) prefetch_tiles<kPrefetchFirst, kMaxT>(r, w, bytes, m, s, e < s + kMaxT ? e : s + kMaxT);
+    return Pref{w, bytes, m, s, e};
+  };
+  auto pref_issue = [&](u32x4 (&r)[kMaxT], const Pref& p, int part) {
+    const int e = p.e < p.s + kMaxT ? p.e : p.s + kMaxT;
+    if (part == 0) prefetch_tiles<0, kPrefetchFirst>(r, p.w, p.bytes, p.m, p.s, e);
+    if (part != 0) prefetch_tiles<kPrefetchFirst, kMaxT>(r, p.w, p.bytes, p.m, p.s, e);
   };
   // control wave: per row lane + 64 j of the workgroup's rows of a level, its
   // scale and, for a norm epilogue, the gain and the residual stream there
@@ -845,8 +857,9 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
     if (nl > 0 && lane < kDw)  // level 0's descriptor
       reinterpret_cast<int*>(ring)[lane] = reinterpret_cast<const int*>(levels)[lane];
   } else {
-    prefetch(ra, 0, levels[0], 0);
-    prefetch(ra, 0, levels[0], 1);
+    const Pref p0 = pref_plan(0, levels[0]);
+    pref_issue(ra, p0, 0);
+    pref_issue(ra, p0, 1);
   }
 
   // The sources of level li's input (li == nl: h) in LDS, after the previous
@@ -893,6 +906,10 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
     const WgRows R = wg_rows(L);
     int s0, s1;
     wg_slice(cols, s0, s1);
+    // where the next level's tiles are (worked out while this level's last
+    // loads land)
+    const OLevel Ln = uni_level(&ring[(li + 1) & 1]);  // not read past the last level
+    const Pref pn = pref_plan(li + 1, Ln);
     // every earlier load (this level's tiles) has completed; saying so on
     // every path lets the compiler count the prefetch below instead of
     // draining it before the products
@@ -900,8 +917,7 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
     // the first kPrefetchFirst tiles of the next level now; the rest after
     // this level's products, so that a large next level holds up neither the
     // conversion nor the products alone
-    const OLevel Ln = uni_level(&ring[(li + 1) & 1]);  // not read past the last level
-    if (wave > 0) prefetch(nxt, li + 1, Ln, 0);
+    if (wave > 0) pref_issue(nxt, pn, 0);
     if (form_elementwise(L.in, cols, stage, region, red, hsave, s0, s1)) __syncthreads();
     const float inv = norm_scale(L.in, cols, red, slots, static_cast<int>(G));
     convert_ternary(stage, cols, region, inv);
@@ -927,7 +943,7 @@ __global__ __launch_bounds__(kThreads, 1) void ordered_step_kernel(const OPlan* 
     __syncthreads();  // every slot of the level is written
     stamp(li, kEvProducts);
     // the rest of the next level's tiles, while the control wave publishes
-    if (wave > 0) prefetch(nxt, li + 1, Ln, 1);
+    if (wave > 0) pref_issue(nxt, pn, 1);
     if (wave == 0) {
       // rows of the workgroup: block bl's sum over the compute waves that
       // touched it, in wave order; then what the rows form for the next
