@@ -389,7 +389,9 @@ int pwg_embed_gather(const int8_t* table, const float* row_scale,
  *   PWG_INPUT_SWIGLU:         x[i] = silu(src[i]) * src[n + i], silu(g) = g / (1 + e^-g)
  *                             (src: the stacked gate|up output, gate first).
  * Buffers may not overlap: x, resid_out, src, resid and gamma are distinct
- * (PWG_ERR_ARG where pointers are equal).  Only the ordered schedules
+ * (PWG_ERR_ARG where pointers are equal), and the level's y overlaps none
+ * of them over their extents (src: 2n values for SWIGLU, n/group for
+ * ATTN1, n otherwise; PWG_ERR_ARG).  Only the ordered schedules
  * (LEVELS, PERSISTENT) at batch 1 take such levels (PWG_ERR_UNSUPPORTED
  * otherwise).  Arithmetic is float32: the mean of squares is a float32 sum,
  * the root and the quotient IEEE float32. */

@@ -245,6 +245,27 @@ int validate_input(const pwg_input& in, int64_t n, const float* x, const char* f
   return PWG_OK;
 }
 
+// A chained level's output may not overlap anything its input is formed
+// from or written to: the level's workgroups form the input while others
+// may already store their rows.
+int check_output_apart(const pwg_input& in, int64_t n, const float* x, const float* y, int64_t rows, const char* fn) {
+  if (in.op == PWG_INPUT_GIVEN) return PWG_OK;
+  const int64_t src_n = in.op == PWG_INPUT_SWIGLU ? 2 * n : in.op == PWG_INPUT_ATTN1 ? n / (in.group > 0 ? in.group : 1) : n;
+  const struct {
+    const float* p;
+    int64_t count;
+    const char* what;
+  } bufs[5] = {{x, n, "x"}, {in.resid_out, n, "resid_out"}, {in.src, src_n, "src"}, {in.resid, n, "resid"},
+               {in.gamma, n, "gamma"}};
+  const uintptr_t y0 = reinterpret_cast<uintptr_t>(y), y1 = y0 + static_cast<uintptr_t>(rows) * 4;
+  for (const auto& b : bufs) {
+    if (!b.p) continue;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(b.p), b1 = b0 + static_cast<uintptr_t>(b.count) * 4;
+    if (b0 < y1 && y0 < b1) return fail(PWG_ERR_ARG, "%s: the level's y overlaps its input's %s", fn, b.what);
+  }
+  return PWG_OK;
+}
+
 int validate_step(const pwg_step_desc* d) {
   const char* fn = "pwg_decode_step_weights";
   if (!d) return fail(PWG_ERR_ARG, "%s: desc is null", fn);
@@ -270,6 +291,7 @@ int validate_step(const pwg_step_desc* d) {
     const pwg_level& L = d->levels[i];
     int rc = validate_ternary(L.w_packed, L.row_scale, L.rows, L.cols, L.x, 1, L.y, fn);
     if (rc == PWG_OK) rc = validate_input(L.in, L.cols, L.x, fn, "level input");
+    if (rc == PWG_OK) rc = check_output_apart(L.in, L.cols, L.x, L.y, L.rows, fn);
     if (rc != PWG_OK) return fail(rc, "%s (level %d)", pwg_last_error(), i);
     any_chained = any_chained || chained(L.in);
   }
@@ -376,8 +398,11 @@ extern "C" int pwg_decode_step_weights(const pwg_step_desc* d, void* stream) {
                           d->emb_scale_out, d->emb_deq_out, stream));
   for (int i = 0; i < d->n_levels; ++i) {
     const pwg_level& L = d->levels[i];
-    if (chained(L.in)) TRY(launch_chain_input(L.in, L.cols, const_cast<float*>(L.x), d, stream));
-    TRY(launch_ternary_gemv(L.w_packed, L.row_scale, L.rows, L.cols, L.x, 1, L.y, stream));
+    if (chained(L.in))  // the GEMV forms its input itself
+      TRY(launch_ternary_gemv_formed(L.w_packed, L.row_scale, L.rows, L.cols, L.in, d, const_cast<float*>(L.x), L.y,
+                                     stream));
+    else
+      TRY(launch_ternary_gemv(L.w_packed, L.row_scale, L.rows, L.cols, L.x, 1, L.y, stream));
   }
   if (chained(d->h_in)) TRY(launch_chain_input(d->h_in, d->hidden, const_cast<float*>(d->h), d, stream));
   return launch_int8_gemv_argmax(d->out_table, d->out_scale, d->vocab, d->hidden, d->h, 1, d->workspace,

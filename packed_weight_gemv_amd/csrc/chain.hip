@@ -1,9 +1,11 @@
-// Input formation of a chained step on the levels schedule: a small kernel
-// forms a level's input (RMSNorm with a gain, one-position grouped-query
-// attention or SwiGLU, with the residual sum) and writes it to the level's x
-// before the level's GEMV runs (page "The Neutrino Engine", section "A 104
+// Input formation of a chained step on the levels schedule, as a kernel of
+// its own: it forms an input vector (RMSNorm with a gain, one-position
+// grouped-query attention or SwiGLU, with the residual sum) and writes it to
+// its x before the consumer runs (page "The Neutrino Engine", section "A 104
 // microsecond floor inside a 694 microsecond step": each projection waits for
-// the activations of the one before it).
+// the activations of the one before it).  The levels schedule runs it for the
+// output projection's input h; the ternary levels form theirs inside their
+// GEMV kernel.
 #include "chain_input.h"
 #include "device_common.h"
 #include "pwg_internal.h"

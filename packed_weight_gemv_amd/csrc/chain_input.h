@@ -8,9 +8,10 @@
 //
 // form_input() is called by every thread of a workgroup of T threads and
 // leaves the formed float32 vector in LDS; store_formed() writes it, and the
-// residual sum, to memory.  The ordered step schedules call both: the levels
-// schedule from a small kernel before the level's GEMV, the persistent
-// schedule in every workgroup after the level barrier.
+// residual sum, to memory.  The levels schedule calls both: every workgroup
+// of a level's GEMV kernel forms the level's whole input, and a small kernel
+// (chain.hip) forms the output projection's.  The persistent schedule forms
+// its inputs with its own routines on the descriptors declared here.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -31,6 +31,7 @@
 // multiplied.  Each wave keeps two groups of kG tile loads in flight across
 // chunk and batch boundaries; x is loaded first, then the first group, and
 // the conversion waits for x alone.
+#include "chain_input.h"
 #include "device_common.h"
 #include "operands.h"
 #include "pwg_internal.h"
@@ -111,6 +112,21 @@ __device__ __forceinline__ XRound load_x_round(__amdgpu_buffer_rsrc_t xr, int co
   return q;
 }
 
+// The same round of T2 quarters from a float vector in LDS.
+__device__ __forceinline__ XRound stage_x_round(const float* stage, int cols, int t0) {
+  const int tid = t0 + static_cast<int>(threadIdx.x);
+  const int beta = tid >> 2, h = (tid >> 1) & 1;
+  const int k0 = 32 * beta + 16 * h;  // cols % 16 == 0: a half is all in or all out
+  XRound q;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 v = k0 < cols ? *reinterpret_cast<const f32x4*>(stage + k0 + 4 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q.v[4 * i + e] = v[e];
+  }
+  return q;
+}
+
 // Converts one round into the LDS operand region (blocks past cols up to the
 // last window are written as zero).  Every thread takes part: the quarters
 // of a block exchange their maxima with lane shuffles.
@@ -181,11 +197,16 @@ __host__ __device__ constexpr size_t fmt_region(int fmt, int64_t cols) {
          (fmt == kB3Tiled ? 1024 : 0);
 }
 
-template <int kFmt>
+// kForm: the chained levels schedule's variant, which forms its input
+// itself (every workgroup forms the whole vector from its sources into LDS,
+// writes its own slice of it to x, and of the residual sum to resid_out),
+// instead of a formation kernel before it.
+template <int kFmt, bool kForm = false>
 __global__ __launch_bounds__(kThreads) void t2_mfma_gemv_kernel(const unsigned char* __restrict__ w,
                                                                  const float* __restrict__ scale, int rows, int cols,
                                                                  const float* __restrict__ x, float* __restrict__ y,
-                                                                 int kw, int nbb) {
+                                                                 int kw, int nbb, chain::DevInput fin,
+                                                                 chain::EmbedSrc femb) {
   extern __shared__ __align__(16) unsigned char smem[];
   const unsigned lane = threadIdx.x & 63u, n = lane & 15u, g = lane >> 4;
   const int wave = uni(static_cast<int>(threadIdx.x >> 6));
@@ -264,7 +285,21 @@ __global__ __launch_bounds__(kThreads) void t2_mfma_gemv_kernel(const unsigned c
       buffer_over(scale, static_cast<unsigned>(rows) * 4u),
       lane < 16u && wave < nblk ? static_cast<unsigned>(((bw0 + wave) * 16 + lane) * 4) : kOff, 0, 0));
   u32x4 ra[kG], rb[kG];
-  {
+  if constexpr (kForm) {
+    // the first weight loads go out before the sources are read; the formed
+    // vector lies in LDS past the slot buffers
+    float* stage = reinterpret_cast<float*>(slots + 2 * slot_buf);
+    load_group(ra);
+    chain::form_input<kThreads>(fin, cols, stage, stage + cols, femb, 0, cols);
+    const int lo = static_cast<int>(static_cast<long>(blockIdx.x) * cols / gridDim.x);
+    const int hi = static_cast<int>((static_cast<long>(blockIdx.x) + 1) * cols / gridDim.x);
+    chain::store_formed(fin, cols, stage, const_cast<float*>(x), femb, lo, hi, static_cast<int>(threadIdx.x), kThreads);
+    for (int r0 = 0; r0 < T * 32; r0 += kThreads) {
+      XRound q = stage_x_round(stage, cols, r0);
+      convert_x_round<kFmt>(q, cols, r0, smem);
+    }
+    __syncthreads();
+  } else {
     XRound q = load_x_round<kFmt>(xr, cols, 0);  // x first: its wait leaves the weight loads in flight
     load_group(ra);
     if (kFmt == kB3Tiled && threadIdx.x < 256u)
@@ -386,22 +421,28 @@ int device_cus() {
   return cus;
 }
 
+// form: the input to form in the kernel (kForm instances), else null.
 int launch(Instance& in, const void* w, const float* s, int64_t rows, int64_t cols, const float* x, int32_t batch,
-           float* y, void* stream) {
+           float* y, void* stream, const chain::DevInput* form = nullptr, const chain::EmbedSrc* emb = nullptr) {
+  // a formed input: cols floats and the norm's per-wave sums past the slots
+  const size_t stage = form ? (static_cast<size_t>(cols) * 4 + (kWaves + 1) * 4 + 15) / 16 * 16 : 0;
+  const size_t budget = kLdsBudget - stage;
   const size_t region = fmt_region(in.fmt, cols);
   const int T = static_cast<int>(in.fmt == kB3Tiled ? ops::b3_windows(cols) : (cols + 255) / 256);
   // slots: all the LDS the operand region leaves (capped); or, for a matrix
   // with at least two blocks per wave at k workgroups per CU, room for k
   // resident workgroups (more waves to hide the load and LDS latencies)
   const long nb = (rows + 15) / 16;
-  size_t slot_room = kLdsBudget - region < kSlotBudget ? kLdsBudget - region : kSlotBudget;
+  if (region + kSlotMin > budget)
+    return fail(PWG_ERR_UNSUPPORTED, "ternary GEMV: %lld columns leave too little LDS", static_cast<long long>(cols));
+  size_t slot_room = budget - region < kSlotBudget ? budget - region : kSlotBudget;
   for (int k = target_residency(in.fmt); k >= 2; --k) {
-    if (kLdsBudget / k >= region + kSlotMin && nb >= static_cast<long>(k) * device_cus() * 2 * kWaves) {
-      slot_room = kLdsBudget / k - region < slot_room ? kLdsBudget / k - region : slot_room;
+    if (budget / k >= region + kSlotMin && nb >= static_cast<long>(k) * device_cus() * 2 * kWaves) {
+      slot_room = budget / k - region < slot_room ? budget / k - region : slot_room;
       break;
     }
   }
-  const size_t lds = region + slot_room;
+  const size_t lds = region + slot_room + stage;
   const long cap = static_cast<long>(device_cus()) * in.occupancy(lds);
   const unsigned grid = static_cast<unsigned>(nb < cap ? nb : cap);
   const long wg_blocks = (nb + grid - 1) / grid;
@@ -426,7 +467,9 @@ int launch(Instance& in, const void* w, const float* s, int64_t rows, int64_t co
   for (int b = 0; b < batch; ++b) {
     const float* xb = x + static_cast<size_t>(b) * cols;
     float* yb = y + static_cast<size_t>(b) * rows;
-    void* args[] = {&wp, const_cast<float**>(&s), &r32, &c32, &xb, &yb, &kw, &nbb};
+    chain::DevInput fin = form ? *form : chain::DevInput{};
+    chain::EmbedSrc femb = emb ? *emb : chain::EmbedSrc{};
+    void* args[] = {&wp, const_cast<float**>(&s), &r32, &c32, &xb, &yb, &kw, &nbb, &fin, &femb};
     const hipError_t e = hipLaunchKernel(in.fn, dim3(grid), dim3(kThreads), args, lds, st);
     if (e != hipSuccess) return fail(PWG_ERR_HIP, "ternary GEMV launch: %s", hipGetErrorString(e));
   }
@@ -440,6 +483,16 @@ int launch_ternary_gemv(const void* w, const float* s, int64_t rows, int64_t col
                         float* y, void* stream) {
   static Instance rowmajor{reinterpret_cast<const void*>(&t2_mfma_gemv_kernel<kT2Rows>), kT2Rows, {0, 0}, {0, 0}};
   return launch(rowmajor, w, s, rows, cols, x, batch, y, stream);
+}
+
+// Row-major T2 blob, batch 1, with the input formed in the kernel from its
+// sources (the chained levels schedule); x receives the formed vector.
+int launch_ternary_gemv_formed(const void* w, const float* s, int64_t rows, int64_t cols, const pwg_input& in,
+                               const pwg_step_desc* d, float* x, float* y, void* stream) {
+  static Instance formed{reinterpret_cast<const void*>(&t2_mfma_gemv_kernel<kT2Rows, true>), kT2Rows, {0, 0}, {0, 0}};
+  const chain::DevInput fin = chain::from_abi(in);
+  const chain::EmbedSrc emb{d->emb_table, d->emb_scale, d->token_in, static_cast<long>(d->vocab)};
+  return launch(formed, w, s, rows, cols, x, 1, y, stream, &fin, &emb);
 }
 
 // Tiled T2 (cols % 256 == 0), batch 1.

@@ -35,6 +35,8 @@ size_t int8_partials(int64_t rows);
 // Batch-1 ternary GEMV on the tiled arrangement (gemv_mfma.hip).
 int launch_ternary_gemv_b3(const void* w, const float* s, int64_t rows, int64_t cols, const float* x, int32_t batch,
                            float* y, void* stream);
+int launch_ternary_gemv_formed(const void* w, const float* s, int64_t rows, int64_t cols, const pwg_input& in,
+                               const pwg_step_desc* d, float* x, float* y, void* stream);
 int launch_ternary_gemv_tiled1(const void* w, const float* s, int64_t rows, int64_t cols, const float* x, float* y,
                                void* stream);
 int launch_argmax_reduce_batch(const unsigned long long* partials, int n, size_t nparts, int32_t batch, int32_t* token,

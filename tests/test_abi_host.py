@@ -392,7 +392,8 @@ def test_tile_rows_argument_errors():
 
 def test_chained_input_errors():
     """Level inputs formed from earlier outputs (pwg_input): unknown ops,
-    missing sources, overlapping buffers, bad head grouping, a negative eps,
+    missing sources, overlapping buffers (among the input's and with the
+    level's own output), bad head grouping, a negative eps,
     over-long inputs and the schedules that cannot order levels are refused
     before anything is enqueued (every call here fails validation)."""
     P = [A + 256 * k for k in range(8)]
@@ -432,6 +433,12 @@ def test_chained_input_errors():
     check(I(pwg.INPUT_ATTN1, 0, 4, 0.0, P[6], None, None, None), ERR_ARG, "heads")
     check(I(pwg.INPUT_ATTN1, 128, 3, 0.0, P[6], None, None, None), ERR_ARG, "heads")    # 384 does not divide 4096
     check(I(pwg.INPUT_ATTN1, 128, 4, 0.0, P[2], None, None, None), ERR_ARG, "overlap")  # src == x
+    # the level's own output lies apart from everything its input reads or writes
+    Y = A + (2 << 20)
+    lv[0] = pwg.Level(P[0], P[1], A + (1 << 20), Y, 64, 4096)
+    check(I(pwg.INPUT_SWIGLU, 0, 0, 0.0, Y - 4 * 4096, None, None, None), ERR_ARG, "y overlaps its input's src")
+    check(I(pwg.INPUT_RMSNORM, 0, 0, 1e-6, None, P[4], P[5], Y + 128), ERR_ARG, "y overlaps its input's resid_out")
+    check(I(pwg.INPUT_ATTN1, 128, 4, 0.0, Y - 4 * 1024 + 16, None, None, None), ERR_ARG, "y overlaps its input's src")
     # ordered schedules only, batch 1 only
     d.schedule, d.weight_layout = pwg.SCHEDULE_STREAM, pwg.LAYOUT_TILED
     d.workspace_bytes = 1 << 40
