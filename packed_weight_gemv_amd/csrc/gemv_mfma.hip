@@ -433,8 +433,9 @@ int launch(Instance& in, const void* w, const float* s, int64_t rows, int64_t co
   // with at least two blocks per wave at k workgroups per CU, room for k
   // resident workgroups (more waves to hide the load and LDS latencies)
   const long nb = (rows + 15) / 16;
-  if (region + kSlotMin > budget)
-    return fail(PWG_ERR_UNSUPPORTED, "ternary GEMV: %lld columns leave too little LDS", static_cast<long long>(cols));
+  if (form && region + kSlotMin > budget)
+    return fail(PWG_ERR_UNSUPPORTED, "ternary GEMV: %lld formed columns leave too little LDS",
+                static_cast<long long>(cols));
   size_t slot_room = budget - region < kSlotBudget ? budget - region : kSlotBudget;
   for (int k = target_residency(in.fmt); k >= 2; --k) {
     if (budget / k >= region + kSlotMin && nb >= static_cast<long>(k) * device_cus() * 2 * kWaves) {
